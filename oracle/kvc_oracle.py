@@ -1,0 +1,265 @@
+"""fp64 reference for KV append, prefill fill and single-query decode attention.
+
+TEST INFRASTRUCTURE: imported only by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py. Written as plain numpy loops so it can be checked
+against the pages by eye; no blocking, no online softmax, no splitting.
+
+Page tags ([KVG], [W1D4], [LA11]) are defined in this package's ``__init__``.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def widen(x) -> np.ndarray:
+    """Exact widening of stored values to fp64.
+
+    Accepts a numpy array or a torch tensor of fp32/fp16/bf16; every such value
+    is exactly representable in fp64, so nothing is rounded here.
+    """
+    if hasattr(x, "detach"):  # torch tensor, possibly bf16 (numpy has no bf16)
+        import torch
+        return x.detach().to(device="cpu", dtype=torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """KV head that query head ``h`` reads.
+
+    [W1D4 §2.3, §3.4]: with h query heads in G groups, query head j uses K/V head
+    floor(j / (h/G)); this is the grouping repeat_interleave produces
+    ([KVG] runnable experiment, expand_kv). MHA is n_kv == n_q, MQA is n_kv == 1.
+    """
+    if n_kv_heads <= 0 or n_q_heads % n_kv_heads != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    return h // (n_q_heads // n_kv_heads)
+
+
+def append(k_cache, v_cache, seq_lens, k_new, v_new):
+    """Write one new token per sequence into a preallocated cache.
+
+    [W1D4 §3.1] KVCache.update: the cache is allocated once to max_len and the
+    T new tokens go to slots [pos, pos+T); here T = 1 and each sequence b has its
+    own pos = seq_lens[b] (the ragged form of the capacity formula in [KVG]
+    "capacity formula"). [KVG] "two equivalent decode paths": the append is an
+    in-place slot write; every other slot stays as it was.
+
+    Arrays may be of any dtype (use integer views for a bitwise model of bf16).
+    k_cache, v_cache: [B, H_kv, T_max, D]; k_new, v_new: [B, H_kv, D].
+    Returns (k_out, v_out, overflow) where overflow[b] is True when slot
+    seq_lens[b] lies outside [0, T_max): that sequence is then left untouched.
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    batch, _, t_max, _ = k_out.shape
+    overflow = np.zeros(batch, dtype=bool)
+    for b in range(batch):
+        pos = int(seq_lens[b])
+        if pos < 0 or pos >= t_max:
+            overflow[b] = True
+            continue
+        k_out[b, :, pos, :] = k_new[b]
+        v_out[b, :, pos, :] = v_new[b]
+    return k_out, v_out, overflow
+
+
+def prefill_fill(k_cache, v_cache, seq_lens, k, v):
+    """Write T_new tokens per sequence at slots [seq_lens[b], seq_lens[b]+T_new).
+
+    [W1D4 §3.1] KVCache.update with T = T_new (prefill, or a prompt fed in chunks
+    when seq_lens[b] > 0, [W1D4 §3.5] test 1). k, v: [B, H_kv, T_new, D].
+    A sequence whose range does not fit in [0, T_max) is left untouched and
+    flagged.
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    batch, _, t_max, _ = k_out.shape
+    t_new = k.shape[2]
+    overflow = np.zeros(batch, dtype=bool)
+    for b in range(batch):
+        pos = int(seq_lens[b])
+        if pos < 0 or pos + t_new > t_max:
+            overflow[b] = True
+            continue
+        for i in range(t_new):
+            k_out[b, :, pos + i, :] = k[b, :, i, :]
+            v_out[b, :, pos + i, :] = v[b, :, i, :]
+    return k_out, v_out, overflow
+
+
+def decode_attention(q, k_cache, v_cache, seq_lens, n_pending: int = 1, scale=None):
+    """Single new query per head attending every cached token, in fp64.
+
+    [LA11 §2.2] single-step decode: after k_t, v_t are appended,
+    s_t = q_t K^T * scale and o_t = softmax(s_t) V over all cached tokens.
+    [KVG] decode_one / [W1D4 §1.3]: one query per head, no mask (every cached
+    token precedes the query). The page's garbled formula lost the square root
+    of the divisor; the glossary's code divides by sqrt(head_dim), which is the
+    default here. [W1D4 §3.4] query head h reads KV head floor(h / (H_q/H_kv)).
+
+    q: [B, H_q, D]; caches [B, H_kv, T_max, D]; each sequence b attends its
+    first N_b = seq_lens[b] + n_pending slots. Softmax is the two-pass textbook
+    form: max, exponentials, sum, weighted sum of V, divide. A sequence with
+    N_b == 0 gives a zero row (softmax over an empty set has no value).
+    Returns fp64 [B, H_q, D].
+    """
+    q = widen(q)
+    k = widen(k_cache)
+    v = widen(v_cache)
+    batch, n_q, d = q.shape
+    n_kv, t_max = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((batch, n_q, d), dtype=np.float64)
+    for b in range(batch):
+        n = int(seq_lens[b]) + int(n_pending)
+        if n > t_max:
+            raise ValueError(f"sequence {b} attends {n} tokens but the cache holds {t_max}")
+        if n <= 0:
+            continue
+        for h in range(n_q):
+            g = kv_head_of(h, n_q, n_kv)
+            keys = k[b, g, :n, :]
+            vals = v[b, g, :n, :]
+            scores = (keys @ q[b, h]) * scale          # [N]
+            m = scores.max()
+            e = np.exp(scores - m)
+            out[b, h] = (e @ vals) / e.sum()
+    return out
+
+
+def causal_attention(q, k, v, n_q_heads: int, n_kv_heads: int, scale=None):
+    """Full causal self-attention over a prefix ("path A" of [KVG]).
+
+    [KVG] prefill: scores = q K^T / sqrt(D) plus an upper-triangular -inf mask
+    (row i sees keys 0..i), softmax along the keys, times V. GQA heads map as
+    in ``kv_head_of``. q: [H_q, T, D]; k, v: [H_kv, T, D]. Returns [H_q, T, D].
+    """
+    q = widen(q)
+    k = widen(k)
+    v = widen(v)
+    _, t, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros_like(q)
+    mask = np.triu(np.full((t, t), -np.inf), 1)
+    for h in range(n_q_heads):
+        g = kv_head_of(h, n_q_heads, n_kv_heads)
+        s = (q[h] @ k[g].T) * scale + mask              # [T, T]
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / e.sum(axis=1, keepdims=True)
+        out[h] = p @ v[g]
+    return out
+
+
+def project(x, w, n_heads: int, head_dim: int):
+    """Per-token projection x @ W split into heads, in fp64.
+
+    [KVG] runnable experiment, project: (x @ W) viewed as (tokens, heads, D) and
+    transposed so that head h owns columns [h*D, (h+1)*D). x: [T, hidden];
+    returns [n_heads, T, D]. Rows are independent, so a longer prefix leaves
+    the earlier rows unchanged ([W1D4 §1.2]).
+    """
+    x = widen(x)
+    w = widen(w)
+    # one row at a time, so a row's bits never depend on how many rows a BLAS
+    # call was given (the invariant above is then exact, not up to rounding)
+    y = np.stack([row @ w for row in x])
+    return y.reshape(x.shape[0], n_heads, head_dim).transpose(1, 0, 2)
+
+
+def _merge_heads(ctx_last):
+    """[H_q, D] context of one position -> [H_q * D] (head-major), as the page's
+    transpose(1, 2).reshape does before the output projection."""
+    return ctx_last.reshape(-1)
+
+
+def toy_path_a(x, wq, wk, wv, wo, n_q: int, n_kv: int, head_dim: int, n_prompt: int):
+    """Path A of [KVG] "two equivalent decode paths": at every decode step the
+    whole prefix is projected again and run through causal attention; only the
+    last position's output is kept, then multiplied by W_o.
+
+    x: [T_total, hidden] (one sequence). Returns (outputs [n_dec, hidden],
+    contexts [n_dec, H_q, D]).
+    """
+    x = widen(x)
+    wo = widen(wo)
+    outputs, contexts = [], []
+    for t in range(n_prompt, x.shape[0]):
+        prefix = x[: t + 1]
+        q = project(prefix, wq, n_q, head_dim)
+        k = project(prefix, wk, n_kv, head_dim)
+        v = project(prefix, wv, n_kv, head_dim)
+        ctx = causal_attention(q, k, v, n_q, n_kv)[:, -1, :]
+        contexts.append(ctx)
+        outputs.append(_merge_heads(ctx) @ wo)
+    return np.stack(outputs), np.stack(contexts)
+
+
+def toy_path_b(x, wq, wk, wv, wo, n_q: int, n_kv: int, head_dim: int, n_prompt: int):
+    """Path B of [KVG]: prefill the prompt's K/V once into a preallocated cache
+    ([W1D4 §3.1]), then per token project only the new position, append its
+    k, v, and let its q attend the whole cache ([W1D4 §1.3]).
+
+    Returns (outputs [n_dec, hidden], contexts [n_dec, H_q, D], k_cache, v_cache)
+    with caches [1, H_kv, T_total, D] in fp64.
+    """
+    x = widen(x)
+    wo = widen(wo)
+    t_total = x.shape[0]
+    k_cache = np.zeros((1, n_kv, t_total, head_dim))
+    v_cache = np.zeros((1, n_kv, t_total, head_dim))
+    seq_lens = np.array([0])
+    kp = project(x[:n_prompt], wk, n_kv, head_dim)[None]
+    vp = project(x[:n_prompt], wv, n_kv, head_dim)[None]
+    k_cache, v_cache, ovf = prefill_fill(k_cache, v_cache, seq_lens, kp, vp)
+    assert not ovf.any()
+    seq_lens = seq_lens + n_prompt
+    outputs, contexts = [], []
+    for t in range(n_prompt, t_total):
+        row = x[t: t + 1]
+        q = project(row, wq, n_q, head_dim)[:, 0, :][None]      # [1, H_q, D]
+        k_new = project(row, wk, n_kv, head_dim)[:, 0, :][None]  # [1, H_kv, D]
+        v_new = project(row, wv, n_kv, head_dim)[:, 0, :][None]
+        k_cache, v_cache, ovf = append(k_cache, v_cache, seq_lens, k_new, v_new)
+        assert not ovf.any()
+        ctx = decode_attention(q, k_cache, v_cache, seq_lens, n_pending=1)[0]
+        contexts.append(ctx)
+        outputs.append(_merge_heads(ctx) @ wo)
+        seq_lens = seq_lens + 1
+    return np.stack(outputs), np.stack(contexts), k_cache, v_cache
+
+
+def cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, elem_bytes: int, lengths) -> int:
+    """Logical K+V payload in bytes.
+
+    [KVG] capacity formula (ragged form 2*L*H_kv*D*s*sum_i T_i); [W1D4 §1.4];
+    [LA11 §2.3] (elements 2*B*H_kv*T*d_k, times bytes per element, times L).
+    The leading 2 counts K and V.
+    """
+    total_tokens = sum(int(t) for t in lengths)
+    return 2 * n_layers * n_kv_heads * head_dim * elem_bytes * total_tokens
+
+
+def concat_append_positions(n_tokens: int) -> int:
+    """Token positions moved when a cache grows by concatenation, one token per
+    step: step t copies the t-1 old positions plus the new one ([W1D4 §3.1],
+    the pages' anti-pattern)."""
+    moved = 0
+    length = 0
+    for _ in range(n_tokens):
+        length += 1
+        moved += length
+    return moved
+
+
+def prealloc_append_positions(n_tokens: int) -> int:
+    """Token positions written when the cache is preallocated: one per step."""
+    written = 0
+    for _ in range(n_tokens):
+        written += 1
+    return written

@@ -1,0 +1,372 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Sources (page title and section):
+  KVG  = glossary "KV 缓存" (llm-glossary.tokens-kit.com/terms/kv-cache/)
+  W1D4 = "第 1 周 · Day 4：KV Cache 与 MQA / GQA" (semidirectx.com course notes)
+  LA11 = "11.7 KV Cache：形状、显存与带宽" (yongzhen.wang textbook)
+"""
+
+import csv
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+UNITS = {"B": 1, "KiB": 2**10, "MiB": 2**20, "GiB": 2**30}
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        lines = [ln for ln in f if not ln.startswith("#")]
+    return list(csv.DictReader(lines))
+
+
+# ---------------------------------------------------------------- capacity --
+
+@pytest.mark.parametrize("row", _rows("capacity_values.csv"), ids=lambda r: r["citation"][:48])
+def test_cache_bytes_matches_printed_values(row):
+    """Every cache size the pages print (tests/golden/capacity_values.csv)."""
+    got = oracle.cache_bytes(int(row["n_layers"]), int(row["n_kv_heads"]), int(row["head_dim"]),
+                             int(row["elem_bytes"]), [int(row["seq_len"])] * int(row["batch"]))
+    want = float(row["value"]) * UNITS[row["unit"]]
+    tol = float(row["rel_tol"])
+    if tol == 0:
+        assert got == want, row["citation"]
+    else:
+        assert abs(got - want) <= tol * want, (got, want, row["citation"])
+
+
+def test_cache_bytes_ragged_form():
+    """KVG capacity formula: a ragged batch counts sum_i T_i, not B * max T."""
+    lens = [3000, 4500, 6000]
+    assert oracle.cache_bytes(32, 32, 128, 2, lens) == 524288 * sum(lens)
+    assert oracle.cache_bytes(32, 32, 128, 2, lens) < oracle.cache_bytes(32, 32, 128, 2, [6000] * 3)
+
+
+def test_concat_versus_prealloc_positions():
+    """W1D4 §3.1 (check group 8): generating 4096 tokens, concatenation moves
+    about 8.39 million positions, preallocation writes 4096, about 2048x."""
+    moved = oracle.concat_append_positions(4096)
+    written = oracle.prealloc_append_positions(4096)
+    assert written == 4096
+    assert round(moved / 1e6, 2) == 8.39
+    assert moved == 4096 * 4097 // 2
+    assert round(moved / written) == 2048
+
+
+# ------------------------------------------------------------- GQA mapping --
+
+def test_kv_head_of_grouping():
+    """W1D4 §2.3 diagram: 8 query heads, 2 KV heads -> q0..q3 read k0, q4..q7 read k1;
+    MQA maps all to k0; MHA is the identity."""
+    assert [oracle.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head_of(h, 8, 1) for h in range(8)] == [0] * 8
+    assert [oracle.kv_head_of(h, 8, 8) for h in range(8)] == list(range(8))
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
+
+
+def _rand(shape, seed, *names, dtype="fp32"):
+    return synth.normal(shape, dtype, seed, *names)
+
+
+def test_gqa_equals_mha_on_repeat_interleaved_cache():
+    """W1D4 §3.4 / KVG expand_kv: GQA sharing must equal MHA over K/V expanded
+    with repeat_interleave (torch's op), exactly; j mod G grouping (torch.repeat)
+    must differ (W1D4 §3.4 warns it raises no error)."""
+    b, hq, hkv, t, d = 2, 8, 2, 11, 16
+    q = _rand((b, hq, d), 1, "q")
+    k = _rand((b, hkv, t, d), 1, "k")
+    v = _rand((b, hkv, t, d), 1, "v")
+    lens = np.array([6, 10])
+    gqa = oracle.decode_attention(q, k, v, lens, n_pending=1)
+    k_exp = torch.repeat_interleave(k, hq // hkv, dim=1)
+    v_exp = torch.repeat_interleave(v, hq // hkv, dim=1)
+    mha = oracle.decode_attention(q, k_exp, v_exp, lens, n_pending=1)
+    assert np.array_equal(gqa, mha)
+    wrong = oracle.decode_attention(q, k.repeat(1, hq // hkv, 1, 1), v.repeat(1, hq // hkv, 1, 1),
+                                    lens, n_pending=1)
+    assert np.abs(wrong - gqa).max() > 1e-3
+
+
+def test_gqa_with_groups_equal_heads_is_mha():
+    """W1D4 §2.3 (check group 6): G = h gives the MHA result, difference exactly 0."""
+    b, h, t, d = 1, 4, 9, 8
+    q = _rand((b, h, d), 2, "q")
+    k = _rand((b, h, t, d), 2, "k")
+    v = _rand((b, h, t, d), 2, "v")
+    lens = np.array([8])
+    out = oracle.decode_attention(q, k, v, lens)
+    for hh in range(h):  # each head alone, as a one-head MHA problem
+        one = oracle.decode_attention(q[:, hh:hh + 1], k[:, hh:hh + 1], v[:, hh:hh + 1], lens)
+        assert np.array_equal(out[:, hh], one[:, 0])
+
+
+# ------------------------------------------------- library routine (SDPA) --
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (8, 1), (6, 3)])
+def test_decode_attention_matches_torch_sdpa(hq, hkv):
+    """Library pin: single-query attention equals torch's
+    scaled_dot_product_attention (fp64, enable_gqa, which groups heads like
+    repeat_interleave per W1D4 §A.3), per sequence over its N_b tokens."""
+    b, t_max, d = 3, 40, 32
+    q = _rand((b, hq, d), 3, "q", hq, hkv).double()
+    k = _rand((b, hkv, t_max, d), 3, "k", hq, hkv).double()
+    v = _rand((b, hkv, t_max, d), 3, "v", hq, hkv).double()
+    lens = np.array([0, 17, 39])
+    got = oracle.decode_attention(q, k, v, lens, n_pending=1)
+    for i in range(b):
+        n = lens[i] + 1
+        ref = F.scaled_dot_product_attention(q[i:i + 1, :, None, :], k[i:i + 1, :, :n], v[i:i + 1, :, :n],
+                                             enable_gqa=True)[0, :, 0, :].numpy()
+        assert np.abs(got[i] - ref).max() < 1e-13
+
+
+def test_decode_attention_n_pending_zero_and_scale_argument():
+    """n_pending counts tokens past seq_lens; an explicit scale replaces 1/sqrt(D)."""
+    b, h, t, d = 1, 2, 12, 8
+    q = _rand((b, h, d), 4, "q").double()
+    k = _rand((b, h, t, d), 4, "k").double()
+    v = _rand((b, h, t, d), 4, "v").double()
+    got = oracle.decode_attention(q, k, v, np.array([7]), n_pending=0, scale=0.3)
+    ref = F.scaled_dot_product_attention(q[:, :, None], k[:, :, :7], v[:, :, :7], scale=0.3)[:, :, 0].numpy()
+    assert np.abs(got - ref).max() < 1e-13
+
+
+def test_causal_attention_matches_torch_sdpa():
+    """Path A's causal prefill (KVG prefill with triu(-inf, 1)) equals torch's
+    SDPA with is_causal=True for square T x T (both masks agree when T_q == T_k)."""
+    hq, hkv, t, d = 4, 2, 13, 4
+    q = _rand((hq, t, d), 5, "q").double()
+    k = _rand((hkv, t, d), 5, "k").double()
+    v = _rand((hkv, t, d), 5, "v").double()
+    got = oracle.causal_attention(q, k, v, hq, hkv)
+    ref = F.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True, enable_gqa=True)[0]
+    assert np.abs(got - ref.numpy()).max() < 1e-13
+
+
+def test_top_left_causal_mask_is_wrong_for_decode():
+    """W1D4 §3.3: SDPA is_causal=True aligns the triangle top-left, so a single
+    query sees only key 0. Decode needs no mask; the two must differ."""
+    hq, t, d = 2, 9, 8
+    q = _rand((1, hq, d), 6, "q").double()
+    k = _rand((1, hq, t, d), 6, "k").double()
+    v = _rand((1, hq, t, d), 6, "v").double()
+    good = oracle.decode_attention(q, k, v, np.array([t - 1]))
+    top_left = F.scaled_dot_product_attention(q[:, :, None], k, v, is_causal=True)[:, :, 0].numpy()
+    assert np.abs(top_left - v[:, :, 0].numpy()).max() < 1e-15   # sees only key 0
+    assert np.abs(good - top_left).max() > 1e-2
+
+
+# -------------------------------------------------------------- closed forms --
+
+def test_single_token_returns_its_value_exactly():
+    """N = 1: softmax of one score is 1, so o = V_0 bit for bit."""
+    q = _rand((2, 4, 8), 7, "q")
+    k = _rand((2, 2, 5, 8), 7, "k")
+    v = _rand((2, 2, 5, 8), 7, "v")
+    out = oracle.decode_attention(q, k, v, np.array([0, 0]), n_pending=1)
+    for h in range(4):
+        assert np.array_equal(out[:, h], oracle.widen(v)[:, h // 2, 0])
+
+
+def test_zero_query_gives_mean_of_values():
+    """q = 0: every score is 0, weights are uniform, o = mean_t V_t."""
+    v = _rand((1, 1, 10, 8), 8, "v").double()
+    k = _rand((1, 1, 10, 8), 8, "k").double()
+    out = oracle.decode_attention(torch.zeros(1, 1, 8, dtype=torch.float64), k, v, np.array([9]))
+    assert np.abs(out[0, 0] - v[0, 0].numpy().mean(axis=0)).max() < 1e-15
+
+
+def test_identical_keys_give_uniform_weights():
+    q = _rand((1, 3, 8), 9, "q").double()
+    k = _rand((1, 1, 1, 8), 9, "k").double().expand(1, 1, 6, 8).contiguous()
+    v = _rand((1, 1, 6, 8), 9, "v").double()
+    out = oracle.decode_attention(q, k, v, np.array([5]))
+    for h in range(3):
+        assert np.abs(out[0, h] - v[0, 0].numpy().mean(axis=0)).max() < 1e-15
+
+
+def test_scale_pins_weights_three_to_one():
+    """Closed form that fixes the 1/sqrt(D) scale and the softmax direction:
+    with D = 4 (scale 1/2) and q.k0 - q.k1 = 2 ln 3, the scores differ by ln 3,
+    so the weights are 3:1 and o = 0.75 v0 + 0.25 v1. Dropping the square root
+    would give 9:1; dividing by D, 1.73:1; softmax of -s, 1:3."""
+    d = 4
+    q = np.array([[[1.0, 0.0, 0.0, 0.0]]])
+    k = np.zeros((1, 1, 2, d))
+    k[0, 0, 0, 0] = 2.0 * math.log(3.0)
+    v = np.array([[[[1.0, 2.0, 3.0, 4.0], [5.0, -6.0, 7.0, -8.0]]]])
+    out = oracle.decode_attention(q, k, v, np.array([1]))
+    want = 0.75 * v[0, 0, 0] + 0.25 * v[0, 0, 1]
+    assert np.abs(out[0, 0] - want).max() < 1e-14
+
+
+def test_dominant_score_selects_its_value():
+    d = 8
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 5, d))
+    k[0, 0, 3, 0] = 200.0 * math.sqrt(d)  # score 200 against 0: weight 1 - 4e-87
+    v = oracle.widen(_rand((1, 1, 5, d), 10, "v"))
+    out = oracle.decode_attention(q, k, v, np.array([4]))
+    assert np.abs(out[0, 0] - v[0, 0, 3]).max() < 1e-15
+
+
+def test_permuting_cached_tokens_leaves_output_unchanged():
+    """No mask, no positions inside the op: a joint permutation of the (K_t, V_t)
+    rows changes only the summation order."""
+    q = _rand((1, 4, 16), 11, "q")
+    k = oracle.widen(_rand((1, 2, 20, 16), 11, "k"))
+    v = oracle.widen(_rand((1, 2, 20, 16), 11, "v"))
+    perm = np.random.default_rng(0).permutation(20)
+    a = oracle.decode_attention(q, k, v, np.array([19]))
+    b = oracle.decode_attention(q, k[:, :, perm], v[:, :, perm], np.array([19]))
+    assert np.abs(a - b).max() < 1e-15
+
+
+def test_weights_sum_to_one_via_constant_values():
+    """If every V row is the same vector c, o = c * sum(p) = c."""
+    q = _rand((1, 2, 8), 12, "q")
+    k = _rand((1, 1, 30, 8), 12, "k")
+    c = np.linspace(-1, 1, 8)
+    v = np.broadcast_to(c, (1, 1, 30, 8)).copy()
+    out = oracle.decode_attention(q, k, v, np.array([29]))
+    assert np.abs(out[0] - c).max() < 1e-15
+
+
+def test_empty_sequence_gives_zero_row():
+    q = _rand((2, 2, 8), 13, "q")
+    k = _rand((2, 2, 4, 8), 13, "k")
+    v = _rand((2, 2, 4, 8), 13, "v")
+    out = oracle.decode_attention(q, k, v, np.array([0, 3]), n_pending=0)
+    assert np.all(out[0] == 0.0) and np.all(np.isfinite(out[1]))
+
+
+def test_mpmath_brute_force_fifty_digits():
+    """Brute force at 50 significant digits on tiny inputs bounds the fp64
+    oracle's rounding error."""
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    hq, hkv, t, d = 4, 2, 7, 5
+    q = oracle.widen(_rand((1, hq, d), 14, "q"))
+    k = oracle.widen(_rand((1, hkv, t, d), 14, "k"))
+    v = oracle.widen(_rand((1, hkv, t, d), 14, "v"))
+    got = oracle.decode_attention(q, k, v, np.array([t - 1]))
+    for h in range(hq):
+        g = h // (hq // hkv)
+        s = [mpmath.fsum(mpmath.mpf(q[0, h, i]) * mpmath.mpf(k[0, g, j, i]) for i in range(d))
+             / mpmath.sqrt(d) for j in range(t)]
+        w = [mpmath.exp(x) for x in s]
+        z = mpmath.fsum(w)
+        for i in range(d):
+            o = mpmath.fsum(w[j] * mpmath.mpf(v[0, g, j, i]) for j in range(t)) / z
+            assert abs(float(o) - got[0, h, i]) < 1e-14
+
+
+# ------------------------------------------------------------ append model --
+
+def test_append_writes_one_slot_bitwise_and_nothing_else():
+    """W1D4 §3.1 update with T = 1, per-sequence positions; KVG: the append is an
+    in-place slot write. bf16 is modelled on its 16-bit patterns."""
+    b, h, t_max, d = 3, 2, 6, 8
+    kc = synth.normal((b, h, t_max, d), "bf16", 15, "kc").view(torch.int16).numpy()
+    vc = synth.normal((b, h, t_max, d), "bf16", 15, "vc").view(torch.int16).numpy()
+    kn = synth.normal((b, h, d), "bf16", 15, "kn").view(torch.int16).numpy()
+    vn = synth.normal((b, h, d), "bf16", 15, "vn").view(torch.int16).numpy()
+    lens = np.array([0, 5, 6])        # last one is full: overflow
+    k2, v2, ovf = oracle.append(kc, vc, lens, kn, vn)
+    assert list(ovf) == [False, False, True]
+    for i, pos in enumerate(lens):
+        for s in range(t_max):
+            if s == pos and not ovf[i]:
+                assert np.array_equal(k2[i, :, s], kn[i]) and np.array_equal(v2[i, :, s], vn[i])
+            else:
+                assert np.array_equal(k2[i, :, s], kc[i, :, s]) and np.array_equal(v2[i, :, s], vc[i, :, s])
+
+
+def test_prefill_fill_chunked_equals_one_shot():
+    """W1D4 §3.5 test 1 includes prefill in chunks: two fills at offsets 0 and 5
+    give the same cache as one fill of 9 tokens; a fill past T_max is refused."""
+    b, h, t_max, d = 2, 2, 12, 4
+    k = oracle.widen(_rand((b, h, 9, d), 16, "k"))
+    v = oracle.widen(_rand((b, h, 9, d), 16, "v"))
+    empty = np.full((b, h, t_max, d), -7.0)
+    k1, v1, _ = oracle.prefill_fill(empty, empty, np.zeros(b, int), k, v)
+    ka, va, _ = oracle.prefill_fill(empty, empty, np.zeros(b, int), k[:, :, :5], v[:, :, :5])
+    kb, vb, _ = oracle.prefill_fill(ka, va, np.full(b, 5), k[:, :, 5:], v[:, :, 5:])
+    assert np.array_equal(k1, kb) and np.array_equal(v1, vb)
+    _, _, ovf = oracle.prefill_fill(empty, empty, np.array([3, 4]), k, v)
+    assert list(ovf) == [False, True]
+
+
+def test_past_kv_rows_do_not_change_when_prefix_grows():
+    """W1D4 §1.2 (check group 1): K/V of the first 12 positions are identical,
+    difference exactly 0, whether the prefix has 12 or 13 tokens."""
+    cfg = synth.CONFIGS["toy_gqa"]
+    x = _rand((13, cfg.hidden), 17, "x")
+    wk = _rand((cfg.hidden, cfg.n_kv_heads * cfg.head_dim), 17, "wk")
+    k12 = oracle.project(x[:12], wk, cfg.n_kv_heads, cfg.head_dim)
+    k13 = oracle.project(x[:13], wk, cfg.n_kv_heads, cfg.head_dim)
+    assert np.array_equal(k12, k13[:, :12])
+
+
+def test_project_head_h_owns_its_column_block():
+    """KVG project: view(tokens, heads, D).transpose -> head h is columns [hD, (h+1)D)."""
+    x = oracle.widen(_rand((5, 16), 18, "x"))
+    w = oracle.widen(_rand((16, 12), 18, "w"))
+    p = oracle.project(x, w, 3, 4)
+    for h in range(3):
+        assert np.abs(p[h] - x @ w[:, 4 * h: 4 * h + 4]).max() < 1e-15
+
+
+# ----------------------------------------------------- path A == path B --
+
+def _toy_inputs(cfg, seed=7, n_q=None, n_kv=None, prompt=None, decode=None):
+    n_q = n_q or cfg.n_q_heads
+    n_kv = n_kv or cfg.n_kv_heads
+    t = (prompt or cfg.prompt) + (decode or cfg.decode)
+    std = 1.0 / math.sqrt(cfg.hidden)
+    wq = synth.normal((cfg.hidden, n_q * cfg.head_dim), "fp32", seed, "toy", "wq", std=std)
+    wk = synth.normal((cfg.hidden, n_kv * cfg.head_dim), "fp32", seed, "toy", "wk", std=std)
+    wv = synth.normal((cfg.hidden, n_kv * cfg.head_dim), "fp32", seed, "toy", "wv", std=std)
+    wo = synth.normal((n_q * cfg.head_dim, cfg.hidden), "fp32", seed, "toy", "wo", std=std)
+    x = synth.normal((t, cfg.hidden), "fp32", seed, "toy", "x")
+    return x, wq, wk, wv, wo
+
+
+def test_toy_full_recompute_equals_incremental_decode():
+    """KVG runnable experiment, toy shape: B=1, hidden 16, H_q=4, H_kv=2, D=4,
+    prompt 8 + 5 decode steps. Path A (full-prefix recompute) and path B
+    (prefill + append + one-query attention) agree per step; the final cache is
+    [1, 2, 13, 4] and its rows are the projected K/V rows."""
+    cfg = synth.CONFIGS["toy_gqa"]
+    x, wq, wk, wv, wo = _toy_inputs(cfg)
+    out_a, ctx_a = oracle.toy_path_a(x, wq, wk, wv, wo, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.prompt)
+    out_b, ctx_b, kc, vc = oracle.toy_path_b(x, wq, wk, wv, wo, cfg.n_q_heads, cfg.n_kv_heads,
+                                             cfg.head_dim, cfg.prompt)
+    assert out_a.shape == (cfg.decode, cfg.hidden)
+    assert np.abs(out_a - out_b).max() < 1e-13
+    assert np.abs(ctx_a - ctx_b).max() < 1e-13
+    assert kc.shape == (1, 2, 13, 4) and vc.shape == (1, 2, 13, 4)
+    assert np.array_equal(kc[0], oracle.project(x, wk, cfg.n_kv_heads, cfg.head_dim))
+    assert np.array_equal(vc[0], oracle.project(x, wv, cfg.n_kv_heads, cfg.head_dim))
+
+
+@pytest.mark.parametrize("n_kv", [8, 2, 1], ids=["MHA", "GQA", "MQA"])
+def test_prefill_plus_decode_equals_full_forward(n_kv):
+    """W1D4 §1.3 (check group 2): prefill 8 then decode 12 equals one forward
+    over 20 tokens up to fp64 rounding (the page reports 3.6e-15 / 6.2e-15 /
+    5.8e-15 for MHA / GQA / MQA)."""
+    cfg = synth.CONFIGS["toy_gqa"]
+    x, wq, wk, wv, wo = _toy_inputs(cfg, seed=20 + n_kv, n_q=8, n_kv=n_kv, prompt=8, decode=12)
+    out_a, _ = oracle.toy_path_a(x, wq, wk, wv, wo, 8, n_kv, cfg.head_dim, 8)
+    out_b, _, _, _ = oracle.toy_path_b(x, wq, wk, wv, wo, 8, n_kv, cfg.head_dim, 8)
+    assert np.abs(out_a - out_b).max() < 5e-14

@@ -1,0 +1,93 @@
+"""Plant plausible mistakes in the oracle (on the CPU, never on the GPU path) and
+check that the pins in test_oracle.py catch each one."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import kvc_oracle as ko
+import tests.test_oracle as pins
+
+
+def _mutant_decode(kind):
+    def decode(q, k_cache, v_cache, seq_lens, n_pending=1, scale=None):
+        q, k, v = ko.widen(q), ko.widen(k_cache), ko.widen(v_cache)
+        batch, n_q, d = q.shape
+        n_kv = k.shape[1]
+        if scale is None:
+            scale = 1.0 / d if kind == "scale_by_d" else 1.0 / math.sqrt(d)
+        out = np.zeros((batch, n_q, d))
+        for b in range(batch):
+            n = int(seq_lens[b]) + (0 if kind == "drop_pending" else int(n_pending))
+            if n <= 0:
+                continue
+            for h in range(n_q):
+                g = h % n_kv if kind == "mod_grouping" else h // (n_q // n_kv)
+                s = (k[b, g, :n] @ q[b, h]) * scale
+                if kind == "negated_scores":
+                    s = -s
+                e = np.exp(s - s.max())
+                out[b, h] = (e @ v[b, g, :n]) / e.sum()
+        return out
+    return decode
+
+
+DECODE_PINS = [
+    pins.test_scale_pins_weights_three_to_one,
+    pins.test_gqa_equals_mha_on_repeat_interleaved_cache,
+    lambda: pins.test_decode_attention_matches_torch_sdpa(8, 2),
+    pins.test_toy_full_recompute_equals_incremental_decode,
+]
+
+
+@pytest.mark.parametrize("kind", ["scale_by_d", "mod_grouping", "drop_pending", "negated_scores"])
+def test_decode_mutants_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "decode_attention", _mutant_decode(kind))
+    monkeypatch.setattr(ko, "decode_attention", _mutant_decode(kind))
+    caught = 0
+    for pin in DECODE_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"no pin caught mutant {kind}"
+
+
+def test_causal_mask_off_by_one_is_caught(monkeypatch):
+    def causal(q, k, v, n_q_heads, n_kv_heads, scale=None):
+        q, k, v = ko.widen(q), ko.widen(k), ko.widen(v)
+        _, t, d = q.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        out = np.zeros_like(q)
+        mask = np.triu(np.full((t, t), -np.inf), 0)       # hides the diagonal too
+        mask[0, 0] = 0.0
+        for h in range(n_q_heads):
+            g = h // (n_q_heads // n_kv_heads)
+            s = (q[h] @ k[g].T) * scale + mask
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            out[h] = (e / e.sum(axis=1, keepdims=True)) @ v[g]
+        return out
+    monkeypatch.setattr(oracle, "causal_attention", causal)
+    monkeypatch.setattr(ko, "causal_attention", causal)
+    with pytest.raises(AssertionError):
+        pins.test_causal_attention_matches_torch_sdpa()
+
+
+def test_cache_bytes_without_k_and_v_factor_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "cache_bytes",
+                        lambda L, h, d, s, lens: L * h * d * s * sum(int(t) for t in lens))
+    row = pins._rows("capacity_values.csv")[0]
+    with pytest.raises(AssertionError):
+        pins.test_cache_bytes_matches_printed_values(row)
+
+
+def test_append_to_wrong_slot_is_caught(monkeypatch):
+    real = ko.append
+
+    def off_by_one(k_cache, v_cache, seq_lens, k_new, v_new):
+        return real(k_cache, v_cache, np.asarray(seq_lens) + 1, k_new, v_new)
+    monkeypatch.setattr(oracle, "append", off_by_one)
+    with pytest.raises(AssertionError):
+        pins.test_append_writes_one_slot_bitwise_and_nothing_else()
