@@ -1,0 +1,317 @@
+"""Decode-step benchmark: achieved HBM GB/s of KV-cache decode attention.
+
+One step is the whole per-layer incremental-decode path over all L layers of
+one batch: for every layer kvc_append (the new token's k, v into slot T_b) and
+kvc_decode_attn (every query head attends T_b + 1 tokens), then one
+kvc_seq_lens_advance. The value is KV bytes read per step, 2*L*H_kv*D*s*
+sum_b(T_b + 1), divided by the step time, with every input already resident in
+HBM. seq_lens is reset to the workload's lengths before the timed steps, so
+step k attends T_b + k + 1 tokens; the byte count follows that exactly.
+
+Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention achieved HBM GB/s (KV bytes read/step time) and % of peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+DOMINANT_KERNEL = "decode_split_kernel"
+KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_append_amd", "csrc", "kvc_kernels.hip")
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gqa_8b")
+    ap.add_argument("--secondary", default="ragged_long",
+                    help="second workload measured in the same run ('none' to skip)")
+    ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = library choice)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-clock budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=7)
+    return ap.parse_args()
+
+
+class Workload:
+    """All L layers of one decode step, resident in HBM, with pre-marshalled
+    C-ABI arguments (so the timed loop does no Python-side tensor work)."""
+
+    def __init__(self, cfg, margin_tokens: int, seed: int, splits: int):
+        import torch
+        import kv_cache_append_amd as kvc
+        import synth
+
+        self.cfg = cfg
+        self.kvc = kvc
+        self.lib = kvc.load()
+        dev = torch.device("cuda:0")
+        self.lengths = cfg.lengths(seed)
+        self.t_max = int(self.lengths.max()) + margin_tokens + 1
+        L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+        tdt = synth.DTYPES[cfg.dtype]
+        self.k = torch.empty((L, B, Hkv, self.t_max, D), dtype=tdt, device=dev)
+        self.v = torch.empty_like(self.k)
+        for l in range(L):  # fill layer by layer (bounded fp32 temporaries)
+            synth.normal(None, cfg.dtype, seed, cfg.name, l, "K", out=self.k[l])
+            synth.normal(None, cfg.dtype, seed, cfg.name, l, "V", out=self.v[l])
+        self.q = torch.stack([synth.normal((B, Hq, D), cfg.dtype, seed, cfg.name, l, "q", device=dev)
+                              for l in range(L)])
+        self.k_new = torch.stack([synth.normal((B, Hkv, D), cfg.dtype, seed, cfg.name, l, "k_new", device=dev)
+                                  for l in range(L)])
+        self.v_new = torch.stack([synth.normal((B, Hkv, D), cfg.dtype, seed, cfg.name, l, "v_new", device=dev)
+                                  for l in range(L)])
+        self.out = torch.empty((L, B, Hq, D), dtype=torch.float32, device=dev)
+        self.seq_lens = self.lengths.to(dev)
+        self.descs = [kvc.cache_desc(self.k[l], self.v[l]) for l in range(L)]
+        self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq)
+        self.ws = torch.empty(kvc.decode_workspace_bytes(self.k[0], self.v[0], Hq, self.splits),
+                              dtype=torch.uint8, device=dev)
+        self.scale = ctypes.c_float(1.0 / math.sqrt(D))
+        torch.cuda.synchronize()
+
+    def reset_lengths(self):
+        self.seq_lens.copy_(self.lengths.to(self.seq_lens.device))
+
+    def step(self, stream_handle, events=None):
+        """Enqueue one decode step (all layers) on the given HIP stream."""
+        lib, cfg = self.lib, self.cfg
+        vp = ctypes.c_void_p
+        seq = vp(self.seq_lens.data_ptr())
+        ws, wsb = vp(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel())
+        sb, sh = self.k_new.stride(1), self.k_new.stride(2)
+        st = vp(stream_handle)
+        for l in range(cfg.n_layers):
+            d = ctypes.byref(self.descs[l])
+            rc = lib.kvc_append(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
+                                None, st)
+            if events is not None:
+                events[l][0].record()
+            rc |= lib.kvc_decode_attn(d, seq, 1, vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
+                                      vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
+            if events is not None:
+                events[l][1].record()
+            if rc:
+                raise RuntimeError(f"libkvc returned {rc} at layer {l}")
+        if lib.kvc_seq_lens_advance(seq, cfg.batch, 1, st):
+            raise RuntimeError("kvc_seq_lens_advance failed")
+
+    def kv_bytes(self, steps: int) -> int:
+        """KV bytes read by `steps` steps starting from the reset lengths."""
+        per_token = 2 * self.cfg.n_layers * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
+        base = int(self.lengths.to("cpu").long().sum())
+        b = self.cfg.batch
+        return per_token * sum(base + b * (k + 1) for k in range(steps))
+
+    def decode_launch_bytes(self, step_index: int) -> int:
+        """Algorithmic K+V bytes one decode launch (one layer) reads at a step."""
+        per_token = 2 * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
+        return per_token * (int(self.lengths.long().sum()) + self.cfg.batch * (step_index + 1))
+
+
+def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(max(warmup, 1)):
+        w.step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        w.reset_lengths()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            w.step(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(max(warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
+    # timed region: exactly `steps` steps from the reset lengths
+    w.reset_lengths()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            w.step(stream.cuda_stream)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    # per-launch duration of the decode call (HIP events on the same stream),
+    # a separate eager pass so the events do not perturb the timed steps
+    w.reset_lengths()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(w.cfg.n_layers)]
+    durs = []
+    n_pass = max(2, min(steps, 5))
+    launch_bytes = 0
+    for k in range(n_pass):
+        w.step(stream.cuda_stream, events=ev)
+        torch.cuda.synchronize()
+        durs.extend(a.elapsed_time(b) for a, b in ev)
+        launch_bytes += w.decode_launch_bytes(k) * w.cfg.n_layers
+    avg_launch_ms = sum(durs) / len(durs)
+    avg_launch_bytes = launch_bytes / len(durs)
+    return ms_total, wall, avg_launch_ms, avg_launch_bytes
+
+
+def _traffic(workload_name: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(cfg, seconds: float, seed: int):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    whole layers of (sequence, KV head) units at the workload's shapes, timed
+    until about `seconds` of wall clock. Reports KV GB/s of the oracle."""
+    import numpy as np
+    import torch
+    import synth
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    lengths = cfg.lengths(seed)
+    g = cfg.group
+    done_bytes, units, t_spent = 0, 0, 0.0
+    b = 0
+    while t_spent < seconds and units < cfg.batch * cfg.n_kv_heads * cfg.n_layers:
+        n = int(lengths[b % cfg.batch]) + 1
+        kv = cfg.n_kv_heads
+        q = synth.normal((1, cfg.n_q_heads, cfg.head_dim), cfg.dtype, seed, "cpu", b, "q")
+        k = synth.normal((1, kv, n, cfg.head_dim), cfg.dtype, seed, "cpu", b, "K")
+        v = synth.normal((1, kv, n, cfg.head_dim), cfg.dtype, seed, "cpu", b, "V")
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, k, v, np.array([n - 1]), n_pending=1)
+        t_spent += time.perf_counter() - t0
+        done_bytes += 2 * kv * n * cfg.head_dim * cfg.elem_bytes
+        units += kv
+        b += 1
+        del q, k, v
+    return {
+        "value": round(done_bytes / t_spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{b} sequences x all {cfg.n_kv_heads} KV heads of one {cfg.name} layer "
+                  f"({units} (sequence, KV head) units, {cfg.group} query heads each, "
+                  f"{done_bytes / 1e9:.3f} GB of K+V) in {t_spent:.1f} s; numpy fp64, BLAS threads={threads}",
+    }
+
+
+def _run_config(name, args, with_cpu):
+    import torch
+    import synth
+    cfg = synth.CONFIGS[name]
+    margin = max(args.steps, args.warmup) + 2
+    w = Workload(cfg, margin, args.seed, args.splits)
+    ms_total, wall, launch_ms, launch_bytes = _measure(w, args.steps, args.warmup, not args.no_graph)
+    kv = w.kv_bytes(args.steps)
+    gbs = kv / (ms_total / 1e3) / 1e9
+    achieved = launch_bytes / (launch_ms / 1e3) / 1e9
+    lens = w.lengths
+    res = {
+        "value": round(gbs, 2),
+        "ms_per_step": round(ms_total / args.steps, 5),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "steps_per_s": round(args.steps / (ms_total / 1e3), 2),
+        "tokens_per_s": round(cfg.batch * args.steps / (ms_total / 1e3), 1),
+        "kv_bytes_per_step": kv // args.steps,
+        "dtype": cfg.dtype,
+        "config": {
+            "workload": name, "description": cfg.description, "layers": cfg.n_layers, "batch": cfg.batch,
+            "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+            "cached_tokens_at_start": {"min": int(lens.min()), "max": int(lens.max()),
+                                       "sum": int(lens.long().sum())},
+            "splits": w.splits, "hip_graph": not args.no_graph,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "kvc_decode_attn (split + merge kernels)",
+            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),
+            "traffic": _traffic(name),
+        },
+    }
+    if with_cpu:
+        res["cpu_baseline"] = _cpu_baseline(cfg, args.cpu_seconds, args.seed)
+    del w
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    main_res = _run_config(args.config, args, with_cpu=not args.no_cpu_baseline)
+    line = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res["dtype"],
+        "data": "synthetic (seeded N(0,1) q/K/V rounded to the cache dtype; no dataset)",
+        "config": main_res["config"],
+        "pct_of_peak": main_res["pct_of_peak"],
+        "steps_per_s": main_res["steps_per_s"],
+        "tokens_per_s": main_res["tokens_per_s"],
+        "wall_ms_per_step": main_res["wall_ms_per_step"],
+        "kv_bytes_per_step": main_res["kv_bytes_per_step"],
+        "roofline": main_res["roofline"],
+    }
+    if "cpu_baseline" in main_res:
+        line["cpu_baseline"] = main_res["cpu_baseline"]
+    if args.secondary and args.secondary != "none":
+        sec = _run_config(args.secondary, args, with_cpu=False)
+        line["secondary"] = {k: sec[k] for k in ("value", "ms_per_step", "pct_of_peak", "steps_per_s",
+                                                   "tokens_per_s", "kv_bytes_per_step", "dtype", "config",
+                                                   "roofline")}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * kvc.h -- KV-cache append and single-query decode attention for AMD Instinct
+ * MI355X (CDNA4, gfx950). C ABI of libkvc.so.
+ *
+ * One decode step of one attention layer, as three web pages on the KV cache
+ * describe it:
+ *   - glossary entry "KV 缓存" (llm-glossary.tokens-kit.com), sections
+ *     "placing it back in the inference chain", "two mathematically equivalent
+ *     decode paths" (path B) and "capacity formula";
+ *   - course notes "第 1 周 · Day 4：KV Cache 与 MQA / GQA" (semidirectx.com),
+ *     §1.3 (prefill and decode), §1.4 (memory formula), §2.3 and §3.4 (GQA
+ *     grouping), §3.1 (preallocated cache and its update);
+ *   - textbook section "11.7 KV Cache：形状、显存与带宽" (yongzhen.wang),
+ *     §2.2 (single-step decode) and §2.3 (memory formula).
+ *
+ * Conventions shared by every call:
+ *   - Pointers named h_* are host pointers; every other data pointer is a
+ *     device pointer (HBM) on the current HIP device.
+ *   - The caller owns every buffer (caches, q, out, workspace, seq_lens,
+ *     status word). The library never allocates or frees device memory, never
+ *     synchronises the stream, and keeps no mutable global state; calls on
+ *     different streams are independent.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and returns
+ *     before it runs. Results are visible after the stream is synchronised.
+ *   - Strides are in elements. The head-dimension axis (D) is contiguous.
+ *   - Host-detectable errors return a status before anything is enqueued and
+ *     with no side effects. Conditions that depend on device data (a full
+ *     cache, a negative length) are handled on the device: the sequence is
+ *     skipped and a bit is OR-ed into the optional device status word.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of cache elements (and of q and k_new/v_new). */
+typedef enum kvc_dtype {
+  KVC_F32 = 0,
+  KVC_F16 = 1,   /* IEEE binary16 */
+  KVC_BF16 = 2   /* bfloat16 */
+} kvc_dtype_t;
+
+typedef enum kvc_status {
+  KVC_OK = 0,
+  KVC_ERR_NULL = 1,        /* a required pointer is NULL */
+  KVC_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or strides overlap rows */
+  KVC_ERR_DTYPE = 3,       /* unknown dtype code */
+  KVC_ERR_ALIGN = 4,       /* a pointer or stride breaks the alignment the kernels need */
+  KVC_ERR_GQA = 5,         /* n_q_heads is not a positive multiple of n_kv_heads */
+  KVC_ERR_WORKSPACE = 6,   /* workspace missing or smaller than kvc_decode_workspace_bytes() */
+  KVC_ERR_UNSUPPORTED = 7, /* head_dim / dtype / group size the decode kernels are not built for */
+  KVC_ERR_HIP = 8          /* the HIP runtime reported an error at launch */
+} kvc_status_t;
+
+/* Bits OR-ed into the optional device status word (uint32_t). */
+#define KVC_DEVERR_CAPACITY 1u  /* a write or read would pass max_len: that sequence was skipped/clamped */
+#define KVC_DEVERR_BADLEN   2u  /* seq_lens[b] < 0: that sequence was skipped / treated as empty */
+
+/*
+ * One layer's preallocated cache: K and V each [batch, n_kv_heads, max_len,
+ * head_dim] with the given element strides (course notes §3.1: allocate once
+ * to the maximum length; glossary "two equivalent decode paths": the new slot
+ * is written in place). K and V share shape, strides and dtype.
+ */
+typedef struct kvc_cache {
+  void* k;
+  void* v;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t max_len;
+  int32_t head_dim;
+  int32_t dtype;       /* kvc_dtype_t */
+  int32_t reserved0;   /* must be 0 */
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_t;
+} kvc_cache_t;
+
+/*
+ * kvc_append -- write the new token's k_t, v_t into slot seq_lens[b] of every
+ * sequence (course notes §3.1 update with one token; glossary path B; textbook
+ * §2.2 "append k_t, v_t to the cache").
+ *
+ *   cache     the layer's cache (device buffers).
+ *   seq_lens  int32[batch], device: tokens already cached per sequence. READ
+ *             ONLY: one array serves all layers of a step; advance it once per
+ *             step with kvc_seq_lens_advance.
+ *   k_new,
+ *   v_new     [batch, n_kv_heads, head_dim] in the cache dtype, element
+ *             strides new_stride_b, new_stride_h (D contiguous).
+ *   dev_status optional uint32 device word; KVC_DEVERR_* bits are OR-ed in.
+ *
+ * The copy is bit-exact. If seq_lens[b] >= max_len (or < 0) nothing is written
+ * for sequence b and the status bit is set. Every other slot is untouched.
+ * batch == 0 is a no-op.
+ */
+kvc_status_t kvc_append(const kvc_cache_t* cache, const int32_t* seq_lens,
+                        const void* k_new, const void* v_new,
+                        int64_t new_stride_b, int64_t new_stride_h,
+                        uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * kvc_prefill_fill -- write t_new tokens per sequence at slots
+ * [seq_lens[b], seq_lens[b] + t_new) (course notes §3.1 update with T tokens;
+ * §1.3 prefill writes every position's K/V; §3.5 chunked prefill when
+ * seq_lens[b] > 0).
+ *
+ *   k, v      [batch, n_kv_heads, t_new, head_dim] in the cache dtype with
+ *             element strides src_stride_b, src_stride_h, src_stride_t.
+ *   t_new     tokens per sequence (0 is a no-op).
+ *
+ * seq_lens is read only. A sequence whose range does not fit in [0, max_len)
+ * is not written and KVC_DEVERR_CAPACITY is set. The copy is bit-exact.
+ */
+kvc_status_t kvc_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens,
+                              const void* k, const void* v,
+                              int64_t src_stride_b, int64_t src_stride_h, int64_t src_stride_t,
+                              int32_t t_new, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * kvc_decode_workspace_bytes -- bytes of device workspace kvc_decode_attn
+ * needs for this cache, query-head count and split count (n_splits = 0 means
+ * the library's choice, the same one kvc_decode_attn makes). The bound holds
+ * for any seq_lens <= max_len. Returns 0 for invalid arguments.
+ */
+size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t n_splits);
+
+/*
+ * kvc_decode_splits -- the number of sequence splits kvc_decode_attn uses for
+ * this cache when n_splits == 0 (0 for invalid arguments).
+ */
+int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads);
+
+/*
+ * kvc_decode_attn -- the single new query of every head attends all cached
+ * tokens: out[b,h,:] = softmax(scale * q[b,h,:] . K[b,g,t,:]) V[b,g,t,:] over
+ * t < N_b = seq_lens[b] + n_pending, with g = h / (n_q_heads / n_kv_heads)
+ * (textbook §2.2 single-step decode; glossary decode path; course notes §3.4
+ * grouping floor(j/(h/G))). No mask: every cached token precedes the query
+ * (course notes §3.3). After kvc_append of the step's token, n_pending = 1
+ * attends the t+1 keys of course notes §1.3.
+ *
+ *   q         [batch, n_q_heads, head_dim], contiguous, cache dtype.
+ *   scale     softmax scale, normally 1/sqrt(head_dim).
+ *   out       [batch, n_q_heads, head_dim], contiguous, dtype out_dtype
+ *             (KVC_F32, or the cache dtype rounded to nearest even).
+ *   workspace device buffer of at least kvc_decode_workspace_bytes(cache,
+ *             n_q_heads, n_splits) bytes, 16-byte aligned; its contents on
+ *             entry do not matter. Not used concurrently by another call.
+ *   n_splits  sequence splits per (sequence, KV head); 0 = library choice.
+ *             The result does not depend on it beyond fp32 rounding order.
+ *
+ * Sequences with N_b == 0 produce a zero row. N_b is clamped to max_len (with
+ * KVC_DEVERR_CAPACITY set) so the kernels never read past the cache.
+ * Accumulation is fp32; results are run-to-run deterministic.
+ * Supported: head_dim in {64, 128, 256} for every dtype, plus head_dim 4..32
+ * (powers of two with head_dim * elem_bytes >= 16); any group size.
+ */
+kvc_status_t kvc_decode_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                             const void* q, int32_t n_q_heads, float scale,
+                             void* out, int32_t out_dtype,
+                             void* workspace, size_t workspace_bytes, int32_t n_splits,
+                             uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * kvc_seq_lens_advance -- seq_lens[b] += n for every b, on the device, once per
+ * step after all layers appended (course notes §3.1: pos += T).
+ */
+kvc_status_t kvc_seq_lens_advance(int32_t* seq_lens, int32_t batch, int32_t n, hipStream_t stream);
+
+/*
+ * kvc_cache_bytes -- logical K+V payload 2 * n_layers * n_kv_heads * head_dim *
+ * elem_bytes * sum_b h_lens[b] (glossary "capacity formula", ragged form;
+ * course notes §1.4; textbook §2.3). Host only. Returns 0 on invalid input.
+ */
+uint64_t kvc_cache_bytes(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                         const int32_t* h_lens, int32_t batch);
+
+/* kvc_status_str -- static, human-readable name of a status code. */
+const char* kvc_status_str(kvc_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

@@ -1,0 +1,173 @@
+"""Python binding of libkvc (KV-cache append + single-query decode attention on
+MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libkvc.so,
+reached through its C ABI (include/kvc.h) with ctypes. PyTorch supplies device
+memory and the current HIP stream. There is no fallback: if the library is not
+built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvc.so")
+
+KVC_F32, KVC_F16, KVC_BF16 = 0, 1, 2
+DTYPE_CODE = {torch.float32: KVC_F32, torch.float16: KVC_F16, torch.bfloat16: KVC_BF16}
+DEVERR_CAPACITY = 1
+DEVERR_BADLEN = 2
+
+STATUS = {
+    0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_ALIGN",
+    5: "KVC_ERR_GQA", 6: "KVC_ERR_WORKSPACE", 7: "KVC_ERR_UNSUPPORTED", 8: "KVC_ERR_HIP",
+}
+
+# Every symbol include/kvc.h declares.
+EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
+           "kvc_decode_attn", "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
+
+
+class KvcError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)}")
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of kvc_cache_t."""
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("max_len", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libkvc.so (built in-tree by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+    cp = ctypes.POINTER(CacheDesc)
+    lib.kvc_append.argtypes = [cp, vp, vp, vp, i64, i64, vp, vp]
+    lib.kvc_append.restype = i32
+    lib.kvc_prefill_fill.argtypes = [cp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+    lib.kvc_prefill_fill.restype = i32
+    lib.kvc_decode_workspace_bytes.argtypes = [cp, i32, i32]
+    lib.kvc_decode_workspace_bytes.restype = sz
+    lib.kvc_decode_splits.argtypes = [cp, i32]
+    lib.kvc_decode_splits.restype = i32
+    lib.kvc_decode_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_decode_attn.restype = i32
+    lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
+    lib.kvc_seq_lens_advance.restype = i32
+    lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
+    lib.kvc_cache_bytes.restype = ctypes.c_uint64
+    lib.kvc_status_str.argtypes = [i32]
+    lib.kvc_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise KvcError(code, where)
+
+
+def cache_desc(k: torch.Tensor, v: torch.Tensor) -> CacheDesc:
+    """kvc_cache_t for one layer's K and V tensors [B, H_kv, T_max, D] (any
+    strides with D contiguous; K and V must share shape, strides and dtype)."""
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype or k.dim() != 4:
+        raise ValueError("K and V must be 4-D with equal shape, strides and dtype")
+    if k.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported cache dtype {k.dtype}")
+    if k.shape[3] > 1 and k.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    b, h, t, d = k.shape
+    sb, sh, st, _ = k.stride()
+    return CacheDesc(k.data_ptr(), v.data_ptr(), b, h, t, d, DTYPE_CODE[k.dtype], 0, sb, sh, st)
+
+
+def append(k_cache, v_cache, seq_lens, k_new, v_new, status=None, stream=None, desc=None):
+    """kvc_append: write k_new/v_new [B, H_kv, D] at slot seq_lens[b]."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(lib.kvc_append(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new),
+                          k_new.stride(0), k_new.stride(1), _ptr(status), _stream(stream)), "kvc_append")
+
+
+def prefill_fill(k_cache, v_cache, seq_lens, k, v, status=None, stream=None):
+    """kvc_prefill_fill: write k/v [B, H_kv, T_new, D] at slots [seq_lens[b], +T_new)."""
+    lib = load()
+    c = cache_desc(k_cache, v_cache)
+    if k.stride() != v.stride() or k.dim() != 4:
+        raise ValueError("k and v must be [B, H_kv, T_new, D] with equal strides")
+    _check(lib.kvc_prefill_fill(ctypes.byref(c), _ptr(seq_lens), _ptr(k), _ptr(v),
+                                k.stride(0), k.stride(1), k.stride(2), k.shape[2],
+                                _ptr(status), _stream(stream)), "kvc_prefill_fill")
+
+
+def decode_workspace_bytes(k_cache, v_cache, n_q_heads: int, n_splits: int = 0) -> int:
+    c = cache_desc(k_cache, v_cache)
+    return int(load().kvc_decode_workspace_bytes(ctypes.byref(c), n_q_heads, n_splits))
+
+
+def decode_splits(k_cache, v_cache, n_q_heads: int) -> int:
+    c = cache_desc(k_cache, v_cache)
+    return int(load().kvc_decode_splits(ctypes.byref(c), n_q_heads))
+
+
+def decode_attn(k_cache, v_cache, seq_lens, q, out, workspace, n_pending: int = 1, scale=None,
+                n_splits: int = 0, status=None, stream=None, desc=None):
+    """kvc_decode_attn: out[b,h] = softmax(scale q.K^T) V over seq_lens[b]+n_pending tokens."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    out_code = DTYPE_CODE[out.dtype]
+    _check(lib.kvc_decode_attn(ctypes.byref(c), _ptr(seq_lens), n_pending, _ptr(q), q.shape[1],
+                               float(scale), _ptr(out), out_code, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), n_splits,
+                               _ptr(status), _stream(stream)), "kvc_decode_attn")
+
+
+def seq_lens_advance(seq_lens, n: int = 1, stream=None):
+    _check(load().kvc_seq_lens_advance(_ptr(seq_lens), seq_lens.numel(), n, _stream(stream)),
+           "kvc_seq_lens_advance")
+
+
+def cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, dtype: torch.dtype, lengths) -> int:
+    lens = [int(x) for x in lengths]
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    return int(load().kvc_cache_bytes(n_layers, n_kv_heads, head_dim, DTYPE_CODE[dtype], arr, len(lens)))
+
+
+def status_str(code: int) -> str:
+    return load().kvc_status_str(code).decode()

@@ -1,0 +1,155 @@
+// Host-side validation, split heuristic, workspace sizing and the pure-host
+// C-ABI calls (kvc_cache_bytes, kvc_status_str). No device code.
+#include <stdint.h>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case KVC_F32: return 4;
+    case KVC_F16: return 2;
+    case KVC_BF16: return 2;
+    default: return 0;
+  }
+}
+
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kvc_status_t check_cache(const kvc_cache_t* c, bool need_vec16) {
+  if (c == nullptr) return KVC_ERR_NULL;
+  const int s = elem_bytes(c->dtype);
+  if (s == 0) return KVC_ERR_DTYPE;
+  if (c->batch < 0 || c->n_kv_heads <= 0 || c->max_len < 0 || c->head_dim <= 0 || c->reserved0 != 0)
+    return KVC_ERR_SHAPE;
+  if (c->batch == 0) return KVC_OK;  // nothing will be touched
+  if (c->k == nullptr || c->v == nullptr) return KVC_ERR_NULL;
+  // Rows of one (b, h) must not overlap, and the D axis is contiguous.
+  if (c->stride_t < c->head_dim) return KVC_ERR_SHAPE;
+  if (c->n_kv_heads > 1 && c->stride_h < c->head_dim) return KVC_ERR_SHAPE;
+  if (c->batch > 1 && c->stride_b < c->head_dim) return KVC_ERR_SHAPE;
+  if (c->stride_b < 0 || c->stride_h < 0) return KVC_ERR_SHAPE;
+  if (!aligned(c->k, s) || !aligned(c->v, s)) return KVC_ERR_ALIGN;
+  if (need_vec16) {
+    if (!aligned(c->k, 16) || !aligned(c->v, 16)) return KVC_ERR_ALIGN;
+    if ((c->stride_t * s) % 16 || (c->stride_h * s) % 16 || (c->stride_b * s) % 16) return KVC_ERR_ALIGN;
+    if ((static_cast<int64_t>(c->head_dim) * s) % 16) return KVC_ERR_ALIGN;
+  }
+  return KVC_OK;
+}
+
+int copy_vector_bytes(const kvc_cache_t* c, const void* src_k, const void* src_v,
+                      const int64_t* src_strides_bytes, int n_src_strides) {
+  const int s = elem_bytes(c->dtype);
+  int vb = 16;
+  auto fits = [&](int64_t x) { return (x % vb) == 0; };
+  while (vb > s) {
+    bool ok = fits(static_cast<int64_t>(c->head_dim) * s) && fits(c->stride_t * s) &&
+              fits(c->stride_h * s) && fits(c->stride_b * s) &&
+              fits(static_cast<int64_t>(reinterpret_cast<uintptr_t>(c->k))) &&
+              fits(static_cast<int64_t>(reinterpret_cast<uintptr_t>(c->v))) &&
+              fits(static_cast<int64_t>(reinterpret_cast<uintptr_t>(src_k))) &&
+              fits(static_cast<int64_t>(reinterpret_cast<uintptr_t>(src_v)));
+    for (int i = 0; ok && i < n_src_strides; ++i) ok = fits(src_strides_bytes[i]);
+    if (ok) break;
+    vb /= 2;
+  }
+  return vb;
+}
+
+bool decode_head_dim_supported(int32_t head_dim, int32_t dtype) {
+  const int s = elem_bytes(dtype);
+  if (s == 0) return false;
+  switch (head_dim) {
+    case 4: case 8: case 16: case 32: case 64: case 128: case 256: break;
+    default: return false;
+  }
+  const int row = head_dim * s;
+  return row >= 16 && row <= 1024;
+}
+
+int heads_per_block(int32_t group) {
+  if (group <= 1) return 1;
+  if (group <= 2) return 2;
+  if (group <= 4) return 4;
+  return 8;
+}
+
+int head_blocks(int32_t group) {
+  const int hb = heads_per_block(group);
+  return (group + hb - 1) / hb;
+}
+
+int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads) {
+  if (c == nullptr || c->n_kv_heads <= 0 || n_q_heads <= 0 || c->batch <= 0) return 1;
+  const int64_t units = static_cast<int64_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
+  const int64_t target_wgs = 2048;        // ~8 workgroups per CU on 256 CUs
+  const int64_t max_chunk = 512;          // tokens per workgroup at most
+  const int64_t min_chunk = 64;           // tokens per workgroup at least
+  int64_t s = (target_wgs + units - 1) / units;
+  const int64_t by_len = (static_cast<int64_t>(c->max_len) + max_chunk - 1) / max_chunk;
+  if (s < by_len) s = by_len;
+  int64_t cap = (static_cast<int64_t>(c->max_len) + min_chunk - 1) / min_chunk;
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > 1024) s = 1024;
+  if (s < 1) s = 1;
+  return static_cast<int32_t>(s);
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
+  const size_t rows = static_cast<size_t>(c->batch) * n_q_heads * n_splits;
+  return round256(rows * c->head_dim * sizeof(float));
+}
+
+size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
+  const size_t rows = static_cast<size_t>(c->batch) * n_q_heads * n_splits;
+  return workspace_ml_offset(c, n_q_heads, n_splits) + round256(rows * 2 * sizeof(float));
+}
+
+}  // namespace kvc
+
+extern "C" uint64_t kvc_cache_bytes(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                                    const int32_t* h_lens, int32_t batch) {
+  const int s = kvc::elem_bytes(dtype);
+  if (s == 0 || n_layers < 0 || n_kv_heads < 0 || head_dim < 0 || batch < 0) return 0;
+  if (batch > 0 && h_lens == nullptr) return 0;
+  uint64_t tokens = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (h_lens[b] < 0) return 0;
+    tokens += static_cast<uint64_t>(h_lens[b]);
+  }
+  return 2ull * static_cast<uint64_t>(n_layers) * static_cast<uint64_t>(n_kv_heads) *
+         static_cast<uint64_t>(head_dim) * static_cast<uint64_t>(s) * tokens;
+}
+
+extern "C" const char* kvc_status_str(kvc_status_t status) {
+  switch (status) {
+    case KVC_OK: return "KVC_OK";
+    case KVC_ERR_NULL: return "KVC_ERR_NULL: a required pointer is NULL";
+    case KVC_ERR_SHAPE: return "KVC_ERR_SHAPE: invalid size or overlapping strides";
+    case KVC_ERR_DTYPE: return "KVC_ERR_DTYPE: unknown dtype";
+    case KVC_ERR_ALIGN: return "KVC_ERR_ALIGN: pointer or stride misaligned for the kernels";
+    case KVC_ERR_GQA: return "KVC_ERR_GQA: n_q_heads is not a positive multiple of n_kv_heads";
+    case KVC_ERR_WORKSPACE: return "KVC_ERR_WORKSPACE: workspace missing or too small";
+    case KVC_ERR_UNSUPPORTED: return "KVC_ERR_UNSUPPORTED: head_dim/dtype not built into the decode kernels";
+    case KVC_ERR_HIP: return "KVC_ERR_HIP: HIP launch error";
+    default: return "KVC_ERR_UNKNOWN";
+  }
+}
+
+extern "C" size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t n_splits) {
+  if (kvc::check_cache(cache, false) != KVC_OK) return 0;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0) return 0;
+  const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
+  return kvc::workspace_bytes(cache, n_q_heads, s);
+}
+
+extern "C" int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads) {
+  if (kvc::check_cache(cache, false) != KVC_OK) return 0;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return 0;
+  return kvc::auto_splits(cache, n_q_heads);
+}

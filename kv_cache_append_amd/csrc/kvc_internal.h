@@ -1,0 +1,44 @@
+// Host-side helpers shared by the C-ABI entry points (no device code here).
+#ifndef KVC_INTERNAL_H_
+#define KVC_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+// Bytes per stored element, 0 for an unknown dtype code.
+int elem_bytes(int32_t dtype);
+
+// Shape, dtype, pointer and stride checks common to every call on a cache.
+// need_vec16: the caller's kernels use 16-byte loads on cache rows.
+kvc_status_t check_cache(const kvc_cache_t* c, bool need_vec16);
+
+// Largest power-of-two byte width (16, 8, 4 or 2, at least the element size)
+// that divides every given byte offset/stride and pointer; used by the copy
+// kernels to pick their vector width.
+int copy_vector_bytes(const kvc_cache_t* c, const void* src_k, const void* src_v,
+                      const int64_t* src_strides_bytes, int n_src_strides);
+
+// Decode kernels are built for these head dims; head_dim * elem_bytes must be
+// a multiple of 16 and at most 1024.
+bool decode_head_dim_supported(int32_t head_dim, int32_t dtype);
+
+// Query heads handled by one decode workgroup (1, 2, 4 or 8) and the number
+// of such head blocks per KV head.
+int heads_per_block(int32_t group);
+int head_blocks(int32_t group);
+
+// Sequence splits per (sequence, KV head, head block) when the caller passes 0.
+int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads);
+
+// Workspace: fp32 partial outputs [B, H_q, S, D] followed by fp32 (max, sum)
+// pairs [B, H_q, S, 2]; each region starts on a 256-byte boundary.
+size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
+size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
+
+}  // namespace kvc
+
+#endif  // KVC_INTERNAL_H_

@@ -1,0 +1,177 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and its host-only logic (validation before any launch, the
+cache-bytes formula, status strings, workspace sizing) behaves as documented."""
+
+import csv
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+def _lib():
+    import kv_cache_append_amd as kvc
+    if not os.path.exists(kvc.LIB_PATH):
+        pytest.fail("libkvc.so is not built (run __graft_entry__.build())")
+    return kvc, kvc.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding_list():
+    import kv_cache_append_amd as kvc
+    assert _declared() == sorted(kvc.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    kvc, lib = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", kvc.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(kvc_\w+)$", out, flags=re.M))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_library_is_built_for_gfx950():
+    """The offload bundle inside libkvc.so (built here from our sources) targets gfx950."""
+    kvc, _ = _lib()
+    blob = open(kvc.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def _rows():
+    path = os.path.join(ROOT, "tests", "golden", "capacity_values.csv")
+    with open(path) as f:
+        return list(csv.DictReader([ln for ln in f if not ln.startswith("#")]))
+
+
+def test_cache_bytes_matches_printed_values():
+    """kvc_cache_bytes against every size the pages print (same golden file
+    that pins the oracle)."""
+    kvc, lib = _lib()
+    units = {"B": 1, "KiB": 2**10, "MiB": 2**20, "GiB": 2**30}
+    code = {2: kvc.KVC_F16, 4: kvc.KVC_F32}
+    for row in _rows():
+        b = int(row["batch"])
+        lens = (ctypes.c_int32 * b)(*([int(row["seq_len"])] * b))
+        got = lib.kvc_cache_bytes(int(row["n_layers"]), int(row["n_kv_heads"]), int(row["head_dim"]),
+                                  code[int(row["elem_bytes"])], lens, b)
+        want = float(row["value"]) * units[row["unit"]]
+        tol = float(row["rel_tol"])
+        assert abs(got - want) <= tol * want, row["citation"]
+
+
+def test_cache_bytes_invalid_inputs_return_zero():
+    _, lib = _lib()
+    lens = (ctypes.c_int32 * 2)(5, -1)
+    assert lib.kvc_cache_bytes(1, 1, 8, 0, lens, 2) == 0          # negative length
+    assert lib.kvc_cache_bytes(1, 1, 8, 9, lens, 1) == 0          # unknown dtype
+    assert lib.kvc_cache_bytes(1, 1, 8, 2, None, 1) == 0          # NULL lengths
+    assert lib.kvc_cache_bytes(1, 1, 8, 2, None, 0) == 0          # empty batch
+
+
+def test_status_strings():
+    kvc, lib = _lib()
+    for code, name in kvc.STATUS.items():
+        assert lib.kvc_status_str(code).decode().startswith(name)
+
+
+def _desc(kvc, **kw):
+    base = dict(k=64, v=128, batch=2, n_kv_heads=2, max_len=16, head_dim=128, dtype=kvc.KVC_BF16,
+                reserved0=0, stride_b=2 * 16 * 128, stride_h=16 * 128, stride_t=128)
+    base.update(kw)
+    return kvc.CacheDesc(**base)
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(dtype=7), 3), (dict(n_kv_heads=0), 2), (dict(head_dim=0), 2),
+    (dict(stride_t=64), 2), (dict(reserved0=1), 2), (dict(k=66), 4), (dict(stride_t=129), 4),
+])
+def test_decode_validation_rejects_before_launch(kw, code):
+    kvc, lib = _lib()
+    c = _desc(kvc, **kw)
+    rc = lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, 1 << 30, 0, None, None)
+    assert rc == code
+
+
+def test_decode_validation_gqa_workspace_unsupported():
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    big = 1 << 30
+    assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 3, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 5
+    assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 0, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 5
+    need = lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, 0)
+    assert need > 0
+    assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, need - 1, 0,
+                               None, None) == 6
+    assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, None, need, 0, None, None) == 6
+    odd = _desc(kvc, head_dim=96, stride_t=96, stride_h=16 * 96, stride_b=2 * 16 * 96)
+    assert lib.kvc_decode_attn(ctypes.byref(odd), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 7
+    assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, kvc.KVC_F16, FAKE, big, 0,
+                               None, None) == 3     # out dtype must be fp32 or the cache dtype
+    assert lib.kvc_decode_attn(ctypes.byref(c), None, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 1
+
+
+def test_workspace_size_formula():
+    """Workspace = fp32 partial outputs [B, H_q, S, D] + (max, sum) pairs, each
+    region rounded to 256 bytes."""
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    for s in (1, 3, 16):
+        rows = 2 * 4 * s
+        want = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+        assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, s) == want
+    auto = lib.kvc_decode_splits(ctypes.byref(c), 4)
+    assert auto >= 1
+    assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, 0) == lib.kvc_decode_workspace_bytes(
+        ctypes.byref(c), 4, auto)
+    assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 3, 0) == 0
+
+
+def test_auto_splits_cover_the_chip():
+    """The library's split choice gives ~2048 workgroups (8 per CU on 256 CUs)
+    for the gqa_8b layer, at most 512 tokens per chunk and at least 64."""
+    kvc, lib = _lib()
+    c = _desc(kvc, batch=16, n_kv_heads=8, max_len=2049, stride_t=128, stride_h=2049 * 128,
+              stride_b=8 * 2049 * 128)
+    s = lib.kvc_decode_splits(ctypes.byref(c), 32)
+    assert 16 * 8 * s >= 2048
+    assert -(-2049 // s) >= 64
+
+
+@pytest.mark.parametrize("call", ["append", "fill"])
+def test_copy_validation(call):
+    kvc, lib = _lib()
+    bad = _desc(kvc, n_kv_heads=-1)
+    ok = _desc(kvc)
+    if call == "append":
+        assert lib.kvc_append(ctypes.byref(bad), FAKE, FAKE, FAKE, 256, 128, None, None) == 2
+        assert lib.kvc_append(ctypes.byref(ok), None, FAKE, FAKE, 256, 128, None, None) == 1
+        assert lib.kvc_append(ctypes.byref(ok), FAKE, FAKE, FAKE, 256, 64, None, None) == 2
+        assert lib.kvc_append(None, FAKE, FAKE, FAKE, 256, 128, None, None) == 1
+        empty = _desc(kvc, batch=0)
+        assert lib.kvc_append(ctypes.byref(empty), None, None, None, 0, 0, None, None) == 0
+    else:
+        assert lib.kvc_prefill_fill(ctypes.byref(ok), FAKE, FAKE, FAKE, 0, 0, 0, -1, None, None) == 2
+        assert lib.kvc_prefill_fill(ctypes.byref(ok), FAKE, FAKE, FAKE, 0, 0, 0, 0, None, None) == 0
+        assert lib.kvc_prefill_fill(ctypes.byref(ok), FAKE, None, FAKE, 0, 0, 0, 3, None, None) == 1
+        assert lib.kvc_prefill_fill(ctypes.byref(ok), FAKE, FAKE, FAKE, 0, 0, 64, 3, None, None) == 2
+
+
+def test_advance_validation():
+    _, lib = _lib()
+    assert lib.kvc_seq_lens_advance(None, -1, 1, None) == 2
+    assert lib.kvc_seq_lens_advance(None, 0, 1, None) == 0
+    assert lib.kvc_seq_lens_advance(None, 4, 1, None) == 1
