@@ -1,8 +1,8 @@
 """Decode-step benchmark: achieved HBM GB/s of KV-cache decode attention.
 
 One step is the whole per-layer incremental-decode path over all L layers of
-one batch: for every layer kvc_append (the new token's k, v into slot T_b) and
-kvc_decode_attn (every query head attends T_b + 1 tokens), then one
+one batch: for every layer kvc_decode_step (the new token's k, v written into
+slot T_b and every query head attending T_b + 1 tokens, one launch), then one
 kvc_seq_lens_advance. The value is KV bytes read per step, 2*L*H_kv*D*s*
 sum_b(T_b + 1), divided by the step time, with every input already resident in
 HBM. seq_lens is reset to the workload's lengths before the timed steps, so
@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention achieved HBM GB/s (KV bytes read/step time) and % of peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-DOMINANT_KERNEL = "decode_split_kernel"
+DOMINANT_KERNEL = "decode_kernel"
 KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_append_amd", "csrc", "kvc_kernels.hip")
 
 
@@ -79,8 +79,7 @@ class Workload:
         self.seq_lens = self.lengths.to(dev)
         self.descs = [kvc.cache_desc(self.k[l], self.v[l]) for l in range(L)]
         self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq)
-        self.ws = torch.empty(kvc.decode_workspace_bytes(self.k[0], self.v[0], Hq, self.splits),
-                              dtype=torch.uint8, device=dev)
+        self.ws = kvc.workspace(self.k[0], self.v[0], Hq, self.splits)
         self.scale = ctypes.c_float(1.0 / math.sqrt(D))
         torch.cuda.synchronize()
 
@@ -97,12 +96,11 @@ class Workload:
         st = vp(stream_handle)
         for l in range(cfg.n_layers):
             d = ctypes.byref(self.descs[l])
-            rc = lib.kvc_append(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
-                                None, st)
             if events is not None:
                 events[l][0].record()
-            rc |= lib.kvc_decode_attn(d, seq, 1, vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
-                                      vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
+            rc = lib.kvc_decode_step(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
+                                     vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
+                                     vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
             if events is not None:
                 events[l][1].record()
             if rc:
@@ -223,7 +221,7 @@ def _cpu_baseline(cfg, seconds: float, seed: int):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{b} sequences x all {cfg.n_kv_heads} KV heads of one {cfg.name} layer "
+        "sample": f"{b} (sequence, layer) slices of {cfg.name}, all {cfg.n_kv_heads} KV heads each "
                   f"({units} (sequence, KV head) units, {cfg.group} query heads each, "
                   f"{done_bytes / 1e9:.3f} GB of K+V) in {t_spent:.1f} s; numpy fp64, BLAS threads={threads}",
     }
@@ -257,7 +255,7 @@ def _run_config(name, args, with_cpu):
             "splits": w.splits, "hip_graph": not args.no_graph,
         },
         "roofline": {
-            "bound": "hbm", "kernel": "kvc_decode_attn (split + merge kernels)",
+            "bound": "hbm", "kernel": "decode_kernel (kvc_decode_step: append + attention + merge, one launch per layer)",
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),

@@ -59,6 +59,9 @@ typedef enum kvc_status {
   KVC_ERR_HIP = 8          /* the HIP runtime reported an error at launch */
 } kvc_status_t;
 
+/* Largest n_splits the decode calls accept (their automatic choice stays below it). */
+#define KVC_MAX_SPLITS 256
+
 /* Bits OR-ed into the optional device status word (uint32_t). */
 #define KVC_DEVERR_CAPACITY 1u  /* a write or read would pass max_len: that sequence was skipped/clamped */
 #define KVC_DEVERR_BADLEN   2u  /* seq_lens[b] < 0: that sequence was skipped / treated as empty */
@@ -125,10 +128,18 @@ kvc_status_t kvc_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens,
                               int32_t t_new, uint32_t* dev_status, hipStream_t stream);
 
 /*
- * kvc_decode_workspace_bytes -- bytes of device workspace kvc_decode_attn
- * needs for this cache, query-head count and split count (n_splits = 0 means
- * the library's choice, the same one kvc_decode_attn makes). The bound holds
- * for any seq_lens <= max_len. Returns 0 for invalid arguments.
+ * kvc_decode_workspace_bytes -- bytes of device workspace kvc_decode_attn /
+ * kvc_decode_step need for this cache, query-head count and split count
+ * (n_splits = 0 means the library's choice, the same one the decode calls
+ * make). The bound holds for any seq_lens <= max_len. Returns 0 for invalid
+ * arguments.
+ *
+ * Layout and lifetime: a region of uint32 tickets (one per sequence, KV head
+ * and block of query heads), then fp32 per-split partial results. The caller
+ * zero-fills the workspace ONCE after allocating it; every decode call leaves
+ * the ticket region zero again, so the same workspace serves any number of
+ * later calls (also with other shapes that fit) without clearing. Calls that
+ * share a workspace must not run concurrently.
  */
 size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t n_splits);
 
@@ -152,18 +163,42 @@ int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads);
  *   out       [batch, n_q_heads, head_dim], contiguous, dtype out_dtype
  *             (KVC_F32, or the cache dtype rounded to nearest even).
  *   workspace device buffer of at least kvc_decode_workspace_bytes(cache,
- *             n_q_heads, n_splits) bytes, 16-byte aligned; its contents on
- *             entry do not matter. Not used concurrently by another call.
- *   n_splits  sequence splits per (sequence, KV head); 0 = library choice.
+ *             n_q_heads, n_splits) bytes, 16-byte aligned, zero-filled once
+ *             after allocation (see kvc_decode_workspace_bytes).
+ *   n_splits  sequence splits per (sequence, KV head), 0..KVC_MAX_SPLITS;
+ *             0 = library choice; larger values return KVC_ERR_SHAPE.
  *             The result does not depend on it beyond fp32 rounding order.
  *
- * Sequences with N_b == 0 produce a zero row. N_b is clamped to max_len (with
+ * Limit: (max_len + 2048) * stride_t * elem_bytes must stay below 2^31 (one
+ * sequence's slice of one KV head is addressed with 32-bit offsets), else
+ * KVC_ERR_SHAPE. Sequences with N_b == 0 produce a zero row. N_b is clamped to max_len (with
  * KVC_DEVERR_CAPACITY set) so the kernels never read past the cache.
  * Accumulation is fp32; results are run-to-run deterministic.
  * Supported: head_dim in {64, 128, 256} for every dtype, plus head_dim 4..32
  * (powers of two with head_dim * elem_bytes >= 16); any group size.
  */
 kvc_status_t kvc_decode_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                             const void* q, int32_t n_q_heads, float scale,
+                             void* out, int32_t out_dtype,
+                             void* workspace, size_t workspace_bytes, int32_t n_splits,
+                             uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * kvc_decode_step -- kvc_append followed by kvc_decode_attn with n_pending = 1,
+ * in one launch: the new token's k_t, v_t are written into slot seq_lens[b]
+ * and every query head attends the seq_lens[b] + 1 tokens [0, seq_lens[b]]
+ * (course notes §1.3: k, v appended, then q attends all t+1 keys; textbook
+ * §2.2). The cache bytes written and the output are identical to the two
+ * separate calls. k_new / v_new are [batch, n_kv_heads, head_dim] with
+ * element strides new_stride_b, new_stride_h; here they must be 16-byte
+ * aligned (pointers and strides in bytes), else KVC_ERR_ALIGN and nothing is
+ * enqueued. seq_lens stays read only. A full cache (seq_lens[b] >= max_len) is
+ * not written, the flag is set and the sequence attends its max_len stored
+ * tokens, as with the separate calls. Other arguments as kvc_decode_attn.
+ */
+kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens,
+                             const void* k_new, const void* v_new,
+                             int64_t new_stride_b, int64_t new_stride_h,
                              const void* q, int32_t n_q_heads, float scale,
                              void* out, int32_t out_dtype,
                              void* workspace, size_t workspace_bytes, int32_t n_splits,

@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvc.so")
+# The in-tree build; KVC_LIBRARY may name another build of the same sources.
+LIB_PATH = os.environ.get("KVC_LIBRARY") or os.path.join(_PKG, "libkvc.so")
 
 KVC_F32, KVC_F16, KVC_BF16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: KVC_F32, torch.float16: KVC_F16, torch.bfloat16: KVC_BF16}
@@ -29,7 +30,7 @@ STATUS = {
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
-           "kvc_decode_attn", "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
+           "kvc_decode_attn", "kvc_decode_step", "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
 
 
 class KvcError(RuntimeError):
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.kvc_decode_splits.restype = i32
     lib.kvc_decode_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_decode_attn.restype = i32
+    lib.kvc_decode_step.argtypes = [cp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_decode_step.restype = i32
     lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
     lib.kvc_seq_lens_advance.restype = i32
     lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
@@ -137,6 +140,15 @@ def decode_workspace_bytes(k_cache, v_cache, n_q_heads: int, n_splits: int = 0) 
     return int(load().kvc_decode_workspace_bytes(ctypes.byref(c), n_q_heads, n_splits))
 
 
+def workspace(k_cache, v_cache, n_q_heads: int, n_splits: int = 0) -> torch.Tensor:
+    """A zero-filled device workspace for the decode calls (zero once; the
+    calls leave it reusable)."""
+    n = decode_workspace_bytes(k_cache, v_cache, n_q_heads, n_splits)
+    if n == 0:
+        raise ValueError("invalid cache/head arguments for a decode workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=k_cache.device)
+
+
 def decode_splits(k_cache, v_cache, n_q_heads: int) -> int:
     c = cache_desc(k_cache, v_cache)
     return int(load().kvc_decode_splits(ctypes.byref(c), n_q_heads))
@@ -156,6 +168,24 @@ def decode_attn(k_cache, v_cache, seq_lens, q, out, workspace, n_pending: int = 
                                float(scale), _ptr(out), out_code, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), n_splits,
                                _ptr(status), _stream(stream)), "kvc_decode_attn")
+
+
+def decode_step(k_cache, v_cache, seq_lens, k_new, v_new, q, out, workspace, scale=None, n_splits: int = 0,
+                status=None, stream=None, desc=None):
+    """kvc_decode_step: append k_new/v_new at slot seq_lens[b] and attend
+    seq_lens[b] + 1 tokens, in one launch."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(lib.kvc_decode_step(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+                               k_new.stride(1), _ptr(q), q.shape[1], float(scale), _ptr(out),
+                               DTYPE_CODE[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               n_splits, _ptr(status), _stream(stream)), "kvc_decode_step")
 
 
 def seq_lens_advance(seq_lens, n: int = 1, stream=None):

@@ -93,16 +93,25 @@ int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads) {
   int64_t cap = (static_cast<int64_t>(c->max_len) + min_chunk - 1) / min_chunk;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
-  if (s > 1024) s = 1024;
+  if (s > KVC_MAX_SPLITS) s = KVC_MAX_SPLITS;
   if (s < 1) s = 1;
   return static_cast<int32_t>(s);
 }
 
 static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+static size_t tickets_bytes(const kvc_cache_t* c, int32_t n_q_heads) {
+  const size_t units = static_cast<size_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
+  return round256(units * sizeof(uint32_t));
+}
+
+size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t /*n_splits*/) {
+  return tickets_bytes(c, n_q_heads);
+}
+
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
   const size_t rows = static_cast<size_t>(c->batch) * n_q_heads * n_splits;
-  return round256(rows * c->head_dim * sizeof(float));
+  return workspace_o_offset(c, n_q_heads, n_splits) + round256(rows * c->head_dim * sizeof(float));
 }
 
 size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
@@ -143,7 +152,7 @@ extern "C" const char* kvc_status_str(kvc_status_t status) {
 
 extern "C" size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t n_splits) {
   if (kvc::check_cache(cache, false) != KVC_OK) return 0;
-  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0) return 0;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return 0;
   const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
   return kvc::workspace_bytes(cache, n_q_heads, s);
 }

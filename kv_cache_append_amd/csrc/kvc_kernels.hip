@@ -7,20 +7,29 @@
 // Decode attention: one query per head attends every cached token (textbook
 // "11.7 KV Cache" §2.2 single-step decode). It is HBM-bound by construction
 // (textbook §1.1 and course notes §1.5: about one FLOP per byte), so the
-// kernel is organised around streaming K/V once:
+// kernel is organised around streaming K/V exactly once, in one launch:
 //   * the T axis of every (sequence, KV head) is cut into n_splits chunks,
 //     one 256-thread workgroup per chunk (and per block of <= 8 query heads);
 //   * within a wave, each cache row of D elements is read by LPR = D*s/16
 //     lanes with one 16-byte load each, so one wave-wide load covers 64/LPR
-//     whole rows of contiguous memory (fully coalesced);
+//     whole rows of contiguous memory (fully coalesced); the next tile's rows
+//     are loaded while the current tile is computed (register double buffer);
 //   * every lane keeps the q slices of all query heads of its GQA group in
 //     registers, so each K/V row is fetched once and used by all of them
 //     (course notes §3.4: query head j reads KV head floor(j/(h/G)); no copy);
-//   * dot products are reduced across the LPR lanes of a row with DPP row
-//     operations; the softmax is online (running max and sum per head, in the
-//     log2 domain), rescaled once per tile of rows;
-//   * each workgroup writes an fp32 partial (max, sum, unnormalised output);
-//     a second kernel merges the partials of every (sequence, query head).
+//   * q.k uses the 2-way dot-product instructions for 16-bit caches; partial
+//     dot products are reduced across the LPR lanes of a row with DPP;
+//   * the softmax is online in the log2 domain with a lazily moved reference:
+//     the running reference only moves when a score exceeds it by more than
+//     2^8, so the accumulators are rarely rescaled (exact in real arithmetic,
+//     bounded exponentials in fp32);
+//   * each workgroup's partial (reference, sum, unnormalised output) goes to
+//     the workspace; the last workgroup of a (sequence, KV head) to finish,
+//     found with a device-scope atomic ticket, merges the partials and writes
+//     the normalised output, then resets its ticket to zero;
+//   * kvc_decode_step additionally takes the step's k_t, v_t: the workgroup
+//     whose chunk holds slot T_b reads that row from k_t/v_t and writes it
+//     into the cache, so append and attention share the launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +40,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- copies --
 
@@ -96,6 +107,13 @@ struct F32T {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(r[i]);
   }
+  // q.k over this lane's 4 elements
+  __device__ static inline float dot(const u32x4 q, const u32x4 k) {
+    float d = __uint_as_float(q[0]) * __uint_as_float(k[0]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) d = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), d);
+    return d;
+  }
   __device__ static inline void store(void* base, int64_t i, float x) { static_cast<float*>(base)[i] = x; }
 };
 
@@ -110,6 +128,17 @@ struct F16T {
       f[2 * i] = static_cast<float>(lo);
       f[2 * i + 1] = static_cast<float>(hi);
     }
+  }
+  // q.k over this lane's 8 elements: four 2-way fp16 dot products, fp32 sum.
+  // (The whole vector is bit-cast once: casting single lanes of the uint
+  // vector inside a loop was compiled to four uses of lane 0.)
+  __device__ static inline float dot(const u32x4 q, const u32x4 k) {
+    const half8_t a = __builtin_bit_cast(half8_t, q);
+    const half8_t b = __builtin_bit_cast(half8_t, k);
+    float d = __builtin_amdgcn_fdot2(a.s01, b.s01, 0.f, false);
+    d = __builtin_amdgcn_fdot2(a.s23, b.s23, d, false);
+    d = __builtin_amdgcn_fdot2(a.s45, b.s45, d, false);
+    return __builtin_amdgcn_fdot2(a.s67, b.s67, d, false);
   }
   __device__ static inline void store(void* base, int64_t i, float x) {
     // Pin x as an fp32 register value first: without this the compiler may
@@ -131,6 +160,15 @@ struct BF16T {
       f[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
     }
   }
+  // q.k over this lane's 8 elements: four 2-way bf16 dot products, fp32 sum
+  __device__ static inline float dot(const u32x4 q, const u32x4 k) {
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, q);
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, k);
+    float d = __builtin_amdgcn_fdot2_f32_bf16(a.s01, b.s01, 0.f, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(a.s23, b.s23, d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(a.s45, b.s45, d, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(a.s67, b.s67, d, false);
+  }
   __device__ static inline void store(void* base, int64_t i, float x) {
     // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
     const uint32_t u = __float_as_uint(x);
@@ -151,8 +189,8 @@ __device__ inline float dpp_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
 constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within each 16 lanes
 
@@ -174,51 +212,133 @@ __device__ inline float group_sum(float x) {
 // ------------------------------------------------------------ decode attn --
 
 struct DecodeParams {
-  const char* k;
-  const char* v;
+  char* k;                     // cache; written only by the fused append
+  char* v;
   int64_t sb, sh, st;          // cache strides in bytes
   const int32_t* seq_lens;
   const char* q;               // [B, H_q, D] cache dtype, contiguous
+  const char* k_new;           // fused append source [B, H_kv, D] or null
+  const char* v_new;
+  int64_t nsb, nsh;            // its strides in bytes
+  uint32_t* ws_cnt;            // [B * H_kv * n_hblk] tickets, zero between calls
   float* ws_o;                 // [B, H_q, S, D]
   float* ws_ml;                // [B, H_q, S, 2]
   void* out;                   // [B, H_q, D]
   uint32_t* status;
-  int32_t batch, n_q, n_kv, group, n_hblk, max_len, n_pending, n_splits;
+  int32_t batch, n_q, n_kv, group, n_hblk, max_len, n_pending, n_splits, out_f32;
   float scale_log2;            // softmax scale * log2(e)
 };
 
-__device__ inline int tokens_attended(const DecodeParams& p, int b, bool* clamped, bool* bad) {
-  int n = p.seq_lens[b];
-  *bad = n < 0;
-  if (n < 0) n = 0;
-  n += p.n_pending;
-  *clamped = n > p.max_len;
-  if (n > p.max_len) n = p.max_len;
-  return n;
+struct SeqInfo {
+  int n;           // tokens attended
+  int append_row;  // slot the fused append writes, or -1
+  uint32_t flags;  // KVC_DEVERR_* bits
+};
+
+__device__ inline SeqInfo seq_info(const DecodeParams& p, int b) {
+  const int c0 = p.seq_lens[b];
+  SeqInfo si;
+  si.flags = 0;
+  const int c = c0 < 0 ? 0 : c0;
+  if (c0 < 0) si.flags |= KVC_DEVERR_BADLEN;
+  si.append_row = -1;
+  int n;
+  if (p.k_new != nullptr) {
+    if (c0 >= 0 && c0 < p.max_len) si.append_row = c0;
+    else si.flags |= KVC_DEVERR_CAPACITY;
+    n = c + 1;
+  } else {
+    n = c + p.n_pending;
+  }
+  if (n > p.max_len) {
+    n = p.max_len;
+    si.flags |= KVC_DEVERR_CAPACITY;
+  }
+  si.n = n;
+  return si;
 }
 
-// Merge two online-softmax states (log2 domain); empty states have m = -inf.
-__device__ inline void merge_state(float& m, float& l, float* a, float m2, float l2, const float* a2, int n) {
-  const float mn = fmaxf(m, m2);
-  const float ref = (mn == -INFINITY) ? 0.f : mn;
-  const float c1 = exp2f(m - ref);
-  const float c2 = exp2f(m2 - ref);
+template <typename ET>
+__device__ inline void store_out(const DecodeParams& p, int64_t idx, float x) {
+  if (p.out_f32) F32T::store(p.out, idx, x);
+  else ET::store(p.out, idx, x);
+}
+
+// exp2 of a non-positive-or-bounded argument; -inf gives 0 (hardware v_exp_f32)
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Merge two online-softmax states (log2 domain, reference r, sum l,
+// unnormalised accumulators a); an empty state has r = -inf and l = a = 0.
+__device__ inline void merge_state(float& r, float& l, float* a, float r2, float l2, const float* a2, int n) {
+  const float mn = fmaxf(r, r2);
+  const float c1 = (r == -INFINITY) ? 0.f : fast_exp2(r - mn);
+  const float c2 = (r2 == -INFINITY) ? 0.f : fast_exp2(r2 - mn);
   l = l * c1 + l2 * c2;
   for (int e = 0; e < n; ++e) a[e] = a[e] * c1 + a2[e] * c2;
-  m = mn;
+  r = mn;
 }
 
+// Buffer resource (V#) over [base, base + bytes): loads past the end return
+// zero and stores past it are dropped (hardware range check). Word 3 is the
+// gfx9-family raw-buffer configuration (32-bit data format, no swizzle).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+// Values every lane of the wave holds alike, moved to scalar registers so
+// buffer resources built from them need no per-lane handling.
+// (The builtin returns a signed int: each half is taken back to uint32_t
+// before widening, or a low word with bit 31 set would sign-extend into the
+// high word and corrupt the address.)
+__device__ inline uint32_t uniform_u32(uint32_t x) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(x)); }
+__device__ inline const char* uniform_ptr(const char* q) {
+  const uint64_t a = reinterpret_cast<uint64_t>(q);
+  const uint64_t lo = uniform_u32(static_cast<uint32_t>(a));
+  const uint64_t hi = uniform_u32(static_cast<uint32_t>(a >> 32));
+  return reinterpret_cast<const char*>(lo | (hi << 32));
+}
+constexpr int kCoherent = 16;   // buffer cache policy: device scope (write-through / miss in the per-XCD L2)
+
+__device__ inline u32x4 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+__device__ inline u32x4 buf_load_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kCoherent));
+}
+__device__ inline void buf_store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), r,
+                                         static_cast<int>(off), 0, kCoherent);
+}
+
+// Tuning constants (measured on MI355X): waves per decode workgroup and row
+// passes per register tile.
+#ifndef KVC_WAVES
+#define KVC_WAVES 4
+#endif
+#ifndef KVC_TILE_PASSES
+#define KVC_TILE_PASSES 2
+#endif
+
+// Workgroups each CU should hold at once: 16-bit caches with up to 4 heads per
+// workgroup fit 128 VGPRs (4 waves per SIMD) without spilling in the loop;
+// the others keep the compiler's default budget.
+template <typename ET, int GB>
+constexpr int decode_min_wgs() { return (ET::kBytes == 2 && GB <= 4) ? 4 : 1; }
+
 template <typename ET, int D, int GB>
-__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void decode_kernel(const DecodeParams p) {
   constexpr int EPL = ET::kPerVec;        // elements per lane per row
   constexpr int LPR = D / EPL;            // lanes per row
   constexpr int RPP = 64 / LPR;           // rows per wave pass
-  constexpr int NW = 4;                   // waves per workgroup
-  constexpr int U = (GB >= 8) ? 2 : 4;    // passes per tile (rescale once per tile)
+  constexpr int NW = KVC_WAVES;           // waves per workgroup
+  constexpr int U = (RPP >= 4) ? KVC_TILE_PASSES : 4;   // passes per tile
+  constexpr int TS = NW * RPP * U;        // rows per workgroup tile
+  constexpr int D4 = D / 4;               // float4 columns of an output row
+  constexpr float kLazy = 8.f;            // reference moves only past ref + 8 (log2 domain)
   static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must split into 16-byte lane slices");
 
   __shared__ float sm_a[NW][GB][D];
   __shared__ float sm_ml[NW][GB][2];
+  __shared__ uint32_t sm_ticket;
 
   int bid = blockIdx.x;
   const int split = bid % p.n_splits;
@@ -228,103 +348,201 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   const int b = unit / p.n_kv;
   const int g = unit - b * p.n_kv;
 
-  bool clamped, bad;
-  const int n = tokens_attended(p, b, &clamped, &bad);
+  const SeqInfo si = seq_info(p, b);
+  if (si.flags != 0 && g == 0 && hb == 0 && split == 0 && threadIdx.x == 0 && p.status != nullptr)
+    atomicOr(p.status, si.flags);
+  const int n = si.n;
+  const int h_first = g * p.group + hb * GB;
+  const int nh = min(GB, p.group - hb * GB);       // valid heads in this block
+  const int64_t orow0 = (static_cast<int64_t>(b) * p.n_q + h_first) * D;
+  if (n <= 0) {                                      // empty sequence: zero rows
+    if (split == 0)
+      for (int t = threadIdx.x; t < nh * D; t += blockDim.x) store_out<ET>(p, orow0 + t, 0.f);
+    return;
+  }
   const int chunk = (n + p.n_splits - 1) / p.n_splits;
   const int t0 = split * chunk;
-  if (t0 >= n) return;                    // also n == 0; the merge skips this split
+  if (t0 >= n) return;                               // inactive split: not counted in ns
   const int t1 = min(t0 + chunk, n);
+  const int ns = (n + chunk - 1) / chunk;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: loop bounds derived from it are wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane / LPR;             // which row of the pass
   const int li = lane % LPR;              // which 16-byte slice of the row
 
-  const int h_first = g * p.group + hb * GB;
-  float qf[GB][EPL];
+  u32x4 qv[GB];
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
-    if (hb * GB + j < p.group) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(
-          p.q + ((static_cast<int64_t>(b) * p.n_q + h_first + j) * D + li * EPL) * ET::kBytes);
-      ET::unpack(raw, qf[j]);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[j][e] *= p.scale_log2;
+    if (j < nh) {
+      qv[j] = *reinterpret_cast<const u32x4*>(p.q + ((static_cast<int64_t>(b) * p.n_q + h_first + j) * D + li * EPL) *
+                                                       ET::kBytes);
     } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[j][e] = 0.f;
+      qv[j] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  float m[GB], l[GB], acc[GB][EPL];
+  float ref[GB], l[GB], acc[GB][EPL];
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
-    m[j] = -INFINITY;
+    ref[j] = -INFINITY;
     l[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
   }
 
-  const char* kb = p.k + b * p.sb + g * p.sh + li * 16;
-  const char* vb = p.v + b * p.sb + g * p.sh + li * 16;
+  const int64_t unit_off = b * p.sb + g * p.sh;
+  // The last attended row (n - 1) is folded in after the streaming loop, as
+  // one extra tile held in registers, by the workgroup whose chunk holds it;
+  // that workgroup streams only [t0, n - 1) from the cache. With the fused
+  // append that row is the new token: it comes from k_new/v_new and the
+  // workgroup of the first head block writes it into the cache, so nothing
+  // waits on the copy and no workgroup reads slot T_b from the cache in this
+  // launch. Both entry points thus add the same rows in the same order, and
+  // kvc_decode_step matches kvc_append + kvc_decode_attn bit for bit.
+  const int arow = si.append_row;
+  const int xrow = n - 1;
+  const bool has_x = xrow >= t0 && xrow < t1;
+  const bool x_new = has_x && arow == xrow;
+  // rows streamed from the cache: [t0, t_end) (a scalar, like every loop bound below)
+  const int t_end = __builtin_amdgcn_readfirstlane(has_x ? xrow : t1);
+  u32x4 nk = u32x4{0u, 0u, 0u, 0u}, nv = u32x4{0u, 0u, 0u, 0u};
+  if (has_x && wave == 0) {
+    const char* ksrc;
+    const char* vsrc;
+    if (x_new) {
+      const int64_t noff = b * p.nsb + g * p.nsh + li * 16;
+      ksrc = p.k_new + noff;
+      vsrc = p.v_new + noff;
+    } else {
+      const int64_t coff = unit_off + static_cast<int64_t>(xrow) * p.st + li * 16;
+      ksrc = p.k + coff;
+      vsrc = p.v + coff;
+    }
+    nk = *reinterpret_cast<const u32x4*>(ksrc);
+    nv = *reinterpret_cast<const u32x4*>(vsrc);
+  }
 
-  // Uniform trip count for the whole wave; rows past t1 are masked per lane group.
-  for (int base = t0 + wave * RPP; base < t1; base += NW * RPP * U) {
-    u32x4 kr[U], vr[U];
-    bool ok[U];
+  // K/V of this unit through buffer resources built per tile on the scalar
+  // unit: base = the tile's first row, range = up to row t_end, so rows of a
+  // tile past t_end read as zero (and are masked), every load is
+  // unconditional, nothing past the streamed range can be read, and the lanes'
+  // offsets are loop constants (no vector address arithmetic in the loop).
+  const uint32_t st = static_cast<uint32_t>(p.st);
+  const char* kunit = p.k + unit_off;
+  const char* vunit = p.v + unit_off;
+  uint32_t voff[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    voff[u] = static_cast<uint32_t>(u * NW * RPP + grp) * st + static_cast<uint32_t>(li) * 16u;
+
+  auto load_tile = [&](int base_any, u32x4 (&K)[U], u32x4 (&V)[U]) {
+    const int base = __builtin_amdgcn_readfirstlane(base_any);
+    const int rows_left = t_end - base;
+    const uint32_t range = rows_left > 0 ? static_cast<uint32_t>(rows_left) * st : 0u;
+    const int64_t boff = static_cast<int64_t>(base) * st;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr(kunit + boff), range);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr(vunit + boff), range);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = base + u * NW * RPP + grp;
-      ok[u] = r < t1;
-      if (ok[u]) {
-        kr[u] = *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(r) * p.st);
-        vr[u] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(r) * p.st);
-      } else {
-        kr[u] = u32x4{0u, 0u, 0u, 0u};
-        vr[u] = u32x4{0u, 0u, 0u, 0u};
-      }
+      K[u] = buf_load(krs, voff[u]);
+      V[u] = buf_load(vrs, voff[u]);
     }
-    float s[GB][U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[EPL];
-      ET::unpack(kr[u], kf);
-#pragma unroll
-      for (int j = 0; j < GB; ++j) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) d = fmaf(qf[j][e], kf[e], d);
-        d = group_sum<LPR>(d);
-        s[j][u] = ok[u] ? d : -INFINITY;
-      }
-    }
+  };
+
+  auto compute_rows = [&](const u32x4 (&K)[U], const u32x4 (&V)[U], const bool (&ok)[U]) {
     float vf[U][EPL];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ET::unpack(vr[u], vf[u]);
+    for (int u = 0; u < U; ++u) ET::unpack(V[u], vf[u]);
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
-      float mt = s[j][0];
+      float s[U];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[j][u]);
-      const float mn = fmaxf(m[j], mt);
-      const float ref = (mn == -INFINITY) ? 0.f : mn;
-      const float corr = exp2f(m[j] - ref);
+      for (int u = 0; u < U; ++u) {
+        s[u] = group_sum<LPR>(ET::dot(qv[j], K[u])) * p.scale_log2;
+        if (ok[u]) mt = fmaxf(mt, s[u]);
+      }
+      const bool need = mt > ref[j] + kLazy;
+      if (__any(need)) {                      // wave-uniform branch, rarely taken after the first tile
+        const float nr = need ? mt : ref[j];
+        const float c = (ref[j] == -INFINITY) ? 0.f : fast_exp2(ref[j] - nr);
+        l[j] *= c;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= c;
+        ref[j] = nr;
+      }
       float pu[U];
       float ps = 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        pu[u] = exp2f(s[j][u] - ref);
+        pu[u] = ok[u] ? fast_exp2(s[u] - ref[j]) : 0.f;
         ps += pu[u];
       }
-      l[j] = l[j] * corr + ps;
-      m[j] = mn;
+      l[j] += ps;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        float a = acc[j][e] * corr;
+        float a = acc[j][e];
 #pragma unroll
         for (int u = 0; u < U; ++u) a = fmaf(pu[u], vf[u][e], a);
         acc[j][e] = a;
       }
+    }
+  };
+
+  // row of pass u relative to the tile's first row, per lane (loop invariant)
+  int rel_row[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) rel_row[u] = u * NW * RPP + grp;
+
+  auto compute_tile = [&](int base, const u32x4 (&K)[U], const u32x4 (&V)[U]) {
+    const int rows_left = __builtin_amdgcn_readfirstlane(t_end - base);   // scalar
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ok[u] = rel_row[u] < rows_left;
+    compute_rows(K, V, ok);
+  };
+
+  // Register triple buffer: two tiles of loads in flight behind the one being
+  // computed. `base` is this wave's first row of a tile (wave-uniform).
+  {
+    int base = __builtin_amdgcn_readfirstlane(t0 + wave * RPP);
+    const int n_tiles = base < t_end ? (t_end - base + TS - 1) / TS : 0;
+    if (n_tiles > 0) {
+      u32x4 K0[U], V0[U], K1[U], V1[U], K2[U], V2[U];
+      load_tile(base, K0, V0);
+      load_tile(base + TS, K1, V1);           // past t_end: zeros from the range check
+      for (int it = 0;; it += 3) {
+        load_tile(base + 2 * TS, K2, V2);
+        compute_tile(base, K0, V0);
+        base += TS;
+        if (it + 1 >= n_tiles) break;
+        load_tile(base + 2 * TS, K0, V0);
+        compute_tile(base, K1, V1);
+        base += TS;
+        if (it + 2 >= n_tiles) break;
+        load_tile(base + 2 * TS, K1, V1);
+        compute_tile(base, K2, V2);
+        base += TS;
+        if (it + 3 >= n_tiles) break;
+      }
+    }
+  }
+  if (has_x && wave == 0) {                    // the last attended row: lane group 0, pass 0
+    u32x4 K[U], V[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      K[u] = u == 0 ? nk : u32x4{0u, 0u, 0u, 0u};
+      V[u] = u == 0 ? nv : u32x4{0u, 0u, 0u, 0u};
+      ok[u] = u == 0 && grp == 0;
+    }
+    compute_rows(K, V, ok);
+    if (x_new && hb == 0 && grp == 0) {        // fused append: write the new row
+      const int64_t coff = unit_off + static_cast<int64_t>(arow) * p.st + li * 16;
+      *reinterpret_cast<u32x4*>(p.k + coff) = nk;
+      *reinterpret_cast<u32x4*>(p.v + coff) = nv;
     }
   }
 
@@ -333,12 +551,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   for (int off = LPR; off < 64; off *= 2) {
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
-      const float m2 = __shfl_xor(m[j], off);
+      const float r2 = __shfl_xor(ref[j], off);
       const float l2 = __shfl_xor(l[j], off);
       float a2[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(acc[j][e], off);
-      merge_state(m[j], l[j], acc[j], m2, l2, a2, EPL);
+      merge_state(ref[j], l[j], acc[j], r2, l2, a2, EPL);
     }
   }
   if (lane < LPR) {
@@ -347,84 +565,127 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) sm_a[wave][j][li * EPL + e] = acc[j][e];
       if (lane == 0) {
-        sm_ml[wave][j][0] = m[j];
+        sm_ml[wave][j][0] = ref[j];
         sm_ml[wave][j][1] = l[j];
       }
     }
   }
   __syncthreads();
 
-  // Merge the NW waves and write this split's partial for each valid head.
-  for (int t = threadIdx.x; t < GB * D; t += blockDim.x) {
-    const int j = t / D;
-    const int d = t - j * D;
-    if (hb * GB + j >= p.group) continue;
-    float mm = -INFINITY;
+  // Merge the NW waves, four output columns per thread. A single active
+  // split writes the normalised output directly; otherwise the partial goes
+  // to the workspace with device-coherent 16-byte stores.
+  const int64_t prow0 = (static_cast<int64_t>(b) * p.n_q + h_first) * p.n_splits;
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(nh * p.n_splits * D * 4));
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(nh * p.n_splits * 2 * 4));
+  for (int t = threadIdx.x; t < nh * D4; t += blockDim.x) {
+    const int j = t / D4;
+    const int d = (t - j * D4) * 4;
+    float rr = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sm_ml[w][j][0]);
-    const float ref = (mm == -INFINITY) ? 0.f : mm;
-    float ll = 0.f, aa = 0.f;
+    for (int w = 0; w < NW; ++w) rr = fmaxf(rr, sm_ml[w][j][0]);
+    float ll = 0.f, aa[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float c = exp2f(sm_ml[w][j][0] - ref);
+      const float rw = sm_ml[w][j][0];
+      const float c = (rw == -INFINITY) ? 0.f : fast_exp2(rw - rr);
       ll += sm_ml[w][j][1] * c;
-      aa += sm_a[w][j][d] * c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) aa[e] += sm_a[w][j][d + e] * c;
     }
-    const int64_t row = (static_cast<int64_t>(b) * p.n_q + h_first + j) * p.n_splits + split;
-    p.ws_o[row * D + d] = aa;
-    if (d == 0) {
-      p.ws_ml[row * 2] = mm;
-      p.ws_ml[row * 2 + 1] = ll;
+    if (ns == 1) {
+      const float inv = 1.f / ll;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out<ET>(p, orow0 + j * D + d + e, aa[e] * inv);
+    } else {
+      const uint32_t row = static_cast<uint32_t>(j * p.n_splits + split);
+      buf_store_coherent(ors, (row * D + d) * 4u,
+                         u32x4{__float_as_uint(aa[0]), __float_as_uint(aa[1]), __float_as_uint(aa[2]),
+                               __float_as_uint(aa[3])});
+      if (d == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rr), mrs, static_cast<int>(row * 8u), 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ll), mrs, static_cast<int>(row * 8u + 4u), 0,
+                                              kCoherent);
+      }
     }
   }
-}
+  if (ns == 1) return;
 
-// One workgroup per (sequence, query head): merge the active splits' partials
-// (log-sum-exp over the per-split maxima) and write the normalised output.
-template <typename OT>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeParams p, int D) {
-  const int b = blockIdx.x / p.n_q;
-  const int h = blockIdx.x - b * p.n_q;
-  bool clamped, bad;
-  const int n = tokens_attended(p, b, &clamped, &bad);
-  if (h == 0 && threadIdx.x == 0 && p.status != nullptr && (clamped || bad))
-    atomicOr(p.status, (clamped ? KVC_DEVERR_CAPACITY : 0u) | (bad ? KVC_DEVERR_BADLEN : 0u));
-  const int64_t orow = (static_cast<int64_t>(b) * p.n_q + h) * D;
-  if (n <= 0) {
-    for (int d = threadIdx.x; d < D; d += blockDim.x) OT::store(p.out, orow + d, 0.f);
-    return;
+  // Last-arriving workgroup of this (sequence, KV head, head block) merges.
+  // The partials were written with device-coherent (write-through) stores;
+  // waiting for their completion before the ticket is taken orders them
+  // before it, and the merging workgroup reads them with device-coherent
+  // loads, so no L2 write-back or invalidate is needed.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint32_t* ticket = p.ws_cnt + static_cast<int64_t>(unit) * p.n_hblk + hb;
+  if (threadIdx.x == 0) sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sm_ticket != static_cast<uint32_t>(ns - 1)) return;
+  // Each thread merges four output columns of one head over all splits,
+  // eight splits per round trip: their (reference, sum) pairs and partial
+  // outputs are requested together, then folded in with a running reference.
+  for (int t = threadIdx.x; t < nh * D4; t += blockDim.x) {
+    const int j = t / D4;
+    const int d = (t - j * D4) * 4;
+    const uint32_t row0 = static_cast<uint32_t>(j * p.n_splits);
+    float mm = -INFINITY, ll = 0.f, aa[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < ns; i0 += 8) {
+      const int cnt = min(8, ns - i0);
+      float rb[8], lb[8];
+      u32x4 ob[8];
+      // unconditional loads (rows past the split count read another head's
+      // data or, past the region, zeros) so that all 24 are in flight at once
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t row = row0 + static_cast<uint32_t>(i0 + k);
+        rb[k] = __uint_as_float(static_cast<uint32_t>(
+            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u), 0, kCoherent)));
+        lb[k] = __uint_as_float(static_cast<uint32_t>(
+            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u + 4u), 0, kCoherent)));
+        ob[k] = buf_load_coherent(ors, (row * D + d) * 4u);
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) bm = k < cnt ? fmaxf(bm, rb[k]) : bm;
+      const float nm = fmaxf(mm, bm);
+      const float c = (mm == -INFINITY) ? 0.f : fast_exp2(mm - nm);
+      ll *= c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) aa[e] *= c;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = k < cnt ? fast_exp2(rb[k] - nm) : 0.f;
+        ll = fmaf(k < cnt ? lb[k] : 0.f, w, ll);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) aa[e] = fmaf(k < cnt ? __uint_as_float(ob[k][e]) : 0.f, w, aa[e]);
+      }
+      mm = nm;
+    }
+    const float inv = 1.f / ll;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out<ET>(p, orow0 + j * D + d + e, aa[e] * inv);
   }
-  const int chunk = (n + p.n_splits - 1) / p.n_splits;
-  const int ns = (n + chunk - 1) / chunk;
-  const int64_t row0 = (static_cast<int64_t>(b) * p.n_q + h) * p.n_splits;
-  float mm = -INFINITY;
-  for (int i = 0; i < ns; ++i) mm = fmaxf(mm, p.ws_ml[(row0 + i) * 2]);
-  float ll = 0.f;
-  for (int i = 0; i < ns; ++i) ll += p.ws_ml[(row0 + i) * 2 + 1] * exp2f(p.ws_ml[(row0 + i) * 2] - mm);
-  const float inv = 1.f / ll;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float a = 0.f;
-    for (int i = 0; i < ns; ++i) a += p.ws_o[(row0 + i) * D + d] * exp2f(p.ws_ml[(row0 + i) * 2] - mm);
-    OT::store(p.out, orow + d, a * inv);
-  }
+  if (threadIdx.x == 0)   // ready for the next call on this workspace
+    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------- dispatch --
 
-typedef void (*SplitKernel)(const DecodeParams);
+typedef void (*DecodeKernel)(const DecodeParams);
 
 template <typename ET, int D>
-SplitKernel pick_gb(int gb) {
+DecodeKernel pick_gb(int gb) {
   switch (gb) {
-    case 1: return decode_split_kernel<ET, D, 1>;
-    case 2: return decode_split_kernel<ET, D, 2>;
-    case 4: return decode_split_kernel<ET, D, 4>;
-    default: return decode_split_kernel<ET, D, 8>;
+    case 1: return decode_kernel<ET, D, 1>;
+    case 2: return decode_kernel<ET, D, 2>;
+    case 4: return decode_kernel<ET, D, 4>;
+    default: return decode_kernel<ET, D, 8>;
   }
 }
 
 template <typename ET>
-SplitKernel pick_d(int d, int gb) {
+DecodeKernel pick_d(int d, int gb) {
   switch (d) {
     case 4: if constexpr (ET::kBytes * 4 >= 16) return pick_gb<ET, 4>(gb); else return nullptr;
     case 8: return pick_gb<ET, 8>(gb);
@@ -437,7 +698,7 @@ SplitKernel pick_d(int d, int gb) {
   }
 }
 
-SplitKernel pick_split_kernel(int dtype, int d, int gb) {
+DecodeKernel pick_decode_kernel(int dtype, int d, int gb) {
   switch (dtype) {
     case KVC_F32: return pick_d<F32T>(d, gb);
     case KVC_F16: return pick_d<F16T>(d, gb);
@@ -485,6 +746,77 @@ kvc_status_t launch_copy(const kvc_cache_t* c, const int32_t* seq_lens, const vo
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+// Shared by kvc_decode_attn (k_new == nullptr) and kvc_decode_step.
+kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,
+                           const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
+                           int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
+                           size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
+  kvc_status_t st = kvc::check_cache(cache, true);
+  if (st != KVC_OK) return st;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
+  if (n_pending < 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return KVC_ERR_SHAPE;
+  if (out_dtype != KVC_F32 && out_dtype != cache->dtype) return KVC_ERR_DTYPE;
+  if (!kvc::decode_head_dim_supported(cache->head_dim, cache->dtype)) return KVC_ERR_UNSUPPORTED;
+  if (cache->batch == 0) return KVC_OK;
+  if (seq_lens == nullptr || q == nullptr || out == nullptr) return KVC_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(q) % 16) return KVC_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(out) % kvc::elem_bytes(out_dtype)) return KVC_ERR_ALIGN;
+  const int s = kvc::elem_bytes(cache->dtype);
+  if (k_new != nullptr) {
+    if (v_new == nullptr) return KVC_ERR_NULL;
+    if (new_stride_b < 0 || new_stride_h < 0) return KVC_ERR_SHAPE;
+    if (cache->n_kv_heads > 1 && new_stride_h < cache->head_dim) return KVC_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16 ||
+        (new_stride_b * s) % 16 || (new_stride_h * s) % 16)
+      return KVC_ERR_ALIGN;
+  }
+  // The kernels address one (sequence, KV head) slice of K/V with 32-bit
+  // byte offsets (plus up to two tiles past the end, read back as zeros).
+  if ((static_cast<int64_t>(cache->max_len) + 2048) * cache->stride_t * s > 0x7fffffffll) return KVC_ERR_SHAPE;
+  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
+  const size_t need = kvc::workspace_bytes(cache, n_q_heads, splits);
+  if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
+
+  const int group = n_q_heads / cache->n_kv_heads;
+  const int gb = kvc::heads_per_block(group);
+  DecodeParams p;
+  p.k = static_cast<char*>(cache->k);
+  p.v = static_cast<char*>(cache->v);
+  p.sb = cache->stride_b * s;
+  p.sh = cache->stride_h * s;
+  p.st = cache->stride_t * s;
+  p.seq_lens = seq_lens;
+  p.q = static_cast<const char*>(q);
+  p.k_new = static_cast<const char*>(k_new);
+  p.v_new = static_cast<const char*>(v_new);
+  p.nsb = new_stride_b * s;
+  p.nsh = new_stride_h * s;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_cnt = reinterpret_cast<uint32_t*>(ws);
+  p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(cache, n_q_heads, splits));
+  p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(cache, n_q_heads, splits));
+  p.out = out;
+  p.status = dev_status;
+  p.batch = cache->batch;
+  p.n_q = n_q_heads;
+  p.n_kv = cache->n_kv_heads;
+  p.group = group;
+  p.n_hblk = kvc::head_blocks(group);
+  p.max_len = cache->max_len;
+  p.n_pending = n_pending;
+  p.n_splits = splits;
+  p.out_f32 = out_dtype == KVC_F32 ? 1 : 0;
+  p.scale_log2 = scale * 1.44269504088896340736f;  // log2(e)
+
+  DecodeKernel k = pick_decode_kernel(cache->dtype, cache->head_dim, gb);
+  if (k == nullptr) return KVC_ERR_UNSUPPORTED;
+  const int64_t wgs = static_cast<int64_t>(cache->batch) * cache->n_kv_heads * p.n_hblk * splits;
+  if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(KVC_WAVES * 64), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI calls --
@@ -523,61 +855,22 @@ extern "C" kvc_status_t kvc_decode_attn(const kvc_cache_t* cache, const int32_t*
                                         const void* q, int32_t n_q_heads, float scale, void* out,
                                         int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                         int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
-  kvc_status_t st = kvc::check_cache(cache, true);
-  if (st != KVC_OK) return st;
-  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
-  if (n_pending < 0 || n_splits < 0) return KVC_ERR_SHAPE;
-  if (out_dtype != KVC_F32 && out_dtype != cache->dtype) return KVC_ERR_DTYPE;
-  if (!kvc::decode_head_dim_supported(cache->head_dim, cache->dtype)) return KVC_ERR_UNSUPPORTED;
-  if (cache->batch == 0) return KVC_OK;
-  if (seq_lens == nullptr || q == nullptr || out == nullptr) return KVC_ERR_NULL;
-  if (reinterpret_cast<uintptr_t>(q) % 16) return KVC_ERR_ALIGN;
-  if (reinterpret_cast<uintptr_t>(out) % kvc::elem_bytes(out_dtype)) return KVC_ERR_ALIGN;
-  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
-  const size_t need = kvc::workspace_bytes(cache, n_q_heads, splits);
-  if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
+  return launch_decode(cache, seq_lens, n_pending, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype,
+                       workspace, workspace_bytes, n_splits, dev_status, stream);
+}
 
-  const int s = kvc::elem_bytes(cache->dtype);
-  const int group = n_q_heads / cache->n_kv_heads;
-  const int gb = kvc::heads_per_block(group);
-  DecodeParams p;
-  p.k = static_cast<const char*>(cache->k);
-  p.v = static_cast<const char*>(cache->v);
-  p.sb = cache->stride_b * s;
-  p.sh = cache->stride_h * s;
-  p.st = cache->stride_t * s;
-  p.seq_lens = seq_lens;
-  p.q = static_cast<const char*>(q);
-  p.ws_o = static_cast<float*>(workspace);
-  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                     kvc::workspace_ml_offset(cache, n_q_heads, splits));
-  p.out = out;
-  p.status = dev_status;
-  p.batch = cache->batch;
-  p.n_q = n_q_heads;
-  p.n_kv = cache->n_kv_heads;
-  p.group = group;
-  p.n_hblk = kvc::head_blocks(group);
-  p.max_len = cache->max_len;
-  p.n_pending = n_pending;
-  p.n_splits = splits;
-  p.scale_log2 = scale * 1.44269504088896340736f;  // log2(e)
-
-  SplitKernel k = pick_split_kernel(cache->dtype, cache->head_dim, gb);
-  if (k == nullptr) return KVC_ERR_UNSUPPORTED;
-  const int64_t wgs = static_cast<int64_t>(cache->batch) * cache->n_kv_heads * p.n_hblk * splits;
-  if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return KVC_ERR_HIP;
-  const dim3 mgrid(static_cast<unsigned>(cache->batch * n_q_heads));
-  const dim3 mblock(cache->head_dim >= 256 ? 256 : (cache->head_dim >= 64 ? cache->head_dim : 64));
-  switch (out_dtype) {
-    case KVC_F32: hipLaunchKernelGGL(decode_merge_kernel<F32T>, mgrid, mblock, 0, stream, p, cache->head_dim); break;
-    case KVC_F16: hipLaunchKernelGGL(decode_merge_kernel<F16T>, mgrid, mblock, 0, stream, p, cache->head_dim); break;
-    default: hipLaunchKernelGGL(decode_merge_kernel<BF16T>, mgrid, mblock, 0, stream, p, cache->head_dim); break;
+extern "C" kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens, const void* k_new,
+                                        const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
+                                        const void* q, int32_t n_q_heads, float scale, void* out,
+                                        int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                        int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
+  if (k_new == nullptr || v_new == nullptr) {
+    kvc_status_t st = kvc::check_cache(cache, true);
+    if (st != KVC_OK) return st;
+    if (cache->batch > 0) return KVC_ERR_NULL;
   }
-  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+  return launch_decode(cache, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
+                       out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream);
 }
 
 extern "C" kvc_status_t kvc_seq_lens_advance(int32_t* seq_lens, int32_t batch, int32_t n, hipStream_t stream) {

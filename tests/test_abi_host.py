@@ -125,13 +125,13 @@ def test_decode_validation_gqa_workspace_unsupported():
 
 
 def test_workspace_size_formula():
-    """Workspace = fp32 partial outputs [B, H_q, S, D] + (max, sum) pairs, each
-    region rounded to 256 bytes."""
+    """Workspace = uint32 tickets [B * H_kv * head blocks] + fp32 partial outputs
+    [B, H_q, S, D] + (reference, sum) pairs, each region rounded to 256 bytes."""
     kvc, lib = _lib()
     c = _desc(kvc)
     for s in (1, 3, 16):
         rows = 2 * 4 * s
-        want = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+        want = 256 + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
         assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, s) == want
     auto = lib.kvc_decode_splits(ctypes.byref(c), 4)
     assert auto >= 1
@@ -175,3 +175,24 @@ def test_advance_validation():
     assert lib.kvc_seq_lens_advance(None, -1, 1, None) == 2
     assert lib.kvc_seq_lens_advance(None, 0, 1, None) == 0
     assert lib.kvc_seq_lens_advance(None, 4, 1, None) == 1
+
+
+def test_decode_step_validation():
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    big = 1 << 30
+    args = lambda kn, vn, sb, sh: (ctypes.byref(c), FAKE, kn, vn, sb, sh, FAKE, 4, 0.1, FAKE, 0, FAKE, big, 0,
+                                   None, None)
+    assert lib.kvc_decode_step(*args(None, FAKE, 256, 128)) == 1
+    assert lib.kvc_decode_step(*args(FAKE, None, 256, 128)) == 1
+    assert lib.kvc_decode_step(*args(ctypes.c_void_p(4104), FAKE, 256, 128)) == 4   # k_new not 16-byte aligned
+    assert lib.kvc_decode_step(*args(FAKE, FAKE, 256, 132)) == 4                     # stride_h * 2 B not /16
+    assert lib.kvc_decode_step(*args(FAKE, FAKE, 256, 64)) == 2                      # heads overlap
+
+
+def test_split_count_limit():
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, 256) > 0
+    assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, 257) == 0
+    assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, 1 << 30, 257, None, None) == 2

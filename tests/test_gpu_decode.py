@@ -24,7 +24,7 @@ def _run(case: DecodeCase, n_splits=0, out_dtype=torch.float32, scale=None):
     dev = case.q.device
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     kvc.append(case.k, case.v, case.seq_lens, case.k_new, case.v_new, status=status)
-    ws = torch.empty(kvc.decode_workspace_bytes(case.k, case.v, case.n_q, n_splits), dtype=torch.uint8, device=dev)
+    ws = kvc.workspace(case.k, case.v, case.n_q, n_splits)
     out = torch.empty((case.batch, case.n_q, case.head_dim), dtype=out_dtype, device=dev)
     kvc.decode_attn(case.k, case.v, case.seq_lens, case.q, out, ws, n_pending=1, n_splits=n_splits,
                     scale=scale, status=status)
@@ -78,7 +78,7 @@ def test_decode_other_head_dims(gpu, head_dim, dtype):
     _check_all(case, out)
 
 
-@pytest.mark.parametrize("n_splits", [1, 2, 7, 64, 3000])
+@pytest.mark.parametrize("n_splits", [1, 2, 7, 64, 256])
 def test_split_count_changes_only_rounding(gpu, n_splits):
     """Any split count gives the oracle's result; more splits than tokens leave
     some workgroups empty."""
@@ -107,7 +107,7 @@ def test_single_token_returns_its_value_exactly(gpu):
 def test_empty_sequence_gives_zero_row(gpu):
     dev = torch.device("cuda")
     case = DecodeCase(batch=2, n_q=4, n_kv=2, head_dim=128, dtype="bf16", lengths=[0, 9], tag="empty")
-    ws = torch.empty(kvc.decode_workspace_bytes(case.k, case.v, 4), dtype=torch.uint8, device=dev)
+    ws = kvc.workspace(case.k, case.v, 4)
     out = torch.full((2, 4, 128), 5.0, device=dev)
     kvc.decode_attn(case.k, case.v, case.seq_lens, case.q, out, ws, n_pending=0)
     torch.cuda.synchronize()
@@ -131,7 +131,7 @@ def test_capacity_clamp_sets_flag_and_never_reads_past_cache(gpu):
     assert int(status.item()) == kvc.DEVERR_CAPACITY
     assert torch.equal(case.k.view(torch.int16), k_before.view(torch.int16))
     status.zero_()
-    ws = torch.empty(kvc.decode_workspace_bytes(case.k, case.v, 2), dtype=torch.uint8, device=dev)
+    ws = kvc.workspace(case.k, case.v, 2)
     out = torch.empty((1, 2, 64), device=dev)
     kvc.decode_attn(case.k, case.v, case.seq_lens, case.q, out, ws, n_pending=1, status=status)
     torch.cuda.synchronize()
@@ -145,7 +145,7 @@ def test_negative_length_is_flagged_and_treated_as_empty(gpu):
     case = DecodeCase(batch=1, n_q=2, n_kv=1, head_dim=128, dtype="bf16", lengths=[3], tag="neg")
     seq = torch.tensor([-5], dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = torch.empty(kvc.decode_workspace_bytes(case.k, case.v, 2), dtype=torch.uint8, device=dev)
+    ws = kvc.workspace(case.k, case.v, 2)
     out = torch.full((1, 2, 128), 3.0, device=dev)
     kvc.decode_attn(case.k, case.v, seq, case.q, out, ws, n_pending=0, status=status)
     torch.cuda.synchronize()

@@ -52,7 +52,7 @@ def run_toy_on_gpu(cfg, x, wq, wk, wv, wo, device):
     kvc.prefill_fill(kc, vc, lens, k_all[None, :, :cfg.prompt].to(device), v_all[None, :, :cfg.prompt].to(device),
                      status=status)
     kvc.seq_lens_advance(lens, cfg.prompt)
-    ws = torch.empty(kvc.decode_workspace_bytes(kc, vc, cfg.n_q_heads), dtype=torch.uint8, device=device)
+    ws = kvc.workspace(kc, vc, cfg.n_q_heads)
     contexts = []
     for t in range(cfg.prompt, t_total):
         k_new = k_all[:, t][None].to(device)
