@@ -44,6 +44,13 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--calib-copy-mib run into HBM bytes per decode launch, written to --pmc-out")
+    ap.add_argument("--pmc-out", default=None, help="output JSON of --pmc-summary")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a known-size reference "
+                         "for HBM byte counters in a profiled run)")
     return ap.parse_args()
 
 
@@ -86,8 +93,8 @@ class Workload:
     def reset_lengths(self):
         self.seq_lens.copy_(self.lengths.to(self.seq_lens.device))
 
-    def step(self, stream_handle, events=None):
-        """Enqueue one decode step (all layers) on the given HIP stream."""
+    def layers(self, stream_handle):
+        """Enqueue the per-layer decode launches of one step (lengths unchanged)."""
         lib, cfg = self.lib, self.cfg
         vp = ctypes.c_void_p
         seq = vp(self.seq_lens.data_ptr())
@@ -96,16 +103,17 @@ class Workload:
         st = vp(stream_handle)
         for l in range(cfg.n_layers):
             d = ctypes.byref(self.descs[l])
-            if events is not None:
-                events[l][0].record()
             rc = lib.kvc_decode_step(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
                                      vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
                                      vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
-            if events is not None:
-                events[l][1].record()
             if rc:
                 raise RuntimeError(f"libkvc returned {rc} at layer {l}")
-        if lib.kvc_seq_lens_advance(seq, cfg.batch, 1, st):
+
+    def step(self, stream_handle):
+        """Enqueue one decode step: every layer, then seq_lens += 1."""
+        self.layers(stream_handle)
+        seq = ctypes.c_void_p(self.seq_lens.data_ptr())
+        if self.lib.kvc_seq_lens_advance(seq, self.cfg.batch, 1, ctypes.c_void_p(stream_handle)):
             raise RuntimeError("kvc_seq_lens_advance failed")
 
     def kv_bytes(self, steps: int) -> int:
@@ -154,22 +162,32 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = e0.elapsed_time(e1)
-    # per-launch duration of the decode call (HIP events on the same stream),
-    # a separate eager pass so the events do not perturb the timed steps
+    # Average duration of one decode launch: the L per-layer launches alone
+    # (lengths held, so every launch reads the same bytes), `reps` passes back
+    # to back, bracketed by HIP events on the launching stream.
     w.reset_lengths()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(w.cfg.n_layers)]
-    durs = []
-    n_pass = max(2, min(steps, 5))
-    launch_bytes = 0
-    for k in range(n_pass):
-        w.step(stream.cuda_stream, events=ev)
+    reps = max(2, min(steps, 10))
+    layers_graph = None
+    if use_graph:
+        layers_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(layers_graph):
+            w.layers(torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
-        durs.extend(a.elapsed_time(b) for a, b in ev)
-        launch_bytes += w.decode_launch_bytes(k) * w.cfg.n_layers
-    avg_launch_ms = sum(durs) / len(durs)
-    avg_launch_bytes = launch_bytes / len(durs)
+        layers_graph.replay()
+    else:
+        w.layers(stream.cuda_stream)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        if layers_graph is not None:
+            layers_graph.replay()
+        else:
+            w.layers(stream.cuda_stream)
+    e1.record()
+    torch.cuda.synchronize()
+    avg_launch_ms = e0.elapsed_time(e1) / (reps * w.cfg.n_layers)
+    avg_launch_bytes = w.decode_launch_bytes(0)
     return ms_total, wall, avg_launch_ms, avg_launch_bytes
 
 
@@ -184,6 +202,54 @@ def _traffic(workload_name: str):
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _pmc_summary(fetch_csv: str, write_csv: str, out_path: str, args):
+    """HBM traffic of the decode kernel from rocprofv3 counters. FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are each scaled by what they read for the
+    device-to-device copy of --calib-copy-mib MiB in the same run (that copy
+    reads and writes exactly that many bytes)."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {"decode": [], "copy": []}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = "decode" if "decode_kernel" in name else ("copy" if "copyBuffer" in name else None)
+            if key:
+                out[key].append(float(r["Counter_Value"]))
+        return out
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    wr = per_kernel(write_csv, "WRITE_SIZE")
+    if not (f["decode"] and f["copy"] and wr["decode"] and wr["copy"]):
+        raise SystemExit("counter CSVs lack decode_kernel or copy dispatches")
+    copy_bytes = args.calib_copy_mib << 20
+    f_scale = copy_bytes / (max(f["copy"]) * 1024)
+    w_scale = copy_bytes / (max(wr["copy"]) * 1024)
+    fetch = sum(f["decode"]) / len(f["decode"]) * 1024 * f_scale
+    write = sum(wr["decode"]) / len(wr["decode"]) * 1024 * w_scale
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    algo = 2 * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes * (int(cfg.lengths(args.seed).long().sum()) + cfg.batch)
+    rec = {
+        "workload": args.config,
+        "kernel": "decode_kernel",
+        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest(),
+        "hbm_bytes_per_launch": int(round(fetch + write)),
+        "fetch_bytes_per_launch": int(round(fetch)),
+        "write_bytes_per_launch": int(round(write)),
+        "algorithmic_kv_bytes_per_launch": algo,
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "calib_copy_bytes": copy_bytes,
+        "decode_dispatches": len(f["decode"]),
+    }
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 def _cpu_baseline(cfg, seconds: float, seed: int):
@@ -271,6 +337,9 @@ def _run_config(name, args, with_cpu):
 
 def main():
     args = _parse()
+    if args.pmc_summary:
+        _pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_out or "traffic.json", args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
@@ -279,6 +348,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     main_res = _run_config(args.config, args, with_cpu=not args.no_cpu_baseline)
     line = {
         "metric": METRIC,

@@ -159,7 +159,8 @@ int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads);
  * attends the t+1 keys of course notes §1.3.
  *
  *   q         [batch, n_q_heads, head_dim], contiguous, cache dtype.
- *   scale     softmax scale, normally 1/sqrt(head_dim).
+ *   scale     softmax scale, normally 1/sqrt(head_dim); must be finite and
+ *             > 0, else KVC_ERR_UNSUPPORTED.
  *   out       [batch, n_q_heads, head_dim], contiguous, dtype out_dtype
  *             (KVC_F32, or the cache dtype rounded to nearest even).
  *   workspace device buffer of at least kvc_decode_workspace_bytes(cache,

@@ -84,17 +84,18 @@ int head_blocks(int32_t group) {
 int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads) {
   if (c == nullptr || c->n_kv_heads <= 0 || n_q_heads <= 0 || c->batch <= 0) return 1;
   const int64_t units = static_cast<int64_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
-  const int64_t target_wgs = 2048;        // ~8 workgroups per CU on 256 CUs
-  const int64_t max_chunk = 512;          // tokens per workgroup at most
-  const int64_t min_chunk = 64;           // tokens per workgroup at least
+  // Measured on MI355X (256 CUs): the fastest launches hold about one
+  // workgroup per CU; more, shorter splits pay the per-workgroup start-up
+  // and merge more often than they gain. At least two splits, so that long
+  // sequences on few CUs still overlap two workgroups' streams.
+  const int64_t target_wgs = 256;
+  const int64_t min_chunk = 256;          // tokens per workgroup at least
   int64_t s = (target_wgs + units - 1) / units;
-  const int64_t by_len = (static_cast<int64_t>(c->max_len) + max_chunk - 1) / max_chunk;
-  if (s < by_len) s = by_len;
-  int64_t cap = (static_cast<int64_t>(c->max_len) + min_chunk - 1) / min_chunk;
+  if (s < 2) s = 2;
+  int64_t cap = static_cast<int64_t>(c->max_len) / min_chunk;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
   if (s > KVC_MAX_SPLITS) s = KVC_MAX_SPLITS;
-  if (s < 1) s = 1;
   return static_cast<int32_t>(s);
 }
 

@@ -108,10 +108,9 @@ struct F32T {
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(r[i]);
   }
   // q.k over this lane's 4 elements
-  __device__ static inline float dot(const u32x4 q, const u32x4 k) {
-    float d = __uint_as_float(q[0]) * __uint_as_float(k[0]);
+  __device__ static inline float dot(const u32x4 q, const u32x4 k, float d) {
 #pragma unroll
-    for (int i = 1; i < 4; ++i) d = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), d);
+    for (int i = 0; i < 4; ++i) d = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), d);
     return d;
   }
   __device__ static inline void store(void* base, int64_t i, float x) { static_cast<float*>(base)[i] = x; }
@@ -132,10 +131,10 @@ struct F16T {
   // q.k over this lane's 8 elements: four 2-way fp16 dot products, fp32 sum.
   // (The whole vector is bit-cast once: casting single lanes of the uint
   // vector inside a loop was compiled to four uses of lane 0.)
-  __device__ static inline float dot(const u32x4 q, const u32x4 k) {
+  __device__ static inline float dot(const u32x4 q, const u32x4 k, float d) {
     const half8_t a = __builtin_bit_cast(half8_t, q);
     const half8_t b = __builtin_bit_cast(half8_t, k);
-    float d = __builtin_amdgcn_fdot2(a.s01, b.s01, 0.f, false);
+    d = __builtin_amdgcn_fdot2(a.s01, b.s01, d, false);
     d = __builtin_amdgcn_fdot2(a.s23, b.s23, d, false);
     d = __builtin_amdgcn_fdot2(a.s45, b.s45, d, false);
     return __builtin_amdgcn_fdot2(a.s67, b.s67, d, false);
@@ -161,10 +160,10 @@ struct BF16T {
     }
   }
   // q.k over this lane's 8 elements: four 2-way bf16 dot products, fp32 sum
-  __device__ static inline float dot(const u32x4 q, const u32x4 k) {
+  __device__ static inline float dot(const u32x4 q, const u32x4 k, float d) {
     const bf16x8_t a = __builtin_bit_cast(bf16x8_t, q);
     const bf16x8_t b = __builtin_bit_cast(bf16x8_t, k);
-    float d = __builtin_amdgcn_fdot2_f32_bf16(a.s01, b.s01, 0.f, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(a.s01, b.s01, d, false);
     d = __builtin_amdgcn_fdot2_f32_bf16(a.s23, b.s23, d, false);
     d = __builtin_amdgcn_fdot2_f32_bf16(a.s45, b.s45, d, false);
     return __builtin_amdgcn_fdot2_f32_bf16(a.s67, b.s67, d, false);
@@ -198,6 +197,36 @@ constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within each 16 lanes
 // After the quad steps all four lanes of a quad hold the same value, so the
 // mirror steps (which pair each lane with one in the other quad / half-row)
 // complete the butterfly.
+// The same butterfly on N independent values, one step across all of them
+// at a time, so no DPP op reads the result of the VALU op just before it.
+template <int W, int N>
+__device__ inline void group_sum_n(float (&x)[N]) {
+  if constexpr (W >= 2) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<kDppQuadXor1>(x[i]);
+  }
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<kDppQuadXor2>(x[i]);
+  }
+  if constexpr (W >= 8) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<kDppHalfMirror>(x[i]);
+  }
+  if constexpr (W >= 16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f<kDppMirror>(x[i]);
+  }
+  if constexpr (W >= 32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], 16);
+  }
+  if constexpr (W >= 64) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], 32);
+  }
+}
+
 template <int W>
 __device__ inline float group_sum(float x) {
   if constexpr (W >= 2) x += dpp_f<kDppQuadXor1>(x);
@@ -309,20 +338,27 @@ __device__ inline void buf_store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off
                                          static_cast<int>(off), 0, kCoherent);
 }
 
-// Tuning constants (measured on MI355X): waves per decode workgroup and row
-// passes per register tile.
+// Tuning constants (measured on MI355X): waves per decode workgroup, row
+// passes per register tile, and tiles of loads kept in flight ahead of the
+// one being computed.
 #ifndef KVC_WAVES
 #define KVC_WAVES 4
 #endif
 #ifndef KVC_TILE_PASSES
 #define KVC_TILE_PASSES 2
 #endif
+#ifndef KVC_PREFETCH
+#define KVC_PREFETCH 2
+#endif
+#ifndef KVC_OCCUPANCY
+#define KVC_OCCUPANCY 4
+#endif
 
-// Workgroups each CU should hold at once: 16-bit caches with up to 4 heads per
-// workgroup fit 128 VGPRs (4 waves per SIMD) without spilling in the loop;
-// the others keep the compiler's default budget.
+// Workgroups each CU should hold at once, which sets the VGPR budget
+// (512 / workgroups per SIMD): 16-bit caches with up to 4 heads per
+// workgroup take KVC_OCCUPANCY; the others keep the compiler's default.
 template <typename ET, int GB>
-constexpr int decode_min_wgs() { return (ET::kBytes == 2 && GB <= 4) ? 4 : 1; }
+constexpr int decode_min_wgs() { return (ET::kBytes == 2 && GB <= 4) ? KVC_OCCUPANCY : 1; }
 
 template <typename ET, int D, int GB>
 __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void decode_kernel(const DecodeParams p) {
@@ -334,17 +370,28 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
   constexpr int TS = NW * RPP * U;        // rows per workgroup tile
   constexpr int D4 = D / 4;               // float4 columns of an output row
   constexpr float kLazy = 8.f;            // reference moves only past ref + 8 (log2 domain)
+  // Reference of a state that has seen no row: finite, so exp2(score - ref)
+  // of a masked (-inf) score is exp2(-inf) = 0 rather than NaN, and far
+  // below any finite score, so exp2(kEmpty - ref) is 0 once a row is seen.
+  constexpr float kEmpty = -1e30f;
   static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must split into 16-byte lane slices");
 
   __shared__ float sm_a[NW][GB][D];
   __shared__ float sm_ml[NW][GB][2];
   __shared__ uint32_t sm_ticket;
 
-  int bid = blockIdx.x;
-  const int split = bid % p.n_splits;
-  bid /= p.n_splits;
-  const int hb = bid % p.n_hblk;
-  const int unit = bid / p.n_hblk;
+  // Workgroup ids go round-robin over the 8 XCDs (id mod 8). The head blocks
+  // of one (unit, split) item read the same K/V rows, so they take ids 8
+  // apart: same XCD, hence the same L2, dispatched back to back. Items are
+  // numbered w = unit * n_splits + split; the grid is padded to a multiple
+  // of 8 items.
+  const int xcd = blockIdx.x & 7;
+  const int r8 = blockIdx.x >> 3;
+  const int hb = r8 % p.n_hblk;
+  const int w_item = (r8 / p.n_hblk) * 8 + xcd;
+  if (w_item >= p.batch * p.n_kv * p.n_splits) return;   // grid padding
+  const int split = w_item % p.n_splits;
+  const int unit = w_item / p.n_splits;
   const int b = unit / p.n_kv;
   const int g = unit - b * p.n_kv;
 
@@ -386,7 +433,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
   float ref[GB], l[GB], acc[GB][EPL];
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
-    ref[j] = -INFINITY;
+    ref[j] = kEmpty;
     l[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
@@ -451,43 +498,52 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
     }
   };
 
-  auto compute_rows = [&](const u32x4 (&K)[U], const u32x4 (&V)[U], const bool (&ok)[U]) {
-    float vf[U][EPL];
+  // One tile of U rows per lane group. bias[u] is 0 for a row to attend and
+  // -inf for a masked one: it seeds the dot product, so a masked row's score
+  // is -inf, drops out of the maximum and gets weight exp2(-inf) = 0 with no
+  // per-head masking (its K and V read as zero through the range check).
+  // The order (all scores, then all weights, then V one row at a time) keeps
+  // few temporaries live next to the buffered tiles.
+  const float sc = p.scale_log2;
+  auto compute_rows = [&](const u32x4 (&K)[U], const u32x4 (&V)[U], const float (&bias)[U]) {
+    float w[GB][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ET::unpack(V[u], vf[u]);
+    for (int j = 0; j < GB; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[j][u] = ET::dot(qv[j], K[u], bias[u]);
+    group_sum_n<LPR>(reinterpret_cast<float (&)[GB * U]>(w));
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
-      float s[U];
-      float mt = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        s[u] = group_sum<LPR>(ET::dot(qv[j], K[u])) * p.scale_log2;
-        if (ok[u]) mt = fmaxf(mt, s[u]);
-      }
+      for (int u = 0; u < U; ++u) w[j][u] *= sc;   // log2-domain score
+      float mt = w[j][0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mt = fmaxf(mt, w[j][u]);   // tile maximum (-inf if all masked)
       const bool need = mt > ref[j] + kLazy;
       if (__any(need)) {                      // wave-uniform branch, rarely taken after the first tile
         const float nr = need ? mt : ref[j];
-        const float c = (ref[j] == -INFINITY) ? 0.f : fast_exp2(ref[j] - nr);
+        const float c = fast_exp2(ref[j] - nr);   // 0 while ref is still the empty value
         l[j] *= c;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[j][e] *= c;
         ref[j] = nr;
       }
-      float pu[U];
       float ps = 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        pu[u] = ok[u] ? fast_exp2(s[u] - ref[j]) : 0.f;
-        ps += pu[u];
+        w[j][u] = fast_exp2(w[j][u] - ref[j]);   // exactly 1 for the row that set ref
+        ps += w[j][u];
       }
       l[j] += ps;
+    }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float a = acc[j][e];
+    for (int u = 0; u < U; ++u) {
+      float vf[EPL];
+      ET::unpack(V[u], vf);
 #pragma unroll
-        for (int u = 0; u < U; ++u) a = fmaf(pu[u], vf[u][e], a);
-        acc[j][e] = a;
-      }
+      for (int j = 0; j < GB; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(w[j][u], vf[e], acc[j][e]);
     }
   };
 
@@ -498,47 +554,48 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
 
   auto compute_tile = [&](int base, const u32x4 (&K)[U], const u32x4 (&V)[U]) {
     const int rows_left = __builtin_amdgcn_readfirstlane(t_end - base);   // scalar
-    bool ok[U];
+    float bias[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ok[u] = rel_row[u] < rows_left;
-    compute_rows(K, V, ok);
+    for (int u = 0; u < U; ++u) bias[u] = rel_row[u] < rows_left ? 0.f : -INFINITY;
+    compute_rows(K, V, bias);
   };
 
-  // Register triple buffer: two tiles of loads in flight behind the one being
-  // computed. `base` is this wave's first row of a tile (wave-uniform).
+  // Register ring of NB tiles: NB - 1 tiles of loads in flight behind the
+  // one being computed. `base` is this wave's first row of a tile
+  // (wave-uniform); tiles past t_end read as zeros and are never computed.
   {
+    constexpr int NB = KVC_PREFETCH + 1;
     int base = __builtin_amdgcn_readfirstlane(t0 + wave * RPP);
     const int n_tiles = base < t_end ? (t_end - base + TS - 1) / TS : 0;
     if (n_tiles > 0) {
-      u32x4 K0[U], V0[U], K1[U], V1[U], K2[U], V2[U];
-      load_tile(base, K0, V0);
-      load_tile(base + TS, K1, V1);           // past t_end: zeros from the range check
-      for (int it = 0;; it += 3) {
-        load_tile(base + 2 * TS, K2, V2);
-        compute_tile(base, K0, V0);
-        base += TS;
-        if (it + 1 >= n_tiles) break;
-        load_tile(base + 2 * TS, K0, V0);
-        compute_tile(base, K1, V1);
-        base += TS;
-        if (it + 2 >= n_tiles) break;
-        load_tile(base + 2 * TS, K1, V1);
-        compute_tile(base, K2, V2);
-        base += TS;
-        if (it + 3 >= n_tiles) break;
+      u32x4 KB[NB][U], VB[NB][U];
+#pragma unroll
+      for (int r = 0; r < NB - 1; ++r) load_tile(base + r * TS, KB[r], VB[r]);
+      bool done = false;
+      for (int it = 0; !done; it += NB) {
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {       // unrolled: ring slots are compile-time
+          load_tile(base + (NB - 1) * TS, KB[(r + NB - 1) % NB], VB[(r + NB - 1) % NB]);
+          compute_tile(base, KB[r], VB[r]);
+          base += TS;
+          if (it + r + 1 >= n_tiles) {
+            done = true;
+            break;
+          }
+        }
       }
     }
   }
   if (has_x && wave == 0) {                    // the last attended row: lane group 0, pass 0
     u32x4 K[U], V[U];
-    bool ok[U];
+    float bias[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       K[u] = u == 0 ? nk : u32x4{0u, 0u, 0u, 0u};
       V[u] = u == 0 ? nv : u32x4{0u, 0u, 0u, 0u};
-      ok[u] = u == 0 && grp == 0;
+      bias[u] = (u == 0 && grp == 0) ? 0.f : -INFINITY;
     }
-    compute_rows(K, V, ok);
+    compute_rows(K, V, bias);
     if (x_new && hb == 0 && grp == 0) {        // fused append: write the new row
       const int64_t coff = unit_off + static_cast<int64_t>(arow) * p.st + li * 16;
       *reinterpret_cast<u32x4*>(p.k + coff) = nk;
@@ -757,6 +814,10 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   if (n_pending < 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return KVC_ERR_SHAPE;
   if (out_dtype != KVC_F32 && out_dtype != cache->dtype) return KVC_ERR_DTYPE;
   if (!kvc::decode_head_dim_supported(cache->head_dim, cache->dtype)) return KVC_ERR_UNSUPPORTED;
+  // Masked rows enter as -inf scores before scaling: a positive finite scale
+  // keeps them -inf (and keeps the order of scores for the running maximum).
+  const float scale_log2 = scale * 1.44269504088896340736f;  // log2(e)
+  if (!(scale > 0.f) || !(scale_log2 < INFINITY)) return KVC_ERR_UNSUPPORTED;
   if (cache->batch == 0) return KVC_OK;
   if (seq_lens == nullptr || q == nullptr || out == nullptr) return KVC_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(q) % 16) return KVC_ERR_ALIGN;
@@ -807,11 +868,12 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.n_pending = n_pending;
   p.n_splits = splits;
   p.out_f32 = out_dtype == KVC_F32 ? 1 : 0;
-  p.scale_log2 = scale * 1.44269504088896340736f;  // log2(e)
+  p.scale_log2 = scale_log2;
 
   DecodeKernel k = pick_decode_kernel(cache->dtype, cache->head_dim, gb);
   if (k == nullptr) return KVC_ERR_UNSUPPORTED;
-  const int64_t wgs = static_cast<int64_t>(cache->batch) * cache->n_kv_heads * p.n_hblk * splits;
+  const int64_t items = static_cast<int64_t>(cache->batch) * cache->n_kv_heads * splits;
+  const int64_t wgs = (items + 7) / 8 * 8 * p.n_hblk;     // see the id mapping in decode_kernel
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(KVC_WAVES * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;

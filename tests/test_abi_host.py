@@ -122,6 +122,9 @@ def test_decode_validation_gqa_workspace_unsupported():
     assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, kvc.KVC_F16, FAKE, big, 0,
                                None, None) == 3     # out dtype must be fp32 or the cache dtype
     assert lib.kvc_decode_attn(ctypes.byref(c), None, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 1
+    for bad in (0.0, -0.1, float("inf"), float("nan"), 3e38):   # scale must be finite and > 0
+        assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, bad, FAKE, 0, FAKE, big, 0,
+                                   None, None) == 7
 
 
 def test_workspace_size_formula():
@@ -141,14 +144,24 @@ def test_workspace_size_formula():
 
 
 def test_auto_splits_cover_the_chip():
-    """The library's split choice gives ~2048 workgroups (8 per CU on 256 CUs)
-    for the gqa_8b layer, at most 512 tokens per chunk and at least 64."""
+    """The library's split choice aims at about one workgroup per CU (256 CUs),
+    at least two splits, and chunks of at least 256 tokens."""
     kvc, lib = _lib()
-    c = _desc(kvc, batch=16, n_kv_heads=8, max_len=2049, stride_t=128, stride_h=2049 * 128,
-              stride_b=8 * 2049 * 128)
-    s = lib.kvc_decode_splits(ctypes.byref(c), 32)
-    assert 16 * 8 * s >= 2048
-    assert -(-2049 // s) >= 64
+
+    def splits(batch, n_kv, n_q, max_len):
+        c = _desc(kvc, batch=batch, n_kv_heads=n_kv, max_len=max_len, stride_t=128,
+                  stride_h=max_len * 128, stride_b=n_kv * max_len * 128)
+        return lib.kvc_decode_splits(ctypes.byref(c), n_q)
+
+    assert splits(16, 8, 32, 2049) == 2          # 128 units of 4 heads
+    assert splits(1, 32, 32, 4097) == 8          # 32 single-head units
+    assert splits(32, 8, 64, 8193) == 2          # 256 units
+    assert splits(24, 32, 32, 6001) == 2         # 768 units
+    assert splits(1, 2, 4, 13) == 1              # short cache: one chunk
+    assert splits(1, 1, 1, 1 << 20) == 256       # capped at KVC_MAX_SPLITS
+    for args in [(16, 8, 32, 2049), (1, 32, 32, 4097), (2, 2, 4, 700)]:
+        s = splits(*args)
+        assert s == 1 or -(-args[3] // s) >= 256
 
 
 @pytest.mark.parametrize("call", ["append", "fill"])
