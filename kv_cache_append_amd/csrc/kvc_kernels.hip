@@ -42,6 +42,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- copies --
 
@@ -131,6 +132,11 @@ struct F16T {
   // q.k over this lane's 8 elements: four 2-way fp16 dot products, fp32 sum.
   // (The whole vector is bit-cast once: casting single lanes of the uint
   // vector inside a loop was compiled to four uses of lane 0.)
+  // C += A * B on 16x16x32 tiles; each lane passes its 8-element slices of A and B.
+  __device__ static inline f32x4 mfma16(const u32x4 a, const u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+  }
   __device__ static inline float dot(const u32x4 q, const u32x4 k, float d) {
     const half8_t a = __builtin_bit_cast(half8_t, q);
     const half8_t b = __builtin_bit_cast(half8_t, k);
@@ -160,6 +166,10 @@ struct BF16T {
     }
   }
   // q.k over this lane's 8 elements: four 2-way bf16 dot products, fp32 sum
+  __device__ static inline f32x4 mfma16(const u32x4 a, const u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  }
   __device__ static inline float dot(const u32x4 q, const u32x4 k, float d) {
     const bf16x8_t a = __builtin_bit_cast(bf16x8_t, q);
     const bf16x8_t b = __builtin_bit_cast(bf16x8_t, k);
@@ -236,6 +246,18 @@ __device__ inline float group_sum(float x) {
   if constexpr (W >= 32) x += __shfl_xor(x, 16);
   if constexpr (W >= 64) x += __shfl_xor(x, 32);
   return x;
+}
+
+// Maximum / sum over each aligned group of 16 lanes (a DPP row); every lane
+// of the group gets the result.
+__device__ inline float row16_max(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+__device__ inline float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
 // ------------------------------------------------------------ decode attn --
@@ -353,15 +375,28 @@ __device__ inline void buf_store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off
 #ifndef KVC_OCCUPANCY
 #define KVC_OCCUPANCY 4
 #endif
+#ifndef KVC_MFMA_PREFETCH
+#define KVC_MFMA_PREFETCH 2
+#endif
+#ifndef KVC_MFMA_OCCUPANCY
+#define KVC_MFMA_OCCUPANCY 2
+#endif
+
+// 16-bit caches whose rows are whole 32-element slices take the matrix-core
+// path (scores on 16x16x32 MFMA, and P.V on 4x4x1 MFMA for 4+ heads).
+template <typename ET, int D>
+constexpr bool decode_uses_mfma() { return ET::kBytes == 2 && D % 32 == 0; }
 
 // Workgroups each CU should hold at once, which sets the VGPR budget
-// (512 / workgroups per SIMD): 16-bit caches with up to 4 heads per
-// workgroup take KVC_OCCUPANCY; the others keep the compiler's default.
-template <typename ET, int GB>
-constexpr int decode_min_wgs() { return (ET::kBytes == 2 && GB <= 4) ? KVC_OCCUPANCY : 1; }
+// (512 / workgroups per SIMD).
+template <typename ET, int D, int GB>
+constexpr int decode_min_wgs() {
+  if constexpr (decode_uses_mfma<ET, D>()) return (GB > 4 || D > 128) ? 1 : KVC_MFMA_OCCUPANCY;
+  return (ET::kBytes == 2 && GB <= 4) ? KVC_OCCUPANCY : 1;
+}
 
 template <typename ET, int D, int GB>
-__global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void decode_kernel(const DecodeParams p) {
   constexpr int EPL = ET::kPerVec;        // elements per lane per row
   constexpr int LPR = D / EPL;            // lanes per row
   constexpr int RPP = 64 / LPR;           // rows per wave pass
@@ -376,8 +411,12 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
   constexpr float kEmpty = -1e30f;
   static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must split into 16-byte lane slices");
 
+  constexpr bool kMfma = decode_uses_mfma<ET, D>();
+  constexpr int NQ = (GB + 3) / 4;         // quads of query heads (matrix-core path)
+
   __shared__ float sm_a[NW][GB][D];
   __shared__ float sm_ml[NW][GB][2];
+  __shared__ float sm_p[kMfma ? NW : 1][16][4 * NQ];   // softmax weights, score layout -> V layout
   __shared__ uint32_t sm_ticket;
 
   // Workgroup ids go round-robin over the 8 XCDs (id mod 8). The head blocks
@@ -418,17 +457,6 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane / LPR;             // which row of the pass
   const int li = lane % LPR;              // which 16-byte slice of the row
-
-  u32x4 qv[GB];
-#pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    if (j < nh) {
-      qv[j] = *reinterpret_cast<const u32x4*>(p.q + ((static_cast<int64_t>(b) * p.n_q + h_first + j) * D + li * EPL) *
-                                                       ET::kBytes);
-    } else {
-      qv[j] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
 
   float ref[GB], l[GB], acc[GB][EPL];
 #pragma unroll
@@ -479,6 +507,216 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
   const uint32_t st = static_cast<uint32_t>(p.st);
   const char* kunit = p.k + unit_off;
   const char* vunit = p.v + unit_off;
+  const float sc = p.scale_log2;
+
+  if constexpr (kMfma) {
+    //------------------------------------------------------------------------
+    // Matrix-core path. A wave takes 16 consecutive rows per tile. Scores
+    // S[h][r] = q_h . K_r come from NM MFMAs 16x16x32 with q as A (row = head,
+    // lanes l%16) and K as B (column = row r = l%16): lane l loads 16 bytes,
+    // slice 4m + l/16, of row l%16 for the m-th MFMA, and q is loaded with the
+    // same slice order, so the sum runs over all D elements. Lane l then holds
+    // S[4(l/16) + t][l%16] in register t: the scores of row l%16 for heads
+    // 4(l/16)..+3. Padded heads (no query) and masked rows start from -inf in
+    // the accumulator, so their weights are exactly 0.
+    // The running reference is one value per head for the whole wave. The
+    // weights go through LDS to the row layout of V (LPR lanes per row, 16
+    // bytes each), where P.V runs on 4x4x1 MFMAs for 4+ heads (block b =
+    // lanes 4b..4b+3, all of one row: A = the weight of head 4q + l%4, B = V
+    // element e of lane l, C = the head quad's outputs for that column) or on
+    // the vector ALU for 1-2 heads.
+    constexpr int NM = D / 32;                // score MFMAs per tile
+    constexpr int NP = 16 / RPP;              // V row passes per tile
+    constexpr int TSM = NW * 16;              // rows per workgroup tile
+    constexpr int NBM = KVC_MFMA_PREFETCH + 1;
+    const int r16 = lane & 15;                // score row of this lane
+    const int kq = lane >> 4;                 // its slice group, and its head quad in the scores
+
+    u32x4 qa[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      qa[m] = u32x4{0u, 0u, 0u, 0u};
+      if (r16 < nh)
+        qa[m] = *reinterpret_cast<const u32x4*>(
+            p.q + ((static_cast<int64_t>(b) * p.n_q + h_first + r16) * D + (4 * m + kq) * EPL) * ET::kBytes);
+    }
+    float hbias[4];                           // 0 where (lane, register) is a real head's score
+#pragma unroll
+    for (int t = 0; t < 4; ++t) hbias[t] = (kq < NQ && 4 * kq + t < nh) ? 0.f : -INFINITY;
+    float refh[4 * NQ];                       // wave-uniform reference per head
+#pragma unroll
+    for (int h = 0; h < 4 * NQ; ++h) refh[h] = kEmpty;
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};    // per-lane sums, score layout
+    f32x4 accq[GB >= 4 ? NQ : 1][EPL];       // 4x4x1 outputs: register i = head 4q + i
+#pragma unroll
+    for (int q = 0; q < (GB >= 4 ? NQ : 1); ++q)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) accq[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t koff[NM], voffm[NP];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) koff[m] = static_cast<uint32_t>(r16) * st + static_cast<uint32_t>(4 * m + kq) * 16u;
+#pragma unroll
+    for (int u = 0; u < NP; ++u)
+      voffm[u] = static_cast<uint32_t>(u * RPP + grp) * st + static_cast<uint32_t>(li) * 16u;
+
+    auto load_tile = [&](int base_any, u32x4 (&K)[NM], u32x4 (&V)[NP]) {
+      const int base = __builtin_amdgcn_readfirstlane(base_any);
+      const int rows_left = t_end - base;
+      const uint32_t range = rows_left > 0 ? static_cast<uint32_t>(rows_left) * st : 0u;
+      const int64_t boff = static_cast<int64_t>(base) * st;
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr(kunit + boff), range);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr(vunit + boff), range);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) K[m] = buf_load(krs, koff[m]);
+#pragma unroll
+      for (int u = 0; u < NP; ++u) V[u] = buf_load(vrs, voffm[u]);
+    };
+
+    auto lane_ref = [&](int t) { return (NQ > 1 && kq == 1) ? refh[4 + t] : refh[t]; };
+
+    const f32x4 hb4 = f32x4{hbias[0], hbias[1], hbias[2], hbias[3]};
+    // rows_left: rows of this tile to attend (all 16 unless it is the last)
+    auto compute = [&](const u32x4 (&K)[NM], const u32x4 (&V)[NP], int rows_left) {
+      f32x4 sv = ET::mfma16(qa[0], K[0], hb4);
+#pragma unroll
+      for (int m = 1; m < NM; ++m) sv = ET::mfma16(qa[m], K[m], sv);
+      if (rows_left < 16) {                   // wave-uniform: only a last, partial tile
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sv[t] = r16 < rows_left ? sv[t] : -INFINITY;
+      }
+      float w[4], rl[4];
+      bool need = false;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        w[t] = sv[t] * sc;                    // log2-domain score
+        rl[t] = lane_ref(t);
+        need = need || (w[t] > rl[t] + kLazy);
+      }
+      if (__any(need)) {                      // wave-uniform, rarely taken after the first tile
+        float mx[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mx[t] = row16_max(w[t]);
+#pragma unroll
+        for (int h = 0; h < 4 * NQ; ++h) {
+          const float mh = lane_value(mx[h & 3], 16 * (h >> 2));
+          const float nr = mh > refh[h] + kLazy ? mh : refh[h];
+          const float c = fast_exp2(refh[h] - nr);   // 0 while the reference is still empty
+          refh[h] = nr;
+          if (kq == (h >> 2)) lsum[h & 3] *= c;
+          if constexpr (GB >= 4) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) accq[h >> 2][e][h & 3] *= c;
+          } else if (h < GB) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rl[t] = lane_ref(t);
+      }
+      f32x4 pw;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        pw[t] = fast_exp2(w[t] - rl[t]);
+        lsum[t] += pw[t];
+      }
+      if (kq < NQ) *reinterpret_cast<f32x4*>(&sm_p[wave][r16][4 * kq]) = pw;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int r = u * RPP + grp;          // row of this lane in pass u
+        float vf[EPL];
+        ET::unpack(V[u], vf);
+        if constexpr (GB >= 4) {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const float a = sm_p[wave][r][4 * q + (lane & 3)];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) accq[q][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, vf[e], accq[q][e], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < GB; ++j) {
+            const float a = sm_p[wave][r][j];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(a, vf[e], acc[j][e]);
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    {
+      int base = __builtin_amdgcn_readfirstlane(t0 + wave * 16);
+      const int n_tiles = base < t_end ? (t_end - base + TSM - 1) / TSM : 0;
+      if (n_tiles > 0) {
+        u32x4 KB[NBM][NM], VB[NBM][NP];
+#pragma unroll
+        for (int r = 0; r < NBM - 1; ++r) load_tile(base + r * TSM, KB[r], VB[r]);
+        bool done = false;
+        for (int it = 0; !done; it += NBM) {
+#pragma unroll
+          for (int r = 0; r < NBM; ++r) {     // unrolled: ring slots are compile-time
+            load_tile(base + (NBM - 1) * TSM, KB[(r + NBM - 1) % NBM], VB[(r + NBM - 1) % NBM]);
+            compute(KB[r], VB[r], __builtin_amdgcn_readfirstlane(t_end - base));
+            base += TSM;
+            if (it + r + 1 >= n_tiles) {
+              done = true;
+              break;
+            }
+          }
+        }
+      }
+    }
+    if (has_x && wave == 0) {                 // the last attended row, as row 0 of one more tile
+      u32x4 K[NM], V[NP];
+      const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : p.k + unit_off + static_cast<int64_t>(xrow) * p.st;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        K[m] = u32x4{0u, 0u, 0u, 0u};
+        if (r16 == 0) K[m] = *reinterpret_cast<const u32x4*>(kx + (4 * m + kq) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < NP; ++u) V[u] = (u == 0 && grp == 0) ? nv : u32x4{0u, 0u, 0u, 0u};
+      compute(K, V, 1);
+    }
+    // Wave totals in the common layout: one reference per head (the same in
+    // every lane), the weight sum in lane group 0 only (the lane-group merge
+    // below adds the groups), accumulators as acc[head][element].
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x = lsum[t];
+      x += dpp_f<kDppQuadXor1>(x);
+      x += dpp_f<kDppQuadXor2>(x);
+      x += dpp_f<kDppHalfMirror>(x);
+      lsum[t] = x + dpp_f<kDppMirror>(x);
+    }
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      ref[j] = refh[j];
+      const float lt = lane_value(lsum[j & 3], 16 * (j >> 2));
+      l[j] = grp == 0 ? lt : 0.f;
+      if constexpr (GB >= 4) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = accq[j >> 2][e][j & 3];
+      }
+    }
+  } else {
+  //--------------------------------------------------------------------------
+  // Vector-ALU path (fp32 caches, and rows that are not whole 32-element
+  // slices): every lane holds its 16-byte slice of q for each head of the
+  // block, and a row's LPR lanes reduce their partial dot products with DPP.
+  u32x4 qv[GB];
+#pragma unroll
+  for (int j = 0; j < GB; ++j) {
+    if (j < nh) {
+      qv[j] = *reinterpret_cast<const u32x4*>(p.q + ((static_cast<int64_t>(b) * p.n_q + h_first + j) * D + li * EPL) *
+                                                       ET::kBytes);
+    } else {
+      qv[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   uint32_t voff[U];
 #pragma unroll
   for (int u = 0; u < U; ++u)
@@ -504,7 +742,6 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
   // per-head masking (its K and V read as zero through the range check).
   // The order (all scores, then all weights, then V one row at a time) keeps
   // few temporaries live next to the buffered tiles.
-  const float sc = p.scale_log2;
   auto compute_rows = [&](const u32x4 (&K)[U], const u32x4 (&V)[U], const float (&bias)[U]) {
     float w[GB][U];
 #pragma unroll
@@ -596,11 +833,13 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, GB>())) void de
       bias[u] = (u == 0 && grp == 0) ? 0.f : -INFINITY;
     }
     compute_rows(K, V, bias);
-    if (x_new && hb == 0 && grp == 0) {        // fused append: write the new row
-      const int64_t coff = unit_off + static_cast<int64_t>(arow) * p.st + li * 16;
-      *reinterpret_cast<u32x4*>(p.k + coff) = nk;
-      *reinterpret_cast<u32x4*>(p.v + coff) = nv;
-    }
+  }
+  }   // vector-ALU path
+
+  if (has_x && wave == 0 && x_new && hb == 0 && grp == 0) {   // fused append: write the new row
+    const int64_t coff = unit_off + static_cast<int64_t>(arow) * p.st + li * 16;
+    *reinterpret_cast<u32x4*>(p.k + coff) = nk;
+    *reinterpret_cast<u32x4*>(p.v + coff) = nv;
   }
 
   // Merge the RPP lane groups of this wave (lanes li, li+LPR, li+2*LPR, ...).
