@@ -191,15 +191,25 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     return ms_total, wall, avg_launch_ms, avg_launch_bytes
 
 
+def _kernel_fingerprint() -> str:
+    """SHA-256 of the kernel source with comments and whitespace removed, so
+    that counter records stay tied to the code and not to its comments."""
+    import re
+    src = open(KERNEL_SOURCE).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = re.sub(r"\s+", " ", src).strip()
+    return hashlib.sha256(src.encode()).hexdigest()
+
+
 def _traffic(workload_name: str):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+    they were taken on the current kernel code; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_code_sha256") != _kernel_fingerprint():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -237,7 +247,7 @@ def _pmc_summary(fetch_csv: str, write_csv: str, out_path: str, args):
     rec = {
         "workload": args.config,
         "kernel": "decode_kernel",
-        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest(),
+        "kernel_code_sha256": _kernel_fingerprint(),
         "hbm_bytes_per_launch": int(round(fetch + write)),
         "fetch_bytes_per_launch": int(round(fetch)),
         "write_bytes_per_launch": int(round(write)),

@@ -65,6 +65,8 @@ typedef enum kvc_status {
 /* Bits OR-ed into the optional device status word (uint32_t). */
 #define KVC_DEVERR_CAPACITY 1u  /* a write or read would pass max_len: that sequence was skipped/clamped */
 #define KVC_DEVERR_BADLEN   2u  /* seq_lens[b] < 0: that sequence was skipped / treated as empty */
+#define KVC_DEVERR_SYNC     4u  /* a split merge gave up waiting for another workgroup (never expected;
+                                   the outputs of that call are not valid) */
 
 /*
  * One layer's preallocated cache: K and V each [batch, n_kv_heads, max_len,
@@ -134,12 +136,15 @@ kvc_status_t kvc_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens,
  * make). The bound holds for any seq_lens <= max_len. Returns 0 for invalid
  * arguments.
  *
- * Layout and lifetime: a region of uint32 tickets (one per sequence, KV head
- * and block of query heads), then fp32 per-split partial results. The caller
- * zero-fills the workspace ONCE after allocating it; every decode call leaves
- * the ticket region zero again, so the same workspace serves any number of
- * later calls (also with other shapes that fit) without clearing. Calls that
- * share a workspace must not run concurrently.
+ * Layout and lifetime: uint32 synchronisation words (a ticket per sequence,
+ * KV head and block of query heads, and a ready flag per such item and
+ * split), then fp32 per-split partial results. The caller zero-fills the
+ * workspace once after allocating it; every decode call leaves the
+ * synchronisation words zero again, so the workspace serves any number of
+ * later calls with the same batch, n_kv_heads, n_q_heads and split count
+ * (any lengths, any layer) without clearing. Where those change, the region
+ * layout moves: zero-fill the workspace again first (or keep one workspace
+ * per geometry). Calls that share a workspace must not run concurrently.
  */
 size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t n_splits);
 

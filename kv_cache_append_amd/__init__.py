@@ -22,6 +22,7 @@ KVC_F32, KVC_F16, KVC_BF16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: KVC_F32, torch.float16: KVC_F16, torch.bfloat16: KVC_BF16}
 DEVERR_CAPACITY = 1
 DEVERR_BADLEN = 2
+DEVERR_SYNC = 4
 
 STATUS = {
     0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_ALIGN",

@@ -86,12 +86,11 @@ int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads) {
   const int64_t units = static_cast<int64_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
   // Measured on MI355X (256 CUs): the fastest launches hold about one
   // workgroup per CU; more, shorter splits pay the per-workgroup start-up
-  // and merge more often than they gain. At least two splits, so that long
-  // sequences on few CUs still overlap two workgroups' streams.
+  // and the merge more often than they gain, and with 256 or more units one
+  // split (no merge) is fastest.
   const int64_t target_wgs = 256;
   const int64_t min_chunk = 256;          // tokens per workgroup at least
   int64_t s = (target_wgs + units - 1) / units;
-  if (s < 2) s = 2;
   int64_t cap = static_cast<int64_t>(c->max_len) / min_chunk;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
@@ -101,13 +100,17 @@ int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads) {
 
 static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-static size_t tickets_bytes(const kvc_cache_t* c, int32_t n_q_heads) {
-  const size_t units = static_cast<size_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
-  return round256(units * sizeof(uint32_t));
+static size_t sync_units(const kvc_cache_t* c, int32_t n_q_heads) {
+  return static_cast<size_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
 }
 
-size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t /*n_splits*/) {
-  return tickets_bytes(c, n_q_heads);
+size_t workspace_flag_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t /*n_splits*/) {
+  return round256(sync_units(c, n_q_heads) * sizeof(uint32_t));
+}
+
+size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
+  return workspace_flag_offset(c, n_q_heads, n_splits) +
+         round256(sync_units(c, n_q_heads) * static_cast<size_t>(n_splits) * sizeof(uint32_t));
 }
 
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {

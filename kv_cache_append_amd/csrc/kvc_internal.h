@@ -34,10 +34,12 @@ int head_blocks(int32_t group);
 // Sequence splits per (sequence, KV head, head block) when the caller passes 0.
 int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads);
 
-// Workspace: uint32 tickets [B * H_kv * head_blocks] (zero between calls),
-// then fp32 partial outputs [B, H_q, S, D], then fp32 (reference, sum) pairs
+// Workspace: uint32 tickets [B * H_kv * head_blocks], then uint32 ready
+// flags [B * H_kv * head_blocks, S] (both zero between calls), then fp32
+// partial outputs [B, H_q, S, D], then fp32 (reference, sum) pairs
 // [B, H_q, S, 2]; each region starts on a 256-byte boundary.
 size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
+size_t workspace_flag_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 

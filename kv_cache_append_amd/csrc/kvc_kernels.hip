@@ -10,23 +10,25 @@
 // kernel is organised around streaming K/V exactly once, in one launch:
 //   * the T axis of every (sequence, KV head) is cut into n_splits chunks,
 //     one 256-thread workgroup per chunk (and per block of <= 8 query heads);
-//   * within a wave, each cache row of D elements is read by LPR = D*s/16
-//     lanes with one 16-byte load each, so one wave-wide load covers 64/LPR
-//     whole rows of contiguous memory (fully coalesced); the next tile's rows
-//     are loaded while the current tile is computed (register double buffer);
-//   * every lane keeps the q slices of all query heads of its GQA group in
-//     registers, so each K/V row is fetched once and used by all of them
-//     (course notes §3.4: query head j reads KV head floor(j/(h/G)); no copy);
-//   * q.k uses the 2-way dot-product instructions for 16-bit caches; partial
-//     dot products are reduced across the LPR lanes of a row with DPP;
+//   * K/V tiles are read through buffer resources whose range ends at the
+//     last row to stream (rows past it read as zero), with a register ring
+//     keeping the next tiles' loads in flight;
+//   * every K/V row is fetched once for all query heads of its group (course
+//     notes §3.4: query head j reads KV head floor(j/(h/G)); no copy);
+//   * 16-bit caches run on the matrix cores: 16 rows x (up to) 16 heads of
+//     scores per v_mfma_f32_16x16x32 chain, weights through LDS to the row
+//     layout of V, and P.V on v_mfma_f32_4x4x1_16b_f32 (fp32 weights) for
+//     4+ heads; fp32 caches take a vector-ALU path with 2-way dot products
+//     and DPP reductions;
 //   * the softmax is online in the log2 domain with a lazily moved reference:
-//     the running reference only moves when a score exceeds it by more than
-//     2^8, so the accumulators are rarely rescaled (exact in real arithmetic,
-//     bounded exponentials in fp32);
+//     it only moves when a score exceeds it by more than 2^8, so the
+//     accumulators are rarely rescaled (exact in real arithmetic, bounded
+//     exponentials in fp32);
 //   * each workgroup's partial (reference, sum, unnormalised output) goes to
-//     the workspace; the last workgroup of a (sequence, KV head) to finish,
-//     found with a device-scope atomic ticket, merges the partials and writes
-//     the normalised output, then resets its ticket to zero;
+//     the workspace; the last workgroup of a (sequence, KV head) to arrive,
+//     found with a device-scope atomic ticket, merges the partials in split
+//     order (bit-identical results whatever the arrival order) and writes the
+//     normalised output, then leaves the ticket and flags at zero;
 //   * kvc_decode_step additionally takes the step's k_t, v_t: the workgroup
 //     whose chunk holds slot T_b reads that row from k_t/v_t and writes it
 //     into the cache, so append and attention share the launch.
@@ -272,6 +274,7 @@ struct DecodeParams {
   const char* v_new;
   int64_t nsb, nsh;            // its strides in bytes
   uint32_t* ws_cnt;            // [B * H_kv * n_hblk] tickets, zero between calls
+  uint32_t* ws_flag;           // [B * H_kv * n_hblk, S] ready flags, zero between calls
   float* ws_o;                 // [B, H_q, S, D]
   float* ws_ml;                // [B, H_q, S, 2]
   void* out;                   // [B, H_q, D]
@@ -409,12 +412,18 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   // of a masked (-inf) score is exp2(-inf) = 0 rather than NaN, and far
   // below any finite score, so exp2(kEmpty - ref) is 0 once a row is seen.
   constexpr float kEmpty = -1e30f;
+  constexpr int kMaxSpins = 1 << 20;      // bound on the merge's wait for ready flags
   static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must split into 16-byte lane slices");
 
   constexpr bool kMfma = decode_uses_mfma<ET, D>();
   constexpr int NQ = (GB + 3) / 4;         // quads of query heads (matrix-core path)
 
-  __shared__ float sm_a[NW][GB][D];
+  // Matrix-core path with up to 4 heads: one softmax reference per wave, so
+  // the wave's lane groups are summed through LDS (32 KB at most) instead of
+  // merged with cross-lane shuffles.
+  constexpr bool kLdsMerge = kMfma && GB <= 4;
+  __shared__ float sm_a[kLdsMerge ? 1 : NW][GB][D];
+  __shared__ float sm_acc[kLdsMerge ? NW : 1][kLdsMerge ? RPP : 1][GB][kLdsMerge ? D : 1];
   __shared__ float sm_ml[NW][GB][2];
   __shared__ float sm_p[kMfma ? NW : 1][16][4 * NQ];   // softmax weights, score layout -> V layout
   __shared__ uint32_t sm_ticket;
@@ -842,6 +851,21 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     *reinterpret_cast<u32x4*>(p.v + coff) = nv;
   }
 
+  if constexpr (kLdsMerge) {
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<f32x4*>(&sm_acc[wave][grp][j][li * EPL + e]) =
+            f32x4{acc[j][e], acc[j][e + 1], acc[j][e + 2], acc[j][e + 3]};
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < GB; ++j) {
+        sm_ml[wave][j][0] = ref[j];
+        sm_ml[wave][j][1] = l[j];
+      }
+    }
+  } else {
   // Merge the RPP lane groups of this wave (lanes li, li+LPR, li+2*LPR, ...).
 #pragma unroll
   for (int off = LPR; off < 64; off *= 2) {
@@ -866,72 +890,139 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       }
     }
   }
+  }
   __syncthreads();
 
-  // Merge the NW waves, four output columns per thread. A single active
-  // split writes the normalised output directly; otherwise the partial goes
-  // to the workspace with device-coherent 16-byte stores.
-  const int64_t prow0 = (static_cast<int64_t>(b) * p.n_q + h_first) * p.n_splits;
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(nh * p.n_splits * D * 4));
-  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(nh * p.n_splits * 2 * 4));
-  for (int t = threadIdx.x; t < nh * D4; t += blockDim.x) {
+  // Merge the NW waves: each thread takes (head, four output columns) items.
+  constexpr int TPT = (GB * D4 + NW * 64 - 1) / (NW * 64);   // items per thread
+  float aa[TPT][4], rv[TPT], lv[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int t = threadIdx.x + i * NW * 64;
     const int j = t / D4;
     const int d = (t - j * D4) * 4;
+    rv[i] = kEmpty;
+    lv[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) aa[i][e] = 0.f;
+    if (t >= nh * D4) continue;
     float rr = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) rr = fmaxf(rr, sm_ml[w][j][0]);
-    float ll = 0.f, aa[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float rw = sm_ml[w][j][0];
       const float c = (rw == -INFINITY) ? 0.f : fast_exp2(rw - rr);
-      ll += sm_ml[w][j][1] * c;
+      lv[i] += sm_ml[w][j][1] * c;
+      if constexpr (kLdsMerge) {
+        f32x4 sg = *reinterpret_cast<const f32x4*>(&sm_acc[w][0][j][d]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) aa[e] += sm_a[w][j][d + e] * c;
-    }
-    if (ns == 1) {
-      const float inv = 1.f / ll;
+        for (int g2 = 1; g2 < RPP; ++g2) sg += *reinterpret_cast<const f32x4*>(&sm_acc[w][g2][j][d]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out<ET>(p, orow0 + j * D + d + e, aa[e] * inv);
-    } else {
-      const uint32_t row = static_cast<uint32_t>(j * p.n_splits + split);
-      buf_store_coherent(ors, (row * D + d) * 4u,
-                         u32x4{__float_as_uint(aa[0]), __float_as_uint(aa[1]), __float_as_uint(aa[2]),
-                               __float_as_uint(aa[3])});
-      if (d == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rr), mrs, static_cast<int>(row * 8u), 0, kCoherent);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ll), mrs, static_cast<int>(row * 8u + 4u), 0,
-                                              kCoherent);
+        for (int e = 0; e < 4; ++e) aa[i][e] += sg[e] * c;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) aa[i][e] += sm_a[w][j][d + e] * c;
       }
     }
+    rv[i] = rr;
   }
-  if (ns == 1) return;
+  auto write_out = [&]() {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int t = threadIdx.x + i * NW * 64;
+      if (t >= nh * D4) continue;
+      const int j = t / D4;
+      const int d = (t - j * D4) * 4;
+      const float inv = 1.f / lv[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out<ET>(p, orow0 + j * D + d + e, aa[i][e] * inv);
+    }
+  };
+  if (ns == 1) {                                   // a single active split: done
+    write_out();
+    return;
+  }
 
-  // Last-arriving workgroup of this (sequence, KV head, head block) merges.
-  // The partials were written with device-coherent (write-through) stores;
-  // waiting for their completion before the ticket is taken orders them
-  // before it, and the merging workgroup reads them with device-coherent
-  // loads, so no L2 write-back or invalidate is needed.
+  // Several splits. Every workgroup publishes its partial (reference, sum,
+  // unnormalised output) with device-coherent stores and takes a ticket
+  // (agent-scope atomic); the last to arrive merges. With two splits the
+  // ticket is taken in the same round trip as the stores, so the workgroup
+  // that is not last raises its split's ready flag once its stores have
+  // completed, and the last one waits for that flag (raised by a workgroup
+  // that already holds a ticket, so the wait is short and bounded). With
+  // more splits, which tend to arrive together, the ticket is taken after
+  // the stores complete, so the last ticket implies every partial is in
+  // place. The merging workgroup folds the partials in with device-coherent
+  // loads, writes the output, and leaves the ticket and the flags at zero
+  // for the next call.
+  const bool early_ticket = ns == 2;
+  const int64_t item = static_cast<int64_t>(unit) * p.n_hblk + hb;
+  uint32_t* ticket = p.ws_cnt + item;
+  uint32_t* flags = p.ws_flag + item * p.n_splits;
+  const int64_t prow0 = (static_cast<int64_t>(b) * p.n_q + h_first) * p.n_splits;
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(nh * p.n_splits * D * 4));
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(nh * p.n_splits * 2 * 4));
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int t = threadIdx.x + i * NW * 64;
+    if (t >= nh * D4) continue;
+    const int j = t / D4;
+    const int d = (t - j * D4) * 4;
+    const uint32_t row = static_cast<uint32_t>(j * p.n_splits + split);
+    buf_store_coherent(ors, (row * D + d) * 4u,
+                       u32x4{__float_as_uint(aa[i][0]), __float_as_uint(aa[i][1]), __float_as_uint(aa[i][2]),
+                             __float_as_uint(aa[i][3])});
+    if (d == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rv[i]), mrs, static_cast<int>(row * 8u), 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv[i]), mrs, static_cast<int>(row * 8u + 4u), 0,
+                                            kCoherent);
+    }
+  }
+  if (early_ticket && threadIdx.x == 0)
+    sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  uint32_t* ticket = p.ws_cnt + static_cast<int64_t>(unit) * p.n_hblk + hb;
-  if (threadIdx.x == 0) sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!early_ticket) {
+    if (threadIdx.x == 0) sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
+  if (sm_ticket != static_cast<uint32_t>(ns - 1)) {
+    if (early_ticket && threadIdx.x == 0)
+      __hip_atomic_store(flags + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+
+  // Last to arrive: with two splits, wait for the other split's flag.
+  for (int k = threadIdx.x; early_ticket && k < ns; k += blockDim.x) {
+    if (k == split) continue;
+    int spins = 0;
+    while (__hip_atomic_load(flags + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (++spins > kMaxSpins) {                 // never expected: flag the call, do not hang
+        if (p.status != nullptr) atomicOr(p.status, KVC_DEVERR_SYNC);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
   __syncthreads();
-  if (sm_ticket != static_cast<uint32_t>(ns - 1)) return;
-  // Each thread merges four output columns of one head over all splits,
-  // eight splits per round trip: their (reference, sum) pairs and partial
-  // outputs are requested together, then folded in with a running reference.
-  for (int t = threadIdx.x; t < nh * D4; t += blockDim.x) {
+  // Fold all splits in split order, eight per round trip, this workgroup's own
+  // split taken from registers (the bits it would have stored), so the result
+  // does not depend on which split arrived last. The other splits' (reference,
+  // sum) pairs and partial outputs are requested together (unconditional
+  // loads: rows past the split count read another head's data or, past the
+  // region, zeros, and are weighted 0), then merged with a running reference.
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int t = threadIdx.x + i * NW * 64;
+    if (t >= nh * D4) continue;
     const int j = t / D4;
     const int d = (t - j * D4) * 4;
     const uint32_t row0 = static_cast<uint32_t>(j * p.n_splits);
-    float mm = -INFINITY, ll = 0.f, aa[4] = {0.f, 0.f, 0.f, 0.f};
+    float mm = -INFINITY, ll = 0.f, am[4] = {0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < ns; i0 += 8) {
-      const int cnt = min(8, ns - i0);
       float rb[8], lb[8];
       u32x4 ob[8];
-      // unconditional loads (rows past the split count read another head's
-      // data or, past the region, zeros) so that all 24 are in flight at once
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const uint32_t row = row0 + static_cast<uint32_t>(i0 + k);
@@ -941,29 +1032,42 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
             __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u + 4u), 0, kCoherent)));
         ob[k] = buf_load_coherent(ors, (row * D + d) * 4u);
       }
+      bool use[8];
       float bm = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) bm = k < cnt ? fmaxf(bm, rb[k]) : bm;
+      for (int k = 0; k < 8; ++k) {
+        use[k] = i0 + k < ns;
+        if (i0 + k == split) {                 // own split: from registers
+          rb[k] = rv[i];
+          lb[k] = lv[i];
+          ob[k] = u32x4{__float_as_uint(aa[i][0]), __float_as_uint(aa[i][1]), __float_as_uint(aa[i][2]),
+                        __float_as_uint(aa[i][3])};
+        }
+        bm = use[k] ? fmaxf(bm, rb[k]) : bm;
+      }
       const float nm = fmaxf(mm, bm);
       const float c = (mm == -INFINITY) ? 0.f : fast_exp2(mm - nm);
       ll *= c;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) aa[e] *= c;
+      for (int e = 0; e < 4; ++e) am[e] *= c;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float w = k < cnt ? fast_exp2(rb[k] - nm) : 0.f;
-        ll = fmaf(k < cnt ? lb[k] : 0.f, w, ll);
+        const float w = use[k] ? fast_exp2(rb[k] - nm) : 0.f;
+        ll = fmaf(use[k] ? lb[k] : 0.f, w, ll);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) aa[e] = fmaf(k < cnt ? __uint_as_float(ob[k][e]) : 0.f, w, aa[e]);
+        for (int e = 0; e < 4; ++e) am[e] = fmaf(use[k] ? __uint_as_float(ob[k][e]) : 0.f, w, am[e]);
       }
       mm = nm;
     }
-    const float inv = 1.f / ll;
+    lv[i] = ll;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out<ET>(p, orow0 + j * D + d + e, aa[e] * inv);
+    for (int e = 0; e < 4; ++e) aa[i][e] = am[e];
   }
-  if (threadIdx.x == 0)   // ready for the next call on this workspace
-    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  write_out();
+  // ready for the next call on this workspace
+  for (int k = threadIdx.x; early_ticket && k < ns; k += blockDim.x)
+    if (k != split) __hip_atomic_store(flags + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------- dispatch --
@@ -1094,6 +1198,7 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.nsh = new_stride_h * s;
   char* ws = static_cast<char*>(workspace);
   p.ws_cnt = reinterpret_cast<uint32_t*>(ws);
+  p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(cache, n_q_heads, splits));
   p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(cache, n_q_heads, splits));
   p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(cache, n_q_heads, splits));
   p.out = out;

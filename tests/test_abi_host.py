@@ -128,13 +128,15 @@ def test_decode_validation_gqa_workspace_unsupported():
 
 
 def test_workspace_size_formula():
-    """Workspace = uint32 tickets [B * H_kv * head blocks] + fp32 partial outputs
-    [B, H_q, S, D] + (reference, sum) pairs, each region rounded to 256 bytes."""
+    """Workspace = uint32 tickets [B * H_kv * head blocks] + uint32 ready flags
+    [B * H_kv * head blocks, S] + fp32 partial outputs [B, H_q, S, D] +
+    (reference, sum) pairs, each region rounded up to 256 bytes."""
     kvc, lib = _lib()
     c = _desc(kvc)
-    for s in (1, 3, 16):
+    for s in (1, 3, 16, 100):
         rows = 2 * 4 * s
-        want = 256 + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+        flags = -(-2 * 2 * s * 4 // 256) * 256
+        want = 256 + flags + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
         assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, s) == want
     auto = lib.kvc_decode_splits(ctypes.byref(c), 4)
     assert auto >= 1
@@ -145,7 +147,7 @@ def test_workspace_size_formula():
 
 def test_auto_splits_cover_the_chip():
     """The library's split choice aims at about one workgroup per CU (256 CUs),
-    at least two splits, and chunks of at least 256 tokens."""
+    with chunks of at least 256 tokens."""
     kvc, lib = _lib()
 
     def splits(batch, n_kv, n_q, max_len):
@@ -155,8 +157,8 @@ def test_auto_splits_cover_the_chip():
 
     assert splits(16, 8, 32, 2049) == 2          # 128 units of 4 heads
     assert splits(1, 32, 32, 4097) == 8          # 32 single-head units
-    assert splits(32, 8, 64, 8193) == 2          # 256 units
-    assert splits(24, 32, 32, 6001) == 2         # 768 units
+    assert splits(32, 8, 64, 8193) == 1          # 256 units
+    assert splits(24, 32, 32, 6001) == 1         # 768 units
     assert splits(1, 2, 4, 13) == 1              # short cache: one chunk
     assert splits(1, 1, 1, 1 << 20) == 256       # capped at KVC_MAX_SPLITS
     for args in [(16, 8, 32, 2049), (1, 32, 32, 4097), (2, 2, 4, 700)]:

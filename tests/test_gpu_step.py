@@ -84,13 +84,15 @@ def test_many_steps_many_layers_one_workspace(gpu):
 
 
 def test_workspace_reused_across_shapes(gpu):
-    """A workspace sized for the larger of two shapes serves both, alternately."""
+    """A workspace sized for the larger of two shapes serves both, alternately,
+    when it is zero-filled again at each change of geometry."""
     big = DecodeCase(batch=6, n_q=32, n_kv=8, head_dim=128, dtype="fp16", lengths=[700] * 6, tag="wsbig")
     small = DecodeCase(batch=2, n_q=4, n_kv=1, head_dim=128, dtype="fp16", lengths=[90, 2000], tag="wssmall")
     n = max(kvc.decode_workspace_bytes(big.k, big.v, 32), kvc.decode_workspace_bytes(small.k, small.v, 4))
     ws = torch.zeros(n, dtype=torch.uint8, device=gpu)
     for rep in range(3):
         for c, hq in ((big, 32), (small, 4)):
+            ws.zero_()
             out = torch.empty((c.batch, hq, 128), device=gpu)
             kvc.decode_attn(c.k, c.v, c.seq_lens, c.q, out, ws, n_pending=0)
             torch.cuda.synchronize()
