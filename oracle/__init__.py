@@ -24,6 +24,7 @@ from .kvc_oracle import (  # noqa: F401
     append,
     cache_bytes,
     causal_attention,
+    chunk_attention,
     concat_append_positions,
     decode_attention,
     kv_head_of,

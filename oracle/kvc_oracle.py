@@ -131,6 +131,46 @@ def decode_attention(q, k_cache, v_cache, seq_lens, n_pending: int = 1, scale=No
     return out
 
 
+def chunk_attention(q, k_cache, v_cache, seq_lens, scale=None):
+    """Several new queries per sequence attending the cache, in fp64.
+
+    A prefill chunk or a speculative verify step: T new tokens have been
+    appended after seq_lens[b] cached ones, and each of their queries attends
+    with the causal mask aligned to the lower right. [W1D4 §3.3] masks: a
+    block of T queries against S keys sees keys 0..S - T + i for query i
+    (a top-left alignment, as SDPA's is_causal uses, would hide cached keys
+    from the block). With T = 1 this is the single-query decode of
+    [LA11 §2.2]; with nothing cached before the block it is the full causal
+    prefill of [KVG] path A. Scale and GQA grouping as in decode_attention.
+
+    q: [B, T, H_q, D] (token-major, as a chunk's projections come out);
+    caches [B, H_kv, T_max, D] already holding the block's rows at slots
+    [seq_lens[b], seq_lens[b] + T). Query i of sequence b attends slots
+    0..seq_lens[b] + i with the two-pass softmax. Returns fp64 [B, T, H_q, D].
+    """
+    q = widen(q)
+    k = widen(k_cache)
+    v = widen(v_cache)
+    batch, t_q, n_q, d = q.shape
+    n_kv, t_max = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((batch, t_q, n_q, d), dtype=np.float64)
+    for b in range(batch):
+        base = int(seq_lens[b])
+        if base < 0 or base + t_q > t_max:
+            raise ValueError(f"sequence {b}: block [{base}, {base + t_q}) does not fit a cache of {t_max}")
+        for i in range(t_q):
+            n = base + i + 1                          # keys 0 .. seq_lens[b] + i
+            for h in range(n_q):
+                g = kv_head_of(h, n_q, n_kv)
+                scores = (k[b, g, :n, :] @ q[b, i, h]) * scale
+                m = scores.max()
+                e = np.exp(scores - m)
+                out[b, i, h] = (e @ v[b, g, :n, :]) / e.sum()
+    return out
+
+
 def causal_attention(q, k, v, n_q_heads: int, n_kv_heads: int, scale=None):
     """Full causal self-attention over a prefix ("path A" of [KVG]).
 

@@ -370,3 +370,106 @@ def test_prefill_plus_decode_equals_full_forward(n_kv):
     out_a, _ = oracle.toy_path_a(x, wq, wk, wv, wo, 8, n_kv, cfg.head_dim, 8)
     out_b, _, _, _ = oracle.toy_path_b(x, wq, wk, wv, wo, 8, n_kv, cfg.head_dim, 8)
     assert np.abs(out_a - out_b).max() < 5e-14
+
+
+# ------------------------------------------- multi-query block (lower right) --
+
+def _block_inputs(seed, b, t_q, hq, hkv, t_max, d):
+    q = _rand((b, t_q, hq, d), seed, "cq", t_q).double()
+    k = _rand((b, hkv, t_max, d), seed, "ck", t_q).double()
+    v = _rand((b, hkv, t_max, d), seed, "cv", t_q).double()
+    return q, k, v
+
+
+@pytest.mark.parametrize("hq,hkv,t_q", [(4, 4, 3), (8, 2, 5), (8, 1, 2), (6, 3, 7)])
+def test_chunk_attention_matches_sdpa_with_lower_right_mask(hq, hkv, t_q):
+    """Library pin: W1D4 §3.3's mask for a block of T queries against S keys is
+    ones(T, S).tril(S - T); torch SDPA (fp64, enable_gqa) with that boolean
+    mask, per sequence over its S = seq_lens[b] + T keys."""
+    b, t_max, d = 3, 40, 16
+    q, k, v = _block_inputs(30, b, t_q, hq, hkv, t_max, d)
+    lens = np.array([0, 11, t_max - t_q])
+    got = oracle.chunk_attention(q, k, v, lens)
+    for i in range(b):
+        s = int(lens[i]) + t_q
+        mask = torch.ones(t_q, s, dtype=torch.bool).tril(s - t_q)
+        ref = F.scaled_dot_product_attention(q[i:i + 1].transpose(1, 2), k[i:i + 1, :, :s], v[i:i + 1, :, :s],
+                                             attn_mask=mask, enable_gqa=True)[0].transpose(0, 1).numpy()
+        assert np.abs(got[i] - ref).max() < 1e-13
+
+
+def test_chunk_attention_with_one_query_is_decode():
+    """T = 1 reduces to the single-query decode with the new token appended
+    (LA11 §2.2), which the SDPA and closed-form pins above fix."""
+    b, hq, hkv, t_max, d = 2, 8, 2, 30, 16
+    q, k, v = _block_inputs(31, b, 1, hq, hkv, t_max, d)
+    lens = np.array([5, 29])
+    got = oracle.chunk_attention(q, k, v, lens)[:, 0]
+    ref = oracle.decode_attention(q[:, 0], k, v, lens, n_pending=1)
+    assert np.abs(got - ref).max() < 1e-15
+
+
+def test_chunk_attention_with_empty_cache_is_causal_prefill():
+    """Nothing cached before the block: the full causal prefill of KVG path A
+    (and SDPA is_causal, since T_q == T_k there)."""
+    hq, hkv, t, d = 4, 2, 13, 8
+    q, k, v = _block_inputs(32, 1, t, hq, hkv, t, d)
+    got = oracle.chunk_attention(q, k, v, np.array([0]))[0]          # [T, H_q, D]
+    ref = oracle.causal_attention(q[0].transpose(0, 1), k[0], v[0], hq, hkv)
+    assert np.abs(got - ref.transpose(1, 0, 2)).max() < 1e-14
+    sd = F.scaled_dot_product_attention(q.transpose(1, 2), k, v, is_causal=True, enable_gqa=True)[0]
+    assert np.abs(got - sd.transpose(0, 1).numpy()).max() < 1e-13
+
+
+def test_chunked_prefill_equals_one_shot_prefill():
+    """W1D4 §3.5, first must-pass test, chunked variant: a prompt prefilled in
+    blocks (each attending the cache plus itself with the lower-right mask)
+    gives the same rows as one causal prefill of the whole prompt."""
+    hq, hkv, t, d = 8, 2, 23, 16
+    q, k, v = _block_inputs(33, 1, t, hq, hkv, t, d)
+    whole = oracle.chunk_attention(q, k, v, np.array([0]))
+    pieces, start = [], 0
+    for size in (5, 1, 9, 8):
+        pieces.append(oracle.chunk_attention(q[:, start:start + size], k, v, np.array([start])))
+        start += size
+    assert np.abs(np.concatenate(pieces, axis=1) - whole).max() < 1e-14
+
+
+def test_top_left_mask_is_wrong_for_a_cached_block():
+    """W1D4 §3.3: with cached keys, SDPA is_causal=True (top-left) hides the
+    cache from the block's early queries; the lower-right result differs."""
+    hq, t_q, s, d = 2, 3, 10, 8
+    q, k, v = _block_inputs(34, 1, t_q, hq, hq, s, d)
+    good = oracle.chunk_attention(q, k, v, np.array([s - t_q]))[0]
+    top_left = F.scaled_dot_product_attention(q.transpose(1, 2), k, v, is_causal=True)[0].transpose(0, 1).numpy()
+    assert np.abs(top_left[0] - v[0, :, 0].numpy()).max() < 1e-15    # query 0 sees only key 0
+    assert np.abs(good - top_left).max() > 1e-2
+
+
+def test_chunk_attention_mpmath_fifty_digits():
+    """Brute force at 50 digits on a tiny block: query i of the block sees keys
+    0..S-T+i."""
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    hq, hkv, t_q, base, d = 2, 1, 3, 4, 4
+    q, k, v = _block_inputs(35, 1, t_q, hq, hkv, base + t_q, d)
+    q, k, v = oracle.widen(q), oracle.widen(k), oracle.widen(v)
+    got = oracle.chunk_attention(q, k, v, np.array([base]))
+    for i in range(t_q):
+        n = base + i + 1
+        for h in range(hq):
+            s = [mpmath.fsum(mpmath.mpf(q[0, i, h, c]) * mpmath.mpf(k[0, 0, j, c]) for c in range(d)) / mpmath.sqrt(d)
+                 for j in range(n)]
+            w = [mpmath.exp(x) for x in s]
+            z = mpmath.fsum(w)
+            for c in range(d):
+                o = mpmath.fsum(w[j] * mpmath.mpf(v[0, 0, j, c]) for j in range(n)) / z
+                assert abs(float(o) - got[0, i, h, c]) < 1e-14
+
+
+def test_chunk_attention_rejects_blocks_that_do_not_fit():
+    q, k, v = _block_inputs(36, 1, 4, 2, 2, 10, 4)
+    with pytest.raises(ValueError):
+        oracle.chunk_attention(q, k, v, np.array([7]))
+    with pytest.raises(ValueError):
+        oracle.chunk_attention(q, k, v, np.array([-1]))

@@ -91,3 +91,52 @@ def test_append_to_wrong_slot_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "append", off_by_one)
     with pytest.raises(AssertionError):
         pins.test_append_writes_one_slot_bitwise_and_nothing_else()
+
+
+def _mutant_chunk(kind):
+    def chunk(q, k_cache, v_cache, seq_lens, scale=None):
+        q, k, v = ko.widen(q), ko.widen(k_cache), ko.widen(v_cache)
+        batch, t_q, n_q, d = q.shape
+        n_kv = k.shape[1]
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        out = np.zeros((batch, t_q, n_q, d))
+        for b in range(batch):
+            base = int(seq_lens[b])
+            for i in range(t_q):
+                if kind == "top_left":
+                    n = i + 1
+                elif kind == "sees_next":
+                    n = min(base + i + 2, base + t_q)
+                elif kind == "misses_self":
+                    n = base + i
+                else:   # "whole_block": no mask inside the block
+                    n = base + t_q
+                if n <= 0:
+                    continue
+                for h in range(n_q):
+                    g = h // (n_q // n_kv)
+                    s = (k[b, g, :n] @ q[b, i, h]) * scale
+                    e = np.exp(s - s.max())
+                    out[b, i, h] = (e @ v[b, g, :n]) / e.sum()
+        return out
+    return chunk
+
+
+CHUNK_PINS = [
+    lambda: pins.test_chunk_attention_matches_sdpa_with_lower_right_mask(8, 2, 5),
+    pins.test_chunked_prefill_equals_one_shot_prefill,
+    pins.test_chunk_attention_with_empty_cache_is_causal_prefill,
+]
+
+
+@pytest.mark.parametrize("kind", ["top_left", "sees_next", "misses_self", "whole_block"])
+def test_chunk_mask_mutants_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "chunk_attention", _mutant_chunk(kind))
+    monkeypatch.setattr(ko, "chunk_attention", _mutant_chunk(kind))
+    caught = 0
+    for pin in CHUNK_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"no pin caught mutant {kind}"
