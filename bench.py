@@ -40,6 +40,9 @@ def _parse():
     ap.add_argument("--secondary", default="ragged_long",
                     help="second workload measured in the same run ('none' to skip)")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = library choice)")
+    ap.add_argument("--block-q", type=int, default=0,
+                    help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
+                         "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -58,12 +61,13 @@ class Workload:
     """All L layers of one decode step, resident in HBM, with pre-marshalled
     C-ABI arguments (so the timed loop does no Python-side tensor work)."""
 
-    def __init__(self, cfg, margin_tokens: int, seed: int, splits: int):
+    def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0):
         import torch
         import kv_cache_append_amd as kvc
         import synth
 
         self.cfg = cfg
+        self.block_q = block_q        # 0: decode step; N: block of N new tokens per sequence
         self.kvc = kvc
         self.lib = kvc.load()
         dev = torch.device("cuda:0")
@@ -76,17 +80,22 @@ class Workload:
         for l in range(L):  # fill layer by layer (bounded fp32 temporaries)
             synth.normal(None, cfg.dtype, seed, cfg.name, l, "K", out=self.k[l])
             synth.normal(None, cfg.dtype, seed, cfg.name, l, "V", out=self.v[l])
-        self.q = torch.stack([synth.normal((B, Hq, D), cfg.dtype, seed, cfg.name, l, "q", device=dev)
-                              for l in range(L)])
-        self.k_new = torch.stack([synth.normal((B, Hkv, D), cfg.dtype, seed, cfg.name, l, "k_new", device=dev)
+        nq = max(block_q, 1)
+        qs = (B, block_q, Hq, D) if block_q else (B, Hq, D)
+        ks = (B, Hkv, block_q, D) if block_q else (B, Hkv, D)
+        self.q = torch.stack([synth.normal(qs, cfg.dtype, seed, cfg.name, l, "q", device=dev) for l in range(L)])
+        self.k_new = torch.stack([synth.normal(ks, cfg.dtype, seed, cfg.name, l, "k_new", device=dev)
                                   for l in range(L)])
-        self.v_new = torch.stack([synth.normal((B, Hkv, D), cfg.dtype, seed, cfg.name, l, "v_new", device=dev)
+        self.v_new = torch.stack([synth.normal(ks, cfg.dtype, seed, cfg.name, l, "v_new", device=dev)
                                   for l in range(L)])
-        self.out = torch.empty((L, B, Hq, D), dtype=torch.float32, device=dev)
+        self.out = torch.empty((L,) + qs, dtype=torch.float32, device=dev)
         self.seq_lens = self.lengths.to(dev)
         self.descs = [kvc.cache_desc(self.k[l], self.v[l]) for l in range(L)]
-        self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq)
-        self.ws = kvc.workspace(self.k[0], self.v[0], Hq, self.splits)
+        self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq * nq)
+        if block_q:
+            self.ws = kvc.block_workspace(self.k[0], self.v[0], Hq, block_q, self.splits)
+        else:
+            self.ws = kvc.workspace(self.k[0], self.v[0], Hq, self.splits)
         self.scale = ctypes.c_float(1.0 / math.sqrt(D))
         torch.cuda.synchronize()
 
@@ -101,6 +110,18 @@ class Workload:
         ws, wsb = vp(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel())
         sb, sh = self.k_new.stride(1), self.k_new.stride(2)
         st = vp(stream_handle)
+        if self.block_q:
+            n = self.block_q
+            ks = self.k_new.stride()
+            for l in range(cfg.n_layers):
+                d = ctypes.byref(self.descs[l])
+                rc = lib.kvc_prefill_fill(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()),
+                                          ks[1], ks[2], ks[3], n, None, st)
+                rc = rc or lib.kvc_block_attn(d, seq, n, vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
+                                              vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
+                if rc:
+                    raise RuntimeError(f"libkvc returned {rc} at layer {l}")
+            return
         for l in range(cfg.n_layers):
             d = ctypes.byref(self.descs[l])
             rc = lib.kvc_decode_step(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
@@ -113,20 +134,21 @@ class Workload:
         """Enqueue one decode step: every layer, then seq_lens += 1."""
         self.layers(stream_handle)
         seq = ctypes.c_void_p(self.seq_lens.data_ptr())
-        if self.lib.kvc_seq_lens_advance(seq, self.cfg.batch, 1, ctypes.c_void_p(stream_handle)):
+        if self.lib.kvc_seq_lens_advance(seq, self.cfg.batch, max(self.block_q, 1), ctypes.c_void_p(stream_handle)):
             raise RuntimeError("kvc_seq_lens_advance failed")
 
     def kv_bytes(self, steps: int) -> int:
         """KV bytes read by `steps` steps starting from the reset lengths."""
         per_token = 2 * self.cfg.n_layers * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
         base = int(self.lengths.to("cpu").long().sum())
-        b = self.cfg.batch
+        b = self.cfg.batch * max(self.block_q, 1)
         return per_token * sum(base + b * (k + 1) for k in range(steps))
 
     def decode_launch_bytes(self, step_index: int) -> int:
         """Algorithmic K+V bytes one decode launch (one layer) reads at a step."""
         per_token = 2 * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
-        return per_token * (int(self.lengths.long().sum()) + self.cfg.batch * (step_index + 1))
+        nq = max(self.block_q, 1)
+        return per_token * (int(self.lengths.long().sum()) + self.cfg.batch * nq * (step_index + 1))
 
 
 def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
@@ -307,8 +329,9 @@ def _run_config(name, args, with_cpu):
     import torch
     import synth
     cfg = synth.CONFIGS[name]
-    margin = max(args.steps, args.warmup) + 2
-    w = Workload(cfg, margin, args.seed, args.splits)
+    nq = max(args.block_q, 1)
+    margin = (max(args.steps, args.warmup) + 2) * nq
+    w = Workload(cfg, margin, args.seed, args.splits, args.block_q)
     ms_total, wall, launch_ms, launch_bytes = _measure(w, args.steps, args.warmup, not args.no_graph)
     kv = w.kv_bytes(args.steps)
     gbs = kv / (ms_total / 1e3) / 1e9
@@ -329,9 +352,13 @@ def _run_config(name, args, with_cpu):
             "cached_tokens_at_start": {"min": int(lens.min()), "max": int(lens.max()),
                                        "sum": int(lens.long().sum())},
             "splits": w.splits, "hip_graph": not args.no_graph,
+            **({"query_block": args.block_q} if args.block_q else {}),
         },
         "roofline": {
-            "bound": "hbm", "kernel": "decode_kernel (kvc_decode_step: append + attention + merge, one launch per layer)",
+            "bound": "hbm",
+            "kernel": ("copy_rows_kernel + decode_kernel (kvc_prefill_fill + kvc_block_attn per layer; time per "
+                       "layer covers both)" if args.block_q else
+                       "decode_kernel (kvc_decode_step: append + attention + merge, one launch per layer)"),
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),

@@ -211,6 +211,45 @@ kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens,
                              uint32_t* dev_status, hipStream_t stream);
 
 /*
+ * kvc_block_attn -- a block of t_q new tokens per sequence (a prefill chunk
+ * or a speculative verify step) attends the cache with the causal mask
+ * aligned to the lower right (course notes "第 1 周 · Day 4" §3.3, masks with
+ * a cache): query i of sequence b sees slots 0 .. seq_lens[b] + i. The
+ * block's own K/V rows must already be in the cache at slots
+ * [seq_lens[b], seq_lens[b] + t_q) (kvc_prefill_fill with the same seq_lens
+ * writes them); seq_lens is only read. Scale and GQA grouping as in
+ * kvc_decode_attn; with t_q = 1 the result is the same as kvc_decode_attn
+ * with n_pending = 1.
+ *
+ *   t_q       queries per sequence, >= 1 (t_q * n_q_heads <= 2^24).
+ *   q         [batch, t_q, n_q_heads, head_dim], contiguous, cache dtype
+ *             (token-major, as a block's projections come out).
+ *   out       [batch, t_q, n_q_heads, head_dim], contiguous, out_dtype.
+ *   workspace at least kvc_block_workspace_bytes(cache, n_q_heads, t_q,
+ *             n_splits) bytes, with the lifetime rules of
+ *             kvc_decode_workspace_bytes (geometry includes t_q).
+ *   n_splits  as for kvc_decode_attn (0 = library choice).
+ *
+ * The (query, head) pairs of a KV head are processed like the query heads of
+ * a larger group, so K/V rows are streamed once per block of up to 8 pairs;
+ * the call suits short blocks (verify steps, small chunks). A sequence whose
+ * block does not fit (seq_lens[b] < 0, or seq_lens[b] + t_q > max_len) gets
+ * zero rows and KVC_DEVERR_BADLEN / KVC_DEVERR_CAPACITY. Host-side errors as
+ * for kvc_decode_attn, and KVC_ERR_SHAPE for t_q < 1.
+ */
+kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
+                            const void* q, int32_t n_q_heads, float scale,
+                            void* out, int32_t out_dtype,
+                            void* workspace, size_t workspace_bytes, int32_t n_splits,
+                            uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * kvc_block_workspace_bytes -- workspace kvc_block_attn needs (0 for invalid
+ * arguments); n_splits = 0 means the library's choice.
+ */
+size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t t_q, int32_t n_splits);
+
+/*
  * kvc_seq_lens_advance -- seq_lens[b] += n for every b, on the device, once per
  * step after all layers appended (course notes §3.1: pos += T).
  */

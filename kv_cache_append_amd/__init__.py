@@ -31,7 +31,8 @@ STATUS = {
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
-           "kvc_decode_attn", "kvc_decode_step", "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
+           "kvc_decode_attn", "kvc_decode_step", "kvc_block_attn", "kvc_block_workspace_bytes",
+           "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
 
 
 class KvcError(RuntimeError):
@@ -76,6 +77,10 @@ def load() -> ctypes.CDLL:
     lib.kvc_decode_attn.restype = i32
     lib.kvc_decode_step.argtypes = [cp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_decode_step.restype = i32
+    lib.kvc_block_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_block_attn.restype = i32
+    lib.kvc_block_workspace_bytes.argtypes = [cp, i32, i32, i32]
+    lib.kvc_block_workspace_bytes.restype = sz
     lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
     lib.kvc_seq_lens_advance.restype = i32
     lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
@@ -150,6 +155,15 @@ def workspace(k_cache, v_cache, n_q_heads: int, n_splits: int = 0) -> torch.Tens
     return torch.zeros(n, dtype=torch.uint8, device=k_cache.device)
 
 
+def block_workspace(k_cache, v_cache, n_q_heads: int, t_q: int, n_splits: int = 0) -> torch.Tensor:
+    """A zero-filled device workspace for kvc_block_attn with this geometry."""
+    c = cache_desc(k_cache, v_cache)
+    n = int(load().kvc_block_workspace_bytes(ctypes.byref(c), n_q_heads, t_q, n_splits))
+    if n == 0:
+        raise ValueError("invalid cache/head/block arguments for a block workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=k_cache.device)
+
+
 def decode_splits(k_cache, v_cache, n_q_heads: int) -> int:
     c = cache_desc(k_cache, v_cache)
     return int(load().kvc_decode_splits(ctypes.byref(c), n_q_heads))
@@ -187,6 +201,22 @@ def decode_step(k_cache, v_cache, seq_lens, k_new, v_new, q, out, workspace, sca
                                k_new.stride(1), _ptr(q), q.shape[1], float(scale), _ptr(out),
                                DTYPE_CODE[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
                                n_splits, _ptr(status), _stream(stream)), "kvc_decode_step")
+
+
+def block_attn(k_cache, v_cache, seq_lens, q, out, workspace, scale=None, n_splits: int = 0, status=None,
+               stream=None, desc=None):
+    """kvc_block_attn: q [B, t_q, H_q, D]; query i of sequence b attends
+    slots 0..seq_lens[b]+i (lower-right causal mask); out like q."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 4:
+        raise ValueError("q and out must be contiguous [B, t_q, H_q, D]")
+    _check(lib.kvc_block_attn(ctypes.byref(c), _ptr(seq_lens), q.shape[1], _ptr(q), q.shape[2], float(scale),
+                              _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                              _stream(stream)), "kvc_block_attn")
 
 
 def seq_lens_advance(seq_lens, n: int = 1, stream=None):

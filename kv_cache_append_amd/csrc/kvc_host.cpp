@@ -161,6 +161,14 @@ extern "C" size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n
   return kvc::workspace_bytes(cache, n_q_heads, s);
 }
 
+extern "C" size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t t_q,
+                                            int32_t n_splits) {
+  if (kvc::check_cache(cache, false) != KVC_OK) return 0;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return 0;
+  if (t_q <= 0 || static_cast<int64_t>(n_q_heads) * t_q > (1 << 24)) return 0;
+  return kvc_decode_workspace_bytes(cache, n_q_heads * t_q, n_splits);
+}
+
 extern "C" int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads) {
   if (kvc::check_cache(cache, false) != KVC_OK) return 0;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return 0;

@@ -280,6 +280,11 @@ struct DecodeParams {
   void* out;                   // [B, H_q, D]
   uint32_t* status;
   int32_t batch, n_q, n_kv, group, n_hblk, max_len, n_pending, n_splits, out_f32;
+  // Block of new queries (kvc_block_attn): t_q queries per sequence, query i
+  // attending slots 0..seq_lens[b] + i. The t_q * group (query, head) pairs
+  // of a KV head play the role of its query heads; pair v is query v / group
+  // of head v % group. Decode has t_q = 1 and block = 0.
+  int32_t t_q, block;
   float scale_log2;            // softmax scale * log2(e)
 };
 
@@ -297,6 +302,12 @@ __device__ inline SeqInfo seq_info(const DecodeParams& p, int b) {
   if (c0 < 0) si.flags |= KVC_DEVERR_BADLEN;
   si.append_row = -1;
   int n;
+  if (p.block) {                  // the whole block must fit: else flagged, zero rows
+    n = c0 + p.t_q;
+    if (c0 >= 0 && n > p.max_len) si.flags |= KVC_DEVERR_CAPACITY;
+    si.n = (c0 < 0 || n > p.max_len) ? 0 : n;
+    return si;
+  }
   if (p.k_new != nullptr) {
     if (c0 >= 0 && c0 < p.max_len) si.append_row = c0;
     else si.flags |= KVC_DEVERR_CAPACITY;
@@ -316,6 +327,17 @@ template <typename ET>
 __device__ inline void store_out(const DecodeParams& p, int64_t idx, float x) {
   if (p.out_f32) F32T::store(p.out, idx, x);
   else ET::store(p.out, idx, x);
+}
+
+// Row of q and out ([B, t_q, H_q, D], token-major) of pair v of KV head g.
+__device__ inline int64_t pair_row(const DecodeParams& p, int b, int g, int v) {
+  const int i = v / p.group;
+  return (static_cast<int64_t>(b) * p.t_q + i) * p.n_q + g * p.group + (v - i * p.group);
+}
+// Slots pair v may attend are [0, limit): seq_lens[b] + i + 1 for a block
+// query i, and n for every head in decode.
+__device__ inline int pair_limit(const DecodeParams& p, int n, int v) {
+  return p.block ? n - p.t_q + v / p.group + 1 : n;
 }
 
 // exp2 of a non-positive-or-bounded argument; -inf gives 0 (hardware v_exp_f32)
@@ -447,12 +469,13 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   if (si.flags != 0 && g == 0 && hb == 0 && split == 0 && threadIdx.x == 0 && p.status != nullptr)
     atomicOr(p.status, si.flags);
   const int n = si.n;
-  const int h_first = g * p.group + hb * GB;
-  const int nh = min(GB, p.group - hb * GB);       // valid heads in this block
-  const int64_t orow0 = (static_cast<int64_t>(b) * p.n_q + h_first) * D;
+  const int gv = p.group * p.t_q;                  // (query, head) pairs of this KV head
+  const int v_first = hb * GB;                     // first pair of this block
+  const int nh = min(GB, gv - v_first);            // valid pairs in this block
   if (n <= 0) {                                      // empty sequence: zero rows
     if (split == 0)
-      for (int t = threadIdx.x; t < nh * D; t += blockDim.x) store_out<ET>(p, orow0 + t, 0.f);
+      for (int t = threadIdx.x; t < nh * D; t += blockDim.x)
+        store_out<ET>(p, pair_row(p, b, g, v_first + t / D) * D + t % D, 0.f);
     return;
   }
   const int chunk = (n + p.n_splits - 1) / p.n_splits;
@@ -547,11 +570,15 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       qa[m] = u32x4{0u, 0u, 0u, 0u};
       if (r16 < nh)
         qa[m] = *reinterpret_cast<const u32x4*>(
-            p.q + ((static_cast<int64_t>(b) * p.n_q + h_first + r16) * D + (4 * m + kq) * EPL) * ET::kBytes);
+            p.q + (pair_row(p, b, g, v_first + r16) * D + (4 * m + kq) * EPL) * ET::kBytes);
     }
     float hbias[4];                           // 0 where (lane, register) is a real head's score
 #pragma unroll
     for (int t = 0; t < 4; ++t) hbias[t] = (kq < NQ && 4 * kq + t < nh) ? 0.f : -INFINITY;
+    int plim[4];                              // slot limit of the pair in (lane, register t)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) plim[t] = pair_limit(p, n, v_first + 4 * kq + t);
+    const bool block = p.block != 0;
     float refh[4 * NQ];                       // wave-uniform reference per head
 #pragma unroll
     for (int h = 0; h < 4 * NQ; ++h) refh[h] = kEmpty;
@@ -585,14 +612,19 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     auto lane_ref = [&](int t) { return (NQ > 1 && kq == 1) ? refh[4 + t] : refh[t]; };
 
     const f32x4 hb4 = f32x4{hbias[0], hbias[1], hbias[2], hbias[3]};
-    // rows_left: rows of this tile to attend (all 16 unless it is the last)
-    auto compute = [&](const u32x4 (&K)[NM], const u32x4 (&V)[NP], int rows_left) {
+    // rows_left: rows of this tile to attend (all 16 unless it is the last);
+    // row0: the tile's first slot, for the per-pair limits of a query block
+    auto compute = [&](const u32x4 (&K)[NM], const u32x4 (&V)[NP], int rows_left, int row0) {
       f32x4 sv = ET::mfma16(qa[0], K[0], hb4);
 #pragma unroll
       for (int m = 1; m < NM; ++m) sv = ET::mfma16(qa[m], K[m], sv);
       if (rows_left < 16) {                   // wave-uniform: only a last, partial tile
 #pragma unroll
         for (int t = 0; t < 4; ++t) sv[t] = r16 < rows_left ? sv[t] : -INFINITY;
+      }
+      if (block) {                            // lower-right causal mask of a query block
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sv[t] = row0 + r16 < plim[t] ? sv[t] : -INFINITY;
       }
       float w[4], rl[4];
       bool need = false;
@@ -668,7 +700,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
 #pragma unroll
           for (int r = 0; r < NBM; ++r) {     // unrolled: ring slots are compile-time
             load_tile(base + (NBM - 1) * TSM, KB[(r + NBM - 1) % NBM], VB[(r + NBM - 1) % NBM]);
-            compute(KB[r], VB[r], __builtin_amdgcn_readfirstlane(t_end - base));
+            compute(KB[r], VB[r], __builtin_amdgcn_readfirstlane(t_end - base), base);
             base += TSM;
             if (it + r + 1 >= n_tiles) {
               done = true;
@@ -688,7 +720,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       }
 #pragma unroll
       for (int u = 0; u < NP; ++u) V[u] = (u == 0 && grp == 0) ? nv : u32x4{0u, 0u, 0u, 0u};
-      compute(K, V, 1);
+      compute(K, V, 1, xrow);
     }
     // Wave totals in the common layout: one reference per head (the same in
     // every lane), the weight sum in lane group 0 only (the lane-group merge
@@ -720,8 +752,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
     if (j < nh) {
-      qv[j] = *reinterpret_cast<const u32x4*>(p.q + ((static_cast<int64_t>(b) * p.n_q + h_first + j) * D + li * EPL) *
-                                                       ET::kBytes);
+      qv[j] = *reinterpret_cast<const u32x4*>(p.q + (pair_row(p, b, g, v_first + j) * D + li * EPL) * ET::kBytes);
     } else {
       qv[j] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -751,12 +782,18 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   // per-head masking (its K and V read as zero through the range check).
   // The order (all scores, then all weights, then V one row at a time) keeps
   // few temporaries live next to the buffered tiles.
-  auto compute_rows = [&](const u32x4 (&K)[U], const u32x4 (&V)[U], const float (&bias)[U]) {
+  int vlim[GB];                                // slot limit of each pair (query blocks)
+#pragma unroll
+  for (int j = 0; j < GB; ++j) vlim[j] = pair_limit(p, n, v_first + j);
+  const bool block = p.block != 0;
+  // row_at[u]: this lane's slot in pass u (for the per-pair limits of a block)
+  auto compute_rows = [&](const u32x4 (&K)[U], const u32x4 (&V)[U], const float (&bias)[U], const int (&row_at)[U]) {
     float w[GB][U];
 #pragma unroll
     for (int j = 0; j < GB; ++j)
 #pragma unroll
-      for (int u = 0; u < U; ++u) w[j][u] = ET::dot(qv[j], K[u], bias[u]);
+      for (int u = 0; u < U; ++u)
+        w[j][u] = ET::dot(qv[j], K[u], (block && row_at[u] >= vlim[j]) ? -INFINITY : bias[u]);
     group_sum_n<LPR>(reinterpret_cast<float (&)[GB * U]>(w));
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
@@ -801,9 +838,13 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   auto compute_tile = [&](int base, const u32x4 (&K)[U], const u32x4 (&V)[U]) {
     const int rows_left = __builtin_amdgcn_readfirstlane(t_end - base);   // scalar
     float bias[U];
+    int row_at[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) bias[u] = rel_row[u] < rows_left ? 0.f : -INFINITY;
-    compute_rows(K, V, bias);
+    for (int u = 0; u < U; ++u) {
+      bias[u] = rel_row[u] < rows_left ? 0.f : -INFINITY;
+      row_at[u] = base + rel_row[u];
+    }
+    compute_rows(K, V, bias, row_at);
   };
 
   // Register ring of NB tiles: NB - 1 tiles of loads in flight behind the
@@ -835,13 +876,15 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   if (has_x && wave == 0) {                    // the last attended row: lane group 0, pass 0
     u32x4 K[U], V[U];
     float bias[U];
+    int row_at[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       K[u] = u == 0 ? nk : u32x4{0u, 0u, 0u, 0u};
       V[u] = u == 0 ? nv : u32x4{0u, 0u, 0u, 0u};
       bias[u] = (u == 0 && grp == 0) ? 0.f : -INFINITY;
+      row_at[u] = xrow;
     }
-    compute_rows(K, V, bias);
+    compute_rows(K, V, bias, row_at);
   }
   }   // vector-ALU path
 
@@ -935,8 +978,9 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       const int j = t / D4;
       const int d = (t - j * D4) * 4;
       const float inv = 1.f / lv[i];
+      const int64_t orow = pair_row(p, b, g, v_first + j) * D + d;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out<ET>(p, orow0 + j * D + d + e, aa[i][e] * inv);
+      for (int e = 0; e < 4; ++e) store_out<ET>(p, orow + e, aa[i][e] * inv);
     }
   };
   if (ns == 1) {                                   // a single active split: done
@@ -960,7 +1004,8 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   const int64_t item = static_cast<int64_t>(unit) * p.n_hblk + hb;
   uint32_t* ticket = p.ws_cnt + item;
   uint32_t* flags = p.ws_flag + item * p.n_splits;
-  const int64_t prow0 = (static_cast<int64_t>(b) * p.n_q + h_first) * p.n_splits;
+  // partial rows: [B, H_kv * pairs, S] (for decode, [B, H_q, S])
+  const int64_t prow0 = ((static_cast<int64_t>(b) * p.n_kv + g) * gv + v_first) * p.n_splits;
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(nh * p.n_splits * D * 4));
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(nh * p.n_splits * 2 * 4));
 #pragma unroll
@@ -1150,10 +1195,16 @@ kvc_status_t launch_copy(const kvc_cache_t* c, const int32_t* seq_lens, const vo
 kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,
                            const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
                            int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
-                           size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
+                           size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status, hipStream_t stream,
+                           int32_t t_q) {
   kvc_status_t st = kvc::check_cache(cache, true);
   if (st != KVC_OK) return st;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
+  // t_q > 0: a block of t_q queries per sequence; the (query, head) pairs are
+  // handled as t_q * n_q_heads virtual heads. t_q == 0: single-query decode.
+  if (t_q < 0 || static_cast<int64_t>(n_q_heads) * (t_q > 0 ? t_q : 1) > (1 << 24)) return KVC_ERR_SHAPE;
+  const int32_t tq = t_q > 0 ? t_q : 1;
+  const int32_t n_qv = n_q_heads * tq;
   if (n_pending < 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return KVC_ERR_SHAPE;
   if (out_dtype != KVC_F32 && out_dtype != cache->dtype) return KVC_ERR_DTYPE;
   if (!kvc::decode_head_dim_supported(cache->head_dim, cache->dtype)) return KVC_ERR_UNSUPPORTED;
@@ -1177,13 +1228,13 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   // The kernels address one (sequence, KV head) slice of K/V with 32-bit
   // byte offsets (plus up to two tiles past the end, read back as zeros).
   if ((static_cast<int64_t>(cache->max_len) + 2048) * cache->stride_t * s > 0x7fffffffll) return KVC_ERR_SHAPE;
-  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
-  const size_t need = kvc::workspace_bytes(cache, n_q_heads, splits);
+  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_qv);
+  const size_t need = kvc::workspace_bytes(cache, n_qv, splits);
   if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
 
   const int group = n_q_heads / cache->n_kv_heads;
-  const int gb = kvc::heads_per_block(group);
+  const int gb = kvc::heads_per_block(group * tq);
   DecodeParams p;
   p.k = static_cast<char*>(cache->k);
   p.v = static_cast<char*>(cache->v);
@@ -1198,21 +1249,23 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.nsh = new_stride_h * s;
   char* ws = static_cast<char*>(workspace);
   p.ws_cnt = reinterpret_cast<uint32_t*>(ws);
-  p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(cache, n_q_heads, splits));
-  p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(cache, n_q_heads, splits));
-  p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(cache, n_q_heads, splits));
+  p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(cache, n_qv, splits));
+  p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(cache, n_qv, splits));
+  p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(cache, n_qv, splits));
   p.out = out;
   p.status = dev_status;
   p.batch = cache->batch;
   p.n_q = n_q_heads;
   p.n_kv = cache->n_kv_heads;
   p.group = group;
-  p.n_hblk = kvc::head_blocks(group);
+  p.n_hblk = kvc::head_blocks(group * tq);
   p.max_len = cache->max_len;
   p.n_pending = n_pending;
   p.n_splits = splits;
   p.out_f32 = out_dtype == KVC_F32 ? 1 : 0;
   p.scale_log2 = scale_log2;
+  p.t_q = tq;
+  p.block = t_q > 0 ? 1 : 0;
 
   DecodeKernel k = pick_decode_kernel(cache->dtype, cache->head_dim, gb);
   if (k == nullptr) return KVC_ERR_UNSUPPORTED;
@@ -1262,7 +1315,7 @@ extern "C" kvc_status_t kvc_decode_attn(const kvc_cache_t* cache, const int32_t*
                                         int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                         int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
   return launch_decode(cache, seq_lens, n_pending, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype,
-                       workspace, workspace_bytes, n_splits, dev_status, stream);
+                       workspace, workspace_bytes, n_splits, dev_status, stream, 0);
 }
 
 extern "C" kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens, const void* k_new,
@@ -1276,7 +1329,17 @@ extern "C" kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t*
     if (cache->batch > 0) return KVC_ERR_NULL;
   }
   return launch_decode(cache, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
-                       out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream);
+                       out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, 0);
+}
+
+extern "C" kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q, const void* q,
+                                       int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
+                                       size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status,
+                                       hipStream_t stream) {
+  if (cache == nullptr) return KVC_ERR_NULL;
+  if (t_q <= 0) return KVC_ERR_SHAPE;
+  return launch_decode(cache, seq_lens, 0, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype, workspace,
+                       workspace_bytes, n_splits, dev_status, stream, t_q);
 }
 
 extern "C" kvc_status_t kvc_seq_lens_advance(int32_t* seq_lens, int32_t batch, int32_t n, hipStream_t stream) {

@@ -211,3 +211,23 @@ def test_split_count_limit():
     assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, 256) > 0
     assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, 257) == 0
     assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, 1 << 30, 257, None, None) == 2
+
+
+def test_block_validation_and_workspace():
+    """kvc_block_attn: t_q < 1 is a shape error, grouping as for decode, and
+    its workspace is the decode workspace of t_q * n_q virtual heads."""
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    big = 1 << 30
+    assert lib.kvc_block_attn(ctypes.byref(c), FAKE, 0, FAKE, 4, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 2
+    assert lib.kvc_block_attn(ctypes.byref(c), FAKE, 3, FAKE, 3, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 5
+    assert lib.kvc_block_attn(None, FAKE, 3, FAKE, 4, 0.1, FAKE, 0, FAKE, big, 0, None, None) == 1
+    assert lib.kvc_block_attn(ctypes.byref(c), FAKE, 3, FAKE, 4, -1.0, FAKE, 0, FAKE, big, 0, None, None) == 7
+    for t_q in (1, 3, 8):
+        for s in (0, 1, 5):
+            assert lib.kvc_block_workspace_bytes(ctypes.byref(c), 4, t_q, s) == \
+                lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4 * t_q, s)
+    assert lib.kvc_block_workspace_bytes(ctypes.byref(c), 4, 0, 0) == 0
+    assert lib.kvc_block_workspace_bytes(ctypes.byref(c), 3, 2, 0) == 0
+    need = lib.kvc_block_workspace_bytes(ctypes.byref(c), 4, 3, 0)
+    assert lib.kvc_block_attn(ctypes.byref(c), FAKE, 3, FAKE, 4, 0.1, FAKE, 0, FAKE, need - 1, 0, None, None) == 6

@@ -1,0 +1,183 @@
+"""GPU parity of kvc_block_attn (a block of new queries per sequence with the
+lower-right causal mask) against oracle.chunk_attention, through the C ABI.
+The block's K/V rows are written with kvc_prefill_fill, as a caller would."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_append_amd as kvc
+import oracle
+import synth
+from tests.gpu_cases import TOL, poison_
+
+pytestmark = pytest.mark.gpu
+
+
+class BlockCase:
+    """Cache [B, H_kv, T_max, D] with seq_lens[b] cached rows, a block of t_q
+    new rows per sequence (k/v) and its queries q [B, t_q, H_q, D]; NaN past
+    the cached rows. Host copies are taken before any libkvc call."""
+
+    def __init__(self, *, batch, n_q, n_kv, d, dtype, lengths, t_q, t_max=None, seed=11, tag="blk",
+                 device="cuda"):
+        self.t_q, self.n_q, self.n_kv, self.dtype = t_q, n_q, n_kv, dtype
+        self.lengths = torch.as_tensor(lengths, dtype=torch.int32)
+        self.t_max = int(t_max if t_max is not None else int(self.lengths.max()) + t_q)
+        tdt = synth.DTYPES[dtype]
+        self.k = poison_(torch.empty((batch, n_kv, self.t_max, d), dtype=tdt, device=device))
+        self.v = poison_(torch.empty_like(self.k))
+        rows = max(int(self.lengths.max()), 1)
+        for name, dst in (("K", self.k), ("V", self.v)):
+            full = synth.normal((batch, n_kv, rows, d), dtype, seed, tag, name, device=device)
+            for b in range(batch):
+                n = int(self.lengths[b])
+                if n > 0:
+                    dst[b, :, :n].copy_(full[b, :, :n])
+        self.k_blk = synth.normal((batch, n_kv, t_q, d), dtype, seed, tag, "kb", device=device)
+        self.v_blk = synth.normal((batch, n_kv, t_q, d), dtype, seed, tag, "vb", device=device)
+        self.q = synth.normal((batch, t_q, n_q, d), dtype, seed, tag, "q", device=device)
+        self.seq_lens = self.lengths.to(device)
+        self.k_host, self.v_host = self.k.cpu(), self.v.cpu()
+        self.kb_host, self.vb_host, self.q_host = self.k_blk.cpu(), self.v_blk.cpu(), self.q.cpu()
+
+    def fill(self):
+        kvc.prefill_fill(self.k, self.v, self.seq_lens, self.k_blk, self.v_blk)
+
+    def oracle(self):
+        """fp64 reference on the host: the block written after the cached rows."""
+        k, v = self.k_host.clone(), self.v_host.clone()
+        for b in range(k.shape[0]):
+            n = int(self.lengths[b])
+            k[b, :, n:n + self.t_q] = self.kb_host[b]
+            v[b, :, n:n + self.t_q] = self.vb_host[b]
+        return oracle.chunk_attention(self.q_host, k, v, self.lengths.numpy())
+
+
+def _run(case: BlockCase, n_splits=0, out_dtype=torch.float32, status=None):
+    out = torch.empty(case.q.shape, dtype=out_dtype, device=case.q.device)
+    ws = kvc.block_workspace(case.k, case.v, case.n_q, case.t_q, n_splits)
+    kvc.block_attn(case.k, case.v, case.seq_lens, case.q, out, ws, n_splits=n_splits, status=status)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("hq,hkv,t_q", [(8, 2, 4), (8, 8, 3), (32, 8, 5), (4, 1, 7), (6, 2, 2), (16, 1, 16)])
+def test_block_matches_oracle(gpu, dtype, hq, hkv, t_q):
+    case = BlockCase(batch=4, n_q=hq, n_kv=hkv, d=128, dtype=dtype, lengths=[0, 37, 300, 1025], t_q=t_q,
+                     tag=f"blk{dtype}{hq}{hkv}{t_q}")
+    case.fill()
+    got = _run(case).double().cpu().numpy()
+    ref = case.oracle()
+    assert not np.isnan(got).any()
+    assert np.abs(got - ref).max() <= TOL[dtype]
+
+
+@pytest.mark.parametrize("d", [64, 256, 32])
+def test_block_other_head_dims(gpu, d):
+    case = BlockCase(batch=2, n_q=8, n_kv=2, d=d, dtype="bf16", lengths=[90, 513], t_q=3, tag=f"blkd{d}")
+    case.fill()
+    assert np.abs(_run(case).double().cpu().numpy() - case.oracle()).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("n_splits", [1, 2, 5, 64])
+def test_block_split_counts(gpu, n_splits):
+    case = BlockCase(batch=3, n_q=8, n_kv=2, d=128, dtype="fp16", lengths=[5, 700, 2000], t_q=4,
+                     tag=f"blks{n_splits}")
+    case.fill()
+    assert np.abs(_run(case, n_splits).double().cpu().numpy() - case.oracle()).max() <= TOL["fp16"]
+
+
+def test_block_of_one_equals_decode_bitwise(gpu):
+    case = BlockCase(batch=3, n_q=32, n_kv=8, d=128, dtype="bf16", lengths=[1, 333, 2047], t_q=1, tag="blk1")
+    case.fill()
+    got = _run(case)
+    out = torch.empty((3, 32, 128), device=gpu)
+    ws = kvc.workspace(case.k, case.v, 32)
+    kvc.decode_attn(case.k, case.v, case.seq_lens, case.q[:, 0].contiguous(), out, ws, n_pending=1)
+    torch.cuda.synchronize()
+    assert torch.equal(got[:, 0], out)
+
+
+def test_block_run_to_run_deterministic(gpu):
+    case = BlockCase(batch=4, n_q=32, n_kv=8, d=128, dtype="bf16", lengths=[100, 900, 1500, 2048], t_q=4,
+                     tag="blkdet")
+    case.fill()
+    a = _run(case, n_splits=2)
+    b = _run(case, n_splits=2)
+    assert torch.equal(a, b)
+
+
+def test_block_out_in_cache_dtype_is_rounded_fp32(gpu):
+    case = BlockCase(batch=2, n_q=8, n_kv=2, d=128, dtype="bf16", lengths=[50, 400], t_q=4, tag="blkod")
+    case.fill()
+    f32 = _run(case)
+    half = _run(case, out_dtype=torch.bfloat16)
+    assert torch.equal(half, f32.to(torch.bfloat16))
+
+
+def test_chunked_prefill_through_the_abi(gpu):
+    """A prompt prefilled in chunks (fill, then block attention, then advance)
+    gives the rows of one causal prefill of the whole prompt (course notes
+    Day 4 §3.5, chunked variant), within the dtype's tolerance."""
+    hq, hkv, d, t = 8, 2, 128, 45
+    tdt = torch.bfloat16
+    k = poison_(torch.empty((1, hkv, t, d), dtype=tdt, device=gpu))
+    v = poison_(torch.empty_like(k))
+    kp = synth.normal((1, hkv, t, d), "bf16", 3, "cp", "k", device=gpu)
+    vp = synth.normal((1, hkv, t, d), "bf16", 3, "cp", "v", device=gpu)
+    qp = synth.normal((1, t, hq, d), "bf16", 3, "cp", "q", device=gpu)
+    seq = torch.zeros(1, dtype=torch.int32, device=gpu)
+    outs, start = [], 0
+    for size in (16, 1, 20, 8):
+        ws = kvc.block_workspace(k, v, hq, size)
+        kvc.prefill_fill(k, v, seq, kp[:, :, start:start + size], vp[:, :, start:start + size])
+        out = torch.empty((1, size, hq, d), device=gpu)
+        kvc.block_attn(k, v, seq, qp[:, start:start + size].contiguous(), out, ws)
+        kvc.seq_lens_advance(seq, size)
+        outs.append(out)
+        start += size
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=1).double().cpu().numpy()
+    ref = oracle.chunk_attention(qp.cpu(), kp.cpu(), vp.cpu(), np.array([0]))
+    assert np.abs(got - ref).max() <= TOL["bf16"]
+
+
+def test_block_that_does_not_fit_gives_zero_rows_and_flags(gpu):
+    case = BlockCase(batch=3, n_q=8, n_kv=2, d=128, dtype="fp16", lengths=[10, 60, 20], t_q=5, t_max=64,
+                     tag="blkfit")
+    case.fill()                                   # sequence 1's block does not fit: not written either
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    got = _run(case, status=status)
+    assert int(status.item()) & kvc.DEVERR_CAPACITY
+    assert torch.count_nonzero(got[1]) == 0
+    k, v = case.k.cpu(), case.v.cpu()
+    for b in (0, 2):
+        r = oracle.chunk_attention(case.q_host[b:b + 1], k[b:b + 1], v[b:b + 1], np.array([int(case.lengths[b])]))
+        assert np.abs(got[b:b + 1].double().cpu().numpy() - r).max() <= TOL["fp16"]
+
+
+def test_block_negative_length_is_flagged(gpu):
+    case = BlockCase(batch=2, n_q=4, n_kv=2, d=128, dtype="fp16", lengths=[10, 30], t_q=2, tag="blkneg")
+    case.fill()
+    case.seq_lens[1] = -3
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    got = _run(case, status=status)
+    assert int(status.item()) & kvc.DEVERR_BADLEN
+    assert torch.count_nonzero(got[1]) == 0
+
+
+def test_verify_step_at_gqa_8b_shape_sampled(gpu):
+    """A speculative verify step of 4 tokens at the 8B GQA shape (B=16, 32/8
+    heads, D=128, T=2048, bf16), with the library's split choice, checked on
+    sampled sequences."""
+    case = BlockCase(batch=16, n_q=32, n_kv=8, d=128, dtype="bf16", lengths=[2048] * 16, t_q=4, tag="blkv8b")
+    case.fill()
+    got = _run(case)
+    k, v = case.k.cpu(), case.v.cpu()
+    for b in (0, 7, 15):
+        r = oracle.chunk_attention(case.q_host[b:b + 1], k[b:b + 1], v[b:b + 1], np.array([2048]))
+        assert np.abs(got[b:b + 1].double().cpu().numpy() - r).max() <= TOL["bf16"]
