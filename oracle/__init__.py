@@ -28,6 +28,11 @@ from .kvc_oracle import (  # noqa: F401
     concat_append_positions,
     decode_attention,
     kv_head_of,
+    paged_append,
+    paged_decode_attention,
+    paged_prefill_fill,
+    paged_slot,
+    paged_view,
     prealloc_append_positions,
     prefill_fill,
     project,

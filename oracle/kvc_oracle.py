@@ -274,6 +274,83 @@ def toy_path_b(x, wq, wk, wv, wo, n_q: int, n_kv: int, head_dim: int, n_prompt: 
     return np.stack(outputs), np.stack(contexts), k_cache, v_cache
 
 
+# ------------------------------------------------------------ paged cache --
+#
+# [KVG] "与上下游术语的关系" and the note under the slot figure, [W1D4] §1.6
+# (fragmentation) and [LA11] §8 (optimisation table): a paged cache stores
+# the same logical K/V sequence in fixed-size physical pages addressed
+# through a per-sequence page table, so that storage need not be contiguous;
+# it does not change the logical sequence or the attention result. Here the
+# pool is [n_pages, H_kv, P, D] and logical slot t of sequence b lives in
+# page block_table[b][t // P] at row t % P. The pages leave the page size
+# open; the library takes any multiple of 16 tokens.
+
+
+def paged_slot(block_table, b: int, t: int, page_size: int):
+    """(physical page, row in page) of logical slot t of sequence b."""
+    return int(block_table[b][t // page_size]), t % page_size
+
+
+def paged_view(pages, block_table, n_tokens: int, lengths=None):
+    """Logical cache [B, H_kv, n_tokens, D] gathered from a page pool
+    [n_pages, H_kv, P, D] through block_table [B, pages per sequence]; with
+    `lengths`, sequence b gathers only its first lengths[b] slots (the rest
+    stay zero, and their table entries are not read)."""
+    pages = np.asarray(pages)
+    batch = len(block_table)
+    n_pages, n_kv, page_size, d = pages.shape
+    out = np.zeros((batch, n_kv, n_tokens, d), dtype=pages.dtype)
+    for b in range(batch):
+        n_b = n_tokens if lengths is None else min(n_tokens, max(int(lengths[b]), 0))
+        for t in range(n_b):
+            pg, r = paged_slot(block_table, b, t, page_size)
+            if not 0 <= pg < n_pages:
+                raise IndexError(f"sequence {b} slot {t}: page {pg} is not in the pool")
+            out[b, :, t, :] = pages[pg, :, r, :]
+    return out
+
+
+def paged_prefill_fill(k_pages, v_pages, block_table, seq_lens, k, v):
+    """Write T_new tokens per sequence at logical slots [seq_lens[b],
+    seq_lens[b] + T_new) through the page table ([W1D4 §3.1] update, paged).
+    A sequence whose block passes the table's capacity, or whose pages are
+    not valid pool indices, is left untouched and reported in `overflow`.
+    k, v: [B, H_kv, T_new, D]. Returns (k_pages', v_pages', overflow)."""
+    k_out = np.array(k_pages, copy=True)
+    v_out = np.array(v_pages, copy=True)
+    n_pages, _, page_size, _ = k_out.shape
+    batch, _, t_new, _ = np.asarray(k).shape
+    cap = len(block_table[0]) * page_size if batch else 0
+    overflow = np.zeros(batch, dtype=bool)
+    for b in range(batch):
+        pos = int(seq_lens[b])
+        slots = [(paged_slot(block_table, b, pos + i, page_size)) for i in range(t_new)
+                 if 0 <= pos and pos + i < cap]
+        if pos < 0 or pos + t_new > cap or any(not 0 <= pg < n_pages for pg, _ in slots):
+            overflow[b] = True
+            continue
+        for i, (pg, r) in enumerate(slots):
+            k_out[pg, :, r, :] = np.asarray(k)[b, :, i, :]
+            v_out[pg, :, r, :] = np.asarray(v)[b, :, i, :]
+    return k_out, v_out, overflow
+
+
+def paged_append(k_pages, v_pages, block_table, seq_lens, k_new, v_new):
+    """One new token per sequence into the paged cache (k_new, v_new:
+    [B, H_kv, D]); see paged_prefill_fill."""
+    return paged_prefill_fill(k_pages, v_pages, block_table, seq_lens,
+                              np.asarray(k_new)[:, :, None, :], np.asarray(v_new)[:, :, None, :])
+
+
+def paged_decode_attention(q, k_pages, v_pages, block_table, seq_lens, n_pending: int = 1, scale=None):
+    """decode_attention over the logical cache the page table describes."""
+    lengths = [max(int(x), 0) + n_pending for x in seq_lens]
+    n = max(lengths) if lengths else 0
+    k = paged_view(widen(k_pages), block_table, n, lengths)
+    v = paged_view(widen(v_pages), block_table, n, lengths)
+    return decode_attention(q, k, v, seq_lens, n_pending=n_pending, scale=scale)
+
+
 def cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, elem_bytes: int, lengths) -> int:
     """Logical K+V payload in bytes.
 

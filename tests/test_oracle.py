@@ -473,3 +473,75 @@ def test_chunk_attention_rejects_blocks_that_do_not_fit():
         oracle.chunk_attention(q, k, v, np.array([7]))
     with pytest.raises(ValueError):
         oracle.chunk_attention(q, k, v, np.array([-1]))
+
+
+# --------------------------------------------------------------- paged cache --
+
+def test_paged_view_worked_example():
+    """A page table by hand: page size 2, sequence 0 owns pages [2, 0, 3],
+    sequence 1 owns [1]; logical slot t of a sequence is row t % 2 of page
+    table[b][t // 2]. Values encode (page, row, d) so every gathered element
+    is checked against its address."""
+    n_pages, hkv, psz, d = 4, 1, 2, 3
+    pages = np.array([[[[100 * p + 10 * r + c for c in range(d)] for r in range(psz)]] for p in range(n_pages)],
+                     dtype=np.float64)
+    table = [[2, 0, 3], [1, 1, 1]]
+    got = oracle.paged_view(pages, table, 6, lengths=[6, 2])
+    assert got[0, 0, :, 0].tolist() == [200, 210, 0, 10, 300, 310]
+    assert got[1, 0, :, 0].tolist() == [100, 110, 0, 0, 0, 0]            # past its length: not gathered
+    assert got[0, 0, 4].tolist() == [300, 301, 302]
+
+
+def _paged_from_contiguous(k, v, psz, seed):
+    """Scatter a contiguous cache [B, H, T, D] into a pool through a random
+    permutation of pages, using paged_prefill_fill from slot 0."""
+    b, h, t, d = k.shape
+    per_seq = -(-t // psz)
+    n_pages = b * per_seq + 3
+    perm = np.random.default_rng(seed).permutation(n_pages)[:b * per_seq]
+    table = perm.reshape(b, per_seq).tolist()
+    kp = np.full((n_pages, h, psz, d), np.nan)
+    vp = np.full((n_pages, h, psz, d), np.nan)
+    kp, vp, ovf = oracle.paged_prefill_fill(kp, vp, table, np.zeros(b, dtype=int), k, v)
+    assert not ovf.any()
+    return kp, vp, table
+
+
+def test_paged_fill_then_view_round_trips_bitwise():
+    """Paging stores the same logical sequence (KVG, relation to
+    PagedAttention): scatter through a page table, gather back, identical."""
+    k = oracle.widen(_rand((3, 2, 37, 8), 40, "pk"))
+    v = oracle.widen(_rand((3, 2, 37, 8), 40, "pv"))
+    kp, vp, table = _paged_from_contiguous(k, v, 4, 41)
+    assert np.array_equal(oracle.paged_view(kp, table, 37), k)
+    assert np.array_equal(oracle.paged_view(vp, table, 37), v)
+
+
+def test_paged_decode_equals_contiguous_decode():
+    """The attention result does not depend on where pages sit in the pool."""
+    b, hq, hkv, t, d = 3, 8, 2, 45, 16
+    q = _rand((b, hq, d), 42, "pq")
+    k = oracle.widen(_rand((b, hkv, t, d), 42, "pk"))
+    v = oracle.widen(_rand((b, hkv, t, d), 42, "pv"))
+    kp, vp, table = _paged_from_contiguous(k, v, 8, 43)
+    lens = np.array([0, 20, 44])
+    want = oracle.decode_attention(q, k, v, lens, n_pending=1)
+    got = oracle.paged_decode_attention(q, kp, vp, table, lens, n_pending=1)
+    assert np.array_equal(got, want)
+
+
+def test_paged_append_writes_one_slot_through_the_table():
+    """The new token lands in row seq_lens[b] % P of page table[b][seq_lens[b] // P];
+    nothing else in the pool changes; a full table or a page outside the pool
+    leaves the sequence untouched and is reported."""
+    n_pages, hkv, psz, d = 6, 2, 4, 3
+    kp = np.arange(n_pages * hkv * psz * d, dtype=np.float64).reshape(n_pages, hkv, psz, d)
+    vp = -kp
+    table = [[5, 1], [0, 9], [2, 3]]
+    kn = np.full((3, hkv, d), 7.0)
+    vn = np.full((3, hkv, d), -7.0)
+    k2, v2, ovf = oracle.paged_append(kp, vp, table, np.array([6, 5, 8]), kn, vn)
+    assert ovf.tolist() == [False, True, True]        # page 9 is not in the pool; slot 8 is past 2 pages
+    assert np.array_equal(k2[1, :, 2], kn[0]) and np.array_equal(v2[1, :, 2], vn[0])
+    changed = np.argwhere(k2 != kp)
+    assert {(int(p), int(r)) for p, _, r, _ in changed} == {(1, 2)}

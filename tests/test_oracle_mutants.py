@@ -140,3 +140,21 @@ def test_chunk_mask_mutants_are_caught(kind, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"no pin caught mutant {kind}"
+
+
+@pytest.mark.parametrize("kind", ["swapped", "off_by_one_page", "row_from_page_start"])
+def test_paged_slot_mutants_are_caught(kind, monkeypatch):
+    def slot(block_table, b, t, page_size):
+        if kind == "swapped":
+            return int(block_table[b][t % page_size]), t // page_size
+        if kind == "off_by_one_page":
+            return int(block_table[b][min(t // page_size + 1, len(block_table[b]) - 1)]), t % page_size
+        return int(block_table[b][t // page_size]), 0
+    monkeypatch.setattr(ko, "paged_slot", slot)
+    caught = 0
+    for pin in (pins.test_paged_view_worked_example, pins.test_paged_fill_then_view_round_trips_bitwise):
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"no pin caught mutant {kind}"
