@@ -40,6 +40,9 @@ def _parse():
     ap.add_argument("--secondary", default="ragged_long",
                     help="second workload measured in the same run ('none' to skip)")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = library choice)")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="page size P: time the decode step on page pools through a page table "
+                         "(kvc_paged_decode_step) instead of contiguous caches")
     ap.add_argument("--block-q", type=int, default=0,
                     help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
                          "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
@@ -61,13 +64,14 @@ class Workload:
     """All L layers of one decode step, resident in HBM, with pre-marshalled
     C-ABI arguments (so the timed loop does no Python-side tensor work)."""
 
-    def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0):
+    def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0, page: int = 0):
         import torch
         import kv_cache_append_amd as kvc
         import synth
 
         self.cfg = cfg
         self.block_q = block_q        # 0: decode step; N: block of N new tokens per sequence
+        self.page = page              # 0: contiguous caches; P: page pools of P-token pages
         self.kvc = kvc
         self.lib = kvc.load()
         dev = torch.device("cuda:0")
@@ -75,7 +79,18 @@ class Workload:
         self.t_max = int(self.lengths.max()) + margin_tokens + 1
         L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
         tdt = synth.DTYPES[cfg.dtype]
-        self.k = torch.empty((L, B, Hkv, self.t_max, D), dtype=tdt, device=dev)
+        if page:
+            # page pools per layer and one page table (a random permutation of
+            # the pool's pages) shared by the layers, as a serving runtime keeps it
+            per_seq = -(-self.t_max // page)
+            self.t_max = per_seq * page
+            n_pages = B * per_seq
+            g = torch.Generator().manual_seed(synth.derive_seed(seed, cfg.name, "pages"))
+            perm = torch.randperm(n_pages, generator=g).to(torch.int32)
+            self.table = perm.reshape(B, per_seq).to(dev)
+            self.k = torch.empty((L, n_pages, Hkv, page, D), dtype=tdt, device=dev)
+        else:
+            self.k = torch.empty((L, B, Hkv, self.t_max, D), dtype=tdt, device=dev)
         self.v = torch.empty_like(self.k)
         for l in range(L):  # fill layer by layer (bounded fp32 temporaries)
             synth.normal(None, cfg.dtype, seed, cfg.name, l, "K", out=self.k[l])
@@ -90,9 +105,18 @@ class Workload:
                                   for l in range(L)])
         self.out = torch.empty((L,) + qs, dtype=torch.float32, device=dev)
         self.seq_lens = self.lengths.to(dev)
-        self.descs = [kvc.cache_desc(self.k[l], self.v[l]) for l in range(L)]
+        if page:
+            self.descs = [kvc.paged_desc(self.k[l], self.v[l], self.table) for l in range(L)]
+        else:
+            self.descs = [kvc.cache_desc(self.k[l], self.v[l]) for l in range(L)]
         self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq * nq)
-        if block_q:
+        if page:
+            # the split choice of the contiguous cache with the same capacity
+            logical = kvc.CacheDesc(self.k.data_ptr(), self.v.data_ptr(), B, Hkv, self.t_max, D,
+                                    kvc.DTYPE_CODE[tdt], 0, Hkv * self.t_max * D, self.t_max * D, D)
+            self.splits = splits if splits > 0 else int(self.lib.kvc_decode_splits(ctypes.byref(logical), Hq))
+            self.ws = kvc.paged_workspace(self.k[0], self.v[0], self.table, Hq, self.splits)
+        elif block_q:
             self.ws = kvc.block_workspace(self.k[0], self.v[0], Hq, block_q, self.splits)
         else:
             self.ws = kvc.workspace(self.k[0], self.v[0], Hq, self.splits)
@@ -122,9 +146,10 @@ class Workload:
                 if rc:
                     raise RuntimeError(f"libkvc returned {rc} at layer {l}")
             return
+        step_fn = lib.kvc_paged_decode_step if self.page else lib.kvc_decode_step
         for l in range(cfg.n_layers):
             d = ctypes.byref(self.descs[l])
-            rc = lib.kvc_decode_step(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
+            rc = step_fn(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
                                      vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
                                      vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
             if rc:
@@ -331,7 +356,7 @@ def _run_config(name, args, with_cpu):
     cfg = synth.CONFIGS[name]
     nq = max(args.block_q, 1)
     margin = (max(args.steps, args.warmup) + 2) * nq
-    w = Workload(cfg, margin, args.seed, args.splits, args.block_q)
+    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged)
     ms_total, wall, launch_ms, launch_bytes = _measure(w, args.steps, args.warmup, not args.no_graph)
     kv = w.kv_bytes(args.steps)
     gbs = kv / (ms_total / 1e3) / 1e9
@@ -353,6 +378,7 @@ def _run_config(name, args, with_cpu):
                                        "sum": int(lens.long().sum())},
             "splits": w.splits, "hip_graph": not args.no_graph,
             **({"query_block": args.block_q} if args.block_q else {}),
+            **({"page_size": args.paged} if args.paged else {}),
         },
         "roofline": {
             "bound": "hbm",

@@ -65,6 +65,8 @@ typedef enum kvc_status {
 /* Bits OR-ed into the optional device status word (uint32_t). */
 #define KVC_DEVERR_CAPACITY 1u  /* a write or read would pass max_len: that sequence was skipped/clamped */
 #define KVC_DEVERR_BADLEN   2u  /* seq_lens[b] < 0: that sequence was skipped / treated as empty */
+#define KVC_DEVERR_PAGE     8u  /* a page-table entry is not an index into the page pool: those rows were
+                                   not written (append/fill) or read as zeros (decode: outputs invalid) */
 #define KVC_DEVERR_SYNC     4u  /* a split merge gave up waiting for another workgroup (never expected;
                                    the outputs of that call are not valid) */
 
@@ -248,6 +250,73 @@ kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* seq_lens, i
  * arguments); n_splits = 0 means the library's choice.
  */
 size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t t_q, int32_t n_splits);
+
+/*
+ * Paged cache (NEXT to the contiguous one): the same logical K/V sequence per
+ * (sequence, KV head), stored in fixed-size pages of a shared pool and
+ * addressed through a per-sequence page table (glossary "KV 缓存", relation
+ * to PagedAttention: paging changes where rows live, not the sequence or the
+ * attention result; course notes §1.6 and textbook §8: it removes the
+ * fragmentation of per-sequence maximum-length allocations). Logical slot t
+ * of sequence b is row t % page_size of page block_table[b * table_stride +
+ * t / page_size]. The capacity of a sequence is pages_per_seq * page_size.
+ */
+typedef struct kvc_paged_cache {
+  void* k_pages;                /* K pool: n_pages pages of [n_kv_heads, page_size, head_dim] (strides below) */
+  void* v_pages;                /* V pool, same geometry and strides */
+  const int32_t* block_table;   /* device, row b holds the physical pages of sequence b's logical pages */
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t page_size;            /* tokens per page: a power of two; >= 16 for the decode calls */
+  int32_t head_dim;
+  int32_t dtype;                /* kvc_dtype_t */
+  int32_t n_pages;              /* pages in each pool */
+  int32_t pages_per_seq;        /* table entries per sequence */
+  int32_t table_stride;         /* elements between table rows, >= pages_per_seq */
+  int64_t stride_page;          /* element strides in the pools; head_dim is contiguous */
+  int64_t stride_h;
+  int64_t stride_t;
+} kvc_paged_cache_t;
+
+/*
+ * kvc_paged_append / kvc_paged_prefill_fill -- as kvc_append and
+ * kvc_prefill_fill, through the page table. A sequence whose block passes
+ * its capacity is skipped (KVC_DEVERR_CAPACITY); a row whose table entry is
+ * not in [0, n_pages) is not written (KVC_DEVERR_PAGE). Any dtype and head
+ * dim; page_size a power of two.
+ */
+kvc_status_t kvc_paged_append(const kvc_paged_cache_t* cache, const int32_t* seq_lens,
+                              const void* k_new, const void* v_new,
+                              int64_t new_stride_b, int64_t new_stride_h,
+                              uint32_t* dev_status, hipStream_t stream);
+kvc_status_t kvc_paged_prefill_fill(const kvc_paged_cache_t* cache, const int32_t* seq_lens,
+                                    const void* k, const void* v,
+                                    int64_t src_stride_b, int64_t src_stride_h, int64_t src_stride_t,
+                                    int32_t t_new, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * kvc_paged_decode_workspace_bytes / kvc_paged_decode_attn /
+ * kvc_paged_decode_step -- as their contiguous counterparts, reading K/V
+ * through the page table (and, for the step, writing the new row into its
+ * page). fp16/bf16 caches with head_dim a multiple of 32 and page_size a
+ * power of two >= 16 (else KVC_ERR_UNSUPPORTED). The result equals the
+ * contiguous call on the same logical cache bit for bit. A table entry
+ * outside the pool sets KVC_DEVERR_PAGE; that page reads as zeros and the
+ * sequence's output is not valid.
+ */
+size_t kvc_paged_decode_workspace_bytes(const kvc_paged_cache_t* cache, int32_t n_q_heads, int32_t n_splits);
+kvc_status_t kvc_paged_decode_attn(const kvc_paged_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                                   const void* q, int32_t n_q_heads, float scale,
+                                   void* out, int32_t out_dtype,
+                                   void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                   uint32_t* dev_status, hipStream_t stream);
+kvc_status_t kvc_paged_decode_step(const kvc_paged_cache_t* cache, const int32_t* seq_lens,
+                                   const void* k_new, const void* v_new,
+                                   int64_t new_stride_b, int64_t new_stride_h,
+                                   const void* q, int32_t n_q_heads, float scale,
+                                   void* out, int32_t out_dtype,
+                                   void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                   uint32_t* dev_status, hipStream_t stream);
 
 /*
  * kvc_seq_lens_advance -- seq_lens[b] += n for every b, on the device, once per

@@ -23,6 +23,7 @@ DTYPE_CODE = {torch.float32: KVC_F32, torch.float16: KVC_F16, torch.bfloat16: KV
 DEVERR_CAPACITY = 1
 DEVERR_BADLEN = 2
 DEVERR_SYNC = 4
+DEVERR_PAGE = 8
 
 STATUS = {
     0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_ALIGN",
@@ -32,6 +33,8 @@ STATUS = {
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
            "kvc_decode_attn", "kvc_decode_step", "kvc_block_attn", "kvc_block_workspace_bytes",
+           "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
+           "kvc_paged_decode_attn", "kvc_paged_decode_step",
            "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
 
 
@@ -81,6 +84,17 @@ def load() -> ctypes.CDLL:
     lib.kvc_block_attn.restype = i32
     lib.kvc_block_workspace_bytes.argtypes = [cp, i32, i32, i32]
     lib.kvc_block_workspace_bytes.restype = sz
+    pp = ctypes.POINTER(PagedCacheDesc)
+    lib.kvc_paged_append.argtypes = [pp, vp, vp, vp, i64, i64, vp, vp]
+    lib.kvc_paged_append.restype = i32
+    lib.kvc_paged_prefill_fill.argtypes = [pp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+    lib.kvc_paged_prefill_fill.restype = i32
+    lib.kvc_paged_decode_workspace_bytes.argtypes = [pp, i32, i32]
+    lib.kvc_paged_decode_workspace_bytes.restype = sz
+    lib.kvc_paged_decode_attn.argtypes = [pp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_paged_decode_attn.restype = i32
+    lib.kvc_paged_decode_step.argtypes = [pp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_paged_decode_step.restype = i32
     lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
     lib.kvc_seq_lens_advance.restype = i32
     lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
@@ -104,6 +118,33 @@ def _stream(stream):
 def _check(code: int, where: str):
     if code != 0:
         raise KvcError(code, where)
+
+
+class PagedCacheDesc(ctypes.Structure):
+    """Mirror of kvc_paged_cache_t."""
+    _fields_ = [
+        ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32), ("table_stride", ctypes.c_int32),
+        ("stride_page", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64),
+    ]
+
+
+def paged_desc(k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor) -> PagedCacheDesc:
+    """kvc_paged_cache_t for page pools [n_pages, H_kv, P, D] (any strides with
+    D contiguous) and an int32 device page table [B, pages_per_seq]."""
+    if k_pages.shape != v_pages.shape or k_pages.stride() != v_pages.stride() or k_pages.dim() != 4:
+        raise ValueError("page pools must be 4-D [n_pages, H_kv, P, D] with equal shape and strides")
+    if k_pages.shape[3] > 1 and k_pages.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [B, pages_per_seq] with contiguous rows")
+    n_pages, h, psz, d = k_pages.shape
+    sp, sh, st, _ = k_pages.stride()
+    b, per_seq = block_table.shape
+    return PagedCacheDesc(k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), b, h, psz, d,
+                          DTYPE_CODE[k_pages.dtype], n_pages, per_seq, block_table.stride(0), sp, sh, st)
 
 
 def cache_desc(k: torch.Tensor, v: torch.Tensor) -> CacheDesc:
@@ -217,6 +258,62 @@ def block_attn(k_cache, v_cache, seq_lens, q, out, workspace, scale=None, n_spli
                               _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
                               workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
                               _stream(stream)), "kvc_block_attn")
+
+
+def paged_prefill_fill(k_pages, v_pages, block_table, seq_lens, k, v, status=None, stream=None):
+    """kvc_paged_prefill_fill: k/v [B, H_kv, T_new, D] to logical slots [seq_lens[b], +T_new)."""
+    c = paged_desc(k_pages, v_pages, block_table)
+    if k.stride() != v.stride() or k.dim() != 4:
+        raise ValueError("k and v must be [B, H_kv, T_new, D] with equal strides")
+    _check(load().kvc_paged_prefill_fill(ctypes.byref(c), _ptr(seq_lens), _ptr(k), _ptr(v), k.stride(0),
+                                         k.stride(1), k.stride(2), k.shape[2], _ptr(status), _stream(stream)),
+           "kvc_paged_prefill_fill")
+
+
+def paged_append(k_pages, v_pages, block_table, seq_lens, k_new, v_new, status=None, stream=None):
+    """kvc_paged_append: k_new/v_new [B, H_kv, D] to logical slot seq_lens[b]."""
+    c = paged_desc(k_pages, v_pages, block_table)
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(load().kvc_paged_append(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+                                   k_new.stride(1), _ptr(status), _stream(stream)), "kvc_paged_append")
+
+
+def paged_workspace(k_pages, v_pages, block_table, n_q_heads: int, n_splits: int = 0) -> torch.Tensor:
+    c = paged_desc(k_pages, v_pages, block_table)
+    n = int(load().kvc_paged_decode_workspace_bytes(ctypes.byref(c), n_q_heads, n_splits))
+    if n == 0:
+        raise ValueError("invalid paged cache/head arguments for a decode workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=k_pages.device)
+
+
+def paged_decode_attn(k_pages, v_pages, block_table, seq_lens, q, out, workspace, n_pending: int = 1, scale=None,
+                      n_splits: int = 0, status=None, stream=None):
+    c = paged_desc(k_pages, v_pages, block_table)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    _check(load().kvc_paged_decode_attn(ctypes.byref(c), _ptr(seq_lens), n_pending, _ptr(q), q.shape[1],
+                                        float(scale), _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                                        _stream(stream)), "kvc_paged_decode_attn")
+
+
+def paged_decode_step(k_pages, v_pages, block_table, seq_lens, k_new, v_new, q, out, workspace, scale=None,
+                      n_splits: int = 0, status=None, stream=None):
+    c = paged_desc(k_pages, v_pages, block_table)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(load().kvc_paged_decode_step(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+                                        k_new.stride(1), _ptr(q), q.shape[1], float(scale), _ptr(out),
+                                        DTYPE_CODE[out.dtype], _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                                        _stream(stream)), "kvc_paged_decode_step")
 
 
 def seq_lens_advance(seq_lens, n: int = 1, stream=None):

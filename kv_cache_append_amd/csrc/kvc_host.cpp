@@ -39,6 +39,39 @@ kvc_status_t check_cache(const kvc_cache_t* c, bool need_vec16) {
   return KVC_OK;
 }
 
+kvc_status_t paged_view(const kvc_paged_cache_t* pc, bool for_decode, kvc_cache_t* view, PageInfo* info) {
+  if (pc == nullptr) return KVC_ERR_NULL;
+  const int32_t ps = pc->page_size;
+  if (ps <= 0 || (ps & (ps - 1)) != 0 || pc->n_pages <= 0 || pc->pages_per_seq <= 0 ||
+      pc->table_stride < pc->pages_per_seq)
+    return KVC_ERR_SHAPE;
+  if (for_decode && ps < 16) return KVC_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(pc->pages_per_seq) * ps > 0x7fffffffll) return KVC_ERR_SHAPE;
+  view->k = pc->k_pages;
+  view->v = pc->v_pages;
+  view->batch = pc->batch;
+  view->n_kv_heads = pc->n_kv_heads;
+  view->max_len = pc->pages_per_seq * ps;
+  view->head_dim = pc->head_dim;
+  view->dtype = pc->dtype;
+  view->reserved0 = 0;
+  view->stride_b = pc->stride_page;
+  view->stride_h = pc->stride_h;
+  view->stride_t = pc->stride_t;
+  // A page's (head, row) grid must not overlap: head-major or row-major.
+  if (pc->n_kv_heads > 1 && pc->stride_h < static_cast<int64_t>(ps) * pc->stride_t &&
+      pc->stride_t < static_cast<int64_t>(pc->n_kv_heads) * pc->stride_h)
+    return KVC_ERR_SHAPE;
+  if (pc->batch > 0 && pc->block_table == nullptr) return KVC_ERR_NULL;
+  info->table = pc->block_table;
+  info->table_stride = pc->table_stride;
+  int shift = 0;
+  while ((1 << shift) < ps) ++shift;
+  info->page_shift = shift;
+  info->n_pages = pc->n_pages;
+  return KVC_OK;
+}
+
 int copy_vector_bytes(const kvc_cache_t* c, const void* src_k, const void* src_v,
                       const int64_t* src_strides_bytes, int n_src_strides) {
   const int s = elem_bytes(c->dtype);
@@ -159,6 +192,14 @@ extern "C" size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return 0;
   const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
   return kvc::workspace_bytes(cache, n_q_heads, s);
+}
+
+extern "C" size_t kvc_paged_decode_workspace_bytes(const kvc_paged_cache_t* cache, int32_t n_q_heads,
+                                                   int32_t n_splits) {
+  kvc_cache_t view;
+  kvc::PageInfo info;
+  if (kvc::paged_view(cache, true, &view, &info) != KVC_OK) return 0;
+  return kvc_decode_workspace_bytes(&view, n_q_heads, n_splits);
 }
 
 extern "C" size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t t_q,

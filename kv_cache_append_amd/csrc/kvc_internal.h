@@ -43,6 +43,19 @@ size_t workspace_flag_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_
 size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 
+// A paged cache seen as a cache descriptor: the pools as k/v, the page
+// stride in place of stride_b, capacity pages_per_seq * page_size as
+// max_len; plus what the kernels need to walk the page table.
+struct PageInfo {
+  const int32_t* table;
+  int32_t table_stride;
+  int32_t page_shift;   // log2(page_size)
+  int32_t n_pages;
+};
+// Checks the paged descriptor (decode: page_size >= 16) and fills `view` and
+// `info`; same status codes as check_cache.
+kvc_status_t paged_view(const kvc_paged_cache_t* pc, bool for_decode, kvc_cache_t* view, PageInfo* info);
+
 }  // namespace kvc
 
 #endif  // KVC_INTERNAL_H_

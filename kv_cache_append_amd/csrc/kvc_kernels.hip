@@ -66,6 +66,10 @@ struct CopyParams {
   int32_t batch, n_kv, max_len, t_new;
   int32_t vecs_per_row;      // row bytes / VB
   int64_t total;             // batch * n_kv * t_new * vecs_per_row
+  // paged cache (table != null): cb is the page stride; slot t of sequence b
+  // is row t & (page_size - 1) of page table[b * table_stride + (t >> page_shift)]
+  const int32_t* table;
+  int32_t table_stride, page_shift, n_pages;
 };
 
 // Thread i copies one VB-byte vector of K and the same vector of V.
@@ -88,7 +92,19 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const CopyParams p) {
       continue;
     }
     const int64_t src = b * p.sb + h * p.sh + t * p.st + static_cast<int64_t>(vv) * VB;
-    const int64_t dst = b * p.cb + h * p.ch + static_cast<int64_t>(pos + t) * p.ct + static_cast<int64_t>(vv) * VB;
+    int64_t dst;
+    if (p.table != nullptr) {
+      const int slot = pos + t;
+      const int pg = p.table[static_cast<int64_t>(b) * p.table_stride + (slot >> p.page_shift)];
+      if (pg < 0 || pg >= p.n_pages) {
+        if (h == 0 && vv == 0 && p.status != nullptr) atomicOr(p.status, KVC_DEVERR_PAGE);
+        continue;
+      }
+      dst = pg * p.cb + h * p.ch + static_cast<int64_t>(slot & ((1 << p.page_shift) - 1)) * p.ct +
+            static_cast<int64_t>(vv) * VB;
+    } else {
+      dst = b * p.cb + h * p.ch + static_cast<int64_t>(pos + t) * p.ct + static_cast<int64_t>(vv) * VB;
+    }
     const V kx = *reinterpret_cast<const V*>(p.ks + src);
     const V vx = *reinterpret_cast<const V*>(p.vs + src);
     *reinterpret_cast<V*>(p.kc + dst) = kx;
@@ -285,6 +301,10 @@ struct DecodeParams {
   // of a KV head play the role of its query heads; pair v is query v / group
   // of head v % group. Decode has t_q = 1 and block = 0.
   int32_t t_q, block;
+  // Paged cache (table != null): sb is the page stride, and the 16-row tile
+  // starting at slot r lives in page table[b * table_stride + (r >> page_shift)].
+  const int32_t* table;
+  int32_t table_stride, page_shift, n_pages;
   float scale_log2;            // softmax scale * log2(e)
 };
 
@@ -327,6 +347,18 @@ template <typename ET>
 __device__ inline void store_out(const DecodeParams& p, int64_t idx, float x) {
   if (p.out_f32) F32T::store(p.out, idx, x);
   else ET::store(p.out, idx, x);
+}
+
+// Byte offset of slot `row` of (sequence b, KV head g) in the cache or page
+// pool, or -1 when its page-table entry is not in the pool.
+__device__ inline int64_t slot_offset(const DecodeParams& p, int b, int g, int row) {
+  if (p.table == nullptr) return b * p.sb + g * p.sh + static_cast<int64_t>(row) * p.st;
+  const int pg = p.table[static_cast<int64_t>(b) * p.table_stride + (row >> p.page_shift)];
+  if (pg < 0 || pg >= p.n_pages) return -1;
+  return pg * p.sb + g * p.sh + static_cast<int64_t>(row & ((1 << p.page_shift) - 1)) * p.st;
+}
+__device__ inline void flag(const DecodeParams& p, uint32_t bits) {
+  if (p.status != nullptr) atomicOr(p.status, bits);
 }
 
 // Row of q and out ([B, t_q, H_q, D], token-major) of pair v of KV head g.
@@ -478,7 +510,8 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
         store_out<ET>(p, pair_row(p, b, g, v_first + t / D) * D + t % D, 0.f);
     return;
   }
-  const int chunk = (n + p.n_splits - 1) / p.n_splits;
+  // chunks are whole 16-row tiles, so a tile never straddles two pages
+  const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
   const int t0 = split * chunk;
   if (t0 >= n) return;                               // inactive split: not counted in ns
   const int t1 = min(t0 + chunk, n);
@@ -523,12 +556,15 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       ksrc = p.k_new + noff;
       vsrc = p.v_new + noff;
     } else {
-      const int64_t coff = unit_off + static_cast<int64_t>(xrow) * p.st + li * 16;
-      ksrc = p.k + coff;
-      vsrc = p.v + coff;
+      const int64_t xo = slot_offset(p, b, g, xrow);
+      ksrc = xo < 0 ? nullptr : p.k + xo + li * 16;
+      vsrc = xo < 0 ? nullptr : p.v + xo + li * 16;
+      if (xo < 0 && lane == 0) flag(p, KVC_DEVERR_PAGE);
     }
-    nk = *reinterpret_cast<const u32x4*>(ksrc);
-    nv = *reinterpret_cast<const u32x4*>(vsrc);
+    if (ksrc != nullptr) {
+      nk = *reinterpret_cast<const u32x4*>(ksrc);
+      nv = *reinterpret_cast<const u32x4*>(vsrc);
+    }
   }
 
   // K/V of this unit through buffer resources built per tile on the scalar
@@ -596,13 +632,43 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     for (int u = 0; u < NP; ++u)
       voffm[u] = static_cast<uint32_t>(u * RPP + grp) * st + static_cast<uint32_t>(li) * 16u;
 
+    // Paged caches: a wave's tiles start at slots wbase0 + k * TSM. Lane j
+    // of `pidv` holds the page of tile (k & ~63) + j, loaded 64 tiles at a
+    // time with one vector load, and a tile's page is taken with readlane, so
+    // no page-table read waits in front of the tile loads.
+    const bool paged = p.table != nullptr;
+    const int wbase0 = t0 + wave * 16;
+    int pidv = -1, pid_block = -1;
+    auto tile_page = [&](int base) {
+      const int k = (base - wbase0) / TSM;    // wave-uniform tile index
+      if ((k >> 6) != pid_block) {
+        pid_block = k >> 6;
+        const int row = wbase0 + ((pid_block << 6) + lane) * TSM;
+        pidv = -1;
+        if (row < t_end) pidv = p.table[static_cast<int64_t>(b) * p.table_stride + (row >> p.page_shift)];
+      }
+      return __builtin_amdgcn_readlane(pidv, k & 63);
+    };
     auto load_tile = [&](int base_any, u32x4 (&K)[NM], u32x4 (&V)[NP]) {
       const int base = __builtin_amdgcn_readfirstlane(base_any);
       const int rows_left = t_end - base;
-      const uint32_t range = rows_left > 0 ? static_cast<uint32_t>(rows_left) * st : 0u;
-      const int64_t boff = static_cast<int64_t>(base) * st;
-      const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr(kunit + boff), range);
-      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr(vunit + boff), range);
+      uint32_t range = rows_left > 0 ? static_cast<uint32_t>(rows_left) * st : 0u;
+      int64_t boff = unit_off + static_cast<int64_t>(base) * st;
+      if (paged) {                            // the tile's 16 rows lie in one page
+        boff = 0;
+        if (rows_left > 0) {
+          const int pg = tile_page(base);
+          range = static_cast<uint32_t>(min(rows_left, 16)) * st;
+          if (pg < 0 || pg >= p.n_pages) {    // not in the pool: read zeros, report
+            range = 0u;
+            if (lane == 0) flag(p, KVC_DEVERR_PAGE);
+          } else {
+            boff = pg * p.sb + g * p.sh + static_cast<int64_t>(base & ((1 << p.page_shift) - 1)) * st;
+          }
+        }
+      }
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr(p.k + boff), range);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr(p.v + boff), range);
 #pragma unroll
       for (int m = 0; m < NM; ++m) K[m] = buf_load(krs, koff[m]);
 #pragma unroll
@@ -712,11 +778,12 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     }
     if (has_x && wave == 0) {                 // the last attended row, as row 0 of one more tile
       u32x4 K[NM], V[NP];
-      const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : p.k + unit_off + static_cast<int64_t>(xrow) * p.st;
+      const int64_t xo = x_new ? 0 : slot_offset(p, b, g, xrow);
+      const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : (xo < 0 ? nullptr : p.k + xo);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         K[m] = u32x4{0u, 0u, 0u, 0u};
-        if (r16 == 0) K[m] = *reinterpret_cast<const u32x4*>(kx + (4 * m + kq) * 16);
+        if (r16 == 0 && kx != nullptr) K[m] = *reinterpret_cast<const u32x4*>(kx + (4 * m + kq) * 16);
       }
 #pragma unroll
       for (int u = 0; u < NP; ++u) V[u] = (u == 0 && grp == 0) ? nv : u32x4{0u, 0u, 0u, 0u};
@@ -889,9 +956,13 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   }   // vector-ALU path
 
   if (has_x && wave == 0 && x_new && hb == 0 && grp == 0) {   // fused append: write the new row
-    const int64_t coff = unit_off + static_cast<int64_t>(arow) * p.st + li * 16;
-    *reinterpret_cast<u32x4*>(p.k + coff) = nk;
-    *reinterpret_cast<u32x4*>(p.v + coff) = nv;
+    const int64_t ao = slot_offset(p, b, g, arow);
+    if (ao >= 0) {
+      *reinterpret_cast<u32x4*>(p.k + ao + li * 16) = nk;
+      *reinterpret_cast<u32x4*>(p.v + ao + li * 16) = nv;
+    } else if (lane == 0) {
+      flag(p, KVC_DEVERR_PAGE);
+    }
   }
 
   if constexpr (kLdsMerge) {
@@ -1154,7 +1225,7 @@ DecodeKernel pick_decode_kernel(int dtype, int d, int gb) {
 
 kvc_status_t launch_copy(const kvc_cache_t* c, const int32_t* seq_lens, const void* ks, const void* vs,
                          int64_t sb, int64_t sh, int64_t st, int32_t t_new, uint32_t* status,
-                         hipStream_t stream) {
+                         hipStream_t stream, const kvc::PageInfo* pg = nullptr) {
   const int s = kvc::elem_bytes(c->dtype);
   CopyParams p;
   p.kc = static_cast<char*>(c->k);
@@ -1173,6 +1244,10 @@ kvc_status_t launch_copy(const kvc_cache_t* c, const int32_t* seq_lens, const vo
   p.n_kv = c->n_kv_heads;
   p.max_len = c->max_len;
   p.t_new = t_new;
+  p.table = pg != nullptr ? pg->table : nullptr;
+  p.table_stride = pg != nullptr ? pg->table_stride : 0;
+  p.page_shift = pg != nullptr ? pg->page_shift : 0;
+  p.n_pages = pg != nullptr ? pg->n_pages : 0;
   const int64_t src_strides[3] = {p.sb, p.sh, p.st};
   const int vb = kvc::copy_vector_bytes(c, ks, vs, src_strides, 3);
   p.vecs_per_row = static_cast<int32_t>((static_cast<int64_t>(c->head_dim) * s) / vb);
@@ -1196,7 +1271,7 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
                            const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
                            int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
                            size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status, hipStream_t stream,
-                           int32_t t_q) {
+                           int32_t t_q, const kvc::PageInfo* pg = nullptr) {
   kvc_status_t st = kvc::check_cache(cache, true);
   if (st != KVC_OK) return st;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
@@ -1266,6 +1341,12 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.scale_log2 = scale_log2;
   p.t_q = tq;
   p.block = t_q > 0 ? 1 : 0;
+  p.table = pg != nullptr ? pg->table : nullptr;
+  p.table_stride = pg != nullptr ? pg->table_stride : 0;
+  p.page_shift = pg != nullptr ? pg->page_shift : 0;
+  p.n_pages = pg != nullptr ? pg->n_pages : 0;
+  // paged caches are read by the matrix-core path only (16-row tiles)
+  if (pg != nullptr && !(s == 2 && cache->head_dim % 32 == 0)) return KVC_ERR_UNSUPPORTED;
 
   DecodeKernel k = pick_decode_kernel(cache->dtype, cache->head_dim, gb);
   if (k == nullptr) return KVC_ERR_UNSUPPORTED;
@@ -1348,4 +1429,73 @@ extern "C" kvc_status_t kvc_seq_lens_advance(int32_t* seq_lens, int32_t batch, i
   if (seq_lens == nullptr) return KVC_ERR_NULL;
   hipLaunchKernelGGL(advance_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, seq_lens, batch, n);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+// ------------------------------------------------------------ paged cache --
+
+extern "C" kvc_status_t kvc_paged_append(const kvc_paged_cache_t* cache, const int32_t* seq_lens,
+                                         const void* k_new, const void* v_new, int64_t new_stride_b,
+                                         int64_t new_stride_h, uint32_t* dev_status, hipStream_t stream) {
+  kvc_cache_t view;
+  kvc::PageInfo info;
+  kvc_status_t st = kvc::paged_view(cache, false, &view, &info);
+  if (st != KVC_OK) return st;
+  st = kvc::check_cache(&view, false);
+  if (st != KVC_OK) return st;
+  if (view.batch == 0) return KVC_OK;
+  if (seq_lens == nullptr || k_new == nullptr || v_new == nullptr) return KVC_ERR_NULL;
+  if (new_stride_b < 0 || new_stride_h < 0) return KVC_ERR_SHAPE;
+  if (view.n_kv_heads > 1 && new_stride_h < view.head_dim) return KVC_ERR_SHAPE;
+  const int s = kvc::elem_bytes(view.dtype);
+  if (reinterpret_cast<uintptr_t>(k_new) % s || reinterpret_cast<uintptr_t>(v_new) % s) return KVC_ERR_ALIGN;
+  return launch_copy(&view, seq_lens, k_new, v_new, new_stride_b, new_stride_h, 0, 1, dev_status, stream, &info);
+}
+
+extern "C" kvc_status_t kvc_paged_prefill_fill(const kvc_paged_cache_t* cache, const int32_t* seq_lens,
+                                               const void* k, const void* v, int64_t src_stride_b,
+                                               int64_t src_stride_h, int64_t src_stride_t, int32_t t_new,
+                                               uint32_t* dev_status, hipStream_t stream) {
+  kvc_cache_t view;
+  kvc::PageInfo info;
+  kvc_status_t st = kvc::paged_view(cache, false, &view, &info);
+  if (st != KVC_OK) return st;
+  st = kvc::check_cache(&view, false);
+  if (st != KVC_OK) return st;
+  if (t_new < 0) return KVC_ERR_SHAPE;
+  if (view.batch == 0 || t_new == 0) return KVC_OK;
+  if (seq_lens == nullptr || k == nullptr || v == nullptr) return KVC_ERR_NULL;
+  if (src_stride_b < 0 || src_stride_h < 0 || src_stride_t < 0) return KVC_ERR_SHAPE;
+  if (t_new > 1 && src_stride_t < view.head_dim) return KVC_ERR_SHAPE;
+  const int s = kvc::elem_bytes(view.dtype);
+  if (reinterpret_cast<uintptr_t>(k) % s || reinterpret_cast<uintptr_t>(v) % s) return KVC_ERR_ALIGN;
+  return launch_copy(&view, seq_lens, k, v, src_stride_b, src_stride_h, src_stride_t, t_new, dev_status, stream,
+                     &info);
+}
+
+extern "C" kvc_status_t kvc_paged_decode_attn(const kvc_paged_cache_t* cache, const int32_t* seq_lens,
+                                              int32_t n_pending, const void* q, int32_t n_q_heads, float scale,
+                                              void* out, int32_t out_dtype, void* workspace,
+                                              size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status,
+                                              hipStream_t stream) {
+  kvc_cache_t view;
+  kvc::PageInfo info;
+  const kvc_status_t st = kvc::paged_view(cache, true, &view, &info);
+  if (st != KVC_OK) return st;
+  return launch_decode(&view, seq_lens, n_pending, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype,
+                       workspace, workspace_bytes, n_splits, dev_status, stream, 0, &info);
+}
+
+extern "C" kvc_status_t kvc_paged_decode_step(const kvc_paged_cache_t* cache, const int32_t* seq_lens,
+                                              const void* k_new, const void* v_new, int64_t new_stride_b,
+                                              int64_t new_stride_h, const void* q, int32_t n_q_heads, float scale,
+                                              void* out, int32_t out_dtype, void* workspace,
+                                              size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status,
+                                              hipStream_t stream) {
+  kvc_cache_t view;
+  kvc::PageInfo info;
+  const kvc_status_t st = kvc::paged_view(cache, true, &view, &info);
+  if (st != KVC_OK) return st;
+  if (view.batch > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_NULL;
+  return launch_decode(&view, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
+                       out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, 0, &info);
 }

@@ -313,26 +313,29 @@ def paged_view(pages, block_table, n_tokens: int, lengths=None):
 def paged_prefill_fill(k_pages, v_pages, block_table, seq_lens, k, v):
     """Write T_new tokens per sequence at logical slots [seq_lens[b],
     seq_lens[b] + T_new) through the page table ([W1D4 §3.1] update, paged).
-    A sequence whose block passes the table's capacity, or whose pages are
-    not valid pool indices, is left untouched and reported in `overflow`.
-    k, v: [B, H_kv, T_new, D]. Returns (k_pages', v_pages', overflow)."""
+    A sequence whose block passes the table's capacity is left untouched;
+    a row whose table entry is not a valid pool index is not written. Both
+    are reported in `flagged`. k, v: [B, H_kv, T_new, D].
+    Returns (k_pages', v_pages', flagged)."""
     k_out = np.array(k_pages, copy=True)
     v_out = np.array(v_pages, copy=True)
     n_pages, _, page_size, _ = k_out.shape
     batch, _, t_new, _ = np.asarray(k).shape
     cap = len(block_table[0]) * page_size if batch else 0
-    overflow = np.zeros(batch, dtype=bool)
+    flagged = np.zeros(batch, dtype=bool)
     for b in range(batch):
         pos = int(seq_lens[b])
-        slots = [(paged_slot(block_table, b, pos + i, page_size)) for i in range(t_new)
-                 if 0 <= pos and pos + i < cap]
-        if pos < 0 or pos + t_new > cap or any(not 0 <= pg < n_pages for pg, _ in slots):
-            overflow[b] = True
+        if pos < 0 or pos + t_new > cap:
+            flagged[b] = True
             continue
-        for i, (pg, r) in enumerate(slots):
+        for i in range(t_new):
+            pg, r = paged_slot(block_table, b, pos + i, page_size)
+            if not 0 <= pg < n_pages:
+                flagged[b] = True
+                continue
             k_out[pg, :, r, :] = np.asarray(k)[b, :, i, :]
             v_out[pg, :, r, :] = np.asarray(v)[b, :, i, :]
-    return k_out, v_out, overflow
+    return k_out, v_out, flagged
 
 
 def paged_append(k_pages, v_pages, block_table, seq_lens, k_new, v_new):

@@ -231,3 +231,39 @@ def test_block_validation_and_workspace():
     assert lib.kvc_block_workspace_bytes(ctypes.byref(c), 3, 2, 0) == 0
     need = lib.kvc_block_workspace_bytes(ctypes.byref(c), 4, 3, 0)
     assert lib.kvc_block_attn(ctypes.byref(c), FAKE, 3, FAKE, 4, 0.1, FAKE, 0, FAKE, need - 1, 0, None, None) == 6
+
+
+def _pdesc(kvc, **kw):
+    base = dict(k_pages=64, v_pages=128, block_table=256, batch=2, n_kv_heads=2, page_size=16, head_dim=128,
+                dtype=kvc.KVC_BF16, n_pages=10, pages_per_seq=4, table_stride=4, stride_page=2 * 16 * 128,
+                stride_h=16 * 128, stride_t=128)
+    base.update(kw)
+    return kvc.PagedCacheDesc(**base)
+
+
+def test_paged_validation_and_workspace():
+    """Paged calls: page size a power of two (>= 16 for decode), table present,
+    non-overlapping page geometry; decode only on 16-bit caches with head_dim
+    a multiple of 32; workspace equals the contiguous one of the same batch,
+    heads and capacity."""
+    kvc, lib = _lib()
+    big = 1 << 30
+    ok = _pdesc(kvc)
+
+    def dec(d):
+        return lib.kvc_paged_decode_attn(ctypes.byref(d), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, FAKE, big, 0, None, None)
+
+    assert dec(_pdesc(kvc, page_size=24)) == 2
+    assert dec(_pdesc(kvc, page_size=8, stride_h=8 * 128, stride_page=2 * 8 * 128)) == 7
+    assert dec(_pdesc(kvc, block_table=None)) == 1
+    assert dec(_pdesc(kvc, table_stride=3)) == 2
+    assert dec(_pdesc(kvc, stride_h=100 * 128 // 100)) == 2          # heads overlap rows of a page
+    assert dec(_pdesc(kvc, dtype=kvc.KVC_F32, stride_page=2 * 16 * 128, stride_h=16 * 128)) == 7
+    # fill/append take P = 8: validation passes and stops at the missing seq_lens (nothing launched)
+    assert lib.kvc_paged_append(ctypes.byref(_pdesc(kvc, page_size=8, stride_h=8 * 128, stride_page=2048)),
+                                None, FAKE, FAKE, 256, 128, None, None) == 1
+    assert lib.kvc_paged_append(None, FAKE, FAKE, FAKE, 256, 128, None, None) == 1
+    contig = _desc(kvc, batch=2, n_kv_heads=2, max_len=64, stride_t=128, stride_h=64 * 128, stride_b=2 * 64 * 128)
+    for s in (0, 1, 3):
+        assert lib.kvc_paged_decode_workspace_bytes(ctypes.byref(ok), 4, s) == \
+            lib.kvc_decode_workspace_bytes(ctypes.byref(contig), 4, s)

@@ -532,8 +532,8 @@ def test_paged_decode_equals_contiguous_decode():
 
 def test_paged_append_writes_one_slot_through_the_table():
     """The new token lands in row seq_lens[b] % P of page table[b][seq_lens[b] // P];
-    nothing else in the pool changes; a full table or a page outside the pool
-    leaves the sequence untouched and is reported."""
+    nothing else in the pool changes; a full table, or a page outside the
+    pool, leaves the row unwritten and is reported."""
     n_pages, hkv, psz, d = 6, 2, 4, 3
     kp = np.arange(n_pages * hkv * psz * d, dtype=np.float64).reshape(n_pages, hkv, psz, d)
     vp = -kp
