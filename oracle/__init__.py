@@ -36,6 +36,9 @@ from .kvc_oracle import (  # noqa: F401
     prealloc_append_positions,
     prefill_fill,
     project,
+    ring_append,
+    ring_decode_attention,
+    ring_slot,
     toy_path_a,
     toy_path_b,
     widen,

@@ -274,6 +274,53 @@ def toy_path_b(x, wq, wk, wv, wo, n_q: int, n_kv: int, head_dim: int, n_prompt: 
     return np.stack(outputs), np.stack(contexts), k_cache, v_cache
 
 
+# ------------------------------------------------------- sliding window --
+#
+# [W1D4 §2.7] sliding-window attention (Mistral): every layer attends only the
+# most recent W tokens, so its cache is capped at W; [W1D4 §1.6]: with RoPE
+# the positions stay baked into the cached K, so the window can roll over a
+# fixed buffer without rebuilding it; [KVG] "与上下游术语的关系": this caps the
+# read length only because the layer itself limits what it sees (it is not a
+# lossless truncation of full attention). Here the cache of a window-W layer
+# has W slots; token number t of a sequence (t counted from 0 over its whole
+# history) lives in slot t % W, overwriting token t - W.
+
+
+def ring_slot(t: int, window: int) -> int:
+    """Slot of token number t in a ring of `window` slots."""
+    return t % window
+
+
+def ring_append(k_cache, v_cache, seq_lens, k_new, v_new):
+    """Write token number seq_lens[b] of each sequence into slot
+    seq_lens[b] % W of its ring (W = the cache's T_max), overwriting the token
+    W positions older. Arrays [B, H_kv, W, D]; k_new, v_new [B, H_kv, D]. A
+    negative count leaves the sequence untouched. Returns (k', v')."""
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    window = k_out.shape[2]
+    for b in range(k_out.shape[0]):
+        t = int(seq_lens[b])
+        if t < 0:
+            continue
+        s = ring_slot(t, window)
+        k_out[b, :, s, :] = np.asarray(k_new)[b]
+        v_out[b, :, s, :] = np.asarray(v_new)[b]
+    return k_out, v_out
+
+
+def ring_decode_attention(q, k_cache, v_cache, seq_lens, n_pending: int = 1, scale=None):
+    """Decode with a sliding window of W = the cache's T_max slots: each
+    sequence attends its most recent min(seq_lens[b] + n_pending, W) tokens,
+    which occupy slots [0, min(seq_lens[b] + n_pending, W)) of the ring in
+    rotated order. With no mask the result does not depend on the order of
+    the (key, value) rows (pinned by the permutation test), so this is the
+    single-query decode over those slots."""
+    window = np.asarray(widen(k_cache)).shape[2]
+    n = [min(max(int(x), 0) + n_pending, window) for x in seq_lens]
+    return decode_attention(q, k_cache, v_cache, np.array(n) - n_pending, n_pending=n_pending, scale=scale)
+
+
 # ------------------------------------------------------------ paged cache --
 #
 # [KVG] "与上下游术语的关系" and the note under the slot figure, [W1D4] §1.6

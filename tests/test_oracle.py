@@ -545,3 +545,47 @@ def test_paged_append_writes_one_slot_through_the_table():
     assert np.array_equal(k2[1, :, 2], kn[0]) and np.array_equal(v2[1, :, 2], vn[0])
     changed = np.argwhere(k2 != kp)
     assert {(int(p), int(r)) for p, _, r, _ in changed} == {(1, 2)}
+
+
+# ----------------------------------------------------------- sliding window --
+
+def _ring_from_history(k_hist, v_hist, window):
+    """Append a whole history token by token into a ring of `window` slots."""
+    b, h, t, d = k_hist.shape
+    kr = np.full((b, h, window, d), np.nan)
+    vr = np.full((b, h, window, d), np.nan)
+    for i in range(t):
+        kr, vr = oracle.ring_append(kr, vr, np.full(b, i), k_hist[:, :, i], v_hist[:, :, i])
+    return kr, vr
+
+
+@pytest.mark.parametrize("t_hist,window", [(5, 8), (8, 8), (9, 8), (37, 8), (100, 16)])
+def test_ring_decode_equals_attention_over_the_last_w_tokens(t_hist, window):
+    """W1D4 §2.7: a window-W layer attends the most recent W tokens. After
+    appending a history of T tokens one by one into a W-slot ring, the ring
+    decode equals the plain decode over rows [max(0, T - W), T) of the full
+    history (contiguous, in order), up to fp64 rounding order."""
+    b, hq, hkv, d = 2, 8, 2, 16
+    k_hist = oracle.widen(_rand((b, hkv, t_hist, d), 50, "rk", t_hist))
+    v_hist = oracle.widen(_rand((b, hkv, t_hist, d), 50, "rv", t_hist))
+    q = oracle.widen(_rand((b, hq, d), 50, "rq", t_hist))
+    kr, vr = _ring_from_history(k_hist, v_hist, window)
+    got = oracle.ring_decode_attention(q, kr, vr, np.full(b, t_hist - 1), n_pending=1)
+    lo = max(0, t_hist - window)
+    want = oracle.decode_attention(q, k_hist[:, :, lo:], v_hist[:, :, lo:], np.full(b, t_hist - lo - 1), n_pending=1)
+    assert np.abs(got - want).max() < 1e-14
+
+
+def test_ring_slots_hold_the_last_w_tokens():
+    """Closed form: after T appends, slot t % W holds token t for t in [T - W, T)."""
+    b, h, t_hist, d, window = 1, 2, 23, 4, 8
+    k_hist = np.arange(b * h * t_hist * d, dtype=np.float64).reshape(b, h, t_hist, d)
+    kr, _ = _ring_from_history(k_hist, -k_hist, window)
+    for t in range(t_hist - window, t_hist):
+        assert np.array_equal(kr[0, :, t % window], k_hist[0, :, t])
+
+
+def test_ring_append_ignores_negative_counts():
+    kr = np.zeros((2, 1, 4, 2))
+    k2, _ = oracle.ring_append(kr, kr, np.array([-1, 6]), np.ones((2, 1, 2)), np.ones((2, 1, 2)))
+    assert np.array_equal(k2[0], kr[0]) and k2[1, 0, 2].tolist() == [1.0, 1.0]

@@ -158,3 +158,31 @@ def test_paged_slot_mutants_are_caught(kind, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"no pin caught mutant {kind}"
+
+
+@pytest.mark.parametrize("kind", ["slot_plus_one", "window_plus_one", "oldest_first_only"])
+def test_ring_mutants_are_caught(kind, monkeypatch):
+    real_slot, real_dec = ko.ring_slot, ko.ring_decode_attention
+    if kind == "slot_plus_one":
+        monkeypatch.setattr(ko, "ring_slot", lambda t, w: (t + 1) % w)
+    elif kind == "window_plus_one":
+        def dec(q, k, v, seq_lens, n_pending=1, scale=None):
+            w = np.asarray(ko.widen(k)).shape[2]
+            n = [min(max(int(x), 0) + n_pending + 1, w) for x in seq_lens]
+            return ko.decode_attention(q, k, v, np.array(n) - n_pending, n_pending=n_pending, scale=scale)
+        monkeypatch.setattr(oracle, "ring_decode_attention", dec)
+    else:
+        def dec(q, k, v, seq_lens, n_pending=1, scale=None):
+            w = np.asarray(ko.widen(k)).shape[2]
+            n = [min(max(int(x), 0) + n_pending, w) - 1 for x in seq_lens]
+            return ko.decode_attention(q, k, v, np.array(n) - n_pending, n_pending=n_pending, scale=scale)
+        monkeypatch.setattr(oracle, "ring_decode_attention", dec)
+    caught = 0
+    for pin in (lambda: pins.test_ring_decode_equals_attention_over_the_last_w_tokens(37, 8),
+                lambda: pins.test_ring_decode_equals_attention_over_the_last_w_tokens(5, 8),
+                pins.test_ring_slots_hold_the_last_w_tokens):
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"no pin caught mutant {kind}"
