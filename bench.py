@@ -43,6 +43,9 @@ def _parse():
     ap.add_argument("--paged", type=int, default=0,
                     help="page size P: time the decode step on page pools through a page table "
                          "(kvc_paged_decode_step) instead of contiguous caches")
+    ap.add_argument("--ring", type=int, default=0,
+                    help="window W: time the decode step on ring caches of W slots (kvc_ring_decode_step, "
+                         "sliding-window attention over the most recent W tokens) instead of full caches")
     ap.add_argument("--block-q", type=int, default=0,
                     help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
                          "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
@@ -64,7 +67,8 @@ class Workload:
     """All L layers of one decode step, resident in HBM, with pre-marshalled
     C-ABI arguments (so the timed loop does no Python-side tensor work)."""
 
-    def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0, page: int = 0):
+    def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0, page: int = 0,
+                 ring: int = 0):
         import torch
         import kv_cache_append_amd as kvc
         import synth
@@ -72,11 +76,12 @@ class Workload:
         self.cfg = cfg
         self.block_q = block_q        # 0: decode step; N: block of N new tokens per sequence
         self.page = page              # 0: contiguous caches; P: page pools of P-token pages
+        self.ring = ring              # 0: full caches; W: ring caches of the most recent W tokens
         self.kvc = kvc
         self.lib = kvc.load()
         dev = torch.device("cuda:0")
         self.lengths = cfg.lengths(seed)
-        self.t_max = int(self.lengths.max()) + margin_tokens + 1
+        self.t_max = ring if ring else int(self.lengths.max()) + margin_tokens + 1
         L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
         tdt = synth.DTYPES[cfg.dtype]
         if page:
@@ -146,7 +151,8 @@ class Workload:
                 if rc:
                     raise RuntimeError(f"libkvc returned {rc} at layer {l}")
             return
-        step_fn = lib.kvc_paged_decode_step if self.page else lib.kvc_decode_step
+        step_fn = (lib.kvc_paged_decode_step if self.page else
+                   lib.kvc_ring_decode_step if self.ring else lib.kvc_decode_step)
         for l in range(cfg.n_layers):
             d = ctypes.byref(self.descs[l])
             rc = step_fn(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
@@ -162,18 +168,24 @@ class Workload:
         if self.lib.kvc_seq_lens_advance(seq, self.cfg.batch, max(self.block_q, 1), ctypes.c_void_p(stream_handle)):
             raise RuntimeError("kvc_seq_lens_advance failed")
 
+    def attended_tokens(self, step_index: int) -> int:
+        """Tokens all sequences attend at step `step_index` from the reset
+        lengths (a ring caps each sequence at its window)."""
+        nq = max(self.block_q, 1)
+        lens = self.lengths.to("cpu").long() + nq * (step_index + 1)
+        if self.ring:
+            lens = lens.clamp(max=self.ring)
+        return int(lens.sum())
+
     def kv_bytes(self, steps: int) -> int:
         """KV bytes read by `steps` steps starting from the reset lengths."""
         per_token = 2 * self.cfg.n_layers * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
-        base = int(self.lengths.to("cpu").long().sum())
-        b = self.cfg.batch * max(self.block_q, 1)
-        return per_token * sum(base + b * (k + 1) for k in range(steps))
+        return per_token * sum(self.attended_tokens(k) for k in range(steps))
 
     def decode_launch_bytes(self, step_index: int) -> int:
         """Algorithmic K+V bytes one decode launch (one layer) reads at a step."""
         per_token = 2 * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
-        nq = max(self.block_q, 1)
-        return per_token * (int(self.lengths.long().sum()) + self.cfg.batch * nq * (step_index + 1))
+        return per_token * self.attended_tokens(step_index)
 
 
 def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
@@ -356,7 +368,9 @@ def _run_config(name, args, with_cpu):
     cfg = synth.CONFIGS[name]
     nq = max(args.block_q, 1)
     margin = (max(args.steps, args.warmup) + 2) * nq
-    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged)
+    if args.ring and (args.block_q or args.paged):
+        raise SystemExit("--ring takes neither --block-q nor --paged")
+    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring)
     ms_total, wall, launch_ms, launch_bytes = _measure(w, args.steps, args.warmup, not args.no_graph)
     kv = w.kv_bytes(args.steps)
     gbs = kv / (ms_total / 1e3) / 1e9
@@ -379,11 +393,14 @@ def _run_config(name, args, with_cpu):
             "splits": w.splits, "hip_graph": not args.no_graph,
             **({"query_block": args.block_q} if args.block_q else {}),
             **({"page_size": args.paged} if args.paged else {}),
+            **({"window": args.ring} if args.ring else {}),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": ("copy_rows_kernel + decode_kernel (kvc_prefill_fill + kvc_block_attn per layer; time per "
                        "layer covers both)" if args.block_q else
+                       "decode_kernel (kvc_ring_decode_step: ring append + windowed attention + merge, one "
+                       "launch per layer)" if args.ring else
                        "decode_kernel (kvc_decode_step: append + attention + merge, one launch per layer)"),
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -252,6 +252,48 @@ kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* seq_lens, i
 size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t t_q, int32_t n_splits);
 
 /*
+ * Ring cache for sliding-window layers (course notes "第 1 周 · Day 4" §2.7:
+ * a layer that only attends its most recent W tokens needs a cache of W
+ * slots; §1.6: with rotary positions baked into the cached K, the window can
+ * roll over a fixed buffer). A kvc_cache_t whose max_len is the window W;
+ * seq_lens[b] counts every token sequence b has seen (not capped at W), and
+ * token number t lives in slot t % W, overwriting token t - W.
+ *
+ * kvc_ring_append / kvc_ring_prefill_fill -- write token numbers
+ * seq_lens[b] .. seq_lens[b] + t_new - 1 into their slots (of a block longer
+ * than W only the last W rows are written, the others would be overwritten
+ * within the block). Never a capacity error; seq_lens[b] < 0 skips the
+ * sequence (KVC_DEVERR_BADLEN). Any dtype and head dim.
+ *
+ * kvc_ring_decode_attn / kvc_ring_decode_step -- each sequence attends its
+ * most recent min(seq_lens[b] + n_pending, W) tokens (n_pending = 1 for the
+ * step, which also writes the new token into slot seq_lens[b] % W). With no
+ * mask the order of the slots does not matter. Arguments, workspace
+ * (kvc_decode_workspace_bytes) and errors as for the contiguous calls; the
+ * step equals kvc_ring_append + kvc_ring_decode_attn bit for bit.
+ */
+kvc_status_t kvc_ring_append(const kvc_cache_t* cache, const int32_t* seq_lens,
+                             const void* k_new, const void* v_new,
+                             int64_t new_stride_b, int64_t new_stride_h,
+                             uint32_t* dev_status, hipStream_t stream);
+kvc_status_t kvc_ring_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens,
+                                   const void* k, const void* v,
+                                   int64_t src_stride_b, int64_t src_stride_h, int64_t src_stride_t,
+                                   int32_t t_new, uint32_t* dev_status, hipStream_t stream);
+kvc_status_t kvc_ring_decode_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                                  const void* q, int32_t n_q_heads, float scale,
+                                  void* out, int32_t out_dtype,
+                                  void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                  uint32_t* dev_status, hipStream_t stream);
+kvc_status_t kvc_ring_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens,
+                                  const void* k_new, const void* v_new,
+                                  int64_t new_stride_b, int64_t new_stride_h,
+                                  const void* q, int32_t n_q_heads, float scale,
+                                  void* out, int32_t out_dtype,
+                                  void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                  uint32_t* dev_status, hipStream_t stream);
+
+/*
  * Paged cache (NEXT to the contiguous one): the same logical K/V sequence per
  * (sequence, KV head), stored in fixed-size pages of a shared pool and
  * addressed through a per-sequence page table (glossary "KV 缓存", relation

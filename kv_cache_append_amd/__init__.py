@@ -35,6 +35,7 @@ EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_
            "kvc_decode_attn", "kvc_decode_step", "kvc_block_attn", "kvc_block_workspace_bytes",
            "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
            "kvc_paged_decode_attn", "kvc_paged_decode_step",
+           "kvc_ring_append", "kvc_ring_prefill_fill", "kvc_ring_decode_attn", "kvc_ring_decode_step",
            "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
 
 
@@ -95,6 +96,14 @@ def load() -> ctypes.CDLL:
     lib.kvc_paged_decode_attn.restype = i32
     lib.kvc_paged_decode_step.argtypes = [pp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_paged_decode_step.restype = i32
+    lib.kvc_ring_append.argtypes = [cp, vp, vp, vp, i64, i64, vp, vp]
+    lib.kvc_ring_append.restype = i32
+    lib.kvc_ring_prefill_fill.argtypes = [cp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+    lib.kvc_ring_prefill_fill.restype = i32
+    lib.kvc_ring_decode_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_ring_decode_attn.restype = i32
+    lib.kvc_ring_decode_step.argtypes = [cp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_ring_decode_step.restype = i32
     lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
     lib.kvc_seq_lens_advance.restype = i32
     lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
@@ -314,6 +323,54 @@ def paged_decode_step(k_pages, v_pages, block_table, seq_lens, k_new, v_new, q, 
                                         DTYPE_CODE[out.dtype], _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
                                         _stream(stream)), "kvc_paged_decode_step")
+
+
+def ring_append(k_cache, v_cache, seq_lens, k_new, v_new, status=None, stream=None):
+    """kvc_ring_append: token number seq_lens[b] into slot seq_lens[b] % W (W = T_max)."""
+    c = cache_desc(k_cache, v_cache)
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(load().kvc_ring_append(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+                                  k_new.stride(1), _ptr(status), _stream(stream)), "kvc_ring_append")
+
+
+def ring_prefill_fill(k_cache, v_cache, seq_lens, k, v, status=None, stream=None):
+    """kvc_ring_prefill_fill: k/v [B, H_kv, T_new, D] as token numbers seq_lens[b].. into the ring."""
+    c = cache_desc(k_cache, v_cache)
+    if k.stride() != v.stride() or k.dim() != 4:
+        raise ValueError("k and v must be [B, H_kv, T_new, D] with equal strides")
+    _check(load().kvc_ring_prefill_fill(ctypes.byref(c), _ptr(seq_lens), _ptr(k), _ptr(v), k.stride(0),
+                                        k.stride(1), k.stride(2), k.shape[2], _ptr(status), _stream(stream)),
+           "kvc_ring_prefill_fill")
+
+
+def ring_decode_attn(k_cache, v_cache, seq_lens, q, out, workspace, n_pending: int = 1, scale=None,
+                     n_splits: int = 0, status=None, stream=None):
+    c = cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    _check(load().kvc_ring_decode_attn(ctypes.byref(c), _ptr(seq_lens), n_pending, _ptr(q), q.shape[1],
+                                       float(scale), _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                                       _stream(stream)), "kvc_ring_decode_attn")
+
+
+def ring_decode_step(k_cache, v_cache, seq_lens, k_new, v_new, q, out, workspace, scale=None, n_splits: int = 0,
+                     status=None, stream=None):
+    c = cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(load().kvc_ring_decode_step(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+                                       k_new.stride(1), _ptr(q), q.shape[1], float(scale), _ptr(out),
+                                       DTYPE_CODE[out.dtype], _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                                       _stream(stream)), "kvc_ring_decode_step")
 
 
 def seq_lens_advance(seq_lens, n: int = 1, stream=None):

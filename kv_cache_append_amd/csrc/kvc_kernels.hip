@@ -70,6 +70,10 @@ struct CopyParams {
   // is row t & (page_size - 1) of page table[b * table_stride + (t >> page_shift)]
   const int32_t* table;
   int32_t table_stride, page_shift, n_pages;
+
+  // ring cache (ring != 0): token number pos + t goes to slot (pos + t) % max_len;
+  // of a block longer than the ring only its last max_len rows are written
+  int32_t ring;
 };
 
 // Thread i copies one VB-byte vector of K and the same vector of V.
@@ -86,6 +90,19 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const CopyParams p) {
     const int h = static_cast<int>(j % p.n_kv);
     const int b = static_cast<int>(j / p.n_kv);
     const int32_t pos = p.seq_lens[b];
+    if (p.ring) {
+      if (pos < 0) {
+        if (h == 0 && t == 0 && vv == 0 && p.status != nullptr) atomicOr(p.status, KVC_DEVERR_BADLEN);
+        continue;
+      }
+      if (t < p.t_new - p.max_len) continue;    // overwritten by a later row of the same block
+      const int slot = static_cast<int>((static_cast<int64_t>(pos) + t) % p.max_len);
+      const int64_t src = b * p.sb + h * p.sh + t * p.st + static_cast<int64_t>(vv) * VB;
+      const int64_t dst = b * p.cb + h * p.ch + static_cast<int64_t>(slot) * p.ct + static_cast<int64_t>(vv) * VB;
+      *reinterpret_cast<V*>(p.kc + dst) = *reinterpret_cast<const V*>(p.ks + src);
+      *reinterpret_cast<V*>(p.vc + dst) = *reinterpret_cast<const V*>(p.vs + src);
+      continue;
+    }
     if (pos < 0 || pos > p.max_len - p.t_new) {
       if (h == 0 && t == 0 && vv == 0 && p.status != nullptr)
         atomicOr(p.status, pos < 0 ? (KVC_DEVERR_BADLEN | KVC_DEVERR_CAPACITY) : KVC_DEVERR_CAPACITY);
@@ -305,12 +322,17 @@ struct DecodeParams {
   // starting at slot r lives in page table[b * table_stride + (r >> page_shift)].
   const int32_t* table;
   int32_t table_stride, page_shift, n_pages;
+  // Ring cache (ring != 0): max_len slots hold the most recent max_len
+  // tokens, token number t in slot t % max_len; decode attends
+  // min(seq_lens[b] + n_pending, max_len) slots.
+  int32_t ring;
   float scale_log2;            // softmax scale * log2(e)
 };
 
 struct SeqInfo {
   int n;           // tokens attended
   int append_row;  // slot the fused append writes, or -1
+  int newest;      // slot of the newest attended token (ring caches; else n - 1)
   uint32_t flags;  // KVC_DEVERR_* bits
 };
 
@@ -322,10 +344,18 @@ __device__ inline SeqInfo seq_info(const DecodeParams& p, int b) {
   if (c0 < 0) si.flags |= KVC_DEVERR_BADLEN;
   si.append_row = -1;
   int n;
+  if (p.ring) {                   // sliding window: no capacity limit, the ring wraps
+    if (c0 >= 0 && p.k_new != nullptr) si.append_row = c0 % p.max_len;
+    n = c0 < 0 ? 0 : min(c0 + (p.k_new != nullptr ? 1 : p.n_pending), p.max_len);
+    si.n = n;
+    si.newest = c0 < 0 ? -1 : (c0 + (p.k_new != nullptr ? 1 : p.n_pending) - 1) % p.max_len;
+    return si;
+  }
   if (p.block) {                  // the whole block must fit: else flagged, zero rows
     n = c0 + p.t_q;
     if (c0 >= 0 && n > p.max_len) si.flags |= KVC_DEVERR_CAPACITY;
     si.n = (c0 < 0 || n > p.max_len) ? 0 : n;
+    si.newest = si.n - 1;
     return si;
   }
   if (p.k_new != nullptr) {
@@ -340,6 +370,7 @@ __device__ inline SeqInfo seq_info(const DecodeParams& p, int b) {
     si.flags |= KVC_DEVERR_CAPACITY;
   }
   si.n = n;
+  si.newest = n - 1;
   return si;
 }
 
@@ -542,11 +573,16 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   // launch. Both entry points thus add the same rows in the same order, and
   // kvc_decode_step matches kvc_append + kvc_decode_attn bit for bit.
   const int arow = si.append_row;
-  const int xrow = n - 1;
+  const int xrow = si.newest;
   const bool has_x = xrow >= t0 && xrow < t1;
   const bool x_new = has_x && arow == xrow;
-  // rows streamed from the cache: [t0, t_end) (a scalar, like every loop bound below)
-  const int t_end = __builtin_amdgcn_readfirstlane(has_x ? xrow : t1);
+  // Rows streamed from the cache: [t0, t_end) (a scalar, like every loop
+  // bound below). A wrapped ring's newest slot can sit inside the chunk: then
+  // the chunk is streamed as two segments, [t0, newest) and (newest, t1), so
+  // that no tile ever needs a mask for that slot.
+  int t_end = __builtin_amdgcn_readfirstlane(has_x ? xrow : t1);
+  const int n_seg = (p.ring != 0 && has_x && xrow != t1 - 1) ? 2 : 1;
+  const int seg1_lo = __builtin_amdgcn_readfirstlane(xrow + 1);
   u32x4 nk = u32x4{0u, 0u, 0u, 0u}, nv = u32x4{0u, 0u, 0u, 0u};
   if (has_x && wave == 0) {
     const char* ksrc;
@@ -754,8 +790,11 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       __builtin_amdgcn_wave_barrier();
     };
 
-    {
-      int base = __builtin_amdgcn_readfirstlane(t0 + wave * 16);
+    // (a second segment occurs on contiguous ring caches only, so the page
+    // lookup, which counts tiles from t0, never sees one)
+    for (int seg = 0; seg < n_seg; ++seg) {
+      if (seg == 1) t_end = t1;
+      int base = __builtin_amdgcn_readfirstlane((seg == 0 ? t0 : seg1_lo) + wave * 16);
       const int n_tiles = base < t_end ? (t_end - base + TSM - 1) / TSM : 0;
       if (n_tiles > 0) {
         u32x4 KB[NBM][NM], VB[NBM][NP];
@@ -908,8 +947,8 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     int row_at[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      bias[u] = rel_row[u] < rows_left ? 0.f : -INFINITY;
       row_at[u] = base + rel_row[u];
+      bias[u] = rel_row[u] < rows_left ? 0.f : -INFINITY;
     }
     compute_rows(K, V, bias, row_at);
   };
@@ -917,9 +956,10 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   // Register ring of NB tiles: NB - 1 tiles of loads in flight behind the
   // one being computed. `base` is this wave's first row of a tile
   // (wave-uniform); tiles past t_end read as zeros and are never computed.
-  {
+  for (int seg = 0; seg < n_seg; ++seg) {
+    if (seg == 1) t_end = t1;
     constexpr int NB = KVC_PREFETCH + 1;
-    int base = __builtin_amdgcn_readfirstlane(t0 + wave * RPP);
+    int base = __builtin_amdgcn_readfirstlane((seg == 0 ? t0 : seg1_lo) + wave * RPP);
     const int n_tiles = base < t_end ? (t_end - base + TS - 1) / TS : 0;
     if (n_tiles > 0) {
       u32x4 KB[NB][U], VB[NB][U];
@@ -1225,7 +1265,7 @@ DecodeKernel pick_decode_kernel(int dtype, int d, int gb) {
 
 kvc_status_t launch_copy(const kvc_cache_t* c, const int32_t* seq_lens, const void* ks, const void* vs,
                          int64_t sb, int64_t sh, int64_t st, int32_t t_new, uint32_t* status,
-                         hipStream_t stream, const kvc::PageInfo* pg = nullptr) {
+                         hipStream_t stream, const kvc::PageInfo* pg = nullptr, bool ring = false) {
   const int s = kvc::elem_bytes(c->dtype);
   CopyParams p;
   p.kc = static_cast<char*>(c->k);
@@ -1248,6 +1288,7 @@ kvc_status_t launch_copy(const kvc_cache_t* c, const int32_t* seq_lens, const vo
   p.table_stride = pg != nullptr ? pg->table_stride : 0;
   p.page_shift = pg != nullptr ? pg->page_shift : 0;
   p.n_pages = pg != nullptr ? pg->n_pages : 0;
+  p.ring = ring ? 1 : 0;
   const int64_t src_strides[3] = {p.sb, p.sh, p.st};
   const int vb = kvc::copy_vector_bytes(c, ks, vs, src_strides, 3);
   p.vecs_per_row = static_cast<int32_t>((static_cast<int64_t>(c->head_dim) * s) / vb);
@@ -1271,7 +1312,7 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
                            const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
                            int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
                            size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status, hipStream_t stream,
-                           int32_t t_q, const kvc::PageInfo* pg = nullptr) {
+                           int32_t t_q, const kvc::PageInfo* pg = nullptr, bool ring = false) {
   kvc_status_t st = kvc::check_cache(cache, true);
   if (st != KVC_OK) return st;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
@@ -1345,6 +1386,7 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.table_stride = pg != nullptr ? pg->table_stride : 0;
   p.page_shift = pg != nullptr ? pg->page_shift : 0;
   p.n_pages = pg != nullptr ? pg->n_pages : 0;
+  p.ring = ring ? 1 : 0;
   // paged caches are read by the matrix-core path only (16-row tiles)
   if (pg != nullptr && !(s == 2 && cache->head_dim % 32 == 0)) return KVC_ERR_UNSUPPORTED;
 
@@ -1498,4 +1540,60 @@ extern "C" kvc_status_t kvc_paged_decode_step(const kvc_paged_cache_t* cache, co
   if (view.batch > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_NULL;
   return launch_decode(&view, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
                        out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, 0, &info);
+}
+
+// ------------------------------------------------------------- ring cache --
+
+extern "C" kvc_status_t kvc_ring_append(const kvc_cache_t* cache, const int32_t* seq_lens, const void* k_new,
+                                        const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
+                                        uint32_t* dev_status, hipStream_t stream) {
+  kvc_status_t st = kvc::check_cache(cache, false);
+  if (st != KVC_OK) return st;
+  if (cache->batch == 0) return KVC_OK;
+  if (cache->max_len <= 0) return KVC_ERR_SHAPE;
+  if (seq_lens == nullptr || k_new == nullptr || v_new == nullptr) return KVC_ERR_NULL;
+  if (new_stride_b < 0 || new_stride_h < 0) return KVC_ERR_SHAPE;
+  if (cache->n_kv_heads > 1 && new_stride_h < cache->head_dim) return KVC_ERR_SHAPE;
+  const int s = kvc::elem_bytes(cache->dtype);
+  if (reinterpret_cast<uintptr_t>(k_new) % s || reinterpret_cast<uintptr_t>(v_new) % s) return KVC_ERR_ALIGN;
+  return launch_copy(cache, seq_lens, k_new, v_new, new_stride_b, new_stride_h, 0, 1, dev_status, stream, nullptr,
+                     true);
+}
+
+extern "C" kvc_status_t kvc_ring_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens, const void* k,
+                                              const void* v, int64_t src_stride_b, int64_t src_stride_h,
+                                              int64_t src_stride_t, int32_t t_new, uint32_t* dev_status,
+                                              hipStream_t stream) {
+  kvc_status_t st = kvc::check_cache(cache, false);
+  if (st != KVC_OK) return st;
+  if (t_new < 0) return KVC_ERR_SHAPE;
+  if (cache->batch == 0 || t_new == 0) return KVC_OK;
+  if (cache->max_len <= 0) return KVC_ERR_SHAPE;
+  if (seq_lens == nullptr || k == nullptr || v == nullptr) return KVC_ERR_NULL;
+  if (src_stride_b < 0 || src_stride_h < 0 || src_stride_t < 0) return KVC_ERR_SHAPE;
+  if (t_new > 1 && src_stride_t < cache->head_dim) return KVC_ERR_SHAPE;
+  const int s = kvc::elem_bytes(cache->dtype);
+  if (reinterpret_cast<uintptr_t>(k) % s || reinterpret_cast<uintptr_t>(v) % s) return KVC_ERR_ALIGN;
+  return launch_copy(cache, seq_lens, k, v, src_stride_b, src_stride_h, src_stride_t, t_new, dev_status, stream,
+                     nullptr, true);
+}
+
+extern "C" kvc_status_t kvc_ring_decode_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                                             const void* q, int32_t n_q_heads, float scale, void* out,
+                                             int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                             int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
+  if (cache != nullptr && cache->batch > 0 && cache->max_len <= 0) return KVC_ERR_SHAPE;
+  return launch_decode(cache, seq_lens, n_pending, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype,
+                       workspace, workspace_bytes, n_splits, dev_status, stream, 0, nullptr, true);
+}
+
+extern "C" kvc_status_t kvc_ring_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens, const void* k_new,
+                                             const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
+                                             const void* q, int32_t n_q_heads, float scale, void* out,
+                                             int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                             int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
+  if (cache != nullptr && cache->batch > 0 && cache->max_len <= 0) return KVC_ERR_SHAPE;
+  if (cache != nullptr && cache->batch > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_NULL;
+  return launch_decode(cache, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
+                       out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, 0, nullptr, true);
 }
