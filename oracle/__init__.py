@@ -22,11 +22,19 @@ invariants or 50-digit brute force); none is "parity unpinned".
 
 from .kvc_oracle import (  # noqa: F401
     append,
+    QFMT_FP8_E4M3,
+    QFMT_INT8,
+    QMAX,
     cache_bytes,
     causal_attention,
     chunk_attention,
     concat_append_positions,
+    code_value,
     decode_attention,
+    dequantize,
+    e4m3_decode_one,
+    e4m3_encode_one,
+    int8_encode_one,
     kv_head_of,
     paged_append,
     paged_decode_attention,
@@ -36,6 +44,10 @@ from .kvc_oracle import (  # noqa: F401
     prealloc_append_positions,
     prefill_fill,
     project,
+    quant_append,
+    quant_decode_attention,
+    quant_prefill_fill,
+    quantize_rows,
     ring_append,
     ring_decode_attention,
     ring_slot,

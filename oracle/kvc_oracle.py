@@ -430,3 +430,160 @@ def prealloc_append_positions(n_tokens: int) -> int:
     for _ in range(n_tokens):
         written += 1
     return written
+
+
+# ------------------------------------------------------------ quantized KV --
+#
+# [LA11] §3.1 (the second counterfactual) and §8 (the table of optimisations):
+# the usual compromise keeps weights in fp16, stores the cache as fp8 or int8
+# and accumulates the softmax in fp32; quantising the cache cuts the bytes each
+# decode step reads, at some loss of precision. [KVG] "MHA、GQA、MLA 与量化如何
+# 改变容量": the real saving also depends on the scale granularity (per token,
+# head or group), zero points and packing, and it shrinks if the kernel widens
+# the cache back to 16 bits in memory before using it. The pages fix no format;
+# this oracle takes the following one (the library implements the same):
+#   * one fp32 scale per (sequence, KV head, token) for K and another for V:
+#     scale = amax / QMAX, an fp32 division, where amax is the largest |x| over
+#     that token's D values of that head and QMAX is 127 (int8) or 448 (the
+#     largest finite fp8 e4m3 value);
+#   * code = encode(x / scale), the quotient an fp32 division; int8 rounds
+#     half to even and clamps to [-127, 127]; fp8 is the OCP 8-bit format
+#     E4M3 (bias 7, no infinities, S.1111.111 is NaN), rounded to nearest even
+#     and saturating at +-448;
+#   * a row of zeros has scale 0 and all codes 0;
+#   * the value a code stands for is code * scale, and attention runs on those
+#     values exactly as decode_attention does.
+# Symmetric codes, no zero point: projected keys and values are centred on
+# zero, and one scale per row then suffices. Codes are held as bytes (int8 as
+# two's complement), scales as float32.
+
+QFMT_FP8_E4M3 = 0
+QFMT_INT8 = 1
+QMAX = {QFMT_FP8_E4M3: 448.0, QFMT_INT8: 127.0}
+
+
+def _round_half_even(x: float) -> int:
+    """Nearest integer, ties to even (Python's round() on a float)."""
+    return int(round(x))
+
+
+def e4m3_encode_one(x: float) -> int:
+    """One value to its OCP E4M3 byte: round to nearest even, saturate at 448.
+
+    The representable magnitudes are m * 2^-9 for m = 0..7 (subnormals, biased
+    exponent 0) and (1 + m/8) * 2^(e-7) for biased exponents e = 1..15, except
+    e = 15 with m = 7, which is NaN. Anything at or above 448 in magnitude
+    (infinities included) becomes 448; NaN becomes 0x7F.
+    """
+    if math.isnan(x):
+        return 0x7F
+    sign = 0x80 if math.copysign(1.0, x) < 0 else 0x00
+    a = abs(x)
+    if a >= 448.0:
+        return sign | 0x7E
+    if a < 2.0 ** -6:                         # subnormal spacing 2^-9
+        m = _round_half_even(a * 2.0 ** 9)    # exact: a power-of-two scaling
+        return sign | (0x08 if m == 8 else m)  # 8 * 2^-9 is the smallest normal
+    frac, ex = math.frexp(a)                  # a = frac * 2^ex, frac in [0.5, 1)
+    e = ex - 1                                # a = (2 frac) * 2^e
+    m = _round_half_even(a * 2.0 ** (3 - e))  # in [8, 16]: 1.mmm scaled by 8
+    if m == 16:
+        e, m = e + 1, 8
+    code = ((e + 7) << 3) | (m - 8)
+    return sign | min(code, 0x7E)             # [448, 464) already saturated above
+
+
+def e4m3_decode_one(code: int) -> float:
+    """Value of an OCP E4M3 byte."""
+    code = int(code) & 0xFF
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 15 and m == 7:
+        return math.nan
+    if e == 0:
+        return s * m * 2.0 ** -9
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def int8_encode_one(y: float) -> int:
+    """Quotient to an int8 code: round half to even, clamp to [-127, 127]."""
+    return max(-127, min(127, _round_half_even(y)))
+
+
+def code_value(code: int, fmt: int) -> float:
+    """The number a code byte stands for before scaling."""
+    if fmt == QFMT_FP8_E4M3:
+        return e4m3_decode_one(code)
+    c = int(code) & 0xFF
+    return float(c - 256 if c >= 128 else c)
+
+
+def quantize_rows(x, fmt: int):
+    """Quantise rows x[..., D] (values exact in fp32) to (codes uint8 [..., D],
+    scales float32 [...]) with one scale per row, as defined above."""
+    x32 = np.asarray(widen(x), dtype=np.float32)
+    lead = x32.shape[:-1]
+    codes = np.zeros(x32.shape, dtype=np.uint8)
+    scales = np.zeros(lead, dtype=np.float32)
+    qmax = np.float32(QMAX[fmt])
+    for idx in np.ndindex(*lead):
+        row = x32[idx]
+        amax = np.max(np.abs(row)) if row.size else np.float32(0)
+        if amax == 0:
+            continue
+        scale = np.float32(amax) / qmax                      # fp32 division
+        scales[idx] = scale
+        for i, xi in enumerate(row):
+            y = float(np.float32(xi) / scale)                 # fp32 division
+            if fmt == QFMT_FP8_E4M3:
+                codes[idx + (i,)] = e4m3_encode_one(y)
+            else:
+                codes[idx + (i,)] = int8_encode_one(y) & 0xFF
+    return codes, scales
+
+
+def dequantize(codes, scales, fmt: int) -> np.ndarray:
+    """fp64 values code * scale; codes [..., D], scales [...]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lut = np.array([code_value(i, fmt) for i in range(256)], dtype=np.float64)
+    return lut[c] * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def quant_prefill_fill(k_codes, v_codes, k_scales, v_scales, seq_lens, k, v, fmt: int):
+    """Quantise T_new rows per sequence (k, v [B, H_kv, T_new, D]) into slots
+    [seq_lens[b], seq_lens[b] + T_new) of a quantised cache (codes
+    [B, H_kv, T_max, D] uint8, scales [B, H_kv, T_max] float32), with
+    prefill_fill's rules: a sequence whose range does not fit in [0, T_max) is
+    left untouched and flagged. Returns (k_codes, v_codes, k_scales, v_scales,
+    overflow)."""
+    kc, vc = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
+    ks, vs = np.array(k_scales, copy=True), np.array(v_scales, copy=True)
+    batch, _, t_max, _ = kc.shape
+    kq, ksq = quantize_rows(k, fmt)
+    vq, vsq = quantize_rows(v, fmt)
+    t_new = kq.shape[2]
+    overflow = np.zeros(batch, dtype=bool)
+    for b in range(batch):
+        pos = int(seq_lens[b])
+        if pos < 0 or pos + t_new > t_max:
+            overflow[b] = True
+            continue
+        kc[b, :, pos:pos + t_new] = kq[b]
+        vc[b, :, pos:pos + t_new] = vq[b]
+        ks[b, :, pos:pos + t_new] = ksq[b]
+        vs[b, :, pos:pos + t_new] = vsq[b]
+    return kc, vc, ks, vs, overflow
+
+
+def quant_append(k_codes, v_codes, k_scales, v_scales, seq_lens, k_new, v_new, fmt: int):
+    """One new token per sequence (k_new, v_new [B, H_kv, D]) quantised into
+    slot seq_lens[b]; the one-row case of quant_prefill_fill."""
+    return quant_prefill_fill(k_codes, v_codes, k_scales, v_scales, seq_lens,
+                              np.asarray(widen(k_new))[:, :, None, :], np.asarray(widen(v_new))[:, :, None, :], fmt)
+
+
+def quant_decode_attention(q, k_codes, k_scales, v_codes, v_scales, seq_lens, fmt: int, n_pending: int = 1,
+                           scale=None):
+    """decode_attention over the values the quantised cache stands for."""
+    return decode_attention(q, dequantize(k_codes, k_scales, fmt), dequantize(v_codes, v_scales, fmt), seq_lens,
+                            n_pending=n_pending, scale=scale)

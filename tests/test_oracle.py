@@ -589,3 +589,172 @@ def test_ring_append_ignores_negative_counts():
     kr = np.zeros((2, 1, 4, 2))
     k2, _ = oracle.ring_append(kr, kr, np.array([-1, 6]), np.ones((2, 1, 2)), np.ones((2, 1, 2)))
     assert np.array_equal(k2[0], kr[0]) and k2[1, 0, 2].tolist() == [1.0, 1.0]
+
+
+# ------------------------------------------------------------ quantized KV --
+# The pages name fp8/int8 caches with per-token/per-head scales ([LA11] §3.1,
+# §8; [KVG] "MHA、GQA、MLA 与量化如何改变容量") but fix no format; the format
+# pinned here is the oracle's stated reading (OCP E4M3 or symmetric int8, one
+# fp32 scale per token and KV head).
+
+def _e4m3_values():
+    """Every finite E4M3 magnitude, ascending (from torch's own decoding)."""
+    v = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    return np.unique(v.astype(np.float64))
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([oracle.e4m3_decode_one(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.isnan(got).sum() == 2                        # S.1111.111 only
+
+
+def test_e4m3_encode_matches_torch_below_the_saturation_point():
+    """torch's fp32 -> float8_e4m3fn conversion (round to nearest even) on
+    every finite value, every midpoint between neighbours, points just either
+    side of each midpoint, and log-uniform random values of both signs."""
+    vals = _e4m3_values()
+    mids = (vals[:-1] + vals[1:]) / 2
+    eps = np.nextafter(mids.astype(np.float32), np.float32(np.inf)).astype(np.float64)
+    below = np.nextafter(mids.astype(np.float32), np.float32(0)).astype(np.float64)
+    rng = np.random.default_rng(3)
+    rand = np.exp2(rng.uniform(-14, np.log2(447.9), 4000))
+    x = np.concatenate([vals, mids, eps, below, rand]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode_one(float(v)) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_closed_forms_and_saturation():
+    """Values fixed by the OCP E4M3 definition, and the oracle's reading for
+    magnitudes at or above 448 (saturate; torch would give NaN there)."""
+    enc = oracle.e4m3_encode_one
+    assert enc(1.0) == 0x38 and enc(-2.0) == 0xC0 and enc(448.0) == 0x7E
+    assert enc(2.0 ** -6) == 0x08 and enc(2.0 ** -9) == 0x01 and enc(0.875 * 2.0 ** -6) == 0x07
+    assert enc(2.0 ** -10) == 0x00 and enc(3 * 2.0 ** -10) == 0x02       # ties to even in the subnormals
+    assert enc(1.0625) == 0x38 and enc(1.1875) == 0x3A                   # ties to even, 1 + m/8
+    assert enc(7.75 * 2.0 ** -9) == 0x08                                 # rounds up to the first normal
+    assert enc(464.0) == 0x7E and enc(1e30) == 0x7E and enc(math.inf) == 0x7E and enc(-math.inf) == 0xFE
+    assert enc(math.nan) == 0x7F and enc(-0.0) == 0x80 and enc(0.0) == 0x00
+
+
+def test_int8_code_rounds_half_to_even_and_clamps():
+    enc = oracle.int8_encode_one
+    assert [enc(x) for x in (2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 126.5, 127.49)] == [2, 4, -2, -4, 0, 2, 126, 127]
+    assert enc(127.6) == 127 and enc(300.0) == 127 and enc(-128.0) == -127
+    assert oracle.code_value(0xFF, oracle.QFMT_INT8) == -1.0 and oracle.code_value(0x81, oracle.QFMT_INT8) == -127.0
+
+
+@pytest.mark.parametrize("fmt", [oracle.QFMT_FP8_E4M3, oracle.QFMT_INT8])
+def test_quantize_rows_scale_and_extreme_code(fmt):
+    """scale = fp32(amax) / QMAX as an fp32 division, computed here with torch;
+    the element of largest magnitude gets the top code; a zero row gets scale
+    0 and zero codes."""
+    x = synth.normal((3, 4, 32), "bf16", 5, "qscale").float()
+    x[1, 2] = 0.0
+    codes, scales = oracle.quantize_rows(x, fmt)
+    qmax = 448.0 if fmt == oracle.QFMT_FP8_E4M3 else 127.0
+    want = x.abs().amax(-1) / torch.tensor(qmax, dtype=torch.float32)
+    want[1, 2] = 0.0
+    assert np.array_equal(scales, want.numpy())
+    assert not codes[1, 2].any() and scales[1, 2] == 0
+    top = 0x7E if fmt == oracle.QFMT_FP8_E4M3 else 127
+    i = x.abs().argmax(-1)
+    for b in range(3):
+        for h in range(4):
+            if b == 1 and h == 2:
+                continue
+            c = int(codes[b, h, i[b, h]])
+            assert c & 0x7F == top if fmt == oracle.QFMT_FP8_E4M3 else (c if c < 128 else 256 - c) == top
+
+
+@pytest.mark.parametrize("fmt", [oracle.QFMT_FP8_E4M3, oracle.QFMT_INT8])
+def test_quantize_rows_error_bounds(fmt):
+    """int8: |x - value| <= scale/2 (plus the fp32 quotient's rounding);
+    fp8: half a unit in the last place of a 3-bit mantissa for normals,
+    2^-10 * scale in the subnormal range."""
+    x = synth.normal((4, 8, 128), "fp32", 6, "qerr").double().numpy()
+    x[0, 0] *= 1e-3
+    codes, scales = oracle.quantize_rows(x.astype(np.float32), fmt)
+    err = np.abs(oracle.dequantize(codes, scales, fmt) - x)
+    s = scales.astype(np.float64)[..., None]
+    if fmt == oracle.QFMT_INT8:
+        assert (err <= s * (0.5 + 2e-5)).all()
+    else:
+        y = np.abs(x) / s
+        bound = np.where(y >= 2.0 ** -6, np.abs(x) * (2.0 ** -4) * (1 + 1e-6), s * 2.0 ** -10 * (1 + 1e-6))
+        assert (err <= bound + 1e-30).all()
+    assert err.max() > 0
+
+
+@pytest.mark.parametrize("fmt", [oracle.QFMT_FP8_E4M3, oracle.QFMT_INT8])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
+def test_quant_decode_matches_sdpa_on_independently_dequantised_cache(fmt, hq, hkv):
+    """The cache's values rebuilt without the oracle's codec (torch's
+    float8_e4m3fn decoding, or int8 as signed bytes, times the scales), then
+    torch SDPA with GQA: K and V scales, token and head indexing all enter."""
+    b, t, d = 3, 40, 32
+    k = synth.normal((b, hkv, t, d), "bf16", 7, "qsd", "k").float()
+    v = synth.normal((b, hkv, t, d), "bf16", 7, "qsd", "v").float()
+    q = synth.normal((b, hq, d), "bf16", 7, "qsd", "q")
+    kc, ks = oracle.quantize_rows(k, fmt)
+    vc, vs = oracle.quantize_rows(v, fmt)
+    lens = np.array([0, 17, 39])
+
+    def deq(c, s):
+        ct = torch.from_numpy(c)
+        base = ct.view(torch.float8_e4m3fn).double() if fmt == oracle.QFMT_FP8_E4M3 else ct.view(torch.int8).double()
+        return base * torch.from_numpy(s).double()[..., None]
+
+    kd, vd = deq(kc, ks), deq(vc, vs)
+    got = oracle.quant_decode_attention(q, kc, ks, vc, vs, lens, fmt, n_pending=1)
+    for bb in range(b):
+        n = int(lens[bb]) + 1
+        ref = F.scaled_dot_product_attention(q[bb:bb + 1, :, None].double(), kd[bb:bb + 1, :, :n],
+                                             vd[bb:bb + 1, :, :n], enable_gqa=True)[:, :, 0]
+        assert np.abs(got[bb] - ref[0].numpy()).max() < 1e-12
+
+
+def test_quant_scale_folding_invariants():
+    """Scaling every K scale by c is the softmax scale times c; scaling every V
+    scale by c scales the output by c (c a power of two, so exact)."""
+    fmt = oracle.QFMT_INT8
+    k = synth.normal((2, 2, 24, 16), "fp32", 8, "qfold", "k")
+    v = synth.normal((2, 2, 24, 16), "fp32", 8, "qfold", "v")
+    q = synth.normal((2, 4, 16), "fp32", 8, "qfold", "q")
+    kc, ks = oracle.quantize_rows(k, fmt)
+    vc, vs = oracle.quantize_rows(v, fmt)
+    lens = np.array([10, 23])
+    base = oracle.quant_decode_attention(q, kc, ks, vc, vs, lens, fmt, n_pending=1)
+    k4 = oracle.quant_decode_attention(q, kc, ks * 4, vc, vs, lens, fmt, n_pending=1, scale=0.25 / 4)
+    ref4 = oracle.quant_decode_attention(q, kc, ks, vc, vs, lens, fmt, n_pending=1, scale=0.25)
+    assert np.allclose(k4, ref4, rtol=0, atol=1e-14)
+    v8 = oracle.quant_decode_attention(q, kc, ks, vc, vs * 8, lens, fmt, n_pending=1)
+    assert np.array_equal(v8, base * 8)
+
+
+def test_quant_append_and_fill_slots():
+    """The rows land at the slots append/prefill_fill would use, quantised as
+    quantize_rows does; other slots and sequences that do not fit stay as
+    they were (and are flagged)."""
+    fmt = oracle.QFMT_FP8_E4M3
+    b, h, t_max, d = 3, 2, 8, 16
+    kc = np.full((b, h, t_max, d), 0x7F, dtype=np.uint8)
+    vc = kc.copy()
+    ks = np.full((b, h, t_max), np.nan, dtype=np.float32)
+    vs = ks.copy()
+    kn = synth.normal((b, h, 3, d), "bf16", 9, "qapp", "k")
+    vn = synth.normal((b, h, 3, d), "bf16", 9, "qapp", "v")
+    kc2, vc2, ks2, vs2, over = oracle.quant_prefill_fill(kc, vc, ks, vs, [0, 6, 7], kn, vn, fmt)
+    assert over.tolist() == [False, True, True]
+    want_c, want_s = oracle.quantize_rows(kn, fmt)
+    assert np.array_equal(kc2[0, :, :3], want_c[0]) and np.array_equal(ks2[0, :, :3], want_s[0])
+    assert (kc2[0, :, 3:] == 0x7F).all() and (kc2[1:] == 0x7F).all() and np.isnan(vs2[1:]).all()
+    kc3, _, ks3, _, over = oracle.quant_append(kc2, vc2, ks2, vs2, [3, -1, 8], kn[:, :, 0], vn[:, :, 0], fmt)
+    assert over.tolist() == [False, True, True]
+    assert np.array_equal(kc3[0, :, 3], want_c[0, :, 0]) and np.array_equal(kc3[0, :, :3], kc2[0, :, :3])

@@ -186,3 +186,48 @@ def test_ring_mutants_are_caught(kind, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"no pin caught mutant {kind}"
+
+
+@pytest.mark.parametrize("kind", ["e4m3_truncate", "int8_half_away", "int8_qmax_128", "v_scale_dropped",
+                                  "k_scale_next_token"])
+def test_quant_mutants_are_caught(kind, monkeypatch):
+    """Plausible mistakes in the quantised-cache oracle, each caught by a pin."""
+    if kind == "e4m3_truncate":
+        real = ko.e4m3_encode_one
+
+        def enc(x):
+            c = real(x)
+            if math.isnan(x) or c & 0x7F == 0x7E:
+                return c
+            # toward zero: step back one code when rounding went up in magnitude
+            return c - 1 if c & 0x7F and abs(ko.e4m3_decode_one(c)) > abs(x) else c
+        monkeypatch.setattr(ko, "e4m3_encode_one", enc)
+        monkeypatch.setattr(oracle, "e4m3_encode_one", enc)
+        pins_to_run = [pins.test_e4m3_encode_matches_torch_below_the_saturation_point,
+                       pins.test_e4m3_closed_forms_and_saturation]
+    elif kind == "int8_half_away":
+        def enc(y):
+            return max(-127, min(127, int(math.copysign(math.floor(abs(y) + 0.5), y))))
+        monkeypatch.setattr(ko, "int8_encode_one", enc)
+        monkeypatch.setattr(oracle, "int8_encode_one", enc)
+        pins_to_run = [pins.test_int8_code_rounds_half_to_even_and_clamps]
+    elif kind == "int8_qmax_128":
+        monkeypatch.setitem(ko.QMAX, ko.QFMT_INT8, 128.0)
+        pins_to_run = [lambda: pins.test_quantize_rows_scale_and_extreme_code(ko.QFMT_INT8)]
+    else:
+        def dec(q, kc, ks, vc, vs, seq_lens, fmt, n_pending=1, scale=None):
+            kd = ko.dequantize(kc, ks, fmt)
+            if kind == "k_scale_next_token":
+                kd = ko.dequantize(kc, np.roll(ks, -1, axis=-1), fmt)
+            vd = ko.dequantize(vc, np.ones_like(vs) if kind == "v_scale_dropped" else vs, fmt)
+            return ko.decode_attention(q, kd, vd, seq_lens, n_pending=n_pending, scale=scale)
+        monkeypatch.setattr(oracle, "quant_decode_attention", dec)
+        pins_to_run = [lambda: pins.test_quant_decode_matches_sdpa_on_independently_dequantised_cache(
+            ko.QFMT_INT8, 8, 2)]
+    caught = 0
+    for pin in pins_to_run:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught mutant {kind}"
