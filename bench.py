@@ -46,6 +46,9 @@ def _parse():
     ap.add_argument("--ring", type=int, default=0,
                     help="window W: time the decode step on ring caches of W slots (kvc_ring_decode_step, "
                          "sliding-window attention over the most recent W tokens) instead of full caches")
+    ap.add_argument("--quant", choices=["fp8", "int8"], default=None,
+                    help="time the decode step on a quantised cache (8-bit codes + per-token fp32 scales; "
+                         "kvc_quant_decode_step) instead of the 16-bit cache")
     ap.add_argument("--block-q", type=int, default=0,
                     help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
                          "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
@@ -68,7 +71,7 @@ class Workload:
     C-ABI arguments (so the timed loop does no Python-side tensor work)."""
 
     def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0, page: int = 0,
-                 ring: int = 0):
+                 ring: int = 0, quant=None):
         import torch
         import kv_cache_append_amd as kvc
         import synth
@@ -77,6 +80,7 @@ class Workload:
         self.block_q = block_q        # 0: decode step; N: block of N new tokens per sequence
         self.page = page              # 0: contiguous caches; P: page pools of P-token pages
         self.ring = ring              # 0: full caches; W: ring caches of the most recent W tokens
+        self.quant = quant            # None: 16-bit cache; "fp8" / "int8": 8-bit codes + per-token scales
         self.kvc = kvc
         self.lib = kvc.load()
         dev = torch.device("cuda:0")
@@ -84,6 +88,9 @@ class Workload:
         self.t_max = ring if ring else int(self.lengths.max()) + margin_tokens + 1
         L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
         tdt = synth.DTYPES[cfg.dtype]
+        if quant:
+            self._init_quant(cfg, seed, splits, dev, tdt)
+            return
         if page:
             # page pools per layer and one page table (a random permutation of
             # the pool's pages) shared by the layers, as a serving runtime keeps it
@@ -128,11 +135,51 @@ class Workload:
         self.scale = ctypes.c_float(1.0 / math.sqrt(D))
         torch.cuda.synchronize()
 
+    def _init_quant(self, cfg, seed, splits, dev, tdt):
+        """Codes [L, B, H_kv, T_max, D] and scales [L, B, H_kv, T_max], each
+        layer quantised on the device from seeded N(0,1) rows of the
+        workload's dtype by kvc_quant_prefill_fill."""
+        import torch
+        import synth
+        kvc = self.kvc
+        L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+        T = self.t_max
+        self.kc = torch.empty((L, B, Hkv, T, D), dtype=torch.uint8, device=dev)
+        self.vc = torch.empty_like(self.kc)
+        self.ks = torch.empty((L, B, Hkv, T), dtype=torch.float32, device=dev)
+        self.vs = torch.empty_like(self.ks)
+        fmt = kvc.QFMT[self.quant]
+        self.descs = [kvc.qcache_desc(self.kc[l], self.vc[l], self.ks[l], self.vs[l], fmt, tdt) for l in range(L)]
+        zero = torch.zeros(B, dtype=torch.int32, device=dev)
+        krows = torch.empty((B, Hkv, T, D), dtype=tdt, device=dev)
+        vrows = torch.empty_like(krows)
+        for l in range(L):   # every slot of the layer, quantised from fresh rows
+            synth.normal(None, cfg.dtype, seed, cfg.name, l, "K", out=krows)
+            synth.normal(None, cfg.dtype, seed, cfg.name, l, "V", out=vrows)
+            kvc.quant_prefill_fill(self.descs[l], zero, krows, vrows)
+        del krows, vrows
+        self.q = torch.stack([synth.normal((B, Hq, D), cfg.dtype, seed, cfg.name, l, "q", device=dev)
+                              for l in range(L)])
+        self.k_new = torch.stack([synth.normal((B, Hkv, D), cfg.dtype, seed, cfg.name, l, "k_new", device=dev)
+                                  for l in range(L)])
+        self.v_new = torch.stack([synth.normal((B, Hkv, D), cfg.dtype, seed, cfg.name, l, "v_new", device=dev)
+                                  for l in range(L)])
+        self.out = torch.empty((L, B, Hq, D), dtype=torch.float32, device=dev)
+        self.seq_lens = self.lengths.to(dev)
+        logical = kvc.CacheDesc(self.kc.data_ptr(), self.vc.data_ptr(), B, Hkv, T, D, kvc.DTYPE_CODE[tdt], 0,
+                                Hkv * T * D, T * D, D)
+        self.splits = splits if splits > 0 else int(self.lib.kvc_decode_splits(ctypes.byref(logical), Hq))
+        self.ws = kvc.quant_workspace(self.descs[0], Hq, self.splits)
+        self.scale = ctypes.c_float(1.0 / math.sqrt(D))
+        torch.cuda.synchronize()
+
     def reset_lengths(self):
         self.seq_lens.copy_(self.lengths.to(self.seq_lens.device))
 
-    def layers(self, stream_handle):
-        """Enqueue the per-layer decode launches of one step (lengths unchanged)."""
+    def layers(self, stream_handle, attn_only: bool = False):
+        """Enqueue the per-layer decode launches of one step (lengths unchanged).
+        attn_only (quantised cache): only the decode launch of each layer, which
+        reads the same bytes as in the step (the slot it appends is attended)."""
         lib, cfg = self.lib, self.cfg
         vp = ctypes.c_void_p
         seq = vp(self.seq_lens.data_ptr())
@@ -151,8 +198,17 @@ class Workload:
                 if rc:
                     raise RuntimeError(f"libkvc returned {rc} at layer {l}")
             return
+        if self.quant and attn_only:
+            for l in range(cfg.n_layers):
+                rc = lib.kvc_quant_decode_attn(ctypes.byref(self.descs[l]), seq, 1, vp(self.q[l].data_ptr()),
+                                               cfg.n_q_heads, self.scale, vp(self.out[l].data_ptr()), 0, ws, wsb,
+                                               self.splits, None, st)
+                if rc:
+                    raise RuntimeError(f"libkvc returned {rc} at layer {l}")
+            return
         step_fn = (lib.kvc_paged_decode_step if self.page else
-                   lib.kvc_ring_decode_step if self.ring else lib.kvc_decode_step)
+                   lib.kvc_ring_decode_step if self.ring else
+                   lib.kvc_quant_decode_step if self.quant else lib.kvc_decode_step)
         for l in range(cfg.n_layers):
             d = ctypes.byref(self.descs[l])
             rc = step_fn(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
@@ -177,15 +233,19 @@ class Workload:
             lens = lens.clamp(max=self.ring)
         return int(lens.sum())
 
+    def token_bytes(self) -> int:
+        """K+V bytes of one token of one layer: 2 * H_kv * D * s, or for a
+        quantised cache 2 * H_kv * (D code bytes + a 4-byte scale)."""
+        row = self.cfg.head_dim + 4 if self.quant else self.cfg.head_dim * self.cfg.elem_bytes
+        return 2 * self.cfg.n_kv_heads * row
+
     def kv_bytes(self, steps: int) -> int:
         """KV bytes read by `steps` steps starting from the reset lengths."""
-        per_token = 2 * self.cfg.n_layers * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
-        return per_token * sum(self.attended_tokens(k) for k in range(steps))
+        return self.cfg.n_layers * self.token_bytes() * sum(self.attended_tokens(k) for k in range(steps))
 
     def decode_launch_bytes(self, step_index: int) -> int:
         """Algorithmic K+V bytes one decode launch (one layer) reads at a step."""
-        per_token = 2 * self.cfg.n_kv_heads * self.cfg.head_dim * self.cfg.elem_bytes
-        return per_token * self.attended_tokens(step_index)
+        return self.token_bytes() * self.attended_tokens(step_index)
 
 
 def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
@@ -231,18 +291,18 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     if use_graph:
         layers_graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(layers_graph):
-            w.layers(torch.cuda.current_stream().cuda_stream)
+            w.layers(torch.cuda.current_stream().cuda_stream, attn_only=bool(w.quant))
         torch.cuda.synchronize()
         layers_graph.replay()
     else:
-        w.layers(stream.cuda_stream)
+        w.layers(stream.cuda_stream, attn_only=bool(w.quant))
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
         if layers_graph is not None:
             layers_graph.replay()
         else:
-            w.layers(stream.cuda_stream)
+            w.layers(stream.cuda_stream, attn_only=bool(w.quant))
     e1.record()
     torch.cuda.synchronize()
     avg_launch_ms = e0.elapsed_time(e1) / (reps * w.cfg.n_layers)
@@ -368,9 +428,9 @@ def _run_config(name, args, with_cpu):
     cfg = synth.CONFIGS[name]
     nq = max(args.block_q, 1)
     margin = (max(args.steps, args.warmup) + 2) * nq
-    if args.ring and (args.block_q or args.paged):
-        raise SystemExit("--ring takes neither --block-q nor --paged")
-    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring)
+    if sum(bool(x) for x in (args.ring, args.block_q, args.paged, args.quant)) > 1:
+        raise SystemExit("--ring, --block-q, --paged and --quant are separate modes")
+    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring, args.quant)
     ms_total, wall, launch_ms, launch_bytes = _measure(w, args.steps, args.warmup, not args.no_graph)
     kv = w.kv_bytes(args.steps)
     gbs = kv / (ms_total / 1e3) / 1e9
@@ -394,6 +454,7 @@ def _run_config(name, args, with_cpu):
             **({"query_block": args.block_q} if args.block_q else {}),
             **({"page_size": args.paged} if args.paged else {}),
             **({"window": args.ring} if args.ring else {}),
+            **({"kv_format": args.quant, "kv_bytes_per_token_head": cfg.head_dim + 4} if args.quant else {}),
         },
         "roofline": {
             "bound": "hbm",
@@ -401,11 +462,14 @@ def _run_config(name, args, with_cpu):
                        "layer covers both)" if args.block_q else
                        "decode_kernel (kvc_ring_decode_step: ring append + windowed attention + merge, one "
                        "launch per layer)" if args.ring else
+                       "decode_kernel on 8-bit codes (kvc_quant_decode_attn, timed alone; the step adds one "
+                       "quantising append launch per layer)" if args.quant else
                        "decode_kernel (kvc_decode_step: append + attention + merge, one launch per layer)"),
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),
-            "traffic": _traffic(name),
+            # counters are taken for the default mode (16-bit contiguous cache)
+            "traffic": None if (args.block_q or args.paged or args.ring or args.quant) else _traffic(name),
         },
     }
     if with_cpu:

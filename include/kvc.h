@@ -361,6 +361,88 @@ kvc_status_t kvc_paged_decode_step(const kvc_paged_cache_t* cache, const int32_t
                                    uint32_t* dev_status, hipStream_t stream);
 
 /*
+ * Quantised cache (NEXT to the 16-bit one): K and V stored as 8-bit codes
+ * with one fp32 scale per (sequence, KV head, token) for K and another for V
+ * (textbook "11.7 KV Cache" §3.1: weights in fp16, cache in fp8/int8, softmax
+ * accumulated in fp32; §8: quantising the cache cuts the bytes read; glossary
+ * "KV 缓存", how quantisation changes capacity: the scale granularity,
+ * packing and the kernel's handling decide the real saving, which is lost if
+ * the cache is widened back to 16 bits in memory first). The pages fix no
+ * format; this library's is:
+ *   scale = amax / QMAX, an fp32 division, amax = max |x| over the row's
+ *           head_dim values, QMAX = 448 (KVC_QFMT_FP8_E4M3) or 127
+ *           (KVC_QFMT_INT8); a row of zeros gets scale 0 and zero codes;
+ *   code  = encode(x / scale), the quotient an fp32 division: OCP 8-bit E4M3
+ *           (bias 7, no infinities, 0x7F/0xFF NaN) rounded to nearest even
+ *           and saturating at +-448, or int8 (two's complement) rounded half
+ *           to even and clamped to [-127, 127];
+ *   a code stands for code * scale, and decode attends those values.
+ * Rows holding NaN or infinity give unspecified codes and scales. Decode
+ * widens the codes in registers, never in memory: per token and head it reads
+ * head_dim + 4 bytes of K and as many of V.
+ */
+#define KVC_QFMT_FP8_E4M3 0
+#define KVC_QFMT_INT8 1
+
+typedef struct kvc_qcache {
+  void* k;                  /* K codes [batch, n_kv_heads, max_len, head_dim], one byte each */
+  void* v;                  /* V codes, same geometry and strides */
+  float* k_scale;           /* K scales [batch, n_kv_heads, max_len], fp32, token axis contiguous */
+  float* v_scale;           /* V scales, same geometry and strides */
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t max_len;
+  int32_t head_dim;         /* 64, 128 or 256 */
+  int32_t format;           /* KVC_QFMT_* */
+  int32_t in_dtype;         /* kvc_dtype_t of the rows appended and of the queries: KVC_F16 or KVC_BF16
+                               (KVC_F32 is accepted by the append and fill calls only) */
+  int64_t stride_b;         /* code strides in bytes (= elements); head_dim contiguous; */
+  int64_t stride_h;         /*   all three multiples of 16 and the code pointers 16-byte aligned */
+  int64_t stride_t;
+  int64_t scale_stride_b;   /* scale strides in floats (the token stride is 1) */
+  int64_t scale_stride_h;
+} kvc_qcache_t;
+
+/*
+ * kvc_quant_append / kvc_quant_prefill_fill -- as kvc_append and
+ * kvc_prefill_fill (same slots, same capacity and negative-length rules), but
+ * each new row (in_dtype, [B, H_kv, D] or [B, H_kv, T_new, D], element
+ * strides) is quantised on the device into its codes and scale.
+ */
+kvc_status_t kvc_quant_append(const kvc_qcache_t* cache, const int32_t* seq_lens,
+                              const void* k_new, const void* v_new,
+                              int64_t new_stride_b, int64_t new_stride_h,
+                              uint32_t* dev_status, hipStream_t stream);
+kvc_status_t kvc_quant_prefill_fill(const kvc_qcache_t* cache, const int32_t* seq_lens,
+                                    const void* k, const void* v,
+                                    int64_t src_stride_b, int64_t src_stride_h, int64_t src_stride_t,
+                                    int32_t t_new, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * kvc_quant_decode_workspace_bytes / kvc_quant_decode_attn -- as
+ * kvc_decode_workspace_bytes and kvc_decode_attn over the values the codes
+ * stand for. q is [B, H_q, D] in in_dtype (KVC_F16 or KVC_BF16, else
+ * KVC_ERR_UNSUPPORTED); out is fp32 or in_dtype. The workspace rules are the
+ * contiguous decode's.
+ *
+ * kvc_quant_decode_step -- kvc_quant_append then kvc_quant_decode_attn with
+ * n_pending = 1, enqueued as those two launches.
+ */
+size_t kvc_quant_decode_workspace_bytes(const kvc_qcache_t* cache, int32_t n_q_heads, int32_t n_splits);
+kvc_status_t kvc_quant_decode_attn(const kvc_qcache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                                   const void* q, int32_t n_q_heads, float scale,
+                                   void* out, int32_t out_dtype,
+                                   void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                   uint32_t* dev_status, hipStream_t stream);
+kvc_status_t kvc_quant_decode_step(const kvc_qcache_t* cache, const int32_t* seq_lens,
+                                   const void* k_new, const void* v_new,
+                                   int64_t new_stride_b, int64_t new_stride_h,
+                                   const void* q, int32_t n_q_heads, float scale,
+                                   void* out, int32_t out_dtype,
+                                   void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                   uint32_t* dev_status, hipStream_t stream);
+
+/*
  * kvc_seq_lens_advance -- seq_lens[b] += n for every b, on the device, once per
  * step after all layers appended (course notes §3.1: pos += T).
  */

@@ -24,6 +24,8 @@ DEVERR_CAPACITY = 1
 DEVERR_BADLEN = 2
 DEVERR_SYNC = 4
 DEVERR_PAGE = 8
+QFMT_FP8_E4M3, QFMT_INT8 = 0, 1
+QFMT = {"fp8": QFMT_FP8_E4M3, "int8": QFMT_INT8}
 
 STATUS = {
     0: "KVC_OK", 1: "KVC_ERR_NULL", 2: "KVC_ERR_SHAPE", 3: "KVC_ERR_DTYPE", 4: "KVC_ERR_ALIGN",
@@ -36,6 +38,8 @@ EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_
            "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
            "kvc_paged_decode_attn", "kvc_paged_decode_step",
            "kvc_ring_append", "kvc_ring_prefill_fill", "kvc_ring_decode_attn", "kvc_ring_decode_step",
+           "kvc_quant_append", "kvc_quant_prefill_fill", "kvc_quant_decode_workspace_bytes",
+           "kvc_quant_decode_attn", "kvc_quant_decode_step",
            "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
 
 
@@ -104,6 +108,17 @@ def load() -> ctypes.CDLL:
     lib.kvc_ring_decode_attn.restype = i32
     lib.kvc_ring_decode_step.argtypes = [cp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_ring_decode_step.restype = i32
+    qp = ctypes.POINTER(QCacheDesc)
+    lib.kvc_quant_append.argtypes = [qp, vp, vp, vp, i64, i64, vp, vp]
+    lib.kvc_quant_append.restype = i32
+    lib.kvc_quant_prefill_fill.argtypes = [qp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+    lib.kvc_quant_prefill_fill.restype = i32
+    lib.kvc_quant_decode_workspace_bytes.argtypes = [qp, i32, i32]
+    lib.kvc_quant_decode_workspace_bytes.restype = sz
+    lib.kvc_quant_decode_attn.argtypes = [qp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_quant_decode_attn.restype = i32
+    lib.kvc_quant_decode_step.argtypes = [qp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_quant_decode_step.restype = i32
     lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
     lib.kvc_seq_lens_advance.restype = i32
     lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
@@ -154,6 +169,38 @@ def paged_desc(k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.
     b, per_seq = block_table.shape
     return PagedCacheDesc(k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), b, h, psz, d,
                           DTYPE_CODE[k_pages.dtype], n_pages, per_seq, block_table.stride(0), sp, sh, st)
+
+
+class QCacheDesc(ctypes.Structure):
+    """Mirror of kvc_qcache_t."""
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("max_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("format", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64),
+        ("scale_stride_b", ctypes.c_int64), ("scale_stride_h", ctypes.c_int64),
+    ]
+
+
+def qcache_desc(k_codes: torch.Tensor, v_codes: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                fmt: int, in_dtype: torch.dtype) -> QCacheDesc:
+    """kvc_qcache_t for uint8 code tensors [B, H_kv, T_max, D] and float32 scale
+    tensors [B, H_kv, T_max] (token axis contiguous); fmt is QFMT_FP8_E4M3 or
+    QFMT_INT8, in_dtype the dtype of the appended rows and of the queries."""
+    if k_codes.shape != v_codes.shape or k_codes.stride() != v_codes.stride() or k_codes.dim() != 4:
+        raise ValueError("K and V codes must be 4-D with equal shape and strides")
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("codes must be uint8")
+    if k_codes.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    b, h, t, d = k_codes.shape
+    if k_scale.shape != (b, h, t) or v_scale.shape != (b, h, t) or k_scale.stride() != v_scale.stride():
+        raise ValueError("scales must be [B, H_kv, T_max] with equal strides")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32 or (t > 1 and k_scale.stride(2) != 1):
+        raise ValueError("scales must be float32 with a contiguous token axis")
+    sb, sh, st, _ = k_codes.stride()
+    return QCacheDesc(k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), b, h, t, d,
+                      int(fmt), DTYPE_CODE[in_dtype], sb, sh, st, k_scale.stride(0), k_scale.stride(1))
 
 
 def cache_desc(k: torch.Tensor, v: torch.Tensor) -> CacheDesc:
@@ -386,3 +433,59 @@ def cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, dtype: torch.dtyp
 
 def status_str(code: int) -> str:
     return load().kvc_status_str(code).decode()
+
+
+# ------------------------------------------------------------ quantised cache --
+
+def quant_append(qc: QCacheDesc, seq_lens, k_new, v_new, status=None, stream=None):
+    """kvc_quant_append: quantise k_new/v_new [B, H_kv, D] into slot seq_lens[b]."""
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(load().kvc_quant_append(ctypes.byref(qc), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+                                   k_new.stride(1), _ptr(status), _stream(stream)), "kvc_quant_append")
+
+
+def quant_prefill_fill(qc: QCacheDesc, seq_lens, k, v, status=None, stream=None):
+    """kvc_quant_prefill_fill: quantise k/v [B, H_kv, T_new, D] into slots [seq_lens[b], +T_new)."""
+    if k.stride() != v.stride() or k.dim() != 4:
+        raise ValueError("k and v must be [B, H_kv, T_new, D] with equal strides")
+    _check(load().kvc_quant_prefill_fill(ctypes.byref(qc), _ptr(seq_lens), _ptr(k), _ptr(v), k.stride(0),
+                                         k.stride(1), k.stride(2), k.shape[2], _ptr(status), _stream(stream)),
+           "kvc_quant_prefill_fill")
+
+
+def quant_workspace(qc: QCacheDesc, n_q_heads: int, n_splits: int = 0, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace for the quantised decode calls."""
+    n = int(load().kvc_quant_decode_workspace_bytes(ctypes.byref(qc), n_q_heads, n_splits))
+    if n == 0:
+        raise ValueError("invalid quantised cache/head arguments for a decode workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def quant_decode_attn(qc: QCacheDesc, seq_lens, q, out, workspace, n_pending: int = 1, scale=None, n_splits: int = 0,
+                      status=None, stream=None):
+    """kvc_quant_decode_attn over the values the codes stand for."""
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    _check(load().kvc_quant_decode_attn(ctypes.byref(qc), _ptr(seq_lens), n_pending, _ptr(q), q.shape[1],
+                                        float(scale), _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                                        _stream(stream)), "kvc_quant_decode_attn")
+
+
+def quant_decode_step(qc: QCacheDesc, seq_lens, k_new, v_new, q, out, workspace, scale=None, n_splits: int = 0,
+                      status=None, stream=None):
+    """kvc_quant_decode_step: quantised append of the step's rows, then decode (n_pending = 1)."""
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(load().kvc_quant_decode_step(ctypes.byref(qc), _ptr(seq_lens), _ptr(k_new), _ptr(v_new),
+                                        k_new.stride(0), k_new.stride(1), _ptr(q), q.shape[1], float(scale),
+                                        _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                                        _stream(stream)), "kvc_quant_decode_step")

@@ -72,6 +72,42 @@ kvc_status_t paged_view(const kvc_paged_cache_t* pc, bool for_decode, kvc_cache_
   return KVC_OK;
 }
 
+kvc_status_t check_qcache(const kvc_qcache_t* c, bool for_decode) {
+  if (c == nullptr) return KVC_ERR_NULL;
+  if (c->format != KVC_QFMT_FP8_E4M3 && c->format != KVC_QFMT_INT8) return KVC_ERR_DTYPE;
+  if (elem_bytes(c->in_dtype) == 0) return KVC_ERR_DTYPE;
+  if (for_decode && c->in_dtype == KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (c->batch < 0 || c->n_kv_heads <= 0 || c->max_len < 0 || c->head_dim <= 0) return KVC_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return KVC_ERR_UNSUPPORTED;
+  if (c->batch == 0) return KVC_OK;  // nothing will be touched
+  if (c->k == nullptr || c->v == nullptr || c->k_scale == nullptr || c->v_scale == nullptr) return KVC_ERR_NULL;
+  if (c->stride_b < 0 || c->stride_h < 0 || c->stride_t < c->head_dim) return KVC_ERR_SHAPE;
+  if (c->n_kv_heads > 1 && c->stride_h < c->head_dim) return KVC_ERR_SHAPE;
+  if (c->batch > 1 && c->stride_b < c->head_dim) return KVC_ERR_SHAPE;
+  if (c->scale_stride_b < 0 || c->scale_stride_h < 0) return KVC_ERR_SHAPE;
+  if (c->n_kv_heads > 1 && c->scale_stride_h < c->max_len) return KVC_ERR_SHAPE;
+  if (c->batch > 1 && c->scale_stride_b < c->max_len) return KVC_ERR_SHAPE;
+  if (!aligned(c->k, 16) || !aligned(c->v, 16)) return KVC_ERR_ALIGN;
+  if (c->stride_b % 16 || c->stride_h % 16 || c->stride_t % 16) return KVC_ERR_ALIGN;
+  if (!aligned(c->k_scale, 4) || !aligned(c->v_scale, 4)) return KVC_ERR_ALIGN;
+  return KVC_OK;
+}
+
+kvc_cache_t qcache_view(const kvc_qcache_t* c) {
+  kvc_cache_t v = {};
+  v.k = c->k;
+  v.v = c->v;
+  v.batch = c->batch;
+  v.n_kv_heads = c->n_kv_heads;
+  v.max_len = c->max_len;
+  v.head_dim = c->head_dim;
+  v.dtype = KVC_F16;   // not read by the split heuristic or the workspace layout
+  v.stride_b = c->stride_b;
+  v.stride_h = c->stride_h;
+  v.stride_t = c->stride_t;
+  return v;
+}
+
 int copy_vector_bytes(const kvc_cache_t* c, const void* src_k, const void* src_v,
                       const int64_t* src_strides_bytes, int n_src_strides) {
   const int s = elem_bytes(c->dtype);
@@ -192,6 +228,14 @@ extern "C" size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return 0;
   const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
   return kvc::workspace_bytes(cache, n_q_heads, s);
+}
+
+extern "C" size_t kvc_quant_decode_workspace_bytes(const kvc_qcache_t* cache, int32_t n_q_heads, int32_t n_splits) {
+  if (kvc::check_qcache(cache, true) != KVC_OK) return 0;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return 0;
+  const kvc_cache_t view = kvc::qcache_view(cache);
+  const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads);
+  return kvc::workspace_bytes(&view, n_q_heads, s);
 }
 
 extern "C" size_t kvc_paged_decode_workspace_bytes(const kvc_paged_cache_t* cache, int32_t n_q_heads,

@@ -56,6 +56,13 @@ struct PageInfo {
 // `info`; same status codes as check_cache.
 kvc_status_t paged_view(const kvc_paged_cache_t* pc, bool for_decode, kvc_cache_t* view, PageInfo* info);
 
+// Checks a quantised cache descriptor. for_decode: the queries must be fp16
+// or bf16 (the append and fill calls also take fp32 rows).
+kvc_status_t check_qcache(const kvc_qcache_t* c, bool for_decode);
+// The geometry of a quantised cache (batch, heads, max_len, head_dim) as a
+// cache descriptor, for the split heuristic and the workspace layout only.
+kvc_cache_t qcache_view(const kvc_qcache_t* c);
+
 }  // namespace kvc
 
 #endif  // KVC_INTERNAL_H_

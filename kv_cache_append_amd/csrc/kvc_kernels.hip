@@ -33,6 +33,7 @@
 //     whose chunk holds slot T_b reads that row from k_t/v_t and writes it
 //     into the cache, so append and attention share the launch.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "kvc.h"
@@ -153,6 +154,7 @@ struct F32T {
 };
 
 struct F16T {
+  static constexpr bool kIsF16 = true;
   static constexpr int kBytes = 2;
   static constexpr int kPerVec = 8;
   __device__ static inline void unpack(const u32x4 r, float* f) {
@@ -191,6 +193,7 @@ struct F16T {
 };
 
 struct BF16T {
+  static constexpr bool kIsF16 = false;
   static constexpr int kBytes = 2;
   static constexpr int kPerVec = 8;
   __device__ static inline void unpack(const u32x4 r, float* f) {
@@ -326,6 +329,11 @@ struct DecodeParams {
   // tokens, token number t in slot t % max_len; decode attends
   // min(seq_lens[b] + n_pending, max_len) slots.
   int32_t ring;
+  // Quantised cache (8-bit codes): fp32 scales per token of K and of V,
+  // [B, H_kv, T_max] with byte strides ssb, ssh and 4 bytes per token.
+  const char* k_scale;
+  const char* v_scale;
+  int64_t ssb, ssh;
   float scale_log2;            // softmax scale * log2(e)
 };
 
@@ -440,12 +448,67 @@ constexpr int kCoherent = 16;   // buffer cache policy: device scope (write-thro
 __device__ inline u32x4 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
 }
+__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0));
+}
 __device__ inline u32x4 buf_load_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kCoherent));
 }
 __device__ inline void buf_store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), r,
                                          static_cast<int>(off), 0, kCoherent);
+}
+
+// 8-bit cache codes (KQ = 1: OCP E4M3, KQ = 2: int8). Every code's value has
+// at most 8 significant bits, so widening it to fp16, bf16 or fp32 is exact;
+// the scales are applied to scores and weights, not here.
+constexpr int kQuantFp8 = 1;
+constexpr int kQuantInt8 = 2;
+
+// Codes in bytes 2*HI, 2*HI+1 of w, as two fp32 values.
+template <int KQ, bool HI>
+__device__ inline void code_pair_f32(uint32_t w, float& a, float& b) {
+  if constexpr (KQ == kQuantFp8) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    a = f[0];
+    b = f[1];
+  } else {
+    a = static_cast<float>(static_cast<int32_t>(w << (HI ? 8 : 24)) >> 24);
+    b = static_cast<float>(static_cast<int32_t>(w << (HI ? 0 : 16)) >> 24);
+  }
+}
+
+// The same two codes as two packed values of the query's 16-bit type.
+template <int KQ, typename ET, bool HI>
+__device__ inline uint32_t code_pair_16(uint32_t w) {
+  if constexpr (KQ == kQuantFp8 && ET::kIsF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  } else {
+    float a, b;
+    code_pair_f32<KQ, HI>(w, a, b);
+    if constexpr (ET::kIsF16) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    } else {   // bf16: the high half of an fp32 value with at most 8 significant bits
+      return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    }
+  }
+}
+
+// Eight codes (two dwords) as the 8-element MFMA operand of the query's type.
+template <int KQ, typename ET>
+__device__ inline u32x4 codes8_16(uint32_t w0, uint32_t w1) {
+  return u32x4{code_pair_16<KQ, ET, false>(w0), code_pair_16<KQ, ET, true>(w0), code_pair_16<KQ, ET, false>(w1),
+               code_pair_16<KQ, ET, true>(w1)};
+}
+
+// Eight codes as fp32 values, in order.
+template <int KQ>
+__device__ inline void codes8_f32(const u32x2 r, float* f) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    code_pair_f32<KQ, false>(r[i], f[4 * i], f[4 * i + 1]);
+    code_pair_f32<KQ, true>(r[i], f[4 * i + 2], f[4 * i + 3]);
+  }
 }
 
 // Tuning constants (measured on MI355X): waves per decode workgroup, row
@@ -477,15 +540,22 @@ constexpr bool decode_uses_mfma() { return ET::kBytes == 2 && D % 32 == 0; }
 
 // Workgroups each CU should hold at once, which sets the VGPR budget
 // (512 / workgroups per SIMD).
-template <typename ET, int D, int GB>
+template <typename ET, int D, int GB, int KQ = 0>
 constexpr int decode_min_wgs() {
-  if constexpr (decode_uses_mfma<ET, D>()) return (GB > 4 || D > 128) ? 1 : KVC_MFMA_OCCUPANCY;
+  if constexpr (KQ != 0 || decode_uses_mfma<ET, D>()) return (GB > 4 || D > 128) ? 1 : KVC_MFMA_OCCUPANCY;
   return (ET::kBytes == 2 && GB <= 4) ? KVC_OCCUPANCY : 1;
 }
 
-template <typename ET, int D, int GB>
-__global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void decode_kernel(const DecodeParams p) {
-  constexpr int EPL = ET::kPerVec;        // elements per lane per row
+// ET: the type of q and out (and of the cache, KQ = 0); KQ != 0: a cache of
+// 8-bit codes with per-token scales (see the format helpers above).
+template <typename ET, int D, int GB, int KQ = 0>
+__global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) void decode_kernel(
+    const DecodeParams p) {
+  constexpr bool kQuant = KQ != 0;
+  // Cache elements per lane of a row in the V layout: one 16-byte slice, or
+  // 8 bytes of 8-bit codes (so the fp32 accumulators per lane stay 8 per head).
+  constexpr int EPL = kQuant ? 8 : ET::kPerVec;
+  constexpr int VSL = kQuant ? 8 : 16;     // bytes per lane slice of a row
   constexpr int LPR = D / EPL;            // lanes per row
   constexpr int RPP = 64 / LPR;           // rows per wave pass
   constexpr int NW = KVC_WAVES;           // waves per workgroup
@@ -500,7 +570,8 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   constexpr int kMaxSpins = 1 << 20;      // bound on the merge's wait for ready flags
   static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must split into 16-byte lane slices");
 
-  constexpr bool kMfma = decode_uses_mfma<ET, D>();
+  constexpr bool kMfma = kQuant || decode_uses_mfma<ET, D>();
+  static_assert(!kQuant || (ET::kBytes == 2 && D % 64 == 0), "8-bit caches: 16-bit queries, D a multiple of 64");
   constexpr int NQ = (GB + 3) / 4;         // quads of query heads (matrix-core path)
 
   // Matrix-core path with up to 4 heads: one softmax reference per wave, so
@@ -588,18 +659,31 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     const char* ksrc;
     const char* vsrc;
     if (x_new) {
-      const int64_t noff = b * p.nsb + g * p.nsh + li * 16;
+      const int64_t noff = b * p.nsb + g * p.nsh + li * VSL;
       ksrc = p.k_new + noff;
       vsrc = p.v_new + noff;
     } else {
       const int64_t xo = slot_offset(p, b, g, xrow);
-      ksrc = xo < 0 ? nullptr : p.k + xo + li * 16;
-      vsrc = xo < 0 ? nullptr : p.v + xo + li * 16;
+      ksrc = xo < 0 ? nullptr : p.k + xo + li * VSL;
+      vsrc = xo < 0 ? nullptr : p.v + xo + li * VSL;
       if (xo < 0 && lane == 0) flag(p, KVC_DEVERR_PAGE);
     }
     if (ksrc != nullptr) {
-      nk = *reinterpret_cast<const u32x4*>(ksrc);
-      nv = *reinterpret_cast<const u32x4*>(vsrc);
+      if constexpr (kQuant) {                  // 8 code bytes of V (K is loaded in the MFMA layout)
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc);
+        nv = u32x4{w[0], w[1], 0u, 0u};
+      } else {
+        nk = *reinterpret_cast<const u32x4*>(ksrc);
+        nv = *reinterpret_cast<const u32x4*>(vsrc);
+      }
+    }
+  }
+  float xks = 0.f, xvs = 0.f;                   // scales of the folded row (8-bit caches)
+  if constexpr (kQuant) {
+    if (has_x && wave == 0) {
+      const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(xrow) * 4;
+      xks = *reinterpret_cast<const float*>(p.k_scale + so);
+      xvs = *reinterpret_cast<const float*>(p.v_scale + so);
     }
   }
 
@@ -629,7 +713,15 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     // lanes 4b..4b+3, all of one row: A = the weight of head 4q + l%4, B = V
     // element e of lane l, C = the head quad's outputs for that column) or on
     // the vector ALU for 1-2 heads.
+    // 8-bit caches: a lane's 16-byte load of a K row holds 16 codes, which
+    // feed two MFMAs after widening to q's type (load i, lane group kq:
+    // elements 64i + 16kq .. +16; the first 8 go to MFMA 2i, the rest to
+    // MFMA 2i+1, and q is loaded in that order). The scores are scaled by the
+    // row's K scale before the masks, and each weight is multiplied by its
+    // row's V scale on its way to LDS (the row sums use the unscaled weights).
     constexpr int NM = D / 32;                // score MFMAs per tile
+    constexpr int NKL = kQuant ? NM / 2 : NM;  // 16-byte K loads per lane per tile
+    using VT = std::conditional_t<kQuant, u32x2, u32x4>;   // a lane's slice of a V row
     constexpr int NP = 16 / RPP;              // V row passes per tile
     constexpr int TSM = NW * 16;              // rows per workgroup tile
     constexpr int NBM = KVC_MFMA_PREFETCH + 1;
@@ -640,9 +732,9 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       qa[m] = u32x4{0u, 0u, 0u, 0u};
+      const int qe = kQuant ? 64 * (m >> 1) + 16 * kq + 8 * (m & 1) : (4 * m + kq) * EPL;   // first element
       if (r16 < nh)
-        qa[m] = *reinterpret_cast<const u32x4*>(
-            p.q + (pair_row(p, b, g, v_first + r16) * D + (4 * m + kq) * EPL) * ET::kBytes);
+        qa[m] = *reinterpret_cast<const u32x4*>(p.q + (pair_row(p, b, g, v_first + r16) * D + qe) * ET::kBytes);
     }
     float hbias[4];                           // 0 where (lane, register) is a real head's score
 #pragma unroll
@@ -661,12 +753,12 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
 #pragma unroll
       for (int e = 0; e < EPL; ++e) accq[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t koff[NM], voffm[NP];
+    uint32_t koff[NKL], voffm[NP];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) koff[m] = static_cast<uint32_t>(r16) * st + static_cast<uint32_t>(4 * m + kq) * 16u;
+    for (int m = 0; m < NKL; ++m) koff[m] = static_cast<uint32_t>(r16) * st + static_cast<uint32_t>(4 * m + kq) * 16u;
 #pragma unroll
     for (int u = 0; u < NP; ++u)
-      voffm[u] = static_cast<uint32_t>(u * RPP + grp) * st + static_cast<uint32_t>(li) * 16u;
+      voffm[u] = static_cast<uint32_t>(u * RPP + grp) * st + static_cast<uint32_t>(li * VSL);
 
     // Paged caches: a wave's tiles start at slots wbase0 + k * TSM. Lane j
     // of `pidv` holds the page of tile (k & ~63) + j, loaded 64 tiles at a
@@ -685,7 +777,9 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       }
       return __builtin_amdgcn_readlane(pidv, k & 63);
     };
-    auto load_tile = [&](int base_any, u32x4 (&K)[NM], u32x4 (&V)[NP]) {
+    // the scales of this unit's rows (8-bit caches), 4 bytes per token
+    const int64_t sunit = b * p.ssb + g * p.ssh;
+    auto load_tile = [&](int base_any, u32x4 (&K)[NKL], VT (&V)[NP], float& KS, float& VS) {
       const int base = __builtin_amdgcn_readfirstlane(base_any);
       const int rows_left = t_end - base;
       uint32_t range = rows_left > 0 ? static_cast<uint32_t>(rows_left) * st : 0u;
@@ -706,9 +800,20 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr(p.k + boff), range);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr(p.v + boff), range);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) K[m] = buf_load(krs, koff[m]);
+      for (int m = 0; m < NKL; ++m) K[m] = buf_load(krs, koff[m]);
 #pragma unroll
-      for (int u = 0; u < NP; ++u) V[u] = buf_load(vrs, voffm[u]);
+      for (int u = 0; u < NP; ++u) {
+        if constexpr (kQuant) V[u] = buf_load8(vrs, voffm[u]);
+        else V[u] = buf_load(vrs, voffm[u]);
+      }
+      if constexpr (kQuant) {                 // row r16's scales; rows past t_end read as 0
+        const uint32_t srange = rows_left > 0 ? static_cast<uint32_t>(rows_left) * 4u : 0u;
+        const int64_t soff = sunit + static_cast<int64_t>(base) * 4;
+        const __amdgpu_buffer_rsrc_t ksr = make_rsrc(uniform_ptr(p.k_scale + soff), srange);
+        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(uniform_ptr(p.v_scale + soff), srange);
+        KS = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(ksr, r16 * 4, 0, 0)));
+        VS = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(vsr, r16 * 4, 0, 0)));
+      }
     };
 
     auto lane_ref = [&](int t) { return (NQ > 1 && kq == 1) ? refh[4 + t] : refh[t]; };
@@ -716,10 +821,22 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
     const f32x4 hb4 = f32x4{hbias[0], hbias[1], hbias[2], hbias[3]};
     // rows_left: rows of this tile to attend (all 16 unless it is the last);
     // row0: the tile's first slot, for the per-pair limits of a query block
-    auto compute = [&](const u32x4 (&K)[NM], const u32x4 (&V)[NP], int rows_left, int row0) {
-      f32x4 sv = ET::mfma16(qa[0], K[0], hb4);
+    // KS, VS: this lane's row's K and V scales (8-bit caches)
+    auto compute = [&](const u32x4 (&K)[NKL], const VT (&V)[NP], float KS, float VS, int rows_left, int row0) {
+      f32x4 sv;
+      if constexpr (kQuant) {
+        sv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 1; m < NM; ++m) sv = ET::mfma16(qa[m], K[m], sv);
+        for (int m = 0; m < NM; ++m)
+          sv = ET::mfma16(qa[m], codes8_16<KQ, ET>(K[m >> 1][2 * (m & 1)], K[m >> 1][2 * (m & 1) + 1]), sv);
+        const float f = KS * sc;              // K scale and softmax scale (log2 domain)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sv[t] = fmaf(sv[t], f, hbias[t]);
+      } else {
+        sv = ET::mfma16(qa[0], K[0], hb4);
+#pragma unroll
+        for (int m = 1; m < NM; ++m) sv = ET::mfma16(qa[m], K[m], sv);
+      }
       if (rows_left < 16) {                   // wave-uniform: only a last, partial tile
 #pragma unroll
         for (int t = 0; t < 4; ++t) sv[t] = r16 < rows_left ? sv[t] : -INFINITY;
@@ -732,7 +849,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       bool need = false;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        w[t] = sv[t] * sc;                    // log2-domain score
+        w[t] = kQuant ? sv[t] : sv[t] * sc;   // log2-domain score
         rl[t] = lane_ref(t);
         need = need || (w[t] > rl[t] + kLazy);
       }
@@ -764,13 +881,15 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
         pw[t] = fast_exp2(w[t] - rl[t]);
         lsum[t] += pw[t];
       }
+      if constexpr (kQuant) pw *= VS;         // V scale of this lane's row
       if (kq < NQ) *reinterpret_cast<f32x4*>(&sm_p[wave][r16][4 * kq]) = pw;
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
         const int r = u * RPP + grp;          // row of this lane in pass u
         float vf[EPL];
-        ET::unpack(V[u], vf);
+        if constexpr (kQuant) codes8_f32<KQ>(V[u], vf);
+        else ET::unpack(V[u], vf);
         if constexpr (GB >= 4) {
 #pragma unroll
           for (int q = 0; q < NQ; ++q) {
@@ -797,15 +916,18 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       int base = __builtin_amdgcn_readfirstlane((seg == 0 ? t0 : seg1_lo) + wave * 16);
       const int n_tiles = base < t_end ? (t_end - base + TSM - 1) / TSM : 0;
       if (n_tiles > 0) {
-        u32x4 KB[NBM][NM], VB[NBM][NP];
+        u32x4 KB[NBM][NKL];
+        VT VB[NBM][NP];
+        float KSB[NBM], VSB[NBM];
 #pragma unroll
-        for (int r = 0; r < NBM - 1; ++r) load_tile(base + r * TSM, KB[r], VB[r]);
+        for (int r = 0; r < NBM - 1; ++r) load_tile(base + r * TSM, KB[r], VB[r], KSB[r], VSB[r]);
         bool done = false;
         for (int it = 0; !done; it += NBM) {
 #pragma unroll
           for (int r = 0; r < NBM; ++r) {     // unrolled: ring slots are compile-time
-            load_tile(base + (NBM - 1) * TSM, KB[(r + NBM - 1) % NBM], VB[(r + NBM - 1) % NBM]);
-            compute(KB[r], VB[r], __builtin_amdgcn_readfirstlane(t_end - base), base);
+            const int nr = (r + NBM - 1) % NBM;
+            load_tile(base + (NBM - 1) * TSM, KB[nr], VB[nr], KSB[nr], VSB[nr]);
+            compute(KB[r], VB[r], KSB[r], VSB[r], __builtin_amdgcn_readfirstlane(t_end - base), base);
             base += TSM;
             if (it + r + 1 >= n_tiles) {
               done = true;
@@ -816,17 +938,21 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
       }
     }
     if (has_x && wave == 0) {                 // the last attended row, as row 0 of one more tile
-      u32x4 K[NM], V[NP];
+      u32x4 K[NKL];
+      VT V[NP];
       const int64_t xo = x_new ? 0 : slot_offset(p, b, g, xrow);
       const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : (xo < 0 ? nullptr : p.k + xo);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
+      for (int m = 0; m < NKL; ++m) {
         K[m] = u32x4{0u, 0u, 0u, 0u};
         if (r16 == 0 && kx != nullptr) K[m] = *reinterpret_cast<const u32x4*>(kx + (4 * m + kq) * 16);
       }
 #pragma unroll
-      for (int u = 0; u < NP; ++u) V[u] = (u == 0 && grp == 0) ? nv : u32x4{0u, 0u, 0u, 0u};
-      compute(K, V, 1, xrow);
+      for (int u = 0; u < NP; ++u) {
+        if constexpr (kQuant) V[u] = (u == 0 && grp == 0) ? u32x2{nv[0], nv[1]} : u32x2{0u, 0u};
+        else V[u] = (u == 0 && grp == 0) ? nv : u32x4{0u, 0u, 0u, 0u};
+      }
+      compute(K, V, r16 == 0 ? xks : 0.f, r16 == 0 ? xvs : 0.f, 1, xrow);
     }
     // Wave totals in the common layout: one reference per head (the same in
     // every lane), the weight sum in lane group 0 only (the lane-group merge
@@ -995,7 +1121,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB>())) void
   }
   }   // vector-ALU path
 
-  if (has_x && wave == 0 && x_new && hb == 0 && grp == 0) {   // fused append: write the new row
+  if (!kQuant && has_x && wave == 0 && x_new && hb == 0 && grp == 0) {   // fused append: write the new row
     const int64_t ao = slot_offset(p, b, g, arow);
     if (ao >= 0) {
       *reinterpret_cast<u32x4*>(p.k + ao + li * 16) = nk;
@@ -1261,6 +1387,273 @@ DecodeKernel pick_decode_kernel(int dtype, int d, int gb) {
     case KVC_BF16: return pick_d<BF16T>(d, gb);
     default: return nullptr;
   }
+}
+
+template <typename ET, int D, int KQ>
+DecodeKernel pick_gb_quant(int gb) {
+  switch (gb) {
+    case 1: return decode_kernel<ET, D, 1, KQ>;
+    case 2: return decode_kernel<ET, D, 2, KQ>;
+    case 4: return decode_kernel<ET, D, 4, KQ>;
+    default: return decode_kernel<ET, D, 8, KQ>;
+  }
+}
+
+template <typename ET, int KQ>
+DecodeKernel pick_d_quant(int d, int gb) {
+  switch (d) {
+    case 64: return pick_gb_quant<ET, 64, KQ>(gb);
+    case 128: return pick_gb_quant<ET, 128, KQ>(gb);
+    case 256: return pick_gb_quant<ET, 256, KQ>(gb);
+    default: return nullptr;
+  }
+}
+
+// Decode over 8-bit codes: q (and out) fp16 or bf16.
+DecodeKernel pick_quant_kernel(int format, int q_dtype, int d, int gb) {
+  const bool fp8 = format == KVC_QFMT_FP8_E4M3;
+  if (q_dtype == KVC_F16) return fp8 ? pick_d_quant<F16T, kQuantFp8>(d, gb) : pick_d_quant<F16T, kQuantInt8>(d, gb);
+  if (q_dtype == KVC_BF16) return fp8 ? pick_d_quant<BF16T, kQuantFp8>(d, gb) : pick_d_quant<BF16T, kQuantInt8>(d, gb);
+  return nullptr;
+}
+
+// ------------------------------------------------ quantised append / fill --
+
+struct QuantParams {
+  char* kc;                  // codes
+  char* vc;
+  char* ks;                  // scales
+  char* vs;
+  int64_t cb, ch, ct;        // code strides in bytes
+  int64_t ssb, ssh;          // scale strides in bytes (4 bytes per token)
+  const char* src_k;         // new rows [B, H_kv, T_new, D] of the input type
+  const char* src_v;
+  int64_t sb, sh, st;        // their strides in bytes
+  const int32_t* seq_lens;
+  uint32_t* status;
+  int32_t batch, n_kv, max_len, t_new;
+};
+
+// fp32 -> OCP E4M3 byte: round to nearest even, saturate at +-448, NaN -> 0x7F.
+__device__ inline uint32_t e4m3_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t au = u & 0x7fffffffu;
+  if (au > 0x7f800000u) return 0x7Fu;                  // NaN
+  const float a = __uint_as_float(au);
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                                 // below 2^-6: multiples of 2^-9
+    // a * 512 is exact; rint rounds ties to even; 8 is the code of 2^-6
+    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.f));
+  }
+  uint32_t e = (au >> 23) - 120u;                      // biased E4M3 exponent (bias 7), 1..15
+  const uint32_t mant = au & 0x7fffffu;
+  uint32_t m = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, ties to even; 8 carries
+  if (m == 8u) {
+    e += 1u;
+    m = 0u;
+  }
+  const uint32_t code = (e << 3) | m;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+template <typename IT>
+__device__ inline float load_elem(const char* row, int i) {
+  if constexpr (IT::kBytes == 4) return reinterpret_cast<const float*>(row)[i];
+  else if constexpr (IT::kIsF16) return static_cast<float>(reinterpret_cast<const _Float16*>(row)[i]);
+  else return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
+}
+
+// One wave per new row (K rows, then V rows): lane l holds elements
+// [l*E, l*E + E). amax over the row by a wave-wide maximum, scale = amax /
+// QMAX and each code from x / scale, both fp32 divisions (correctly rounded),
+// then E code bytes per lane and the scale from lane 0.
+template <typename IT, int KQ, int D>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const QuantParams p) {
+  constexpr int E = D / 64;
+  constexpr float kQmax = KQ == kQuantFp8 ? 448.f : 127.f;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = static_cast<int64_t>(p.batch) * p.n_kv * p.t_new;
+  const int64_t n_waves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  for (int64_t r = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6; r < 2 * rows; r += n_waves) {
+    const bool is_v = r >= rows;
+    const int64_t rr = is_v ? r - rows : r;
+    const int i = static_cast<int>(rr % p.t_new);
+    const int64_t bg = rr / p.t_new;
+    const int g = static_cast<int>(bg % p.n_kv);
+    const int b = static_cast<int>(bg / p.n_kv);
+    const int pos = p.seq_lens[b];
+    if (pos < 0 || static_cast<int64_t>(pos) + p.t_new > p.max_len) {   // whole sequence skipped
+      if (lane == 0 && !is_v && g == 0 && i == 0 && p.status != nullptr)
+        atomicOr(p.status, pos < 0 ? KVC_DEVERR_BADLEN : KVC_DEVERR_CAPACITY);
+      continue;
+    }
+    const char* src = (is_v ? p.src_v : p.src_k) + b * p.sb + g * p.sh + static_cast<int64_t>(i) * p.st;
+    float x[E];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      x[e] = load_elem<IT>(src, lane * E + e);
+      amax = fmaxf(amax, fabsf(x[e]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float scale = amax / kQmax;
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      uint32_t c = 0u;
+      if (amax > 0.f) {
+        const float y = x[e] / scale;
+        if constexpr (KQ == kQuantFp8) {
+          c = e4m3_from_f32(y);
+        } else {
+          c = static_cast<uint32_t>(static_cast<int32_t>(fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f))) & 0xffu;
+        }
+      }
+      packed |= c << (8 * e);
+    }
+    const int slot = pos + i;
+    char* dst = (is_v ? p.vc : p.kc) + b * p.cb + g * p.ch + static_cast<int64_t>(slot) * p.ct + lane * E;
+    if constexpr (E == 1) *reinterpret_cast<uint8_t*>(dst) = static_cast<uint8_t>(packed);
+    else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+    else *reinterpret_cast<uint32_t*>(dst) = packed;
+    if (lane == 0)
+      *reinterpret_cast<float*>((is_v ? p.vs : p.ks) + b * p.ssb + g * p.ssh + static_cast<int64_t>(slot) * 4) =
+          amax > 0.f ? scale : 0.f;
+  }
+}
+
+typedef void (*QuantKernel)(const QuantParams);
+
+template <typename IT, int KQ>
+QuantKernel pick_quant_rows_d(int d) {
+  switch (d) {
+    case 64: return quant_rows_kernel<IT, KQ, 64>;
+    case 128: return quant_rows_kernel<IT, KQ, 128>;
+    case 256: return quant_rows_kernel<IT, KQ, 256>;
+    default: return nullptr;
+  }
+}
+
+template <int KQ>
+QuantKernel pick_quant_rows_t(int in_dtype, int d) {
+  switch (in_dtype) {
+    case KVC_F32: return pick_quant_rows_d<F32T, KQ>(d);
+    case KVC_F16: return pick_quant_rows_d<F16T, KQ>(d);
+    case KVC_BF16: return pick_quant_rows_d<BF16T, KQ>(d);
+    default: return nullptr;
+  }
+}
+
+kvc_status_t launch_quant_rows(const kvc_qcache_t* c, const int32_t* seq_lens, const void* k, const void* v,
+                               int64_t sb, int64_t sh, int64_t st, int32_t t_new, uint32_t* status,
+                               hipStream_t stream) {
+  kvc_status_t rc = kvc::check_qcache(c, false);
+  if (rc != KVC_OK) return rc;
+  if (t_new < 0) return KVC_ERR_SHAPE;
+  if (c->batch == 0 || t_new == 0) return KVC_OK;
+  if (seq_lens == nullptr || k == nullptr || v == nullptr) return KVC_ERR_NULL;
+  if (sb < 0 || sh < 0 || st < 0) return KVC_ERR_SHAPE;
+  if (t_new > 1 && st < c->head_dim) return KVC_ERR_SHAPE;
+  const int s = kvc::elem_bytes(c->in_dtype);
+  if (reinterpret_cast<uintptr_t>(k) % s || reinterpret_cast<uintptr_t>(v) % s) return KVC_ERR_ALIGN;
+  const QuantKernel kern = c->format == KVC_QFMT_FP8_E4M3 ? pick_quant_rows_t<kQuantFp8>(c->in_dtype, c->head_dim)
+                                                          : pick_quant_rows_t<kQuantInt8>(c->in_dtype, c->head_dim);
+  if (kern == nullptr) return KVC_ERR_UNSUPPORTED;
+  QuantParams p;
+  p.kc = static_cast<char*>(c->k);
+  p.vc = static_cast<char*>(c->v);
+  p.ks = reinterpret_cast<char*>(c->k_scale);
+  p.vs = reinterpret_cast<char*>(c->v_scale);
+  p.cb = c->stride_b;
+  p.ch = c->stride_h;
+  p.ct = c->stride_t;
+  p.ssb = c->scale_stride_b * 4;
+  p.ssh = c->scale_stride_h * 4;
+  p.src_k = static_cast<const char*>(k);
+  p.src_v = static_cast<const char*>(v);
+  p.sb = sb * s;
+  p.sh = sh * s;
+  p.st = st * s;
+  p.seq_lens = seq_lens;
+  p.status = status;
+  p.batch = c->batch;
+  p.n_kv = c->n_kv_heads;
+  p.max_len = c->max_len;
+  p.t_new = t_new;
+  const int64_t waves = 2 * static_cast<int64_t>(c->batch) * c->n_kv_heads * t_new;
+  int64_t blocks = (waves + 3) / 4;             // 4 waves per 256-thread block
+  if (blocks > 65536) blocks = 65536;           // the wave loop covers the rest
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens, int32_t n_pending, const void* q,
+                                 int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status,
+                                 hipStream_t stream) {
+  kvc_status_t rc = kvc::check_qcache(c, true);
+  if (rc != KVC_OK) return rc;
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return KVC_ERR_GQA;
+  if (n_pending < 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return KVC_ERR_SHAPE;
+  if (out_dtype != KVC_F32 && out_dtype != c->in_dtype) return KVC_ERR_DTYPE;
+  const float scale_log2 = scale * 1.44269504088896340736f;  // log2(e)
+  if (!(scale > 0.f) || !(scale_log2 < INFINITY)) return KVC_ERR_UNSUPPORTED;
+  if (c->batch == 0) return KVC_OK;
+  if (seq_lens == nullptr || q == nullptr || out == nullptr) return KVC_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(q) % 16) return KVC_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(out) % kvc::elem_bytes(out_dtype)) return KVC_ERR_ALIGN;
+  if ((static_cast<int64_t>(c->max_len) + 2048) * c->stride_t > 0x7fffffffll) return KVC_ERR_SHAPE;
+  const kvc_cache_t view = kvc::qcache_view(c);
+  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads);
+  const size_t need = kvc::workspace_bytes(&view, n_q_heads, splits);
+  if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
+  const int group = n_q_heads / c->n_kv_heads;
+  const DecodeKernel k = pick_quant_kernel(c->format, c->in_dtype, c->head_dim, kvc::heads_per_block(group));
+  if (k == nullptr) return KVC_ERR_UNSUPPORTED;
+
+  DecodeParams p = {};
+  p.k = static_cast<char*>(c->k);
+  p.v = static_cast<char*>(c->v);
+  p.sb = c->stride_b;
+  p.sh = c->stride_h;
+  p.st = c->stride_t;
+  p.seq_lens = seq_lens;
+  p.q = static_cast<const char*>(q);
+  p.k_new = nullptr;
+  p.v_new = nullptr;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_cnt = reinterpret_cast<uint32_t*>(ws);
+  p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(&view, n_q_heads, splits));
+  p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(&view, n_q_heads, splits));
+  p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(&view, n_q_heads, splits));
+  p.out = out;
+  p.status = dev_status;
+  p.batch = c->batch;
+  p.n_q = n_q_heads;
+  p.n_kv = c->n_kv_heads;
+  p.group = group;
+  p.n_hblk = kvc::head_blocks(group);
+  p.max_len = c->max_len;
+  p.n_pending = n_pending;
+  p.n_splits = splits;
+  p.out_f32 = out_dtype == KVC_F32 ? 1 : 0;
+  p.t_q = 1;
+  p.block = 0;
+  p.table = nullptr;
+  p.ring = 0;
+  p.k_scale = reinterpret_cast<const char*>(c->k_scale);
+  p.v_scale = reinterpret_cast<const char*>(c->v_scale);
+  p.ssb = c->scale_stride_b * 4;
+  p.ssh = c->scale_stride_h * 4;
+  p.scale_log2 = scale_log2;
+  const int64_t items = static_cast<int64_t>(c->batch) * c->n_kv_heads * splits;
+  const int64_t wgs = (items + 7) / 8 * 8 * p.n_hblk;     // see the id mapping in decode_kernel
+  if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(KVC_WAVES * 64), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
 kvc_status_t launch_copy(const kvc_cache_t* c, const int32_t* seq_lens, const void* ks, const void* vs,
@@ -1596,4 +1989,61 @@ extern "C" kvc_status_t kvc_ring_decode_step(const kvc_cache_t* cache, const int
   if (cache != nullptr && cache->batch > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_NULL;
   return launch_decode(cache, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
                        out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, 0, nullptr, true);
+}
+
+// -------------------------------------------------------- quantised cache --
+
+extern "C" kvc_status_t kvc_quant_append(const kvc_qcache_t* cache, const int32_t* seq_lens, const void* k_new,
+                                         const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
+                                         uint32_t* dev_status, hipStream_t stream) {
+  return launch_quant_rows(cache, seq_lens, k_new, v_new, new_stride_b, new_stride_h, 0, 1, dev_status, stream);
+}
+
+extern "C" kvc_status_t kvc_quant_prefill_fill(const kvc_qcache_t* cache, const int32_t* seq_lens, const void* k,
+                                               const void* v, int64_t src_stride_b, int64_t src_stride_h,
+                                               int64_t src_stride_t, int32_t t_new, uint32_t* dev_status,
+                                               hipStream_t stream) {
+  return launch_quant_rows(cache, seq_lens, k, v, src_stride_b, src_stride_h, src_stride_t, t_new, dev_status,
+                           stream);
+}
+
+extern "C" kvc_status_t kvc_quant_decode_attn(const kvc_qcache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                                              const void* q, int32_t n_q_heads, float scale, void* out,
+                                              int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                              int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
+  return launch_quant_decode(cache, seq_lens, n_pending, q, n_q_heads, scale, out, out_dtype, workspace,
+                             workspace_bytes, n_splits, dev_status, stream);
+}
+
+extern "C" kvc_status_t kvc_quant_decode_step(const kvc_qcache_t* cache, const int32_t* seq_lens, const void* k_new,
+                                              const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
+                                              const void* q, int32_t n_q_heads, float scale, void* out,
+                                              int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                              int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
+  // validate the attention arguments before enqueueing the append, so a
+  // host-detectable error leaves nothing enqueued
+  kvc_status_t rc = kvc::check_qcache(cache, true);
+  if (rc != KVC_OK) return rc;
+  if (cache->batch > 0) {
+    if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
+    if (n_splits < 0 || n_splits > KVC_MAX_SPLITS) return KVC_ERR_SHAPE;
+    if (out_dtype != KVC_F32 && out_dtype != cache->in_dtype) return KVC_ERR_DTYPE;
+    if (!(scale > 0.f) || !(scale * 1.44269504088896340736f < INFINITY)) return KVC_ERR_UNSUPPORTED;
+    if (seq_lens == nullptr || q == nullptr || out == nullptr || k_new == nullptr || v_new == nullptr)
+      return KVC_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(out) % kvc::elem_bytes(out_dtype)) return KVC_ERR_ALIGN;
+    if ((static_cast<int64_t>(cache->max_len) + 2048) * cache->stride_t > 0x7fffffffll) return KVC_ERR_SHAPE;
+    const kvc_cache_t view = kvc::qcache_view(cache);
+    const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads);
+    if (workspace == nullptr || workspace_bytes < kvc::workspace_bytes(&view, n_q_heads, splits))
+      return KVC_ERR_WORKSPACE;
+    if (pick_quant_kernel(cache->format, cache->in_dtype, cache->head_dim,
+                          kvc::heads_per_block(n_q_heads / cache->n_kv_heads)) == nullptr)
+      return KVC_ERR_UNSUPPORTED;
+  }
+  rc = launch_quant_rows(cache, seq_lens, k_new, v_new, new_stride_b, new_stride_h, 0, 1, dev_status, stream);
+  if (rc != KVC_OK) return rc;
+  return launch_quant_decode(cache, seq_lens, 1, q, n_q_heads, scale, out, out_dtype, workspace, workspace_bytes,
+                             n_splits, dev_status, stream);
 }

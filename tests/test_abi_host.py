@@ -267,3 +267,60 @@ def test_paged_validation_and_workspace():
     for s in (0, 1, 3):
         assert lib.kvc_paged_decode_workspace_bytes(ctypes.byref(ok), 4, s) == \
             lib.kvc_decode_workspace_bytes(ctypes.byref(contig), 4, s)
+
+
+def _qdesc(kvc, **kw):
+    """A valid kvc_qcache_t over fake device addresses (never dereferenced):
+    B=2, H_kv=2, T_max=64, D=128, fp8 codes, bf16 rows/queries."""
+    f = dict(k=4096, v=8192, k_scale=12288, v_scale=16384, batch=2, n_kv_heads=2, max_len=64, head_dim=128,
+             format=kvc.QFMT_FP8_E4M3, in_dtype=kvc.KVC_BF16, stride_b=2 * 64 * 128, stride_h=64 * 128,
+             stride_t=128, scale_stride_b=2 * 64, scale_stride_h=64)
+    f.update(kw)
+    return kvc.QCacheDesc(**f)
+
+
+def test_quant_validation_and_workspace():
+    """Quantised calls: format and dtype codes, head dims 64/128/256, scale
+    and code pointers present, 16-byte code strides, non-overlapping scale
+    rows, fp16/bf16 queries for decode; the decode workspace equals the
+    contiguous cache's of the same geometry. Every case fails before launch."""
+    kvc, lib = _lib()
+    big = 1 << 30
+
+    def dec(d, n_q=4, scale=0.1, out_dtype=0, ws_bytes=big, splits=0):
+        return lib.kvc_quant_decode_attn(ctypes.byref(d), FAKE, 1, FAKE, n_q, scale, FAKE, out_dtype, FAKE, ws_bytes,
+                                         splits, None, None)
+
+    assert dec(_qdesc(kvc, format=2)) == 3
+    assert dec(_qdesc(kvc, in_dtype=7)) == 3
+    assert dec(_qdesc(kvc, in_dtype=kvc.KVC_F32)) == 7                # fp32 queries: not for decode
+    assert dec(_qdesc(kvc, head_dim=96, stride_t=96, stride_h=64 * 96, stride_b=2 * 64 * 96)) == 7
+    assert dec(_qdesc(kvc, k_scale=None)) == 1
+    assert dec(_qdesc(kvc, stride_t=136)) == 4                        # not a multiple of 16 bytes
+    assert dec(_qdesc(kvc, k=4100)) == 4
+    assert dec(_qdesc(kvc, scale_stride_h=32)) == 2                   # scale rows of two heads overlap
+    assert dec(_qdesc(kvc, stride_t=64)) == 2                         # rows overlap
+    assert dec(_qdesc(kvc), n_q=3) == 5
+    assert dec(_qdesc(kvc), scale=-1.0) == 7
+    assert dec(_qdesc(kvc), out_dtype=kvc.KVC_F16) == 3               # out must be fp32 or the query type
+    assert dec(_qdesc(kvc), splits=257) == 2
+    need = lib.kvc_quant_decode_workspace_bytes(ctypes.byref(_qdesc(kvc)), 4, 0)
+    assert dec(_qdesc(kvc), ws_bytes=need - 1) == 6
+    contig = _desc(kvc, batch=2, n_kv_heads=2, max_len=64, stride_t=128, stride_h=64 * 128, stride_b=2 * 64 * 128)
+    for s in (0, 1, 3):
+        assert lib.kvc_quant_decode_workspace_bytes(ctypes.byref(_qdesc(kvc)), 4, s) == \
+            lib.kvc_decode_workspace_bytes(ctypes.byref(contig), 4, s)
+    assert lib.kvc_quant_decode_workspace_bytes(ctypes.byref(_qdesc(kvc, in_dtype=kvc.KVC_F32)), 4, 0) == 0
+    # append / fill: fp32 rows are accepted, so validation passes and stops at the missing seq_lens
+    assert lib.kvc_quant_append(ctypes.byref(_qdesc(kvc, in_dtype=kvc.KVC_F32)), None, FAKE, FAKE, 256, 128,
+                                None, None) == 1
+    assert lib.kvc_quant_append(None, FAKE, FAKE, FAKE, 256, 128, None, None) == 1
+    assert lib.kvc_quant_prefill_fill(ctypes.byref(_qdesc(kvc)), FAKE, FAKE, FAKE, 0, 0, 0, -1, None, None) == 2
+    assert lib.kvc_quant_prefill_fill(ctypes.byref(_qdesc(kvc)), FAKE, FAKE, FAKE, 0, 0, 0, 0, None, None) == 0
+    assert lib.kvc_quant_prefill_fill(ctypes.byref(_qdesc(kvc)), FAKE, FAKE, FAKE, 0, 0, 64, 3, None, None) == 2
+    # the step validates the attention arguments before it enqueues the append
+    step = lambda **kw: lib.kvc_quant_decode_step(ctypes.byref(_qdesc(kvc)), FAKE, FAKE, FAKE, 256, 128, FAKE,
+                                                  kw.get("n_q", 4), 0.1, FAKE, 0, FAKE, kw.get("ws", big), 0,
+                                                  None, None)
+    assert step(n_q=3) == 5
+    assert step(ws=need - 1) == 6
