@@ -121,12 +121,15 @@ class Workload:
             self.descs = [kvc.paged_desc(self.k[l], self.v[l], self.table) for l in range(L)]
         else:
             self.descs = [kvc.cache_desc(self.k[l], self.v[l]) for l in range(L)]
-        self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq * nq)
+        # the library's split choice for the lengths the first timed step attends
+        attended = self._attended_at_start()
+        self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq * nq, lengths=attended)
         if page:
             # the split choice of the contiguous cache with the same capacity
             logical = kvc.CacheDesc(self.k.data_ptr(), self.v.data_ptr(), B, Hkv, self.t_max, D,
                                     kvc.DTYPE_CODE[tdt], 0, Hkv * self.t_max * D, self.t_max * D, D)
-            self.splits = splits if splits > 0 else int(self.lib.kvc_decode_splits(ctypes.byref(logical), Hq))
+            self.splits = splits if splits > 0 else kvc.decode_splits(None, None, Hq, lengths=attended,
+                                                                      desc=logical)
             self.ws = kvc.paged_workspace(self.k[0], self.v[0], self.table, Hq, self.splits)
         elif block_q:
             self.ws = kvc.block_workspace(self.k[0], self.v[0], Hq, block_q, self.splits)
@@ -168,10 +171,18 @@ class Workload:
         self.seq_lens = self.lengths.to(dev)
         logical = kvc.CacheDesc(self.kc.data_ptr(), self.vc.data_ptr(), B, Hkv, T, D, kvc.DTYPE_CODE[tdt], 0,
                                 Hkv * T * D, T * D, D)
-        self.splits = splits if splits > 0 else int(self.lib.kvc_decode_splits(ctypes.byref(logical), Hq))
+        self.splits = splits if splits > 0 else kvc.decode_splits(None, None, Hq, lengths=self._attended_at_start(),
+                                                                  desc=logical)
         self.ws = kvc.quant_workspace(self.descs[0], Hq, self.splits)
         self.scale = ctypes.c_float(1.0 / math.sqrt(D))
         torch.cuda.synchronize()
+
+    def _attended_at_start(self):
+        """Tokens each sequence attends in the first step (host values)."""
+        n = self.lengths.to("cpu").long() + max(self.block_q, 1)
+        if self.ring:
+            n = n.clamp(max=self.ring)
+        return n.tolist()
 
     def reset_lengths(self):
         self.seq_lens.copy_(self.lengths.to(self.seq_lens.device))

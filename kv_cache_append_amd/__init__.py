@@ -34,7 +34,7 @@ STATUS = {
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
-           "kvc_decode_attn", "kvc_decode_step", "kvc_block_attn", "kvc_block_workspace_bytes",
+           "kvc_decode_attn", "kvc_decode_step", "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes",
            "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
            "kvc_paged_decode_attn", "kvc_paged_decode_step",
            "kvc_ring_append", "kvc_ring_prefill_fill", "kvc_ring_decode_attn", "kvc_ring_decode_step",
@@ -81,6 +81,8 @@ def load() -> ctypes.CDLL:
     lib.kvc_decode_workspace_bytes.restype = sz
     lib.kvc_decode_splits.argtypes = [cp, i32]
     lib.kvc_decode_splits.restype = i32
+    lib.kvc_decode_splits_for_lengths.argtypes = [cp, i32, ctypes.POINTER(i32)]
+    lib.kvc_decode_splits_for_lengths.restype = i32
     lib.kvc_decode_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_decode_attn.restype = i32
     lib.kvc_decode_step.argtypes = [cp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
@@ -261,9 +263,17 @@ def block_workspace(k_cache, v_cache, n_q_heads: int, t_q: int, n_splits: int = 
     return torch.zeros(n, dtype=torch.uint8, device=k_cache.device)
 
 
-def decode_splits(k_cache, v_cache, n_q_heads: int) -> int:
-    c = cache_desc(k_cache, v_cache)
-    return int(load().kvc_decode_splits(ctypes.byref(c), n_q_heads))
+def decode_splits(k_cache, v_cache, n_q_heads: int, lengths=None, desc=None) -> int:
+    """kvc_decode_splits, or kvc_decode_splits_for_lengths when the attended
+    lengths (one per sequence, host values) are given."""
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if lengths is None:
+        return int(load().kvc_decode_splits(ctypes.byref(c), n_q_heads))
+    lens = [int(x) for x in lengths]
+    if len(lens) != c.batch:
+        raise ValueError("one length per sequence")
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    return int(load().kvc_decode_splits_for_lengths(ctypes.byref(c), n_q_heads, arr))
 
 
 def decode_attn(k_cache, v_cache, seq_lens, q, out, workspace, n_pending: int = 1, scale=None,

@@ -2,6 +2,12 @@
 // C-ABI calls (kvc_cache_bytes, kvc_status_str). No device code.
 #include <stdint.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <utility>
+#include <vector>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -167,6 +173,99 @@ int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads) {
   return static_cast<int32_t>(s);
 }
 
+// Workgroups of the decode kernel each CU holds at once: the kernels' launch
+// bounds (decode_min_wgs in the kernel source) in host form.
+static int resident_wgs(int32_t dtype, int32_t head_dim, int gb) {
+  const int s = elem_bytes(dtype);
+  if (s == 2 && head_dim % 32 == 0) return (gb > 4 || head_dim > 128) ? 1 : 2;   // matrix-core path
+  return (s == 2 && gb <= 4) ? 4 : 1;
+}
+
+// Modelled duration (microseconds) of one decode launch with S splits over
+// sequences of lens[b] tokens. Each of the chip's CUs streams HBM at an equal
+// share of the measured streaming rate, shared equally by the workgroups
+// resident on it (at most per_cu); workgroups are handed out in launch order
+// to whichever CU frees a slot first; a workgroup costs a fixed start-up time
+// on top of its bytes; a launch with S > 1 splits ends with the split merge.
+static double model_launch_us(const int32_t* lens, int32_t batch, int32_t n_kv, int hblk, double row_bytes,
+                              int per_cu, int32_t S) {
+  constexpr int kCus = 256;                    // MI355X compute units
+  constexpr double kCuBytesPerUs = 5.7e6 / kCus;   // 5.7 TB/s measured streaming rate, per CU
+  constexpr double kStartUs = 1.0;             // per workgroup: arguments, lengths, first loads
+  const double merge_us = S == 1 ? 0.0 : 2.5 + 0.5 * (S - 2);
+  std::vector<double> work;
+  work.reserve(static_cast<size_t>(batch) * n_kv * S * hblk);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = lens[b] < 0 ? 0 : lens[b];
+    const int64_t chunk = ((n + S - 1) / S + 15) / 16 * 16;
+    for (int32_t g = 0; g < n_kv; ++g)
+      for (int32_t sp = 0; sp < S; ++sp) {
+        const int64_t t0 = sp * chunk;
+        const int64_t rows = t0 >= n ? 0 : std::min<int64_t>(n, t0 + chunk) - t0;
+        for (int h = 0; h < hblk; ++h) work.push_back(kStartUs + rows * row_bytes / kCuBytesPerUs);
+      }
+  }
+  // process sharing on each CU, driven by the earliest completion
+  constexpr int kMaxResident = 4;
+  double rem[kCus][kMaxResident];
+  int cnt[kCus];
+  double last[kCus];
+  size_t next = 0;
+  for (int c = 0; c < kCus; ++c) {
+    cnt[c] = 0;
+    last[c] = 0.0;
+  }
+  for (int slot = 0; slot < per_cu; ++slot)
+    for (int c = 0; c < kCus && next < work.size(); ++c) rem[c][cnt[c]++] = work[next++];
+  typedef std::pair<double, int> Ev;
+  std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> heap;
+  auto done_at = [&](int c) {
+    double m = rem[c][0];
+    for (int i = 1; i < cnt[c]; ++i) m = std::min(m, rem[c][i]);
+    return last[c] + m * cnt[c];
+  };
+  for (int c = 0; c < kCus; ++c)
+    if (cnt[c] > 0) heap.push(Ev(done_at(c), c));
+  double t_end = 0.0;
+  while (!heap.empty()) {
+    const Ev ev = heap.top();
+    heap.pop();
+    const int c = ev.second;
+    const double dt = (ev.first - last[c]) / cnt[c];
+    int k = 0;
+    for (int i = 0; i < cnt[c]; ++i)
+      if (rem[c][i] - dt > 1e-9) rem[c][k++] = rem[c][i] - dt;
+    cnt[c] = k;
+    last[c] = ev.first;
+    t_end = std::max(t_end, ev.first);
+    while (cnt[c] < per_cu && next < work.size()) rem[c][cnt[c]++] = work[next++];
+    if (cnt[c] > 0) heap.push(Ev(done_at(c), c));
+  }
+  return t_end + merge_us;
+}
+
+int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_t* lens) {
+  const int32_t group = n_q_heads / c->n_kv_heads;
+  const int gb = heads_per_block(group);
+  const int per_cu = std::min(resident_wgs(c->dtype, c->head_dim, gb), 4);
+  const double row_bytes = 2.0 * c->head_dim * elem_bytes(c->dtype);   // K and V of one token
+  int32_t cap = c->max_len / 256;            // chunks of 256 tokens at least, as the default rule
+  if (cap < 1) cap = 1;
+  if (cap > 32) cap = 32;
+  int32_t best = 1;
+  double best_us = 0.0;
+  static const int32_t kCandidates[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32};
+  for (int32_t S : kCandidates) {
+    if (S > cap) break;
+    const double t = model_launch_us(lens, c->batch, c->n_kv_heads, head_blocks(group), row_bytes, per_cu, S);
+    if (S == 1 || t < best_us) {
+      best = S;
+      best_us = t;
+    }
+  }
+  return best;
+}
+
 static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 static size_t sync_units(const kvc_cache_t* c, int32_t n_q_heads) {
@@ -252,6 +351,13 @@ extern "C" size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return 0;
   if (t_q <= 0 || static_cast<int64_t>(n_q_heads) * t_q > (1 << 24)) return 0;
   return kvc_decode_workspace_bytes(cache, n_q_heads * t_q, n_splits);
+}
+
+extern "C" int32_t kvc_decode_splits_for_lengths(const kvc_cache_t* cache, int32_t n_q_heads,
+                                                 const int32_t* h_lens) {
+  if (kvc::check_cache(cache, false) != KVC_OK || cache->batch <= 0 || h_lens == nullptr) return 0;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return 0;
+  return kvc::splits_for_lengths(cache, n_q_heads, h_lens);
 }
 
 extern "C" int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads) {

@@ -33,6 +33,9 @@ int head_blocks(int32_t group);
 
 // Sequence splits per (sequence, KV head, head block) when the caller passes 0.
 int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads);
+// Splits chosen from the sequences' lengths (host array of c->batch values)
+// by modelling the launch; see kvc_decode_splits_for_lengths.
+int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_t* lens);
 
 // Workspace: uint32 tickets [B * H_kv * head_blocks], then uint32 ready
 // flags [B * H_kv * head_blocks, S] (both zero between calls), then fp32

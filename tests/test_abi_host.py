@@ -324,3 +324,30 @@ def test_quant_validation_and_workspace():
                                                   None, None)
     assert step(n_q=3) == 5
     assert step(ws=need - 1) == 6
+
+
+def test_splits_for_lengths_model_choices():
+    """The length-aware split choice on the bench workloads' geometries: the
+    counts measured fastest on MI355X for the uniform batches (equal to the
+    length-blind rule), and several splits for the ragged batch, whose
+    one-split launch leaves a long tail (measured 5.2 -> 5.7 TB/s)."""
+    import synth
+    kvc, lib = _lib()
+
+    def pick(b, h, t, d, dt, nq, lens):
+        c = _desc(kvc, batch=b, n_kv_heads=h, max_len=t, head_dim=d, dtype=dt, stride_t=d, stride_h=t * d,
+                  stride_b=h * t * d)
+        arr = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
+        return lib.kvc_decode_splits_for_lengths(ctypes.byref(c), nq, arr), lib.kvc_decode_splits(ctypes.byref(c), nq)
+
+    assert pick(16, 8, 2100, 128, kvc.KVC_BF16, 32, [2049] * 16) == (2, 2)
+    assert pick(1, 32, 4130, 128, kvc.KVC_F16, 32, [4097]) == (8, 8)
+    assert pick(32, 8, 8300, 128, kvc.KVC_BF16, 64, [8193] * 32) == (1, 1)
+    assert pick(32, 1, 8300, 128, kvc.KVC_BF16, 64, [8193] * 32) == (1, 1)
+    ragged = synth.CONFIGS["ragged_long"].lengths(7).numpy() + 1
+    got, default = pick(24, 32, 6100, 128, kvc.KVC_F16, 32, ragged)
+    assert default == 1 and 2 <= got <= 8
+    c = _desc(kvc)
+    arr = (ctypes.c_int32 * 8)(*([100] * 8))
+    assert lib.kvc_decode_splits_for_lengths(ctypes.byref(c), 3, arr) == 0       # not a GQA multiple
+    assert lib.kvc_decode_splits_for_lengths(ctypes.byref(c), 4, None) == 0
