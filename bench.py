@@ -171,8 +171,9 @@ class Workload:
         self.seq_lens = self.lengths.to(dev)
         logical = kvc.CacheDesc(self.kc.data_ptr(), self.vc.data_ptr(), B, Hkv, T, D, kvc.DTYPE_CODE[tdt], 0,
                                 Hkv * T * D, T * D, D)
-        self.splits = splits if splits > 0 else kvc.decode_splits(None, None, Hq, lengths=self._attended_at_start(),
-                                                                  desc=logical)
+        # the length-blind rule: the launch model behind the length-aware
+        # choice is calibrated on the 16-bit kernels only
+        self.splits = splits if splits > 0 else kvc.decode_splits(None, None, Hq, desc=logical)
         self.ws = kvc.quant_workspace(self.descs[0], Hq, self.splits)
         self.scale = ctypes.c_float(1.0 / math.sqrt(D))
         torch.cuda.synchronize()

@@ -165,7 +165,8 @@ int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads);
  * start-up cost per workgroup and a merge cost per extra split -- for split
  * counts from 1 up to min(32, max_len / 256) and returns the fastest. Uneven
  * lengths (a ragged batch) get more, shorter splits than kvc_decode_splits
- * gives, so that no CU is left with a long tail. Host only, a few
+ * gives, so that no CU is left with a long tail. The model is calibrated on
+ * the (bandwidth-bound) 16-bit decode kernels. Host only, a few
  * milliseconds for a few thousand (sequence, KV head) pairs; 0 for invalid
  * arguments. Pass the result as n_splits (and size the workspace for it).
  */
@@ -441,7 +442,9 @@ kvc_status_t kvc_quant_prefill_fill(const kvc_qcache_t* cache, const int32_t* se
  * contiguous decode's.
  *
  * kvc_quant_decode_step -- kvc_quant_append then kvc_quant_decode_attn with
- * n_pending = 1, enqueued as those two launches.
+ * n_pending = 1, in one launch: the workgroup that attends slot seq_lens[b]
+ * quantises the new row itself, folds it in and writes its codes and scale.
+ * Codes, scales and output equal those of the two calls bit for bit.
  */
 size_t kvc_quant_decode_workspace_bytes(const kvc_qcache_t* cache, int32_t n_q_heads, int32_t n_splits);
 kvc_status_t kvc_quant_decode_attn(const kvc_qcache_t* cache, const int32_t* seq_lens, int32_t n_pending,

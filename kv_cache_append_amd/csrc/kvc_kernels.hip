@@ -331,8 +331,8 @@ struct DecodeParams {
   int32_t ring;
   // Quantised cache (8-bit codes): fp32 scales per token of K and of V,
   // [B, H_kv, T_max] with byte strides ssb, ssh and 4 bytes per token.
-  const char* k_scale;
-  const char* v_scale;
+  char* k_scale;                 // written only by the fused append
+  char* v_scale;
   int64_t ssb, ssh;
   float scale_log2;            // softmax scale * log2(e)
 };
@@ -511,6 +511,81 @@ __device__ inline void codes8_f32(const u32x2 r, float* f) {
   }
 }
 
+// fp32 -> OCP E4M3 byte: round to nearest even, saturate at +-448, NaN -> 0x7F.
+__device__ inline uint32_t e4m3_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t au = u & 0x7fffffffu;
+  if (au > 0x7f800000u) return 0x7Fu;                  // NaN
+  const float a = __uint_as_float(au);
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                                 // below 2^-6: multiples of 2^-9
+    // a * 512 is exact; rint rounds ties to even; 8 is the code of 2^-6
+    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.f));
+  }
+  uint32_t e = (au >> 23) - 120u;                      // biased E4M3 exponent (bias 7), 1..15
+  const uint32_t mant = au & 0x7fffffu;
+  uint32_t m = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, ties to even; 8 carries
+  if (m == 8u) {
+    e += 1u;
+    m = 0u;
+  }
+  const uint32_t code = (e << 3) | m;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+template <typename IT>
+__device__ inline float load_elem(const char* row, int i) {
+  if constexpr (IT::kBytes == 4) return reinterpret_cast<const float*>(row)[i];
+  else if constexpr (IT::kIsF16) return static_cast<float>(reinterpret_cast<const _Float16*>(row)[i]);
+  else return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
+}
+
+// Quantise one row of D values held by a wave (lane l: elements
+// [l*E, l*E + E), E = D/64) as the format defines: amax by a wave-wide
+// maximum, scale = amax / QMAX and each code from x / scale, both fp32
+// divisions (correctly rounded). Returns the scale (0 for a row of zeros) and
+// the lane's E code bytes packed little-endian. Every lane of the wave must
+// take part.
+template <typename IT, int KQ, int D>
+__device__ inline float quant_row(const char* src, int lane, uint32_t& packed) {
+  constexpr int E = D / 64;
+  constexpr float kQmax = KQ == kQuantFp8 ? 448.f : 127.f;
+  float x[E];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = load_elem<IT>(src, lane * E + e);
+    amax = fmaxf(amax, fabsf(x[e]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / kQmax;
+  packed = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t c = 0u;
+    if (amax > 0.f) {
+      const float y = x[e] / scale;
+      if constexpr (KQ == kQuantFp8) {
+        c = e4m3_from_f32(y);
+      } else {
+        c = static_cast<uint32_t>(static_cast<int32_t>(fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f))) & 0xffu;
+      }
+    }
+    packed |= c << (8 * e);
+  }
+  return amax > 0.f ? scale : 0.f;
+}
+
+// E code bytes of one lane, little-endian, to dst.
+template <int E>
+__device__ inline void store_codes(char* dst, uint32_t packed) {
+  if constexpr (E == 1) *reinterpret_cast<uint8_t*>(dst) = static_cast<uint8_t>(packed);
+  else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+  else *reinterpret_cast<uint32_t*>(dst) = packed;
+}
+
 // Tuning constants (measured on MI355X): waves per decode workgroup, row
 // passes per register tile, and tiles of loads kept in flight ahead of the
 // one being computed.
@@ -583,6 +658,9 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   __shared__ float sm_ml[NW][GB][2];
   __shared__ float sm_p[kMfma ? NW : 1][16][4 * NQ];   // softmax weights, score layout -> V layout
   __shared__ uint32_t sm_ticket;
+  // 8-bit caches, fused append: the new row's K and V codes, staged so that
+  // they can be read in the score layout (K) and the row layout (V)
+  __shared__ __align__(16) uint8_t sm_x[kQuant ? 2 : 1][kQuant ? D : 16];
 
   // Workgroup ids go round-robin over the 8 XCDs (id mod 8). The head blocks
   // of one (unit, split) item read the same K/V rows, so they take ids 8
@@ -670,8 +748,10 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
     }
     if (ksrc != nullptr) {
       if constexpr (kQuant) {                  // 8 code bytes of V (K is loaded in the MFMA layout)
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc);
-        nv = u32x4{w[0], w[1], 0u, 0u};
+        if (!x_new) {                          // (a new row is quantised below)
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc);
+          nv = u32x4{w[0], w[1], 0u, 0u};
+        }
       } else {
         nk = *reinterpret_cast<const u32x4*>(ksrc);
         nv = *reinterpret_cast<const u32x4*>(vsrc);
@@ -681,9 +761,37 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   float xks = 0.f, xvs = 0.f;                   // scales of the folded row (8-bit caches)
   if constexpr (kQuant) {
     if (has_x && wave == 0) {
-      const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(xrow) * 4;
-      xks = *reinterpret_cast<const float*>(p.k_scale + so);
-      xvs = *reinterpret_cast<const float*>(p.v_scale + so);
+      if (x_new) {
+        // The step's new row, quantised as kvc_quant_append does (the same
+        // device function), so the fused step matches append + decode bit
+        // for bit; its codes go through LDS to the K and V layouts.
+        const int64_t noff = b * p.nsb + g * p.nsh;
+        uint32_t xkc, xvc;                     // this lane's code bytes of the new row
+        xks = quant_row<ET, KQ, D>(p.k_new + noff, lane, xkc);
+        xvs = quant_row<ET, KQ, D>(p.v_new + noff, lane, xvc);
+        store_codes<D / 64>(reinterpret_cast<char*>(&sm_x[0][lane * (D / 64)]), xkc);
+        store_codes<D / 64>(reinterpret_cast<char*>(&sm_x[1][lane * (D / 64)]), xvc);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        const u32x2 w = *reinterpret_cast<const u32x2*>(&sm_x[1][li * VSL]);
+        nv = u32x4{w[0], w[1], 0u, 0u};
+        // the first head block also writes the row into the cache: no
+        // workgroup of this launch reads that slot from memory
+        if (hb == 0) {
+          const int64_t ao = slot_offset(p, b, g, arow);
+          store_codes<D / 64>(p.k + ao + lane * (D / 64), xkc);
+          store_codes<D / 64>(p.v + ao + lane * (D / 64), xvc);
+          if (lane == 0) {
+            const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(arow) * 4;
+            *reinterpret_cast<float*>(p.k_scale + so) = xks;
+            *reinterpret_cast<float*>(p.v_scale + so) = xvs;
+          }
+        }
+      } else {
+        const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(xrow) * 4;
+        xks = *reinterpret_cast<const float*>(p.k_scale + so);
+        xvs = *reinterpret_cast<const float*>(p.v_scale + so);
+      }
     }
   }
 
@@ -945,7 +1053,11 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
 #pragma unroll
       for (int m = 0; m < NKL; ++m) {
         K[m] = u32x4{0u, 0u, 0u, 0u};
-        if (r16 == 0 && kx != nullptr) K[m] = *reinterpret_cast<const u32x4*>(kx + (4 * m + kq) * 16);
+        if (kQuant && x_new) {
+          if (r16 == 0) K[m] = *reinterpret_cast<const u32x4*>(&sm_x[0][(4 * m + kq) * 16]);
+        } else if (r16 == 0 && kx != nullptr) {
+          K[m] = *reinterpret_cast<const u32x4*>(kx + (4 * m + kq) * 16);
+        }
       }
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
@@ -1434,36 +1546,6 @@ struct QuantParams {
   int32_t batch, n_kv, max_len, t_new;
 };
 
-// fp32 -> OCP E4M3 byte: round to nearest even, saturate at +-448, NaN -> 0x7F.
-__device__ inline uint32_t e4m3_from_f32(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t au = u & 0x7fffffffu;
-  if (au > 0x7f800000u) return 0x7Fu;                  // NaN
-  const float a = __uint_as_float(au);
-  if (a >= 448.f) return sign | 0x7Eu;
-  if (a < 0.015625f) {                                 // below 2^-6: multiples of 2^-9
-    // a * 512 is exact; rint rounds ties to even; 8 is the code of 2^-6
-    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.f));
-  }
-  uint32_t e = (au >> 23) - 120u;                      // biased E4M3 exponent (bias 7), 1..15
-  const uint32_t mant = au & 0x7fffffu;
-  uint32_t m = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, ties to even; 8 carries
-  if (m == 8u) {
-    e += 1u;
-    m = 0u;
-  }
-  const uint32_t code = (e << 3) | m;
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
-template <typename IT>
-__device__ inline float load_elem(const char* row, int i) {
-  if constexpr (IT::kBytes == 4) return reinterpret_cast<const float*>(row)[i];
-  else if constexpr (IT::kIsF16) return static_cast<float>(reinterpret_cast<const _Float16*>(row)[i]);
-  else return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
-}
-
 // One wave per new row (K rows, then V rows): lane l holds elements
 // [l*E, l*E + E). amax over the row by a wave-wide maximum, scale = amax /
 // QMAX and each code from x / scale, both fp32 divisions (correctly rounded),
@@ -1471,7 +1553,6 @@ __device__ inline float load_elem(const char* row, int i) {
 template <typename IT, int KQ, int D>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const QuantParams p) {
   constexpr int E = D / 64;
-  constexpr float kQmax = KQ == kQuantFp8 ? 448.f : 127.f;
   const int lane = threadIdx.x & 63;
   const int64_t rows = static_cast<int64_t>(p.batch) * p.n_kv * p.t_new;
   const int64_t n_waves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
@@ -1489,38 +1570,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const QuantParams p) {
       continue;
     }
     const char* src = (is_v ? p.src_v : p.src_k) + b * p.sb + g * p.sh + static_cast<int64_t>(i) * p.st;
-    float x[E];
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      x[e] = load_elem<IT>(src, lane * E + e);
-      amax = fmaxf(amax, fabsf(x[e]));
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const float scale = amax / kQmax;
-    uint32_t packed = 0u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      uint32_t c = 0u;
-      if (amax > 0.f) {
-        const float y = x[e] / scale;
-        if constexpr (KQ == kQuantFp8) {
-          c = e4m3_from_f32(y);
-        } else {
-          c = static_cast<uint32_t>(static_cast<int32_t>(fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f))) & 0xffu;
-        }
-      }
-      packed |= c << (8 * e);
-    }
+    uint32_t packed;
+    const float scale = quant_row<IT, KQ, D>(src, lane, packed);
     const int slot = pos + i;
-    char* dst = (is_v ? p.vc : p.kc) + b * p.cb + g * p.ch + static_cast<int64_t>(slot) * p.ct + lane * E;
-    if constexpr (E == 1) *reinterpret_cast<uint8_t*>(dst) = static_cast<uint8_t>(packed);
-    else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
-    else *reinterpret_cast<uint32_t*>(dst) = packed;
+    store_codes<E>((is_v ? p.vc : p.kc) + b * p.cb + g * p.ch + static_cast<int64_t>(slot) * p.ct + lane * E, packed);
     if (lane == 0)
-      *reinterpret_cast<float*>((is_v ? p.vs : p.ks) + b * p.ssb + g * p.ssh + static_cast<int64_t>(slot) * 4) =
-          amax > 0.f ? scale : 0.f;
+      *reinterpret_cast<float*>((is_v ? p.vs : p.ks) + b * p.ssb + g * p.ssh + static_cast<int64_t>(slot) * 4) = scale;
   }
 }
 
@@ -1589,10 +1644,13 @@ kvc_status_t launch_quant_rows(const kvc_qcache_t* c, const int32_t* seq_lens, c
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+// k_new != nullptr: the fused step (the new rows quantised into slot
+// seq_lens[b] by the workgroup that attends them; n_pending must be 1).
 kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens, int32_t n_pending, const void* q,
                                  int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
                                  size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                                 int64_t new_stride_b = 0, int64_t new_stride_h = 0) {
   kvc_status_t rc = kvc::check_qcache(c, true);
   if (rc != KVC_OK) return rc;
   if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return KVC_ERR_GQA;
@@ -1605,6 +1663,13 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
   if (reinterpret_cast<uintptr_t>(q) % 16) return KVC_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(out) % kvc::elem_bytes(out_dtype)) return KVC_ERR_ALIGN;
   if ((static_cast<int64_t>(c->max_len) + 2048) * c->stride_t > 0x7fffffffll) return KVC_ERR_SHAPE;
+  const int s_in = kvc::elem_bytes(c->in_dtype);
+  if (k_new != nullptr) {
+    if (v_new == nullptr) return KVC_ERR_NULL;
+    if (new_stride_b < 0 || new_stride_h < 0) return KVC_ERR_SHAPE;
+    if (c->n_kv_heads > 1 && new_stride_h < c->head_dim) return KVC_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(k_new) % s_in || reinterpret_cast<uintptr_t>(v_new) % s_in) return KVC_ERR_ALIGN;
+  }
   const kvc_cache_t view = kvc::qcache_view(c);
   const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads);
   const size_t need = kvc::workspace_bytes(&view, n_q_heads, splits);
@@ -1622,8 +1687,10 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
   p.st = c->stride_t;
   p.seq_lens = seq_lens;
   p.q = static_cast<const char*>(q);
-  p.k_new = nullptr;
-  p.v_new = nullptr;
+  p.k_new = static_cast<const char*>(k_new);
+  p.v_new = static_cast<const char*>(v_new);
+  p.nsb = new_stride_b * s_in;
+  p.nsh = new_stride_h * s_in;
   char* ws = static_cast<char*>(workspace);
   p.ws_cnt = reinterpret_cast<uint32_t*>(ws);
   p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(&view, n_q_heads, splits));
@@ -1644,8 +1711,8 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
   p.block = 0;
   p.table = nullptr;
   p.ring = 0;
-  p.k_scale = reinterpret_cast<const char*>(c->k_scale);
-  p.v_scale = reinterpret_cast<const char*>(c->v_scale);
+  p.k_scale = reinterpret_cast<char*>(c->k_scale);
+  p.v_scale = reinterpret_cast<char*>(c->v_scale);
   p.ssb = c->scale_stride_b * 4;
   p.ssh = c->scale_stride_h * 4;
   p.scale_log2 = scale_log2;
@@ -2020,30 +2087,7 @@ extern "C" kvc_status_t kvc_quant_decode_step(const kvc_qcache_t* cache, const i
                                               const void* q, int32_t n_q_heads, float scale, void* out,
                                               int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                               int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
-  // validate the attention arguments before enqueueing the append, so a
-  // host-detectable error leaves nothing enqueued
-  kvc_status_t rc = kvc::check_qcache(cache, true);
-  if (rc != KVC_OK) return rc;
-  if (cache->batch > 0) {
-    if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
-    if (n_splits < 0 || n_splits > KVC_MAX_SPLITS) return KVC_ERR_SHAPE;
-    if (out_dtype != KVC_F32 && out_dtype != cache->in_dtype) return KVC_ERR_DTYPE;
-    if (!(scale > 0.f) || !(scale * 1.44269504088896340736f < INFINITY)) return KVC_ERR_UNSUPPORTED;
-    if (seq_lens == nullptr || q == nullptr || out == nullptr || k_new == nullptr || v_new == nullptr)
-      return KVC_ERR_NULL;
-    if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
-    if (reinterpret_cast<uintptr_t>(out) % kvc::elem_bytes(out_dtype)) return KVC_ERR_ALIGN;
-    if ((static_cast<int64_t>(cache->max_len) + 2048) * cache->stride_t > 0x7fffffffll) return KVC_ERR_SHAPE;
-    const kvc_cache_t view = kvc::qcache_view(cache);
-    const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads);
-    if (workspace == nullptr || workspace_bytes < kvc::workspace_bytes(&view, n_q_heads, splits))
-      return KVC_ERR_WORKSPACE;
-    if (pick_quant_kernel(cache->format, cache->in_dtype, cache->head_dim,
-                          kvc::heads_per_block(n_q_heads / cache->n_kv_heads)) == nullptr)
-      return KVC_ERR_UNSUPPORTED;
-  }
-  rc = launch_quant_rows(cache, seq_lens, k_new, v_new, new_stride_b, new_stride_h, 0, 1, dev_status, stream);
-  if (rc != KVC_OK) return rc;
+  if (cache != nullptr && cache->batch > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_NULL;
   return launch_quant_decode(cache, seq_lens, 1, q, n_q_heads, scale, out, out_dtype, workspace, workspace_bytes,
-                             n_splits, dev_status, stream);
+                             n_splits, dev_status, stream, k_new, v_new, new_stride_b, new_stride_h);
 }
