@@ -49,6 +49,9 @@ def _parse():
     ap.add_argument("--quant", choices=["fp8", "int8"], default=None,
                     help="time the decode step on a quantised cache (8-bit codes + per-token fp32 scales; "
                          "kvc_quant_decode_step) instead of the 16-bit cache")
+    ap.add_argument("--layout", choices=["bhtd", "bthd"], default="bhtd",
+                    help="cache storage order: [B, H_kv, T, D] (head-major) or [B, T, H_kv, D] (token-major, "
+                         "viewed as [B, H_kv, T, D] through strides)")
     ap.add_argument("--block-q", type=int, default=0,
                     help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
                          "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
@@ -60,6 +63,8 @@ def _parse():
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--calib-copy-mib run into HBM bytes per decode launch, written to --pmc-out")
     ap.add_argument("--pmc-out", default=None, help="output JSON of --pmc-summary")
+    ap.add_argument("--stream-gib", type=int, default=4,
+                    help="GiB read by the streaming-read calibration (kvc_stream_read); 0 skips it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a known-size reference "
                          "for HBM byte counters in a profiled run)")
@@ -71,7 +76,7 @@ class Workload:
     C-ABI arguments (so the timed loop does no Python-side tensor work)."""
 
     def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0, page: int = 0,
-                 ring: int = 0, quant=None):
+                 ring: int = 0, quant=None, layout: str = "bhtd"):
         import torch
         import kv_cache_append_amd as kvc
         import synth
@@ -101,6 +106,8 @@ class Workload:
             perm = torch.randperm(n_pages, generator=g).to(torch.int32)
             self.table = perm.reshape(B, per_seq).to(dev)
             self.k = torch.empty((L, n_pages, Hkv, page, D), dtype=tdt, device=dev)
+        elif layout == "bthd":   # token-major storage, the heads of a token adjacent
+            self.k = torch.empty((L, B, self.t_max, Hkv, D), dtype=tdt, device=dev).transpose(2, 3)
         else:
             self.k = torch.empty((L, B, Hkv, self.t_max, D), dtype=tdt, device=dev)
         self.v = torch.empty_like(self.k)
@@ -282,17 +289,20 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     w.reset_lengths()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(steps):
+    for i in range(steps):
         if graph is not None:
             graph.replay()
         else:
             w.step(stream.cuda_stream)
+        marks[i].record()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = e0.elapsed_time(e1)
+    step_ms = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, steps)]
     # Average duration of one decode launch: the L per-layer launches alone
     # (lengths held, so every launch reads the same bytes), `reps` passes back
     # to back, bracketed by HIP events on the launching stream.
@@ -319,7 +329,7 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     torch.cuda.synchronize()
     avg_launch_ms = e0.elapsed_time(e1) / (reps * w.cfg.n_layers)
     avg_launch_bytes = w.decode_launch_bytes(0)
-    return ms_total, wall, avg_launch_ms, avg_launch_bytes
+    return ms_total, wall, avg_launch_ms, avg_launch_bytes, step_ms
 
 
 def _kernel_fingerprint() -> str:
@@ -442,8 +452,11 @@ def _run_config(name, args, with_cpu):
     margin = (max(args.steps, args.warmup) + 2) * nq
     if sum(bool(x) for x in (args.ring, args.block_q, args.paged, args.quant)) > 1:
         raise SystemExit("--ring, --block-q, --paged and --quant are separate modes")
-    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring, args.quant)
-    ms_total, wall, launch_ms, launch_bytes = _measure(w, args.steps, args.warmup, not args.no_graph)
+    if args.layout != "bhtd" and (args.paged or args.quant):
+        raise SystemExit("--layout applies to contiguous 16-bit caches")
+    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring, args.quant, args.layout)
+    ms_total, wall, launch_ms, launch_bytes, step_ms = _measure(w, args.steps, args.warmup, not args.no_graph)
+    step_sorted = sorted(step_ms)
     kv = w.kv_bytes(args.steps)
     gbs = kv / (ms_total / 1e3) / 1e9
     achieved = launch_bytes / (launch_ms / 1e3) / 1e9
@@ -451,6 +464,10 @@ def _run_config(name, args, with_cpu):
     res = {
         "value": round(gbs, 2),
         "ms_per_step": round(ms_total / args.steps, 5),
+        # each step's own time (HIP events between steps); steps later in the
+        # run attend slightly more tokens
+        "step_ms": {"median": round(step_sorted[len(step_sorted) // 2], 5), "min": round(step_sorted[0], 5),
+                    "max": round(step_sorted[-1], 5)},
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "steps_per_s": round(args.steps / (ms_total / 1e3), 2),
@@ -466,6 +483,7 @@ def _run_config(name, args, with_cpu):
             **({"query_block": args.block_q} if args.block_q else {}),
             **({"page_size": args.paged} if args.paged else {}),
             **({"window": args.ring} if args.ring else {}),
+            **({"layout": args.layout} if args.layout != "bhtd" else {}),
             **({"kv_format": args.quant, "kv_bytes_per_token_head": cfg.head_dim + 4} if args.quant else {}),
         },
         "roofline": {
@@ -480,6 +498,8 @@ def _run_config(name, args, with_cpu):
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),
+            **({"stream_read_gbs": round(args.stream_gbs, 1), "frac_of_stream": round(achieved / args.stream_gbs, 4)}
+               if args.stream_gbs else {}),
             # counters are taken for the default mode (16-bit contiguous cache)
             "traffic": None if (args.block_q or args.paged or args.ring or args.quant) else _traffic(name),
         },
@@ -512,6 +532,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # the chip's streaming-read rate with the decode kernel's loads, over 4 GiB
+    # (far past the on-chip caches): the achievable ceiling beside the 8 TB/s peak
+    args.stream_gbs = None
+    if args.stream_gib > 0:
+        import kv_cache_append_amd as kvc
+        args.stream_gbs = kvc.stream_read_rate(n_bytes=args.stream_gib << 30)
+        torch.cuda.empty_cache()
     main_res = _run_config(args.config, args, with_cpu=not args.no_cpu_baseline)
     line = {
         "metric": METRIC,
@@ -521,6 +548,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": main_res["ms_per_step"],
+        "step_ms": main_res["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -538,7 +566,7 @@ def main():
         line["cpu_baseline"] = main_res["cpu_baseline"]
     if args.secondary and args.secondary != "none":
         sec = _run_config(args.secondary, args, with_cpu=False)
-        line["secondary"] = {k: sec[k] for k in ("value", "ms_per_step", "pct_of_peak", "steps_per_s",
+        line["secondary"] = {k: sec[k] for k in ("value", "ms_per_step", "step_ms", "pct_of_peak", "steps_per_s",
                                                    "tokens_per_s", "kv_bytes_per_step", "dtype", "config",
                                                    "roofline")}
     print(json.dumps(line), flush=True)

@@ -474,6 +474,20 @@ kvc_status_t kvc_seq_lens_advance(int32_t* seq_lens, int32_t batch, int32_t n, h
 uint64_t kvc_cache_bytes(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
                          const int32_t* h_lens, int32_t batch);
 
+/*
+ * kvc_stream_read -- a measurement aid, not part of the decode path: reads
+ * every byte of buf (device, 16-byte aligned, bytes a multiple of 16) once
+ * with the 16-byte buffer loads the decode kernel uses, from n_workgroups
+ * workgroups of 256 threads, and stores one XOR fold per thread into sink
+ * (device, kvc_stream_read_sink_bytes(n_workgroups) bytes) so no load is
+ * dropped. Timed over a buffer far larger than the caches on the chip, it
+ * gives the streaming-read rate that bounds any kernel streaming the same
+ * bytes (textbook "11.7 KV Cache" §4.4: decode sits on the bandwidth roof).
+ */
+size_t kvc_stream_read_sink_bytes(int32_t n_workgroups);
+kvc_status_t kvc_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
+                             hipStream_t stream);
+
 /* kvc_status_str -- static, human-readable name of a status code. */
 const char* kvc_status_str(kvc_status_t status);
 

@@ -40,7 +40,8 @@ EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_
            "kvc_ring_append", "kvc_ring_prefill_fill", "kvc_ring_decode_attn", "kvc_ring_decode_step",
            "kvc_quant_append", "kvc_quant_prefill_fill", "kvc_quant_decode_workspace_bytes",
            "kvc_quant_decode_attn", "kvc_quant_decode_step",
-           "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str")
+           "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str", "kvc_stream_read_sink_bytes",
+           "kvc_stream_read")
 
 
 class KvcError(RuntimeError):
@@ -121,6 +122,10 @@ def load() -> ctypes.CDLL:
     lib.kvc_quant_decode_attn.restype = i32
     lib.kvc_quant_decode_step.argtypes = [qp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_quant_decode_step.restype = i32
+    lib.kvc_stream_read_sink_bytes.argtypes = [i32]
+    lib.kvc_stream_read_sink_bytes.restype = sz
+    lib.kvc_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.kvc_stream_read.restype = i32
     lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
     lib.kvc_seq_lens_advance.restype = i32
     lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
@@ -499,3 +504,27 @@ def quant_decode_step(qc: QCacheDesc, seq_lens, k_new, v_new, q, out, workspace,
                                         _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
                                         _stream(stream)), "kvc_quant_decode_step")
+
+
+def stream_read_rate(n_bytes: int = 4 << 30, grids=(512, 2048, 8192), reps: int = 5, device="cuda") -> float:
+    """Best streaming-read rate in GB/s of kvc_stream_read over an n_bytes
+    device buffer across the given grid sizes (per grid: one warm-up launch,
+    then `reps` launches timed with HIP events on the launching stream)."""
+    lib = load()
+    buf = torch.empty(n_bytes, dtype=torch.uint8, device=device)
+    sink = torch.empty(int(lib.kvc_stream_read_sink_bytes(max(grids))), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for n_wg in grids:
+        run = lambda: _check(lib.kvc_stream_read(_ptr(buf), n_bytes, _ptr(sink), n_wg, _stream(stream)),
+                             "kvc_stream_read")
+        run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, n_bytes / (e0.elapsed_time(e1) / reps / 1e3) / 1e9)
+    del buf, sink
+    return best
