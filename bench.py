@@ -52,6 +52,9 @@ def _parse():
     ap.add_argument("--layout", choices=["bhtd", "bthd"], default="bhtd",
                     help="cache storage order: [B, H_kv, T, D] (head-major) or [B, T, H_kv, D] (token-major, "
                          "viewed as [B, H_kv, T, D] through strides)")
+    ap.add_argument("--page-order", choices=["random", "interleaved"], default="random",
+                    help="paged caches: pages handed out in a random order, or interleaved by position "
+                         "(page p of every sequence adjacent, as sequences growing together receive them)")
     ap.add_argument("--block-q", type=int, default=0,
                     help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
                          "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
@@ -76,7 +79,7 @@ class Workload:
     C-ABI arguments (so the timed loop does no Python-side tensor work)."""
 
     def __init__(self, cfg, margin_tokens: int, seed: int, splits: int, block_q: int = 0, page: int = 0,
-                 ring: int = 0, quant=None, layout: str = "bhtd"):
+                 ring: int = 0, quant=None, layout: str = "bhtd", page_order: str = "random"):
         import torch
         import kv_cache_append_amd as kvc
         import synth
@@ -103,7 +106,10 @@ class Workload:
             self.t_max = per_seq * page
             n_pages = B * per_seq
             g = torch.Generator().manual_seed(synth.derive_seed(seed, cfg.name, "pages"))
-            perm = torch.randperm(n_pages, generator=g).to(torch.int32)
+            if page_order == "interleaved":   # page p of sequence b is pool page p * B + b
+                perm = (torch.arange(per_seq).view(1, per_seq) * B + torch.arange(B).view(B, 1)).to(torch.int32)
+            else:
+                perm = torch.randperm(n_pages, generator=g).to(torch.int32)
             self.table = perm.reshape(B, per_seq).to(dev)
             self.k = torch.empty((L, n_pages, Hkv, page, D), dtype=tdt, device=dev)
         elif layout == "bthd":   # token-major storage, the heads of a token adjacent
@@ -130,7 +136,8 @@ class Workload:
             self.descs = [kvc.cache_desc(self.k[l], self.v[l]) for l in range(L)]
         # the library's split choice for the lengths the first timed step attends
         attended = self._attended_at_start()
-        self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq * nq, lengths=attended)
+        if not page:
+            self.splits = splits if splits > 0 else kvc.decode_splits(self.k[0], self.v[0], Hq * nq, lengths=attended)
         if page:
             # the split choice of the contiguous cache with the same capacity
             logical = kvc.CacheDesc(self.k.data_ptr(), self.v.data_ptr(), B, Hkv, self.t_max, D,
@@ -454,7 +461,8 @@ def _run_config(name, args, with_cpu):
         raise SystemExit("--ring, --block-q, --paged and --quant are separate modes")
     if args.layout != "bhtd" and (args.paged or args.quant):
         raise SystemExit("--layout applies to contiguous 16-bit caches")
-    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring, args.quant, args.layout)
+    w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring, args.quant, args.layout,
+                 args.page_order)
     ms_total, wall, launch_ms, launch_bytes, step_ms = _measure(w, args.steps, args.warmup, not args.no_graph)
     step_sorted = sorted(step_ms)
     kv = w.kv_bytes(args.steps)
@@ -481,7 +489,7 @@ def _run_config(name, args, with_cpu):
                                        "sum": int(lens.long().sum())},
             "splits": w.splits, "hip_graph": not args.no_graph,
             **({"query_block": args.block_q} if args.block_q else {}),
-            **({"page_size": args.paged} if args.paged else {}),
+            **({"page_size": args.paged, "page_order": args.page_order} if args.paged else {}),
             **({"window": args.ring} if args.ring else {}),
             **({"layout": args.layout} if args.layout != "bhtd" else {}),
             **({"kv_format": args.quant, "kv_bytes_per_token_head": cfg.head_dim + 4} if args.quant else {}),
