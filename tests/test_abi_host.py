@@ -351,3 +351,15 @@ def test_splits_for_lengths_model_choices():
     arr = (ctypes.c_int32 * 8)(*([100] * 8))
     assert lib.kvc_decode_splits_for_lengths(ctypes.byref(c), 3, arr) == 0       # not a GQA multiple
     assert lib.kvc_decode_splits_for_lengths(ctypes.byref(c), 4, None) == 0
+
+
+def test_offset_bound_of_a_slice():
+    """The kernels address a (sequence, KV head) slice with 32-bit offsets:
+    (T_max + 2048) * stride_t * s must stay below 2^31. At the bound the call
+    gets as far as the workspace check; one token past it is KVC_ERR_SHAPE.
+    Neither launches (the workspace is absent)."""
+    kvc, lib = _lib()
+    top = (2**31 - 1) // 256 - 2048
+    for t_max, want in ((top, 6), (top + 1, 2)):
+        c = _desc(kvc, batch=1, n_kv_heads=1, max_len=t_max, stride_t=128, stride_h=t_max * 128, stride_b=t_max * 128)
+        assert lib.kvc_decode_attn(ctypes.byref(c), FAKE, 1, FAKE, 4, 0.1, FAKE, 0, None, 0, 0, None, None) == want
