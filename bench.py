@@ -464,6 +464,10 @@ def _run_config(name, args, with_cpu):
     w = Workload(cfg, margin, args.seed, args.splits, args.block_q, args.paged, args.ring, args.quant, args.layout,
                  args.page_order)
     ms_total, wall, launch_ms, launch_bytes, step_ms = _measure(w, args.steps, args.warmup, not args.no_graph)
+    # the same bytes per launch read by a kernel that only streams them
+    import kv_cache_append_amd as kvc
+    launch_read = (kvc.stream_read_launch_rate(int(launch_bytes) // 16 * 16, n_bytes=args.stream_gib << 30)
+                   if args.stream_gib > 0 else None)
     step_sorted = sorted(step_ms)
     kv = w.kv_bytes(args.steps)
     gbs = kv / (ms_total / 1e3) / 1e9
@@ -508,6 +512,8 @@ def _run_config(name, args, with_cpu):
             "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),
             **({"stream_read_gbs": round(args.stream_gbs, 1), "frac_of_stream": round(achieved / args.stream_gbs, 4)}
                if args.stream_gbs else {}),
+            **({"launch_read_gbs": round(launch_read, 1), "frac_of_launch_read": round(achieved / launch_read, 4)}
+               if launch_read else {}),
             # counters are taken for the default mode (16-bit contiguous cache)
             "traffic": None if (args.block_q or args.paged or args.ring or args.quant) else _traffic(name),
         },

@@ -528,3 +528,38 @@ def stream_read_rate(n_bytes: int = 4 << 30, grids=(512, 2048, 8192), reps: int 
         best = max(best, n_bytes / (e0.elapsed_time(e1) / reps / 1e3) / 1e9)
     del buf, sink
     return best
+
+
+def stream_read_launch_rate(launch_bytes: int, n_bytes: int = 4 << 30, grids=(256, 512, 1024), launches: int = 64,
+                            device="cuda") -> float:
+    """Best rate in GB/s of kvc_stream_read launches that each read
+    launch_bytes (a multiple of 16) back to back, every launch a different
+    region of an n_bytes buffer (at least two regions, so no launch finds its
+    bytes in a cache), across the given grid sizes; timed with HIP events
+    over `launches` launches per grid after one warm-up pass. This is what a
+    kernel that only streams the same bytes in one launch reaches, fixed
+    launch costs included."""
+    if launch_bytes <= 0 or launch_bytes % 16:
+        raise ValueError("launch_bytes must be a positive multiple of 16")
+    lib = load()
+    regions = max(2, n_bytes // launch_bytes)
+    buf = torch.empty(regions * launch_bytes, dtype=torch.uint8, device=device)
+    sink = torch.empty(int(lib.kvc_stream_read_sink_bytes(max(grids))), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream()
+    base = buf.data_ptr()
+    best = 0.0
+    for n_wg in grids:
+        def run(i):
+            _check(lib.kvc_stream_read(ctypes.c_void_p(base + (i % regions) * launch_bytes), launch_bytes,
+                                       _ptr(sink), n_wg, _stream(stream)), "kvc_stream_read")
+        for i in range(regions):
+            run(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(launches):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, launch_bytes / (e0.elapsed_time(e1) / launches / 1e3) / 1e9)
+    del buf, sink
+    return best

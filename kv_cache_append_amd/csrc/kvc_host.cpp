@@ -197,11 +197,14 @@ static double model_launch_us(const int32_t* lens, int32_t batch, int32_t n_kv, 
   work.reserve(static_cast<size_t>(batch) * n_kv * S * hblk);
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = lens[b] < 0 ? 0 : lens[b];
-    const int64_t chunk = ((n + S - 1) / S + 15) / 16 * 16;
+    // the decode kernel's split of [0, n): n - 1 rows in equal 16-row-tile
+    // chunks, the last active split also taking row n - 1
+    const int64_t chunk = std::max<int64_t>(16, ((n - 1 + S - 1) / S + 15) / 16 * 16);
+    const int64_t ns = n > 1 ? std::min<int64_t>(S, (n - 1 + chunk - 1) / chunk) : (n == 1 ? 1 : 0);
     for (int32_t g = 0; g < n_kv; ++g)
-      for (int32_t sp = 0; sp < S; ++sp) {
+      for (int64_t sp = 0; sp < S; ++sp) {   // (an inactive split's workgroup only starts)
         const int64_t t0 = sp * chunk;
-        const int64_t rows = t0 >= n ? 0 : std::min<int64_t>(n, t0 + chunk) - t0;
+        const int64_t rows = sp >= ns ? 0 : (sp == ns - 1 ? n : t0 + chunk) - t0;
         for (int h = 0; h < hblk; ++h) work.push_back(kStartUs + rows * row_bytes / kCuBytesPerUs);
       }
   }

@@ -695,12 +695,15 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
         store_out<ET>(p, pair_row(p, b, g, v_first + t / D) * D + t % D, 0.f);
     return;
   }
-  // chunks are whole 16-row tiles, so a tile never straddles two pages
-  const int chunk = ((n + p.n_splits - 1) / p.n_splits + 15) & ~15;
+  // The newest attended row is folded in apart from the stream (below), so
+  // the chunks share out the other n - 1 rows: equal whole 16-row tiles (a
+  // tile never straddles two pages), the last active split also holding row
+  // n - 1. ns splits are active.
+  const int chunk = max(16, ((n - 1 + p.n_splits - 1) / p.n_splits + 15) & ~15);
+  const int ns = n > 1 ? min(p.n_splits, (n - 1 + chunk - 1) / chunk) : 1;
+  if (split >= ns) return;                           // inactive split: not counted in ns
   const int t0 = split * chunk;
-  if (t0 >= n) return;                               // inactive split: not counted in ns
-  const int t1 = min(t0 + chunk, n);
-  const int ns = (n + chunk - 1) / chunk;
+  const int t1 = split == ns - 1 ? n : t0 + chunk;
 
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: loop bounds derived from it are wave-uniform
@@ -738,28 +741,41 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   const int n_seg = (p.ring != 0 && has_x && xrow != t1 - 1) ? 2 : 1;
   const int seg1_lo = __builtin_amdgcn_readfirstlane(xrow + 1);
   u32x4 nk = u32x4{0u, 0u, 0u, 0u}, nv = u32x4{0u, 0u, 0u, 0u};
+  // The row's K in the matrix-core layout (lanes l with l % 16 == 0 hold
+  // 16-byte slice 4m + l / 16 for MFMA m), requested here with the rest of
+  // the row so that no load waits after the streaming loop.
+  constexpr int NXK = kMfma ? (kQuant ? D / 64 : D / 32) : 1;
+  u32x4 xk[NXK];
+#pragma unroll
+  for (int m = 0; m < NXK; ++m) xk[m] = u32x4{0u, 0u, 0u, 0u};
   if (has_x && wave == 0) {
-    const char* ksrc;
-    const char* vsrc;
+    const char* krow;
+    const char* vrow;
     if (x_new) {
-      const int64_t noff = b * p.nsb + g * p.nsh + li * VSL;
-      ksrc = p.k_new + noff;
-      vsrc = p.v_new + noff;
+      const int64_t noff = b * p.nsb + g * p.nsh;
+      krow = p.k_new + noff;
+      vrow = p.v_new + noff;
     } else {
       const int64_t xo = slot_offset(p, b, g, xrow);
-      ksrc = xo < 0 ? nullptr : p.k + xo + li * VSL;
-      vsrc = xo < 0 ? nullptr : p.v + xo + li * VSL;
+      krow = xo < 0 ? nullptr : p.k + xo;
+      vrow = xo < 0 ? nullptr : p.v + xo;
       if (xo < 0 && lane == 0) flag(p, KVC_DEVERR_PAGE);
     }
-    if (ksrc != nullptr) {
+    if (krow != nullptr) {
       if constexpr (kQuant) {                  // 8 code bytes of V (K is loaded in the MFMA layout)
         if (!x_new) {                          // (a new row is quantised below)
-          const u32x2 w = *reinterpret_cast<const u32x2*>(vsrc);
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vrow + li * VSL);
           nv = u32x4{w[0], w[1], 0u, 0u};
         }
       } else {
-        nk = *reinterpret_cast<const u32x4*>(ksrc);
-        nv = *reinterpret_cast<const u32x4*>(vsrc);
+        nk = *reinterpret_cast<const u32x4*>(krow + li * VSL);
+        nv = *reinterpret_cast<const u32x4*>(vrow + li * VSL);
+      }
+      if constexpr (kMfma) {
+        if ((!kQuant || !x_new) && (lane & 15) == 0) {   // (a new 8-bit row's codes come through LDS)
+#pragma unroll
+          for (int m = 0; m < NXK; ++m) xk[m] = *reinterpret_cast<const u32x4*>(krow + (4 * m + (lane >> 4)) * 16);
+        }
       }
     }
   }
@@ -1053,16 +1069,12 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
     if (has_x && wave == 0) {                 // the last attended row, as row 0 of one more tile
       u32x4 K[NKL];
       VT V[NP];
-      const int64_t xo = x_new ? 0 : slot_offset(p, b, g, xrow);
-      const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : (xo < 0 ? nullptr : p.k + xo);
+      static_assert(NKL == NXK, "x-row K slices");
 #pragma unroll
       for (int m = 0; m < NKL; ++m) {
-        K[m] = u32x4{0u, 0u, 0u, 0u};
-        if (kQuant && x_new) {
-          if (r16 == 0) K[m] = *reinterpret_cast<const u32x4*>(&sm_x[0][(4 * m + kq) * 16]);
-        } else if (r16 == 0 && kx != nullptr) {
-          K[m] = *reinterpret_cast<const u32x4*>(kx + (4 * m + kq) * 16);
-        }
+        K[m] = xk[m];
+        if (kQuant && x_new) K[m] = r16 == 0 ? *reinterpret_cast<const u32x4*>(&sm_x[0][(4 * m + kq) * 16])
+                                             : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < NP; ++u) {

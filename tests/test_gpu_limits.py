@@ -97,3 +97,12 @@ def test_stream_read_reads_every_word_once(gpu):
     words = buf.cpu().numpy().view(np.uint32).reshape(-1, stride, 4)     # [rounds, thread, dword]
     want = np.bitwise_xor.reduce(np.bitwise_xor.reduce(words, axis=0), axis=1)
     assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
+
+
+def test_stream_read_launch_rate_is_finite(gpu):
+    """The per-launch streaming ceiling the bench reports: launches of a fixed
+    size over distinct regions, a positive finite rate."""
+    rate = kvc.stream_read_launch_rate(1 << 20, n_bytes=8 << 20, grids=(64,), launches=4)
+    assert np.isfinite(rate) and rate > 0
+    with pytest.raises(ValueError):
+        kvc.stream_read_launch_rate(1000)
