@@ -1038,6 +1038,29 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
       __builtin_amdgcn_wave_barrier();
     };
 
+    // The last attended row, as row 0 of one more tile. Wave 0 folds it in
+    // right after its first streamed tile, while its next tiles are still in
+    // flight, rather than after the loop, where the wave would run it alone.
+    bool x_done = false;
+    auto fold_x = [&]() {
+      u32x4 K[NKL];
+      VT V[NP];
+      static_assert(NKL == NXK, "x-row K slices");
+#pragma unroll
+      for (int m = 0; m < NKL; ++m) {
+        K[m] = xk[m];
+        if (kQuant && x_new) K[m] = r16 == 0 ? *reinterpret_cast<const u32x4*>(&sm_x[0][(4 * m + kq) * 16])
+                                             : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        if constexpr (kQuant) V[u] = (u == 0 && grp == 0) ? u32x2{nv[0], nv[1]} : u32x2{0u, 0u};
+        else V[u] = (u == 0 && grp == 0) ? nv : u32x4{0u, 0u, 0u, 0u};
+      }
+      compute(K, V, r16 == 0 ? xks : 0.f, r16 == 0 ? xvs : 0.f, 1, xrow);
+      x_done = true;
+    };
+
     // (a second segment occurs on contiguous ring caches only, so the page
     // lookup, which counts tiles from t0, never sees one)
     for (int seg = 0; seg < n_seg; ++seg) {
@@ -1057,6 +1080,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
             const int nr = (r + NBM - 1) % NBM;
             load_tile(base + (NBM - 1) * TSM, KB[nr], VB[nr], KSB[nr], VSB[nr]);
             compute(KB[r], VB[r], KSB[r], VSB[r], __builtin_amdgcn_readfirstlane(t_end - base), base);
+            if (!x_done && has_x && wave == 0) fold_x();
             base += TSM;
             if (it + r + 1 >= n_tiles) {
               done = true;
@@ -1066,23 +1090,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
         }
       }
     }
-    if (has_x && wave == 0) {                 // the last attended row, as row 0 of one more tile
-      u32x4 K[NKL];
-      VT V[NP];
-      static_assert(NKL == NXK, "x-row K slices");
-#pragma unroll
-      for (int m = 0; m < NKL; ++m) {
-        K[m] = xk[m];
-        if (kQuant && x_new) K[m] = r16 == 0 ? *reinterpret_cast<const u32x4*>(&sm_x[0][(4 * m + kq) * 16])
-                                             : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        if constexpr (kQuant) V[u] = (u == 0 && grp == 0) ? u32x2{nv[0], nv[1]} : u32x2{0u, 0u};
-        else V[u] = (u == 0 && grp == 0) ? nv : u32x4{0u, 0u, 0u, 0u};
-      }
-      compute(K, V, r16 == 0 ? xks : 0.f, r16 == 0 ? xvs : 0.f, 1, xrow);
-    }
+    if (!x_done && has_x && wave == 0) fold_x();   // (wave 0 streamed no tile)
     // Wave totals in the common layout: one reference per head (the same in
     // every lane), the weight sum in lane group 0 only (the lane-group merge
     // below adds the groups), accumulators as acc[head][element].
