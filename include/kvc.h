@@ -160,15 +160,17 @@ int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads);
  * kvc_decode_splits_for_lengths -- a split count for a decode call on this
  * cache when the caller knows the lengths it will attend (h_lens: host array
  * of cache->batch token counts, e.g. seq_lens + n_pending). It models the
- * launch -- every CU streaming an equal share of HBM bandwidth, shared by the
- * workgroups resident on it, workgroups dispatched in launch order, a fixed
- * start-up cost per workgroup and a merge cost per extra split -- for split
- * counts from 1 up to min(32, max_len / 256) and returns the fastest. Uneven
- * lengths (a ragged batch) get more, shorter splits than kvc_decode_splits
- * gives, so that no CU is left with a long tail. The model is calibrated on
- * the (bandwidth-bound) 16-bit decode kernels. Host only, a few
- * milliseconds for a few thousand (sequence, KV head) pairs; 0 for invalid
- * arguments. Pass the result as n_splits (and size the workspace for it).
+ * launch -- workgroups dispatched in launch order to the CUs' slots, the
+ * running ones sharing the chip's streaming rate up to what one workgroup
+ * reaches alone, a fixed start-up cost per workgroup and a merge cost per
+ * extra split -- for split counts from 1 up to min(32, max_len / 256). It
+ * returns kvc_decode_splits's count unless the model expects another count
+ * to be more than a sixth faster, as when a few sequences are far longer
+ * than the rest; those get more, shorter splits, so that no CU is left with
+ * a long tail. The model is calibrated on the (bandwidth-bound) 16-bit
+ * decode kernels. Host only, a few milliseconds for a few thousand
+ * (sequence, KV head) pairs; 0 for invalid arguments. Pass the result as
+ * n_splits (and size the workspace for it).
  */
 int32_t kvc_decode_splits_for_lengths(const kvc_cache_t* cache, int32_t n_q_heads, const int32_t* h_lens);
 

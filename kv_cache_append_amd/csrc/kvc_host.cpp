@@ -182,15 +182,18 @@ static int resident_wgs(int32_t dtype, int32_t head_dim, int gb) {
 }
 
 // Modelled duration (microseconds) of one decode launch with S splits over
-// sequences of lens[b] tokens. Each of the chip's CUs streams HBM at an equal
-// share of the measured streaming rate, shared equally by the workgroups
-// resident on it (at most per_cu); workgroups are handed out in launch order
-// to whichever CU frees a slot first; a workgroup costs a fixed start-up time
-// on top of its bytes; a launch with S > 1 splits ends with the split merge.
+// sequences of lens[b] tokens. The launch's workgroups are handed out in
+// launch order to per_cu slots on each of the chip's CUs; the workgroups
+// running at a time share the chip's streaming rate equally, each at most
+// the rate one workgroup reaches alone; a workgroup costs a fixed start-up
+// time on top of its bytes; a launch with S > 1 splits ends with the split
+// merge. (The rates are measured on MI355X with the 16-bit kernels: about
+// 6.4 TB/s for a full chip, about 36 GB/s for a workgroup on its own.)
 static double model_launch_us(const int32_t* lens, int32_t batch, int32_t n_kv, int hblk, double row_bytes,
                               int per_cu, int32_t S) {
   constexpr int kCus = 256;                    // MI355X compute units
-  constexpr double kCuBytesPerUs = 5.7e6 / kCus;   // 5.7 TB/s measured streaming rate, per CU
+  constexpr double kChipBytesPerUs = 6.4e6;    // all workgroups together
+  constexpr double kWgBytesPerUs = 36.0e3;     // one workgroup alone
   constexpr double kStartUs = 1.0;             // per workgroup: arguments, lengths, first loads
   const double merge_us = S == 1 ? 0.0 : 2.5 + 0.5 * (S - 2);
   std::vector<double> work;
@@ -205,46 +208,27 @@ static double model_launch_us(const int32_t* lens, int32_t batch, int32_t n_kv, 
       for (int64_t sp = 0; sp < S; ++sp) {   // (an inactive split's workgroup only starts)
         const int64_t t0 = sp * chunk;
         const int64_t rows = sp >= ns ? 0 : (sp == ns - 1 ? n : t0 + chunk) - t0;
-        for (int h = 0; h < hblk; ++h) work.push_back(kStartUs + rows * row_bytes / kCuBytesPerUs);
+        for (int h = 0; h < hblk; ++h) work.push_back(kStartUs * kWgBytesPerUs + rows * row_bytes);
       }
   }
-  // process sharing on each CU, driven by the earliest completion
-  constexpr int kMaxResident = 4;
-  double rem[kCus][kMaxResident];
-  int cnt[kCus];
-  double last[kCus];
+  // Every running workgroup moves at the same rate, so they finish in order
+  // of the progress mark (bytes per workgroup since the launch) at which
+  // their bytes run out; wall time is accumulated between marks at the rate
+  // the number of running workgroups allows.
+  const size_t slots = static_cast<size_t>(kCus) * per_cu;
+  std::priority_queue<double, std::vector<double>, std::greater<double>> finish;
   size_t next = 0;
-  for (int c = 0; c < kCus; ++c) {
-    cnt[c] = 0;
-    last[c] = 0.0;
+  while (finish.size() < slots && next < work.size()) finish.push(work[next++]);
+  double mark = 0.0, t = 0.0;
+  while (!finish.empty()) {
+    const double f = finish.top();
+    const double rate = std::min(kWgBytesPerUs, kChipBytesPerUs / static_cast<double>(finish.size()));
+    t += (f - mark) / rate;
+    mark = f;
+    finish.pop();
+    if (next < work.size()) finish.push(mark + work[next++]);
   }
-  for (int slot = 0; slot < per_cu; ++slot)
-    for (int c = 0; c < kCus && next < work.size(); ++c) rem[c][cnt[c]++] = work[next++];
-  typedef std::pair<double, int> Ev;
-  std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> heap;
-  auto done_at = [&](int c) {
-    double m = rem[c][0];
-    for (int i = 1; i < cnt[c]; ++i) m = std::min(m, rem[c][i]);
-    return last[c] + m * cnt[c];
-  };
-  for (int c = 0; c < kCus; ++c)
-    if (cnt[c] > 0) heap.push(Ev(done_at(c), c));
-  double t_end = 0.0;
-  while (!heap.empty()) {
-    const Ev ev = heap.top();
-    heap.pop();
-    const int c = ev.second;
-    const double dt = (ev.first - last[c]) / cnt[c];
-    int k = 0;
-    for (int i = 0; i < cnt[c]; ++i)
-      if (rem[c][i] - dt > 1e-9) rem[c][k++] = rem[c][i] - dt;
-    cnt[c] = k;
-    last[c] = ev.first;
-    t_end = std::max(t_end, ev.first);
-    while (cnt[c] < per_cu && next < work.size()) rem[c][cnt[c]++] = work[next++];
-    if (cnt[c] > 0) heap.push(Ev(done_at(c), c));
-  }
-  return t_end + merge_us;
+  return t + merge_us;
 }
 
 int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_t* lens) {
@@ -266,7 +250,13 @@ int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_
       best_us = t;
     }
   }
-  return best;
+  // The model is coarse (it does not see, for one, that whole units stream
+  // faster than short chunks), so the length-blind count stands unless the
+  // model expects another count to cut the launch by more than a sixth, as
+  // for a batch with a few sequences far longer than the rest.
+  const int32_t blind = std::min<int32_t>(auto_splits(c, n_q_heads), cap);
+  const double blind_us = model_launch_us(lens, c->batch, c->n_kv_heads, head_blocks(group), row_bytes, per_cu, blind);
+  return best_us < blind_us * (1.0 - 1.0 / 6.0) ? best : blind;
 }
 
 static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
