@@ -215,3 +215,19 @@ def test_full_size_layer_sampled_units(gpu, name):
     assert status == 0
     worst = _check_all(case, out)
     print(f"{name}: max-abs {worst:.3e} over {len(case.host)} units")
+
+
+def test_length_aware_split_choice_on_a_very_uneven_batch(gpu):
+    """One sequence far longer than the rest: the length-aware choice takes
+    many splits (more than the length-blind rule), and the decode with that
+    count matches the oracle on every unit."""
+    lengths = [20000] + [40] * 7
+    case = DecodeCase(batch=8, n_q=32, n_kv=8, head_dim=128, dtype="bf16", lengths=lengths, tag="uneven",
+                      device=gpu)
+    attended = [n + 1 for n in lengths]
+    s_len = kvc.decode_splits(case.k, case.v, case.n_q, lengths=attended)
+    s_blind = kvc.decode_splits(case.k, case.v, case.n_q)
+    assert s_len > s_blind
+    out, status = _run(case, n_splits=s_len)
+    assert status == 0
+    _check_all(case, out)
