@@ -138,11 +138,10 @@ kvc_status_t kvc_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens,
  * make). The bound holds for any seq_lens <= max_len. Returns 0 for invalid
  * arguments.
  *
- * Layout and lifetime: uint32 synchronisation words (a ticket per sequence,
- * KV head and block of query heads, and a ready flag per such item and
- * split), then fp32 per-split partial results. The caller zero-fills the
- * workspace once after allocating it; every decode call leaves the
- * synchronisation words zero again, so the workspace serves any number of
+ * Layout and lifetime: uint32 ready flags (one per sequence, KV head, block
+ * of query heads and split), then fp32 per-split partial results. The
+ * caller zero-fills the workspace once after allocating it; every decode
+ * call leaves the flags zero again, so the workspace serves any number of
  * later calls with the same batch, n_kv_heads, n_q_heads and split count
  * (any lengths, any layer) without clearing. Where those change, the region
  * layout moves: zero-fill the workspace again first (or keep one workspace

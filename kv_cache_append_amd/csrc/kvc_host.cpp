@@ -265,9 +265,7 @@ static size_t sync_units(const kvc_cache_t* c, int32_t n_q_heads) {
   return static_cast<size_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
 }
 
-size_t workspace_flag_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t /*n_splits*/) {
-  return round256(sync_units(c, n_q_heads) * sizeof(uint32_t));
-}
+size_t workspace_flag_offset(const kvc_cache_t*, int32_t, int32_t) { return 0; }
 
 size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
   return workspace_flag_offset(c, n_q_heads, n_splits) +

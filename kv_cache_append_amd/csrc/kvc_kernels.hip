@@ -24,11 +24,11 @@
 //     it only moves when a score exceeds it by more than 2^8, so the
 //     accumulators are rarely rescaled (exact in real arithmetic, bounded
 //     exponentials in fp32);
-//   * each workgroup's partial (reference, sum, unnormalised output) goes to
-//     the workspace; the last workgroup of a (sequence, KV head) to arrive,
-//     found with a device-scope atomic ticket, merges the partials in split
-//     order (bit-identical results whatever the arrival order) and writes the
-//     normalised output, then leaves the ticket and flags at zero;
+//   * with several splits, every split but the last publishes its partial
+//     (reference, sum, unnormalised output) in the workspace and raises a
+//     ready flag; the last split's workgroup waits for those flags, merges
+//     the partials in split order (bit-identical results run to run) and
+//     writes the normalised output, then leaves the flags at zero;
 //   * kvc_decode_step additionally takes the step's k_t, v_t: the workgroup
 //     whose chunk holds slot T_b reads that row from k_t/v_t and writes it
 //     into the cache, so append and attention share the launch.
@@ -309,7 +309,6 @@ struct DecodeParams {
   const char* k_new;           // fused append source [B, H_kv, D] or null
   const char* v_new;
   int64_t nsb, nsh;            // its strides in bytes
-  uint32_t* ws_cnt;            // [B * H_kv * n_hblk] tickets, zero between calls
   uint32_t* ws_flag;           // [B * H_kv * n_hblk, S] ready flags, zero between calls
   float* ws_o;                 // [B, H_q, S, D]
   float* ws_ml;                // [B, H_q, S, 2]
@@ -667,7 +666,6 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   __shared__ float sm_acc[kLdsMerge ? NW : 1][kLdsMerge ? RPP : 1][GB][kLdsMerge ? D : 1];
   __shared__ float sm_ml[NW][GB][2];
   __shared__ float sm_p[kMfma ? NW : 1][16][4 * NQ];   // softmax weights, score layout -> V layout
-  __shared__ uint32_t sm_ticket;
   // 8-bit caches, fused append: the new row's K and V codes, staged so that
   // they can be read in the score layout (K) and the row layout (V)
   __shared__ __align__(16) uint8_t sm_x[kQuant ? 2 : 1][kQuant ? D : 16];
@@ -1369,66 +1367,53 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
     return;
   }
 
-  // Several splits. Every workgroup publishes its partial (reference, sum,
-  // unnormalised output) with device-coherent stores and takes a ticket
-  // (agent-scope atomic); the last to arrive merges. With two splits the
-  // ticket is taken in the same round trip as the stores, so the workgroup
-  // that is not last raises its split's ready flag once its stores have
-  // completed, and the last one waits for that flag (raised by a workgroup
-  // that already holds a ticket, so the wait is short and bounded). With
-  // more splits, which tend to arrive together, the ticket is taken after
-  // the stores complete, so the last ticket implies every partial is in
-  // place. The merging workgroup folds the partials in with device-coherent
-  // loads, writes the output, and leaves the ticket and the flags at zero
-  // for the next call.
-  const bool early_ticket = ns == 2;
+  // Several splits. The last active split merges; the others publish their
+  // partial (reference, sum, unnormalised output) with device-coherent
+  // stores, wait for them to complete and raise their split's ready flag.
+  // The merging workgroup waits for the other splits' flags, folds the
+  // partials in, writes the output and leaves the flags at zero for the next
+  // call. It has the highest workgroup id of its item, and a workgroup that
+  // publishes never waits, so with workgroups dispatched in id order on each
+  // XCD every awaited workgroup is dispatched and finishes; the wait is
+  // bounded all the same.
   const int64_t item = static_cast<int64_t>(unit) * p.n_hblk + hb;
-  uint32_t* ticket = p.ws_cnt + item;
   uint32_t* flags = p.ws_flag + item * p.n_splits;
   // partial rows: [B, H_kv * pairs, S] (for decode, [B, H_q, S])
   const int64_t prow0 = ((static_cast<int64_t>(b) * p.n_kv + g) * gv + v_first) * p.n_splits;
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(nh * p.n_splits * D * 4));
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(nh * p.n_splits * 2 * 4));
+  if (split != ns - 1) {
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int t = threadIdx.x + i * NW * 64;
-    if (t >= nh * D4) continue;
-    const int j = t / D4;
-    const int d = (t - j * D4) * 4;
-    const uint32_t row = static_cast<uint32_t>(j * p.n_splits + split);
-    buf_store_coherent(ors, (row * D + d) * 4u,
-                       u32x4{__float_as_uint(aa[i][0]), __float_as_uint(aa[i][1]), __float_as_uint(aa[i][2]),
-                             __float_as_uint(aa[i][3])});
-    if (d == 0) {
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rv[i]), mrs, static_cast<int>(row * 8u), 0, kCoherent);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv[i]), mrs, static_cast<int>(row * 8u + 4u), 0,
-                                            kCoherent);
+    for (int i = 0; i < TPT; ++i) {
+      const int t = threadIdx.x + i * NW * 64;
+      if (t >= nh * D4) continue;
+      const int j = t / D4;
+      const int d = (t - j * D4) * 4;
+      const uint32_t row = static_cast<uint32_t>(j * p.n_splits + split);
+      buf_store_coherent(ors, (row * D + d) * 4u,
+                         u32x4{__float_as_uint(aa[i][0]), __float_as_uint(aa[i][1]), __float_as_uint(aa[i][2]),
+                               __float_as_uint(aa[i][3])});
+      if (d == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rv[i]), mrs, static_cast<int>(row * 8u), 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv[i]), mrs, static_cast<int>(row * 8u + 4u), 0,
+                                              kCoherent);
+      }
     }
-  }
-  if (early_ticket && threadIdx.x == 0)
-    sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (!early_ticket) {
-    if (threadIdx.x == 0) sm_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-  }
-  if (sm_ticket != static_cast<uint32_t>(ns - 1)) {
-    if (early_ticket && threadIdx.x == 0)
-      __hip_atomic_store(flags + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
-  // Last to arrive: with two splits, wait for the other split's flag.
-  for (int k = threadIdx.x; early_ticket && k < ns; k += blockDim.x) {
-    if (k == split) continue;
+  // The merging workgroup: wait for the other splits' flags.
+  for (int k = threadIdx.x; k < ns - 1; k += blockDim.x) {
     int spins = 0;
     while (__hip_atomic_load(flags + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       if (++spins > kMaxSpins) {                 // never expected: flag the call, do not hang
         if (p.status != nullptr) atomicOr(p.status, KVC_DEVERR_SYNC);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
@@ -1491,9 +1476,8 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   }
   write_out();
   // ready for the next call on this workspace
-  for (int k = threadIdx.x; early_ticket && k < ns; k += blockDim.x)
-    if (k != split) __hip_atomic_store(flags + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int k = threadIdx.x; k < ns - 1; k += blockDim.x)
+    __hip_atomic_store(flags + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------- dispatch --
@@ -1724,7 +1708,6 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
   p.nsb = new_stride_b * s_in;
   p.nsh = new_stride_h * s_in;
   char* ws = static_cast<char*>(workspace);
-  p.ws_cnt = reinterpret_cast<uint32_t*>(ws);
   p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(&view, n_q_heads, splits));
   p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(&view, n_q_heads, splits));
   p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(&view, n_q_heads, splits));
@@ -1856,7 +1839,6 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.nsb = new_stride_b * s;
   p.nsh = new_stride_h * s;
   char* ws = static_cast<char*>(workspace);
-  p.ws_cnt = reinterpret_cast<uint32_t*>(ws);
   p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(cache, n_qv, splits));
   p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(cache, n_qv, splits));
   p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(cache, n_qv, splits));

@@ -128,15 +128,15 @@ def test_decode_validation_gqa_workspace_unsupported():
 
 
 def test_workspace_size_formula():
-    """Workspace = uint32 tickets [B * H_kv * head blocks] + uint32 ready flags
-    [B * H_kv * head blocks, S] + fp32 partial outputs [B, H_q, S, D] +
-    (reference, sum) pairs, each region rounded up to 256 bytes."""
+    """Workspace = uint32 ready flags [B * H_kv * head blocks, S] + fp32
+    partial outputs [B, H_q, S, D] + (reference, sum) pairs, each region
+    rounded up to 256 bytes."""
     kvc, lib = _lib()
     c = _desc(kvc)
     for s in (1, 3, 16, 100):
         rows = 2 * 4 * s
         flags = -(-2 * 2 * s * 4 // 256) * 256
-        want = 256 + flags + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+        want = flags + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
         assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, s) == want
     auto = lib.kvc_decode_splits(ctypes.byref(c), 4)
     assert auto >= 1
