@@ -1418,8 +1418,8 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   }
   __syncthreads();
   // Fold all splits in split order, eight per round trip, this workgroup's own
-  // split taken from registers (the bits it would have stored), so the result
-  // does not depend on which split arrived last. The other splits' (reference,
+  // (last) split taken from registers, so the order, and with it every output
+  // bit, is the same on every run. The other splits' (reference,
   // sum) pairs and partial outputs are requested together (unconditional
   // loads: rows past the split count read another head's data or, past the
   // region, zeros, and are weighted 0), then merged with a running reference.
