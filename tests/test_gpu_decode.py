@@ -231,3 +231,21 @@ def test_length_aware_split_choice_on_a_very_uneven_batch(gpu):
     out, status = _run(case, n_splits=s_len)
     assert status == 0
     _check_all(case, out)
+
+
+def test_many_splits_on_an_oversubscribed_grid(gpu):
+    """512 (sequence, KV head) units at 32 splits each: 16,384 active
+    workgroups, 32 times what the chip holds at once, so most merging
+    workgroups wait on splits dispatched after them on other CUs. No wait
+    may time out (status stays 0) and sampled units match the oracle."""
+    lengths = synth.ragged_lengths(64, 3000, 4096, 11, "oversub").tolist()
+    sample = [(0, 0), (13, 5), (40, 2), (63, 7)]
+    case = DecodeCase(batch=64, n_q=32, n_kv=8, head_dim=128, dtype="bf16", lengths=lengths, tag="oversub",
+                      device=gpu, host_rows=sample)
+    out, status = _run(case, n_splits=32)
+    assert status == 0
+    grp = case.n_q // case.n_kv
+    got = out.double().cpu().numpy()
+    for b, g in sample:
+        ref = _oracle_unit(case, b, g)
+        assert np.abs(got[b, g * grp:(g + 1) * grp] - ref).max() <= TOL["bf16"]
