@@ -424,30 +424,36 @@ def _cpu_baseline(cfg, seconds: float, seed: int):
     except Exception:
         threads = 1
     lengths = cfg.lengths(seed)
-    g = cfg.group
     done_bytes, units, t_spent = 0, 0, 0.0
     b = 0
-    while t_spent < seconds and units < cfg.batch * cfg.n_kv_heads * cfg.n_layers:
-        n = int(lengths[b % cfg.batch]) + 1
+    inputs = {}
+    # (sequence, layer) slices in step order, repeated over later steps until
+    # about `seconds` of oracle time (at most 100 steps); each sequence's
+    # inputs are drawn once
+    while t_spent < seconds and b < 100 * cfg.batch * cfg.n_layers:
+        i = b % cfg.batch
+        n = int(lengths[i]) + 1
         kv = cfg.n_kv_heads
-        q = synth.normal((1, cfg.n_q_heads, cfg.head_dim), cfg.dtype, seed, "cpu", b, "q")
-        k = synth.normal((1, kv, n, cfg.head_dim), cfg.dtype, seed, "cpu", b, "K")
-        v = synth.normal((1, kv, n, cfg.head_dim), cfg.dtype, seed, "cpu", b, "V")
+        if i not in inputs:
+            inputs[i] = (synth.normal((1, cfg.n_q_heads, cfg.head_dim), cfg.dtype, seed, "cpu", i, "q"),
+                         synth.normal((1, kv, n, cfg.head_dim), cfg.dtype, seed, "cpu", i, "K"),
+                         synth.normal((1, kv, n, cfg.head_dim), cfg.dtype, seed, "cpu", i, "V"))
+        q, k, v = inputs[i]
         t0 = time.perf_counter()
         oracle.decode_attention(q, k, v, np.array([n - 1]), n_pending=1)
         t_spent += time.perf_counter() - t0
         done_bytes += 2 * kv * n * cfg.head_dim * cfg.elem_bytes
         units += kv
         b += 1
-        del q, k, v
+    del inputs
     return {
         "value": round(done_bytes / t_spent / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{b} (sequence, layer) slices of {cfg.name}, all {cfg.n_kv_heads} KV heads each "
-                  f"({units} (sequence, KV head) units, {cfg.group} query heads each, "
-                  f"{done_bytes / 1e9:.3f} GB of K+V) in {t_spent:.1f} s; numpy fp64, BLAS threads={threads}",
+        "sample": f"{b} (sequence, layer) slices of {cfg.name} ({b / (cfg.batch * cfg.n_layers):.2f} steps), all "
+                  f"{cfg.n_kv_heads} KV heads each ({units} (sequence, KV head) units, {cfg.group} query heads "
+                  f"each, {done_bytes / 1e9:.3f} GB of K+V) in {t_spent:.1f} s; numpy fp64, BLAS threads={threads}",
     }
 
 
