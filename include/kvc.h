@@ -269,6 +269,35 @@ kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* seq_lens, i
 size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t t_q, int32_t n_splits);
 
 /*
+ * kvc_prefill_attn -- the same operation as kvc_block_attn (query i of
+ * sequence b attends slots 0 .. seq_lens[b] + i; course notes "第 1 周 ·
+ * Day 4" §3.3, masks with a cache), tiled for long blocks: a whole prompt
+ * (seq_lens[b] = 0 gives the causal prefill of §1.3) or a long prefill chunk.
+ * The block's K/V rows must already be in the cache at slots
+ * [seq_lens[b], seq_lens[b] + t_q); seq_lens is only read.
+ *
+ *   cache     fp16 or bf16, head_dim 64 or 128 (else KVC_ERR_UNSUPPORTED;
+ *             fp32 caches and other head dims use kvc_block_attn).
+ *   t_q       queries per sequence, >= 1.
+ *   q         [batch, t_q, n_q_heads, head_dim], contiguous, cache dtype,
+ *             16-byte aligned.
+ *   out       [batch, t_q, n_q_heads, head_dim], contiguous, out_dtype
+ *             (KVC_F32 or the cache dtype).
+ *   scale     softmax scale, finite and > 0.
+ *
+ * Scores and accumulation are fp32 on the matrix cores; the softmax weights
+ * enter the weighted sum of V as two 16-bit parts (about 16 significant
+ * bits). No workspace: every output row is produced by one workgroup. A
+ * sequence whose block does not fit (seq_lens[b] < 0, or seq_lens[b] + t_q >
+ * max_len) gets zero rows and KVC_DEVERR_BADLEN / KVC_DEVERR_CAPACITY.
+ * Host-side errors: KVC_ERR_NULL, KVC_ERR_GQA, KVC_ERR_DTYPE, KVC_ERR_ALIGN,
+ * KVC_ERR_SHAPE (t_q < 1, or a slice too large for 32-bit offsets).
+ */
+kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
+                              const void* q, int32_t n_q_heads, float scale,
+                              void* out, int32_t out_dtype, uint32_t* dev_status, hipStream_t stream);
+
+/*
  * Ring cache for sliding-window layers (course notes "第 1 周 · Day 4" §2.7:
  * a layer that only attends its most recent W tokens needs a cache of W
  * slots; §1.6: with rotary positions baked into the cached K, the window can

@@ -35,6 +35,7 @@ STATUS = {
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
            "kvc_decode_attn", "kvc_decode_step", "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes",
+           "kvc_prefill_attn",
            "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
            "kvc_paged_decode_attn", "kvc_paged_decode_step",
            "kvc_ring_append", "kvc_ring_prefill_fill", "kvc_ring_decode_attn", "kvc_ring_decode_step",
@@ -92,6 +93,8 @@ def load() -> ctypes.CDLL:
     lib.kvc_block_attn.restype = i32
     lib.kvc_block_workspace_bytes.argtypes = [cp, i32, i32, i32]
     lib.kvc_block_workspace_bytes.restype = sz
+    lib.kvc_prefill_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, vp]
+    lib.kvc_prefill_attn.restype = i32
     pp = ctypes.POINTER(PagedCacheDesc)
     lib.kvc_paged_append.argtypes = [pp, vp, vp, vp, i64, i64, vp, vp]
     lib.kvc_paged_append.restype = i32
@@ -329,6 +332,19 @@ def block_attn(k_cache, v_cache, seq_lens, q, out, workspace, scale=None, n_spli
                               _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
                               workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
                               _stream(stream)), "kvc_block_attn")
+
+
+def prefill_attn(k_cache, v_cache, seq_lens, q, out, scale=None, status=None, stream=None, desc=None):
+    """kvc_prefill_attn: as block_attn (query i of sequence b attends slots
+    0..seq_lens[b]+i), tiled on the matrix cores for long blocks; no workspace."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 4:
+        raise ValueError("q and out must be contiguous [B, t_q, H_q, D]")
+    _check(lib.kvc_prefill_attn(ctypes.byref(c), _ptr(seq_lens), q.shape[1], _ptr(q), q.shape[2], float(scale),
+                                _ptr(out), DTYPE_CODE[out.dtype], _ptr(status), _stream(stream)), "kvc_prefill_attn")
 
 
 def paged_prefill_fill(k_pages, v_pages, block_table, seq_lens, k, v, status=None, stream=None):

@@ -1,0 +1,412 @@
+// Causal attention of a long block of new queries over the cache (a whole
+// prompt, or a long prefill chunk) on the CDNA4 matrix cores.
+//
+// The operation is the one kvc_block_attn computes (course notes
+// "第 1 周 · Day 4" §3.3, masks with a cache; with nothing cached before the
+// block it is the causal prefill of §1.3): query i of sequence b sees cache
+// slots 0 .. seq_lens[b] + i. For a block of hundreds or thousands of queries
+// the work is a pair of dense products per head, so it is tiled as flash
+// attention is:
+//   * one 256-thread workgroup per (sequence, query head, 128 queries); each
+//     of its four waves owns 32 queries (two 16-query column blocks);
+//   * the unit's K/V rows go through LDS in tiles of 64 keys: K as it is
+//     stored (padded rows), V transposed (one row per head-dim element), so
+//     both products read their matrix-core operands as 16-byte LDS loads;
+//   * scores are computed transposed, S^T = K Q^T, on
+//     v_mfma_f32_16x16x32_{bf16,f16}: a lane then holds the scores of one
+//     query, so the running maximum, the rescale and the weights stay in its
+//     registers (a max over the four lanes that share a query is the only
+//     exchange);
+//   * the output is accumulated transposed too, O^T += V^T P^T, with the
+//     fp32 weights P split into two 16-bit parts (P = hi + lo, both exact
+//     sums of bits), so the product keeps about 16 significant bits of each
+//     weight while running on the 16-bit matrix cores; accumulation is fp32;
+//   * a 128-query tile of a sequence whose block starts at slot c needs keys
+//     [0, c + last query + 1) only; the mask is applied in the tiles that
+//     cross the diagonal, and a wave skips tiles it cannot see.
+// Workgroups of one (sequence, KV head) share its K/V: when the unit count
+// is a multiple of eight they are placed on one XCD (the dispatcher deals
+// workgroup ids round-robin over the eight XCDs), heaviest query tiles first.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvc.h"
+#include "kvc_internal.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kQTile = 128;      // queries per workgroup
+constexpr int kKTile = 64;       // keys per LDS tile
+constexpr int kVtRow = 144;      // bytes per transposed-V row in LDS: 64 keys + 8 elements of padding
+
+struct PrefillParams {
+  const char* k;
+  const char* v;
+  int64_t sb, sh, st;            // cache strides in bytes
+  const int32_t* seq_lens;
+  const char* q;                 // [B, t_q, H_q, D]
+  void* out;                     // [B, t_q, H_q, D]
+  uint32_t* status;
+  int32_t batch, n_q, n_kv, group, t_q, max_len, n_qt, out_f32, xcd_major;
+  float scale_log2;              // softmax scale times log2(e)
+};
+
+// 16-bit cache element types: the matrix-core product, the split of two
+// fp32 weights into high and low 16-bit parts (packed two to a word, first
+// weight in the low half), and the output store.
+struct Bf16P {
+  __device__ static inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  }
+  // hi keeps the top 16 bits of each weight (a bf16 value), lo the top 16
+  // bits of the exact remainder: hi + lo carries 16 of the 24 bits.
+  __device__ static inline void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+    const float r0 = p0 - __uint_as_float(u0 & 0xffff0000u);
+    const float r1 = p1 - __uint_as_float(u1 & 0xffff0000u);
+    hi = (u0 >> 16) | (u1 & 0xffff0000u);
+    lo = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xffff0000u);
+  }
+  __device__ static inline void store(void* base, int64_t i, float x) {
+    // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN
+    const uint32_t u = __float_as_uint(x);
+    uint16_t h;
+    if ((u & 0x7fffffffu) > 0x7f800000u) h = static_cast<uint16_t>((u >> 16) | 0x40u);
+    else h = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    static_cast<uint16_t*>(base)[i] = h;
+  }
+};
+
+struct F16P {
+  __device__ static inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+  }
+  // hi = fp16(p) (nearest), lo = fp16(p - hi); the remainder is exact in fp32
+  __device__ static inline void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const _Float16 h0 = static_cast<_Float16>(p0), h1 = static_cast<_Float16>(p1);
+    const float r0 = p0 - static_cast<float>(h0), r1 = p1 - static_cast<float>(h1);
+    hi = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+    lo = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(r0), static_cast<_Float16>(r1)});
+  }
+  __device__ static inline void store(void* base, int64_t i, float x) {
+    asm volatile("" : "+v"(x));   // keep the fp32 value: one rounding, to nearest even
+    static_cast<_Float16*>(base)[i] = static_cast<_Float16>(x);
+  }
+};
+
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ inline u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+// The slot of key kk (0..31) of a 32-key chunk in a transposed-V row. The
+// score product leaves lane group g (lanes 16g .. 16g+15) with keys 4g..4g+3
+// of each 16-key block; the output product takes 8 consecutive slots per
+// lane group, so slots 8g..8g+7 hold keys 4g..4g+3 and 16+4g..16+4g+3.
+__device__ inline int vt_slot(int kk) { return 8 * ((kk & 15) >> 2) + (kk & 3) + 4 * (kk >> 4); }
+
+template <typename ET, int D>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
+  constexpr int NC = D / 32;            // 32-element slices of a row (score product depth)
+  constexpr int ND = D / 16;            // 16-element output blocks
+  constexpr int KR = 2 * D + 16;        // bytes per K row in LDS (16 bytes of padding)
+  constexpr int NKL = D / 32;           // 16-byte K loads per thread per tile
+  constexpr int NVP = D / 64;           // V passes per tile, two 16-byte loads each
+  __shared__ __attribute__((aligned(16))) char sk[kKTile * KR];
+  __shared__ __attribute__((aligned(16))) char svt[D * kVtRow];
+
+  const int units = p.batch * p.n_kv;
+  const int per_unit = p.group * p.n_qt;
+  int unit, qt, hg;
+  if (p.xcd_major) {                    // one unit's workgroups on one XCD
+    const int xcd = blockIdx.x & 7;
+    const int j = blockIdx.x >> 3;
+    unit = (j / per_unit) * 8 + xcd;
+    const int r = j % per_unit;
+    qt = p.n_qt - 1 - r / p.group;
+    hg = r % p.group;
+  } else {
+    const int j = blockIdx.x;
+    const int per_qt = units * p.group;
+    qt = p.n_qt - 1 - j / per_qt;
+    const int r = j % per_qt;
+    unit = r / p.group;
+    hg = r % p.group;
+  }
+  if (unit >= units) return;             // grid padding
+  const int b = unit / p.n_kv;
+  const int g = unit - b * p.n_kv;
+  const int h = g * p.group + hg;
+  const int c0 = p.seq_lens[b];
+  const int i0 = qt * kQTile;
+  const int nq = min(kQTile, p.t_q - i0);  // queries of this tile
+  if (c0 < 0 || c0 + p.t_q > p.max_len) {   // the block does not fit: zero rows, flagged once
+    if (threadIdx.x == 0 && qt == 0 && hg == 0 && g == 0 && p.status != nullptr)
+      atomicOr(p.status, c0 < 0 ? KVC_DEVERR_BADLEN : KVC_DEVERR_CAPACITY);
+    for (int t = threadIdx.x; t < nq * D; t += blockDim.x) {
+      const int64_t idx = ((static_cast<int64_t>(b) * p.t_q + i0 + t / D) * p.n_q + h) * D + t % D;
+      if (p.out_f32) static_cast<float*>(p.out)[idx] = 0.f;
+      else ET::store(p.out, idx, 0.f);
+    }
+    return;
+  }
+  const int n = c0 + p.t_q;                            // rows in the cache for this block
+  const int n_tiles = (c0 + i0 + nq + kKTile - 1) / kKTile;   // keys [0, c0 + i0 + nq) are seen
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int wq0 = i0 + 32 * wave;                      // first query of this wave
+  const bool wactive = wq0 < p.t_q;
+  const int wlim = c0 + min(wq0 + 32, p.t_q);          // this wave's queries see keys [0, wlim)
+  const int wmin = c0 + wq0 + 1;                       // ... and all of them keys [0, wmin)
+
+  // The query rows as B operands of the score product (column = query
+  // r16 of block qb, 8 elements 32c + 8grp .. of the row), and their limits.
+  u32x4 qf[2][NC];
+  int lim[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int iq = wq0 + 16 * qb + r16;
+    lim[qb] = c0 + iq + 1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[qb][c] = u32x4{0u, 0u, 0u, 0u};
+      if (iq < p.t_q)
+        qf[qb][c] = *reinterpret_cast<const u32x4*>(
+            p.q + ((((static_cast<int64_t>(b) * p.t_q + iq) * p.n_q + h) * D) + 32 * c + 8 * grp) * 2);
+    }
+  }
+
+  const int64_t uoff = b * p.sb + g * p.sh;
+  const uint32_t st = static_cast<uint32_t>(p.st);
+  const __amdgpu_buffer_rsrc_t krs = rsrc(p.k + uoff, static_cast<uint32_t>(n) * st);
+  const __amdgpu_buffer_rsrc_t vrs = rsrc(p.v + uoff, static_cast<uint32_t>(n) * st);
+
+  // Tile staging: thread tid loads K chunks tid + 256m (row idx / (D/8),
+  // 16-byte chunk idx % (D/8)) and V rows 2kp, 2kp+1 (kp = tid % 32) at
+  // chunk tid / 32 + 8 pass.
+  u32x4 kr[NKL], vr[2 * NVP];
+  auto load_tile = [&](int t) {
+    const uint32_t base = static_cast<uint32_t>(t * kKTile) * st;
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+      const int idx = tid + 256 * m;
+      kr[m] = bload(krs, base + static_cast<uint32_t>(idx / (D / 8)) * st + static_cast<uint32_t>(idx % (D / 8)) * 16u);
+    }
+#pragma unroll
+    for (int ps = 0; ps < NVP; ++ps) {
+      const int kp = tid & 31;
+      const int dc = (tid >> 5) + 8 * ps;
+      vr[2 * ps] = bload(vrs, base + static_cast<uint32_t>(2 * kp) * st + dc * 16u);
+      vr[2 * ps + 1] = bload(vrs, base + static_cast<uint32_t>(2 * kp + 1) * st + dc * 16u);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+      const int idx = tid + 256 * m;
+      *reinterpret_cast<u32x4*>(sk + (idx / (D / 8)) * KR + (idx % (D / 8)) * 16) = kr[m];
+    }
+#pragma unroll
+    for (int ps = 0; ps < NVP; ++ps) {
+      const int kp = tid & 31;
+      const int dc = (tid >> 5) + 8 * ps;
+      const int key0 = 2 * kp;                           // keys key0, key0 + 1 share one word
+      const int col = (32 * (key0 >> 5) + vt_slot(key0 & 31)) * 2;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w0 = vr[2 * ps][m], w1 = vr[2 * ps + 1][m];
+        const int d = 8 * dc + 2 * m;
+        *reinterpret_cast<uint32_t*>(svt + d * kVtRow + col) = (w0 & 0xffffu) | (w1 << 16);
+        *reinterpret_cast<uint32_t*>(svt + (d + 1) * kVtRow + col) = (w0 >> 16) | (w1 & 0xffff0000u);
+      }
+    }
+  };
+
+  float mrun[2] = {-INFINITY, -INFINITY};   // running maximum (log2 domain), per query
+  float lrun[2] = {0.f, 0.f};               // this lane's part of the running sum
+  f32x4 o[2][ND];                           // O^T: lane holds elements 16db + 4grp + i of query r16
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < ND; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int t) {
+    f32x4 s[2][4];                          // S^T: lane holds keys 16kb + 4grp + i of query r16
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sk + (16 * kb + r16) * KR + (32 * c + 8 * grp) * 2);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) s[qb][kb] = ET::mfma(a, qf[qb][c], s[qb][kb]);
+      }
+    const bool masked = (t + 1) * kKTile > wmin;       // wave-uniform: the tile crosses the diagonal
+    u32x4 phi[2][2], plo[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[qb][kb][i] * p.scale_log2;
+          if (masked) x = (t * kKTile + 16 * kb + 4 * grp + i < lim[qb]) ? x : -INFINITY;
+          s[qb][kb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(mrun[qb], mx);
+      const float alpha = mrun[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[qb] - mn);
+      mrun[qb] = mn;
+      lrun[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha;
+      float e[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          e[kb][i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - mn);   // masked: exp2(-inf) = 0
+          lrun[qb] += e[kb][i];
+        }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        uint32_t hi[4], lo[4];
+        ET::split(e[2 * kc][0], e[2 * kc][1], hi[0], lo[0]);
+        ET::split(e[2 * kc][2], e[2 * kc][3], hi[1], lo[1]);
+        ET::split(e[2 * kc + 1][0], e[2 * kc + 1][1], hi[2], lo[2]);
+        ET::split(e[2 * kc + 1][2], e[2 * kc + 1][3], hi[3], lo[3]);
+        phi[qb][kc] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        plo[qb][kc] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(svt + (16 * db + r16) * kVtRow + (32 * kc + 8 * grp) * 2);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          o[qb][db] = ET::mfma(a, phi[qb][kc], o[qb][db]);
+          o[qb][db] = ET::mfma(a, plo[qb][kc], o[qb][db]);
+        }
+      }
+  };
+
+  load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();                        // every wave is done with the previous tile
+    store_tile();
+    __syncthreads();
+    if (t + 1 < n_tiles) load_tile(t + 1);  // in flight while this tile is computed
+    if (wactive && t * kKTile < wlim) compute(t);
+  }
+  if (!wactive) return;
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = lrun[qb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = 1.f / l;
+    const int iq = wq0 + 16 * qb + r16;
+    if (iq < p.t_q) {
+      const int64_t row = ((static_cast<int64_t>(b) * p.t_q + iq) * p.n_q + h) * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = o[qb][db][i] * inv;
+          const int64_t idx = row + 16 * db + 4 * grp + i;
+          if (p.out_f32) static_cast<float*>(p.out)[idx] = x;
+          else ET::store(p.out, idx, x);
+        }
+    }
+  }
+}
+
+typedef void (*PrefillKernel)(const PrefillParams);
+
+PrefillKernel pick_prefill_kernel(int32_t dtype, int32_t d) {
+  if (dtype == KVC_BF16 && d == 128) return prefill_kernel<Bf16P, 128>;
+  if (dtype == KVC_BF16 && d == 64) return prefill_kernel<Bf16P, 64>;
+  if (dtype == KVC_F16 && d == 128) return prefill_kernel<F16P, 128>;
+  if (dtype == KVC_F16 && d == 64) return prefill_kernel<F16P, 64>;
+  return nullptr;
+}
+
+}  // namespace
+
+extern "C" kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
+                                         const void* q, int32_t n_q_heads, float scale, void* out, int32_t out_dtype,
+                                         uint32_t* dev_status, hipStream_t stream) {
+  kvc_status_t st = kvc::check_cache(cache, true);
+  if (st != KVC_OK) return st;
+  if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
+  if (t_q <= 0) return KVC_ERR_SHAPE;
+  if (out_dtype != KVC_F32 && out_dtype != cache->dtype) return KVC_ERR_DTYPE;
+  PrefillKernel kern = pick_prefill_kernel(cache->dtype, cache->head_dim);
+  if (kern == nullptr) return KVC_ERR_UNSUPPORTED;
+  const float scale_log2 = scale * 1.44269504088896340736f;  // log2(e)
+  if (!(scale > 0.f) || !(scale_log2 < INFINITY)) return KVC_ERR_UNSUPPORTED;
+  if (cache->batch == 0) return KVC_OK;
+  if (seq_lens == nullptr || q == nullptr || out == nullptr) return KVC_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(q) % 16) return KVC_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(out) % kvc::elem_bytes(out_dtype)) return KVC_ERR_ALIGN;
+  const int s = kvc::elem_bytes(cache->dtype);
+  // one (sequence, KV head) slice is addressed with 32-bit byte offsets,
+  // plus up to one tile past its end (read back as zeros)
+  if ((static_cast<int64_t>(cache->max_len) + kKTile) * cache->stride_t * s > 0x7fffffffll) return KVC_ERR_SHAPE;
+  const int64_t n_qt = (static_cast<int64_t>(t_q) + kQTile - 1) / kQTile;
+  const int64_t units = static_cast<int64_t>(cache->batch) * cache->n_kv_heads;
+  const int64_t group = n_q_heads / cache->n_kv_heads;
+  const bool xcd_major = units % 8 == 0;
+  const int64_t wgs = xcd_major ? units * group * n_qt : units * group * n_qt;
+  if (wgs > 0x7fffffffll || static_cast<int64_t>(t_q) * n_q_heads > (1ll << 30)) return KVC_ERR_SHAPE;
+
+  PrefillParams p;
+  p.k = static_cast<const char*>(cache->k);
+  p.v = static_cast<const char*>(cache->v);
+  p.sb = cache->stride_b * s;
+  p.sh = cache->stride_h * s;
+  p.st = cache->stride_t * s;
+  p.seq_lens = seq_lens;
+  p.q = static_cast<const char*>(q);
+  p.out = out;
+  p.status = dev_status;
+  p.batch = cache->batch;
+  p.n_q = n_q_heads;
+  p.n_kv = cache->n_kv_heads;
+  p.group = static_cast<int32_t>(group);
+  p.t_q = t_q;
+  p.max_len = cache->max_len;
+  p.n_qt = static_cast<int32_t>(n_qt);
+  p.out_f32 = out_dtype == KVC_F32 ? 1 : 0;
+  p.xcd_major = xcd_major ? 1 : 0;
+  p.scale_log2 = scale_log2;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}

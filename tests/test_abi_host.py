@@ -233,6 +233,30 @@ def test_block_validation_and_workspace():
     assert lib.kvc_block_attn(ctypes.byref(c), FAKE, 3, FAKE, 4, 0.1, FAKE, 0, FAKE, need - 1, 0, None, None) == 6
 
 
+def test_prefill_validation_rejects_before_launch():
+    """kvc_prefill_attn: every case below fails on the host before a launch."""
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    f = lib.kvc_prefill_attn
+    assert f(None, FAKE, 3, FAKE, 4, 0.1, FAKE, 0, None, None) == 1                       # no cache
+    assert f(ctypes.byref(c), FAKE, 0, FAKE, 4, 0.1, FAKE, 0, None, None) == 2             # t_q < 1
+    assert f(ctypes.byref(c), FAKE, 3, FAKE, 3, 0.1, FAKE, 0, None, None) == 5             # 3 % 2 heads
+    assert f(ctypes.byref(c), FAKE, 3, FAKE, 4, 0.1, FAKE, kvc.KVC_F16, None, None) == 3   # out dtype
+    assert f(ctypes.byref(c), FAKE, 3, FAKE, 4, -1.0, FAKE, 0, None, None) == 7            # scale
+    assert f(ctypes.byref(c), FAKE, 3, FAKE, 4, float("inf"), FAKE, 0, None, None) == 7
+    c32 = _desc(kvc, dtype=kvc.KVC_F32)                                                  # fp32 cache
+    assert f(ctypes.byref(c32), FAKE, 3, FAKE, 4, 0.1, FAKE, 0, None, None) == 7
+    c96 = _desc(kvc, head_dim=96, stride_b=2 * 16 * 96, stride_h=16 * 96, stride_t=96)    # head dim 96
+    assert f(ctypes.byref(c96), FAKE, 3, FAKE, 4, 0.1, FAKE, 0, None, None) == 7
+    assert f(ctypes.byref(c), None, 3, FAKE, 4, 0.1, FAKE, 0, None, None) == 1             # no seq_lens
+    assert f(ctypes.byref(c), FAKE, 3, ctypes.c_void_p(4104), 4, 0.1, FAKE, 0, None, None) == 4   # q alignment
+    assert f(ctypes.byref(c), FAKE, 3, FAKE, 4, 0.1, ctypes.c_void_p(4098), 0, None, None) == 4   # out alignment
+    huge = _desc(kvc, max_len=1 << 23, stride_b=2 * (1 << 23) * 128, stride_h=(1 << 23) * 128)
+    assert f(ctypes.byref(huge), FAKE, 3, FAKE, 4, 0.1, FAKE, 0, None, None) == 2          # 32-bit offsets
+    empty = _desc(kvc, batch=0)
+    assert f(ctypes.byref(empty), None, 3, None, 4, 0.1, None, 0, None, None) == 0         # nothing to do
+
+
 def _pdesc(kvc, **kw):
     base = dict(k_pages=64, v_pages=128, block_table=256, batch=2, n_kv_heads=2, page_size=16, head_dim=128,
                 dtype=kvc.KVC_BF16, n_pages=10, pages_per_seq=4, table_stride=4, stride_page=2 * 16 * 128,
