@@ -32,6 +32,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kvc.h"
 #include "kvc_internal.h"
 
@@ -68,13 +70,14 @@ struct Bf16P {
                                                    c, 0, 0, 0);
   }
   // hi keeps the top 16 bits of each weight (a bf16 value), lo the top 16
-  // bits of the exact remainder: hi + lo carries 16 of the 24 bits.
+  // bits of the exact remainder: hi + lo carries 16 of the 24 bits. (The
+  // byte permute takes bytes 2-3 of each word: 0x07060302 over {p1, p0}.)
   __device__ static inline void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
     const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
     const float r0 = p0 - __uint_as_float(u0 & 0xffff0000u);
     const float r1 = p1 - __uint_as_float(u1 & 0xffff0000u);
-    hi = (u0 >> 16) | (u1 & 0xffff0000u);
-    lo = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xffff0000u);
+    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+    lo = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
   }
   __device__ static inline void store(void* base, int64_t i, float x) {
     // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN
@@ -91,12 +94,13 @@ struct F16P {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
                                                   0, 0, 0);
   }
-  // hi = fp16(p) (nearest), lo = fp16(p - hi); the remainder is exact in fp32
+  // hi = fp16(p) rounded toward zero, lo = fp16(p - hi) likewise; the
+  // remainder is exact in fp32 (one packed conversion per pair)
   __device__ static inline void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-    const _Float16 h0 = static_cast<_Float16>(p0), h1 = static_cast<_Float16>(p1);
-    const float r0 = p0 - static_cast<float>(h0), r1 = p1 - static_cast<float>(h1);
-    hi = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
-    lo = __builtin_bit_cast(uint32_t, half2_t{static_cast<_Float16>(r0), static_cast<_Float16>(r1)});
+    const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+    const float r0 = p0 - static_cast<float>(h[0]), r1 = p1 - static_cast<float>(h[1]);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
   }
   __device__ static inline void store(void* base, int64_t i, float x) {
     asm volatile("" : "+v"(x));   // keep the fp32 value: one rounding, to nearest even
@@ -238,7 +242,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     }
   };
 
-  float mrun[2] = {-INFINITY, -INFINITY};   // running maximum (log2 domain), per query
+  // Per query: the reference r (log2 domain) the weights are taken against,
+  // exp2(score - r). It moves only when a score passes r + 8, so weights stay
+  // below 2^8 and the accumulators are rescaled only in those (rare) tiles.
+  constexpr float kLazy = 8.f;
+  float mrun[2] = {-INFINITY, -INFINITY};
   float lrun[2] = {0.f, 0.f};               // this lane's part of the running sum
   f32x4 o[2][ND];                           // O^T: lane holds elements 16db + 4grp + i of query r16
 #pragma unroll
@@ -246,7 +254,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
     for (int db = 0; db < ND; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int t) {
+  auto compute = [&](int t, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;   // the tile crosses the diagonal
     f32x4 s[2][4];                          // S^T: lane holds keys 16kb + 4grp + i of query r16
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -260,45 +269,44 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) s[qb][kb] = ET::mfma(a, qf[qb][c], s[qb][kb]);
       }
-    const bool masked = (t + 1) * kKTile > wmin;       // wave-uniform: the tile crosses the diagonal
+    const float c = p.scale_log2;
     u32x4 phi[2][2], plo[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
+      float mx = -INFINITY;                  // raw scores: the scale is positive
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = s[qb][kb][i] * p.scale_log2;
-          if (masked) x = (t * kKTile + 16 * kb + 4 * grp + i < lim[qb]) ? x : -INFINITY;
-          s[qb][kb][i] = x;
-          mx = fmaxf(mx, x);
+          if constexpr (kMask)
+            s[qb][kb][i] = (t * kKTile + 16 * kb + 4 * grp + i < lim[qb]) ? s[qb][kb][i] : -INFINITY;
+          mx = fmaxf(mx, s[qb][kb][i]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(mrun[qb], mx);
-      const float alpha = mrun[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[qb] - mn);
-      mrun[qb] = mn;
-      lrun[qb] *= alpha;
+      if (__any(mx * c > mrun[qb] + kLazy)) {   // wave-uniform; every tile at first
+        mx = fmaxf(mx, __shfl_xor(mx, 16));    // the query's maximum over its four lanes
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * c;
+        const bool up = ms > mrun[qb] + kLazy;   // the four lanes of a query agree
+        const float alpha = !up ? 1.f : (mrun[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[qb] - ms));
+        mrun[qb] = up ? ms : mrun[qb];
+        lrun[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha;
-      float e[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[kb][i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - mn);   // masked: exp2(-inf) = 0
-          lrun[qb] += e[kb][i];
-        }
+          for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha;
+      }
+      const float nr = -mrun[qb];
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
+        float e[8];                          // slots 8grp .. 8grp+7 of this 32-key chunk
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          e[j] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * kc + (j >> 2)][j & 3], c, nr));   // masked: 0
+          lrun[qb] += e[j];
+        }
         uint32_t hi[4], lo[4];
-        ET::split(e[2 * kc][0], e[2 * kc][1], hi[0], lo[0]);
-        ET::split(e[2 * kc][2], e[2 * kc][3], hi[1], lo[1]);
-        ET::split(e[2 * kc + 1][0], e[2 * kc + 1][1], hi[2], lo[2]);
-        ET::split(e[2 * kc + 1][2], e[2 * kc + 1][3], hi[3], lo[3]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ET::split(e[2 * w], e[2 * w + 1], hi[w], lo[w]);
         phi[qb][kc] = u32x4{hi[0], hi[1], hi[2], hi[3]};
         plo[qb][kc] = u32x4{lo[0], lo[1], lo[2], lo[3]};
       }
@@ -316,14 +324,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
       }
   };
 
-  load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
+  // Tiles below t_split hold no key past any query's limit; the others are
+  // computed with the mask. (Two loops, one kind of tile each, so that each
+  // is compiled on its own.)
+  const int t_split = (c0 + i0 + 1) / kKTile;
+  auto step = [&](int t, auto mask_tag) {
     __syncthreads();                        // every wave is done with the previous tile
     store_tile();
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(t + 1);  // in flight while this tile is computed
-    if (wactive && t * kKTile < wlim) compute(t);
-  }
+    if (wactive && t * kKTile < wlim) compute(t, mask_tag);
+  };
+  load_tile(0);
+  int t = 0;
+  for (; t < t_split; ++t) step(t, std::false_type{});
+  for (; t < n_tiles; ++t) step(t, std::true_type{});
   if (!wactive) return;
 
 #pragma unroll
