@@ -58,6 +58,10 @@ def _parse():
     ap.add_argument("--block-q", type=int, default=0,
                     help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
                          "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="time a prompt prefill of N tokens per sequence on the config's layer shape instead "
+                         "of the decode step: per layer kvc_prefill_fill + kvc_prefill_attn (causal attention "
+                         "on the matrix cores); one JSON line in TFLOP/s")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -531,6 +535,85 @@ def _run_config(name, args, with_cpu):
     return res
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense matrix-core peak per 16-bit type
+
+
+def _run_prefill(args) -> dict:
+    """A prompt prefill on the config's layer shape: every sequence starts
+    empty and takes --prefill N tokens. Per layer, kvc_prefill_fill writes the
+    prompt's K/V into that layer's cache and kvc_prefill_attn computes the
+    causal attention of its N queries. FLOPs count q.K and P.V (2 each per
+    query, key and head-dim element) over the keys each query sees,
+    N(N+1)/2 per (sequence, query head)."""
+    import torch
+    import kv_cache_append_amd as kvc
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    if cfg.dtype not in MFMA_PEAK_TFLOPS:
+        raise SystemExit(f"--prefill needs a 16-bit cache ({cfg.name} is {cfg.dtype})")
+    B, hq, hkv, d, n_layers, t = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_layers, args.prefill
+    dev = torch.device("cuda:0")
+    tdt = synth.DTYPES[cfg.dtype]
+    k = [torch.empty((B, hkv, t, d), dtype=tdt, device=dev) for _ in range(n_layers)]
+    v = [torch.empty_like(x) for x in k]
+    k_src = synth.normal((B, hkv, t, d), cfg.dtype, args.seed, cfg.name, "prefill", "K", device=dev)
+    v_src = synth.normal((B, hkv, t, d), cfg.dtype, args.seed, cfg.name, "prefill", "V", device=dev)
+    q = synth.normal((B, t, hq, d), cfg.dtype, args.seed, cfg.name, "prefill", "q", device=dev)
+    out = torch.empty_like(q)
+    seq = torch.zeros(B, dtype=torch.int32, device=dev)
+    descs = [kvc.cache_desc(k[i], v[i]) for i in range(n_layers)]
+
+    def fill_all():
+        for i in range(n_layers):
+            kvc.prefill_fill(k[i], v[i], seq, k_src, v_src)
+
+    def attn_all():
+        for i in range(n_layers):
+            kvc.prefill_attn(k[i], v[i], seq, q, out, desc=descs[i])
+
+    for _ in range(args.warmup):
+        fill_all()
+        attn_all()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for s_ in range(args.steps):
+        fill_all()
+        attn_all()
+        ev[s_ + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms_total = ev[0].elapsed_time(ev[-1])
+    reps = 3                                    # attention launches alone, for the roofline
+    e0.record()
+    for _ in range(reps):
+        attn_all()
+    e1.record()
+    torch.cuda.synchronize()
+    launch_ms = e0.elapsed_time(e1) / (reps * n_layers)
+    flops_launch = 4.0 * d * hq * B * t * (t + 1) / 2
+    ms_step = ms_total / args.steps
+    value = flops_launch * n_layers / (ms_step * 1e-3) / 1e12
+    achieved = flops_launch / (launch_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    srt = sorted(step_ms)
+    return {
+        "metric": "prompt-prefill causal attention TFLOP/s (q.K and P.V FLOPs / step time)",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "step_ms": {"median": srt[len(srt) // 2], "min": srt[0], "max": srt[-1]},
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) prompt q/K/V rounded to the cache dtype; no dataset)",
+        "config": {"workload": f"{cfg.name} prompt prefill", "batch": B, "prompt_tokens": t, "n_layers": n_layers,
+                   "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
+                   "step": "per layer kvc_prefill_fill + kvc_prefill_attn"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "launch_us": launch_ms * 1e3,
+                     "flops_per_launch": flops_launch},
+    }
+
+
 def main():
     args = _parse()
     if args.pmc_summary:
@@ -544,6 +627,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.prefill > 0:
+        print(json.dumps(_run_prefill(args)), flush=True)
+        return
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
