@@ -427,8 +427,8 @@ extern "C" kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t
   const int64_t n_qt = (static_cast<int64_t>(t_q) + kQTile - 1) / kQTile;
   const int64_t units = static_cast<int64_t>(cache->batch) * cache->n_kv_heads;
   const int64_t group = n_q_heads / cache->n_kv_heads;
-  const bool xcd_major = units % 8 == 0;
-  const int64_t wgs = xcd_major ? units * group * n_qt : units * group * n_qt;
+  const bool xcd_major = units % 8 == 0;                // ids map to units XCD by XCD (see the kernel)
+  const int64_t wgs = units * group * n_qt;
   if (wgs > 0x7fffffffll || static_cast<int64_t>(t_q) * n_q_heads > (1ll << 30)) return KVC_ERR_SHAPE;
 
   PrefillParams p;
