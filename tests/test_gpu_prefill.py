@@ -128,3 +128,22 @@ def test_prefill_full_size_sampled_rows(gpu):
         ref = oracle.chunk_attention(case.q_host[b:b + 1, i:i + 1], case.kb_host[b:b + 1], case.vb_host[b:b + 1],
                                      np.array([i]))[0, 0, h]
         assert np.abs(got[b, i, h].double().cpu().numpy() - ref).max() <= TOL["bf16"], (b, i, h)
+
+
+def test_prefill_token_major_cache_equals_head_major_bitwise(gpu):
+    """A token-major cache ([B, T, H_kv, D] storage seen as [B, H_kv, T, D]
+    through strides) gives the same bits as the head-major cache: only the
+    addressing differs."""
+    case = BlockCase(batch=2, n_q=8, n_kv=2, d=128, dtype="bf16", lengths=[30, 200], t_q=150, tag="pftm")
+    case.fill()
+    ref = _run(case)
+    b, h, t, d = case.k.shape
+    k_tm = torch.full((b, t, h, d), float("nan"), dtype=case.k.dtype, device=gpu).permute(0, 2, 1, 3)
+    v_tm = torch.full_like(k_tm, float("nan"))
+    k_tm.copy_(case.k)
+    v_tm.copy_(case.v)
+    out = torch.full_like(ref, float("nan"))
+    kvc.prefill_attn(k_tm, v_tm, case.seq_lens, case.q, out)
+    torch.cuda.synchronize()
+    assert k_tm.stride(2) == h * d
+    assert torch.equal(out, ref)
