@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
   const int c0 = p.seq_lens[b];
   const int i0 = qt * kQTile;
   const int nq = min(kQTile, p.t_q - i0);  // queries of this tile
-  if (c0 < 0 || c0 + p.t_q > p.max_len) {   // the block does not fit: zero rows, flagged once
+  if (c0 < 0 || c0 > p.max_len - p.t_q) {   // the block does not fit (no overflow): zero rows, flagged once
     if (threadIdx.x == 0 && qt == 0 && hg == 0 && g == 0 && p.status != nullptr)
       atomicOr(p.status, c0 < 0 ? KVC_DEVERR_BADLEN : KVC_DEVERR_CAPACITY);
     for (int t = threadIdx.x; t < nq * D; t += blockDim.x) {

@@ -92,6 +92,12 @@ def test_prefill_blocks_that_do_not_fit_are_zero_and_flagged(gpu):
     assert int(status.item()) == kvc.DEVERR_CAPACITY | kvc.DEVERR_BADLEN
     assert np.abs(got[0] - ref).max() <= TOL["bf16"]
     assert (got[1] == 0).all() and (got[2] == 0).all()
+    # a length whose sum with t_q passes 2^31 is a capacity error too
+    status.zero_()
+    case.seq_lens.copy_(torch.tensor([10, 2**31 - 5, 20], dtype=torch.int32))
+    got = _run(case, status=status).double().cpu().numpy()
+    assert int(status.item()) == kvc.DEVERR_CAPACITY
+    assert (got[1] == 0).all() and np.abs(got[0] - ref).max() <= TOL["bf16"]
 
 
 def test_prefill_out_in_cache_dtype_is_rounded_fp32(gpu):
