@@ -350,32 +350,29 @@ __device__ inline SeqInfo seq_info(const DecodeParams& p, int b) {
   const int c = c0 < 0 ? 0 : c0;
   if (c0 < 0) si.flags |= KVC_DEVERR_BADLEN;
   si.append_row = -1;
-  int n;
+  // lengths plus new tokens are summed in 64 bits: a length near 2^31 is a
+  // capacity case, not a wrapped negative count
+  const int add = p.k_new != nullptr ? 1 : (p.block ? p.t_q : p.n_pending);
+  const int64_t n64 = static_cast<int64_t>(c) + add;
   if (p.ring) {                   // sliding window: no capacity limit, the ring wraps
     if (c0 >= 0 && p.k_new != nullptr) si.append_row = c0 % p.max_len;
-    n = c0 < 0 ? 0 : min(c0 + (p.k_new != nullptr ? 1 : p.n_pending), p.max_len);
+    const int n = c0 < 0 ? 0 : static_cast<int>(min(n64, static_cast<int64_t>(p.max_len)));
     si.n = n;
-    si.newest = c0 < 0 ? -1 : (c0 + (p.k_new != nullptr ? 1 : p.n_pending) - 1) % p.max_len;
+    si.newest = c0 < 0 ? -1 : static_cast<int>((n64 - 1) % p.max_len);
     return si;
   }
   if (p.block) {                  // the whole block must fit: else flagged, zero rows
-    n = c0 + p.t_q;
-    if (c0 >= 0 && n > p.max_len) si.flags |= KVC_DEVERR_CAPACITY;
-    si.n = (c0 < 0 || n > p.max_len) ? 0 : n;
+    if (c0 >= 0 && n64 > p.max_len) si.flags |= KVC_DEVERR_CAPACITY;
+    si.n = (c0 < 0 || n64 > p.max_len) ? 0 : static_cast<int>(n64);
     si.newest = si.n - 1;
     return si;
   }
   if (p.k_new != nullptr) {
     if (c0 >= 0 && c0 < p.max_len) si.append_row = c0;
     else si.flags |= KVC_DEVERR_CAPACITY;
-    n = c + 1;
-  } else {
-    n = c + p.n_pending;
   }
-  if (n > p.max_len) {
-    n = p.max_len;
-    si.flags |= KVC_DEVERR_CAPACITY;
-  }
+  int n = static_cast<int>(min(n64, static_cast<int64_t>(p.max_len)));
+  if (n64 > p.max_len) si.flags |= KVC_DEVERR_CAPACITY;
   si.n = n;
   si.newest = n - 1;
   return si;

@@ -138,6 +138,14 @@ def test_capacity_clamp_sets_flag_and_never_reads_past_cache(gpu):
     assert int(status.item()) == kvc.DEVERR_CAPACITY
     ref = oracle.decode_attention(case.q_host, case.k.cpu(), case.v.cpu(), np.array([t_max]), n_pending=0)
     assert np.abs(out.double().cpu().numpy() - ref).max() <= TOL["fp16"]
+    # a length near 2^31 (its sum with n_pending passes int32) clamps the same way
+    status.zero_()
+    huge = torch.full_like(case.seq_lens, 2**31 - 1)
+    out2 = torch.empty_like(out)
+    kvc.decode_attn(case.k, case.v, huge, case.q, out2, ws, n_pending=1, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kvc.DEVERR_CAPACITY
+    assert torch.equal(out2, out)
 
 
 def test_negative_length_is_flagged_and_treated_as_empty(gpu):
