@@ -251,7 +251,10 @@ kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens,
  *
  * The (query, head) pairs of a KV head are processed like the query heads of
  * a larger group, so K/V rows are streamed once per block of up to 8 pairs;
- * the call suits short blocks (verify steps, small chunks). A sequence whose
+ * this suits short blocks (verify steps, small chunks). Blocks of t_q >= 8
+ * with t_q * (n_q_heads / n_kv_heads) >= 32 on fp16/bf16 caches with head_dim
+ * 64 or 128 run on the kernel of kvc_prefill_attn instead (the same result
+ * bits as that call; n_splits is then unused, the workspace rules stand). A sequence whose
  * block does not fit (seq_lens[b] < 0, or seq_lens[b] + t_q > max_len) gets
  * zero rows and KVC_DEVERR_BADLEN / KVC_DEVERR_CAPACITY. Host-side errors as
  * for kvc_decode_attn, and KVC_ERR_SHAPE for t_q < 1.

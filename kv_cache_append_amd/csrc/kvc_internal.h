@@ -66,6 +66,14 @@ kvc_status_t check_qcache(const kvc_qcache_t* c, bool for_decode);
 // cache descriptor, for the split heuristic and the workspace layout only.
 kvc_cache_t qcache_view(const kvc_qcache_t* c);
 
+// The matrix-core prefill kernel (kvc_prefill.hip): whether it is built for
+// this dtype and head dim, and its launch (arguments as kvc_prefill_attn,
+// already validated except for what the kernel itself needs).
+bool prefill_supported(int32_t dtype, int32_t head_dim);
+kvc_status_t launch_prefill(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q, const void* q,
+                            int32_t n_q_heads, float scale, void* out, int32_t out_dtype, uint32_t* dev_status,
+                            hipStream_t stream);
+
 }  // namespace kvc
 
 #endif  // KVC_INTERNAL_H_

@@ -404,6 +404,14 @@ PrefillKernel pick_prefill_kernel(int32_t dtype, int32_t d) {
 
 }  // namespace
 
+bool kvc::prefill_supported(int32_t dtype, int32_t head_dim) { return pick_prefill_kernel(dtype, head_dim) != nullptr; }
+
+kvc_status_t kvc::launch_prefill(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q, const void* q,
+                                 int32_t n_q_heads, float scale, void* out, int32_t out_dtype, uint32_t* dev_status,
+                                 hipStream_t stream) {
+  return kvc_prefill_attn(cache, seq_lens, t_q, q, n_q_heads, scale, out, out_dtype, dev_status, stream);
+}
+
 extern "C" kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
                                          const void* q, int32_t n_q_heads, float scale, void* out, int32_t out_dtype,
                                          uint32_t* dev_status, hipStream_t stream) {

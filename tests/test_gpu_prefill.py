@@ -153,3 +153,20 @@ def test_prefill_token_major_cache_equals_head_major_bitwise(gpu):
     torch.cuda.synchronize()
     assert k_tm.stride(2) == h * d
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("hq,hkv,t_q", [(8, 2, 16), (32, 8, 8), (8, 8, 40)])
+def test_long_blocks_of_block_attn_run_on_the_prefill_kernel(gpu, hq, hkv, t_q):
+    """kvc_block_attn hands blocks of >= 8 queries with >= 32 (query, head)
+    pairs per KV head to the prefill kernel: the same bits as
+    kvc_prefill_attn, and within the bar of the oracle."""
+    case = BlockCase(batch=2, n_q=hq, n_kv=hkv, d=128, dtype="bf16", lengths=[70, 1000], t_q=t_q,
+                     tag=f"pfroute{hq}{hkv}{t_q}")
+    case.fill()
+    direct = _run(case)
+    routed = torch.full_like(direct, float("nan"))
+    ws = kvc.block_workspace(case.k, case.v, hq, t_q)
+    kvc.block_attn(case.k, case.v, case.seq_lens, case.q, routed, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(routed, direct)
+    assert np.abs(routed.double().cpu().numpy() - case.oracle()).max() <= TOL["bf16"]
