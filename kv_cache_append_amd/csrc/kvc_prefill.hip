@@ -261,6 +261,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Raised wave priority for the score products, back to normal for the
+    // softmax: measured 1-2.5 % faster (the other wave's arithmetic then
+    // fills the matrix cores' gaps rather than the reverse).
+    __builtin_amdgcn_s_setprio(2);
     // K slices of block kb + 1 are requested while block kb's products run
     u32x4 ka[2][NC];
 #pragma unroll
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * NC, 0);
     const float c = p.scale_log2;
+    __builtin_amdgcn_s_setprio(0);
     u32x4 phi[2][2], plo[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
