@@ -2,11 +2,13 @@
 
 One step is the whole per-layer incremental-decode path over all L layers of
 one batch: for every layer kvc_decode_step (the new token's k, v written into
-slot T_b and every query head attending T_b + 1 tokens, one launch), then one
-kvc_seq_lens_advance. The value is KV bytes read per step, 2*L*H_kv*D*s*
-sum_b(T_b + 1), divided by the step time, with every input already resident in
-HBM. seq_lens is reset to the workload's lengths before the timed steps, so
-step k attends T_b + k + 1 tokens; the byte count follows that exactly.
+slot T_b and every query head attending T_b + 1 tokens, one launch), the last
+layer's launch (kvc_decode_step_advance) also writing seq_lens + 1 for the next
+step into a second length array (steps alternate the two arrays). The value is
+KV bytes read per step, 2*L*H_kv*D*s*sum_b(T_b + 1), divided by the step time,
+with every input already resident in HBM. The lengths are reset to the
+workload's before the timed steps, so step k attends T_b + k + 1 tokens; the
+byte count follows that exactly.
 
 Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -28,7 +30,9 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attention achieved HBM GB/s (KV bytes read/step time) and % of peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 DOMINANT_KERNEL = "decode_kernel"
-KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_append_amd", "csrc", "kvc_kernels.hip")
+# the decode kernels' sources (counter records are tied to their code)
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_append_amd", "csrc", f)
+                  for f in ("kvc_kernels.hip", "kvc_wide.hip", "kvc_tile.h")]
 
 
 def _parse():
@@ -37,8 +41,9 @@ def _parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gqa_8b")
-    ap.add_argument("--secondary", default="ragged_long",
-                    help="second workload measured in the same run ('none' to skip)")
+    ap.add_argument("--also", default="ragged_long,mha_7b,gqa_70b,mqa_70b",
+                    help="comma-separated workloads measured in the same run after --config, each with its own "
+                         "value, step time and roofline in the line's 'workloads' list ('none' to skip)")
     ap.add_argument("--splits", type=int, default=0, help="decode splits (0 = library choice)")
     ap.add_argument("--paged", type=int, default=0,
                     help="page size P: time the decode step on page pools through a page table "
@@ -96,10 +101,17 @@ class Workload:
         self.kvc = kvc
         self.lib = kvc.load()
         dev = torch.device("cuda:0")
+        # device status word (KVC_DEVERR_* bits) passed to every call of the run
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.lengths = cfg.lengths(seed)
         self.t_max = ring if ring else int(self.lengths.max()) + margin_tokens + 1
         L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
         tdt = synth.DTYPES[cfg.dtype]
+        # contiguous 16-bit caches with 16..128 (query, head) pairs per KV head
+        # run on the wide-group kernel (long query blocks on the prefill kernel)
+        pairs = cfg.group * max(block_q, 1)
+        self.wide = (not (page or ring or quant) and cfg.dtype in ("fp16", "bf16") and cfg.head_dim in (64, 128)
+                     and 16 <= pairs <= 128 and not (block_q >= 8 and pairs >= 32))
         if quant:
             self._init_quant(cfg, seed, splits, dev, tdt)
             return
@@ -134,6 +146,12 @@ class Workload:
                                   for l in range(L)])
         self.out = torch.empty((L,) + qs, dtype=torch.float32, device=dev)
         self.seq_lens = self.lengths.to(dev)
+        # The decode step on contiguous 16-bit-or-fp32 caches ends with
+        # kvc_decode_step_advance: the last layer's launch also writes the next
+        # step's lengths into the other of two arrays (no separate advance
+        # launch), so consecutive steps alternate the arrays.
+        self.fused_advance = not (block_q or page or ring or quant)
+        self.seq_lens_alt = torch.empty_like(self.seq_lens)
         if page:
             self.descs = [kvc.paged_desc(self.k[l], self.v[l], self.table) for l in range(L)]
         else:
@@ -205,14 +223,19 @@ class Workload:
 
     def reset_lengths(self):
         self.seq_lens.copy_(self.lengths.to(self.seq_lens.device))
+        if hasattr(self, "seq_lens_alt"):
+            self.seq_lens_alt.copy_(self.seq_lens)
 
-    def layers(self, stream_handle, attn_only: bool = False):
+    def layers(self, stream_handle, attn_only: bool = False, lens_in=None, lens_out=None):
         """Enqueue the per-layer decode launches of one step (lengths unchanged).
         attn_only (quantised cache): only the decode launch of each layer, which
-        reads the same bytes as in the step (the slot it appends is attended)."""
+        reads the same bytes as in the step (the slot it appends is attended).
+        lens_in / lens_out: the step's length array and, for the last layer's
+        kvc_decode_step_advance, the array the next step's lengths go to."""
         lib, cfg = self.lib, self.cfg
         vp = ctypes.c_void_p
-        seq = vp(self.seq_lens.data_ptr())
+        seq = vp((self.seq_lens if lens_in is None else lens_in).data_ptr())
+        stat = vp(self.status.data_ptr())
         ws, wsb = vp(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel())
         sb, sh = self.k_new.stride(1), self.k_new.stride(2)
         st = vp(stream_handle)
@@ -222,9 +245,9 @@ class Workload:
             for l in range(cfg.n_layers):
                 d = ctypes.byref(self.descs[l])
                 rc = lib.kvc_prefill_fill(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()),
-                                          ks[1], ks[2], ks[3], n, None, st)
+                                          ks[1], ks[2], ks[3], n, stat, st)
                 rc = rc or lib.kvc_block_attn(d, seq, n, vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
-                                              vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
+                                              vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, stat, st)
                 if rc:
                     raise RuntimeError(f"libkvc returned {rc} at layer {l}")
             return
@@ -232,7 +255,7 @@ class Workload:
             for l in range(cfg.n_layers):
                 rc = lib.kvc_quant_decode_attn(ctypes.byref(self.descs[l]), seq, 1, vp(self.q[l].data_ptr()),
                                                cfg.n_q_heads, self.scale, vp(self.out[l].data_ptr()), 0, ws, wsb,
-                                               self.splits, None, st)
+                                               self.splits, stat, st)
                 if rc:
                     raise RuntimeError(f"libkvc returned {rc} at layer {l}")
             return
@@ -241,14 +264,26 @@ class Workload:
                    lib.kvc_quant_decode_step if self.quant else lib.kvc_decode_step)
         for l in range(cfg.n_layers):
             d = ctypes.byref(self.descs[l])
-            rc = step_fn(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
-                                     vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
-                                     vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, None, st)
+            if lens_out is not None and l == cfg.n_layers - 1:
+                rc = lib.kvc_decode_step_advance(d, seq, vp(lens_out.data_ptr()), vp(self.k_new[l].data_ptr()),
+                                                 vp(self.v_new[l].data_ptr()), sb, sh, vp(self.q[l].data_ptr()),
+                                                 cfg.n_q_heads, self.scale, vp(self.out[l].data_ptr()), 0, ws, wsb,
+                                                 self.splits, stat, st)
+            else:
+                rc = step_fn(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()), sb, sh,
+                             vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
+                             vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, stat, st)
             if rc:
                 raise RuntimeError(f"libkvc returned {rc} at layer {l}")
 
-    def step(self, stream_handle):
-        """Enqueue one decode step: every layer, then seq_lens += 1."""
+    def step(self, stream_handle, parity: int = 0):
+        """Enqueue one decode step: every layer, then seq_lens += 1 (in the
+        last layer's launch when fused_advance: step `parity` 0 reads
+        seq_lens and writes seq_lens_alt, parity 1 the reverse)."""
+        if self.fused_advance:
+            a, b = (self.seq_lens, self.seq_lens_alt) if parity % 2 == 0 else (self.seq_lens_alt, self.seq_lens)
+            self.layers(stream_handle, lens_in=a, lens_out=b)
+            return
         self.layers(stream_handle)
         seq = ctypes.c_void_p(self.seq_lens.data_ptr())
         if self.lib.kvc_seq_lens_advance(seq, self.cfg.batch, max(self.block_q, 1), ctypes.c_void_p(stream_handle)):
@@ -282,38 +317,55 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     import torch
 
     stream = torch.cuda.current_stream()
-    for _ in range(max(warmup, 1)):
-        w.step(stream.cuda_stream)
+    for i in range(max(warmup, 1)):
+        w.step(stream.cuda_stream, i)
     torch.cuda.synchronize()
-    graph = None
+    # one HIP graph per step; with the fused advance two, one per direction
+    # of the length arrays, replayed alternately
+    graphs = None
     if use_graph:
         w.reset_lengths()
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            w.step(torch.cuda.current_stream().cuda_stream)
+        graphs = []
+        for parity in range(2 if w.fused_advance else 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                w.step(torch.cuda.current_stream().cuda_stream, parity)
+            graphs.append(g)
         torch.cuda.synchronize()
-        for _ in range(max(warmup, 1)):
-            graph.replay()
+        for i in range(max(warmup, 1)):
+            graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
-    # timed region: exactly `steps` steps from the reset lengths
+
+    def run_step(i):
+        if graphs is not None:
+            graphs[i % len(graphs)].replay()
+        else:
+            w.step(stream.cuda_stream, i)
+
+    # timed region: exactly `steps` steps from the reset lengths, back to back
     w.reset_lengths()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     e0.record()
     for i in range(steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            w.step(stream.cuda_stream)
-        marks[i].record()
+        run_step(i)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = e0.elapsed_time(e1)
-    step_ms = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, steps)]
+    # each step's own time, from a second pass over the same steps with an
+    # event after every step (kept out of the timed region)
+    w.reset_lengths()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
+        run_step(i)
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
     # Average duration of one decode launch: the L per-layer launches alone
     # (lengths held, so every launch reads the same bytes), `reps` passes back
     # to back, bracketed by HIP events on the launching stream.
@@ -347,7 +399,7 @@ def _kernel_fingerprint() -> str:
     """SHA-256 of the kernel source with comments and whitespace removed, so
     that counter records stay tied to the code and not to its comments."""
     import re
-    src = open(KERNEL_SOURCE).read()
+    src = "".join(open(p).read() for p in KERNEL_SOURCES)
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = re.sub(r"\s+", " ", src).strip()
@@ -379,7 +431,8 @@ def _pmc_summary(fetch_csv: str, write_csv: str, out_path: str, args):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = "decode" if "decode_kernel" in name else ("copy" if "copyBuffer" in name else None)
+            key = ("decode" if ("decode_kernel" in name or "wide_decode_kernel" in name) else
+                   "copy" if "copyBuffer" in name else None)
             if key:
                 out[key].append(float(r["Counter_Value"]))
         return out
@@ -398,7 +451,7 @@ def _pmc_summary(fetch_csv: str, write_csv: str, out_path: str, args):
     algo = 2 * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes * (int(cfg.lengths(args.seed).long().sum()) + cfg.batch)
     rec = {
         "workload": args.config,
-        "kernel": "decode_kernel",
+        "kernel": "wide_decode_kernel" if cfg.group >= 16 else "decode_kernel",
         "kernel_code_sha256": _kernel_fingerprint(),
         "hbm_bytes_per_launch": int(round(fetch + write)),
         "fetch_bytes_per_launch": int(round(fetch)),
@@ -414,6 +467,24 @@ def _pmc_summary(fetch_csv: str, write_csv: str, out_path: str, args):
     print(json.dumps(rec))
 
 
+def _host_cpu() -> dict:
+    """Cores this process may run on and the host CPU's model name."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cores": int(cores), "cpu_model": model}
+
+
 def _cpu_baseline(cfg, seconds: float, seed: int):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     whole layers of (sequence, KV head) units at the workload's shapes, timed
@@ -422,11 +493,15 @@ def _cpu_baseline(cfg, seconds: float, seed: int):
     import torch
     import synth
     import oracle
+    host = _host_cpu()
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas_threads = 1
+    # the oracle's loop is one Python thread; its matrix-vector products run on
+    # the BLAS pool, which cannot use more cores than the process may run on
+    threads = max(1, min(blas_threads, host["affinity_cores"]))
     lengths = cfg.lengths(seed)
     done_bytes, units, t_spent = 0, 0, 0.0
     b = 0
@@ -455,9 +530,14 @@ def _cpu_baseline(cfg, seconds: float, seed: int):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
+        "affinity_cores": host["affinity_cores"],
+        "cpu_model": host["cpu_model"],
+        "blas_threads": int(blas_threads),
         "sample": f"{b} (sequence, layer) slices of {cfg.name} ({b / (cfg.batch * cfg.n_layers):.2f} steps), all "
                   f"{cfg.n_kv_heads} KV heads each ({units} (sequence, KV head) units, {cfg.group} query heads "
-                  f"each, {done_bytes / 1e9:.3f} GB of K+V) in {t_spent:.1f} s; numpy fp64, BLAS threads={threads}",
+                  f"each, {done_bytes / 1e9:.3f} GB of K+V) in {t_spent:.1f} s; numpy fp64 on one Python thread, its matrix-vector "
+                  f"products on {threads} BLAS threads ({host['affinity_cores']} cores in the process affinity mask, "
+                  f"{host['cpu_model']})",
     }
 
 
@@ -478,6 +558,8 @@ def _run_config(name, args, with_cpu):
     import kv_cache_append_amd as kvc
     launch_read = (kvc.stream_read_launch_rate(int(launch_bytes) // 16 * 16, n_bytes=args.stream_gib << 30)
                    if args.stream_gib > 0 else None)
+    torch.cuda.synchronize()
+    status = int(w.status.item())          # KVC_DEVERR_* bits of every call of the run (0 expected)
     step_sorted = sorted(step_ms)
     kv = w.kv_bytes(args.steps)
     gbs = kv / (ms_total / 1e3) / 1e9
@@ -485,6 +567,7 @@ def _run_config(name, args, with_cpu):
     lens = w.lengths
     res = {
         "value": round(gbs, 2),
+        "unit": "GB/s",
         "ms_per_step": round(ms_total / args.steps, 5),
         # each step's own time (HIP events between steps); steps later in the
         # run attend slightly more tokens
@@ -495,6 +578,7 @@ def _run_config(name, args, with_cpu):
         "steps_per_s": round(args.steps / (ms_total / 1e3), 2),
         "tokens_per_s": round(cfg.batch * args.steps / (ms_total / 1e3), 1),
         "kv_bytes_per_step": kv // args.steps,
+        "status": status,
         "dtype": cfg.dtype,
         "config": {
             "workload": name, "description": cfg.description, "layers": cfg.n_layers, "batch": cfg.batch,
@@ -516,7 +600,9 @@ def _run_config(name, args, with_cpu):
                        "launch per layer)" if args.ring else
                        "decode_kernel on 8-bit codes (kvc_quant_decode_attn, timed alone; the step adds one "
                        "quantising append launch per layer)" if args.quant else
-                       "decode_kernel (kvc_decode_step: append + attention + merge, one launch per layer)"),
+                       ("wide_decode_kernel" if w.wide else "decode_kernel") +
+                       " (kvc_decode_step: append + attention + merge, one launch per layer; the last layer's "
+                       "launch also advances the lengths)"),
             "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),
@@ -666,16 +752,26 @@ def main():
         "tokens_per_s": main_res["tokens_per_s"],
         "wall_ms_per_step": main_res["wall_ms_per_step"],
         "kv_bytes_per_step": main_res["kv_bytes_per_step"],
+        "status": main_res["status"],
         "roofline": main_res["roofline"],
     }
     if "cpu_baseline" in main_res:
         line["cpu_baseline"] = main_res["cpu_baseline"]
-    if args.secondary and args.secondary != "none":
-        sec = _run_config(args.secondary, args, with_cpu=False)
-        line["secondary"] = {k: sec[k] for k in ("value", "ms_per_step", "step_ms", "pct_of_peak", "steps_per_s",
-                                                   "tokens_per_s", "kv_bytes_per_step", "dtype", "config",
-                                                   "roofline")}
+    # the other workloads, each on its own resident caches (freed in between)
+    others = [x for x in (args.also or "").split(",") if x and x != "none" and x != args.config]
+    if others:
+        line["workloads"] = []
+        for name in others:
+            r = _run_config(name, args, with_cpu=False)
+            line["workloads"].append({"workload": name, **{k: r[k] for k in (
+                "value", "unit", "ms_per_step", "step_ms", "pct_of_peak", "steps_per_s", "tokens_per_s",
+                "kv_bytes_per_step", "status", "dtype", "config", "roofline")}})
+    bad = [(e["config"]["workload"] if "config" in e else "?", e["status"])
+           for e in [main_res] + line.get("workloads", []) if e["status"]]
     print(json.dumps(line), flush=True)
+    if bad:
+        print(f"device status bits set during the run: {bad}", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

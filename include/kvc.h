@@ -18,8 +18,9 @@
  *     device pointer (HBM) on the current HIP device.
  *   - The caller owns every buffer (caches, q, out, workspace, seq_lens,
  *     status word). The library never allocates or frees device memory, never
- *     synchronises the stream, and keeps no mutable global state; calls on
- *     different streams are independent.
+ *     synchronises the stream, and keeps no mutable global state apart from
+ *     one test setting (kvc_debug_set_merge_spin_limit); calls on different
+ *     streams are independent.
  *   - Work is enqueued on `stream` (NULL = the null stream) and returns
  *     before it runs. Results are visible after the stream is synchronised.
  *   - Strides are in elements. The head-dimension axis (D) is contiguous.
@@ -68,7 +69,8 @@ typedef enum kvc_status {
 #define KVC_DEVERR_PAGE     8u  /* a page-table entry is not an index into the page pool: those rows were
                                    not written (append/fill) or read as zeros (decode: outputs invalid) */
 #define KVC_DEVERR_SYNC     4u  /* a split merge gave up waiting for another workgroup (never expected;
-                                   the outputs of that call are not valid) */
+                                   the outputs of that call are not valid; the workspace stays usable:
+                                   see kvc_decode_workspace_bytes) */
 
 /*
  * One layer's preallocated cache: K and V each [batch, n_kv_heads, max_len,
@@ -139,13 +141,18 @@ kvc_status_t kvc_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens,
  * arguments.
  *
  * Layout and lifetime: uint32 ready flags (one per sequence, KV head, block
- * of query heads and split), then fp32 per-split partial results. The
- * caller zero-fills the workspace once after allocating it; every decode
- * call leaves the flags zero again, so the workspace serves any number of
- * later calls with the same batch, n_kv_heads, n_q_heads and split count
- * (any lengths, any layer) without clearing. Where those change, the region
- * layout moves: zero-fill the workspace again first (or keep one workspace
- * per geometry). Calls that share a workspace must not run concurrently.
+ * of query heads and split; the last split's word of each block holds that
+ * block's epoch, a count of its merges), then fp32 per-split partial
+ * results. The caller zero-fills the workspace once after allocating it. A
+ * call's publishing splits raise their flags to epoch + 1 and its merging
+ * split waits for exactly that value, then advances the epoch, so the
+ * workspace serves any number of later calls with the same batch,
+ * n_kv_heads, n_q_heads and split count (any lengths, any layer) without
+ * clearing, including calls after one that reported KVC_DEVERR_SYNC: a flag
+ * raised late in that call holds an old epoch's value and is never taken
+ * for a later call's. Where the geometry changes, the region layout moves:
+ * zero-fill the workspace again first (or keep one workspace per geometry).
+ * Calls that share a workspace must not run concurrently.
  */
 size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t n_splits);
 
@@ -201,6 +208,11 @@ int32_t kvc_decode_splits_for_lengths(const kvc_cache_t* cache, int32_t n_q_head
  * Accumulation is fp32; results are run-to-run deterministic.
  * Supported: head_dim in {64, 128, 256} for every dtype, plus head_dim 4..32
  * (powers of two with head_dim * elem_bytes >= 16); any group size.
+ * Groups of 16..128 query heads per KV head on fp16/bf16 caches with head_dim
+ * 64 or 128 run on a kernel that streams each KV head's K/V once for the
+ * whole group, both products on the matrix cores (course notes §2.2, §2.5:
+ * the group shares its K/V, saving bytes, not FLOPs); the other shapes read
+ * K/V once per block of up to 8 query heads.
  */
 kvc_status_t kvc_decode_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
                              const void* q, int32_t n_q_heads, float scale,
@@ -230,6 +242,28 @@ kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens,
                              uint32_t* dev_status, hipStream_t stream);
 
 /*
+ * kvc_decode_step_advance -- kvc_decode_step for the last layer of a decode
+ * step: the same launch also writes seq_lens_next[b] = seq_lens[b] + 1 for
+ * every sequence (what kvc_seq_lens_advance does in a launch of its own;
+ * course notes §3.1: each update advances the write position). The
+ * lengths are read from seq_lens and written to seq_lens_next, int32[batch]
+ * device arrays that must not overlap (KVC_ERR_SHAPE), so no workgroup of the
+ * launch sees a changed length; the next step reads seq_lens_next (a
+ * caller alternates two arrays). Cache bytes and outputs are those of
+ * kvc_decode_step; seq_lens_next is written whatever the device status (a
+ * negative or full length plus one, as kvc_seq_lens_advance would).
+ * NULL seq_lens_next (with batch > 0): KVC_ERR_NULL. Other arguments as
+ * kvc_decode_step.
+ */
+kvc_status_t kvc_decode_step_advance(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t* seq_lens_next,
+                                     const void* k_new, const void* v_new,
+                                     int64_t new_stride_b, int64_t new_stride_h,
+                                     const void* q, int32_t n_q_heads, float scale,
+                                     void* out, int32_t out_dtype,
+                                     void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                     uint32_t* dev_status, hipStream_t stream);
+
+/*
  * kvc_block_attn -- a block of t_q new tokens per sequence (a prefill chunk
  * or a speculative verify step) attends the cache with the causal mask
  * aligned to the lower right (course notes "第 1 周 · Day 4" §3.3, masks with
@@ -250,8 +284,11 @@ kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t* seq_lens,
  *   n_splits  as for kvc_decode_attn (0 = library choice).
  *
  * The (query, head) pairs of a KV head are processed like the query heads of
- * a larger group, so K/V rows are streamed once per block of up to 8 pairs;
- * this suits short blocks (verify steps, small chunks). Blocks of t_q >= 8
+ * a larger group, so K/V rows are streamed once per block of up to 8 pairs,
+ * or, on fp16/bf16 caches with head_dim 64 or 128 and 16..128 pairs per KV
+ * head, once for all of them (the wide-group kernel, as for decode with 16+
+ * query heads per KV head); this suits short blocks (verify steps, small
+ * chunks). Blocks of t_q >= 8
  * with t_q * (n_q_heads / n_kv_heads) >= 32 on fp16/bf16 caches with head_dim
  * 64 or 128 run on the kernel of kvc_prefill_attn instead (the same result
  * bits as that call; n_splits is then unused, the workspace rules stand). A sequence whose
@@ -523,6 +560,18 @@ kvc_status_t kvc_stream_read(const void* buf, size_t bytes, uint32_t* sink, int3
 
 /* kvc_status_str -- static, human-readable name of a status code. */
 const char* kvc_status_str(kvc_status_t status);
+
+/*
+ * kvc_debug_set_merge_spin_limit -- a test hook, not for production use: the
+ * number of polls after which the decode split merge stops waiting for
+ * another split's ready flag and reports KVC_DEVERR_SYNC (default about
+ * 2^20, tens of milliseconds; values below 0 are taken as 0). Process-wide,
+ * read by each later decode launch; returns the previous value. This
+ * setting is the only state the library keeps between calls. Tests use it
+ * to force the time-out path from the host and check that the workspace
+ * stays usable afterwards.
+ */
+int32_t kvc_debug_set_merge_spin_limit(int32_t spins);
 
 #ifdef __cplusplus
 }

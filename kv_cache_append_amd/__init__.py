@@ -34,7 +34,7 @@ STATUS = {
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
-           "kvc_decode_attn", "kvc_decode_step", "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes",
+           "kvc_decode_attn", "kvc_decode_step", "kvc_decode_step_advance", "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes",
            "kvc_prefill_attn",
            "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
            "kvc_paged_decode_attn", "kvc_paged_decode_step",
@@ -42,7 +42,7 @@ EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_
            "kvc_quant_append", "kvc_quant_prefill_fill", "kvc_quant_decode_workspace_bytes",
            "kvc_quant_decode_attn", "kvc_quant_decode_step",
            "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str", "kvc_stream_read_sink_bytes",
-           "kvc_stream_read")
+           "kvc_stream_read", "kvc_debug_set_merge_spin_limit")
 
 
 class KvcError(RuntimeError):
@@ -135,6 +135,10 @@ def load() -> ctypes.CDLL:
     lib.kvc_cache_bytes.restype = ctypes.c_uint64
     lib.kvc_status_str.argtypes = [i32]
     lib.kvc_status_str.restype = ctypes.c_char_p
+    lib.kvc_debug_set_merge_spin_limit.argtypes = [i32]
+    lib.kvc_debug_set_merge_spin_limit.restype = i32
+    lib.kvc_decode_step_advance.argtypes = [cp, vp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_decode_step_advance.restype = i32
     _lib = lib
     return lib
 
@@ -301,9 +305,11 @@ def decode_attn(k_cache, v_cache, seq_lens, q, out, workspace, n_pending: int = 
 
 
 def decode_step(k_cache, v_cache, seq_lens, k_new, v_new, q, out, workspace, scale=None, n_splits: int = 0,
-                status=None, stream=None, desc=None):
+                status=None, stream=None, desc=None, seq_lens_next=None):
     """kvc_decode_step: append k_new/v_new at slot seq_lens[b] and attend
-    seq_lens[b] + 1 tokens, in one launch."""
+    seq_lens[b] + 1 tokens, in one launch. With seq_lens_next (another int32
+    [B] device array), kvc_decode_step_advance: the same launch also writes
+    seq_lens_next[b] = seq_lens[b] + 1 (the last layer of a step)."""
     lib = load()
     c = desc if desc is not None else cache_desc(k_cache, v_cache)
     if scale is None:
@@ -312,6 +318,13 @@ def decode_step(k_cache, v_cache, seq_lens, k_new, v_new, q, out, workspace, sca
         raise ValueError("q and out must be contiguous [B, H_q, D]")
     if k_new.stride() != v_new.stride() or k_new.dim() != 3:
         raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    if seq_lens_next is not None:
+        _check(lib.kvc_decode_step_advance(ctypes.byref(c), _ptr(seq_lens), _ptr(seq_lens_next), _ptr(k_new),
+                                           _ptr(v_new), k_new.stride(0), k_new.stride(1), _ptr(q), q.shape[1],
+                                           float(scale), _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                                           _stream(stream)), "kvc_decode_step_advance")
+        return
     _check(lib.kvc_decode_step(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
                                k_new.stride(1), _ptr(q), q.shape[1], float(scale), _ptr(out),
                                DTYPE_CODE[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -464,6 +477,12 @@ def cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, dtype: torch.dtyp
 
 def status_str(code: int) -> str:
     return load().kvc_status_str(code).decode()
+
+
+def debug_set_merge_spin_limit(spins: int) -> int:
+    """kvc_debug_set_merge_spin_limit (a test hook): polls before the split
+    merge stops waiting and reports KVC_DEVERR_SYNC; returns the previous value."""
+    return int(load().kvc_debug_set_merge_spin_limit(int(spins)))
 
 
 # ------------------------------------------------------------ quantised cache --

@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <queue>
 #include <utility>
@@ -156,9 +157,17 @@ int head_blocks(int32_t group) {
   return (group + hb - 1) / hb;
 }
 
-int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads) {
+bool routes_wide(const kvc_cache_t* c, int32_t n_q_heads) {
+  if (c == nullptr || c->n_kv_heads <= 0 || n_q_heads <= 0) return false;
+  return wide_supported(c->dtype, c->head_dim, n_q_heads / c->n_kv_heads);
+}
+
+int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads, bool wide) {
   if (c == nullptr || c->n_kv_heads <= 0 || n_q_heads <= 0 || c->batch <= 0) return 1;
-  const int64_t units = static_cast<int64_t>(c->batch) * c->n_kv_heads * head_blocks(n_q_heads / c->n_kv_heads);
+  // workgroups per split: one per (sequence, KV head) on the wide-group
+  // kernel, one per (sequence, KV head, head block) on the other
+  const int64_t units = static_cast<int64_t>(c->batch) * c->n_kv_heads *
+                        (wide ? 1 : head_blocks(n_q_heads / c->n_kv_heads));
   // Measured on MI355X (256 CUs): the fastest launches hold about one
   // workgroup per CU; more, shorter splits pay the per-workgroup start-up
   // and the merge more often than they gain, and with 256 or more units one
@@ -234,7 +243,11 @@ static double model_launch_us(const int32_t* lens, int32_t batch, int32_t n_kv, 
 int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_t* lens) {
   const int32_t group = n_q_heads / c->n_kv_heads;
   const int gb = heads_per_block(group);
-  const int per_cu = std::min(resident_wgs(c->dtype, c->head_dim, gb), 4);
+  const bool wide = routes_wide(c, n_q_heads);
+  // the wide-group kernel: one workgroup per (sequence, KV head) and split,
+  // one per CU
+  const int per_cu = wide ? 1 : std::min(resident_wgs(c->dtype, c->head_dim, gb), 4);
+  const int hblk = wide ? 1 : head_blocks(group);
   const double row_bytes = 2.0 * c->head_dim * elem_bytes(c->dtype);   // K and V of one token
   int32_t cap = c->max_len / 256;            // chunks of 256 tokens at least, as the default rule
   if (cap < 1) cap = 1;
@@ -244,7 +257,7 @@ int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_
   static const int32_t kCandidates[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32};
   for (int32_t S : kCandidates) {
     if (S > cap) break;
-    const double t = model_launch_us(lens, c->batch, c->n_kv_heads, head_blocks(group), row_bytes, per_cu, S);
+    const double t = model_launch_us(lens, c->batch, c->n_kv_heads, hblk, row_bytes, per_cu, S);
     if (S == 1 || t < best_us) {
       best = S;
       best_us = t;
@@ -254,10 +267,16 @@ int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_
   // faster than short chunks), so the length-blind count stands unless the
   // model expects another count to cut the launch by more than a sixth, as
   // for a batch with a few sequences far longer than the rest.
-  const int32_t blind = std::min<int32_t>(auto_splits(c, n_q_heads), cap);
-  const double blind_us = model_launch_us(lens, c->batch, c->n_kv_heads, head_blocks(group), row_bytes, per_cu, blind);
+  const int32_t blind = std::min<int32_t>(auto_splits(c, n_q_heads, wide), cap);
+  const double blind_us = model_launch_us(lens, c->batch, c->n_kv_heads, hblk, row_bytes, per_cu, blind);
   return best_us < blind_us * (1.0 - 1.0 / 6.0) ? best : blind;
 }
+
+// The one setting the library keeps between calls (a test hook; see
+// kvc_debug_set_merge_spin_limit).
+static std::atomic<int32_t> g_merge_spins{1 << 20};
+
+int32_t merge_spin_limit() { return g_merge_spins.load(std::memory_order_relaxed); }
 
 static size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -275,6 +294,16 @@ size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_spl
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
   const size_t rows = static_cast<size_t>(c->batch) * n_q_heads * n_splits;
   return workspace_o_offset(c, n_q_heads, n_splits) + round256(rows * c->head_dim * sizeof(float));
+}
+
+WsRegions workspace_regions(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits, void* ws) {
+  char* base = static_cast<char*>(ws);
+  WsRegions r;
+  r.flags = reinterpret_cast<uint32_t*>(base + workspace_flag_offset(c, n_q_heads, n_splits));
+  r.flag_stride = n_splits;
+  r.o = reinterpret_cast<float*>(base + workspace_o_offset(c, n_q_heads, n_splits));
+  r.ml = reinterpret_cast<float*>(base + workspace_ml_offset(c, n_q_heads, n_splits));
+  return r;
 }
 
 size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
@@ -313,10 +342,17 @@ extern "C" const char* kvc_status_str(kvc_status_t status) {
   }
 }
 
+extern "C" int32_t kvc_debug_set_merge_spin_limit(int32_t spins) {
+  if (spins < 0) spins = 0;
+  return kvc::g_merge_spins.exchange(spins, std::memory_order_relaxed);
+}
+
 extern "C" size_t kvc_decode_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t n_splits) {
   if (kvc::check_cache(cache, false) != KVC_OK) return 0;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return 0;
-  const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads);
+  // (the wide-group kernel's count is never below the other kernel's, so a
+  // workspace sized for it also serves paged and ring calls of this geometry)
+  const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_q_heads, kvc::routes_wide(cache, n_q_heads));
   return kvc::workspace_bytes(cache, n_q_heads, s);
 }
 
@@ -354,5 +390,5 @@ extern "C" int32_t kvc_decode_splits_for_lengths(const kvc_cache_t* cache, int32
 extern "C" int32_t kvc_decode_splits(const kvc_cache_t* cache, int32_t n_q_heads) {
   if (kvc::check_cache(cache, false) != KVC_OK) return 0;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return 0;
-  return kvc::auto_splits(cache, n_q_heads);
+  return kvc::auto_splits(cache, n_q_heads, kvc::routes_wide(cache, n_q_heads));
 }

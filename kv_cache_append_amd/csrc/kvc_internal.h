@@ -7,6 +7,30 @@
 
 #include "kvc.h"
 
+// Decode split placement and exchange (device code): with
+// KVC_XCD_COLOCATE every workgroup of a (sequence, KV head) unit takes a
+// workgroup id with the same residue mod 8, so the dispatcher, which deals
+// ids round-robin over the eight XCDs, places the unit's splits on one XCD.
+// KVC_XCHG_POLICY is the buffer cache policy of the splits' exchange
+// (partials and ready flags): 16, device scope (write-through, miss in the
+// per-XCD L2). With KVC_LOCAL_EXCHANGE (splits on one XCD) the exchange
+// stays in that XCD's L2 instead: plain stores (the CU's L1 writes through
+// to L2), ready flags polled with L2 atomics (KVC_XCHG_L2_POLL), and plain
+// loads of partials the merging CU has not read before in the launch.
+#ifndef KVC_XCD_COLOCATE
+#define KVC_XCD_COLOCATE 0
+#endif
+#ifndef KVC_LOCAL_EXCHANGE
+#define KVC_LOCAL_EXCHANGE 0
+#endif
+#if KVC_XCD_COLOCATE && KVC_LOCAL_EXCHANGE
+#define KVC_XCHG_POLICY 0
+#define KVC_XCHG_L2_POLL 1
+#else
+#define KVC_XCHG_POLICY 16
+#define KVC_XCHG_L2_POLL 0
+#endif
+
 namespace kvc {
 
 // Bytes per stored element, 0 for an unknown dtype code.
@@ -31,17 +55,45 @@ bool decode_head_dim_supported(int32_t head_dim, int32_t dtype);
 int heads_per_block(int32_t group);
 int head_blocks(int32_t group);
 
-// Sequence splits per (sequence, KV head, head block) when the caller passes 0.
-int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads);
+// Sequence splits per (sequence, KV head, head block) when the caller passes
+// 0. n_q_heads counts (query, head) pairs for a query block. With wide = true
+// (a contiguous 16-bit cache the wide-group kernel serves) the count is that
+// kernel's, which runs one workgroup per (sequence, KV head) and split.
+int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads, bool wide = false);
+// Whether a contiguous decode of this cache and pair count runs on the
+// wide-group kernel.
+bool routes_wide(const kvc_cache_t* c, int32_t n_q_heads);
 // Splits chosen from the sequences' lengths (host array of c->batch values)
 // by modelling the launch; see kvc_decode_splits_for_lengths.
 int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_t* lens);
 
-// Workspace: uint32 tickets [B * H_kv * head_blocks], then uint32 ready
-// flags [B * H_kv * head_blocks, S] (both zero between calls), then fp32
-// partial outputs [B, H_q, S, D], then fp32 (reference, sum) pairs
-// [B, H_q, S, 2]; each region starts on a 256-byte boundary.
+// Workspace: uint32 ready flags [B * H_kv * head_blocks, S] (word S - 1 of
+// each row is that block's merge epoch), then fp32 partial outputs
+// [B, H_q, S, D], then fp32 (reference, sum) pairs [B, H_q, S, 2]; each
+// region starts on a 256-byte boundary.
 size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
+
+// Where a decode call's split exchange lives: ready flags (one row of
+// flag_stride words per (sequence, KV head, head block); the row's last word
+// is that block's merge epoch), partial outputs [B, H_kv * pairs, S, D] and
+// partial (reference, sum) pairs [B, H_kv * pairs, S, 2]. A caller's
+// workspace has rows of S words (workspace_regions); the library's own
+// scratch (kvc_decode_step_noalloc) has rows of KVC_MAX_SPLITS words.
+struct WsRegions {
+  uint32_t* flags;
+  int32_t flag_stride;
+  float* o;
+  float* ml;
+};
+WsRegions workspace_regions(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits, void* ws);
+// Lays out a decode call's exchange space once its split count is known.
+typedef kvc_status_t (*RegionsFn)(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits, WsRegions* out);
+// kvc_decode_step with the exchange in space that regions_fn lays out
+// instead of a caller's workspace (same validation, kernels and results).
+kvc_status_t decode_step_in_regions(const kvc_cache_t* cache, const int32_t* seq_lens, const void* k_new,
+                                    const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
+                                    int32_t n_q_heads, float scale, void* out, int32_t out_dtype, int32_t n_splits,
+                                    uint32_t* dev_status, hipStream_t stream, RegionsFn regions_fn);
 size_t workspace_flag_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
@@ -65,6 +117,25 @@ kvc_status_t check_qcache(const kvc_qcache_t* c, bool for_decode);
 // The geometry of a quantised cache (batch, heads, max_len, head_dim) as a
 // cache descriptor, for the split heuristic and the workspace layout only.
 kvc_cache_t qcache_view(const kvc_qcache_t* c);
+
+// The wide-group decode kernel (kvc_wide.hip): fp16/bf16 caches with head
+// dim 64 or 128 and KVC_WIDE_MIN_PAIRS..128 (query, head) pairs per KV head
+// (group size times queries per sequence); contiguous caches. Its launch
+// takes arguments already validated by launch_decode.
+#ifndef KVC_WIDE_MIN_PAIRS
+#define KVC_WIDE_MIN_PAIRS 16
+#endif
+bool wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs);
+kvc_status_t launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,
+                         const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
+                         int32_t n_q_heads, int32_t t_q, float scale_log2, void* out, int32_t out_dtype,
+                         const WsRegions& ws, int32_t splits, int32_t* lens_next, uint32_t* dev_status,
+                         hipStream_t stream);
+
+// Bound on the polls of the decode split merge's wait for ready flags (about
+// 2^20 by default; kvc_debug_set_merge_spin_limit changes it for tests of the
+// time-out path).
+int32_t merge_spin_limit();
 
 // The matrix-core prefill kernel (kvc_prefill.hip): whether it is built for
 // this dtype and head dim, and its launch (arguments as kvc_prefill_attn,

@@ -309,7 +309,7 @@ struct DecodeParams {
   const char* k_new;           // fused append source [B, H_kv, D] or null
   const char* v_new;
   int64_t nsb, nsh;            // its strides in bytes
-  uint32_t* ws_flag;           // [B * H_kv * n_hblk, S] ready flags, zero between calls
+  uint32_t* ws_flag;           // [B * H_kv * n_hblk, flag_stride] ready flags; a row's last word is its epoch
   float* ws_o;                 // [B, H_q, S, D]
   float* ws_ml;                // [B, H_q, S, 2]
   void* out;                   // [B, H_q, D]
@@ -334,6 +334,9 @@ struct DecodeParams {
   char* v_scale;
   int64_t ssb, ssh;
   float scale_log2;            // softmax scale * log2(e)
+  int32_t merge_spins;         // bound on the split merge's wait for ready flags (polls)
+  int32_t flag_stride;         // words per flag row (>= n_splits)
+  int32_t* lens_next;          // kvc_decode_step_advance: seq_lens[b] + 1 written here, or null
 };
 
 struct SeqInfo {
@@ -373,6 +376,7 @@ __device__ inline SeqInfo seq_info(const DecodeParams& p, int b) {
   }
   int n = static_cast<int>(min(n64, static_cast<int64_t>(p.max_len)));
   if (n64 > p.max_len) si.flags |= KVC_DEVERR_CAPACITY;
+  if (c0 < 0) n = 0;               // a negative length: a zero row, nothing attended
   si.n = n;
   si.newest = n - 1;
   return si;
@@ -439,7 +443,10 @@ __device__ inline const char* uniform_ptr(const char* q) {
   const uint64_t hi = uniform_u32(static_cast<uint32_t>(a >> 32));
   return reinterpret_cast<const char*>(lo | (hi << 32));
 }
-constexpr int kCoherent = 16;   // buffer cache policy: device scope (write-through / miss in the per-XCD L2)
+// Cache policy of the split exchange (partials, ready flags): device scope
+// (16: write-through, miss in the per-XCD L2) unless set otherwise in
+// kvc_internal.h.
+constexpr int kXchg = KVC_XCHG_POLICY;
 // Cache policy of the K/V stream: every row is read once per launch, so the
 // loads carry the non-temporal hint (`nt`). Measured on MI355X (same box,
 // interleaved runs) it streams 6-7 % faster than the default policy on every
@@ -452,12 +459,12 @@ __device__ inline u32x4 buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, kStream));
 }
-__device__ inline u32x4 buf_load_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kCoherent));
+__device__ inline u32x4 buf_load_xchg(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kXchg));
 }
-__device__ inline void buf_store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
+__device__ inline void buf_store_xchg(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), r,
-                                         static_cast<int>(off), 0, kCoherent);
+                                         static_cast<int>(off), 0, kXchg);
 }
 
 // 8-bit cache codes (KQ = 1: OCP E4M3, KQ = 2: int8). Every code's value has
@@ -648,7 +655,6 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   // of a masked (-inf) score is exp2(-inf) = 0 rather than NaN, and far
   // below any finite score, so exp2(kEmpty - ref) is 0 once a row is seen.
   constexpr float kEmpty = -1e30f;
-  constexpr int kMaxSpins = 1 << 20;      // bound on the merge's wait for ready flags
   static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must split into 16-byte lane slices");
 
   constexpr bool kMfma = kQuant || decode_uses_mfma<ET, D>();
@@ -667,22 +673,46 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   // they can be read in the score layout (K) and the row layout (V)
   __shared__ __align__(16) uint8_t sm_x[kQuant ? 2 : 1][kQuant ? D : 16];
 
-  // Workgroup ids go round-robin over the 8 XCDs (id mod 8). The head blocks
-  // of one (unit, split) item read the same K/V rows, so they take ids 8
-  // apart: same XCD, hence the same L2, dispatched back to back. Items are
-  // numbered w = unit * n_splits + split; the grid is padded to a multiple
-  // of 8 items.
+  // Workgroup ids go round-robin over the 8 XCDs (id mod 8). Every
+  // workgroup of a (sequence, KV head) unit takes an id with the same residue
+  // mod 8, so the unit's splits and head blocks run on one XCD: the head
+  // blocks read the same K/V rows through one L2, and the splits exchange
+  // their partials through it. On its XCD a unit's workgroups take
+  // consecutive slots, head blocks innermost, then splits, so the merging
+  // split (the last) has the highest id of its item. The grid is padded to a
+  // multiple of 8 units.
   const int xcd = blockIdx.x & 7;
   const int r8 = blockIdx.x >> 3;
   const int hb = r8 % p.n_hblk;
+#if KVC_XCD_COLOCATE
+  const int rest = r8 / p.n_hblk;
+  const int split = rest % p.n_splits;
+  const int unit = (rest / p.n_splits) * 8 + xcd;
+  if (unit >= p.batch * p.n_kv) return;             // grid padding
+#else
   const int w_item = (r8 / p.n_hblk) * 8 + xcd;
   if (w_item >= p.batch * p.n_kv * p.n_splits) return;   // grid padding
   const int split = w_item % p.n_splits;
   const int unit = w_item / p.n_splits;
+#endif
   const int b = unit / p.n_kv;
   const int g = unit - b * p.n_kv;
+  // The item's epoch (word S - 1 of its flags: no split publishes there),
+  // requested now and used after the stream. A publisher raises its flag to
+  // epoch + 1; the merger waits for exactly that value and then advances the
+  // epoch, so flags never need clearing and a flag raised after a merge gave
+  // up waiting (KVC_DEVERR_SYNC) cannot be taken for the next call's.
+  const int64_t item = static_cast<int64_t>(unit) * p.n_hblk + hb;
+  uint32_t* const flags = p.ws_flag + item * p.flag_stride;
+  uint32_t epoch = 0u;
+  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   const SeqInfo si = seq_info(p, b);
+  // kvc_decode_step_advance (the last layer of a step): the next step's
+  // lengths, written by one workgroup per sequence into another array, so no
+  // workgroup of this launch reads a changed length
+  if (p.lens_next != nullptr && g == 0 && split == 0 && hb == 0 && threadIdx.x == 0)
+    p.lens_next[b] = p.seq_lens[b] + 1;
   if (si.flags != 0 && g == 0 && hb == 0 && split == 0 && threadIdx.x == 0 && p.status != nullptr)
     atomicOr(p.status, si.flags);
   const int n = si.n;
@@ -1365,20 +1395,22 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   }
 
   // Several splits. The last active split merges; the others publish their
-  // partial (reference, sum, unnormalised output) with device-coherent
-  // stores, wait for them to complete and raise their split's ready flag.
-  // The merging workgroup waits for the other splits' flags, folds the
-  // partials in, writes the output and leaves the flags at zero for the next
-  // call. It has the highest workgroup id of its item, and a workgroup that
-  // publishes never waits, so with workgroups dispatched in id order on each
-  // XCD every awaited workgroup is dispatched and finishes; the wait is
-  // bounded all the same.
-  const int64_t item = static_cast<int64_t>(unit) * p.n_hblk + hb;
-  uint32_t* flags = p.ws_flag + item * p.n_splits;
+  // partial (reference, sum, unnormalised output), wait for the stores to
+  // complete and raise their split's ready flag to epoch + 1. The merging
+  // workgroup waits for the other splits' flags, folds the partials in,
+  // writes the output and advances the item's epoch for the next call. It
+  // has the highest workgroup id of its item, and a workgroup that publishes
+  // never waits, so with workgroups dispatched in id order on each XCD every
+  // awaited workgroup is dispatched and finishes; the wait is bounded all the
+  // same.
   // partial rows: [B, H_kv * pairs, S] (for decode, [B, H_q, S])
   const int64_t prow0 = ((static_cast<int64_t>(b) * p.n_kv + g) * gv + v_first) * p.n_splits;
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(nh * p.n_splits * D * 4));
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(nh * p.n_splits * 2 * 4));
+  const __amdgpu_buffer_rsrc_t frs = make_rsrc(flags, static_cast<uint32_t>(p.flag_stride * 4));
+  // first use of the epoch: its load (issued at entry) is waited for here,
+  // not in front of the stream
+  asm volatile("" : "+v"(epoch));
   if (split != ns - 1) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -1387,30 +1419,43 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
       const int j = t / D4;
       const int d = (t - j * D4) * 4;
       const uint32_t row = static_cast<uint32_t>(j * p.n_splits + split);
-      buf_store_coherent(ors, (row * D + d) * 4u,
+      buf_store_xchg(ors, (row * D + d) * 4u,
                          u32x4{__float_as_uint(aa[i][0]), __float_as_uint(aa[i][1]), __float_as_uint(aa[i][2]),
                                __float_as_uint(aa[i][3])});
       if (d == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rv[i]), mrs, static_cast<int>(row * 8u), 0, kCoherent);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv[i]), mrs, static_cast<int>(row * 8u + 4u), 0,
-                                              kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rv[i]), mrs, static_cast<int>(row * 8u), 0, kXchg);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv[i]), mrs, static_cast<int>(row * 8u + 4u), 0, kXchg);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>(split * 4), 0, kXchg);
     return;
   }
 
-  // The merging workgroup: wait for the other splits' flags.
+  // The merging workgroup: wait for the other splits' flags to reach this
+  // call's value (epoch + 1).
   for (int k = threadIdx.x; k < ns - 1; k += blockDim.x) {
     int spins = 0;
-    while (__hip_atomic_load(flags + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      if (++spins > kMaxSpins) {                 // never expected: flag the call, do not hang
+    for (;;) {
+#if KVC_XCHG_L2_POLL
+      // (a compare-and-swap that writes back what it finds: an atomic, so it
+      // is performed in L2 and returns L2's value; an idempotent add or load
+      // would be turned into a load the CU's L1 may serve)
+      uint32_t f = epoch + 1u;
+      __hip_atomic_compare_exchange_strong(flags + k, &f, epoch + 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+#else
+      const uint32_t f = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(frs, k * 4, 0, kXchg));
+#endif
+      if (f == epoch + 1u) break;
+      if (++spins > p.merge_spins) {             // never expected: flag the call, do not hang
         if (p.status != nullptr) atomicOr(p.status, KVC_DEVERR_SYNC);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
+      asm volatile("" ::: "memory");
     }
   }
   __syncthreads();
@@ -1435,10 +1480,10 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
       for (int k = 0; k < 8; ++k) {
         const uint32_t row = row0 + static_cast<uint32_t>(i0 + k);
         rb[k] = __uint_as_float(static_cast<uint32_t>(
-            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u), 0, kCoherent)));
+            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u), 0, kXchg)));
         lb[k] = __uint_as_float(static_cast<uint32_t>(
-            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u + 4u), 0, kCoherent)));
-        ob[k] = buf_load_coherent(ors, (row * D + d) * 4u);
+            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u + 4u), 0, kXchg)));
+        ob[k] = buf_load_xchg(ors, (row * D + d) * 4u);
       }
       bool use[8];
       float bm = -INFINITY;
@@ -1472,9 +1517,9 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
     for (int e = 0; e < 4; ++e) aa[i][e] = am[e];
   }
   write_out();
-  // ready for the next call on this workspace
-  for (int k = threadIdx.x; k < ns - 1; k += blockDim.x)
-    __hip_atomic_store(flags + k, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the next call on this workspace waits for flags of epoch + 2
+  if (threadIdx.x == 0)
+    __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>((p.flag_stride - 1) * 4), 0, kXchg);
 }
 
 // ------------------------------------------------------------- dispatch --
@@ -1540,6 +1585,16 @@ DecodeKernel pick_quant_kernel(int format, int q_dtype, int d, int gb) {
   if (q_dtype == KVC_F16) return fp8 ? pick_d_quant<F16T, kQuantFp8>(d, gb) : pick_d_quant<F16T, kQuantInt8>(d, gb);
   if (q_dtype == KVC_BF16) return fp8 ? pick_d_quant<BF16T, kQuantFp8>(d, gb) : pick_d_quant<BF16T, kQuantInt8>(d, gb);
   return nullptr;
+}
+
+// Workgroups of a decode launch over `units` (sequence, KV head) units: see
+// the id mapping at the top of decode_kernel.
+int64_t decode_grid(int64_t units, int32_t splits, int32_t n_hblk) {
+#if KVC_XCD_COLOCATE
+  return (units + 7) / 8 * 8 * splits * n_hblk;
+#else
+  return (units * splits + 7) / 8 * 8 * n_hblk;
+#endif
 }
 
 // ------------------------------------------------ quantised append / fill --
@@ -1704,10 +1759,12 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
   p.v_new = static_cast<const char*>(v_new);
   p.nsb = new_stride_b * s_in;
   p.nsh = new_stride_h * s_in;
-  char* ws = static_cast<char*>(workspace);
-  p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(&view, n_q_heads, splits));
-  p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(&view, n_q_heads, splits));
-  p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(&view, n_q_heads, splits));
+  const kvc::WsRegions wr = kvc::workspace_regions(&view, n_q_heads, splits, workspace);
+  p.ws_flag = wr.flags;
+  p.flag_stride = wr.flag_stride;
+  p.ws_o = wr.o;
+  p.ws_ml = wr.ml;
+  p.lens_next = nullptr;
   p.out = out;
   p.status = dev_status;
   p.batch = c->batch;
@@ -1728,8 +1785,8 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
   p.ssb = c->scale_stride_b * 4;
   p.ssh = c->scale_stride_h * 4;
   p.scale_log2 = scale_log2;
-  const int64_t items = static_cast<int64_t>(c->batch) * c->n_kv_heads * splits;
-  const int64_t wgs = (items + 7) / 8 * 8 * p.n_hblk;     // see the id mapping in decode_kernel
+  p.merge_spins = kvc::merge_spin_limit();
+  const int64_t wgs = decode_grid(static_cast<int64_t>(c->batch) * c->n_kv_heads, splits, p.n_hblk);
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(KVC_WAVES * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
@@ -1784,7 +1841,8 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
                            const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
                            int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
                            size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status, hipStream_t stream,
-                           int32_t t_q, const kvc::PageInfo* pg = nullptr, bool ring = false) {
+                           int32_t t_q, const kvc::PageInfo* pg = nullptr, bool ring = false,
+                           int32_t* lens_next = nullptr, kvc::RegionsFn regions_fn = nullptr) {
   kvc_status_t st = kvc::check_cache(cache, true);
   if (st != KVC_OK) return st;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
@@ -1816,10 +1874,21 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   // The kernels address one (sequence, KV head) slice of K/V with 32-bit
   // byte offsets (plus up to two tiles past the end, read back as zeros).
   if ((static_cast<int64_t>(cache->max_len) + 2048) * cache->stride_t * s > 0x7fffffffll) return KVC_ERR_SHAPE;
-  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_qv);
-  const size_t need = kvc::workspace_bytes(cache, n_qv, splits);
-  if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
+  // Contiguous 16-bit caches with 16..128 (query, head) pairs per KV head run
+  // on the wide-group kernel (K/V streamed once for all pairs, both products
+  // on the matrix cores).
+  const bool wide = pg == nullptr && !ring && kvc::routes_wide(cache, n_qv);
+  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_qv, wide);
+  kvc::WsRegions wr;
+  if (regions_fn != nullptr) {                   // exchange space the caller of this function lays out
+    st = regions_fn(cache, n_qv, splits, &wr);
+    if (st != KVC_OK) return st;
+  } else {
+    const size_t need = kvc::workspace_bytes(cache, n_qv, splits);
+    if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
+    wr = kvc::workspace_regions(cache, n_qv, splits, workspace);
+  }
 
   const int group = n_q_heads / cache->n_kv_heads;
   // A block of 8 or more queries with at least 32 (query, head) pairs per KV
@@ -1831,6 +1900,9 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   if (t_q >= 8 && group * t_q >= 32 && pg == nullptr && !ring && k_new == nullptr &&
       kvc::prefill_supported(cache->dtype, cache->head_dim))
     return kvc::launch_prefill(cache, seq_lens, t_q, q, n_q_heads, scale, out, out_dtype, dev_status, stream);
+  if (wide)
+    return kvc::launch_wide(cache, seq_lens, n_pending, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, t_q,
+                            scale_log2, out, out_dtype, wr, splits, lens_next, dev_status, stream);
   const int gb = kvc::heads_per_block(group * tq);
   DecodeParams p;
   p.k = static_cast<char*>(cache->k);
@@ -1844,10 +1916,11 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.v_new = static_cast<const char*>(v_new);
   p.nsb = new_stride_b * s;
   p.nsh = new_stride_h * s;
-  char* ws = static_cast<char*>(workspace);
-  p.ws_flag = reinterpret_cast<uint32_t*>(ws + kvc::workspace_flag_offset(cache, n_qv, splits));
-  p.ws_o = reinterpret_cast<float*>(ws + kvc::workspace_o_offset(cache, n_qv, splits));
-  p.ws_ml = reinterpret_cast<float*>(ws + kvc::workspace_ml_offset(cache, n_qv, splits));
+  p.ws_flag = wr.flags;
+  p.flag_stride = wr.flag_stride;
+  p.ws_o = wr.o;
+  p.ws_ml = wr.ml;
+  p.lens_next = lens_next;
   p.out = out;
   p.status = dev_status;
   p.batch = cache->batch;
@@ -1872,8 +1945,8 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
 
   DecodeKernel k = pick_decode_kernel(cache->dtype, cache->head_dim, gb);
   if (k == nullptr) return KVC_ERR_UNSUPPORTED;
-  const int64_t items = static_cast<int64_t>(cache->batch) * cache->n_kv_heads * splits;
-  const int64_t wgs = (items + 7) / 8 * 8 * p.n_hblk;     // see the id mapping in decode_kernel
+  p.merge_spins = kvc::merge_spin_limit();
+  const int64_t wgs = decode_grid(static_cast<int64_t>(cache->batch) * cache->n_kv_heads, splits, p.n_hblk);
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(KVC_WAVES * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
@@ -1933,6 +2006,33 @@ extern "C" kvc_status_t kvc_decode_step(const kvc_cache_t* cache, const int32_t*
   }
   return launch_decode(cache, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
                        out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, 0);
+}
+
+extern "C" kvc_status_t kvc_decode_step_advance(const kvc_cache_t* cache, const int32_t* seq_lens,
+                                                int32_t* seq_lens_next, const void* k_new, const void* v_new,
+                                                int64_t new_stride_b, int64_t new_stride_h, const void* q,
+                                                int32_t n_q_heads, float scale, void* out, int32_t out_dtype,
+                                                void* workspace, size_t workspace_bytes, int32_t n_splits,
+                                                uint32_t* dev_status, hipStream_t stream) {
+  if (cache != nullptr && cache->batch > 0) {
+    if (k_new == nullptr || v_new == nullptr || seq_lens_next == nullptr) return KVC_ERR_NULL;
+    // the two length arrays must not overlap: the launch reads one and writes the other
+    const int32_t* a = seq_lens;
+    const int32_t* e = seq_lens_next;
+    if (a != nullptr && e < a + cache->batch && a < e + cache->batch) return KVC_ERR_SHAPE;
+  }
+  return launch_decode(cache, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
+                       out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, 0, nullptr, false,
+                       seq_lens_next);
+}
+
+kvc_status_t kvc::decode_step_in_regions(const kvc_cache_t* cache, const int32_t* seq_lens, const void* k_new,
+                                         const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
+                                         const void* q, int32_t n_q_heads, float scale, void* out, int32_t out_dtype,
+                                         int32_t n_splits, uint32_t* dev_status, hipStream_t stream,
+                                         RegionsFn regions_fn) {
+  return launch_decode(cache, seq_lens, 1, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
+                       out_dtype, nullptr, 0, n_splits, dev_status, stream, 0, nullptr, false, nullptr, regions_fn);
 }
 
 extern "C" kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q, const void* q,

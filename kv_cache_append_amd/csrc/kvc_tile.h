@@ -1,0 +1,75 @@
+// Device helpers shared by the matrix-core attention kernels (prefill and
+// wide-group decode): 16-bit element traits for v_mfma_f32_16x16x32 and the
+// split of fp32 weights into two 16-bit parts, buffer resources, and the key
+// order of a transposed-V row in LDS. Device code only; include inside an
+// anonymous namespace of a .hip file.
+#ifndef KVC_TILE_H_
+#define KVC_TILE_H_
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// 16-bit cache element types: the matrix-core product, the split of two
+// fp32 weights into high and low 16-bit parts (packed two to a word, first
+// weight in the low half), and the output store.
+struct Bf16P {
+  __device__ static inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  }
+  // hi keeps the top 16 bits of each weight (a bf16 value), lo the top 16
+  // bits of the exact remainder: hi + lo carries 16 of the 24 bits. (The
+  // byte permute takes bytes 2-3 of each word: 0x07060302 over {p1, p0}.)
+  __device__ static inline void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+    const float r0 = p0 - __uint_as_float(u0 & 0xffff0000u);
+    const float r1 = p1 - __uint_as_float(u1 & 0xffff0000u);
+    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+    lo = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+  }
+  __device__ static inline void store(void* base, int64_t i, float x) {
+    // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN
+    const uint32_t u = __float_as_uint(x);
+    uint16_t h;
+    if ((u & 0x7fffffffu) > 0x7f800000u) h = static_cast<uint16_t>((u >> 16) | 0x40u);
+    else h = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    static_cast<uint16_t*>(base)[i] = h;
+  }
+};
+
+struct F16P {
+  __device__ static inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+  }
+  // hi = fp16(p) rounded toward zero, lo = fp16(p - hi) likewise; the
+  // remainder is exact in fp32 (one packed conversion per pair)
+  __device__ static inline void split(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+    const float r0 = p0 - static_cast<float>(h[0]), r1 = p1 - static_cast<float>(h[1]);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+  }
+  __device__ static inline void store(void* base, int64_t i, float x) {
+    asm volatile("" : "+v"(x));   // keep the fp32 value: one rounding, to nearest even
+    static_cast<_Float16*>(base)[i] = static_cast<_Float16>(x);
+  }
+};
+
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ inline u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+// The slot of key kk (0..31) of a 32-key chunk in a transposed-V row. The
+// score product leaves lane group g (lanes 16g .. 16g+15) with keys 4g..4g+3
+// of each 16-key block; the output product takes 8 consecutive slots per
+// lane group, so slots 8g..8g+7 hold keys 4g..4g+3 and 16+4g..16+4g+3.
+__device__ inline int vt_slot(int kk) { return 8 * ((kk & 15) >> 2) + (kk & 3) + 4 * (kk >> 4); }
+
+#endif  // KVC_TILE_H_

@@ -1,0 +1,606 @@
+// Decode attention for wide groups: many query heads per KV head (MQA, wide
+// GQA) or, for a block of new queries, many (query, head) pairs per KV head,
+// on the CDNA4 matrix cores, with each KV head's K/V streamed from HBM once
+// for all of them.
+//
+// Grouping query heads onto fewer KV heads saves cache bytes, not FLOPs
+// (course notes "第 1 周 · Day 4" §2.2 and §2.5), and the saving only reaches
+// the decode step if the shared K/V rows are read once for the whole group,
+// through the head map rather than by copying heads (glossary "KV 缓存",
+// "从教学代码到生产实现还差什么"). With 64 query heads on one KV head a
+// decode step does 64 FLOPs per cache byte, past what the vector ALU
+// sustains at HBM rate, so both products run on v_mfma_f32_16x16x32:
+//   * one 256-thread workgroup per (sequence, KV head, split of the T axis);
+//     the unit's K/V rows of the split go through LDS in tiles of 64 keys,
+//     K as stored (padded rows), V transposed (one row per head-dim element),
+//     read by all four waves; the next tiles' loads are in flight meanwhile;
+//   * each wave owns column blocks of 16 (query, head) pairs; scores are
+//     computed transposed, S^T = K Q^T, so a lane holds the scores of one
+//     pair and the online softmax (a lazily moved reference, as in the other
+//     decode kernel) stays in its registers;
+//   * the output is accumulated transposed, O^T += V^T P^T, with each fp32
+//     weight split into two 16-bit parts (hi + lo, about 16 significant
+//     bits) so the product keeps the weights' precision; accumulation fp32;
+//   * the newest attended row is folded in by the last split as a tile of its
+//     own (from k_new/v_new in the fused step, which also writes it into the
+//     cache), so kvc_decode_step and kvc_append + kvc_decode_attn add the same
+//     rows in the same order;
+//   * splits publish (reference, sum, unnormalised output) per pair and the
+//     last split merges them in split order, with the same workspace, epoch
+//     flags and workgroup placement as the other decode kernel (every split
+//     of a unit on one XCD).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kvc.h"
+#include "kvc_internal.h"
+
+namespace {
+
+#include "kvc_tile.h"
+
+constexpr int kWTile = 64;       // keys per LDS tile
+constexpr int kWVtRow = 144;     // bytes per transposed-V row in LDS: 64 keys + 8 elements of padding
+constexpr int kNt = 2;           // cache policy of the K/V stream: non-temporal (each row read once)
+constexpr int kXchgW = KVC_XCHG_POLICY;
+
+#ifndef KVC_WIDE_PREFETCH
+#define KVC_WIDE_PREFETCH 2      // register tiles of loads in flight behind the one being staged
+#endif
+
+struct WideParams {
+  char* k;                       // cache; written only by the fused append
+  char* v;
+  int64_t sb, sh, st;            // cache strides in bytes
+  const int32_t* seq_lens;
+  const char* q;                 // [B, t_q, H_q, D] (decode: t_q = 1)
+  const char* k_new;             // fused append source [B, H_kv, D] or null
+  const char* v_new;
+  int64_t nsb, nsh;              // its strides in bytes
+  uint32_t* ws_flag;             // [B * H_kv * n_hblk, flag_stride]: this kernel uses head block 0's row
+  float* ws_o;                   // [B, H_kv * pairs, S, D]
+  float* ws_ml;                  // [B, H_kv * pairs, S, 2]
+  void* out;                     // like q; fp32 or the cache dtype
+  uint32_t* status;
+  int32_t batch, n_q, n_kv, group, n_hblk, max_len, n_pending, n_splits, out_f32;
+  int32_t t_q, block;            // block of t_q queries (lower-right causal mask), or decode (block = 0)
+  float scale_log2;              // softmax scale * log2(e)
+  int32_t merge_spins;           // bound on the merge's wait for ready flags (polls)
+  int32_t flag_stride;           // words per flag row (>= n_splits); the last is the epoch
+  int32_t* lens_next;            // kvc_decode_step_advance: seq_lens[b] + 1 written here, or null
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t wrsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+template <int kPolicy>
+__device__ inline u32x4 wload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kPolicy));
+}
+__device__ inline void wstore(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), r,
+                                         static_cast<int>(off), 0, kXchgW);
+}
+// Values every lane holds alike, in scalar registers (for buffer resources).
+__device__ inline const char* uniform_cptr(const char* q) {
+  const uint64_t a = reinterpret_cast<uint64_t>(q);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  return reinterpret_cast<const char*>(lo | (hi << 32));
+}
+
+// Row of q and out ([B, t_q, H_q, D], token-major) of pair v of KV head g:
+// pair v is query v / group of head v % group.
+__device__ inline int64_t wpair_row(const WideParams& p, int b, int g, int v) {
+  const int i = v / p.group;
+  return (static_cast<int64_t>(b) * p.t_q + i) * p.n_q + g * p.group + (v - i * p.group);
+}
+
+// ET: Bf16P or F16P (the cache dtype); QB: column blocks of 16 pairs per wave.
+template <typename ET, int D, int QB>
+__global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p) {
+  constexpr int NC = D / 32;            // 32-element slices of a row (score product depth)
+  constexpr int ND = D / 16;            // 16-element output blocks
+  constexpr int KR = 2 * D + 16;        // bytes per K row in LDS (16 bytes of padding)
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int NKL = kWTile * CPR / 256;   // 16-byte K loads per thread per tile
+  constexpr int NVP = D / 64;           // V passes per tile, two 16-byte loads (two keys) each
+  constexpr int NB = KVC_WIDE_PREFETCH + 1;
+  constexpr float kLazy = 8.f;          // the reference moves only past ref + 8 (log2 domain)
+  // Reference of a pair that has seen no key: finite, so that exp2 of a
+  // masked (-inf) score against it is 0 rather than NaN, and far below any
+  // score, so the first key seen replaces it (and zeroes its weight).
+  constexpr float kEmpty = -1e30f;
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  __shared__ __attribute__((aligned(16))) char sk[kWTile * KR];
+  __shared__ __attribute__((aligned(16))) char svt[D * kWVtRow];
+
+  // Workgroup placement: every split of a unit on one XCD (id residue mod 8),
+  // the unit's splits in consecutive slots there, the merging split last.
+  const int xcd = blockIdx.x & 7;
+  const int r8 = blockIdx.x >> 3;
+  const int split = r8 % p.n_splits;
+  const int unit = (r8 / p.n_splits) * 8 + xcd;
+  if (unit >= p.batch * p.n_kv) return;              // grid padding
+  const int b = unit / p.n_kv;
+  const int g = unit - b * p.n_kv;
+  // the unit's epoch (see the merge below), requested now and used at the end
+  uint32_t* const flags = p.ws_flag + static_cast<int64_t>(unit) * p.n_hblk * p.flag_stride;
+  uint32_t epoch = 0u;
+  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // Rows attended (n), the slot the fused append writes, device-side flags.
+  const int c0 = p.seq_lens[b];
+  // kvc_decode_step_advance: the next step's lengths, into another array
+  if (p.lens_next != nullptr && g == 0 && split == 0 && threadIdx.x == 0) p.lens_next[b] = c0 + 1;
+  const int c = c0 < 0 ? 0 : c0;
+  uint32_t dflags = c0 < 0 ? KVC_DEVERR_BADLEN : 0u;
+  const int add = p.k_new != nullptr ? 1 : (p.block ? p.t_q : p.n_pending);
+  const int64_t n64 = static_cast<int64_t>(c) + add;
+  int n, append_row = -1;
+  if (p.block) {                                     // the whole block must fit
+    if (c0 >= 0 && n64 > p.max_len) dflags |= KVC_DEVERR_CAPACITY;
+    n = (c0 < 0 || n64 > p.max_len) ? 0 : static_cast<int>(n64);
+  } else {
+    if (p.k_new != nullptr) {
+      if (c0 >= 0 && c0 < p.max_len) append_row = c0;
+      else dflags |= KVC_DEVERR_CAPACITY;
+    }
+    n = static_cast<int>(min(n64, static_cast<int64_t>(p.max_len)));
+    if (n64 > p.max_len) dflags |= KVC_DEVERR_CAPACITY;
+    if (c0 < 0) n = 0;             // a negative length: a zero row, nothing attended
+  }
+  if (dflags != 0 && g == 0 && split == 0 && threadIdx.x == 0 && p.status != nullptr) atomicOr(p.status, dflags);
+  const int gv = p.group * p.t_q;                    // (query, head) pairs of this KV head
+  auto store_out = [&](int64_t idx, float x) {
+    if (p.out_f32) static_cast<float*>(p.out)[idx] = x;
+    else ET::store(p.out, idx, x);
+  };
+  if (n <= 0) {                                      // empty sequence: zero rows
+    if (split == 0)
+      for (int t = threadIdx.x; t < gv * D; t += blockDim.x) store_out(wpair_row(p, b, g, t / D) * D + t % D, 0.f);
+    return;
+  }
+  // The T axis in equal whole tiles; decode folds the newest row (n - 1) in
+  // apart from the stream, in the last active split.
+  const int streamed = p.block ? n : n - 1;
+  const int chunk = max(kWTile, ((streamed + p.n_splits - 1) / p.n_splits + kWTile - 1) & ~(kWTile - 1));
+  const int ns = streamed > 0 ? min(p.n_splits, (streamed + chunk - 1) / chunk) : 1;
+  if (split >= ns) return;                           // inactive split
+  const int t0 = split * chunk;
+  const int t_end = split == ns - 1 ? streamed : t0 + chunk;   // rows streamed from the cache: [t0, t_end)
+  const bool has_x = !p.block && split == ns - 1;
+  const bool x_new = has_x && append_row == n - 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int ncb = (gv + 15) / 16;
+
+  // The fused append: the newest row into its slot (no workgroup of this
+  // launch reads that slot from the cache).
+  if (x_new && wave == 0 && lane < CPR) {
+    const int64_t noff = b * p.nsb + g * p.nsh + lane * 16;
+    const int64_t aoff = b * p.sb + g * p.sh + static_cast<int64_t>(append_row) * p.st + lane * 16;
+    *reinterpret_cast<u32x4*>(p.k + aoff) = *reinterpret_cast<const u32x4*>(p.k_new + noff);
+    *reinterpret_cast<u32x4*>(p.v + aoff) = *reinterpret_cast<const u32x4*>(p.v_new + noff);
+  }
+
+  // The wave's pairs as B operands of the score product (column = pair r16
+  // of column block wave + 4j, 8 elements 32c + 8grp of its query row), and
+  // each pair's slot limit (lower-right causal mask of a query block).
+  u32x4 qf[QB][NC];
+  int plim[QB];
+  bool cb_on[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int cb = wave + 4 * j;
+    cb_on[j] = cb < ncb;
+    const int v = cb * 16 + r16;
+    plim[j] = p.block ? n - p.t_q + v / p.group + 1 : n;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      qf[j][cc] = u32x4{0u, 0u, 0u, 0u};
+      if (cb_on[j] && v < gv)
+        qf[j][cc] = *reinterpret_cast<const u32x4*>(p.q + (wpair_row(p, b, g, v) * D + 32 * cc + 8 * grp) * 2);
+    }
+  }
+
+  const uint32_t st = static_cast<uint32_t>(p.st);
+  const char* kunit = uniform_cptr(p.k + (b * p.sb + g * p.sh));
+  const char* vunit = uniform_cptr(p.v + (b * p.sb + g * p.sh));
+  // K/V of the streamed rows; rows past t_end read as zero (and are masked)
+  const __amdgpu_buffer_rsrc_t krs = wrsrc(kunit, static_cast<uint32_t>(t_end) * st);
+  const __amdgpu_buffer_rsrc_t vrs = wrsrc(vunit, static_cast<uint32_t>(t_end) * st);
+
+  // Tile staging: thread tid loads K chunks tid + 256m (row idx / CPR, chunk
+  // idx % CPR) and V rows 2kp, 2kp + 1 (kp = tid % 32) at chunk tid / 32 + 8ps.
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t kr_, __amdgpu_buffer_rsrc_t vr_, uint32_t base, u32x4 (&kr)[NKL],
+                       u32x4 (&vr)[2 * NVP]) {
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+      const int idx = tid + 256 * m;
+      kr[m] = wload<kNt>(kr_, base + static_cast<uint32_t>(idx / CPR) * st + static_cast<uint32_t>(idx % CPR) * 16u);
+    }
+#pragma unroll
+    for (int ps = 0; ps < NVP; ++ps) {
+      const int kp = tid & 31;
+      const int dc = (tid >> 5) + 8 * ps;
+      vr[2 * ps] = wload<kNt>(vr_, base + static_cast<uint32_t>(2 * kp) * st + dc * 16u);
+      vr[2 * ps + 1] = wload<kNt>(vr_, base + static_cast<uint32_t>(2 * kp + 1) * st + dc * 16u);
+    }
+  };
+  auto store_tile = [&](const u32x4 (&kr)[NKL], const u32x4 (&vr)[2 * NVP]) {
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+      const int idx = tid + 256 * m;
+      *reinterpret_cast<u32x4*>(sk + (idx / CPR) * KR + (idx % CPR) * 16) = kr[m];
+    }
+#pragma unroll
+    for (int ps = 0; ps < NVP; ++ps) {
+      const int kp = tid & 31;
+      const int dc = (tid >> 5) + 8 * ps;
+      const int key0 = 2 * kp;                           // keys key0, key0 + 1 share one word
+      const int col = (32 * (key0 >> 5) + vt_slot(key0 & 31)) * 2;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w0 = vr[2 * ps][m], w1 = vr[2 * ps + 1][m];
+        const int d = 8 * dc + 2 * m;
+        *reinterpret_cast<uint32_t*>(svt + d * kWVtRow + col) = (w0 & 0xffffu) | (w1 << 16);
+        *reinterpret_cast<uint32_t*>(svt + (d + 1) * kWVtRow + col) = (w0 >> 16) | (w1 & 0xffff0000u);
+      }
+    }
+  };
+
+  // Per pair: the reference r (log2 domain) the weights are taken against,
+  // exp2(score - r). It moves only when a score passes r + 8, so weights stay
+  // below 2^8 and the accumulators are rescaled only in those (rare) tiles.
+  float mrun[QB], lrun[QB];                 // lrun: this lane's part of the pair's sum
+  f32x4 o[QB][ND];                          // O^T: lane holds elements 16db + 4grp + i of pair r16
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    mrun[j] = kEmpty;
+    lrun[j] = 0.f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sc = p.scale_log2;
+
+  // One staged tile whose first key is slot tb. kMask: keys at or past lim,
+  // or past a pair's own limit, get weight 0 (only in tiles that reach them).
+  auto compute = [&](int tb, int lim, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      if (!cb_on[j]) continue;                // wave-uniform
+      f32x4 s[4];                             // S^T: lane holds keys 16kb + 4grp + i of pair r16
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      u32x4 ka[2][NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+        ka[0][cc] = *reinterpret_cast<const u32x4*>(sk + r16 * KR + (32 * cc + 8 * grp) * 2);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb + 1 < 4) {
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc)
+            ka[(kb + 1) & 1][cc] =
+                *reinterpret_cast<const u32x4*>(sk + (16 * (kb + 1) + r16) * KR + (32 * cc + 8 * grp) * 2);
+        }
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) s[kb] = ET::mfma(ka[kb & 1][cc], qf[j][cc], s[kb]);
+      }
+      float mx = -INFINITY;                   // raw scores: the scale is positive
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (kMask) {
+            const int key = tb + 16 * kb + 4 * grp + i;
+            s[kb][i] = (key < lim && key < plim[j]) ? s[kb][i] : -INFINITY;
+          }
+          mx = fmaxf(mx, s[kb][i]);
+        }
+      if (__any(mx * sc > mrun[j] + kLazy)) {   // wave-uniform; the first tile always
+        mx = fmaxf(mx, __shfl_xor(mx, 16));    // the pair's maximum over its four lanes
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * sc;
+        const bool up = ms > mrun[j] + kLazy;   // the four lanes of a pair agree
+        const float alpha = up ? __builtin_amdgcn_exp2f(mrun[j] - ms) : 1.f;   // 0 from the empty reference
+        mrun[j] = up ? ms : mrun[j];
+        lrun[j] *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[j][db][i] *= alpha;
+      }
+      const float nr = -mrun[j];
+      u32x4 phi[2], plo[2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        float e[8];                           // slots 8grp .. 8grp+7 of this 32-key chunk
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          e[jj] = __builtin_amdgcn_exp2f(fmaf(s[2 * kc + (jj >> 2)][jj & 3], sc, nr));   // masked: 0
+          lrun[j] += e[jj];
+        }
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ET::split(e[2 * w], e[2 * w + 1], hi[w], lo[w]);
+        phi[kc] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        plo[kc] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(svt + (16 * db + r16) * kWVtRow + (32 * kc + 8 * grp) * 2);
+          o[j][db] = ET::mfma(a, phi[kc], o[j][db]);
+          o[j][db] = ET::mfma(a, plo[kc], o[j][db]);
+        }
+    }
+  };
+
+  // The stream: a register ring of NB tiles, NB - 1 of them in flight while
+  // one is staged into LDS and computed. Tiles reaching mask_from (the end of
+  // the streamed rows, or the first slot some pair of a block may not see)
+  // are computed with the mask.
+  const int n_tiles = (t_end - t0 + kWTile - 1) / kWTile;
+  const int mask_from = p.block ? min(t_end, n - p.t_q + 1) : t_end;
+  u32x4 kr[NB][NKL], vr[NB][2 * NVP];
+#pragma unroll
+  for (int r = 0; r < NB - 1; ++r)
+    if (r < n_tiles) load_tile(krs, vrs, static_cast<uint32_t>(t0 + r * kWTile) * st, kr[r], vr[r]);
+  for (int it = 0; it < n_tiles; it += NB) {
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {            // unrolled: ring slots are compile-time
+      const int t = it + r;
+      if (t >= n_tiles) break;                // uniform
+      const int nxt = t + NB - 1;
+      if (nxt < n_tiles)
+        load_tile(krs, vrs, static_cast<uint32_t>(t0 + nxt * kWTile) * st, kr[(r + NB - 1) % NB],
+                  vr[(r + NB - 1) % NB]);
+      __syncthreads();                        // every wave is done with the previous tile
+      store_tile(kr[r], vr[r]);
+      __syncthreads();
+      const int tb = t0 + t * kWTile;
+      if (tb + kWTile > mask_from) compute(tb, t_end, std::true_type{});
+      else compute(tb, t_end, std::false_type{});
+    }
+  }
+  if (has_x) {
+    // The newest row as key 0 of one more tile: from k_new/v_new in the fused
+    // step, else from the cache; the other 63 keys read as zero (one-row
+    // range) and are masked.
+    const int xrow = n - 1;
+    const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xrow) * p.st;
+    const char* vx = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xrow) * p.st;
+    u32x4 kx_r[NKL], vx_r[2 * NVP];
+    load_tile(wrsrc(uniform_cptr(kx), D * 2), wrsrc(uniform_cptr(vx), D * 2), 0u, kx_r, vx_r);
+    __syncthreads();
+    store_tile(kx_r, vx_r);
+    __syncthreads();
+    compute(xrow, xrow + 1, std::true_type{});
+  }
+
+  // Totals per pair: the lane groups' sums.
+  float lt[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    float l = lrun[j];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    lt[j] = l;
+  }
+  auto write_out = [&](int j, const f32x4 (&acc)[ND], float l) {
+    const int v = (wave + 4 * j) * 16 + r16;
+    if (v >= gv) return;
+    const float inv = 1.f / l;
+    const int64_t row = wpair_row(p, b, g, v) * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_out(row + 16 * db + 4 * grp + i, acc[db][i] * inv);
+  };
+  if (ns == 1) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+      if (cb_on[j]) write_out(j, o[j], lt[j]);
+    return;
+  }
+
+  // Several splits: as in the other decode kernel, every split but the last
+  // publishes its partial (reference, sum, unnormalised output) and raises
+  // its ready flag to epoch + 1; the last waits for those flags, folds the
+  // partials in split order (its own from registers), writes the output and
+  // advances the unit's epoch. It has the highest workgroup id of its unit
+  // on the XCD, and a publishing workgroup never waits, so every awaited
+  // workgroup is dispatched and finishes; the wait is bounded all the same.
+  const int64_t prow0 = (static_cast<int64_t>(b) * p.n_kv + g) * gv * p.n_splits;
+  const __amdgpu_buffer_rsrc_t ors =
+      wrsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(gv) * p.n_splits * D * 4u);
+  const __amdgpu_buffer_rsrc_t mrs = wrsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(gv) * p.n_splits * 8u);
+  const __amdgpu_buffer_rsrc_t frs = wrsrc(flags, static_cast<uint32_t>(p.flag_stride) * 4u);
+  // first use of the epoch: its load (issued at entry) is waited for here,
+  // not in front of the stream
+  asm volatile("" : "+v"(epoch));
+  if (split != ns - 1) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int v = (wave + 4 * j) * 16 + r16;
+      if (!cb_on[j] || v >= gv) continue;
+      const uint32_t row = static_cast<uint32_t>(v * p.n_splits + split);
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+        wstore(ors, (row * D + 16 * db + 4 * grp) * 4u,
+               u32x4{__float_as_uint(o[j][db][0]), __float_as_uint(o[j][db][1]), __float_as_uint(o[j][db][2]),
+                     __float_as_uint(o[j][db][3])});
+      if (grp == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mrun[j]), mrs, static_cast<int>(row * 8u), 0, kXchgW);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt[j]), mrs, static_cast<int>(row * 8u + 4u), 0, kXchgW);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>(split * 4), 0, kXchgW);
+    return;
+  }
+  for (int k = tid; k < ns - 1; k += blockDim.x) {
+    int spins = 0;
+    for (;;) {
+#if KVC_XCHG_L2_POLL
+      // (a compare-and-swap that writes back what it finds: an atomic, so it
+      // is performed in L2 and returns L2's value; an idempotent add or load
+      // would be turned into a load the CU's L1 may serve)
+      uint32_t f = epoch + 1u;
+      __hip_atomic_compare_exchange_strong(flags + k, &f, epoch + 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+#else
+      const uint32_t f = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(frs, k * 4, 0, kXchgW));
+#endif
+      if (f == epoch + 1u) break;
+      if (++spins > p.merge_spins) {           // never expected: flag the call, do not hang
+        if (p.status != nullptr) atomicOr(p.status, KVC_DEVERR_SYNC);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      asm volatile("" ::: "memory");
+    }
+  }
+  __syncthreads();
+  // Fold the splits in split order, two per round trip: running reference
+  // mm, sum ll and accumulators acc; this workgroup's own split (the last)
+  // from registers.
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int v = (wave + 4 * j) * 16 + r16;
+    if (!cb_on[j]) continue;
+    const uint32_t vrow = static_cast<uint32_t>((v < gv ? v : 0) * p.n_splits);
+    float mm = -INFINITY, ll = 0.f;
+    f32x4 acc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ns; k0 += 2) {
+      float rb[2], lb[2];
+      u32x4 ob[2][ND];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint32_t row = vrow + static_cast<uint32_t>(k0 + kk);
+        rb[kk] = __uint_as_float(static_cast<uint32_t>(
+            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u), 0, kXchgW)));
+        lb[kk] = __uint_as_float(static_cast<uint32_t>(
+            __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u + 4u), 0, kXchgW)));
+#pragma unroll
+        for (int db = 0; db < ND; ++db) ob[kk][db] = wload<kXchgW>(ors, (row * D + 16 * db + 4 * grp) * 4u);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k = k0 + kk;
+        if (k >= ns) break;                    // uniform
+        float r_k = rb[kk], l_k = lb[kk];
+        if (k == split) {                      // own split: from registers
+          r_k = mrun[j];
+          l_k = lt[j];
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+            ob[kk][db] = u32x4{__float_as_uint(o[j][db][0]), __float_as_uint(o[j][db][1]),
+                               __float_as_uint(o[j][db][2]), __float_as_uint(o[j][db][3])};
+        }
+        const float nm = fmaxf(mm, r_k);
+        const float c1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm - nm);
+        const float c2 = __builtin_amdgcn_exp2f(r_k - nm);
+        ll = ll * c1 + l_k * c2;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * c1 + __uint_as_float(ob[kk][db][i]) * c2;
+        mm = nm;
+      }
+    }
+    write_out(j, acc, ll);
+  }
+  // the next call on this workspace waits for flags of epoch + 2
+  if (tid == 0)
+    __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>((p.flag_stride - 1) * 4), 0, kXchgW);
+}
+
+typedef void (*WideKernel)(const WideParams);
+
+template <typename ET, int D>
+WideKernel pick_wide_qb(int qb) {
+  return qb <= 1 ? wide_decode_kernel<ET, D, 1> : wide_decode_kernel<ET, D, 2>;
+}
+
+WideKernel pick_wide_kernel(int32_t dtype, int32_t d, int qb) {
+  if (dtype == KVC_BF16 && d == 128) return pick_wide_qb<Bf16P, 128>(qb);
+  if (dtype == KVC_BF16 && d == 64) return pick_wide_qb<Bf16P, 64>(qb);
+  if (dtype == KVC_F16 && d == 128) return pick_wide_qb<F16P, 128>(qb);
+  if (dtype == KVC_F16 && d == 64) return pick_wide_qb<F16P, 64>(qb);
+  return nullptr;
+}
+
+}  // namespace
+
+bool kvc::wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs) {
+  return (dtype == KVC_BF16 || dtype == KVC_F16) && (head_dim == 64 || head_dim == 128) &&
+         pairs >= KVC_WIDE_MIN_PAIRS && pairs <= 128;
+}
+
+kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
+                              const void* k_new, const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
+                              const void* q, int32_t n_q_heads, int32_t t_q, float scale_log2, void* out,
+                              int32_t out_dtype, const kvc::WsRegions& ws, int32_t splits, int32_t* lens_next,
+                              uint32_t* dev_status, hipStream_t stream) {
+  // (arguments validated by the caller)
+  const int s = kvc::elem_bytes(cache->dtype);
+  const int32_t tq = t_q > 0 ? t_q : 1;
+  const int32_t group = n_q_heads / cache->n_kv_heads;
+  const int32_t pairs = group * tq;
+  const int qb = (pairs + 63) / 64;
+  WideKernel kern = pick_wide_kernel(cache->dtype, cache->head_dim, qb);
+  if (kern == nullptr || qb > 2) return KVC_ERR_UNSUPPORTED;
+  WideParams p;
+  p.k = static_cast<char*>(cache->k);
+  p.v = static_cast<char*>(cache->v);
+  p.sb = cache->stride_b * s;
+  p.sh = cache->stride_h * s;
+  p.st = cache->stride_t * s;
+  p.seq_lens = seq_lens;
+  p.q = static_cast<const char*>(q);
+  p.k_new = static_cast<const char*>(k_new);
+  p.v_new = static_cast<const char*>(v_new);
+  p.nsb = new_stride_b * s;
+  p.nsh = new_stride_h * s;
+  p.ws_flag = ws.flags;
+  p.flag_stride = ws.flag_stride;
+  p.ws_o = ws.o;
+  p.ws_ml = ws.ml;
+  p.lens_next = lens_next;
+  p.out = out;
+  p.status = dev_status;
+  p.batch = cache->batch;
+  p.n_q = n_q_heads;
+  p.n_kv = cache->n_kv_heads;
+  p.group = group;
+  p.n_hblk = kvc::head_blocks(pairs);
+  p.max_len = cache->max_len;
+  p.n_pending = n_pending;
+  p.n_splits = splits;
+  p.out_f32 = out_dtype == KVC_F32 ? 1 : 0;
+  p.t_q = tq;
+  p.block = t_q > 0 ? 1 : 0;
+  p.scale_log2 = scale_log2;
+  p.merge_spins = kvc::merge_spin_limit();
+  const int64_t units = static_cast<int64_t>(cache->batch) * cache->n_kv_heads;
+  const int64_t wgs = (units + 7) / 8 * 8 * splits;    // see the placement in the kernel
+  if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}

@@ -368,7 +368,9 @@ def test_splits_for_lengths_model_choices():
     assert pick(16, 8, 2100, 128, kvc.KVC_BF16, 32, [2049] * 16) == (2, 2)
     assert pick(1, 32, 4130, 128, kvc.KVC_F16, 32, [4097]) == (8, 8)
     assert pick(32, 8, 8300, 128, kvc.KVC_BF16, 64, [8193] * 32) == (1, 1)
-    assert pick(32, 1, 8300, 128, kvc.KVC_BF16, 64, [8193] * 32) == (1, 1)
+    # 64 query heads on one KV head run on the wide-group kernel, one
+    # workgroup per (sequence, KV head) and split: 32 units need 8 splits
+    assert pick(32, 1, 8300, 128, kvc.KVC_BF16, 64, [8193] * 32) == (8, 8)
     ragged = synth.CONFIGS["ragged_long"].lengths(7).numpy() + 1
     assert pick(24, 32, 6100, 128, kvc.KVC_F16, 32, ragged) == (1, 1)
     assert pick(24, 32, 4096, 128, kvc.KVC_F16, 32, [min(int(x), 4096) for x in ragged]) == (1, 1)   # ring, W=4096

@@ -161,6 +161,28 @@ def test_negative_length_is_flagged_and_treated_as_empty(gpu):
     assert torch.all(out == 0)
 
 
+@pytest.mark.parametrize("n_q", [8, 32])
+def test_negative_length_in_the_fused_step_gives_a_zero_row(gpu, n_q):
+    """The fused step with a negative length: nothing written, nothing
+    attended, a zero row and KVC_DEVERR_BADLEN (group 4 on the 8-head-block
+    kernel, group 32 on the wide-group kernel); the other sequence is right."""
+    case = DecodeCase(batch=2, n_q=n_q, n_kv=1, head_dim=128, dtype="bf16", lengths=[40, 9], tag=f"negstep{n_q}",
+                      device=gpu)
+    k, v = case.oracle_inputs(0, 0)
+    ref0 = oracle.decode_attention(case.q_host[0:1], k[None, None], v[None, None], np.array([40]), n_pending=1)[0]
+    case.seq_lens.copy_(torch.tensor([40, -2], dtype=torch.int32))
+    before = case.k[1].clone()
+    ws = kvc.workspace(case.k, case.v, n_q)
+    out = torch.full((2, n_q, 128), 3.0, device=gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    kvc.decode_step(case.k, case.v, case.seq_lens, case.k_new, case.v_new, case.q, out, ws, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & kvc.DEVERR_BADLEN
+    assert torch.all(out[1] == 0)
+    assert torch.equal(case.k[1].view(torch.int16), before.view(torch.int16))
+    assert np.abs(out[0].double().cpu().numpy() - ref0).max() <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_output_in_cache_dtype_is_rne_of_fp32_output(gpu, dtype):
     """out_dtype = cache dtype gives exactly the fp32 result rounded to nearest
@@ -215,14 +237,33 @@ def _full_size_case(name, rng_units=6):
 
 @pytest.mark.parametrize("name", ["mha_7b", "gqa_8b", "ragged_long", "gqa_70b", "mqa_70b"])
 def test_full_size_layer_sampled_units(gpu, name):
-    """One layer at the workload's full shape and the same launch (auto split
-    count) the benchmark times; the oracle checks sampled (sequence, KV head)
-    units, all query heads of each."""
+    """One layer at the workload's full shape through the entry point the
+    benchmark times, kvc_decode_step (append, then attend T_b + 1 tokens, in
+    one launch: course notes "第 1 周 · Day 4" §1.3), with the split count the
+    benchmark takes (the length-aware choice for the attended lengths). The
+    oracle checks sampled (sequence, KV head) units, all query heads of each;
+    the appended rows are checked bit for bit; and the unfused calls
+    (kvc_append + kvc_decode_attn, same split count) give the same bits."""
     cfg, case = _full_size_case(name)
-    out, status = _run(case)
-    assert status == 0
-    worst = _check_all(case, out)
-    print(f"{name}: max-abs {worst:.3e} over {len(case.host)} units")
+    dev = case.q.device
+    attended = [int(n) + 1 for n in case.lengths]
+    splits = kvc.decode_splits(case.k, case.v, case.n_q, lengths=attended)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = kvc.workspace(case.k, case.v, case.n_q, splits)
+    out_step = torch.empty((case.batch, case.n_q, case.head_dim), dtype=torch.float32, device=dev)
+    kvc.decode_step(case.k, case.v, case.seq_lens, case.k_new, case.v_new, case.q, out_step, ws,
+                    n_splits=splits, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    worst = _check_all(case, out_step)
+    for b, g in case.host:
+        t = int(case.lengths[b])
+        assert torch.equal(case.k[b, g, t].cpu().view(torch.int16), case.host[(b, g)][2].view(torch.int16))
+        assert torch.equal(case.v[b, g, t].cpu().view(torch.int16), case.host[(b, g)][3].view(torch.int16))
+    out, status2 = _run(case, n_splits=splits)     # appends the same rows again, then attends
+    assert status2 == 0
+    assert torch.equal(out, out_step)
+    print(f"{name}: {splits} split(s), max-abs {worst:.3e} over {len(case.host)} units")
 
 
 def test_length_aware_split_choice_on_a_very_uneven_batch(gpu):

@@ -114,7 +114,13 @@ def test_paged_decode_matches_oracle_and_contiguous(gpu, dtype, page, hq, hkv):
     kvc.append(c.k, c.v, lens1, c.k_new, c.v_new)
     got = _paged_out(c)
     ref_c = _contig_out(c)
-    assert torch.equal(got, ref_c)                 # paging changes where rows live, not the result
+    # paging changes where rows live, not the result: the same kernel gives
+    # the same bits; a contiguous cache with 16+ query heads per KV head runs
+    # on the wide-group kernel (paged caches do not), another summation order
+    if hq // hkv >= 16:
+        assert (got - ref_c).abs().max().item() <= 2 * TOL[dtype]
+    else:
+        assert torch.equal(got, ref_c)
     table = c.table.cpu().tolist()
     ref = oracle.paged_decode_attention(c.q.cpu(), c.kp.cpu(), c.vp.cpu(), table, c.lengths.numpy(), n_pending=1)
     assert np.abs(got.double().cpu().numpy() - ref).max() <= TOL[dtype]

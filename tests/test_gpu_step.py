@@ -48,9 +48,9 @@ def _host_layer(k, v, lens):
 
 
 def test_many_steps_many_layers_one_workspace(gpu):
-    """Three layers, eight steps, one shared workspace (its tickets must come
-    back to zero after every launch); every output against the oracle on host
-    copies that follow the appends."""
+    """Three layers, eight steps, one shared workspace (its merge epochs move
+    on with every launch and no flag is ever cleared); every output against
+    the oracle on host copies that follow the appends."""
     L, B, hq, hkv, d = 3, 4, 8, 2, 128
     lens0 = [5, 130, 0, 513]
     t_max = max(lens0) + 9
@@ -71,7 +71,13 @@ def test_many_steps_many_layers_one_workspace(gpu):
             outs.append((out, q.cpu(), kn.cpu(), vn.cpu()))
         kvc.seq_lens_advance(seq, 1)
         torch.cuda.synchronize()
-        assert int(ws[:256].view(torch.int32).abs().sum()) == 0     # tickets back to zero
+        # two splits per (sequence, KV head) here; sequences 1 and 3 merge in
+        # every call (3 layers per step), 0 and 2 are short enough for one
+        # split: each merge raised the publisher's flag to the block's epoch
+        # + 1 and then advanced the epoch (word 1), and nothing else moved
+        words = ws[:64].view(torch.int32).cpu().view(B * hkv, 2)
+        merges = [L * (step + 1) if b in (1, 3) else 0 for b in range(B) for _ in range(hkv)]
+        assert words[:, 1].tolist() == merges and words[:, 0].tolist() == merges
         for l, (out, q, kn, vn) in enumerate(outs):
             hk, hv = host[l]
             for bb in range(B):
@@ -165,3 +171,48 @@ def test_hip_graph_replay_matches_eager(gpu):
             assert torch.equal(oe, og), rep
         for ce, cg in zip(eager[0], graphed[0]):
             assert torch.equal(ce.k.view(torch.int16), cg.k.view(torch.int16))
+
+
+def test_workspace_stays_usable_after_a_merge_gives_up(gpu):
+    """The split merge's wait is bounded: a merger that gives up reports
+    KVC_DEVERR_SYNC and that call's outputs are not valid. The test hook
+    sets the bound to a single poll, so mergers that find a partner's flag not
+    yet raised give up at once; their partners raise the flag afterwards, in
+    the same launch. The next calls on the same workspace, with the default
+    bound and other queries, must wait for their own partners (a late flag
+    holds the previous epoch's value) and match the oracle with no status bit."""
+    lens = [2048] * 16
+    case = DecodeCase(batch=16, n_q=32, n_kv=8, head_dim=128, dtype="bf16", lengths=lens, tag="syncrec",
+                      device=gpu, host_rows=[(0, 0), (7, 3), (15, 7)])
+    kvc.append(case.k, case.v, case.seq_lens, case.k_new, case.v_new)
+    ws = kvc.workspace(case.k, case.v, case.n_q, 2)
+    out = torch.empty((case.batch, case.n_q, 128), device=gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    qs = [synth.normal((case.batch, case.n_q, 128), "bf16", 7, "syncrec", "q", i, device=gpu) for i in range(4)]
+    prev = kvc.debug_set_merge_spin_limit(0)
+    gave_up = 0
+    try:
+        for i in range(8):                    # until some merge gives up
+            status.zero_()
+            kvc.decode_attn(case.k, case.v, case.seq_lens, qs[i % 2], out, ws, n_pending=1, n_splits=2,
+                            status=status)
+            torch.cuda.synchronize()
+            if int(status.item()) & kvc.DEVERR_SYNC:
+                gave_up = i + 1
+                break
+    finally:
+        kvc.debug_set_merge_spin_limit(prev)
+    print(f"a merge gave up on call {gave_up}" if gave_up else "no merge gave up in 8 calls")
+    grp = case.n_q // case.n_kv
+    for q in qs[2:]:                           # queries no earlier call used
+        status.zero_()
+        kvc.decode_attn(case.k, case.v, case.seq_lens, q, out, ws, n_pending=1, n_splits=2, status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        got = out.double().cpu().numpy()
+        qh = q.cpu()
+        for (b, g) in case.host:
+            k, v = case.oracle_inputs(b, g)
+            ref = oracle.decode_attention(qh[b:b + 1, g * grp:(g + 1) * grp], k[None, None], v[None, None],
+                                          np.array([lens[b]]), n_pending=1)[0]
+            assert np.abs(got[b, g * grp:(g + 1) * grp] - ref).max() <= TOL["bf16"]

@@ -547,6 +547,30 @@ def test_paged_append_writes_one_slot_through_the_table():
     assert {(int(p), int(r)) for p, _, r, _ in changed} == {(1, 2)}
 
 
+def test_paged_fill_skips_only_the_rows_of_a_page_outside_the_pool():
+    """Reading R29 (the pages leave invalid page-table entries open): a block
+    of 12 rows over pages of 4, whose middle page id is outside the pool,
+    still writes the 8 rows of its two valid pages; the 4 rows of the bad
+    page are not written anywhere, and the sequence is reported. The other
+    sequence is written in full and not reported."""
+    n_pages, hkv, psz, d = 5, 1, 4, 2
+    kp = np.full((n_pages, hkv, psz, d), -1.0)
+    vp = np.full((n_pages, hkv, psz, d), -2.0)
+    table = [[3, 7, 0], [1, 2, 4]]                      # page 7 is not in the pool of 5
+    k = np.arange(2 * hkv * 12 * d, dtype=np.float64).reshape(2, hkv, 12, d)
+    v = k + 1000.0
+    k2, v2, flagged = oracle.paged_prefill_fill(kp, vp, table, np.array([0, 0]), k, v)
+    assert flagged.tolist() == [True, False]
+    assert np.array_equal(k2[3, :, :, :], k[0, :, 0:4]) and np.array_equal(v2[3], v[0, :, 0:4])
+    assert np.array_equal(k2[0, :, :, :], k[0, :, 8:12]) and np.array_equal(v2[0], v[0, :, 8:12])
+    for p, rows in ((1, slice(0, 4)), (2, slice(4, 8)), (4, slice(8, 12))):
+        assert np.array_equal(k2[p], k[1, :, rows]) and np.array_equal(v2[p], v[1, :, rows])
+    # every pool row is accounted for: sequence 0's rows 4..7 went nowhere
+    written = {3, 0, 1, 2, 4}
+    assert written == set(range(n_pages))
+    assert not np.isin(k[0, :, 4:8], k2).any()
+
+
 # ----------------------------------------------------------- sliding window --
 
 def _ring_from_history(k_hist, v_hist, window):
