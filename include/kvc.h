@@ -264,6 +264,29 @@ kvc_status_t kvc_decode_step_advance(const kvc_cache_t* cache, const int32_t* se
                                      uint32_t* dev_status, hipStream_t stream);
 
 /*
+ * kvc_decode_step_noalloc -- kvc_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid hipMalloc): no workspace argument, and the call allocates
+ * nothing. The split exchange (ready flags with their epochs, partial
+ * results) lives in a device array of the library, 16 MiB on each GPU it
+ * runs on, allocated when the library is loaded there and held until the
+ * process ends. Calls of any geometry may follow one another on it. A call
+ * whose exchange does not fit -- more than 2048 (sequence, KV head, block of
+ * query heads) rows, or more partial results than the rest of the array holds
+ * (batch * n_q_heads * splits * (head_dim + 2) * 4 bytes, about 14 MiB) --
+ * returns KVC_ERR_WORKSPACE before anything is enqueued. Every call on one
+ * GPU uses the same array: calls that overlap in time on one GPU (on two
+ * streams) race and must not be issued. Results are bit-identical to
+ * kvc_decode_step with the same n_splits. Other arguments as kvc_decode_step.
+ */
+kvc_status_t kvc_decode_step_noalloc(const kvc_cache_t* cache, const int32_t* seq_lens,
+                                     const void* k_new, const void* v_new,
+                                     int64_t new_stride_b, int64_t new_stride_h,
+                                     const void* q, int32_t n_q_heads, float scale,
+                                     void* out, int32_t out_dtype, int32_t n_splits,
+                                     uint32_t* dev_status, hipStream_t stream);
+
+/*
  * kvc_block_attn -- a block of t_q new tokens per sequence (a prefill chunk
  * or a speculative verify step) attends the cache with the causal mask
  * aligned to the lower right (course notes "第 1 周 · Day 4" §3.3, masks with

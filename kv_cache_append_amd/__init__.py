@@ -34,7 +34,8 @@ STATUS = {
 
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
-           "kvc_decode_attn", "kvc_decode_step", "kvc_decode_step_advance", "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes",
+           "kvc_decode_attn", "kvc_decode_step", "kvc_decode_step_advance", "kvc_decode_step_noalloc",
+           "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes",
            "kvc_prefill_attn",
            "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
            "kvc_paged_decode_attn", "kvc_paged_decode_step",
@@ -139,6 +140,8 @@ def load() -> ctypes.CDLL:
     lib.kvc_debug_set_merge_spin_limit.restype = i32
     lib.kvc_decode_step_advance.argtypes = [cp, vp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_decode_step_advance.restype = i32
+    lib.kvc_decode_step_noalloc.argtypes = [cp, vp, vp, vp, i64, i64, vp, i32, f32, vp, i32, i32, vp, vp]
+    lib.kvc_decode_step_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -329,6 +332,24 @@ def decode_step(k_cache, v_cache, seq_lens, k_new, v_new, q, out, workspace, sca
                                k_new.stride(1), _ptr(q), q.shape[1], float(scale), _ptr(out),
                                DTYPE_CODE[out.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
                                n_splits, _ptr(status), _stream(stream)), "kvc_decode_step")
+
+
+def decode_step_noalloc(k_cache, v_cache, seq_lens, k_new, v_new, q, out, scale=None, n_splits: int = 0,
+                        status=None, stream=None, desc=None):
+    """kvc_decode_step_noalloc: kvc_decode_step with the split exchange in the
+    library's own device array instead of a workspace (nothing allocated)."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B, H_q, D]")
+    if k_new.stride() != v_new.stride() or k_new.dim() != 3:
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with equal strides")
+    _check(lib.kvc_decode_step_noalloc(ctypes.byref(c), _ptr(seq_lens), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+                                       k_new.stride(1), _ptr(q), q.shape[1], float(scale), _ptr(out),
+                                       DTYPE_CODE[out.dtype], n_splits, _ptr(status), _stream(stream)),
+           "kvc_decode_step_noalloc")
 
 
 def block_attn(k_cache, v_cache, seq_lens, q, out, workspace, scale=None, n_splits: int = 0, status=None,

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 
 ARCH = "gfx950"
-SOURCES = ["kvc_host.cpp", "kvc_kernels.hip", "kvc_calib.hip", "kvc_prefill.hip", "kvc_wide.hip"]
+SOURCES = ["kvc_host.cpp", "kvc_kernels.hip", "kvc_calib.hip", "kvc_prefill.hip", "kvc_wide.hip", "kvc_noalloc.hip"]
 
 # Packed-FP32 VALU ops (v_pk_*_f32) are turned off for all device code: the
 # kernels are written as scalar fp32 arithmetic and must compile to it.
