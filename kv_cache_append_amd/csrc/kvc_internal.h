@@ -18,10 +18,10 @@
 // to L2), ready flags polled with L2 atomics (KVC_XCHG_L2_POLL), and plain
 // loads of partials the merging CU has not read before in the launch.
 #ifndef KVC_XCD_COLOCATE
-#define KVC_XCD_COLOCATE 0
+#define KVC_XCD_COLOCATE 1
 #endif
 #ifndef KVC_LOCAL_EXCHANGE
-#define KVC_LOCAL_EXCHANGE 0
+#define KVC_LOCAL_EXCHANGE 1
 #endif
 #if KVC_XCD_COLOCATE && KVC_LOCAL_EXCHANGE
 #define KVC_XCHG_POLICY 0
