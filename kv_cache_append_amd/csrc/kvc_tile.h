@@ -30,14 +30,13 @@ struct Bf16P {
     hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
     lo = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
   }
-  __device__ static inline void store(void* base, int64_t i, float x) {
-    // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN
+  // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN
+  __device__ static inline uint16_t bits(float x) {
     const uint32_t u = __float_as_uint(x);
-    uint16_t h;
-    if ((u & 0x7fffffffu) > 0x7f800000u) h = static_cast<uint16_t>((u >> 16) | 0x40u);
-    else h = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    static_cast<uint16_t*>(base)[i] = h;
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
   }
+  __device__ static inline void store(void* base, int64_t i, float x) { static_cast<uint16_t*>(base)[i] = bits(x); }
 };
 
 struct F16P {
@@ -53,10 +52,13 @@ struct F16P {
     hi = __builtin_bit_cast(uint32_t, h);
     lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
   }
-  __device__ static inline void store(void* base, int64_t i, float x) {
-    asm volatile("" : "+v"(x));   // keep the fp32 value: one rounding, to nearest even
-    static_cast<_Float16*>(base)[i] = static_cast<_Float16>(x);
+  // fp32 -> fp16 bits, round to nearest even (the fp32 value is pinned
+  // first, so the conversion is one rounding of it)
+  __device__ static inline uint16_t bits(float x) {
+    asm volatile("" : "+v"(x));
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
   }
+  __device__ static inline void store(void* base, int64_t i, float x) { static_cast<uint16_t*>(base)[i] = bits(x); }
 };
 
 // Buffer resource over [base, base + bytes): loads past the end return zero.

@@ -45,6 +45,13 @@ namespace {
 
 constexpr int kWTile = 64;       // keys per LDS tile
 constexpr int kWVtRow = 144;     // bytes per transposed-V row in LDS: 64 keys + 8 elements of padding
+
+// Transposed V in LDS: row d holds the tile's 64 keys (slot order, 8 chunks of
+// 16 bytes), chunk c stored at c ^ vt_swz(d). The staging writes rows 8 apart
+// from the lanes of one instruction; without the swizzle they would all fall
+// on the same banks (the padding only separates neighbouring rows, which the
+// output product reads together).
+__device__ inline int vt_swz(int d) { return (d >> 3) & 7; }
 constexpr int kNt = 2;           // cache policy of the K/V stream: non-temporal (each row read once)
 constexpr int kXchgW = KVC_XCHG_POLICY;
 
@@ -68,6 +75,7 @@ struct WideParams {
   uint32_t* status;
   int32_t batch, n_q, n_kv, group, n_hblk, max_len, n_pending, n_splits, out_f32;
   int32_t t_q, block;            // block of t_q queries (lower-right causal mask), or decode (block = 0)
+  int32_t out_vec;               // out is 16-byte aligned: four elements per store
   float scale_log2;              // softmax scale * log2(e)
   int32_t merge_spins;           // bound on the merge's wait for ready flags (polls)
   int32_t flag_stride;           // words per flag row (>= n_splits); the last is the epoch
@@ -80,6 +88,13 @@ __device__ inline __amdgpu_buffer_rsrc_t wrsrc(const void* base, uint32_t bytes)
 template <int kPolicy>
 __device__ inline u32x4 wload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kPolicy));
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Load of W words (4: 16 bytes, 2: 8 bytes)
+template <int W, int kPolicy>
+__device__ inline auto wloadw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (W == 4) return wload<kPolicy>(r, off);
+  else return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, kPolicy));
 }
 __device__ inline void wstore(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), r,
@@ -101,23 +116,45 @@ __device__ inline int64_t wpair_row(const WideParams& p, int b, int g, int v) {
 }
 
 // ET: Bf16P or F16P (the cache dtype); QB: column blocks of 16 pairs per wave.
+//
+// Eight waves: wave w takes column blocks (w % 4) + 4j and the half w / 4 of
+// every 64-key tile (keys 32 kh .. 32 kh + 31), so two waves of a SIMD work
+// side by side on each tile and hide each other's LDS and matrix-core
+// latency. The two halves' softmax states are merged through LDS at the end,
+// each wave keeping half of the head dim; the split merge then runs on all
+// eight waves, each over its (column block, half of D).
 template <typename ET, int D, int QB>
-__global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p) {
+__global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p) {
+  constexpr int NT = 512;               // threads per workgroup
   constexpr int NC = D / 32;            // 32-element slices of a row (score product depth)
   constexpr int ND = D / 16;            // 16-element output blocks
+  constexpr int NDH = ND / 2;           // output blocks of a wave after the halves merge
   constexpr int KR = 2 * D + 16;        // bytes per K row in LDS (16 bytes of padding)
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int NKL = kWTile * CPR / 256;   // 16-byte K loads per thread per tile
-  constexpr int NVP = D / 64;           // V passes per tile, two 16-byte loads (two keys) each
-  constexpr int NB = KVC_WIDE_PREFETCH + 1;
+  constexpr int NKL = kWTile * CPR / NT;   // 16-byte K loads per thread per tile
+  constexpr int VW = D / 32;            // V words per key and thread: every thread stages two keys' VW words
+  // register tiles: two in flight behind the one staged (one with two column
+  // blocks per wave, whose accumulators need the registers)
+  constexpr int NB = QB == 1 ? KVC_WIDE_PREFETCH + 1 : 2;
   constexpr float kLazy = 8.f;          // the reference moves only past ref + 8 (log2 domain)
   // Reference of a pair that has seen no key: finite, so that exp2 of a
   // masked (-inf) score against it is 0 rather than NaN, and far below any
   // score, so the first key seen replaces it (and zeroes its weight).
   constexpr float kEmpty = -1e30f;
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  __shared__ __attribute__((aligned(16))) char sk[kWTile * KR];
-  __shared__ __attribute__((aligned(16))) char svt[D * kWVtRow];
+  static_assert(NKL >= 1 && 32 * (D / (2 * VW)) == NT, "tile loads");
+  using VVec = std::conditional_t<VW == 4, u32x4, u32x2>;
+  constexpr int NDH_ = D / 32;
+  // LDS: a K tile and a transposed V tile during the stream; at the end the
+  // halves each wave passes its partner ([8 waves][QB][NDH][64 lanes] f32x4)
+  // and the references and sums ([8 waves][QB][64 lanes][2]).
+  constexpr int kTileBytes = kWTile * KR + D * kWVtRow;
+  constexpr int kXoBytes = 8 * QB * NDH_ * 64 * 16;
+  constexpr int kXmlBytes = 8 * QB * 64 * 8;
+  constexpr int kLds = kTileBytes > kXoBytes + kXmlBytes ? kTileBytes : kXoBytes + kXmlBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kLds];
+  char* const sk = smem;
+  char* const svt = smem + kWTile * KR;
 
   // Workgroup placement: every split of a unit on one XCD (id residue mod 8),
   // the unit's splits in consecutive slots there, the merging split last.
@@ -179,6 +216,8 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cbw = wave & 3;                          // first column block of this wave
+  const int kh = wave >> 2;                          // which half of each tile's keys
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   const int ncb = (gv + 15) / 16;
@@ -193,14 +232,14 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
   }
 
   // The wave's pairs as B operands of the score product (column = pair r16
-  // of column block wave + 4j, 8 elements 32c + 8grp of its query row), and
+  // of column block cbw + 4j, 8 elements 32c + 8grp of its query row), and
   // each pair's slot limit (lower-right causal mask of a query block).
   u32x4 qf[QB][NC];
   int plim[QB];
   bool cb_on[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const int cb = wave + 4 * j;
+    const int cb = cbw + 4 * j;
     cb_on[j] = cb < ncb;
     const int v = cb * 16 + r16;
     plim[j] = p.block ? n - p.t_q + v / p.group + 1 : n;
@@ -219,42 +258,43 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
   const __amdgpu_buffer_rsrc_t krs = wrsrc(kunit, static_cast<uint32_t>(t_end) * st);
   const __amdgpu_buffer_rsrc_t vrs = wrsrc(vunit, static_cast<uint32_t>(t_end) * st);
 
-  // Tile staging: thread tid loads K chunks tid + 256m (row idx / CPR, chunk
-  // idx % CPR) and V rows 2kp, 2kp + 1 (kp = tid % 32) at chunk tid / 32 + 8ps.
+  // Tile staging: thread tid loads K chunks tid + NT m (row idx / CPR, chunk
+  // idx % CPR) and, of V, elements 2 VW dc .. + 2 VW - 1 (dc = tid % 16) of
+  // rows 2kp and 2kp + 1 (kp = tid / 16), so that each load instruction
+  // reads whole rows (partial-line requests from many rows at once halved
+  // the stream rate on MI355X). Every thread does the same loads
+  // and LDS stores, with no branch around them: a load or a use of its
+  // registers under a branch makes the compiler's wait counting lose track of
+  // the loads in flight and wait for nearly all of them, which empties the
+  // ring at every tile.
+  const uint32_t v_off = static_cast<uint32_t>(2 * (tid >> 4)) * st + static_cast<uint32_t>(tid & 15) * (4u * VW);
   auto load_tile = [&](__amdgpu_buffer_rsrc_t kr_, __amdgpu_buffer_rsrc_t vr_, uint32_t base, u32x4 (&kr)[NKL],
-                       u32x4 (&vr)[2 * NVP]) {
+                       VVec (&vr)[2]) {
 #pragma unroll
     for (int m = 0; m < NKL; ++m) {
-      const int idx = tid + 256 * m;
+      const int idx = tid + NT * m;
       kr[m] = wload<kNt>(kr_, base + static_cast<uint32_t>(idx / CPR) * st + static_cast<uint32_t>(idx % CPR) * 16u);
     }
-#pragma unroll
-    for (int ps = 0; ps < NVP; ++ps) {
-      const int kp = tid & 31;
-      const int dc = (tid >> 5) + 8 * ps;
-      vr[2 * ps] = wload<kNt>(vr_, base + static_cast<uint32_t>(2 * kp) * st + dc * 16u);
-      vr[2 * ps + 1] = wload<kNt>(vr_, base + static_cast<uint32_t>(2 * kp + 1) * st + dc * 16u);
-    }
+    vr[0] = wloadw<VW, kNt>(vr_, base + v_off);
+    vr[1] = wloadw<VW, kNt>(vr_, base + v_off + st);
   };
-  auto store_tile = [&](const u32x4 (&kr)[NKL], const u32x4 (&vr)[2 * NVP]) {
+  auto store_tile = [&](const u32x4 (&kr)[NKL], const VVec (&vr)[2]) {
 #pragma unroll
     for (int m = 0; m < NKL; ++m) {
-      const int idx = tid + 256 * m;
+      const int idx = tid + NT * m;
       *reinterpret_cast<u32x4*>(sk + (idx / CPR) * KR + (idx % CPR) * 16) = kr[m];
     }
+    const int kp = tid >> 4;
+    const int dc = tid & 15;
+    const int key0 = 2 * kp;                             // keys key0, key0 + 1 share one word
+    const int col = (32 * (key0 >> 5) + vt_slot(key0 & 31)) * 2;
+    const int d0 = 2 * VW * dc;                          // rows d0 .. d0 + 2 VW - 1: one swizzle
+    char* const vrow = svt + d0 * kWVtRow + ((((col >> 4) ^ vt_swz(d0)) << 4) | (col & 15));
 #pragma unroll
-    for (int ps = 0; ps < NVP; ++ps) {
-      const int kp = tid & 31;
-      const int dc = (tid >> 5) + 8 * ps;
-      const int key0 = 2 * kp;                           // keys key0, key0 + 1 share one word
-      const int col = (32 * (key0 >> 5) + vt_slot(key0 & 31)) * 2;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t w0 = vr[2 * ps][m], w1 = vr[2 * ps + 1][m];
-        const int d = 8 * dc + 2 * m;
-        *reinterpret_cast<uint32_t*>(svt + d * kWVtRow + col) = (w0 & 0xffffu) | (w1 << 16);
-        *reinterpret_cast<uint32_t*>(svt + (d + 1) * kWVtRow + col) = (w0 >> 16) | (w1 & 0xffff0000u);
-      }
+    for (int m = 0; m < VW; ++m) {
+      const uint32_t w0 = vr[0][m], w1 = vr[1][m];
+      *reinterpret_cast<uint32_t*>(vrow + 2 * m * kWVtRow) = (w0 & 0xffffu) | (w1 << 16);
+      *reinterpret_cast<uint32_t*>(vrow + (2 * m + 1) * kWVtRow) = (w0 >> 16) | (w1 & 0xffff0000u);
     }
   };
 
@@ -272,41 +312,37 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
   }
   const float sc = p.scale_log2;
 
-  // One staged tile whose first key is slot tb. kMask: keys at or past lim,
-  // or past a pair's own limit, get weight 0 (only in tiles that reach them).
+  // This wave's half of one staged tile whose first key is slot tb (keys
+  // tb + 32 kh .. + 31). kMask: keys at or past lim, or past a pair's own
+  // limit, get weight 0 (only in tiles that reach them).
   auto compute = [&](int tb, int lim, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       if (!cb_on[j]) continue;                // wave-uniform
-      f32x4 s[4];                             // S^T: lane holds keys 16kb + 4grp + i of pair r16
+      f32x4 s[2];                             // S^T: lane holds keys 32kh + 16kk + 4grp + i of pair r16
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 2; ++kk) s[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
       u32x4 ka[2][NC];
 #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+          ka[kk][cc] = *reinterpret_cast<const u32x4*>(sk + (32 * kh + 16 * kk + r16) * KR + (32 * cc + 8 * grp) * 2);
+#pragma unroll
       for (int cc = 0; cc < NC; ++cc)
-        ka[0][cc] = *reinterpret_cast<const u32x4*>(sk + r16 * KR + (32 * cc + 8 * grp) * 2);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb + 1 < 4) {
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc)
-            ka[(kb + 1) & 1][cc] =
-                *reinterpret_cast<const u32x4*>(sk + (16 * (kb + 1) + r16) * KR + (32 * cc + 8 * grp) * 2);
-        }
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) s[kb] = ET::mfma(ka[kb & 1][cc], qf[j][cc], s[kb]);
-      }
+        for (int kk = 0; kk < 2; ++kk) s[kk] = ET::mfma(ka[kk][cc], qf[j][cc], s[kk]);
       float mx = -INFINITY;                   // raw scores: the scale is positive
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (kMask) {
-            const int key = tb + 16 * kb + 4 * grp + i;
-            s[kb][i] = (key < lim && key < plim[j]) ? s[kb][i] : -INFINITY;
+            const int key = tb + 32 * kh + 16 * kk + 4 * grp + i;
+            s[kk][i] = (key < lim && key < plim[j]) ? s[kk][i] : -INFINITY;
           }
-          mx = fmaxf(mx, s[kb][i]);
+          mx = fmaxf(mx, s[kk][i]);
         }
       if (__any(mx * sc > mrun[j] + kLazy)) {   // wave-uniform; the first tile always
         mx = fmaxf(mx, __shfl_xor(mx, 16));    // the pair's maximum over its four lanes
@@ -322,29 +358,24 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
           for (int i = 0; i < 4; ++i) o[j][db][i] *= alpha;
       }
       const float nr = -mrun[j];
-      u32x4 phi[2], plo[2];
+      float e[8];                             // slots 8grp .. 8grp+7 of this wave's 32-key chunk
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        float e[8];                           // slots 8grp .. 8grp+7 of this 32-key chunk
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          e[jj] = __builtin_amdgcn_exp2f(fmaf(s[2 * kc + (jj >> 2)][jj & 3], sc, nr));   // masked: 0
-          lrun[j] += e[jj];
-        }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) ET::split(e[2 * w], e[2 * w + 1], hi[w], lo[w]);
-        phi[kc] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        plo[kc] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      for (int jj = 0; jj < 8; ++jj) {
+        e[jj] = __builtin_amdgcn_exp2f(fmaf(s[jj >> 2][jj & 3], sc, nr));   // masked: 0
+        lrun[j] += e[jj];
       }
+      uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+      for (int w = 0; w < 4; ++w) ET::split(e[2 * w], e[2 * w + 1], hi[w], lo[w]);
+      const u32x4 phi = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      const u32x4 plo = u32x4{lo[0], lo[1], lo[2], lo[3]};
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(svt + (16 * db + r16) * kWVtRow + (32 * kc + 8 * grp) * 2);
-          o[j][db] = ET::mfma(a, phi[kc], o[j][db]);
-          o[j][db] = ET::mfma(a, plo[kc], o[j][db]);
-        }
+      for (int db = 0; db < ND; ++db) {
+        const int vd = 16 * db + r16;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(svt + vd * kWVtRow + (((4 * kh + grp) ^ vt_swz(vd)) << 4));
+        o[j][db] = ET::mfma(a, phi, o[j][db]);
+        o[j][db] = ET::mfma(a, plo, o[j][db]);
+      }
     }
   };
 
@@ -354,23 +385,34 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
   // are computed with the mask.
   const int n_tiles = (t_end - t0 + kWTile - 1) / kWTile;
   const int mask_from = p.block ? min(t_end, n - p.t_q + 1) : t_end;
-  u32x4 kr[NB][NKL], vr[NB][2 * NVP];
+  // (tiles past the streamed rows are loaded too, as zeros, so that no load
+  // sits under a branch)
+  u32x4 kr[NB][NKL];
+  VVec vr[NB][2];
 #pragma unroll
-  for (int r = 0; r < NB - 1; ++r)
-    if (r < n_tiles) load_tile(krs, vrs, static_cast<uint32_t>(t0 + r * kWTile) * st, kr[r], vr[r]);
+  for (int r = 0; r < NB - 1; ++r) {
+    load_tile(krs, vrs, static_cast<uint32_t>(t0 + r * kWTile) * st, kr[r], vr[r]);
+    // issue order as in the loop (tile by tile), so that the waits the
+    // compiler derives for the first pass match the later ones
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Every pass runs all NB slots, loads and staging included, and only the
+  // products stop at the last tile: an exit from the middle of a pass (an
+  // edge back to the loop head, or one the compiler routes through it) makes
+  // the compiler assume that slot's loads still in flight at the head, and
+  // wait there for nearly all loads on every pass, emptying the ring.
   for (int it = 0; it < n_tiles; it += NB) {
 #pragma unroll
     for (int r = 0; r < NB; ++r) {            // unrolled: ring slots are compile-time
       const int t = it + r;
-      if (t >= n_tiles) break;                // uniform
       const int nxt = t + NB - 1;
-      if (nxt < n_tiles)
-        load_tile(krs, vrs, static_cast<uint32_t>(t0 + nxt * kWTile) * st, kr[(r + NB - 1) % NB],
-                  vr[(r + NB - 1) % NB]);
+      load_tile(krs, vrs, static_cast<uint32_t>(t0 + nxt * kWTile) * st, kr[(r + NB - 1) % NB],
+                vr[(r + NB - 1) % NB]);
       __syncthreads();                        // every wave is done with the previous tile
       store_tile(kr[r], vr[r]);
       __syncthreads();
       const int tb = t0 + t * kWTile;
+      if (t >= n_tiles) continue;             // uniform; past the last tile the staged rows are zeros
       if (tb + kWTile > mask_from) compute(tb, t_end, std::true_type{});
       else compute(tb, t_end, std::false_type{});
     }
@@ -382,7 +424,8 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
     const int xrow = n - 1;
     const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xrow) * p.st;
     const char* vx = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xrow) * p.st;
-    u32x4 kx_r[NKL], vx_r[2 * NVP];
+    u32x4 kx_r[NKL];
+    VVec vx_r[2];
     load_tile(wrsrc(uniform_cptr(kx), D * 2), wrsrc(uniform_cptr(vx), D * 2), 0u, kx_r, vx_r);
     __syncthreads();
     store_tile(kx_r, vx_r);
@@ -390,29 +433,85 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
     compute(xrow, xrow + 1, std::true_type{});
   }
 
+  // Merge the two key halves of every column block: each wave of a pair
+  // (w, w + 4) passes the other the half of the head dim it gives up (LDS,
+  // reusing the tile buffers) with its reference and sum; both then hold the
+  // merged state of their own half (wave kh keeps blocks NDH kh .. + NDH).
+  __syncthreads();                            // every wave is done with the last tile
+  float* const xo = reinterpret_cast<float*>(smem);               // [8 waves][QB][NDH][64 lanes][4]
+  float* const xml = reinterpret_cast<float*>(smem + kXoBytes);   // [8 waves][QB][64 lanes][2]
+  static_assert(NDH == NDH_, "half blocks");
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+#pragma unroll
+    for (int h = 0; h < NDH; ++h) {          // the other wave's half (indices fixed at compile
+      const f32x4 give = kh ? o[j][h] : o[j][NDH + h];   // time: the accumulators stay in registers)
+      *reinterpret_cast<f32x4*>(&xo[(((wave * QB + j) * NDH + h) * 64 + lane) * 4]) = give;
+    }
+    xml[((wave * QB + j) * 64 + lane) * 2] = mrun[j];
+    xml[((wave * QB + j) * 64 + lane) * 2 + 1] = lrun[j];
+  }
+  __syncthreads();
+  const int partner = wave ^ 4;
+  f32x4 oh[QB][NDH];                          // this wave's half, merged over both key halves
+  float mh[QB], lh[QB];                       // merged reference; this lane's part of the sum
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const float m2 = xml[((partner * QB + j) * 64 + lane) * 2];
+    const float l2 = xml[((partner * QB + j) * 64 + lane) * 2 + 1];
+    const float mm = fmaxf(mrun[j], m2);
+    const float c1 = __builtin_amdgcn_exp2f(mrun[j] - mm);   // 0 for an empty half (its reference kEmpty)
+    const float c2 = __builtin_amdgcn_exp2f(m2 - mm);
+    mh[j] = mm;
+    lh[j] = lrun[j] * c1 + l2 * c2;
+#pragma unroll
+    for (int h = 0; h < NDH; ++h) {
+      const f32x4 other = *reinterpret_cast<const f32x4*>(&xo[(((partner * QB + j) * NDH + h) * 64 + lane) * 4]);
+      const f32x4 mine = kh ? o[j][NDH + h] : o[j][h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oh[j][h][i] = mine[i] * c1 + other[i] * c2;
+    }
+  }
   // Totals per pair: the lane groups' sums.
   float lt[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    float l = lrun[j];
+    float l = lh[j];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     lt[j] = l;
   }
-  auto write_out = [&](int j, const f32x4 (&acc)[ND], float l) {
-    const int v = (wave + 4 * j) * 16 + r16;
+  // A lane's four consecutive output elements per block go out in one store
+  // (16 bytes of fp32, or 8 of the cache dtype rounded to nearest even)
+  // when out is 16-byte aligned.
+  auto write_out = [&](int j, const f32x4 (&acc)[NDH], float l) {
+    const int v = (cbw + 4 * j) * 16 + r16;
     if (v >= gv) return;
     const float inv = 1.f / l;
     const int64_t row = wpair_row(p, b, g, v) * D;
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+    for (int h = 0; h < NDH; ++h) {
+      const int64_t idx = row + 16 * (NDH * kh + h) + 4 * grp;
+      f32x4 y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_out(row + 16 * db + 4 * grp + i, acc[db][i] * inv);
+      for (int i = 0; i < 4; ++i) y[i] = acc[h][i] * inv;
+      if (p.out_vec && p.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + idx) = y;
+      } else if (p.out_vec) {
+        const uint32_t w0 = static_cast<uint32_t>(ET::bits(y[0])) | (static_cast<uint32_t>(ET::bits(y[1])) << 16);
+        const uint32_t w1 = static_cast<uint32_t>(ET::bits(y[2])) | (static_cast<uint32_t>(ET::bits(y[3])) << 16);
+        *reinterpret_cast<uint32_t __attribute__((ext_vector_type(2)))*>(static_cast<uint16_t*>(p.out) + idx) =
+            (uint32_t __attribute__((ext_vector_type(2)))){w0, w1};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_out(idx + i, y[i]);
+      }
+    }
   };
   if (ns == 1) {
 #pragma unroll
     for (int j = 0; j < QB; ++j)
-      if (cb_on[j]) write_out(j, o[j], lt[j]);
+      if (cb_on[j]) write_out(j, oh[j], lt[j]);
     return;
   }
 
@@ -423,10 +522,12 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
   // advances the unit's epoch. It has the highest workgroup id of its unit
   // on the XCD, and a publishing workgroup never waits, so every awaited
   // workgroup is dispatched and finishes; the wait is bounded all the same.
-  const int64_t prow0 = (static_cast<int64_t>(b) * p.n_kv + g) * gv * p.n_splits;
-  const __amdgpu_buffer_rsrc_t ors =
-      wrsrc(p.ws_o + prow0 * D, static_cast<uint32_t>(gv) * p.n_splits * D * 4u);
-  const __amdgpu_buffer_rsrc_t mrs = wrsrc(p.ws_ml + prow0 * 2, static_cast<uint32_t>(gv) * p.n_splits * 8u);
+  // Partial rows of this unit: [split][pair] (rows of D floats, and (reference,
+  // sum) pairs), so that one split's pairs are adjacent: a wave's 16 pairs are
+  // 16 consecutive rows, spread over the L2 channels.
+  const int64_t ubase = static_cast<int64_t>(unit) * p.n_splits * gv;
+  const __amdgpu_buffer_rsrc_t ors = wrsrc(p.ws_o + ubase * D, static_cast<uint32_t>(gv) * p.n_splits * D * 4u);
+  const __amdgpu_buffer_rsrc_t mrs = wrsrc(p.ws_ml + ubase * 2, static_cast<uint32_t>(gv) * p.n_splits * 8u);
   const __amdgpu_buffer_rsrc_t frs = wrsrc(flags, static_cast<uint32_t>(p.flag_stride) * 4u);
   // first use of the epoch: its load (issued at entry) is waited for here,
   // not in front of the stream
@@ -434,16 +535,16 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
   if (split != ns - 1) {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
-      const int v = (wave + 4 * j) * 16 + r16;
+      const int v = (cbw + 4 * j) * 16 + r16;
       if (!cb_on[j] || v >= gv) continue;
-      const uint32_t row = static_cast<uint32_t>(v * p.n_splits + split);
+      const uint32_t row = static_cast<uint32_t>(split * gv + v);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-        wstore(ors, (row * D + 16 * db + 4 * grp) * 4u,
-               u32x4{__float_as_uint(o[j][db][0]), __float_as_uint(o[j][db][1]), __float_as_uint(o[j][db][2]),
-                     __float_as_uint(o[j][db][3])});
-      if (grp == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mrun[j]), mrs, static_cast<int>(row * 8u), 0, kXchgW);
+      for (int h = 0; h < NDH; ++h)
+        wstore(ors, (row * D + 16 * (NDH * kh + h) + 4 * grp) * 4u,
+               u32x4{__float_as_uint(oh[j][h][0]), __float_as_uint(oh[j][h][1]), __float_as_uint(oh[j][h][2]),
+                     __float_as_uint(oh[j][h][3])});
+      if (kh == 0 && grp == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mh[j]), mrs, static_cast<int>(row * 8u), 0, kXchgW);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt[j]), mrs, static_cast<int>(row * 8u + 4u), 0, kXchgW);
       }
     }
@@ -475,58 +576,61 @@ __global__ __launch_bounds__(256, 1) void wide_decode_kernel(const WideParams p)
     }
   }
   __syncthreads();
-  // Fold the splits in split order, two per round trip: running reference
-  // mm, sum ll and accumulators acc; this workgroup's own split (the last)
-  // from registers.
+  // Fold the splits in split order, eight (four with two column blocks) per
+  // round trip, all their loads in flight together: running reference mm,
+  // sum ll and accumulators acc over this wave's (column block, half of the
+  // head dim); this workgroup's own split (the last) from registers.
+  constexpr int R = QB == 1 ? 8 : 4;
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const int v = (wave + 4 * j) * 16 + r16;
+    const int v = (cbw + 4 * j) * 16 + r16;
     if (!cb_on[j]) continue;
-    const uint32_t vrow = static_cast<uint32_t>((v < gv ? v : 0) * p.n_splits);
+    const uint32_t vrow = static_cast<uint32_t>(v < gv ? v : 0);
     float mm = -INFINITY, ll = 0.f;
-    f32x4 acc[ND];
+    f32x4 acc[NDH];
 #pragma unroll
-    for (int db = 0; db < ND; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < ns; k0 += 2) {
-      float rb[2], lb[2];
-      u32x4 ob[2][ND];
+    for (int h = 0; h < NDH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < ns; k0 += R) {
+      float rb[R], lb[R];
+      u32x4 ob[R][NDH];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint32_t row = vrow + static_cast<uint32_t>(k0 + kk);
+      for (int kk = 0; kk < R; ++kk) {       // rows past the region read as zero
+        const uint32_t row = static_cast<uint32_t>((k0 + kk) * gv) + vrow;   // past the region: zeros
         rb[kk] = __uint_as_float(static_cast<uint32_t>(
             __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u), 0, kXchgW)));
         lb[kk] = __uint_as_float(static_cast<uint32_t>(
             __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u + 4u), 0, kXchgW)));
 #pragma unroll
-        for (int db = 0; db < ND; ++db) ob[kk][db] = wload<kXchgW>(ors, (row * D + 16 * db + 4 * grp) * 4u);
+        for (int h = 0; h < NDH; ++h) ob[kk][h] = wload<kXchgW>(ors, (row * D + 16 * (NDH * kh + h) + 4 * grp) * 4u);
       }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < R; ++kk) {
         const int k = k0 + kk;
         if (k >= ns) break;                    // uniform
         float r_k = rb[kk], l_k = lb[kk];
         if (k == split) {                      // own split: from registers
-          r_k = mrun[j];
+          r_k = mh[j];
           l_k = lt[j];
 #pragma unroll
-          for (int db = 0; db < ND; ++db)
-            ob[kk][db] = u32x4{__float_as_uint(o[j][db][0]), __float_as_uint(o[j][db][1]),
-                               __float_as_uint(o[j][db][2]), __float_as_uint(o[j][db][3])};
+          for (int h = 0; h < NDH; ++h)
+            ob[kk][h] = u32x4{__float_as_uint(oh[j][h][0]), __float_as_uint(oh[j][h][1]),
+                              __float_as_uint(oh[j][h][2]), __float_as_uint(oh[j][h][3])};
         }
         const float nm = fmaxf(mm, r_k);
         const float c1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm - nm);
         const float c2 = __builtin_amdgcn_exp2f(r_k - nm);
         ll = ll * c1 + l_k * c2;
 #pragma unroll
-        for (int db = 0; db < ND; ++db)
+        for (int h = 0; h < NDH; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * c1 + __uint_as_float(ob[kk][db][i]) * c2;
+          for (int i = 0; i < 4; ++i) acc[h][i] = acc[h][i] * c1 + __uint_as_float(ob[kk][h][i]) * c2;
         mm = nm;
       }
     }
     write_out(j, acc, ll);
   }
   // the next call on this workspace waits for flags of epoch + 2
+  __syncthreads();
   if (tid == 0)
     __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>((p.flag_stride - 1) * 4), 0, kXchgW);
 }
@@ -596,11 +700,12 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.out_f32 = out_dtype == KVC_F32 ? 1 : 0;
   p.t_q = tq;
   p.block = t_q > 0 ? 1 : 0;
+  p.out_vec = reinterpret_cast<uintptr_t>(out) % 16 == 0 ? 1 : 0;
   p.scale_log2 = scale_log2;
   p.merge_spins = kvc::merge_spin_limit();
   const int64_t units = static_cast<int64_t>(cache->batch) * cache->n_kv_heads;
   const int64_t wgs = (units + 7) / 8 * 8 * splits;    // see the placement in the kernel
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(512), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
