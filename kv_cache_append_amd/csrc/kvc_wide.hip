@@ -145,16 +145,15 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   static_assert(NKL >= 1 && 32 * (D / (2 * VW)) == NT, "tile loads");
   using VVec = std::conditional_t<VW == 4, u32x4, u32x2>;
   constexpr int NDH_ = D / 32;
-  // LDS: a K tile and a transposed V tile during the stream; at the end the
-  // halves each wave passes its partner ([8 waves][QB][NDH][64 lanes] f32x4)
-  // and the references and sums ([8 waves][QB][64 lanes][2]).
+  // LDS: two tile buffers (a K tile and a transposed V tile each) during the
+  // stream, one computed while the next is staged; at the end the halves
+  // each wave passes its partner ([8 waves][QB][NDH][64 lanes] f32x4) and
+  // the references and sums ([8 waves][QB][64 lanes][2]).
   constexpr int kTileBytes = kWTile * KR + D * kWVtRow;
   constexpr int kXoBytes = 8 * QB * NDH_ * 64 * 16;
   constexpr int kXmlBytes = 8 * QB * 64 * 8;
-  constexpr int kLds = kTileBytes > kXoBytes + kXmlBytes ? kTileBytes : kXoBytes + kXmlBytes;
+  constexpr int kLds = 2 * kTileBytes > kXoBytes + kXmlBytes ? 2 * kTileBytes : kXoBytes + kXmlBytes;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
-  char* const sk = smem;
-  char* const svt = smem + kWTile * KR;
 
   // Workgroup placement: every split of a unit on one XCD (id residue mod 8),
   // the unit's splits in consecutive slots there, the merging split last.
@@ -165,10 +164,10 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   if (unit >= p.batch * p.n_kv) return;              // grid padding
   const int b = unit / p.n_kv;
   const int g = unit - b * p.n_kv;
-  // the unit's epoch (see the merge below), requested now and used at the end
+  // the unit's epoch (see the merge below), requested behind the first
+  // tiles' loads and used at the end
   uint32_t* const flags = p.ws_flag + static_cast<int64_t>(unit) * p.n_hblk * p.flag_stride;
   uint32_t epoch = 0u;
-  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Rows attended (n), the slot the fused append writes, device-side flags.
   const int c0 = p.seq_lens[b];
@@ -223,17 +222,26 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int ncb = (gv + 15) / 16;
 
   // The fused append: the newest row into its slot (no workgroup of this
-  // launch reads that slot from the cache).
-  if (x_new && wave == 0 && lane < CPR) {
-    const int64_t noff = b * p.nsb + g * p.nsh + lane * 16;
-    const int64_t aoff = b * p.sb + g * p.sh + static_cast<int64_t>(append_row) * p.st + lane * 16;
-    *reinterpret_cast<u32x4*>(p.k + aoff) = *reinterpret_cast<const u32x4*>(p.k_new + noff);
-    *reinterpret_cast<u32x4*>(p.v + aoff) = *reinterpret_cast<const u32x4*>(p.v_new + noff);
-  }
+  // launch reads that slot from the cache). Its loads are issued first and
+  // its stores after the first tiles' loads, so that waiting for the row
+  // holds nothing else back. Every lane runs them: those with nothing to
+  // copy see an empty buffer range (loads read zero, stores are dropped), as
+  // a load under a branch would make the compiler wait for every load issued
+  // before it.
+  const uint32_t arange = x_new && wave == 0 ? static_cast<uint32_t>(D * 2) : 0u;
+  const int64_t nrow = b * p.nsb + g * p.nsh;
+  const __amdgpu_buffer_rsrc_t kn_rs = wrsrc(uniform_cptr(p.k_new != nullptr ? p.k_new + nrow : p.k), arange);
+  const __amdgpu_buffer_rsrc_t vn_rs = wrsrc(uniform_cptr(p.v_new != nullptr ? p.v_new + nrow : p.v), arange);
+  const u32x4 kn_row = wload<0>(kn_rs, static_cast<uint32_t>(lane) * 16u);
+  const u32x4 vn_row = wload<0>(vn_rs, static_cast<uint32_t>(lane) * 16u);
 
   // The wave's pairs as B operands of the score product (column = pair r16
   // of column block cbw + 4j, 8 elements 32c + 8grp of its query row), and
-  // each pair's slot limit (lower-right causal mask of a query block).
+  // each pair's slot limit (lower-right causal mask of a query block). The
+  // rows of a unit's pairs lie within t_q * H_q rows of its first one; a
+  // lane with no pair reads past the range (zeros).
+  const char* const qunit = uniform_cptr(p.q + ((static_cast<int64_t>(b) * p.t_q) * p.n_q + g * p.group) * D * 2);
+  const __amdgpu_buffer_rsrc_t qrs = wrsrc(qunit, static_cast<uint32_t>(p.t_q * p.n_q * D * 2));
   u32x4 qf[QB][NC];
   int plim[QB];
   bool cb_on[QB];
@@ -243,12 +251,12 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     cb_on[j] = cb < ncb;
     const int v = cb * 16 + r16;
     plim[j] = p.block ? n - p.t_q + v / p.group + 1 : n;
+    const int qi = v / p.group;
+    const uint32_t qoff = cb_on[j] && v < gv
+                              ? static_cast<uint32_t>(((qi * p.n_q + (v - qi * p.group)) * D + 8 * grp) * 2)
+                              : 0x80000000u;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      qf[j][cc] = u32x4{0u, 0u, 0u, 0u};
-      if (cb_on[j] && v < gv)
-        qf[j][cc] = *reinterpret_cast<const u32x4*>(p.q + (wpair_row(p, b, g, v) * D + 32 * cc + 8 * grp) * 2);
-    }
+    for (int cc = 0; cc < NC; ++cc) qf[j][cc] = wload<0>(qrs, qoff + 64u * cc);
   }
 
   const uint32_t st = static_cast<uint32_t>(p.st);
@@ -278,7 +286,9 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     vr[0] = wloadw<VW, kNt>(vr_, base + v_off);
     vr[1] = wloadw<VW, kNt>(vr_, base + v_off + st);
   };
-  auto store_tile = [&](const u32x4 (&kr)[NKL], const VVec (&vr)[2]) {
+  auto store_tile = [&](const u32x4 (&kr)[NKL], const VVec (&vr)[2], int buf) {
+    char* const sk = smem + buf * kTileBytes;
+    char* const svt = sk + kWTile * KR;
 #pragma unroll
     for (int m = 0; m < NKL; ++m) {
       const int idx = tid + NT * m;
@@ -313,35 +323,46 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const float sc = p.scale_log2;
 
   // This wave's half of one staged tile whose first key is slot tb (keys
-  // tb + 32 kh .. + 31). kMask: keys at or past lim, or past a pair's own
-  // limit, get weight 0 (only in tiles that reach them).
-  auto compute = [&](int tb, int lim, auto mask_tag) {
-    constexpr bool kMask = decltype(mask_tag)::value;
+  // tb + 32 kh .. + 31); keys at or past lim, or past a pair's own limit,
+  // get weight 0. One code path for every tile: the mask costs a compare and
+  // a select per score, less than the register copies two paths would need.
+  auto compute = [&](int tb, int lim, int buf) {
+    const char* const sk = smem + buf * kTileBytes;
+    const char* const svt = sk + kWTile * KR;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       if (!cb_on[j]) continue;                // wave-uniform
-      f32x4 s[2];                             // S^T: lane holds keys 32kh + 16kk + 4grp + i of pair r16
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) s[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-      u32x4 ka[2][NC];
+      // Every LDS read of the tile is issued first (K rows for the scores,
+      // transposed V for the output), so that their latency overlaps the
+      // score products and the softmax instead of stalling each product.
+      u32x4 ka[2][NC], va[ND];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc)
           ka[kk][cc] = *reinterpret_cast<const u32x4*>(sk + (32 * kh + 16 * kk + r16) * KR + (32 * cc + 8 * grp) * 2);
 #pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int vd = 16 * db + r16;
+        va[db] = *reinterpret_cast<const u32x4*>(svt + vd * kWVtRow + (((4 * kh + grp) ^ vt_swz(vd)) << 4));
+      }
+      f32x4 s[2];                             // S^T: lane holds keys 32kh + 16kk + 4grp + i of pair r16
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) s[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) s[kk] = ET::mfma(ka[kk][cc], qf[j][cc], s[kk]);
+      // keys at or past lim, or past the pair's own limit, get weight 0: room
+      // is how many keys from this lane's first one are still attended (64
+      // or more in every tile but the last of a split and a block's tail)
+      const int room = min(lim, plim[j]) - tb - (32 * kh + 4 * grp);
       float mx = -INFINITY;                   // raw scores: the scale is positive
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if constexpr (kMask) {
-            const int key = tb + 32 * kh + 16 * kk + 4 * grp + i;
-            s[kk][i] = (key < lim && key < plim[j]) ? s[kk][i] : -INFINITY;
-          }
+          s[kk][i] = 16 * kk + i < room ? s[kk][i] : -INFINITY;
           mx = fmaxf(mx, s[kk][i]);
         }
       if (__any(mx * sc > mrun[j] + kLazy)) {   // wave-uniform; the first tile always
@@ -369,22 +390,19 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       for (int w = 0; w < 4; ++w) ET::split(e[2 * w], e[2 * w + 1], hi[w], lo[w]);
       const u32x4 phi = u32x4{hi[0], hi[1], hi[2], hi[3]};
       const u32x4 plo = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      // high parts of every block, then low parts: no product waits on the
+      // one before it (each block still adds hi, then lo)
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int vd = 16 * db + r16;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(svt + vd * kWVtRow + (((4 * kh + grp) ^ vt_swz(vd)) << 4));
-        o[j][db] = ET::mfma(a, phi, o[j][db]);
-        o[j][db] = ET::mfma(a, plo, o[j][db]);
-      }
+      for (int db = 0; db < ND; ++db) o[j][db] = ET::mfma(va[db], phi, o[j][db]);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) o[j][db] = ET::mfma(va[db], plo, o[j][db]);
     }
   };
 
-  // The stream: a register ring of NB tiles, NB - 1 of them in flight while
-  // one is staged into LDS and computed. Tiles reaching mask_from (the end of
-  // the streamed rows, or the first slot some pair of a block may not see)
-  // are computed with the mask.
+  // The stream: a register ring of NB tiles, NB - 1 of them in flight, and
+  // two LDS buffers: each step computes tile t from one buffer, then stages
+  // tile t + 1 (loaded two steps before) into the other, with one barrier.
   const int n_tiles = (t_end - t0 + kWTile - 1) / kWTile;
-  const int mask_from = p.block ? min(t_end, n - p.t_q + 1) : t_end;
   // (tiles past the streamed rows are loaded too, as zeros, so that no load
   // sits under a branch)
   u32x4 kr[NB][NKL];
@@ -396,6 +414,20 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     // compiler derives for the first pass match the later ones
     __builtin_amdgcn_sched_barrier(0);
   }
+  // (loaded here rather than at entry: a register the compiler shares with
+  // the address arithmetic above would otherwise wait for it there)
+  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {
+    const int64_t aoff = static_cast<int64_t>(append_row < 0 ? 0 : append_row) * p.st;
+    const __amdgpu_buffer_rsrc_t ka_rs = wrsrc(uniform_cptr(kunit + aoff), arange);
+    const __amdgpu_buffer_rsrc_t va_rs = wrsrc(uniform_cptr(vunit + aoff), arange);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, kn_row),
+                                           ka_rs, static_cast<int>(lane * 16), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, vn_row),
+                                           va_rs, static_cast<int>(lane * 16), 0, 0);
+  }
+  store_tile(kr[0], vr[0], 0);
+  __syncthreads();
   // Every pass runs all NB slots, loads and staging included, and only the
   // products stop at the last tile: an exit from the middle of a pass (an
   // edge back to the loop head, or one the compiler routes through it) makes
@@ -408,13 +440,12 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       const int nxt = t + NB - 1;
       load_tile(krs, vrs, static_cast<uint32_t>(t0 + nxt * kWTile) * st, kr[(r + NB - 1) % NB],
                 vr[(r + NB - 1) % NB]);
-      __syncthreads();                        // every wave is done with the previous tile
-      store_tile(kr[r], vr[r]);
+      if (t < n_tiles) compute(t0 + t * kWTile, t_end, t & 1);   // uniform
+      // tile t + 1 into the other buffer (zeros past the last tile); the
+      // barrier also keeps the next step's staging off this step's buffer
+      // until every wave has computed it
+      store_tile(kr[(r + 1) % NB], vr[(r + 1) % NB], (t + 1) & 1);
       __syncthreads();
-      const int tb = t0 + t * kWTile;
-      if (t >= n_tiles) continue;             // uniform; past the last tile the staged rows are zeros
-      if (tb + kWTile > mask_from) compute(tb, t_end, std::true_type{});
-      else compute(tb, t_end, std::false_type{});
     }
   }
   if (has_x) {
@@ -427,10 +458,9 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     u32x4 kx_r[NKL];
     VVec vx_r[2];
     load_tile(wrsrc(uniform_cptr(kx), D * 2), wrsrc(uniform_cptr(vx), D * 2), 0u, kx_r, vx_r);
+    store_tile(kx_r, vx_r, 0);              // both buffers are free after the stream's last barrier
     __syncthreads();
-    store_tile(kx_r, vx_r);
-    __syncthreads();
-    compute(xrow, xrow + 1, std::true_type{});
+    compute(xrow, xrow + 1, 0);
   }
 
   // Merge the two key halves of every column block: each wave of a pair
@@ -529,7 +559,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const __amdgpu_buffer_rsrc_t ors = wrsrc(p.ws_o + ubase * D, static_cast<uint32_t>(gv) * p.n_splits * D * 4u);
   const __amdgpu_buffer_rsrc_t mrs = wrsrc(p.ws_ml + ubase * 2, static_cast<uint32_t>(gv) * p.n_splits * 8u);
   const __amdgpu_buffer_rsrc_t frs = wrsrc(flags, static_cast<uint32_t>(p.flag_stride) * 4u);
-  // first use of the epoch: its load (issued at entry) is waited for here,
+  // first use of the epoch: its load (issued with the first tiles) is waited for here,
   // not in front of the stream
   asm volatile("" : "+v"(epoch));
   if (split != ns - 1) {
