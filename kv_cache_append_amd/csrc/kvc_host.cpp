@@ -286,9 +286,14 @@ static size_t sync_units(const kvc_cache_t* c, int32_t n_q_heads) {
 
 size_t workspace_flag_offset(const kvc_cache_t*, int32_t, int32_t) { return 0; }
 
-size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
+size_t workspace_sync_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
   return workspace_flag_offset(c, n_q_heads, n_splits) +
          round256(sync_units(c, n_q_heads) * static_cast<size_t>(n_splits) * sizeof(uint32_t));
+}
+
+size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
+  return workspace_sync_offset(c, n_q_heads, n_splits) +
+         round256(static_cast<size_t>(c->batch) * c->n_kv_heads * kWideSyncBytes);
 }
 
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
@@ -301,6 +306,7 @@ WsRegions workspace_regions(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_s
   WsRegions r;
   r.flags = reinterpret_cast<uint32_t*>(base + workspace_flag_offset(c, n_q_heads, n_splits));
   r.flag_stride = n_splits;
+  r.sync = reinterpret_cast<uint32_t*>(base + workspace_sync_offset(c, n_q_heads, n_splits));
   r.o = reinterpret_cast<float*>(base + workspace_o_offset(c, n_q_heads, n_splits));
   r.ml = reinterpret_cast<float*>(base + workspace_ml_offset(c, n_q_heads, n_splits));
   return r;

@@ -68,9 +68,10 @@ bool routes_wide(const kvc_cache_t* c, int32_t n_q_heads);
 int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_t* lens);
 
 // Workspace: uint32 ready flags [B * H_kv * head_blocks, S] (word S - 1 of
-// each row is that block's merge epoch), then fp32 partial outputs
-// [B, H_q, S, D], then fp32 (reference, sum) pairs [B, H_q, S, 2]; each
-// region starts on a 256-byte boundary.
+// each row is that block's merge epoch), then the wide-group kernel's merge
+// words [B * H_kv, kWideSyncWords] (uint32), then fp32 partial outputs [B, H_q, S, D],
+// then fp32 (reference, sum) pairs [B, H_q, S, 2]; each region starts on a
+// 256-byte boundary.
 size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 
 // Where a decode call's split exchange lives: ready flags (one row of
@@ -82,9 +83,17 @@ size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits
 struct WsRegions {
   uint32_t* flags;
   int32_t flag_stride;
+  uint32_t* sync;   // the wide-group kernel: kWideSyncWords per (sequence, KV head)
   float* o;
   float* ml;
 };
+// Per (sequence, KV head), for the wide-group kernel's spread merge (up to
+// kWideSpreadMax splits): an arrival count and one claim word per output
+// slice, in a row of kWideSyncWords uint32.
+constexpr int kWideSpreadMax = 32;
+constexpr int kWideSyncWords = 64;
+constexpr size_t kWideSyncBytes = kWideSyncWords * sizeof(uint32_t);
+static_assert(1 + kWideSpreadMax <= kWideSyncWords, "spread merge words");
 WsRegions workspace_regions(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits, void* ws);
 // Lays out a decode call's exchange space once its split count is known.
 typedef kvc_status_t (*RegionsFn)(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits, WsRegions* out);
@@ -95,6 +104,7 @@ kvc_status_t decode_step_in_regions(const kvc_cache_t* cache, const int32_t* seq
                                     int32_t n_q_heads, float scale, void* out, int32_t out_dtype, int32_t n_splits,
                                     uint32_t* dev_status, hipStream_t stream, RegionsFn regions_fn);
 size_t workspace_flag_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
+size_t workspace_sync_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
 

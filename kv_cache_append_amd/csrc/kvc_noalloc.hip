@@ -10,7 +10,10 @@
 // row's epoch word (its last) stays in place whatever the geometry of the
 // calls: flags only ever hold epoch values and an epoch only grows, so a
 // flag left by an earlier call, of any geometry, never equals what a later
-// call waits for. The partial outputs and (reference, sum) pairs follow,
+// call waits for. The wide-group kernel's merge words come next, one pair
+// per (sequence, KV head) row, tagged with the epoch of the call that wrote
+// them, so that stale words are told apart the same way. The partial
+// outputs and (reference, sum) pairs follow,
 // rewritten by every call before they are read. The array is zero at load,
 // the state the epoch protocol starts from. Calls that overlap on one GPU
 // (two streams at once) share the array and race.
@@ -32,7 +35,10 @@ namespace {
 
 constexpr size_t kScratchBytes = static_cast<size_t>(KVC_NOALLOC_SCRATCH_MIB) << 20;
 constexpr size_t kScratchFlagBytes = static_cast<size_t>(KVC_NOALLOC_MAX_ROWS) * KVC_MAX_SPLITS * 4;
-static_assert(kScratchFlagBytes % 256 == 0 && kScratchFlagBytes < kScratchBytes, "scratch layout");
+constexpr size_t kScratchSyncBytes = static_cast<size_t>(KVC_NOALLOC_MAX_ROWS) * kvc::kWideSyncBytes;
+constexpr size_t kScratchHeadBytes = kScratchFlagBytes + kScratchSyncBytes;
+static_assert(kScratchFlagBytes % 256 == 0 && kScratchSyncBytes % 256 == 0 && kScratchHeadBytes < kScratchBytes,
+              "scratch layout");
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
@@ -64,15 +70,16 @@ kvc_status_t noalloc_regions(const kvc_cache_t* c, int32_t n_q_heads, int32_t sp
   const int64_t o_bytes = (prows * c->head_dim * 4 + 255) & ~int64_t{255};
   const int64_t ml_bytes = (prows * 8 + 255) & ~int64_t{255};
   if (rows > KVC_NOALLOC_MAX_ROWS ||
-      static_cast<int64_t>(kScratchFlagBytes) + o_bytes + ml_bytes > static_cast<int64_t>(kScratchBytes))
+      static_cast<int64_t>(kScratchHeadBytes) + o_bytes + ml_bytes > static_cast<int64_t>(kScratchBytes))
     return KVC_ERR_WORKSPACE;
   uint8_t* base = nullptr;
   const kvc_status_t st = scratch_on_current_device(&base);
   if (st != KVC_OK) return st;
   r->flags = reinterpret_cast<uint32_t*>(base);
   r->flag_stride = KVC_MAX_SPLITS;
-  r->o = reinterpret_cast<float*>(base + kScratchFlagBytes);
-  r->ml = reinterpret_cast<float*>(base + kScratchFlagBytes + o_bytes);
+  r->sync = reinterpret_cast<uint32_t*>(base + kScratchFlagBytes);   // (sequence, KV head) rows <= rows
+  r->o = reinterpret_cast<float*>(base + kScratchHeadBytes);
+  r->ml = reinterpret_cast<float*>(base + kScratchHeadBytes + o_bytes);
   return KVC_OK;
 }
 

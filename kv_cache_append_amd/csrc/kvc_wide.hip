@@ -54,6 +54,13 @@ constexpr int kWVtRow = 144;     // bytes per transposed-V row in LDS: 64 keys +
 __device__ inline int vt_swz(int d) { return (d >> 3) & 7; }
 constexpr int kNt = 2;           // cache policy of the K/V stream: non-temporal (each row read once)
 constexpr int kXchgW = KVC_XCHG_POLICY;
+// Splits up to which the merge is spread over the splits
+constexpr int kSpreadMax = kvc::kWideSpreadMax;
+static_assert(kSpreadMax <= 32, "one lane of a wave per slice, claims in 32 bits");
+// Scope of the spread merge's atomics: a unit's splits share one XCD's L2
+// (workgroup placement), where atomics are performed; otherwise the device.
+constexpr int kSyncScope =
+    (KVC_XCD_COLOCATE && KVC_LOCAL_EXCHANGE) ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
 
 #ifndef KVC_WIDE_PREFETCH
 #define KVC_WIDE_PREFETCH 2      // register tiles of loads in flight behind the one being staged
@@ -69,6 +76,7 @@ struct WideParams {
   const char* v_new;
   int64_t nsb, nsh;              // its strides in bytes
   uint32_t* ws_flag;             // [B * H_kv * n_hblk, flag_stride]: this kernel uses head block 0's row
+  uint32_t* ws_sync;             // [B * H_kv, kWideSyncWords]: arrival count and slice claims of the spread merge
   float* ws_o;                   // [B, H_kv * pairs, S, D]
   float* ws_ml;                  // [B, H_kv * pairs, S, 2]
   void* out;                     // like q; fp32 or the cache dtype
@@ -511,6 +519,21 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     l += __shfl_xor(l, 32);
     lt[j] = l;
   }
+  // Four consecutive output elements from element idx: one 16-byte (fp32)
+  // or 8-byte (cache dtype, rounded to nearest even) store when out is
+  // 16-byte aligned.
+  auto store4 = [&](int64_t idx, const f32x4& y) {
+    if (p.out_vec && p.out_f32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + idx) = y;
+    } else if (p.out_vec) {
+      const uint32_t w0 = static_cast<uint32_t>(ET::bits(y[0])) | (static_cast<uint32_t>(ET::bits(y[1])) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(ET::bits(y[2])) | (static_cast<uint32_t>(ET::bits(y[3])) << 16);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + idx) = u32x2{w0, w1};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_out(idx + i, y[i]);
+    }
+  };
   // A lane's four consecutive output elements per block go out in one store
   // (16 bytes of fp32, or 8 of the cache dtype rounded to nearest even)
   // when out is 16-byte aligned.
@@ -525,17 +548,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       f32x4 y;
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] = acc[h][i] * inv;
-      if (p.out_vec && p.out_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + idx) = y;
-      } else if (p.out_vec) {
-        const uint32_t w0 = static_cast<uint32_t>(ET::bits(y[0])) | (static_cast<uint32_t>(ET::bits(y[1])) << 16);
-        const uint32_t w1 = static_cast<uint32_t>(ET::bits(y[2])) | (static_cast<uint32_t>(ET::bits(y[3])) << 16);
-        *reinterpret_cast<uint32_t __attribute__((ext_vector_type(2)))*>(static_cast<uint16_t*>(p.out) + idx) =
-            (uint32_t __attribute__((ext_vector_type(2)))){w0, w1};
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_out(idx + i, y[i]);
-      }
+      store4(idx, y);
     }
   };
   if (ns == 1) {
@@ -562,7 +575,9 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // first use of the epoch: its load (issued with the first tiles) is waited for here,
   // not in front of the stream
   asm volatile("" : "+v"(epoch));
-  if (split != ns - 1) {
+  // This split's partial into its rows of the exchange, complete in L2 when
+  // the function returns.
+  auto publish = [&]() {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const int v = (cbw + 4 * j) * 16 + r16;
@@ -579,6 +594,140 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  if (ns <= kSpreadMax) {
+    // The spread merge: every split publishes its partial and counts itself
+    // in; the unit's output is cut into ns slices of (pair, 4 elements)
+    // items, and split k merges slice k once all splits have arrived, so
+    // the merge's reads and writes are shared by ns workgroups instead of
+    // falling on one. A split waits for the others only for a bounded time;
+    // the last to arrive waits for nothing and, after its own slice, merges
+    // every slice no one has claimed (those of splits that gave up waiting).
+    // Per (sequence, KV head): an arrival count, which the last arrival
+    // returns to zero when it is done, and one claim word per slice, raised
+    // to epoch + 1 by the one workgroup that merges the slice (an atomic
+    // maximum: each slice is written once, and a claim left by an earlier
+    // call is below this call's value). The last arrival then advances the
+    // epoch, which also tells splits still waiting that the merge is done.
+    publish();
+    __syncthreads();
+    uint32_t* const sync = p.ws_sync + static_cast<int64_t>(unit) * kvc::kWideSyncWords;
+    uint32_t* const claims = sync + 1;
+    __shared__ uint32_t ss[2];
+    if (tid == 0) {
+      const uint32_t ticket = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, kSyncScope) + 1u;
+      uint32_t state = ticket >= static_cast<uint32_t>(ns) ? 2u : 0u;   // 2: last, 1: all arrived, 0: gave up
+      for (int spins = 0; state == 0u && spins < p.merge_spins; ++spins) {
+        __builtin_amdgcn_s_sleep(1);
+        // (exchanges that write back what they find: performed in L2)
+        uint32_t c = static_cast<uint32_t>(ns), e = epoch;
+        __hip_atomic_compare_exchange_strong(sync, &c, c, __ATOMIC_RELAXED, __ATOMIC_RELAXED, kSyncScope);
+        __hip_atomic_compare_exchange_strong(flags + p.flag_stride - 1, &e, e, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             kSyncScope);
+        if (c >= static_cast<uint32_t>(ns)) state = 1u;
+        else if (e != epoch) break;            // the merge is done: nothing left to claim
+      }
+      ss[0] = state;
+    }
+    __syncthreads();
+    const uint32_t state = ss[0];
+    // Slice k: items [k I / ns, (k + 1) I / ns) of the I = pairs * D / 4, each
+    // a pair's 4 consecutive elements; the splits folded in split order, as
+    // in the last-split merge, with loads of whole rows per wave. With claim,
+    // the slice is claimed first, and the loads of each thread's first item
+    // are issued while the claim's answer is on its way.
+    auto merge_slice = [&](int k, bool claim) {
+      constexpr int C4 = D / 4;
+      constexpr int R = 8;
+      const int items = gv * C4;
+      const int i1 = (k + 1) * items / ns;
+      uint32_t old = 0u;
+      if (claim && tid == 0) old = __hip_atomic_fetch_max(claims + k, epoch + 1u, __ATOMIC_RELAXED, kSyncScope);
+      u32x4 ob[R];
+      u32x2 mlb[R];
+      // one round: splits k0 .. k0 + R - 1 of item it (rows past the region,
+      // or no item at all, read as zero)
+      auto load_round = [&](int it, int k0) {
+        const int v = it / C4;
+        const bool any = it < i1;
+#pragma unroll
+        for (int kk = 0; kk < R; ++kk) {
+          const uint32_t row = static_cast<uint32_t>((k0 + kk) * gv + v);
+          const uint32_t mo = any ? row * 8u : 0x80000000u;
+          const uint32_t oo = any ? (row * D + 4 * (it - v * C4)) * 4u : 0x80000000u;
+          mlb[kk] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(mrs, static_cast<int>(mo), 0, kXchgW));
+          ob[kk] = wload<kXchgW>(ors, oo);
+        }
+      };
+      int it = k * items / ns + tid;
+      load_round(it, 0);
+      if (claim) {
+        if (tid == 0) ss[1] = old < epoch + 1u;
+        __syncthreads();
+        if (!ss[1]) return;                   // uniform: another workgroup merges this slice
+      }
+      for (bool pre = true; it < i1; it += NT, pre = false) {
+        const int v = it / C4;
+        float mm = -INFINITY, ll = 0.f;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < ns; k0 += R) {
+          if (!pre || k0 > 0) load_round(it, k0);
+#pragma unroll
+          for (int kk = 0; kk < R; ++kk) {
+            if (k0 + kk >= ns) break;
+            const float r_k = __uint_as_float(mlb[kk][0]), l_k = __uint_as_float(mlb[kk][1]);
+            const float nm = fmaxf(mm, r_k);
+            const float c1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm - nm);
+            const float c2 = __builtin_amdgcn_exp2f(r_k - nm);
+            ll = ll * c1 + l_k * c2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = acc[i] * c1 + __uint_as_float(ob[kk][i]) * c2;
+            mm = nm;
+          }
+        }
+        const float inv = 1.f / ll;
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = acc[i] * inv;
+        store4(wpair_row(p, b, g, v) * D + 4 * (it - v * C4), y);
+      }
+    };
+    if (state != 0u) merge_slice(split, true);
+    if (state == 2u) {
+      // every slice not yet claimed (normally none: the others claimed theirs
+      // while this one merged its own), claimed at once, one lane per slice,
+      // and merged here
+      __syncthreads();
+      if (wave == 0) {
+        const bool won = lane < ns && lane != split &&
+                         __hip_atomic_fetch_max(claims + lane, epoch + 1u, __ATOMIC_RELAXED, kSyncScope) < epoch + 1u;
+        const uint64_t m = __ballot(won);
+        if (lane == 0) ss[1] = static_cast<uint32_t>(m);
+      }
+      __syncthreads();
+      const uint32_t won = ss[1];
+      for (int k = 0; k < ns; ++k)
+        if ((won >> k) & 1u) merge_slice(k, false);
+      // the count back to zero for the next call, then the epoch advanced
+      __syncthreads();
+      if (tid == 0) {
+        __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, kSyncScope);
+        __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>((p.flag_stride - 1) * 4), 0, kXchgW);
+      }
+    }
+    return;
+  }
+
+  // More splits than the claim mask holds: every split but the last
+  // publishes its partial and raises its ready flag to epoch + 1; the last
+  // waits for those flags, folds the partials in split order (its own from
+  // registers), writes the output and advances the unit's epoch. It has the
+  // highest workgroup id of its unit on the XCD, and a publishing workgroup
+  // never waits, so every awaited workgroup is dispatched and finishes; the
+  // wait is bounded all the same.
+  if (split != ns - 1) {
+    publish();
     __syncthreads();
     if (tid == 0) __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>(split * 4), 0, kXchgW);
     return;
@@ -714,6 +863,7 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.nsh = new_stride_h * s;
   p.ws_flag = ws.flags;
   p.flag_stride = ws.flag_stride;
+  p.ws_sync = ws.sync;
   p.ws_o = ws.o;
   p.ws_ml = ws.ml;
   p.lens_next = lens_next;

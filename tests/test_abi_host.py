@@ -128,7 +128,8 @@ def test_decode_validation_gqa_workspace_unsupported():
 
 
 def test_workspace_size_formula():
-    """Workspace = uint32 ready flags [B * H_kv * head blocks, S] + fp32
+    """Workspace = uint32 ready flags [B * H_kv * head blocks, S] + the
+    wide-group merge words (64 uint32 per (sequence, KV head)) + fp32
     partial outputs [B, H_q, S, D] + (reference, sum) pairs, each region
     rounded up to 256 bytes."""
     kvc, lib = _lib()
@@ -136,7 +137,8 @@ def test_workspace_size_formula():
     for s in (1, 3, 16, 100):
         rows = 2 * 4 * s
         flags = -(-2 * 2 * s * 4 // 256) * 256
-        want = flags + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+        sync = -(-2 * 2 * 256 // 256) * 256
+        want = flags + sync + -(-rows * 128 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
         assert lib.kvc_decode_workspace_bytes(ctypes.byref(c), 4, s) == want
     auto = lib.kvc_decode_splits(ctypes.byref(c), 4)
     assert auto >= 1

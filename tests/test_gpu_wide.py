@@ -164,3 +164,56 @@ def test_wide_capacity_and_negative_lengths(gpu):
     assert np.abs(got[1] - ref1).max() <= TOL["bf16"]
     assert (got[2] == 0).all()
     assert torch.equal(case.k[1].view(torch.int16), k_before.view(torch.int16))
+
+
+def test_wide_spread_merge_rescued_when_splits_give_up(gpu):
+    """The spread merge: every split merges one slice of the output once all
+    splits have arrived; a split that stops waiting leaves its slice to the
+    last one to arrive, which claims and merges every unclaimed slice. With
+    the wait bound at zero polls every split but the last gives up at once,
+    so the last merges all slices: the outputs must carry no status bit,
+    match the oracle and equal, bit for bit, those of the default bound (the
+    same fold order), call after call on one workspace."""
+    lens = [300, 2047, 4000, 1]
+    case = DecodeCase(batch=4, n_q=64, n_kv=1, head_dim=128, dtype="bf16", lengths=lens, tag="widerescue",
+                      device=gpu)
+    kvc.append(case.k, case.v, case.seq_lens, case.k_new, case.v_new)
+    ws = kvc.workspace(case.k, case.v, 64, 8)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    ref_out = torch.empty((4, 64, 128), device=gpu)
+    kvc.decode_attn(case.k, case.v, case.seq_lens, case.q, ref_out, ws, n_pending=1, n_splits=8, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.abs(ref_out.double().cpu().numpy() - _oracle_all(case)).max() <= TOL["bf16"]
+    prev = kvc.debug_set_merge_spin_limit(0)
+    try:
+        for i in range(4):
+            out = torch.full((4, 64, 128), float("nan"), device=gpu)
+            kvc.decode_attn(case.k, case.v, case.seq_lens, case.q, out, ws, n_pending=1, n_splits=8,
+                            status=status)
+            torch.cuda.synchronize()
+            assert int(status.item()) == 0, i
+            assert torch.equal(out, ref_out), i
+    finally:
+        kvc.debug_set_merge_spin_limit(prev)
+    out = torch.empty_like(ref_out)
+    kvc.decode_attn(case.k, case.v, case.seq_lens, case.q, out, ws, n_pending=1, n_splits=8, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and torch.equal(out, ref_out)
+
+
+def test_wide_more_splits_than_the_spread_merge_takes(gpu):
+    """More than 32 active splits per (sequence, KV head): the last split
+    merges with ready flags instead; outputs against the oracle."""
+    lens = [2200, 2400]
+    case = DecodeCase(batch=2, n_q=32, n_kv=1, head_dim=64, dtype="fp16", lengths=lens, tag="wide35",
+                      device=gpu)
+    ws = kvc.workspace(case.k, case.v, 32, 36)
+    out = torch.empty((2, 32, 64), device=gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    for _ in range(2):
+        kvc.decode_step(case.k, case.v, case.seq_lens, case.k_new, case.v_new, case.q, out, ws, n_splits=36,
+                        status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert np.abs(out.double().cpu().numpy() - _oracle_all(case)).max() <= TOL["fp16"]
