@@ -30,9 +30,10 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attention achieved HBM GB/s (KV bytes read/step time) and % of peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 DOMINANT_KERNEL = "decode_kernel"
-# the decode kernels' sources (counter records are tied to their code)
-KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_append_amd", "csrc", f)
-                  for f in ("kvc_kernels.hip", "kvc_wide.hip", "kvc_tile.h")]
+# each decode kernel's sources (a counter record is tied to its kernel's code)
+KERNEL_SOURCES = {k: [os.path.join(ROOT, "kv_cache_append_amd", "csrc", f) for f in files]
+                  for k, files in (("decode_kernel", ("kvc_kernels.hip", "kvc_internal.h")),
+                                   ("wide_decode_kernel", ("kvc_wide.hip", "kvc_tile.h", "kvc_internal.h")))}
 
 
 def _parse():
@@ -395,11 +396,11 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     return ms_total, wall, avg_launch_ms, avg_launch_bytes, step_ms
 
 
-def _kernel_fingerprint() -> str:
-    """SHA-256 of the kernel source with comments and whitespace removed, so
-    that counter records stay tied to the code and not to its comments."""
+def _kernel_fingerprint(kernel: str) -> str:
+    """SHA-256 of the kernel's sources with comments and whitespace removed,
+    so that counter records stay tied to the code and not to its comments."""
     import re
-    src = "".join(open(p).read() for p in KERNEL_SOURCES)
+    src = "".join(open(p).read() for p in KERNEL_SOURCES[kernel])
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = re.sub(r"\s+", " ", src).strip()
@@ -413,7 +414,7 @@ def _traffic(workload_name: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_code_sha256") != _kernel_fingerprint():
+    if rec.get("kernel_code_sha256") != _kernel_fingerprint(rec.get("kernel", "decode_kernel")):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -449,10 +450,11 @@ def _pmc_summary(fetch_csv: str, write_csv: str, out_path: str, args):
     import synth
     cfg = synth.CONFIGS[args.config]
     algo = 2 * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes * (int(cfg.lengths(args.seed).long().sum()) + cfg.batch)
+    kernel = "wide_decode_kernel" if cfg.group >= 16 else "decode_kernel"
     rec = {
         "workload": args.config,
-        "kernel": "wide_decode_kernel" if cfg.group >= 16 else "decode_kernel",
-        "kernel_code_sha256": _kernel_fingerprint(),
+        "kernel": kernel,
+        "kernel_code_sha256": _kernel_fingerprint(kernel),
         "hbm_bytes_per_launch": int(round(fetch + write)),
         "fetch_bytes_per_launch": int(round(fetch)),
         "write_bytes_per_launch": int(round(write)),
