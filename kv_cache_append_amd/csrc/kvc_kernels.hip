@@ -346,8 +346,7 @@ struct SeqInfo {
   uint32_t flags;  // KVC_DEVERR_* bits
 };
 
-__device__ inline SeqInfo seq_info(const DecodeParams& p, int b) {
-  const int c0 = p.seq_lens[b];
+__device__ inline SeqInfo seq_info(const DecodeParams& p, int c0) {
   SeqInfo si;
   si.flags = 0;
   const int c = c0 < 0 ? 0 : c0;
@@ -447,6 +446,9 @@ __device__ inline const char* uniform_ptr(const char* q) {
 // (16: write-through, miss in the per-XCD L2) unless set otherwise in
 // kvc_internal.h.
 constexpr int kXchg = KVC_XCHG_POLICY;
+// Scope of the epoch's read at entry: the exchange's own (an item's
+// workgroups share one XCD's L2 with the default placement and exchange)
+constexpr int kEpochScope = KVC_XCHG_POLICY == 0 ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
 // Cache policy of the K/V stream: every row is read once per launch, so the
 // loads carry the non-temporal hint (`nt`). Measured on MI355X (same box,
 // interleaved runs) it streams 6-7 % faster than the default policy on every
@@ -697,22 +699,28 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
 #endif
   const int b = unit / p.n_kv;
   const int g = unit - b * p.n_kv;
-  // The item's epoch (word S - 1 of its flags: no split publishes there),
-  // requested now and used after the stream. A publisher raises its flag to
-  // epoch + 1; the merger waits for exactly that value and then advances the
-  // epoch, so flags never need clearing and a flag raised after a merge gave
-  // up waiting (KVC_DEVERR_SYNC) cannot be taken for the next call's.
+  // The sequence's length, then the item's epoch (word S - 1 of its flags:
+  // no split publishes there), requested in that order so that the wait
+  // for the length does not also wait for the epoch, which is used only
+  // after the stream. A publisher raises its flag to epoch + 1; the merger
+  // waits for exactly that value and then advances the epoch, so flags
+  // never need clearing and a flag raised after a merge gave up waiting
+  // (KVC_DEVERR_SYNC) cannot be taken for the next call's. With the item's
+  // workgroups on one XCD the epoch is read from that XCD's L2, where the
+  // previous call's merger (on the same XCD) left it.
+  const int c0 = p.seq_lens[b];
+  asm volatile("" ::: "memory");
   const int64_t item = static_cast<int64_t>(unit) * p.n_hblk + hb;
   uint32_t* const flags = p.ws_flag + item * p.flag_stride;
   uint32_t epoch = 0u;
-  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, kEpochScope);
 
-  const SeqInfo si = seq_info(p, b);
+  const SeqInfo si = seq_info(p, c0);
   // kvc_decode_step_advance (the last layer of a step): the next step's
   // lengths, written by one workgroup per sequence into another array, so no
   // workgroup of this launch reads a changed length
   if (p.lens_next != nullptr && g == 0 && split == 0 && hb == 0 && threadIdx.x == 0)
-    p.lens_next[b] = p.seq_lens[b] + 1;
+    p.lens_next[b] = c0 + 1;
   if (si.flags != 0 && g == 0 && hb == 0 && split == 0 && threadIdx.x == 0 && p.status != nullptr)
     atomicOr(p.status, si.flags);
   const int n = si.n;
