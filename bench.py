@@ -113,6 +113,7 @@ class Workload:
         pairs = cfg.group * max(block_q, 1)
         self.wide = (not (page or ring or quant) and cfg.dtype in ("fp16", "bf16") and cfg.head_dim in (64, 128)
                      and 16 <= pairs <= 128 and not (block_q >= 8 and pairs >= 32))
+        self.fused_advance = not (block_q or page or ring or quant)   # (see below)
         if quant:
             self._init_quant(cfg, seed, splits, dev, tdt)
             return
@@ -596,8 +597,8 @@ def _run_config(name, args, with_cpu):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("copy_rows_kernel + decode_kernel (kvc_prefill_fill + kvc_block_attn per layer; time per "
-                       "layer covers both)" if args.block_q else
+            "kernel": ("copy_rows_kernel + " + ("wide_decode_kernel" if w.wide else "decode_kernel") +
+                       " (kvc_prefill_fill + kvc_block_attn per layer; time per layer covers both)" if args.block_q else
                        "decode_kernel (kvc_ring_decode_step: ring append + windowed attention + merge, one "
                        "launch per layer)" if args.ring else
                        "decode_kernel on 8-bit codes (kvc_quant_decode_attn, timed alone; the step adds one "
