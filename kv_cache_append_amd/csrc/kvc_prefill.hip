@@ -43,7 +43,24 @@ namespace {
 
 constexpr int kQTile = 128;      // queries per workgroup
 constexpr int kKTile = 64;       // keys per LDS tile
-constexpr int kVtRow = 144;      // bytes per transposed-V row in LDS: 64 keys + 8 elements of padding
+
+// K and V tiles sit in LDS as stored (row-major, no padding) with the 16-byte
+// chunks of row r permuted by chunk ^ tile_swz(r): the score product's K
+// reads (8 consecutive rows at one chunk) and the output product's
+// transposing V reads (4 consecutive rows, two chunks each) then fall on
+// distinct banks.
+__device__ inline int tile_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Four 16-bit elements of column d0 + i from four consecutive rows, into
+// lane i of each 16-lane group (ds_read_b64_tr_b16): lane s of the group
+// points at elements d0 + 4 (s % 4) .. + 3 of row s / 4.
+__device__ inline u32x2 lds_read_tr(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(p))));
+}
 
 struct PrefillParams {
   const char* k;
@@ -62,11 +79,12 @@ template <typename ET, int D>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
   constexpr int NC = D / 32;            // 32-element slices of a row (score product depth)
   constexpr int ND = D / 16;            // 16-element output blocks
-  constexpr int KR = 2 * D + 16;        // bytes per K row in LDS (16 bytes of padding)
-  constexpr int NKL = D / 32;           // 16-byte K loads per thread per tile
-  constexpr int NVP = D / 64;           // V passes per tile, two 16-byte loads each
-  __shared__ __attribute__((aligned(16))) char sk[kKTile * KR];
-  __shared__ __attribute__((aligned(16))) char svt[D * kVtRow];
+  constexpr int RB = 2 * D;             // bytes per K or V row in LDS
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int kTileBytes = kKTile * RB;   // one K or one V tile
+  constexpr int NLD = kKTile * CPR / 256;   // 16-byte loads per thread per tile, K and V each
+  // two buffers of a K tile and a V tile: one computed while the next lands
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
 
   const int units = p.batch * p.n_kv;
   const int per_unit = p.group * p.n_qt;
@@ -138,44 +156,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
   const __amdgpu_buffer_rsrc_t krs = rsrc(p.k + uoff, static_cast<uint32_t>(n) * st);
   const __amdgpu_buffer_rsrc_t vrs = rsrc(p.v + uoff, static_cast<uint32_t>(n) * st);
 
-  // Tile staging: thread tid loads K chunks tid + 256m (row idx / (D/8),
-  // 16-byte chunk idx % (D/8)) and V rows 2kp, 2kp+1 (kp = tid % 32) at
-  // chunk tid / 32 + 8 pass.
-  u32x4 kr[NKL], vr[2 * NVP];
-  auto load_tile = [&](int t) {
+  // Tiles go from memory straight to LDS (buffer loads to LDS: lane l of a
+  // load writes the 16 bytes at the load's LDS base + 16 l), with no
+  // registers or stores in between: load i of wave w fills chunk positions
+  // 64 (NLD w + i) + lane of the tile, i.e. row / chunk position (q / CPR,
+  // q % CPR), from the row's chunk q % CPR ^ tile_swz(row). Rows past the
+  // block's end read as zeros.
+  auto load_tile = [&](int t, int buf) {
     const uint32_t base = static_cast<uint32_t>(t * kKTile) * st;
+    char* const kb = smem + buf * 2 * kTileBytes;
 #pragma unroll
-    for (int m = 0; m < NKL; ++m) {
-      const int idx = tid + 256 * m;
-      kr[m] = bload(krs, base + static_cast<uint32_t>(idx / (D / 8)) * st + static_cast<uint32_t>(idx % (D / 8)) * 16u);
-    }
-#pragma unroll
-    for (int ps = 0; ps < NVP; ++ps) {
-      const int kp = tid & 31;
-      const int dc = (tid >> 5) + 8 * ps;
-      vr[2 * ps] = bload(vrs, base + static_cast<uint32_t>(2 * kp) * st + dc * 16u);
-      vr[2 * ps + 1] = bload(vrs, base + static_cast<uint32_t>(2 * kp + 1) * st + dc * 16u);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int m = 0; m < NKL; ++m) {
-      const int idx = tid + 256 * m;
-      *reinterpret_cast<u32x4*>(sk + (idx / (D / 8)) * KR + (idx % (D / 8)) * 16) = kr[m];
-    }
-#pragma unroll
-    for (int ps = 0; ps < NVP; ++ps) {
-      const int kp = tid & 31;
-      const int dc = (tid >> 5) + 8 * ps;
-      const int key0 = 2 * kp;                           // keys key0, key0 + 1 share one word
-      const int col = (32 * (key0 >> 5) + vt_slot(key0 & 31)) * 2;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t w0 = vr[2 * ps][m], w1 = vr[2 * ps + 1][m];
-        const int d = 8 * dc + 2 * m;
-        *reinterpret_cast<uint32_t*>(svt + d * kVtRow + col) = (w0 & 0xffffu) | (w1 << 16);
-        *reinterpret_cast<uint32_t*>(svt + (d + 1) * kVtRow + col) = (w0 >> 16) | (w1 & 0xffff0000u);
-      }
+    for (int i = 0; i < NLD; ++i) {
+      const int m = wave * NLD + i;
+      const int q = m * 64 + lane;
+      const int row = q / CPR;
+      const uint32_t off = base + static_cast<uint32_t>(row) * st + static_cast<uint32_t>((q % CPR) ^ tile_swz(row)) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr)(kb + m * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr)(kb + kTileBytes + m * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -191,8 +188,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
     for (int db = 0; db < ND; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int t, auto mask_tag) {
+  // Per-lane parts of the LDS addresses: K row r16's chunk 4c + grp sits at
+  // (4c + grp) ^ swz (swz of the row: 16 kb + r16 has r16's low bits); a V
+  // read of keys 4 grp + r16 / 4 (+ 32 kc, + 16) takes elements
+  // 16 db + 4 (r16 % 4) .., chunk 2 db + (r16 % 4) / 2 ^ vsw, byte vsub.
+  const int kswz = tile_swz(r16);
+  const int vrow = 4 * grp + (r16 >> 2);
+  const int vx = ((r16 & 3) >> 1) ^ tile_swz(vrow);
+  const int voff = vrow * RB + 8 * (r16 & 1);
+  auto compute = [&](int t, int buf, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;   // the tile crosses the diagonal
+    const char* const sk = smem + buf * 2 * kTileBytes;
+    const char* const sv = sk + kTileBytes;
     f32x4 s[2][4];                          // S^T: lane holds keys 16kb + 4grp + i of query r16
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -206,13 +213,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     u32x4 ka[2][NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      ka[0][c] = *reinterpret_cast<const u32x4*>(sk + r16 * KR + (32 * c + 8 * grp) * 2);
+      ka[0][c] = *reinterpret_cast<const u32x4*>(sk + r16 * RB + ((4 * c + grp) ^ kswz) * 16);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       if (kb + 1 < 4) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          ka[(kb + 1) & 1][c] = *reinterpret_cast<const u32x4*>(sk + (16 * (kb + 1) + r16) * KR + (32 * c + 8 * grp) * 2);
+          ka[(kb + 1) & 1][c] =
+              *reinterpret_cast<const u32x4*>(sk + (16 * (kb + 1) + r16) * RB + ((4 * c + grp) ^ kswz) * 16);
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -275,7 +283,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(svt + (16 * db + r16) * kVtRow + (32 * kc + 8 * grp) * 2);
+        // V^T rows 16 db + r16, keys 32 kc + 4 grp .. + 3 and 32 kc + 16 + 4 grp .. + 3
+        // (the slots of the weights' lane layout)
+        const char* const vp = sv + 32 * kc * RB + voff + ((2 * db) ^ vx) * 16;
+        const u32x2 lo4 = lds_read_tr(vp), hi4 = lds_read_tr(vp + 16 * RB);
+        const u32x4 a = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           o[qb][db] = ET::mfma(a, phi[qb][kc], o[qb][db]);
@@ -299,14 +311,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
   // computed with the mask. (Two loops, one kind of tile each, so that each
   // is compiled on its own.)
   const int t_split = (c0 + i0 + 1) / kKTile;
+  // A step waits for this wave's loads of tile t, then the barrier: every
+  // wave's loads of tile t have landed, and every wave is done with tile
+  // t - 1, whose buffer then takes tile t + 1's loads (issued for every
+  // step, past the last tile too: loads under a branch would make the
+  // compiler wait for all loads in flight) while tile t is computed.
   auto step = [&](int t, auto mask_tag) {
-    __syncthreads();                        // every wave is done with the previous tile
-    store_tile();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);  // in flight while this tile is computed
-    if (wactive && t * kKTile < wlim) compute(t, mask_tag);
+    load_tile(t + 1, (t + 1) & 1);
+    if (wactive && t * kKTile < wlim) compute(t, t & 1, mask_tag);
   };
-  load_tile(0);
+  load_tile(0, 0);
   int t = 0;
   for (; t < t_split; ++t) step(t, std::false_type{});
   for (; t < n_tiles; ++t) step(t, std::true_type{});

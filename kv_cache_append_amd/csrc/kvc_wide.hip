@@ -97,7 +97,6 @@ template <int kPolicy>
 __device__ inline u32x4 wload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kPolicy));
 }
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Load of W words (4: 16 bytes, 2: 8 bytes)
 template <int W, int kPolicy>
 __device__ inline auto wloadw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
