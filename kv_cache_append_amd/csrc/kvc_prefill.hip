@@ -44,24 +44,6 @@ namespace {
 constexpr int kQTile = 128;      // queries per workgroup
 constexpr int kKTile = 64;       // keys per LDS tile
 
-// K and V tiles sit in LDS as stored (row-major, no padding) with the 16-byte
-// chunks of row r permuted by chunk ^ tile_swz(r): the score product's K
-// reads (8 consecutive rows at one chunk) and the output product's
-// transposing V reads (4 consecutive rows, two chunks each) then fall on
-// distinct banks.
-__device__ inline int tile_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Four 16-bit elements of column d0 + i from four consecutive rows, into
-// lane i of each 16-lane group (ds_read_b64_tr_b16): lane s of the group
-// points at elements d0 + 4 (s % 4) .. + 3 of row s / 4.
-__device__ inline u32x2 lds_read_tr(const char* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                       (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(p))));
-}
-
 struct PrefillParams {
   const char* k;
   const char* v;
@@ -153,8 +135,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 
   const int64_t uoff = b * p.sb + g * p.sh;
   const uint32_t st = static_cast<uint32_t>(p.st);
-  const __amdgpu_buffer_rsrc_t krs = rsrc(p.k + uoff, static_cast<uint32_t>(n) * st);
-  const __amdgpu_buffer_rsrc_t vrs = rsrc(p.v + uoff, static_cast<uint32_t>(n) * st);
+  const u32x4 kw = rsrc_words(p.k + uoff, static_cast<uint32_t>(n) * st);
+  const u32x4 vw = rsrc_words(p.v + uoff, static_cast<uint32_t>(n) * st);
 
   // Tiles go from memory straight to LDS (buffer loads to LDS: lane l of a
   // load writes the 16 bytes at the load's LDS base + 16 l), with no
@@ -162,17 +144,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
   // 64 (NLD w + i) + lane of the tile, i.e. row / chunk position (q / CPR,
   // q % CPR), from the row's chunk q % CPR ^ tile_swz(row). Rows past the
   // block's end read as zeros.
+  const uint32_t smem_lds = KVC_LDS_ADDR(smem);
   auto load_tile = [&](int t, int buf) {
     const uint32_t base = static_cast<uint32_t>(t * kKTile) * st;
-    char* const kb = smem + buf * 2 * kTileBytes;
+    const uint32_t kb = smem_lds + buf * 2 * kTileBytes;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int m = wave * NLD + i;
       const int q = m * 64 + lane;
       const int row = q / CPR;
       const uint32_t off = base + static_cast<uint32_t>(row) * st + static_cast<uint32_t>((q % CPR) ^ tile_swz(row)) * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr)(kb + m * 1024), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr)(kb + kTileBytes + m * 1024), 16, off, 0, 0, 0);
+      lds_load16<false>(kw, off, kb + m * 1024);
+      lds_load16<false>(vw, off, kb + kTileBytes + m * 1024);
     }
   };
 
@@ -323,6 +306,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     if (wactive && t * kKTile < wlim) compute(t, t & 1, mask_tag);
   };
   load_tile(0, 0);
+  // The query registers, used here so that the compiler waits for their
+  // loads once, ahead of the loop: a wait it placed in the loop would count
+  // only the loads it knows of, not the tile loads, and so wait for those.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) asm volatile("" ::"v"(qf[qb][c]));
   int t = 0;
   for (; t < t_split; ++t) step(t, std::false_type{});
   for (; t < n_tiles; ++t) step(t, std::true_type{});

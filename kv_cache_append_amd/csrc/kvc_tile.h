@@ -75,4 +75,58 @@ __device__ inline u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // lane group, so slots 8g..8g+7 hold keys 4g..4g+3 and 16+4g..16+4g+3.
 __device__ inline int vt_slot(int kk) { return 8 * ((kk & 15) >> 2) + (kk & 3) + 4 * (kk >> 4); }
 
+
+// K and V tiles in LDS (the prefill and wide-group kernels) sit as stored
+// (row-major, no padding), with the 16-byte chunks of row r permuted by
+// chunk ^ tile_swz(r): the score product's K
+// reads (8 consecutive rows at one chunk) and the output product's
+// transposing V reads (4 consecutive rows, two chunks each) then fall on
+// distinct banks.
+__device__ inline int tile_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Four 16-bit elements of column d0 + i from four consecutive rows, into
+// lane i of each 16-lane group (ds_read_b64_tr_b16): lane s of the group
+// points at elements d0 + 4 (s % 4) .. + 3 of row s / 4.
+__device__ inline u32x2 lds_read_tr(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) i16x4*)(const_cast<char*>(p))));
+}
+
+// Buffer descriptor words (base, 16-bit stride 0, byte range, raw format) in
+// scalar registers, for the LDS loads below.
+__device__ inline u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu)),
+               static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000u};
+}
+
+// The LDS address of a __shared__ array (for M0 below).
+#define KVC_LDS_ADDR(arr) \
+  static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(arr)))
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes at
+// voff land at LDS address lds + 16 l (buffer_load_dwordx4 ... lds, the
+// address in M0); offsets past the range write zeros. Written as inline assembly so
+// that the compiler does not take later LDS reads of other buffers for
+// reads of this load's destination and wait for every load in flight
+// before them; the caller waits (s_waitcnt vmcnt) before reading the data.
+// kNt: the non-temporal hint (rows read once).
+template <bool kNt>
+__device__ inline void lds_load16(const u32x4& rs, uint32_t voff, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  if constexpr (kNt)
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rs), "s"(m0)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m0)
+                 : "memory");
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// the wave are outstanding (the other counters left alone)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 #endif  // KVC_TILE_H_

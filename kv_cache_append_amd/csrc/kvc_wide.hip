@@ -44,15 +44,6 @@ namespace {
 #include "kvc_tile.h"
 
 constexpr int kWTile = 64;       // keys per LDS tile
-constexpr int kWVtRow = 144;     // bytes per transposed-V row in LDS: 64 keys + 8 elements of padding
-
-// Transposed V in LDS: row d holds the tile's 64 keys (slot order, 8 chunks of
-// 16 bytes), chunk c stored at c ^ vt_swz(d). The staging writes rows 8 apart
-// from the lanes of one instruction; without the swizzle they would all fall
-// on the same banks (the padding only separates neighbouring rows, which the
-// output product reads together).
-__device__ inline int vt_swz(int d) { return (d >> 3) & 7; }
-constexpr int kNt = 2;           // cache policy of the K/V stream: non-temporal (each row read once)
 constexpr int kXchgW = KVC_XCHG_POLICY;
 // Splits up to which the merge is spread over the splits
 constexpr int kSpreadMax = kvc::kWideSpreadMax;
@@ -62,8 +53,8 @@ static_assert(kSpreadMax <= 32, "one lane of a wave per slice, claims in 32 bits
 constexpr int kSyncScope =
     (KVC_XCD_COLOCATE && KVC_LOCAL_EXCHANGE) ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
 
-#ifndef KVC_WIDE_PREFETCH
-#define KVC_WIDE_PREFETCH 2      // register tiles of loads in flight behind the one being staged
+#ifndef KVC_WIDE_BUFFERS
+#define KVC_WIDE_BUFFERS 4       // LDS tile buffers: the tiles in flight behind the one computed, plus it
 #endif
 
 struct WideParams {
@@ -96,12 +87,6 @@ __device__ inline __amdgpu_buffer_rsrc_t wrsrc(const void* base, uint32_t bytes)
 template <int kPolicy>
 __device__ inline u32x4 wload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kPolicy));
-}
-// Load of W words (4: 16 bytes, 2: 8 bytes)
-template <int W, int kPolicy>
-__device__ inline auto wloadw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (W == 4) return wload<kPolicy>(r, off);
-  else return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, kPolicy));
 }
 __device__ inline void wstore(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, x), r,
@@ -136,30 +121,27 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   constexpr int NC = D / 32;            // 32-element slices of a row (score product depth)
   constexpr int ND = D / 16;            // 16-element output blocks
   constexpr int NDH = ND / 2;           // output blocks of a wave after the halves merge
-  constexpr int KR = 2 * D + 16;        // bytes per K row in LDS (16 bytes of padding)
+  constexpr int RB = 2 * D;             // bytes per K or V row in LDS
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int NKL = kWTile * CPR / NT;   // 16-byte K loads per thread per tile
-  constexpr int VW = D / 32;            // V words per key and thread: every thread stages two keys' VW words
-  // register tiles: two in flight behind the one staged (one with two column
-  // blocks per wave, whose accumulators need the registers)
-  constexpr int NB = QB == 1 ? KVC_WIDE_PREFETCH + 1 : 2;
+  constexpr int TB = kWTile * RB;       // one K or one V tile
+  constexpr int NL = kWTile * CPR / NT;   // 16-byte loads per thread per tile, K and V each
+  constexpr int NBUF = KVC_WIDE_BUFFERS;
   constexpr float kLazy = 8.f;          // the reference moves only past ref + 8 (log2 domain)
   // Reference of a pair that has seen no key: finite, so that exp2 of a
   // masked (-inf) score against it is 0 rather than NaN, and far below any
   // score, so the first key seen replaces it (and zeroes its weight).
   constexpr float kEmpty = -1e30f;
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  static_assert(NKL >= 1 && 32 * (D / (2 * VW)) == NT, "tile loads");
-  using VVec = std::conditional_t<VW == 4, u32x4, u32x2>;
+  static_assert(NL >= 1 && NL * NT == kWTile * CPR && NBUF >= 2, "tile loads");
   constexpr int NDH_ = D / 32;
-  // LDS: two tile buffers (a K tile and a transposed V tile each) during the
-  // stream, one computed while the next is staged; at the end the halves
+  // LDS: NBUF tile buffers (a K tile and a V tile each) during the stream,
+  // NBUF - 1 of them filling while one is computed; at the end the halves
   // each wave passes its partner ([8 waves][QB][NDH][64 lanes] f32x4) and
   // the references and sums ([8 waves][QB][64 lanes][2]).
-  constexpr int kTileBytes = kWTile * KR + D * kWVtRow;
+  constexpr int kBufBytes = 2 * TB;
   constexpr int kXoBytes = 8 * QB * NDH_ * 64 * 16;
   constexpr int kXmlBytes = 8 * QB * 64 * 8;
-  constexpr int kLds = 2 * kTileBytes > kXoBytes + kXmlBytes ? 2 * kTileBytes : kXoBytes + kXmlBytes;
+  constexpr int kLds = NBUF * kBufBytes > kXoBytes + kXmlBytes ? NBUF * kBufBytes : kXoBytes + kXmlBytes;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
 
   // Workgroup placement: every split of a unit on one XCD (id residue mod 8),
@@ -230,8 +212,8 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
 
   // The fused append: the newest row into its slot (no workgroup of this
   // launch reads that slot from the cache). Its loads are issued first and
-  // its stores after the first tiles' loads, so that waiting for the row
-  // holds nothing else back. Every lane runs them: those with nothing to
+  // its stores after the stream, so that waiting for the row holds nothing
+  // else back. Every lane runs them: those with nothing to
   // copy see an empty buffer range (loads read zero, stores are dropped), as
   // a load under a branch would make the compiler wait for every load issued
   // before it.
@@ -270,49 +252,30 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const char* kunit = uniform_cptr(p.k + (b * p.sb + g * p.sh));
   const char* vunit = uniform_cptr(p.v + (b * p.sb + g * p.sh));
   // K/V of the streamed rows; rows past t_end read as zero (and are masked)
-  const __amdgpu_buffer_rsrc_t krs = wrsrc(kunit, static_cast<uint32_t>(t_end) * st);
-  const __amdgpu_buffer_rsrc_t vrs = wrsrc(vunit, static_cast<uint32_t>(t_end) * st);
+  const u32x4 krs = rsrc_words(kunit, static_cast<uint32_t>(t_end) * st);
+  const u32x4 vrs = rsrc_words(vunit, static_cast<uint32_t>(t_end) * st);
 
-  // Tile staging: thread tid loads K chunks tid + NT m (row idx / CPR, chunk
-  // idx % CPR) and, of V, elements 2 VW dc .. + 2 VW - 1 (dc = tid % 16) of
-  // rows 2kp and 2kp + 1 (kp = tid / 16), so that each load instruction
-  // reads whole rows (partial-line requests from many rows at once halved
-  // the stream rate on MI355X). Every thread does the same loads
-  // and LDS stores, with no branch around them: a load or a use of its
-  // registers under a branch makes the compiler's wait counting lose track of
-  // the loads in flight and wait for nearly all of them, which empties the
-  // ring at every tile.
-  const uint32_t v_off = static_cast<uint32_t>(2 * (tid >> 4)) * st + static_cast<uint32_t>(tid & 15) * (4u * VW);
-  auto load_tile = [&](__amdgpu_buffer_rsrc_t kr_, __amdgpu_buffer_rsrc_t vr_, uint32_t base, u32x4 (&kr)[NKL],
-                       VVec (&vr)[2]) {
+  // Tiles go from memory straight to LDS (buffer loads to LDS: lane l of a
+  // load writes the 16 bytes at the load's LDS base + 16 l), with no
+  // registers or stores in between: load i of wave w fills chunk positions
+  // 64 (NL w + i) + lane of the tile, i.e. row / chunk position
+  // (q / CPR, q % CPR), from the row's chunk q % CPR ^ tile_swz(row). Rows
+  // past the streamed ones read as zeros (and are masked).
+  const uint32_t smem_lds = KVC_LDS_ADDR(smem);
+  auto load_tile_from = [&](const u32x4& kr_, const u32x4& vr_, uint32_t base, int buf) {
+    const uint32_t kb = smem_lds + buf * kBufBytes;
 #pragma unroll
-    for (int m = 0; m < NKL; ++m) {
-      const int idx = tid + NT * m;
-      kr[m] = wload<kNt>(kr_, base + static_cast<uint32_t>(idx / CPR) * st + static_cast<uint32_t>(idx % CPR) * 16u);
+    for (int i = 0; i < NL; ++i) {
+      const int m = wave * NL + i;
+      const int q = m * 64 + lane;
+      const int row = q / CPR;
+      const uint32_t off = base + static_cast<uint32_t>(row) * st + static_cast<uint32_t>((q % CPR) ^ tile_swz(row)) * 16u;
+      lds_load16<true>(kr_, off, kb + m * 1024);
+      lds_load16<true>(vr_, off, kb + TB + m * 1024);
     }
-    vr[0] = wloadw<VW, kNt>(vr_, base + v_off);
-    vr[1] = wloadw<VW, kNt>(vr_, base + v_off + st);
   };
-  auto store_tile = [&](const u32x4 (&kr)[NKL], const VVec (&vr)[2], int buf) {
-    char* const sk = smem + buf * kTileBytes;
-    char* const svt = sk + kWTile * KR;
-#pragma unroll
-    for (int m = 0; m < NKL; ++m) {
-      const int idx = tid + NT * m;
-      *reinterpret_cast<u32x4*>(sk + (idx / CPR) * KR + (idx % CPR) * 16) = kr[m];
-    }
-    const int kp = tid >> 4;
-    const int dc = tid & 15;
-    const int key0 = 2 * kp;                             // keys key0, key0 + 1 share one word
-    const int col = (32 * (key0 >> 5) + vt_slot(key0 & 31)) * 2;
-    const int d0 = 2 * VW * dc;                          // rows d0 .. d0 + 2 VW - 1: one swizzle
-    char* const vrow = svt + d0 * kWVtRow + ((((col >> 4) ^ vt_swz(d0)) << 4) | (col & 15));
-#pragma unroll
-    for (int m = 0; m < VW; ++m) {
-      const uint32_t w0 = vr[0][m], w1 = vr[1][m];
-      *reinterpret_cast<uint32_t*>(vrow + 2 * m * kWVtRow) = (w0 & 0xffffu) | (w1 << 16);
-      *reinterpret_cast<uint32_t*>(vrow + (2 * m + 1) * kWVtRow) = (w0 >> 16) | (w1 & 0xffff0000u);
-    }
+  auto load_tile = [&](int t, int buf) {
+    load_tile_from(krs, vrs, static_cast<uint32_t>(t0 + t * kWTile) * st, buf);
   };
 
   // Per pair: the reference r (log2 domain) the weights are taken against,
@@ -333,9 +296,17 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // tb + 32 kh .. + 31); keys at or past lim, or past a pair's own limit,
   // get weight 0. One code path for every tile: the mask costs a compare and
   // a select per score, less than the register copies two paths would need.
+  // Per-lane parts of the LDS addresses: K row r16 (+ 32 kh + 16 kk) has
+  // its chunk 4 cc + grp at (4 cc + grp) ^ kswz; the transposing V reads
+  // take keys 32 kh + 4 grp + r16 / 4 (and + 16), elements 16 db + 4 (r16 % 4)
+  // .., i.e. chunk 2 db + (r16 % 4) / 2 at (2 db) ^ vx, byte 8 (r16 % 2).
+  const int kswz = tile_swz(r16);
+  const int vrow = 4 * grp + (r16 >> 2);
+  const int vx = ((r16 & 3) >> 1) ^ tile_swz(vrow);
+  const int voff = (32 * kh + vrow) * RB + 8 * (r16 & 1);
   auto compute = [&](int tb, int lim, int buf) {
-    const char* const sk = smem + buf * kTileBytes;
-    const char* const svt = sk + kWTile * KR;
+    const char* const sk = smem + buf * kBufBytes;
+    const char* const sv = sk + TB;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       if (!cb_on[j]) continue;                // wave-uniform
@@ -347,11 +318,12 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc)
-          ka[kk][cc] = *reinterpret_cast<const u32x4*>(sk + (32 * kh + 16 * kk + r16) * KR + (32 * cc + 8 * grp) * 2);
+          ka[kk][cc] = *reinterpret_cast<const u32x4*>(sk + (32 * kh + 16 * kk + r16) * RB + ((4 * cc + grp) ^ kswz) * 16);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int vd = 16 * db + r16;
-        va[db] = *reinterpret_cast<const u32x4*>(svt + vd * kWVtRow + (((4 * kh + grp) ^ vt_swz(vd)) << 4));
+      for (int db = 0; db < ND; ++db) {       // V^T rows 16 db + r16, in the weights' key slots
+        const char* const vp = sv + voff + ((2 * db) ^ vx) * 16;
+        const u32x2 lo4 = lds_read_tr(vp), hi4 = lds_read_tr(vp + 16 * RB);
+        va[db] = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
       }
       f32x4 s[2];                             // S^T: lane holds keys 32kh + 16kk + 4grp + i of pair r16
 #pragma unroll
@@ -406,25 +378,53 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     }
   };
 
-  // The stream: a register ring of NB tiles, NB - 1 of them in flight, and
-  // two LDS buffers: each step computes tile t from one buffer, then stages
-  // tile t + 1 (loaded two steps before) into the other, with one barrier.
+  // The stream: NBUF LDS buffers, NBUF - 1 tiles in flight while one is
+  // computed. A step waits for this wave's loads of tile t (the later tiles'
+  // loads may stay in flight), then the barrier: every wave's loads of tile t
+  // have landed, and every wave is done with tile t - 1, whose buffer then
+  // takes tile t + NBUF - 1. Every pass runs all NBUF steps, their loads
+  // included (tiles past the last read zeros and are not computed): the wait
+  // counts are fixed only if every step issues the same loads.
   const int n_tiles = (t_end - t0 + kWTile - 1) / kWTile;
-  // (tiles past the streamed rows are loaded too, as zeros, so that no load
-  // sits under a branch)
-  u32x4 kr[NB][NKL];
-  VVec vr[NB][2];
+  // the unit's epoch (see the merge), requested ahead of the tiles, so the
+  // first tile's wait covers it
+  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, kSyncScope);
 #pragma unroll
-  for (int r = 0; r < NB - 1; ++r) {
-    load_tile(krs, vrs, static_cast<uint32_t>(t0 + r * kWTile) * st, kr[r], vr[r]);
-    // issue order as in the loop (tile by tile), so that the waits the
-    // compiler derives for the first pass match the later ones
-    __builtin_amdgcn_sched_barrier(0);
+  for (int r = 0; r < NBUF - 1; ++r) load_tile(r, r);
+  // The query registers, used here so that the compiler waits for their
+  // loads once, ahead of the loop: a wait it placed in the loop would count
+  // only the loads it knows of, not the tile loads, and so wait for those.
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) asm volatile("" ::"v"(qf[j][cc]));
+  for (int it = 0; it < n_tiles; it += NBUF) {
+#pragma unroll
+    for (int r = 0; r < NBUF; ++r) {          // unrolled: buffers are compile-time
+      const int t = it + r;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * 2 * NL));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_tile(t + NBUF - 1, (r + NBUF - 1) % NBUF);
+      if (t < n_tiles) compute(t0 + t * kWTile, t_end, r);   // uniform
+    }
   }
-  // (loaded here rather than at entry: a register the compiler shares with
-  // the address arithmetic above would otherwise wait for it there)
-  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every load landed and every wave done with the buffers
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  if (has_x) {
+    // The newest row as key 0 of one more tile: from k_new/v_new in the fused
+    // step, else from the cache; the other 63 keys read as zero (one-row
+    // range) and are masked.
+    const int xrow = n - 1;
+    const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xrow) * p.st;
+    const char* vx_ = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xrow) * p.st;
+    load_tile_from(rsrc_words(kx, D * 2), rsrc_words(vx_, D * 2), 0u, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    compute(xrow, xrow + 1, 0);
+  }
   {
+    // the fused append's stores (the row's loads were issued at entry)
     const int64_t aoff = static_cast<int64_t>(append_row < 0 ? 0 : append_row) * p.st;
     const __amdgpu_buffer_rsrc_t ka_rs = wrsrc(uniform_cptr(kunit + aoff), arange);
     const __amdgpu_buffer_rsrc_t va_rs = wrsrc(uniform_cptr(vunit + aoff), arange);
@@ -432,42 +432,6 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
                                            ka_rs, static_cast<int>(lane * 16), 0, 0);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, vn_row),
                                            va_rs, static_cast<int>(lane * 16), 0, 0);
-  }
-  store_tile(kr[0], vr[0], 0);
-  __syncthreads();
-  // Every pass runs all NB slots, loads and staging included, and only the
-  // products stop at the last tile: an exit from the middle of a pass (an
-  // edge back to the loop head, or one the compiler routes through it) makes
-  // the compiler assume that slot's loads still in flight at the head, and
-  // wait there for nearly all loads on every pass, emptying the ring.
-  for (int it = 0; it < n_tiles; it += NB) {
-#pragma unroll
-    for (int r = 0; r < NB; ++r) {            // unrolled: ring slots are compile-time
-      const int t = it + r;
-      const int nxt = t + NB - 1;
-      load_tile(krs, vrs, static_cast<uint32_t>(t0 + nxt * kWTile) * st, kr[(r + NB - 1) % NB],
-                vr[(r + NB - 1) % NB]);
-      if (t < n_tiles) compute(t0 + t * kWTile, t_end, t & 1);   // uniform
-      // tile t + 1 into the other buffer (zeros past the last tile); the
-      // barrier also keeps the next step's staging off this step's buffer
-      // until every wave has computed it
-      store_tile(kr[(r + 1) % NB], vr[(r + 1) % NB], (t + 1) & 1);
-      __syncthreads();
-    }
-  }
-  if (has_x) {
-    // The newest row as key 0 of one more tile: from k_new/v_new in the fused
-    // step, else from the cache; the other 63 keys read as zero (one-row
-    // range) and are masked.
-    const int xrow = n - 1;
-    const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xrow) * p.st;
-    const char* vx = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xrow) * p.st;
-    u32x4 kx_r[NKL];
-    VVec vx_r[2];
-    load_tile(wrsrc(uniform_cptr(kx), D * 2), wrsrc(uniform_cptr(vx), D * 2), 0u, kx_r, vx_r);
-    store_tile(kx_r, vx_r, 0);              // both buffers are free after the stream's last barrier
-    __syncthreads();
-    compute(xrow, xrow + 1, 0);
   }
 
   // Merge the two key halves of every column block: each wave of a pair

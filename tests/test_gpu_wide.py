@@ -217,3 +217,29 @@ def test_wide_more_splits_than_the_spread_merge_takes(gpu):
         torch.cuda.synchronize()
         assert int(status.item()) == 0
         assert np.abs(out.double().cpu().numpy() - _oracle_all(case)).max() <= TOL["fp16"]
+
+
+def test_wide_spread_merge_on_an_oversubscribed_grid(gpu):
+    """256 (sequence, KV head) units of 16 pairs at 16 splits each: 4,096
+    workgroups, 16 times what the chip holds at once, so splits wait on
+    partners dispatched after them. Every slice must still be merged once:
+    status stays 0 and sampled units match the oracle."""
+    lengths = synth.ragged_lengths(64, 900, 1500, 11, "wideover").tolist()
+    sample = [(0, 0), (17, 3), (40, 1), (63, 3)]
+    case = DecodeCase(batch=64, n_q=64, n_kv=4, head_dim=128, dtype="bf16", lengths=lengths, tag="wideover",
+                      device=gpu, host_rows=sample)
+    ws = kvc.workspace(case.k, case.v, 64, 16)
+    out = torch.full((64, 64, 128), float("nan"), device=gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    kvc.decode_step(case.k, case.v, case.seq_lens, case.k_new, case.v_new, case.q, out, ws, n_splits=16,
+                    status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all()
+    grp = 16
+    for b, g in sample:
+        k, v = case.oracle_inputs(b, g)
+        ref = oracle.decode_attention(case.q_host[b:b + 1, g * grp:(g + 1) * grp], k[None, None], v[None, None],
+                                      np.array([int(case.lengths[b])]), n_pending=1)[0]
+        assert np.abs(got[b, g * grp:(g + 1) * grp] - ref).max() <= TOL["bf16"], (b, g)
