@@ -142,11 +142,15 @@ kvc_status_t kvc_prefill_fill(const kvc_cache_t* cache, const int32_t* seq_lens,
  *
  * Layout and lifetime: uint32 ready flags (one per sequence, KV head, block
  * of query heads and split; the last split's word of each block holds that
- * block's epoch, a count of its merges), then fp32 per-split partial
- * results. The caller zero-fills the workspace once after allocating it. A
- * call's publishing splits raise their flags to epoch + 1 and its merging
- * split waits for exactly that value, then advances the epoch, so the
- * workspace serves any number of later calls with the same batch,
+ * block's epoch, a count of its merges), then 64 uint32 words per
+ * (sequence, KV head) for the wide-group kernel's shared merge (an arrival
+ * count that each call returns to zero, per-split claim words that hold the
+ * epoch of the call that last claimed them, and that merge's own epoch in
+ * the last word), then fp32 per-split partial results. The caller zero-fills the workspace once after
+ * allocating it. A call's publishing splits raise their flags (or claims) to
+ * epoch + 1 and its merging split waits for exactly that value, then
+ * advances the epoch, so the workspace serves any number of later calls with
+ * the same batch,
  * n_kv_heads, n_q_heads and split count (any lengths, any layer) without
  * clearing, including calls after one that reported KVC_DEVERR_SYNC: a flag
  * raised late in that call holds an old epoch's value and is never taken

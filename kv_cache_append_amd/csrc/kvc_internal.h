@@ -88,12 +88,13 @@ struct WsRegions {
   float* ml;
 };
 // Per (sequence, KV head), for the wide-group kernel's spread merge (up to
-// kWideSpreadMax splits): an arrival count and one claim word per output
-// slice, in a row of kWideSyncWords uint32.
+// kWideSpreadMax splits): an arrival count (word 0), one claim word per
+// output slice (words 1 ..) and the merge epoch (the last word), in a row of
+// kWideSyncWords uint32.
 constexpr int kWideSpreadMax = 32;
 constexpr int kWideSyncWords = 64;
 constexpr size_t kWideSyncBytes = kWideSyncWords * sizeof(uint32_t);
-static_assert(1 + kWideSpreadMax <= kWideSyncWords, "spread merge words");
+static_assert(1 + kWideSpreadMax < kWideSyncWords, "spread merge words");
 WsRegions workspace_regions(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits, void* ws);
 // Lays out a decode call's exchange space once its split count is known.
 typedef kvc_status_t (*RegionsFn)(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits, WsRegions* out);

@@ -10,11 +10,12 @@
 // row's epoch word (its last) stays in place whatever the geometry of the
 // calls: flags only ever hold epoch values and an epoch only grows, so a
 // flag left by an earlier call, of any geometry, never equals what a later
-// call waits for. The wide-group kernel's merge words come next, one pair
-// per (sequence, KV head) row, tagged with the epoch of the call that wrote
-// them, so that stale words are told apart the same way. The partial
-// outputs and (reference, sum) pairs follow,
-// rewritten by every call before they are read. The array is zero at load,
+// call waits for. The wide-group kernel's merge words come next, one row of
+// 64 per (sequence, KV head) at a fixed stride, which holds its own epoch
+// beside the claim words compared with it, so that stale claims are told
+// apart the same way whatever the geometry; its arrival count is back at
+// zero after every call. The partial outputs and (reference, sum) pairs
+// follow, rewritten by every call before they are read. The array is zero at load,
 // the state the epoch protocol starts from. Calls that overlap on one GPU
 // (two streams at once) share the array and race.
 

@@ -10,25 +10,28 @@
 // "从教学代码到生产实现还差什么"). With 64 query heads on one KV head a
 // decode step does 64 FLOPs per cache byte, past what the vector ALU
 // sustains at HBM rate, so both products run on v_mfma_f32_16x16x32:
-//   * one 256-thread workgroup per (sequence, KV head, split of the T axis);
-//     the unit's K/V rows of the split go through LDS in tiles of 64 keys,
-//     K as stored (padded rows), V transposed (one row per head-dim element),
-//     read by all four waves; the next tiles' loads are in flight meanwhile;
-//   * each wave owns column blocks of 16 (query, head) pairs; scores are
-//     computed transposed, S^T = K Q^T, so a lane holds the scores of one
-//     pair and the online softmax (a lazily moved reference, as in the other
-//     decode kernel) stays in its registers;
-//   * the output is accumulated transposed, O^T += V^T P^T, with each fp32
-//     weight split into two 16-bit parts (hi + lo, about 16 significant
-//     bits) so the product keeps the weights' precision; accumulation fp32;
+//   * one 512-thread workgroup (8 waves) per (sequence, KV head, split of
+//     the T axis); the split's K/V rows go from memory straight into LDS
+//     (buffer loads with the LDS destination) in tiles of 64 keys, as stored
+//     with the 16-byte chunks of each row permuted, through a ring of four
+//     tile buffers, so three tiles are in flight while one is computed;
+//   * each wave owns column blocks of 16 (query, head) pairs and half of each
+//     tile's keys; scores are computed transposed, S^T = K Q^T, so a lane
+//     holds the scores of one pair and the online softmax (a lazily moved
+//     reference, as in the other decode kernel) stays in its registers;
+//   * the output is accumulated transposed, O^T += V^T P^T, V^T read from the
+//     row-major tile with the transposing LDS reads; each fp32 weight is
+//     split into two 16-bit parts (hi + lo, about 16 significant bits) so the
+//     product keeps the weights' precision; accumulation fp32;
 //   * the newest attended row is folded in by the last split as a tile of its
 //     own (from k_new/v_new in the fused step, which also writes it into the
 //     cache), so kvc_decode_step and kvc_append + kvc_decode_attn add the same
 //     rows in the same order;
-//   * splits publish (reference, sum, unnormalised output) per pair and the
-//     last split merges them in split order, with the same workspace, epoch
-//     flags and workgroup placement as the other decode kernel (every split
-//     of a unit on one XCD).
+//   * splits publish (reference, sum, unnormalised output) per pair; up to 32
+//     splits share the merge (each split merges a slice of the unit's pairs
+//     once all have published, the last to arrive takes what no split
+//     claimed), more splits merge in the last split, in split order either
+//     way; every split of a unit runs on one XCD.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -154,8 +157,12 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int b = unit / p.n_kv;
   const int g = unit - b * p.n_kv;
   // the unit's epoch (see the merge below), requested behind the first
-  // tiles' loads and used at the end
+  // tiles' loads and used at the end: the last word of the unit's flag row
+  // for the last-split merge, the last word of its merge-word row for the
+  // spread merge, each in the row whose words it is compared with
   uint32_t* const flags = p.ws_flag + static_cast<int64_t>(unit) * p.n_hblk * p.flag_stride;
+  uint32_t* const sync = p.ws_sync + static_cast<int64_t>(unit) * kvc::kWideSyncWords;
+  uint32_t* const sync_epoch = sync + (kvc::kWideSyncWords - 1);
   uint32_t epoch = 0u;
 
   // Rows attended (n), the slot the fused append writes, device-side flags.
@@ -388,7 +395,9 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int n_tiles = (t_end - t0 + kWTile - 1) / kWTile;
   // the unit's epoch (see the merge), requested ahead of the tiles, so the
   // first tile's wait covers it
-  if (p.n_splits > 1) epoch = __hip_atomic_load(flags + p.flag_stride - 1, __ATOMIC_RELAXED, kSyncScope);
+  if (ns > 1)
+    epoch = __hip_atomic_load(ns <= kSpreadMax ? sync_epoch : flags + p.flag_stride - 1, __ATOMIC_RELAXED,
+                              kSyncScope);
 #pragma unroll
   for (int r = 0; r < NBUF - 1; ++r) load_tile(r, r);
   // The query registers, used here so that the compiler waits for their
@@ -567,15 +576,17 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     // falling on one. A split waits for the others only for a bounded time;
     // the last to arrive waits for nothing and, after its own slice, merges
     // every slice no one has claimed (those of splits that gave up waiting).
-    // Per (sequence, KV head): an arrival count, which the last arrival
-    // returns to zero when it is done, and one claim word per slice, raised
-    // to epoch + 1 by the one workgroup that merges the slice (an atomic
-    // maximum: each slice is written once, and a claim left by an earlier
-    // call is below this call's value). The last arrival then advances the
-    // epoch, which also tells splits still waiting that the merge is done.
+    // Per (sequence, KV head), in one row of merge words: an arrival count,
+    // which the last arrival returns to zero when it is done, one claim word
+    // per slice, raised to epoch + 1 by the one workgroup that merges the
+    // slice (an atomic maximum: each slice is written once), and the epoch
+    // itself (the row's last word). The last arrival advances the epoch,
+    // which also tells splits still waiting that the merge is done. A claim
+    // is only ever raised to its own row's epoch + 1 and that epoch then
+    // grows, so a claim left by an earlier call, of any geometry, is below
+    // this call's value.
     publish();
     __syncthreads();
-    uint32_t* const sync = p.ws_sync + static_cast<int64_t>(unit) * kvc::kWideSyncWords;
     uint32_t* const claims = sync + 1;
     __shared__ uint32_t ss[2];
     if (tid == 0) {
@@ -586,8 +597,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
         // (exchanges that write back what they find: performed in L2)
         uint32_t c = static_cast<uint32_t>(ns), e = epoch;
         __hip_atomic_compare_exchange_strong(sync, &c, c, __ATOMIC_RELAXED, __ATOMIC_RELAXED, kSyncScope);
-        __hip_atomic_compare_exchange_strong(flags + p.flag_stride - 1, &e, e, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             kSyncScope);
+        __hip_atomic_compare_exchange_strong(sync_epoch, &e, e, __ATOMIC_RELAXED, __ATOMIC_RELAXED, kSyncScope);
         if (c >= static_cast<uint32_t>(ns)) state = 1u;
         else if (e != epoch) break;            // the merge is done: nothing left to claim
       }
@@ -676,7 +686,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       __syncthreads();
       if (tid == 0) {
         __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, kSyncScope);
-        __builtin_amdgcn_raw_buffer_store_b32(epoch + 1u, frs, static_cast<int>((p.flag_stride - 1) * 4), 0, kXchgW);
+        __hip_atomic_store(sync_epoch, epoch + 1u, __ATOMIC_RELAXED, kSyncScope);
       }
     }
     return;

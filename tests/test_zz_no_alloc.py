@@ -70,3 +70,34 @@ def test_noalloc_rejects_calls_past_its_array(gpu):
                                      vp(case.q.data_ptr()), 64, ctypes.c_float(0.0883883), vp(out.data_ptr()), 0, 64,
                                      None, vp(torch.cuda.current_stream().cuda_stream))
     assert rc == 6     # KVC_ERR_WORKSPACE: 64 x 64 x 64 splits x 128 x 4 B of partials is past 16 MiB
+
+
+def test_noalloc_wide_calls_across_group_sizes(gpu):
+    """Wide-group calls whose head-block count changes between calls: the
+    merge words of a (sequence, KV head) stay at one place in the array while
+    its flag row moves with the geometry, so the spread merge's claims must be
+    compared with an epoch kept beside them. Every call, after three calls of
+    another geometry, equals the workspace entry point bit for bit and is
+    within the oracle's bar."""
+    lens = [700, 1300, 64, 999]
+    for i, grp in enumerate([16, 16, 16, 64, 16, 32]):
+        nq = 2 * grp
+        a = DecodeCase(batch=4, n_q=nq, n_kv=2, head_dim=128, dtype="bf16", lengths=lens, tag=f"nag{i}", device=gpu)
+        w = DecodeCase(batch=4, n_q=nq, n_kv=2, head_dim=128, dtype="bf16", lengths=lens, tag=f"nag{i}", device=gpu)
+        out_a = torch.full((4, nq, 128), float("nan"), device=gpu)
+        out_w = torch.empty_like(out_a)
+        st_a = torch.zeros(1, dtype=torch.int32, device=gpu)
+        st_w = torch.zeros(1, dtype=torch.int32, device=gpu)
+        _noalloc(a, out_a, 4, st_a)
+        ws = kvc.workspace(w.k, w.v, nq, 4)
+        kvc.decode_step(w.k, w.v, w.seq_lens, w.k_new, w.v_new, w.q, out_w, ws, n_splits=4, status=st_w)
+        torch.cuda.synchronize()
+        print(f"call {i}: group {grp}", flush=True)
+        assert int(st_a.item()) == 0 and int(st_w.item()) == 0
+        assert torch.equal(out_a, out_w)
+        got = out_a.double().cpu().numpy()
+        for (bb, g) in [(0, 1), (1, 0), (3, 1)]:
+            k, v = a.oracle_inputs(bb, g)
+            ref = oracle.decode_attention(a.q_host[bb:bb + 1, g * grp:(g + 1) * grp], k[None, None], v[None, None],
+                                          np.array([lens[bb]]), n_pending=1)[0]
+            assert np.abs(got[bb, g * grp:(g + 1) * grp] - ref).max() <= TOL["bf16"]
