@@ -108,11 +108,11 @@ class Workload:
         self.t_max = ring if ring else int(self.lengths.max()) + margin_tokens + 1
         L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
         tdt = synth.DTYPES[cfg.dtype]
-        # contiguous 16-bit caches with 16..128 (query, head) pairs per KV head
+        # contiguous 16-bit caches with 8..128 (query, head) pairs per KV head
         # run on the wide-group kernel (long query blocks on the prefill kernel)
         pairs = cfg.group * max(block_q, 1)
         self.wide = (not (page or ring or quant) and cfg.dtype in ("fp16", "bf16") and cfg.head_dim in (64, 128)
-                     and 16 <= pairs <= 128 and not (block_q >= 8 and pairs >= 32))
+                     and 8 <= pairs <= 128 and not (block_q >= 8 and pairs >= 32))
         self.fused_advance = not (block_q or page or ring or quant)   # (see below)
         if quant:
             self._init_quant(cfg, seed, splits, dev, tdt)
@@ -451,7 +451,8 @@ def _pmc_summary(fetch_csv: str, write_csv: str, out_path: str, args):
     import synth
     cfg = synth.CONFIGS[args.config]
     algo = 2 * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes * (int(cfg.lengths(args.seed).long().sum()) + cfg.batch)
-    kernel = "wide_decode_kernel" if cfg.group >= 16 else "decode_kernel"
+    kernel = ("wide_decode_kernel" if cfg.dtype in ("fp16", "bf16") and cfg.head_dim in (64, 128) and cfg.group >= 8
+              else "decode_kernel")
     rec = {
         "workload": args.config,
         "kernel": kernel,

@@ -212,7 +212,7 @@ int32_t kvc_decode_splits_for_lengths(const kvc_cache_t* cache, int32_t n_q_head
  * Accumulation is fp32; results are run-to-run deterministic.
  * Supported: head_dim in {64, 128, 256} for every dtype, plus head_dim 4..32
  * (powers of two with head_dim * elem_bytes >= 16); any group size.
- * Groups of 16..128 query heads per KV head on fp16/bf16 caches with head_dim
+ * Groups of 8..128 query heads per KV head on fp16/bf16 caches with head_dim
  * 64 or 128 run on a kernel that streams each KV head's K/V once for the
  * whole group, both products on the matrix cores (course notes §2.2, §2.5:
  * the group shares its K/V, saving bytes, not FLOPs); the other shapes read
@@ -312,8 +312,8 @@ kvc_status_t kvc_decode_step_noalloc(const kvc_cache_t* cache, const int32_t* se
  *
  * The (query, head) pairs of a KV head are processed like the query heads of
  * a larger group, so K/V rows are streamed once per block of up to 8 pairs,
- * or, on fp16/bf16 caches with head_dim 64 or 128 and 16..128 pairs per KV
- * head, once for all of them (the wide-group kernel, as for decode with 16+
+ * or, on fp16/bf16 caches with head_dim 64 or 128 and 8..128 pairs per KV
+ * head, once for all of them (the wide-group kernel, as for decode with 8+
  * query heads per KV head); this suits short blocks (verify steps, small
  * chunks). Blocks of t_q >= 8
  * with t_q * (n_q_heads / n_kv_heads) >= 32 on fp16/bf16 caches with head_dim

@@ -134,7 +134,7 @@ kvc_cache_t qcache_view(const kvc_qcache_t* c);
 // (group size times queries per sequence); contiguous caches. Its launch
 // takes arguments already validated by launch_decode.
 #ifndef KVC_WIDE_MIN_PAIRS
-#define KVC_WIDE_MIN_PAIRS 16
+#define KVC_WIDE_MIN_PAIRS 8
 #endif
 bool wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs);
 kvc_status_t launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,

@@ -1882,7 +1882,7 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   // The kernels address one (sequence, KV head) slice of K/V with 32-bit
   // byte offsets (plus up to two tiles past the end, read back as zeros).
   if ((static_cast<int64_t>(cache->max_len) + 2048) * cache->stride_t * s > 0x7fffffffll) return KVC_ERR_SHAPE;
-  // Contiguous 16-bit caches with 16..128 (query, head) pairs per KV head run
+  // Contiguous 16-bit caches with 8..128 (query, head) pairs per KV head run
   // on the wide-group kernel (K/V streamed once for all pairs, both products
   // on the matrix cores).
   const bool wide = pg == nullptr && !ring && kvc::routes_wide(cache, n_qv);

@@ -1,4 +1,4 @@
-"""GPU parity of the wide-group decode kernel (16 to 128 (query, head) pairs
+"""GPU parity of the wide-group decode kernel (8 to 128 (query, head) pairs
 per KV head on a contiguous fp16/bf16 cache with head dim 64 or 128: MQA,
 wide GQA and query blocks), through the C ABI, against the fp64 oracle.
 
@@ -35,12 +35,13 @@ def _oracle_all(case: DecodeCase):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("n_q,n_kv", [(16, 1), (32, 1), (64, 1), (128, 1), (64, 2)])
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("n_q,n_kv", [(8, 1), (24, 2), (16, 1), (32, 1), (64, 1), (128, 1), (64, 2)])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3])
 def test_wide_decode_step_matches_oracle(gpu, dtype, d, n_q, n_kv, splits):
     """The fused step (append + attend T_b + 1 rows) on the wide kernel, for
-    lengths on and around the 64-key tile and empty sequences, with one, three
-    or the library's number of splits; the appended rows are exact."""
+    lengths on and around the 64-key tile and empty sequences, with one, two
+    (last-split merge), three (spread merge) or the library's number of
+    splits; the appended rows are exact."""
     case = DecodeCase(batch=len(LENS), n_q=n_q, n_kv=n_kv, head_dim=d, dtype=dtype, lengths=LENS,
                       tag=f"wide{dtype}{d}{n_q}{n_kv}", device=gpu)
     ws = kvc.workspace(case.k, case.v, n_q, splits)
@@ -126,7 +127,7 @@ def test_wide_out_in_cache_dtype_is_rounded_fp32_out(gpu, dtype):
 @pytest.mark.parametrize("splits", [0, 3])
 def test_wide_query_block_matches_oracle(gpu, dtype, hq, hkv, t_q, splits):
     """A block of t_q new queries per sequence (speculative verify, short
-    prefill chunks) with 16..128 (query, head) pairs per KV head runs on the
+    prefill chunks) with 8..128 (query, head) pairs per KV head runs on the
     wide kernel; the lower-right causal mask of course notes §3.3."""
     case = BlockCase(batch=4, n_q=hq, n_kv=hkv, d=128, dtype=dtype, lengths=[0, 37, 300, 1025], t_q=t_q,
                      tag=f"wblk{dtype}{hq}{hkv}{t_q}", device=gpu)
