@@ -786,73 +786,77 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   u32x4 xk[NXK];
 #pragma unroll
   for (int m = 0; m < NXK; ++m) xk[m] = u32x4{0u, 0u, 0u, 0u};
-  if (has_x && wave == 0) {
-    const char* krow;
-    const char* vrow;
-    if (x_new) {
-      const int64_t noff = b * p.nsb + g * p.nsh;
-      krow = p.k_new + noff;
-      vrow = p.v_new + noff;
-    } else {
-      const int64_t xo = slot_offset(p, b, g, xrow);
-      krow = xo < 0 ? nullptr : p.k + xo;
-      vrow = xo < 0 ? nullptr : p.v + xo;
-      if (xo < 0 && lane == 0) flag(p, KVC_DEVERR_PAGE);
-    }
-    if (krow != nullptr) {
-      if constexpr (kQuant) {                  // 8 code bytes of V (K is loaded in the MFMA layout)
-        if (!x_new) {                          // (a new row is quantised below)
-          const u32x2 w = *reinterpret_cast<const u32x2*>(vrow + li * VSL);
-          nv = u32x4{w[0], w[1], 0u, 0u};
-        }
-      } else {
-        nk = *reinterpret_cast<const u32x4*>(krow + li * VSL);
-        nv = *reinterpret_cast<const u32x4*>(vrow + li * VSL);
-      }
-      if constexpr (kMfma) {
-        if ((!kQuant || !x_new) && (lane & 15) == 0) {   // (a new 8-bit row's codes come through LDS)
-#pragma unroll
-          for (int m = 0; m < NXK; ++m) xk[m] = *reinterpret_cast<const u32x4*>(krow + (4 * m + (lane >> 4)) * 16);
-        }
-      }
-    }
-  }
   float xks = 0.f, xvs = 0.f;                   // scales of the folded row (8-bit caches)
-  if constexpr (kQuant) {
+  // The row's loads (and, for a new row on an 8-bit cache, its
+  // quantisation), issued by each path after its first tiles' loads.
+  auto load_x_row = [&]() {
     if (has_x && wave == 0) {
+      const char* krow;
+      const char* vrow;
       if (x_new) {
-        // The step's new row, quantised as kvc_quant_append does (the same
-        // device function), so the fused step matches append + decode bit
-        // for bit; its codes go through LDS to the K and V layouts.
         const int64_t noff = b * p.nsb + g * p.nsh;
-        uint32_t xkc, xvc;                     // this lane's code bytes of the new row
-        xks = quant_row<ET, KQ, D>(p.k_new + noff, lane, xkc);
-        xvs = quant_row<ET, KQ, D>(p.v_new + noff, lane, xvc);
-        store_codes<D / 64>(reinterpret_cast<char*>(&sm_x[0][lane * (D / 64)]), xkc);
-        store_codes<D / 64>(reinterpret_cast<char*>(&sm_x[1][lane * (D / 64)]), xvc);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_wave_barrier();
-        const u32x2 w = *reinterpret_cast<const u32x2*>(&sm_x[1][li * VSL]);
-        nv = u32x4{w[0], w[1], 0u, 0u};
-        // the first head block also writes the row into the cache: no
-        // workgroup of this launch reads that slot from memory
-        if (hb == 0) {
-          const int64_t ao = slot_offset(p, b, g, arow);
-          store_codes<D / 64>(p.k + ao + lane * (D / 64), xkc);
-          store_codes<D / 64>(p.v + ao + lane * (D / 64), xvc);
-          if (lane == 0) {
-            const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(arow) * 4;
-            *reinterpret_cast<float*>(p.k_scale + so) = xks;
-            *reinterpret_cast<float*>(p.v_scale + so) = xvs;
+        krow = p.k_new + noff;
+        vrow = p.v_new + noff;
+      } else {
+        const int64_t xo = slot_offset(p, b, g, xrow);
+        krow = xo < 0 ? nullptr : p.k + xo;
+        vrow = xo < 0 ? nullptr : p.v + xo;
+        if (xo < 0 && lane == 0) flag(p, KVC_DEVERR_PAGE);
+      }
+      if (krow != nullptr) {
+        if constexpr (kQuant) {                  // 8 code bytes of V (K is loaded in the MFMA layout)
+          if (!x_new) {                          // (a new row is quantised below)
+            const u32x2 w = *reinterpret_cast<const u32x2*>(vrow + li * VSL);
+            nv = u32x4{w[0], w[1], 0u, 0u};
+          }
+        } else {
+          nk = *reinterpret_cast<const u32x4*>(krow + li * VSL);
+          nv = *reinterpret_cast<const u32x4*>(vrow + li * VSL);
+        }
+        if constexpr (kMfma) {
+          if ((!kQuant || !x_new) && (lane & 15) == 0) {   // (a new 8-bit row's codes come through LDS)
+#pragma unroll
+            for (int m = 0; m < NXK; ++m) xk[m] = *reinterpret_cast<const u32x4*>(krow + (4 * m + (lane >> 4)) * 16);
           }
         }
-      } else {
-        const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(xrow) * 4;
-        xks = *reinterpret_cast<const float*>(p.k_scale + so);
-        xvs = *reinterpret_cast<const float*>(p.v_scale + so);
       }
     }
-  }
+    if constexpr (kQuant) {
+      if (has_x && wave == 0) {
+        if (x_new) {
+          // The step's new row, quantised as kvc_quant_append does (the same
+          // device function), so the fused step matches append + decode bit
+          // for bit; its codes go through LDS to the K and V layouts.
+          const int64_t noff = b * p.nsb + g * p.nsh;
+          uint32_t xkc, xvc;                     // this lane's code bytes of the new row
+          xks = quant_row<ET, KQ, D>(p.k_new + noff, lane, xkc);
+          xvs = quant_row<ET, KQ, D>(p.v_new + noff, lane, xvc);
+          store_codes<D / 64>(reinterpret_cast<char*>(&sm_x[0][lane * (D / 64)]), xkc);
+          store_codes<D / 64>(reinterpret_cast<char*>(&sm_x[1][lane * (D / 64)]), xvc);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_wave_barrier();
+          const u32x2 w = *reinterpret_cast<const u32x2*>(&sm_x[1][li * VSL]);
+          nv = u32x4{w[0], w[1], 0u, 0u};
+          // the first head block also writes the row into the cache: no
+          // workgroup of this launch reads that slot from memory
+          if (hb == 0) {
+            const int64_t ao = slot_offset(p, b, g, arow);
+            store_codes<D / 64>(p.k + ao + lane * (D / 64), xkc);
+            store_codes<D / 64>(p.v + ao + lane * (D / 64), xvc);
+            if (lane == 0) {
+              const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(arow) * 4;
+              *reinterpret_cast<float*>(p.k_scale + so) = xks;
+              *reinterpret_cast<float*>(p.v_scale + so) = xvs;
+            }
+          }
+        } else {
+          const int64_t so = b * p.ssb + g * p.ssh + static_cast<int64_t>(xrow) * 4;
+          xks = *reinterpret_cast<const float*>(p.k_scale + so);
+          xvs = *reinterpret_cast<const float*>(p.v_scale + so);
+        }
+      }
+    }
+  };
 
   // K/V of this unit through buffer resources built per tile on the scalar
   // unit: base = the tile's first row, range = up to row t_end, so rows of a
@@ -894,31 +898,6 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
     constexpr int NBM = KVC_MFMA_PREFETCH + 1;
     const int r16 = lane & 15;                // score row of this lane
     const int kq = lane >> 4;                 // its slice group, and its head quad in the scores
-
-    u32x4 qa[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      qa[m] = u32x4{0u, 0u, 0u, 0u};
-      const int qe = kQuant ? 64 * (m >> 1) + 16 * kq + 8 * (m & 1) : (4 * m + kq) * EPL;   // first element
-      if (r16 < nh)
-        qa[m] = *reinterpret_cast<const u32x4*>(p.q + (pair_row(p, b, g, v_first + r16) * D + qe) * ET::kBytes);
-    }
-    float hbias[4];                           // 0 where (lane, register) is a real head's score
-#pragma unroll
-    for (int t = 0; t < 4; ++t) hbias[t] = (kq < NQ && 4 * kq + t < nh) ? 0.f : -INFINITY;
-    int plim[4];                              // slot limit of the pair in (lane, register t)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) plim[t] = pair_limit(p, n, v_first + 4 * kq + t);
-    const bool block = p.block != 0;
-    float refh[4 * NQ];                       // wave-uniform reference per head
-#pragma unroll
-    for (int h = 0; h < 4 * NQ; ++h) refh[h] = kEmpty;
-    float lsum[4] = {0.f, 0.f, 0.f, 0.f};    // per-lane sums, score layout
-    f32x4 accq[GB >= 4 ? NQ : 1][EPL];       // 4x4x1 outputs: register i = head 4q + i
-#pragma unroll
-    for (int q = 0; q < (GB >= 4 ? NQ : 1); ++q)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) accq[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     uint32_t koff[NKL], voffm[NP];
 #pragma unroll
@@ -982,6 +961,47 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
         VS = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(vsr, r16 * 4, 0, kStream)));
       }
     };
+
+    // The first tiles' loads leave first: they need only the split's rows,
+    // and the query and newest-row loads and the per-pair setup below then
+    // run while those loads are in flight instead of ahead of them.
+    u32x4 KB[NBM][NKL];
+    VT VB[NBM][NP];
+    float KSB[NBM], VSB[NBM];
+    const int base0 = __builtin_amdgcn_readfirstlane(t0 + wave * 16);
+    const int n_tiles0 = base0 < t_end ? (t_end - base0 + TSM - 1) / TSM : 0;
+    if constexpr (kQuant) load_x_row();       // (a new 8-bit row is quantised: its wait stays ahead of the tiles)
+    if (n_tiles0 > 0) {
+#pragma unroll
+      for (int r = 0; r < NBM - 1; ++r) load_tile(base0 + r * TSM, KB[r], VB[r], KSB[r], VSB[r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!kQuant) load_x_row();
+
+    u32x4 qa[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      qa[m] = u32x4{0u, 0u, 0u, 0u};
+      const int qe = kQuant ? 64 * (m >> 1) + 16 * kq + 8 * (m & 1) : (4 * m + kq) * EPL;   // first element
+      if (r16 < nh)
+        qa[m] = *reinterpret_cast<const u32x4*>(p.q + (pair_row(p, b, g, v_first + r16) * D + qe) * ET::kBytes);
+    }
+    float hbias[4];                           // 0 where (lane, register) is a real head's score
+#pragma unroll
+    for (int t = 0; t < 4; ++t) hbias[t] = (kq < NQ && 4 * kq + t < nh) ? 0.f : -INFINITY;
+    int plim[4];                              // slot limit of the pair in (lane, register t)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) plim[t] = pair_limit(p, n, v_first + 4 * kq + t);
+    const bool block = p.block != 0;
+    float refh[4 * NQ];                       // wave-uniform reference per head
+#pragma unroll
+    for (int h = 0; h < 4 * NQ; ++h) refh[h] = kEmpty;
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};    // per-lane sums, score layout
+    f32x4 accq[GB >= 4 ? NQ : 1][EPL];       // 4x4x1 outputs: register i = head 4q + i
+#pragma unroll
+    for (int q = 0; q < (GB >= 4 ? NQ : 1); ++q)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) accq[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto lane_ref = [&](int t) { return (NQ > 1 && kq == 1) ? refh[4 + t] : refh[t]; };
 
@@ -1081,6 +1101,12 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
     // flight, rather than after the loop, where the wave would run it alone.
     bool x_done = false;
     auto fold_x = [&]() {
+      // The row's registers are made opaque here: otherwise the compiler
+      // hoists their selects and conversions ahead of the streaming loop,
+      // and its wait for the row's loads there holds back the first tiles'.
+      asm volatile("" : "+v"(nv));
+#pragma unroll
+      for (int m = 0; m < NXK; ++m) asm volatile("" : "+v"(xk[m]));
       u32x4 K[NKL];
       VT V[NP];
       static_assert(NKL == NXK, "x-row K slices");
@@ -1103,14 +1129,13 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
     // lookup, which counts tiles from t0, never sees one)
     for (int seg = 0; seg < n_seg; ++seg) {
       if (seg == 1) t_end = t1;
-      int base = __builtin_amdgcn_readfirstlane((seg == 0 ? t0 : seg1_lo) + wave * 16);
-      const int n_tiles = base < t_end ? (t_end - base + TSM - 1) / TSM : 0;
+      int base = seg == 0 ? base0 : __builtin_amdgcn_readfirstlane(seg1_lo + wave * 16);
+      const int n_tiles = seg == 0 ? n_tiles0 : (base < t_end ? (t_end - base + TSM - 1) / TSM : 0);
       if (n_tiles > 0) {
-        u32x4 KB[NBM][NKL];
-        VT VB[NBM][NP];
-        float KSB[NBM], VSB[NBM];
+        if (seg == 1) {                       // (seg 0's first tiles were requested above)
 #pragma unroll
-        for (int r = 0; r < NBM - 1; ++r) load_tile(base + r * TSM, KB[r], VB[r], KSB[r], VSB[r]);
+          for (int r = 0; r < NBM - 1; ++r) load_tile(base + r * TSM, KB[r], VB[r], KSB[r], VSB[r]);
+        }
         bool done = false;
         for (int it = 0; !done; it += NBM) {
 #pragma unroll
@@ -1157,6 +1182,7 @@ __global__ __launch_bounds__(KVC_WAVES * 64, (decode_min_wgs<ET, D, GB, KQ>())) 
   // Vector-ALU path (fp32 caches, and rows that are not whole 32-element
   // slices): every lane holds its 16-byte slice of q for each head of the
   // block, and a row's LPR lanes reduce their partial dot products with DPP.
+  load_x_row();
   u32x4 qv[GB];
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
