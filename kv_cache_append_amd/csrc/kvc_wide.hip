@@ -167,6 +167,39 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   uint32_t* const sync_epoch = sync + (kvc::kWideSyncWords - 1);
   uint32_t epoch = 0u;
 
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cbw = wave & 3;                          // first column block of this wave
+  const int kh = wave >> 2;                          // which half of each tile's keys
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int gv = p.group * p.t_q;                    // (query, head) pairs of this KV head
+  const int ncb = (gv + 15) / 16;
+
+  // The wave's pairs as B operands of the score product (column = pair r16
+  // of column block cbw + 4j, 8 elements 32c + 8grp of its query row),
+  // requested first: they do not depend on the sequence's length, so their
+  // round trip overlaps the length's. The rows of a unit's pairs lie within
+  // t_q * H_q rows of its first one; a lane with no pair reads past the
+  // range (zeros).
+  const char* const qunit = uniform_cptr(p.q + ((static_cast<int64_t>(b) * p.t_q) * p.n_q + g * p.group) * D * 2);
+  const __amdgpu_buffer_rsrc_t qrs = wrsrc(qunit, static_cast<uint32_t>(p.t_q * p.n_q * D * 2));
+  u32x4 qf[QB][NC];
+  bool cb_on[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const int cb = cbw + 4 * j;
+    cb_on[j] = cb < ncb;
+    const int v = cb * 16 + r16;
+    const int qi = v / p.group;
+    const uint32_t qoff = cb_on[j] && v < gv
+                              ? static_cast<uint32_t>(((qi * p.n_q + (v - qi * p.group)) * D + 8 * grp) * 2)
+                              : 0x80000000u;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) qf[j][cc] = wload<0>(qrs, qoff + 64u * cc);
+  }
+
   // Rows attended (n), the slot the fused append writes, device-side flags.
   const int c0 = p.seq_lens[b];
   // kvc_decode_step_advance: the next step's lengths, into another array
@@ -189,7 +222,6 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     if (c0 < 0) n = 0;             // a negative length: a zero row, nothing attended
   }
   if (dflags != 0 && g == 0 && split == 0 && threadIdx.x == 0 && p.status != nullptr) atomicOr(p.status, dflags);
-  const int gv = p.group * p.t_q;                    // (query, head) pairs of this KV head
   auto store_out = [&](int64_t idx, float x) {
     if (p.out_f32) static_cast<float*>(p.out)[idx] = x;
     else ET::store(p.out, idx, x);
@@ -197,6 +229,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   if (n <= 0) {                                      // empty sequence: zero rows
     if (split == 0)
       for (int t = threadIdx.x; t < gv * D; t += blockDim.x) store_out(wpair_row(p, b, g, t / D) * D + t % D, 0.f);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the query loads)
     return;
   }
   // The T axis in equal whole tiles; decode folds the newest row (n - 1) in
@@ -204,21 +237,15 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int streamed = p.block ? n : n - 1;
   const int chunk = max(kWTile, ((streamed + p.n_splits - 1) / p.n_splits + kWTile - 1) & ~(kWTile - 1));
   const int ns = streamed > 0 ? min(p.n_splits, (streamed + chunk - 1) / chunk) : 1;
-  if (split >= ns) return;                           // inactive split
+  if (split >= ns) {                                 // inactive split
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the query loads)
+    return;
+  }
   const bool spread = ns >= kSpreadMin && ns <= kSpreadMax;   // how the splits merge (below)
   const int t0 = split * chunk;
   const int t_end = split == ns - 1 ? streamed : t0 + chunk;   // rows streamed from the cache: [t0, t_end)
   const bool has_x = !p.block && split == ns - 1;
   const bool x_new = has_x && append_row == n - 1;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cbw = wave & 3;                          // first column block of this wave
-  const int kh = wave >> 2;                          // which half of each tile's keys
-  const int r16 = lane & 15;
-  const int grp = lane >> 4;
-  const int ncb = (gv + 15) / 16;
 
   // The fused append: the newest row into its slot (no workgroup of this
   // launch reads that slot from the cache). Its loads are issued first and
@@ -234,28 +261,12 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const u32x4 kn_row = wload<0>(kn_rs, static_cast<uint32_t>(lane) * 16u);
   const u32x4 vn_row = wload<0>(vn_rs, static_cast<uint32_t>(lane) * 16u);
 
-  // The wave's pairs as B operands of the score product (column = pair r16
-  // of column block cbw + 4j, 8 elements 32c + 8grp of its query row), and
-  // each pair's slot limit (lower-right causal mask of a query block). The
-  // rows of a unit's pairs lie within t_q * H_q rows of its first one; a
-  // lane with no pair reads past the range (zeros).
-  const char* const qunit = uniform_cptr(p.q + ((static_cast<int64_t>(b) * p.t_q) * p.n_q + g * p.group) * D * 2);
-  const __amdgpu_buffer_rsrc_t qrs = wrsrc(qunit, static_cast<uint32_t>(p.t_q * p.n_q * D * 2));
-  u32x4 qf[QB][NC];
+  // Each pair's slot limit (lower-right causal mask of a query block).
   int plim[QB];
-  bool cb_on[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const int cb = cbw + 4 * j;
-    cb_on[j] = cb < ncb;
-    const int v = cb * 16 + r16;
+    const int v = (cbw + 4 * j) * 16 + r16;
     plim[j] = p.block ? n - p.t_q + v / p.group + 1 : n;
-    const int qi = v / p.group;
-    const uint32_t qoff = cb_on[j] && v < gv
-                              ? static_cast<uint32_t>(((qi * p.n_q + (v - qi * p.group)) * D + 8 * grp) * 2)
-                              : 0x80000000u;
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) qf[j][cc] = wload<0>(qrs, qoff + 64u * cc);
   }
 
   const uint32_t st = static_cast<uint32_t>(p.st);
@@ -396,6 +407,15 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // included (tiles past the last read zeros and are not computed): the wait
   // counts are fixed only if every step issues the same loads.
   const int n_tiles = (t_end - t0 + kWTile - 1) / kWTile;
+  // The query registers, used here so that the compiler waits for their
+  // loads once, before the tiles' loads: a wait it placed later would count
+  // only the loads it knows of, not the tiles' (inline assembly), and so
+  // wait for most of those too. The query loads left at the start of the
+  // kernel, so this wait is normally over at once.
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) asm volatile("" ::"v"(qf[j][cc]));
   // the unit's epoch (see the merge), requested ahead of the tiles, so the
   // first tile's wait covers it
   if (ns > 1)
@@ -403,13 +423,6 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
                               kSyncScope);
 #pragma unroll
   for (int r = 0; r < NBUF - 1; ++r) load_tile(r, r);
-  // The query registers, used here so that the compiler waits for their
-  // loads once, ahead of the loop: a wait it placed in the loop would count
-  // only the loads it knows of, not the tile loads, and so wait for those.
-#pragma unroll
-  for (int j = 0; j < QB; ++j)
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) asm volatile("" ::"v"(qf[j][cc]));
   for (int it = 0; it < n_tiles; it += NBUF) {
 #pragma unroll
     for (int r = 0; r < NBUF; ++r) {          // unrolled: buffers are compile-time
