@@ -62,8 +62,8 @@ def _parse():
                     help="paged caches: pages handed out in a random order, or interleaved by position "
                          "(page p of every sequence adjacent, as sequences growing together receive them)")
     ap.add_argument("--block-q", type=int, default=0,
-                    help="time a block of N new tokens per sequence per layer (kvc_prefill_fill + "
-                         "kvc_block_attn, e.g. a speculative verify step) instead of the decode step")
+                    help="time a block of N new tokens per sequence per layer (kvc_block_step: the block's "
+                         "fill and its attention, e.g. a speculative verify step) instead of the decode step")
     ap.add_argument("--prefill", type=int, default=0,
                     help="time a prompt prefill of N tokens per sequence on the config's layer shape instead "
                          "of the decode step: per layer kvc_prefill_fill + kvc_prefill_attn (causal attention "
@@ -111,8 +111,9 @@ class Workload:
         # contiguous 16-bit caches with 8..128 (query, head) pairs per KV head
         # run on the wide-group kernel (long query blocks on the prefill kernel)
         pairs = cfg.group * max(block_q, 1)
-        self.wide = (not (page or ring or quant) and cfg.dtype in ("fp16", "bf16") and cfg.head_dim in (64, 128)
-                     and 8 <= pairs <= 128 and not (block_q >= 8 and pairs >= 32))
+        sixteen = cfg.dtype in ("fp16", "bf16") and cfg.head_dim in (64, 128)
+        self.block_prefill = bool(block_q) and sixteen and block_q >= 8 and pairs >= 32
+        self.wide = not (page or ring or quant) and sixteen and 8 <= pairs <= 128 and not self.block_prefill
         self.fused_advance = not (block_q or page or ring or quant)   # (see below)
         if quant:
             self._init_quant(cfg, seed, splits, dev, tdt)
@@ -246,10 +247,9 @@ class Workload:
             ks = self.k_new.stride()
             for l in range(cfg.n_layers):
                 d = ctypes.byref(self.descs[l])
-                rc = lib.kvc_prefill_fill(d, seq, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()),
-                                          ks[1], ks[2], ks[3], n, stat, st)
-                rc = rc or lib.kvc_block_attn(d, seq, n, vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
-                                              vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, stat, st)
+                rc = lib.kvc_block_step(d, seq, n, vp(self.k_new[l].data_ptr()), vp(self.v_new[l].data_ptr()),
+                                        ks[1], ks[2], ks[3], vp(self.q[l].data_ptr()), cfg.n_q_heads, self.scale,
+                                        vp(self.out[l].data_ptr()), 0, ws, wsb, self.splits, stat, st)
                 if rc:
                     raise RuntimeError(f"libkvc returned {rc} at layer {l}")
             return
@@ -598,8 +598,10 @@ def _run_config(name, args, with_cpu):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("copy_rows_kernel + " + ("wide_decode_kernel" if w.wide else "decode_kernel") +
-                       " (kvc_prefill_fill + kvc_block_attn per layer; time per layer covers both)" if args.block_q else
+            "kernel": (("wide_decode_kernel (kvc_block_step per layer: the block's fill and attention in one launch)"
+                        if w.wide else "copy_rows_kernel + " + ("prefill_kernel" if w.block_prefill else "decode_kernel") +
+                        " (kvc_block_step per layer: fill, then attention; time per layer covers both)")
+                       if args.block_q else
                        "decode_kernel (kvc_ring_decode_step: ring append + windowed attention + merge, one "
                        "launch per layer)" if args.ring else
                        "decode_kernel on 8-bit codes (kvc_quant_decode_attn, timed alone; the step adds one "

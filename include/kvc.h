@@ -336,6 +336,40 @@ kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* seq_lens, i
 size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, int32_t t_q, int32_t n_splits);
 
 /*
+ * kvc_block_step -- kvc_prefill_fill of a block's t_q new rows per sequence
+ * followed by kvc_block_attn over them, the block form of kvc_decode_step
+ * (course notes "第 1 周 · Day 4" §3.1, the cache update of T new tokens, and
+ * §3.3, the lower-right causal mask with a cache): k_new/v_new rows t of
+ * sequence b are written into slots seq_lens[b] + t, and query i of the block
+ * attends slots 0 .. seq_lens[b] + i. Cache bytes and output bits are those
+ * of the two separate calls with the same arguments.
+ *
+ *   k_new, v_new  [batch, n_kv_heads, t_q, head_dim] rows in the cache dtype
+ *             with element strides new_stride_b, new_stride_h, new_stride_t
+ *             (head_dim contiguous; new_stride_t >= head_dim when t_q > 1).
+ *   Other arguments as kvc_block_attn (workspace sized by
+ *             kvc_block_workspace_bytes); seq_lens is only read.
+ *
+ * Where the block runs on the wide-group kernel (fp16/bf16, head_dim 64 or
+ * 128, 8..128 (query, head) pairs per KV head, not a prefill-kernel block)
+ * and k_new/v_new rows are 16-byte aligned, this is one launch: the kernel
+ * folds the block's rows in from k_new/v_new and writes them into the cache
+ * (no workgroup reads those slots from the cache). Otherwise it enqueues the
+ * fill, then the attention. A block that does not fit (seq_lens[b] < 0 or
+ * seq_lens[b] + t_q > max_len) is not written, gets zero rows and sets
+ * KVC_DEVERR_BADLEN / KVC_DEVERR_CAPACITY, as with the separate calls.
+ * Host-side errors as for kvc_prefill_fill and kvc_block_attn, returned
+ * before anything is enqueued.
+ */
+kvc_status_t kvc_block_step(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
+                            const void* k_new, const void* v_new,
+                            int64_t new_stride_b, int64_t new_stride_h, int64_t new_stride_t,
+                            const void* q, int32_t n_q_heads, float scale,
+                            void* out, int32_t out_dtype,
+                            void* workspace, size_t workspace_bytes, int32_t n_splits,
+                            uint32_t* dev_status, hipStream_t stream);
+
+/*
  * kvc_prefill_attn -- the same operation as kvc_block_attn (query i of
  * sequence b attends slots 0 .. seq_lens[b] + i; course notes "第 1 周 ·
  * Day 4" §3.3, masks with a cache), tiled for long blocks: a whole prompt

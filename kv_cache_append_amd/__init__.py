@@ -35,7 +35,7 @@ STATUS = {
 # Every symbol include/kvc.h declares.
 EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_decode_splits",
            "kvc_decode_attn", "kvc_decode_step", "kvc_decode_step_advance", "kvc_decode_step_noalloc",
-           "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes",
+           "kvc_decode_splits_for_lengths", "kvc_block_attn", "kvc_block_workspace_bytes", "kvc_block_step",
            "kvc_prefill_attn",
            "kvc_paged_append", "kvc_paged_prefill_fill", "kvc_paged_decode_workspace_bytes",
            "kvc_paged_decode_attn", "kvc_paged_decode_step",
@@ -92,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.kvc_decode_step.restype = i32
     lib.kvc_block_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
     lib.kvc_block_attn.restype = i32
+    lib.kvc_block_step.argtypes = [cp, vp, i32, vp, vp, i64, i64, i64, vp, i32, f32, vp, i32, vp, sz, i32, vp, vp]
+    lib.kvc_block_step.restype = i32
     lib.kvc_block_workspace_bytes.argtypes = [cp, i32, i32, i32]
     lib.kvc_block_workspace_bytes.restype = sz
     lib.kvc_prefill_attn.argtypes = [cp, vp, i32, vp, i32, f32, vp, i32, vp, vp]
@@ -366,6 +368,26 @@ def block_attn(k_cache, v_cache, seq_lens, q, out, workspace, scale=None, n_spli
                               _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
                               workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
                               _stream(stream)), "kvc_block_attn")
+
+
+def block_step(k_cache, v_cache, seq_lens, k_new, v_new, q, out, workspace, scale=None, n_splits: int = 0,
+               status=None, stream=None, desc=None):
+    """kvc_block_step: write k_new/v_new [B, H_kv, t_q, D] at slots
+    [seq_lens[b], +t_q), then block_attn over them (one launch where the
+    wide-group kernel serves the block)."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 4:
+        raise ValueError("q and out must be contiguous [B, t_q, H_q, D]")
+    if k_new.dim() != 4 or k_new.stride() != v_new.stride() or k_new.stride(3) != 1:
+        raise ValueError("k_new and v_new must be [B, H_kv, t_q, D] with equal strides and D contiguous")
+    _check(lib.kvc_block_step(ctypes.byref(c), _ptr(seq_lens), q.shape[1], _ptr(k_new), _ptr(v_new),
+                              k_new.stride(0), k_new.stride(1), k_new.stride(2), _ptr(q), q.shape[2], float(scale),
+                              _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
+                              _stream(stream)), "kvc_block_step")
 
 
 def prefill_attn(k_cache, v_cache, seq_lens, q, out, scale=None, status=None, stream=None, desc=None):

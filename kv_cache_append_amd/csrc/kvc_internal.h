@@ -137,11 +137,13 @@ kvc_cache_t qcache_view(const kvc_qcache_t* c);
 #define KVC_WIDE_MIN_PAIRS 8
 #endif
 bool wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs);
+// check_only: every host check, nothing enqueued (for a call that enqueues a
+// second launch after a first one and must fail before either).
 kvc_status_t launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,
-                         const void* v_new, int64_t new_stride_b, int64_t new_stride_h, const void* q,
-                         int32_t n_q_heads, int32_t t_q, float scale_log2, void* out, int32_t out_dtype,
-                         const WsRegions& ws, int32_t splits, int32_t* lens_next, uint32_t* dev_status,
-                         hipStream_t stream);
+                         const void* v_new, int64_t new_stride_b, int64_t new_stride_h, int64_t new_stride_t,
+                         const void* q, int32_t n_q_heads, int32_t t_q, float scale_log2, void* out,
+                         int32_t out_dtype, const WsRegions& ws, int32_t splits, int32_t* lens_next,
+                         uint32_t* dev_status, hipStream_t stream, bool check_only = false);
 
 // Bound on the polls of the decode split merge's wait for ready flags (about
 // 2^20 by default; kvc_debug_set_merge_spin_limit changes it for tests of the
@@ -149,12 +151,12 @@ kvc_status_t launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int3
 int32_t merge_spin_limit();
 
 // The matrix-core prefill kernel (kvc_prefill.hip): whether it is built for
-// this dtype and head dim, and its launch (arguments as kvc_prefill_attn,
-// already validated except for what the kernel itself needs).
+// this dtype and head dim, and its checks and launch (kvc_prefill_attn;
+// check_only as for launch_wide).
 bool prefill_supported(int32_t dtype, int32_t head_dim);
 kvc_status_t launch_prefill(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q, const void* q,
                             int32_t n_q_heads, float scale, void* out, int32_t out_dtype, uint32_t* dev_status,
-                            hipStream_t stream);
+                            hipStream_t stream, bool check_only = false);
 
 }  // namespace kvc
 

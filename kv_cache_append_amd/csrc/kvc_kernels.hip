@@ -1876,7 +1876,8 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
                            int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
                            size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status, hipStream_t stream,
                            int32_t t_q, const kvc::PageInfo* pg = nullptr, bool ring = false,
-                           int32_t* lens_next = nullptr, kvc::RegionsFn regions_fn = nullptr) {
+                           int32_t* lens_next = nullptr, kvc::RegionsFn regions_fn = nullptr,
+                           int64_t new_stride_t = 0, bool check_only = false) {
   kvc_status_t st = kvc::check_cache(cache, true);
   if (st != KVC_OK) return st;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
@@ -1904,6 +1905,11 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
     if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16 ||
         (new_stride_b * s) % 16 || (new_stride_h * s) % 16)
       return KVC_ERR_ALIGN;
+    if (t_q > 0) {                               // a fused fill: the block's rows, on the wide-group kernel only
+      if (new_stride_t < 0 || (t_q > 1 && new_stride_t < cache->head_dim)) return KVC_ERR_SHAPE;
+      if ((new_stride_t * s) % 16) return KVC_ERR_ALIGN;
+      if (pg != nullptr || ring || !kvc::routes_wide(cache, n_qv)) return KVC_ERR_UNSUPPORTED;
+    }
   }
   // The kernels address one (sequence, KV head) slice of K/V with 32-bit
   // byte offsets (plus up to two tiles past the end, read back as zeros).
@@ -1933,10 +1939,12 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   // the same (checked above); n_splits is then unused.
   if (t_q >= 8 && group * t_q >= 32 && pg == nullptr && !ring && k_new == nullptr &&
       kvc::prefill_supported(cache->dtype, cache->head_dim))
-    return kvc::launch_prefill(cache, seq_lens, t_q, q, n_q_heads, scale, out, out_dtype, dev_status, stream);
+    return kvc::launch_prefill(cache, seq_lens, t_q, q, n_q_heads, scale, out, out_dtype, dev_status, stream,
+                               check_only);
   if (wide)
-    return kvc::launch_wide(cache, seq_lens, n_pending, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, t_q,
-                            scale_log2, out, out_dtype, wr, splits, lens_next, dev_status, stream);
+    return kvc::launch_wide(cache, seq_lens, n_pending, k_new, v_new, new_stride_b, new_stride_h, new_stride_t, q,
+                            n_q_heads, t_q, scale_log2, out, out_dtype, wr, splits, lens_next, dev_status, stream,
+                            check_only);
   const int gb = kvc::heads_per_block(group * tq);
   DecodeParams p;
   p.k = static_cast<char*>(cache->k);
@@ -1982,6 +1990,7 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   p.merge_spins = kvc::merge_spin_limit();
   const int64_t wgs = decode_grid(static_cast<int64_t>(cache->batch) * cache->n_kv_heads, splits, p.n_hblk);
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
+  if (check_only) return KVC_OK;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(KVC_WAVES * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
@@ -2075,6 +2084,46 @@ extern "C" kvc_status_t kvc_block_attn(const kvc_cache_t* cache, const int32_t* 
                                        hipStream_t stream) {
   if (cache == nullptr) return KVC_ERR_NULL;
   if (t_q <= 0) return KVC_ERR_SHAPE;
+  return launch_decode(cache, seq_lens, 0, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype, workspace,
+                       workspace_bytes, n_splits, dev_status, stream, t_q);
+}
+
+extern "C" kvc_status_t kvc_block_step(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
+                                       const void* k_new, const void* v_new, int64_t new_stride_b,
+                                       int64_t new_stride_h, int64_t new_stride_t, const void* q, int32_t n_q_heads,
+                                       float scale, void* out, int32_t out_dtype, void* workspace,
+                                       size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status,
+                                       hipStream_t stream) {
+  if (cache == nullptr) return KVC_ERR_NULL;
+  if (t_q <= 0) return KVC_ERR_SHAPE;
+  kvc_status_t st = kvc::check_cache(cache, false);
+  if (st != KVC_OK) return st;
+  if (cache->batch > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_NULL;
+  if (new_stride_b < 0 || new_stride_h < 0 || new_stride_t < 0) return KVC_ERR_SHAPE;
+  if (t_q > 1 && new_stride_t < cache->head_dim) return KVC_ERR_SHAPE;
+  const int s = kvc::elem_bytes(cache->dtype);
+  if (reinterpret_cast<uintptr_t>(k_new) % s || reinterpret_cast<uintptr_t>(v_new) % s) return KVC_ERR_ALIGN;
+  // One launch where the wide-group kernel serves the block (it folds the
+  // block's rows in from k_new/v_new and writes them into the cache): 16-byte
+  // aligned rows, the rows within what its threads copy in one pass, and not
+  // a block long enough for the prefill kernel.
+  const bool gqa_ok = n_q_heads > 0 && n_q_heads % cache->n_kv_heads == 0;
+  const int64_t pairs = gqa_ok ? static_cast<int64_t>(n_q_heads / cache->n_kv_heads) * t_q : 0;
+  const bool prefill_route = t_q >= 8 && pairs >= 32 && kvc::prefill_supported(cache->dtype, cache->head_dim);
+  const bool aligned = reinterpret_cast<uintptr_t>(k_new) % 16 == 0 && reinterpret_cast<uintptr_t>(v_new) % 16 == 0 &&
+                       (new_stride_b * s) % 16 == 0 && (new_stride_h * s) % 16 == 0 && (new_stride_t * s) % 16 == 0;
+  if (gqa_ok && !prefill_route && aligned && kvc::routes_wide(cache, static_cast<int32_t>(n_q_heads * t_q)) &&
+      static_cast<int64_t>(t_q) * (cache->head_dim / 8) <= 512)
+    return launch_decode(cache, seq_lens, 0, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
+                         out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, t_q, nullptr, false,
+                         nullptr, nullptr, new_stride_t);
+  // Otherwise the fill, then the attention; the attention's checks run
+  // first, so that a call that fails enqueues nothing.
+  st = launch_decode(cache, seq_lens, 0, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype, workspace,
+                     workspace_bytes, n_splits, dev_status, stream, t_q, nullptr, false, nullptr, nullptr, 0, true);
+  if (st != KVC_OK || cache->batch == 0) return st;
+  st = launch_copy(cache, seq_lens, k_new, v_new, new_stride_b, new_stride_h, new_stride_t, t_q, dev_status, stream);
+  if (st != KVC_OK) return st;
   return launch_decode(cache, seq_lens, 0, nullptr, nullptr, 0, 0, q, n_q_heads, scale, out, out_dtype, workspace,
                        workspace_bytes, n_splits, dev_status, stream, t_q);
 }

@@ -356,13 +356,7 @@ bool kvc::prefill_supported(int32_t dtype, int32_t head_dim) { return pick_prefi
 
 kvc_status_t kvc::launch_prefill(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q, const void* q,
                                  int32_t n_q_heads, float scale, void* out, int32_t out_dtype, uint32_t* dev_status,
-                                 hipStream_t stream) {
-  return kvc_prefill_attn(cache, seq_lens, t_q, q, n_q_heads, scale, out, out_dtype, dev_status, stream);
-}
-
-extern "C" kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
-                                         const void* q, int32_t n_q_heads, float scale, void* out, int32_t out_dtype,
-                                         uint32_t* dev_status, hipStream_t stream) {
+                                 hipStream_t stream, bool check_only) {
   kvc_status_t st = kvc::check_cache(cache, true);
   if (st != KVC_OK) return st;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0) return KVC_ERR_GQA;
@@ -386,6 +380,7 @@ extern "C" kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t
   const bool xcd_major = units % 8 == 0;                // ids map to units XCD by XCD (see the kernel)
   const int64_t wgs = units * group * n_qt;
   if (wgs > 0x7fffffffll || static_cast<int64_t>(t_q) * n_q_heads > (1ll << 30)) return KVC_ERR_SHAPE;
+  if (check_only) return KVC_OK;                      // every check done, nothing enqueued
 
   PrefillParams p;
   p.k = static_cast<const char*>(cache->k);
@@ -409,4 +404,10 @@ extern "C" kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t
   p.scale_log2 = scale_log2;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+extern "C" kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t t_q,
+                                         const void* q, int32_t n_q_heads, float scale, void* out, int32_t out_dtype,
+                                         uint32_t* dev_status, hipStream_t stream) {
+  return kvc::launch_prefill(cache, seq_lens, t_q, q, n_q_heads, scale, out, out_dtype, dev_status, stream, false);
 }

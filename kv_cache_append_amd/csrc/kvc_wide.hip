@@ -68,9 +68,9 @@ struct WideParams {
   int64_t sb, sh, st;            // cache strides in bytes
   const int32_t* seq_lens;
   const char* q;                 // [B, t_q, H_q, D] (decode: t_q = 1)
-  const char* k_new;             // fused append source [B, H_kv, D] or null
+  const char* k_new;             // fused append source [B, H_kv, D] (a block: [B, H_kv, t_q, D]) or null
   const char* v_new;
-  int64_t nsb, nsh;              // its strides in bytes
+  int64_t nsb, nsh, nst;         // its strides in bytes (nst: between a block's rows)
   uint32_t* ws_flag;             // [B * H_kv * n_hblk, flag_stride]: this kernel uses head block 0's row
   uint32_t* ws_sync;             // [B * H_kv, kWideSyncWords]: arrival count and slice claims of the spread merge
   float* ws_o;                   // [B, H_kv * pairs, S, D]
@@ -206,12 +206,13 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   if (p.lens_next != nullptr && g == 0 && split == 0 && threadIdx.x == 0) p.lens_next[b] = c0 + 1;
   const int c = c0 < 0 ? 0 : c0;
   uint32_t dflags = c0 < 0 ? KVC_DEVERR_BADLEN : 0u;
-  const int add = p.k_new != nullptr ? 1 : (p.block ? p.t_q : p.n_pending);
+  const int add = p.block ? p.t_q : (p.k_new != nullptr ? 1 : p.n_pending);
   const int64_t n64 = static_cast<int64_t>(c) + add;
   int n, append_row = -1;
   if (p.block) {                                     // the whole block must fit
     if (c0 >= 0 && n64 > p.max_len) dflags |= KVC_DEVERR_CAPACITY;
     n = (c0 < 0 || n64 > p.max_len) ? 0 : static_cast<int>(n64);
+    if (p.k_new != nullptr && n > 0) append_row = c0;   // the fused fill writes slots c0 .. c0 + t_q - 1
   } else {
     if (p.k_new != nullptr) {
       if (c0 >= 0 && c0 < p.max_len) append_row = c0;
@@ -232,9 +233,14 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the query loads)
     return;
   }
-  // The T axis in equal whole tiles; decode folds the newest row (n - 1) in
-  // apart from the stream, in the last active split.
-  const int streamed = p.block ? n : n - 1;
+  // The T axis in equal whole tiles. The newest rows -- the newest one in
+  // decode, the block's own t_q rows for a block -- are folded in apart from
+  // the stream, as one more tile, by the last active split: then a fused
+  // append (or fill), whose rows come from k_new/v_new, and the separate
+  // calls, which read them from the cache, add the same rows in the same
+  // order.
+  const int xrows = p.block ? p.t_q : 1;
+  const int streamed = n - xrows;
   const int chunk = max(kWTile, ((streamed + p.n_splits - 1) / p.n_splits + kWTile - 1) & ~(kWTile - 1));
   const int ns = streamed > 0 ? min(p.n_splits, (streamed + chunk - 1) / chunk) : 1;
   if (split >= ns) {                                 // inactive split
@@ -244,22 +250,26 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const bool spread = ns >= kSpreadMin && ns <= kSpreadMax;   // how the splits merge (below)
   const int t0 = split * chunk;
   const int t_end = split == ns - 1 ? streamed : t0 + chunk;   // rows streamed from the cache: [t0, t_end)
-  const bool has_x = !p.block && split == ns - 1;
-  const bool x_new = has_x && append_row == n - 1;
+  const bool has_x = split == ns - 1;
+  const int xfirst = n - xrows;                      // the first folded row
+  const bool x_new = has_x && append_row == xfirst;
 
-  // The fused append: the newest row into its slot (no workgroup of this
-  // launch reads that slot from the cache). Its loads are issued first and
-  // its stores after the stream, so that waiting for the row holds nothing
-  // else back. Every lane runs them: those with nothing to
-  // copy see an empty buffer range (loads read zero, stores are dropped), as
-  // a load under a branch would make the compiler wait for every load issued
-  // before it.
-  const uint32_t arange = x_new && wave == 0 ? static_cast<uint32_t>(D * 2) : 0u;
+  // The fused append (or fill): the newest rows into their slots (no
+  // workgroup of this launch reads those slots from the cache). Their loads
+  // are issued first and their stores after the stream, so that waiting for
+  // them holds nothing else back: thread tid takes 16-byte chunk tid % CPR of
+  // row tid / CPR (the host keeps xrows * CPR within the workgroup). Every
+  // thread runs them: those with nothing to copy see an empty buffer range
+  // (loads read zero, stores are dropped), as a load under a branch would
+  // make the compiler wait for every load issued before it.
+  const int64_t nst = p.block ? p.nst : static_cast<int64_t>(D * 2);   // between the new rows
+  const uint32_t arange = x_new ? static_cast<uint32_t>((xrows - 1) * nst + D * 2) : 0u;
+  const uint32_t aoff_new = static_cast<uint32_t>((tid / CPR) * nst + (tid % CPR) * 16);
   const int64_t nrow = b * p.nsb + g * p.nsh;
   const __amdgpu_buffer_rsrc_t kn_rs = wrsrc(uniform_cptr(p.k_new != nullptr ? p.k_new + nrow : p.k), arange);
   const __amdgpu_buffer_rsrc_t vn_rs = wrsrc(uniform_cptr(p.v_new != nullptr ? p.v_new + nrow : p.v), arange);
-  const u32x4 kn_row = wload<0>(kn_rs, static_cast<uint32_t>(lane) * 16u);
-  const u32x4 vn_row = wload<0>(vn_rs, static_cast<uint32_t>(lane) * 16u);
+  const u32x4 kn_row = wload<0>(kn_rs, aoff_new);
+  const u32x4 vn_row = wload<0>(vn_rs, aoff_new);
 
   // Each pair's slot limit (lower-right causal mask of a query block).
   int plim[QB];
@@ -283,20 +293,21 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // (q / CPR, q % CPR), from the row's chunk q % CPR ^ tile_swz(row). Rows
   // past the streamed ones read as zeros (and are masked).
   const uint32_t smem_lds = KVC_LDS_ADDR(smem);
-  auto load_tile_from = [&](const u32x4& kr_, const u32x4& vr_, uint32_t base, int buf) {
+  auto load_tile_from = [&](const u32x4& kr_, const u32x4& vr_, uint32_t base, int buf, uint32_t rstride) {
     const uint32_t kb = smem_lds + buf * kBufBytes;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int m = wave * NL + i;
       const int q = m * 64 + lane;
       const int row = q / CPR;
-      const uint32_t off = base + static_cast<uint32_t>(row) * st + static_cast<uint32_t>((q % CPR) ^ tile_swz(row)) * 16u;
+      const uint32_t off =
+          base + static_cast<uint32_t>(row) * rstride + static_cast<uint32_t>((q % CPR) ^ tile_swz(row)) * 16u;
       lds_load16<true>(kr_, off, kb + m * 1024);
       lds_load16<true>(vr_, off, kb + TB + m * 1024);
     }
   };
   auto load_tile = [&](int t, int buf) {
-    load_tile_from(krs, vrs, static_cast<uint32_t>(t0 + t * kWTile) * st, buf);
+    load_tile_from(krs, vrs, static_cast<uint32_t>(t0 + t * kWTile) * st, buf, st);
   };
 
   // Per pair: the reference r (log2 domain) the weights are taken against,
@@ -437,26 +448,29 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   if (has_x) {
-    // The newest row as key 0 of one more tile: from k_new/v_new in the fused
-    // step, else from the cache; the other 63 keys read as zero (one-row
-    // range) and are masked.
-    const int xrow = n - 1;
-    const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xrow) * p.st;
-    const char* vx_ = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xrow) * p.st;
-    load_tile_from(rsrc_words(kx, D * 2), rsrc_words(vx_, D * 2), 0u, 0);
+    // The newest rows as keys 0 .. xrows - 1 of one more tile: from
+    // k_new/v_new in the fused step, else from the cache; the other keys read
+    // as zero (the range ends with the last row) and are masked.
+    const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xfirst) * p.st;
+    const char* vx_ = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xfirst) * p.st;
+    const uint32_t xstride = x_new ? static_cast<uint32_t>(nst) : st;
+    const uint32_t xrange = static_cast<uint32_t>(xrows - 1) * xstride + D * 2;
+    load_tile_from(rsrc_words(kx, xrange), rsrc_words(vx_, xrange), 0u, 0, xstride);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    compute(xrow, xrow + 1, 0);
+    compute(xfirst, n, 0);
   }
   {
-    // the fused append's stores (the row's loads were issued at entry)
+    // the fused append's stores (the rows' loads were issued at entry)
     const int64_t aoff = static_cast<int64_t>(append_row < 0 ? 0 : append_row) * p.st;
-    const __amdgpu_buffer_rsrc_t ka_rs = wrsrc(uniform_cptr(kunit + aoff), arange);
-    const __amdgpu_buffer_rsrc_t va_rs = wrsrc(uniform_cptr(vunit + aoff), arange);
+    const uint32_t crange = x_new ? static_cast<uint32_t>((xrows - 1) * st + D * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t ka_rs = wrsrc(uniform_cptr(kunit + aoff), crange);
+    const __amdgpu_buffer_rsrc_t va_rs = wrsrc(uniform_cptr(vunit + aoff), crange);
+    const int coff = static_cast<int>((tid / CPR) * st + (tid % CPR) * 16);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, kn_row),
-                                           ka_rs, static_cast<int>(lane * 16), 0, 0);
+                                           ka_rs, coff, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, vn_row),
-                                           va_rs, static_cast<int>(lane * 16), 0, 0);
+                                           va_rs, coff, 0, 0);
   }
 
   // Merge the two key halves of every column block: each wave of a pair
@@ -827,9 +841,10 @@ bool kvc::wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs) {
 
 kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
                               const void* k_new, const void* v_new, int64_t new_stride_b, int64_t new_stride_h,
-                              const void* q, int32_t n_q_heads, int32_t t_q, float scale_log2, void* out,
-                              int32_t out_dtype, const kvc::WsRegions& ws, int32_t splits, int32_t* lens_next,
-                              uint32_t* dev_status, hipStream_t stream) {
+                              int64_t new_stride_t, const void* q, int32_t n_q_heads, int32_t t_q,
+                              float scale_log2, void* out, int32_t out_dtype, const kvc::WsRegions& ws,
+                              int32_t splits, int32_t* lens_next, uint32_t* dev_status, hipStream_t stream,
+                              bool check_only) {
   // (arguments validated by the caller)
   const int s = kvc::elem_bytes(cache->dtype);
   const int32_t tq = t_q > 0 ? t_q : 1;
@@ -850,6 +865,11 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.v_new = static_cast<const char*>(v_new);
   p.nsb = new_stride_b * s;
   p.nsh = new_stride_h * s;
+  p.nst = new_stride_t * s;
+  // a block's rows are folded in as one tile, each thread loading one chunk
+  // of the rows a fused fill appends
+  if (t_q > 0 && (t_q > kWTile || (k_new != nullptr && t_q * (cache->head_dim / 8) > 512)))
+    return KVC_ERR_UNSUPPORTED;
   p.ws_flag = ws.flags;
   p.flag_stride = ws.flag_stride;
   p.ws_sync = ws.sync;
@@ -875,6 +895,7 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   const int64_t units = static_cast<int64_t>(cache->batch) * cache->n_kv_heads;
   const int64_t wgs = (units + 7) / 8 * 8 * splits;    // see the placement in the kernel
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
+  if (check_only) return KVC_OK;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(512), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }

@@ -235,6 +235,33 @@ def test_block_validation_and_workspace():
     assert lib.kvc_block_attn(ctypes.byref(c), FAKE, 3, FAKE, 4, 0.1, FAKE, 0, FAKE, need - 1, 0, None, None) == 6
 
 
+def test_block_step_validation_rejects_before_launch():
+    """kvc_block_step: the fill's and the attention's host checks, on both
+    of its routes (one fused launch for 16-byte aligned rows on the
+    wide-group kernel; otherwise fill, then attention, both checked before
+    either is enqueued). Every case fails before a launch."""
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    big = 1 << 30
+    odd = ctypes.c_void_p(4096 + 2)          # element-aligned, not 16-byte aligned: the two-launch route
+
+    def f(cache=ctypes.byref(c), t_q=4, kn=FAKE, vn=FAKE, sb=1024, sh=512, st=128, nq=4, scale=0.1, ws=big):
+        return lib.kvc_block_step(cache, FAKE, t_q, kn, vn, sb, sh, st, FAKE, nq, scale, FAKE, 0, FAKE, ws, 0,
+                                  None, None)
+
+    assert f(cache=None) == 1                                   # no cache
+    assert f(t_q=0) == 2                                        # t_q < 1
+    assert f(kn=None) == 1 and f(vn=None) == 1                  # no rows to append
+    assert f(sb=-1) == 2                                        # negative stride
+    assert f(st=64) == 2                                        # rows of a block overlap
+    assert f(kn=ctypes.c_void_p(4097)) == 4                     # not element-aligned
+    for kn in (FAKE, odd):                                      # both routes
+        assert f(kn=kn, nq=3) == 5                              # 3 query heads over 2 KV heads
+        assert f(kn=kn, scale=-1.0) == 7                        # scale must be positive
+        need = lib.kvc_block_workspace_bytes(ctypes.byref(c), 4, 4, 0)
+        assert f(kn=kn, ws=need - 1) == 6                       # workspace too small
+
+
 def test_prefill_validation_rejects_before_launch():
     """kvc_prefill_attn: every case below fails on the host before a launch."""
     kvc, lib = _lib()

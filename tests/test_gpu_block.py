@@ -91,12 +91,14 @@ def test_block_split_counts(gpu, n_splits):
     assert np.abs(_run(case, n_splits).double().cpu().numpy() - case.oracle()).max() <= TOL["fp16"]
 
 
-def test_block_of_one_equals_decode_bitwise(gpu):
-    case = BlockCase(batch=3, n_q=32, n_kv=8, d=128, dtype="bf16", lengths=[1, 333, 2047], t_q=1, tag="blk1")
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 2)])     # the decode kernel; the wide-group kernel
+def test_block_of_one_equals_decode_bitwise(gpu, hq, hkv):
+    case = BlockCase(batch=3, n_q=hq, n_kv=hkv, d=128, dtype="bf16", lengths=[1, 333, 2047], t_q=1,
+                     tag=f"blk1{hq}")
     case.fill()
     got = _run(case)
-    out = torch.empty((3, 32, 128), device=gpu)
-    ws = kvc.workspace(case.k, case.v, 32)
+    out = torch.empty((3, hq, 128), device=gpu)
+    ws = kvc.workspace(case.k, case.v, hq)
     kvc.decode_attn(case.k, case.v, case.seq_lens, case.q[:, 0].contiguous(), out, ws, n_pending=1)
     torch.cuda.synchronize()
     assert torch.equal(got[:, 0], out)
@@ -181,3 +183,99 @@ def test_verify_step_at_gqa_8b_shape_sampled(gpu):
     for b in (0, 7, 15):
         r = oracle.chunk_attention(case.q_host[b:b + 1], k[b:b + 1], v[b:b + 1], np.array([2048]))
         assert np.abs(got[b:b + 1].double().cpu().numpy() - r).max() <= TOL["bf16"]
+
+
+# kvc_block_step: the fill and the attention of a block in one call (one
+# launch where the wide-group kernel serves the block).
+@pytest.mark.parametrize("dtype,d,hq,hkv,t_q", [
+    ("bf16", 128, 32, 8, 4),      # 16 pairs: one fused launch (the 4-token verify at the 8B GQA shape)
+    ("bf16", 128, 32, 8, 2),      # 8 pairs: fused
+    ("fp16", 128, 16, 1, 5),      # MQA-like, 80 pairs: fused
+    ("bf16", 128, 1, 1, 20),      # 20 pairs, t_q = 20: fused (the block's rows fill most of a tile)
+    ("bf16", 64, 16, 2, 3),       # D = 64: fused
+    ("fp16", 128, 8, 8, 3),       # 3 pairs: fill, then the decode kernel
+    ("fp16", 128, 64, 1, 3),      # 192 pairs: fill, then the decode kernel
+    ("bf16", 128, 32, 8, 8),      # 32 pairs, t_q = 8: fill, then the prefill kernel
+    ("fp32", 128, 8, 2, 4),       # fp32 cache: fill, then the decode kernel
+])
+@pytest.mark.parametrize("n_splits", [0, 3])
+def test_block_step_equals_fill_then_attn(gpu, dtype, d, hq, hkv, t_q, n_splits):
+    """Cache bytes and output bits of kvc_block_step equal those of
+    kvc_prefill_fill + kvc_block_attn on the same inputs, on every route, and
+    the output is within the bar of the fp64 oracle."""
+    lens = [0, 37, 300, 1025]
+    tag = f"bstep{dtype}{d}{hq}{hkv}{t_q}"
+    a = BlockCase(batch=4, n_q=hq, n_kv=hkv, d=d, dtype=dtype, lengths=lens, t_q=t_q, tag=tag)
+    w = BlockCase(batch=4, n_q=hq, n_kv=hkv, d=d, dtype=dtype, lengths=lens, t_q=t_q, tag=tag)
+    out_a = torch.full(a.q.shape, float("nan"), device=gpu)
+    st_a = torch.zeros(1, dtype=torch.int32, device=gpu)
+    ws = kvc.block_workspace(a.k, a.v, hq, t_q, n_splits)
+    kvc.block_step(a.k, a.v, a.seq_lens, a.k_blk, a.v_blk, a.q, out_a, ws, n_splits=n_splits, status=st_a)
+    w.fill()
+    st_w = torch.zeros(1, dtype=torch.int32, device=gpu)
+    out_w = _run(w, n_splits=n_splits, status=st_w)
+    torch.cuda.synchronize()
+    assert int(st_a.item()) == 0 and int(st_w.item()) == 0
+    assert torch.equal(out_a, out_w)
+    iv = torch.int32 if dtype == "fp32" else torch.int16
+    assert torch.equal(a.k.view(iv), w.k.view(iv)) and torch.equal(a.v.view(iv), w.v.view(iv))
+    assert np.abs(out_a.double().cpu().numpy() - a.oracle()).max() <= TOL[dtype]
+
+
+def test_block_step_repeated_with_a_strided_source(gpu):
+    """Three verify blocks in a row through kvc_block_step (the lengths moved
+    by the block each time), the block's rows taken from a token-major
+    [B, t_q, H_kv, D] buffer through strides, against the oracle over the
+    cache the steps built."""
+    b_, hq, hkv, d, t_q = 3, 32, 4, 128, 4
+    case = BlockCase(batch=b_, n_q=hq, n_kv=hkv, d=d, dtype="bf16", lengths=[5, 190, 700], t_q=t_q,
+                     t_max=720, tag="bstep_seq")
+    k_ref, v_ref = case.k_host.clone(), case.v_host.clone()
+    lens = case.lengths.clone()
+    ws = kvc.block_workspace(case.k, case.v, hq, t_q, 0)
+    for step in range(3):
+        kb = synth.normal((b_, t_q, hkv, d), "bf16", 11, "bstep_seq", step, "k", device=gpu)
+        vb = synth.normal((b_, t_q, hkv, d), "bf16", 11, "bstep_seq", step, "v", device=gpu)
+        q = synth.normal((b_, t_q, hq, d), "bf16", 11, "bstep_seq", step, "q", device=gpu)
+        out = torch.empty((b_, t_q, hq, d), device=gpu)
+        status = torch.zeros(1, dtype=torch.int32, device=gpu)
+        kvc.block_step(case.k, case.v, case.seq_lens, kb.transpose(1, 2), vb.transpose(1, 2), q, out, ws,
+                       status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        for bb in range(b_):
+            n = int(lens[bb])
+            k_ref[bb, :, n:n + t_q] = kb[bb].transpose(0, 1).cpu()
+            v_ref[bb, :, n:n + t_q] = vb[bb].transpose(0, 1).cpu()
+        ref = oracle.chunk_attention(q.cpu(), k_ref, v_ref, lens.numpy())
+        assert np.abs(out.double().cpu().numpy() - ref).max() <= TOL["bf16"]
+        lens += t_q
+        kvc.seq_lens_advance(case.seq_lens, t_q)
+    got_k = case.k.cpu()
+    for bb in range(b_):
+        n = int(lens[bb])
+        assert torch.equal(got_k[bb, :, :n].view(torch.int16), k_ref[bb, :, :n].view(torch.int16))
+
+
+@pytest.mark.parametrize("hq", [32, 2])     # one fused launch (80 pairs); fill then attention (5 pairs)
+def test_block_step_that_does_not_fit_or_has_a_negative_length(gpu, hq):
+    """A block past max_len is not written and gets zero rows (capacity flag);
+    a negative length gets zero rows (bad-length flag); the other sequences
+    are exact, as with the separate calls."""
+    case = BlockCase(batch=3, n_q=hq, n_kv=2, d=128, dtype="bf16", lengths=[10, 60, 20], t_q=5, t_max=64,
+                     tag=f"bstepfit{hq}")
+    case.seq_lens[2] = -4
+    out = torch.empty(case.q.shape, device=gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    ws = kvc.block_workspace(case.k, case.v, hq, 5, 0)
+    kvc.block_step(case.k, case.v, case.seq_lens, case.k_blk, case.v_blk, case.q, out, ws, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & kvc.DEVERR_CAPACITY and int(status.item()) & kvc.DEVERR_BADLEN
+    assert torch.count_nonzero(out[1]) == 0 and torch.count_nonzero(out[2]) == 0
+    k = case.k.cpu()
+    assert torch.isnan(k[1, :, 60:].float()).all()           # not written
+    kr, vr = case.k_host.clone(), case.v_host.clone()
+    kr[0, :, 10:15], vr[0, :, 10:15] = case.kb_host[0], case.vb_host[0]
+    r = oracle.chunk_attention(case.q_host[:1], kr[:1], vr[:1], np.array([10]))
+    assert np.abs(out[:1].double().cpu().numpy() - r).max() <= TOL["bf16"]
+
