@@ -397,6 +397,44 @@ def _measure(w: Workload, steps: int, warmup: int, use_graph: bool):
     return ms_total, wall, avg_launch_ms, avg_launch_bytes, step_ms
 
 
+def _split_read_ms(w: Workload, use_graph: bool, reps: int = 10):
+    """Average duration in ms of one kvc_split_read launch -- the decode
+    launch's workgroups, K/V loads and split exchange without the attention's
+    arithmetic -- over the L layers' caches with the step's split count and
+    the lengths the per-launch pass held, back to back (one HIP graph of the
+    L launches), bracketed by HIP events on the launching stream."""
+    import torch
+    import kv_cache_append_amd as kvc
+    cfg, lib, vp = w.cfg, w.lib, ctypes.c_void_p
+    units = cfg.batch * cfg.n_kv_heads
+    out = torch.empty(units * 2048, dtype=torch.uint8, device=w.k.device)
+    ws = kvc.split_read_workspace(w.k[0], w.v[0], w.splits)
+    seq = vp(w.seq_lens.data_ptr())
+
+    def run(h):
+        for l in range(cfg.n_layers):
+            if lib.kvc_split_read(ctypes.byref(w.descs[l]), seq, w.splits, vp(out.data_ptr()), vp(ws.data_ptr()),
+                                  ws.numel(), vp(h)):
+                raise RuntimeError("kvc_split_read failed")
+
+    stream = torch.cuda.current_stream()
+    g = None
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    (g.replay() if g is not None else run(stream.cuda_stream))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        (g.replay() if g is not None else run(stream.cuda_stream))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * cfg.n_layers)
+
+
 def _kernel_fingerprint(kernel: str) -> str:
     """SHA-256 of the kernel's sources with comments and whitespace removed,
     so that counter records stay tied to the code and not to its comments."""
@@ -562,6 +600,10 @@ def _run_config(name, args, with_cpu):
     import kv_cache_append_amd as kvc
     launch_read = (kvc.stream_read_launch_rate(int(launch_bytes) // 16 * 16, n_bytes=args.stream_gib << 30)
                    if args.stream_gib > 0 else None)
+    # the same launches' loads and split exchange without the arithmetic
+    # (contiguous caches, the decode step)
+    split_read_ms = (None if (args.block_q or args.paged or args.ring or args.quant or args.layout != "bhtd")
+                     else _split_read_ms(w, not args.no_graph))
     torch.cuda.synchronize()
     status = int(w.status.item())          # KVC_DEVERR_* bits of every call of the run (0 expected)
     step_sorted = sorted(step_ms)
@@ -614,6 +656,8 @@ def _run_config(name, args, with_cpu):
             "launch_ms": round(launch_ms, 5), "launch_bytes": int(launch_bytes),
             **({"stream_read_gbs": round(args.stream_gbs, 1), "frac_of_stream": round(achieved / args.stream_gbs, 4)}
                if args.stream_gbs else {}),
+            **({"split_read_us": round(split_read_ms * 1e3, 2),
+                "frac_of_split_read": round(split_read_ms / launch_ms, 4)} if split_read_ms is not None else {}),
             **({"launch_read_gbs": round(launch_read, 1), "frac_of_launch_read": round(achieved / launch_read, 4)}
                if launch_read else {}),
             # counters are taken for the default mode (16-bit contiguous cache)

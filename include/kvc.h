@@ -619,6 +619,33 @@ size_t kvc_stream_read_sink_bytes(int32_t n_workgroups);
 kvc_status_t kvc_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
                              hipStream_t stream);
 
+/*
+ * kvc_split_read -- a measurement aid, not part of the decode path: the data
+ * movement of a decode launch on this cache without its arithmetic. It runs
+ * the workgroups of a decode call with n_splits splits (one per (sequence,
+ * KV head) unit and split, a unit's splits on one XCD), reads the K and V
+ * rows [0, seq_lens[b] + 1) of every unit once with the decode kernel's
+ * 16-byte non-temporal loads of 16-row tiles, merges its four waves through
+ * LDS, and exchanges the splits' partial results as decode does (the other
+ * splits publish 2 KB and raise an epoch flag; the last split waits, folds
+ * and writes). Every loaded 16-byte word is XOR-folded into the unit's 2 KB
+ * of out ([units][128] 16-byte words, device), so no load is dropped and the
+ * XOR of a unit's words is the XOR of every word of its rows. Timed beside
+ * the decode launch, it separates the cost of the stream and the split
+ * exchange, which any split decode pays, from that of the attention's
+ * arithmetic (textbook "11.7 KV Cache" §4.4, course notes §1.5).
+ *
+ *   cache     fp32/fp16/bf16, head_dim * elem_bytes of 64, 128, 256 or 512
+ *             bytes (else KVC_ERR_UNSUPPORTED); 16-byte aligned rows.
+ *   workspace kvc_split_read_workspace_bytes(cache, n_splits) bytes, 256-byte
+ *             aligned, zero-filled once after allocation (epoch flags, as
+ *             for kvc_decode_workspace_bytes; one workspace per geometry).
+ *   n_splits  1..KVC_MAX_SPLITS.
+ */
+size_t kvc_split_read_workspace_bytes(const kvc_cache_t* cache, int32_t n_splits);
+kvc_status_t kvc_split_read(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_splits, void* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* kvc_status_str -- static, human-readable name of a status code. */
 const char* kvc_status_str(kvc_status_t status);
 

@@ -43,7 +43,7 @@ EXPORTS = ("kvc_append", "kvc_prefill_fill", "kvc_decode_workspace_bytes", "kvc_
            "kvc_quant_append", "kvc_quant_prefill_fill", "kvc_quant_decode_workspace_bytes",
            "kvc_quant_decode_attn", "kvc_quant_decode_step",
            "kvc_seq_lens_advance", "kvc_cache_bytes", "kvc_status_str", "kvc_stream_read_sink_bytes",
-           "kvc_stream_read", "kvc_debug_set_merge_spin_limit")
+           "kvc_stream_read", "kvc_split_read_workspace_bytes", "kvc_split_read", "kvc_debug_set_merge_spin_limit")
 
 
 class KvcError(RuntimeError):
@@ -132,6 +132,10 @@ def load() -> ctypes.CDLL:
     lib.kvc_stream_read_sink_bytes.restype = sz
     lib.kvc_stream_read.argtypes = [vp, sz, vp, i32, vp]
     lib.kvc_stream_read.restype = i32
+    lib.kvc_split_read_workspace_bytes.argtypes = [cp, i32]
+    lib.kvc_split_read_workspace_bytes.restype = sz
+    lib.kvc_split_read.argtypes = [cp, vp, i32, vp, vp, sz, vp]
+    lib.kvc_split_read.restype = i32
     lib.kvc_seq_lens_advance.argtypes = [vp, i32, i32, vp]
     lib.kvc_seq_lens_advance.restype = i32
     lib.kvc_cache_bytes.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), i32]
@@ -582,6 +586,26 @@ def quant_decode_step(qc: QCacheDesc, seq_lens, k_new, v_new, q, out, workspace,
                                         _ptr(out), DTYPE_CODE[out.dtype], _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), n_splits, _ptr(status),
                                         _stream(stream)), "kvc_quant_decode_step")
+
+
+def split_read_workspace(k_cache, v_cache, n_splits: int, desc=None) -> torch.Tensor:
+    """Zero-filled workspace for kvc_split_read (one per geometry)."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    n = int(lib.kvc_split_read_workspace_bytes(ctypes.byref(c), n_splits))
+    if n == 0:
+        raise KvcError(2, "kvc_split_read_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=k_cache.device if k_cache is not None else "cuda")
+
+
+def split_read(k_cache, v_cache, seq_lens, n_splits: int, out, workspace, stream=None, desc=None):
+    """kvc_split_read: the decode launch's loads and split exchange without
+    its arithmetic; out is [units, 128] 16-byte words (2 KB per (sequence, KV
+    head) unit), the XOR fold of every word the unit's rows hold."""
+    lib = load()
+    c = desc if desc is not None else cache_desc(k_cache, v_cache)
+    _check(lib.kvc_split_read(ctypes.byref(c), _ptr(seq_lens), n_splits, _ptr(out), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)), "kvc_split_read")
 
 
 def stream_read_rate(n_bytes: int = 4 << 30, grids=(512, 2048, 8192), reps: int = 5, device="cuda") -> float:

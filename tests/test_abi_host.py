@@ -262,6 +262,28 @@ def test_block_step_validation_rejects_before_launch():
         assert f(kn=kn, ws=need - 1) == 6                       # workspace too small
 
 
+def test_split_read_validation_and_workspace():
+    """kvc_split_read (the decode launch's loads and split exchange, no
+    arithmetic): host checks fail before a launch; the workspace holds the
+    flags (256-byte aligned) and 2 KB per (unit, split)."""
+    kvc, lib = _lib()
+    c = _desc(kvc)
+    ws = lib.kvc_split_read_workspace_bytes(ctypes.byref(c), 3)
+    assert ws == 256 + 4 * 3 * 2048                            # 2 x 2 units, 3 splits
+    assert lib.kvc_split_read_workspace_bytes(ctypes.byref(c), 0) == 0
+    assert lib.kvc_split_read_workspace_bytes(ctypes.byref(c), 257) == 0
+    big = 1 << 30
+    f = lambda cc, splits=3, out=FAKE, wsp=FAKE, n=big: lib.kvc_split_read(cc, FAKE, splits, out, wsp, n, None)
+    assert f(None) == 1 and f(ctypes.byref(c), out=None) == 1
+    assert f(ctypes.byref(c), splits=0) == 2
+    assert f(ctypes.byref(c), n=ws - 1) == 6
+    assert f(ctypes.byref(c), wsp=ctypes.c_void_p(4096 + 16)) == 4     # workspace not 256-byte aligned
+    small = _desc(kvc, head_dim=8, stride_b=2 * 16 * 8, stride_h=16 * 8, stride_t=8)   # 16-byte rows
+    assert f(ctypes.byref(small)) == 7
+    bad = _desc(kvc, dtype=9)
+    assert f(ctypes.byref(bad)) == 3
+
+
 def test_prefill_validation_rejects_before_launch():
     """kvc_prefill_attn: every case below fails on the host before a launch."""
     kvc, lib = _lib()

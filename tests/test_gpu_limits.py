@@ -106,3 +106,36 @@ def test_stream_read_launch_rate_is_finite(gpu):
     assert np.isfinite(rate) and rate > 0
     with pytest.raises(ValueError):
         kvc.stream_read_launch_rate(1000)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64), ("fp16", 256), ("bf16", 32)])
+def test_split_read_reads_every_row_once(gpu, dtype, d):
+    """kvc_split_read (the decode launch's loads and split exchange without
+    its arithmetic): for every (sequence, KV head) unit, the XOR of its 128
+    output words equals the host's XOR of every 16-byte word of its K and V
+    rows [0, seq_lens[b] + 1), for 1, 2 and 7 splits and on a second call on
+    the same workspace (the flags' epochs), so each row is read once and
+    every partial is folded in once."""
+    tdt = synth.DTYPES[dtype]
+    b_, hkv, t_max = 5, 3, 2100
+    lens = [0, 1, 17, 300, 2048]
+    raw = torch.randint(-(1 << 15), 1 << 15, (2, b_, hkv, t_max, d * tdt.itemsize // 2), dtype=torch.int16,
+                        device=gpu)
+    k, v = raw[0].view(tdt), raw[1].view(tdt)
+    seq = torch.tensor(lens, dtype=torch.int32, device=gpu)
+    kh = k.cpu().view(torch.int16).numpy().view(np.uint32)
+    vh = v.cpu().view(torch.int16).numpy().view(np.uint32)
+    want = np.zeros((b_ * hkv, 4), dtype=np.uint32)
+    for bb in range(b_):
+        n = min(lens[bb] + 1, t_max)
+        for g in range(hkv):
+            words = np.concatenate([kh[bb, g, :n].reshape(-1, 4), vh[bb, g, :n].reshape(-1, 4)])
+            want[bb * hkv + g] = np.bitwise_xor.reduce(words, axis=0)
+    for splits in (1, 2, 7):
+        ws = kvc.split_read_workspace(k, v, splits)
+        for rep in range(2):
+            out = torch.full((b_ * hkv, 128, 4), -1, dtype=torch.int32, device=gpu)
+            kvc.split_read(k, v, seq, splits, out, ws)
+            torch.cuda.synchronize()
+            got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32), axis=1)
+            assert np.array_equal(got, want), (splits, rep)
