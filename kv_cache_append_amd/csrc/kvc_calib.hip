@@ -121,17 +121,18 @@ __global__ __launch_bounds__(kThreads, 2) void split_read_kernel(const SplitRead
       vv[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, static_cast<int>(voff), 0, kStream));
     }
   };
-  u32x4 ka[NPL], va[NPL], kb[NPL], vb[NPL];
-  load(0, ka, va);                                      // (no tile: reads zeros)
-  for (int t = 0; t < n_tiles; t += 2) {           // one tile ahead; its loads leave before any wait
-    load(t + 1, kb, vb);
-    __builtin_amdgcn_sched_barrier(0);
+  // a ring of two tile buffers, as the decode kernel keeps: tile t + 1's
+  // loads leave before the wait for tile t (tiles past the last read zeros)
+  u32x4 kbuf[2][NPL], vbuf[2][NPL];
+  load(0, kbuf[0], vbuf[0]);
+  for (int it = 0; it < n_tiles; it += 2) {
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) acc ^= ka[m] ^ va[m];
-    load(t + 2, ka, va);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int r = 0; r < 2; ++r) {
+      load(it + r + 1, kbuf[r ^ 1], vbuf[r ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) acc ^= kb[m] ^ vb[m];   // (zeros past the last tile)
+      for (int m = 0; m < NPL; ++m) acc ^= kbuf[r][m] ^ vbuf[r][m];
+    }
   }
   // the waves' merge through LDS; the first 64 words of the partial hold it
   sm[wave][lane] = acc;
