@@ -73,7 +73,7 @@ struct WideParams {
   int64_t nsb, nsh, nst;         // its strides in bytes (nst: between a block's rows)
   uint32_t* ws_flag;             // [B * H_kv * n_hblk, flag_stride]: this kernel uses head block 0's row
   uint32_t* ws_sync;             // [B * H_kv, kWideSyncWords]: arrival count and slice claims of the spread merge
-  float* ws_o;                   // [B, H_kv * pairs, S, D]
+  float* ws_o;                   // per unit [S][D / 16][pairs][16]: see pofs in the kernel
   float* ws_ml;                  // [B, H_kv * pairs, S, 2]
   void* out;                     // like q; fp32 or the cache dtype
   uint32_t* status;
@@ -567,9 +567,8 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // advances the unit's epoch. It has the highest workgroup id of its unit
   // on the XCD, and a publishing workgroup never waits, so every awaited
   // workgroup is dispatched and finishes; the wait is bounded all the same.
-  // Partial rows of this unit: [split][pair] (rows of D floats, and (reference,
-  // sum) pairs), so that one split's pairs are adjacent: a wave's 16 pairs are
-  // 16 consecutive rows, spread over the L2 channels.
+  // This unit's exchange: gv * S * D partial output floats (in the order
+  // pofs gives below) and (reference, sum) pairs [split][pair].
   const int64_t ubase = static_cast<int64_t>(unit) * p.n_splits * gv;
   const __amdgpu_buffer_rsrc_t ors = wrsrc(p.ws_o + ubase * D, static_cast<uint32_t>(gv) * p.n_splits * D * 4u);
   const __amdgpu_buffer_rsrc_t mrs = wrsrc(p.ws_ml + ubase * 2, static_cast<uint32_t>(gv) * p.n_splits * 8u);
@@ -577,8 +576,16 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // first use of the epoch: its load (issued with the first tiles) is waited for here,
   // not in front of the stream
   asm volatile("" : "+v"(epoch));
-  // This split's partial into its rows of the exchange, complete in L2 when
-  // the function returns.
+  // Partial outputs of the unit in the registers' order: split k, output
+  // block db (16 elements), pair v, 4-element group g4 at 16-byte word
+  // ((k ND + db) gv + v) 4 + g4, so one store of a wave (16 pairs x 4
+  // groups of one block) covers 1 KB of whole cache lines (a store of half a
+  // line would have the cache fetch the other half from memory first).
+  auto pofs = [&](int k, int db, int v, int g4) {
+    return static_cast<uint32_t>((((k * ND + db) * gv + v) * 4 + g4) * 16);
+  };
+  // This split's partial into the exchange, complete in L2 when the function
+  // returns.
   auto publish = [&]() {
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
@@ -587,7 +594,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       const uint32_t row = static_cast<uint32_t>(split * gv + v);
 #pragma unroll
       for (int h = 0; h < NDH; ++h)
-        wstore(ors, (row * D + 16 * (NDH * kh + h) + 4 * grp) * 4u,
+        wstore(ors, pofs(split, NDH * kh + h, v, grp),
                u32x4{__float_as_uint(oh[j][h][0]), __float_as_uint(oh[j][h][1]), __float_as_uint(oh[j][h][2]),
                      __float_as_uint(oh[j][h][3])});
       if (kh == 0 && grp == 0) {
@@ -636,14 +643,14 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     __syncthreads();
     const uint32_t state = ss[0];
     // Slice k: items [k I / ns, (k + 1) I / ns) of the I = pairs * D / 4, each
-    // a pair's 4 consecutive elements; the splits folded in split order, as
-    // in the last-split merge, with loads of whole rows per wave. With claim,
+    // a pair's 4 consecutive elements, in the exchange's order (block, pair,
+    // group), so a wave's loads cover whole lines; the splits folded in split
+    // order, as in the last-split merge. With claim,
     // the slice is claimed first, and the loads of each thread's first item
     // are issued while the claim's answer is on its way.
     auto merge_slice = [&](int k, bool claim) {
-      constexpr int C4 = D / 4;
       constexpr int R = 8;
-      const int items = gv * C4;
+      const int items = gv * (D / 4);                  // item: (block db, pair v, group g4), the exchange's order
       const int i1 = (k + 1) * items / ns;
       uint32_t old = 0u;
       if (claim && tid == 0) old = __hip_atomic_fetch_max(claims + k, epoch + 1u, __ATOMIC_RELAXED, kSyncScope);
@@ -652,13 +659,13 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       // one round: splits k0 .. k0 + R - 1 of item it (rows past the region,
       // or no item at all, read as zero)
       auto load_round = [&](int it, int k0) {
-        const int v = it / C4;
+        const int db = it / (gv * 4), v = (it - db * gv * 4) >> 2, g4 = it & 3;
         const bool any = it < i1;
 #pragma unroll
         for (int kk = 0; kk < R; ++kk) {
           const uint32_t row = static_cast<uint32_t>((k0 + kk) * gv + v);
           const uint32_t mo = any ? row * 8u : 0x80000000u;
-          const uint32_t oo = any ? (row * D + 4 * (it - v * C4)) * 4u : 0x80000000u;
+          const uint32_t oo = any ? pofs(k0 + kk, db, v, g4) : 0x80000000u;
           mlb[kk] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(mrs, static_cast<int>(mo), 0, kXchgW));
           ob[kk] = wload<kXchgW>(ors, oo);
         }
@@ -671,7 +678,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
         if (!ss[1]) return;                   // uniform: another workgroup merges this slice
       }
       for (bool pre = true; it < i1; it += NT, pre = false) {
-        const int v = it / C4;
+        const int db = it / (gv * 4), v = (it - db * gv * 4) >> 2, g4 = it & 3;
         float mm = -INFINITY, ll = 0.f;
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < ns; k0 += R) {
@@ -693,7 +700,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
         f32x4 y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = acc[i] * inv;
-        store4(wpair_row(p, b, g, v) * D + 4 * (it - v * C4), y);
+        store4(wpair_row(p, b, g, v) * D + 16 * db + 4 * g4, y);
       }
     };
     if (state != 0u) merge_slice(split, true);
@@ -783,7 +790,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
         lb[kk] = __uint_as_float(static_cast<uint32_t>(
             __builtin_amdgcn_raw_buffer_load_b32(mrs, static_cast<int>(row * 8u + 4u), 0, kXchgW)));
 #pragma unroll
-        for (int h = 0; h < NDH; ++h) ob[kk][h] = wload<kXchgW>(ors, (row * D + 16 * (NDH * kh + h) + 4 * grp) * 4u);
+        for (int h = 0; h < NDH; ++h) ob[kk][h] = wload<kXchgW>(ors, pofs(k0 + kk, NDH * kh + h, vrow, grp));
       }
 #pragma unroll
       for (int kk = 0; kk < R; ++kk) {
