@@ -262,32 +262,41 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         plo[qb][kc] = u32x4{lo[0], lo[1], lo[2], lo[3]};
       }
     }
+    // V^T operands k = 2 db + kc: rows 16 db + r16, keys 32 kc + 4 grp .. + 3
+    // and 32 kc + 16 + 4 grp .. + 3 (the slots of the weights' lane layout),
+    // two transposing reads each, requested kVAhead operands ahead of their
+    // products. Each operand's four products take the high parts of both
+    // query blocks, then the low parts (no product waits on the one before).
+    constexpr int NV = 2 * ND;
+    constexpr int kVAhead = 2;
+    auto read_v = [&](int k) -> u32x4 {
+      const char* const vp = sv + 32 * (k & 1) * RB + voff + ((2 * (k >> 1)) ^ vx) * 16;
+      const u32x2 lo4 = lds_read_tr(vp), hi4 = lds_read_tr(vp + 16 * RB);
+      return u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+    };
+    u32x4 va[kVAhead + 1];
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+    for (int k = 0; k < kVAhead; ++k) va[k] = read_v(k);
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        // V^T rows 16 db + r16, keys 32 kc + 4 grp .. + 3 and 32 kc + 16 + 4 grp .. + 3
-        // (the slots of the weights' lane layout)
-        const char* const vp = sv + 32 * kc * RB + voff + ((2 * db) ^ vx) * 16;
-        const u32x2 lo4 = lds_read_tr(vp), hi4 = lds_read_tr(vp + 16 * RB);
-        const u32x4 a = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+    for (int k = 0; k < NV; ++k) {
+      if (k + kVAhead < NV) va[(k + kVAhead) % (kVAhead + 1)] = read_v(k + kVAhead);
+      const u32x4 a = va[k % (kVAhead + 1)];
+      const int db = k >> 1, kc = k & 1;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          o[qb][db] = ET::mfma(a, phi[qb][kc], o[qb][db]);
-          o[qb][db] = ET::mfma(a, plo[qb][kc], o[qb][db]);
-        }
-      }
-    // issue order: two V^T slice reads ahead, then (one read, four products);
-    // measured 1-5 % faster at D = 128 and 1.5 % slower at D = 64, so D = 128 only
-    if constexpr (D == 128) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int qb = 0; qb < 2; ++qb) o[qb][db] = ET::mfma(a, phi[qb][kc], o[qb][db]);
 #pragma unroll
-      for (int k = 0; k < 2 * ND - 2; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      for (int qb = 0; qb < 2; ++qb) o[qb][db] = ET::mfma(a, plo[qb][kc], o[qb][db]);
     }
+    // issue order: the first kVAhead operands' reads, then (the reads of
+    // operand k + kVAhead, the four products of operand k); with the
+    // compiler's own order the products of each operand waited for its reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
+#pragma unroll
+    for (int k = 0; k < NV - kVAhead; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * kVAhead, 0);
   };
 
   // Tiles below t_split hold no key past any query's limit; the others are
