@@ -312,13 +312,13 @@ kvc_status_t kvc_decode_step_noalloc(const kvc_cache_t* cache, const int32_t* se
  *
  * The (query, head) pairs of a KV head are processed like the query heads of
  * a larger group, so K/V rows are streamed once per block of up to 8 pairs,
- * or, on fp16/bf16 caches with head_dim 64 or 128 and 8..128 pairs per KV
- * head, once for all of them (the wide-group kernel, as for decode with 8+
- * query heads per KV head); this suits short blocks (verify steps, small
- * chunks). Blocks of t_q >= 8
- * with t_q * (n_q_heads / n_kv_heads) >= 32 on fp16/bf16 caches with head_dim
- * 64 or 128 run on the kernel of kvc_prefill_attn instead (the same result
- * bits as that call; n_splits is then unused, the workspace rules stand). A sequence whose
+ * or, on fp16/bf16 caches with head_dim 64 or 128, 8..128 pairs per KV head
+ * and t_q <= 64, once for all of them (the wide-group kernel, as for decode
+ * with 8+ query heads per KV head); this suits verify steps and chunks of up
+ * to 64 tokens. Other blocks of t_q >= 8 with t_q * (n_q_heads / n_kv_heads)
+ * >= 32 on fp16/bf16 caches with head_dim 64 or 128 run on the kernel of
+ * kvc_prefill_attn (the same result bits as that call; n_splits is then
+ * unused, the workspace rules stand). A sequence whose
  * block does not fit (seq_lens[b] < 0, or seq_lens[b] + t_q > max_len) gets
  * zero rows and KVC_DEVERR_BADLEN / KVC_DEVERR_CAPACITY. Host-side errors as
  * for kvc_decode_attn, and KVC_ERR_SHAPE for t_q < 1.
@@ -351,8 +351,8 @@ size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, in
  *             kvc_block_workspace_bytes); seq_lens is only read.
  *
  * Where the block runs on the wide-group kernel (fp16/bf16, head_dim 64 or
- * 128, 8..128 (query, head) pairs per KV head, not a prefill-kernel block)
- * and k_new/v_new rows are 16-byte aligned, this is one launch: the kernel
+ * 128, 8..128 (query, head) pairs per KV head), t_q * head_dim <= 4096 and
+ * k_new/v_new rows are 16-byte aligned, this is one launch: the kernel
  * folds the block's rows in from k_new/v_new and writes them into the cache
  * (no workgroup reads those slots from the cache). Otherwise it enqueues the
  * fill, then the attention. A block that does not fit (seq_lens[b] < 0 or

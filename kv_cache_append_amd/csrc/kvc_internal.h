@@ -137,6 +137,9 @@ kvc_cache_t qcache_view(const kvc_qcache_t* c);
 #define KVC_WIDE_MIN_PAIRS 8
 #endif
 bool wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs);
+// The longest block of queries the wide-group kernel takes: the block's
+// rows are folded in as one LDS tile of keys.
+constexpr int kWideMaxBlock = 64;
 // check_only: every host check, nothing enqueued (for a call that enqueues a
 // second launch after a first one and must fail before either).
 kvc_status_t launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,

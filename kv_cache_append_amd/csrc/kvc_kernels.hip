@@ -1932,13 +1932,16 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
 
   const int group = n_q_heads / cache->n_kv_heads;
   // A block of 8 or more queries with at least 32 (query, head) pairs per KV
-  // head goes to the matrix-core prefill kernel, which reads each head's K/V
-  // once for all its queries: at the gqa_8b shape (2048 cached tokens) it is
-  // faster from 8 queries on (68 against 82 us per layer), while 8-pair
-  // blocks here re-stream the K/V once per block. The workspace contract stays
-  // the same (checked above); n_splits is then unused.
-  if (t_q >= 8 && group * t_q >= 32 && pg == nullptr && !ring && k_new == nullptr &&
-      kvc::prefill_supported(cache->dtype, cache->head_dim))
+  // head that the wide-group kernel does not take (more than 128 pairs, or
+  // more than kWideMaxBlock queries) goes to the matrix-core prefill kernel,
+  // which reads each query head's K/V once for all its queries; within the
+  // wide kernel's range that kernel is faster (it reads each KV head's K/V
+  // once for all pairs: gqa_8b verify blocks of 8, 16 and 32 queries 1.8x,
+  // 1.6x and 1.2x, mha_7b blocks of 32 and 64 queries 4.7x and 3.8x), and
+  // below 32 pairs the decode kernels are. The workspace contract stays the
+  // same (checked above); n_splits is then unused.
+  if (t_q >= 8 && group * t_q >= 32 && !(wide && t_q <= kvc::kWideMaxBlock) && pg == nullptr && !ring &&
+      k_new == nullptr && kvc::prefill_supported(cache->dtype, cache->head_dim))
     return kvc::launch_prefill(cache, seq_lens, t_q, q, n_q_heads, scale, out, out_dtype, dev_status, stream,
                                check_only);
   if (wide)
@@ -2105,14 +2108,11 @@ extern "C" kvc_status_t kvc_block_step(const kvc_cache_t* cache, const int32_t* 
   if (reinterpret_cast<uintptr_t>(k_new) % s || reinterpret_cast<uintptr_t>(v_new) % s) return KVC_ERR_ALIGN;
   // One launch where the wide-group kernel serves the block (it folds the
   // block's rows in from k_new/v_new and writes them into the cache): 16-byte
-  // aligned rows, the rows within what its threads copy in one pass, and not
-  // a block long enough for the prefill kernel.
+  // aligned rows, and the rows within what its threads copy in one pass.
   const bool gqa_ok = n_q_heads > 0 && n_q_heads % cache->n_kv_heads == 0;
-  const int64_t pairs = gqa_ok ? static_cast<int64_t>(n_q_heads / cache->n_kv_heads) * t_q : 0;
-  const bool prefill_route = t_q >= 8 && pairs >= 32 && kvc::prefill_supported(cache->dtype, cache->head_dim);
   const bool aligned = reinterpret_cast<uintptr_t>(k_new) % 16 == 0 && reinterpret_cast<uintptr_t>(v_new) % 16 == 0 &&
                        (new_stride_b * s) % 16 == 0 && (new_stride_h * s) % 16 == 0 && (new_stride_t * s) % 16 == 0;
-  if (gqa_ok && !prefill_route && aligned && kvc::routes_wide(cache, static_cast<int32_t>(n_q_heads * t_q)) &&
+  if (gqa_ok && aligned && kvc::routes_wide(cache, static_cast<int32_t>(n_q_heads * t_q)) &&
       static_cast<int64_t>(t_q) * (cache->head_dim / 8) <= 512)
     return launch_decode(cache, seq_lens, 0, k_new, v_new, new_stride_b, new_stride_h, q, n_q_heads, scale, out,
                          out_dtype, workspace, workspace_bytes, n_splits, dev_status, stream, t_q, nullptr, false,

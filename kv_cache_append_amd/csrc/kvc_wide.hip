@@ -875,7 +875,8 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.nst = new_stride_t * s;
   // a block's rows are folded in as one tile, each thread loading one chunk
   // of the rows a fused fill appends
-  if (t_q > 0 && (t_q > kWTile || (k_new != nullptr && t_q * (cache->head_dim / 8) > 512)))
+  static_assert(kvc::kWideMaxBlock <= kWTile, "a block is one tile");
+  if (t_q > 0 && (t_q > kvc::kWideMaxBlock || (k_new != nullptr && t_q * (cache->head_dim / 8) > 512)))
     return KVC_ERR_UNSUPPORTED;
   p.ws_flag = ws.flags;
   p.flag_stride = ws.flag_stride;

@@ -76,6 +76,28 @@ def test_block_matches_oracle(gpu, dtype, hq, hkv, t_q):
     assert np.abs(got - ref).max() <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv,t_q", [
+    ("bf16", 128, 8, 8, 64),      # MHA chunk of 64 tokens: 64 pairs
+    ("fp16", 128, 32, 8, 32),     # 128 pairs
+    ("bf16", 64, 16, 8, 64),      # D = 64, 128 pairs
+    ("bf16", 128, 4, 4, 40),      # 40 pairs, a block that is not a multiple of 16
+])
+def test_blocks_up_to_64_queries_on_the_wide_kernel(gpu, dtype, d, hq, hkv, t_q):
+    """Blocks of 8..64 queries with 8..128 (query, head) pairs per KV head
+    (the wide-group kernel's range): within the bar of the oracle, the
+    block's own keys under the causal mask included, and run to run
+    deterministic."""
+    case = BlockCase(batch=4, n_q=hq, n_kv=hkv, d=d, dtype=dtype, lengths=[0, 37, 300, 1025], t_q=t_q,
+                     tag=f"wblk{dtype}{d}{hq}{hkv}{t_q}")
+    case.fill()
+    got = _run(case)
+    again = _run(case)
+    assert torch.equal(got, again)
+    g = got.double().cpu().numpy()
+    assert not np.isnan(g).any()
+    assert np.abs(g - case.oracle()).max() <= TOL[dtype]
+
+
 @pytest.mark.parametrize("d", [64, 256, 32])
 def test_block_other_head_dims(gpu, d):
     case = BlockCase(batch=2, n_q=8, n_kv=2, d=d, dtype="bf16", lengths=[90, 513], t_q=3, tag=f"blkd{d}")
@@ -195,7 +217,11 @@ def test_verify_step_at_gqa_8b_shape_sampled(gpu):
     ("bf16", 64, 16, 2, 3),       # D = 64: fused
     ("fp16", 128, 8, 8, 3),       # 3 pairs: fill, then the decode kernel
     ("fp16", 128, 64, 1, 3),      # 192 pairs: fill, then the decode kernel
-    ("bf16", 128, 32, 8, 8),      # 32 pairs, t_q = 8: fill, then the prefill kernel
+    ("bf16", 128, 32, 8, 8),      # 32 pairs, t_q = 8: fused
+    ("bf16", 128, 32, 8, 32),     # 128 pairs, t_q = 32: fused (the rows fill the threads' one pass)
+    ("bf16", 128, 8, 8, 48),      # 48 pairs, t_q = 48: fill, then the wide-group kernel
+    ("bf16", 64, 16, 8, 64),      # D = 64, 128 pairs, t_q = 64: fused
+    ("fp16", 128, 8, 8, 80),      # t_q = 80: fill, then the prefill kernel
     ("fp32", 128, 8, 2, 4),       # fp32 cache: fill, then the decode kernel
 ])
 @pytest.mark.parametrize("n_splits", [0, 3])

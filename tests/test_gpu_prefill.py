@@ -69,10 +69,11 @@ def test_prefill_whole_prompt_is_causal_attention(gpu):
 def test_prefill_equals_block_attn_within_tolerance(gpu):
     """kvc_prefill_attn and kvc_block_attn compute the same thing: both sit
     within the bf16 bar of the oracle, so within twice it of each other. A
-    block of 7 queries at group 4 (28 (query, head) pairs per KV head) stays
-    on the decode kernel in kvc_block_attn (blocks of 8+ queries with 32+
-    pairs go to the prefill kernel), and 500 cached tokens span several
-    64-key tiles of the prefill kernel, so two different kernels are compared."""
+    block of 7 queries at group 4 (28 (query, head) pairs per KV head) runs
+    on the wide-group kernel in kvc_block_attn (only blocks of 8+ queries
+    and 32+ pairs that kernel does not take go to the prefill kernel), and
+    500 cached tokens span several 64-key tiles of the prefill kernel, so two
+    different kernels are compared."""
     t_q = 7
     case = BlockCase(batch=2, n_q=8, n_kv=2, d=128, dtype="bf16", lengths=[17, 500], t_q=t_q, tag="pfblk")
     case.fill()
@@ -163,11 +164,12 @@ def test_prefill_token_major_cache_equals_head_major_bitwise(gpu):
     assert torch.equal(out, ref)
 
 
-@pytest.mark.parametrize("hq,hkv,t_q", [(8, 2, 16), (32, 8, 8), (8, 8, 40)])
+@pytest.mark.parametrize("hq,hkv,t_q", [(32, 8, 40), (8, 8, 80), (8, 2, 72), (64, 1, 8)])
 def test_long_blocks_of_block_attn_run_on_the_prefill_kernel(gpu, hq, hkv, t_q):
     """kvc_block_attn hands blocks of >= 8 queries with >= 32 (query, head)
-    pairs per KV head to the prefill kernel: the same bits as
-    kvc_prefill_attn, and within the bar of the oracle."""
+    pairs per KV head that the wide-group kernel does not take (more than
+    128 pairs, or more than 64 queries) to the prefill kernel: the same bits
+    as kvc_prefill_attn, and within the bar of the oracle."""
     case = BlockCase(batch=2, n_q=hq, n_kv=hkv, d=128, dtype="bf16", lengths=[70, 1000], t_q=t_q,
                      tag=f"pfroute{hq}{hkv}{t_q}")
     case.fill()
