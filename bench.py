@@ -108,14 +108,14 @@ class Workload:
         self.t_max = ring if ring else int(self.lengths.max()) + margin_tokens + 1
         L, B, Hkv, Hq, D = cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
         tdt = synth.DTYPES[cfg.dtype]
-        # contiguous 16-bit caches with 8..128 (query, head) pairs per KV head
+        # contiguous 16-bit caches with 8..512 (query, head) pairs per KV head
         # and blocks of at most 64 queries run on the wide-group kernel; other
         # blocks of 8+ queries and 32+ pairs on the prefill kernel
         pairs = cfg.group * max(block_q, 1)
         sixteen = cfg.dtype in ("fp16", "bf16") and cfg.head_dim in (64, 128)
         self.block_prefill = (bool(block_q) and sixteen and block_q >= 8 and pairs >= 32
-                              and not (8 <= pairs <= 128 and block_q <= 64))
-        self.wide = not (page or ring or quant) and sixteen and 8 <= pairs <= 128 and not self.block_prefill
+                              and not (8 <= pairs <= 512 and block_q <= 64))
+        self.wide = not (page or ring or quant) and sixteen and 8 <= pairs <= 512 and not self.block_prefill
         self.fused_advance = not (block_q or page or ring or quant)   # (see below)
         if quant:
             self._init_quant(cfg, seed, splits, dev, tdt)

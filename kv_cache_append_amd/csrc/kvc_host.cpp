@@ -164,10 +164,10 @@ bool routes_wide(const kvc_cache_t* c, int32_t n_q_heads) {
 
 int32_t auto_splits(const kvc_cache_t* c, int32_t n_q_heads, bool wide) {
   if (c == nullptr || c->n_kv_heads <= 0 || n_q_heads <= 0 || c->batch <= 0) return 1;
-  // workgroups per split: one per (sequence, KV head) on the wide-group
-  // kernel, one per (sequence, KV head, head block) on the other
+  // workgroups per split: one per (sequence, KV head, pair block) on the
+  // wide-group kernel, one per (sequence, KV head, head block) on the other
   const int64_t units = static_cast<int64_t>(c->batch) * c->n_kv_heads *
-                        (wide ? 1 : head_blocks(n_q_heads / c->n_kv_heads));
+                        (wide ? wide_pair_blocks(n_q_heads / c->n_kv_heads) : head_blocks(n_q_heads / c->n_kv_heads));
   // Measured on MI355X (256 CUs): the fastest launches hold about one
   // workgroup per CU; more, shorter splits pay the per-workgroup start-up
   // and the merge more often than they gain, and with 256 or more units one
@@ -247,7 +247,7 @@ int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_
   // the wide-group kernel: one workgroup per (sequence, KV head) and split,
   // one per CU
   const int per_cu = wide ? 1 : std::min(resident_wgs(c->dtype, c->head_dim, gb), 4);
-  const int hblk = wide ? 1 : head_blocks(group);
+  const int hblk = wide ? wide_pair_blocks(group) : head_blocks(group);
   const double row_bytes = 2.0 * c->head_dim * elem_bytes(c->dtype);   // K and V of one token
   int32_t cap = c->max_len / 256;            // chunks of 256 tokens at least, as the default rule
   if (cap < 1) cap = 1;
@@ -293,7 +293,8 @@ size_t workspace_sync_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_
 
 size_t workspace_o_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {
   return workspace_sync_offset(c, n_q_heads, n_splits) +
-         round256(static_cast<size_t>(c->batch) * c->n_kv_heads * kWideSyncBytes);
+         round256(static_cast<size_t>(c->batch) * c->n_kv_heads * wide_pair_blocks(n_q_heads / c->n_kv_heads) *
+                  kWideSyncBytes);
 }
 
 size_t workspace_ml_offset(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits) {

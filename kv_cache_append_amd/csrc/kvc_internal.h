@@ -69,7 +69,7 @@ int32_t splits_for_lengths(const kvc_cache_t* c, int32_t n_q_heads, const int32_
 
 // Workspace: uint32 ready flags [B * H_kv * head_blocks, S] (word S - 1 of
 // each row is that block's merge epoch), then the wide-group kernel's merge
-// words [B * H_kv, kWideSyncWords] (uint32), then fp32 partial outputs [B, H_q, S, D],
+// words [B * H_kv * pair blocks, kWideSyncWords] (uint32), then fp32 partial outputs [B, H_q, S, D],
 // then fp32 (reference, sum) pairs [B, H_q, S, 2]; each region starts on a
 // 256-byte boundary.
 size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits);
@@ -83,14 +83,14 @@ size_t workspace_bytes(const kvc_cache_t* c, int32_t n_q_heads, int32_t n_splits
 struct WsRegions {
   uint32_t* flags;
   int32_t flag_stride;
-  uint32_t* sync;   // the wide-group kernel: kWideSyncWords per (sequence, KV head)
+  uint32_t* sync;   // the wide-group kernel: kWideSyncWords per (sequence, KV head, pair block)
   float* o;
   float* ml;
 };
-// Per (sequence, KV head), for the wide-group kernel's spread merge (up to
-// kWideSpreadMax splits): an arrival count (word 0), one claim word per
-// output slice (words 1 ..) and the merge epoch (the last word), in a row of
-// kWideSyncWords uint32.
+// Per (sequence, KV head, pair block), for the wide-group kernel's spread
+// merge (up to kWideSpreadMax splits): an arrival count (word 0), one claim
+// word per output slice (words 1 ..) and the merge epoch (the last word), in
+// a row of kWideSyncWords uint32.
 constexpr int kWideSpreadMax = 32;
 constexpr int kWideSyncWords = 64;
 constexpr size_t kWideSyncBytes = kWideSyncWords * sizeof(uint32_t);
@@ -130,12 +130,20 @@ kvc_status_t check_qcache(const kvc_qcache_t* c, bool for_decode);
 kvc_cache_t qcache_view(const kvc_qcache_t* c);
 
 // The wide-group decode kernel (kvc_wide.hip): fp16/bf16 caches with head
-// dim 64 or 128 and KVC_WIDE_MIN_PAIRS..128 (query, head) pairs per KV head
-// (group size times queries per sequence); contiguous caches. Its launch
-// takes arguments already validated by launch_decode.
+// dim 64 or 128 and KVC_WIDE_MIN_PAIRS..kWideMaxPairs (query, head) pairs per
+// KV head (group size times queries per sequence); contiguous caches. One
+// workgroup takes up to kWidePairBlock pairs of a (sequence, KV head) unit;
+// a unit with more pairs has several such pair blocks, each streaming the
+// unit's K/V (on the unit's XCD, so all but the first mostly from its L2).
+// Its launch takes arguments already validated by launch_decode.
 #ifndef KVC_WIDE_MIN_PAIRS
 #define KVC_WIDE_MIN_PAIRS 8
 #endif
+constexpr int kWidePairBlock = 128;
+constexpr int kWideMaxPairs = 512;
+inline int wide_pair_blocks(int32_t pairs) {
+  return pairs <= kWidePairBlock ? 1 : (pairs + kWidePairBlock - 1) / kWidePairBlock;
+}
 bool wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs);
 // The longest block of queries the wide-group kernel takes: the block's
 // rows are folded in as one LDS tile of keys.

@@ -37,6 +37,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kvc.h"
@@ -71,13 +72,14 @@ struct WideParams {
   const char* k_new;             // fused append source [B, H_kv, D] (a block: [B, H_kv, t_q, D]) or null
   const char* v_new;
   int64_t nsb, nsh, nst;         // its strides in bytes (nst: between a block's rows)
-  uint32_t* ws_flag;             // [B * H_kv * n_hblk, flag_stride]: this kernel uses head block 0's row
-  uint32_t* ws_sync;             // [B * H_kv, kWideSyncWords]: arrival count and slice claims of the spread merge
-  float* ws_o;                   // per unit [S][D / 16][pairs][16]: see pofs in the kernel
+  uint32_t* ws_flag;             // [B * H_kv * n_hblk, flag_stride]: pair block pb uses head block pb's row
+  uint32_t* ws_sync;             // [B * H_kv * n_pb, kWideSyncWords]: arrival count and slice claims of the spread merge
+  float* ws_o;                   // per unit and pair block [S][D / 16][its pairs][16]: see pofs in the kernel
   float* ws_ml;                  // [B, H_kv * pairs, S, 2]
   void* out;                     // like q; fp32 or the cache dtype
   uint32_t* status;
   int32_t batch, n_q, n_kv, group, n_hblk, max_len, n_pending, n_splits, out_f32;
+  int32_t n_pb;                  // pair blocks per unit (kWidePairBlock pairs each, the last the rest)
   int32_t t_q, block;            // block of t_q queries (lower-right causal mask), or decode (block = 0)
   int32_t out_vec;               // out is 16-byte aligned: four elements per store
   float scale_log2;              // softmax scale * log2(e)
@@ -150,11 +152,14 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   __shared__ __attribute__((aligned(16))) char smem[kLds];
 
   // Workgroup placement: every split of a unit on one XCD (id residue mod 8),
-  // the unit's splits in consecutive slots there, the merging split last.
+  // the unit's splits in consecutive slots there, the merging split last;
+  // the splits of the unit's pair blocks one block after the other.
   const int xcd = blockIdx.x & 7;
   const int r8 = blockIdx.x >> 3;
   const int split = r8 % p.n_splits;
-  const int unit = (r8 / p.n_splits) * 8 + xcd;
+  const int w8 = r8 / p.n_splits;
+  const int pb = w8 % p.n_pb;
+  const int unit = (w8 / p.n_pb) * 8 + xcd;
   if (unit >= p.batch * p.n_kv) return;              // grid padding
   const int b = unit / p.n_kv;
   const int g = unit - b * p.n_kv;
@@ -162,8 +167,8 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // tiles' loads and used at the end: the last word of the unit's flag row
   // for the last-split merge, the last word of its merge-word row for the
   // spread merge, each in the row whose words it is compared with
-  uint32_t* const flags = p.ws_flag + static_cast<int64_t>(unit) * p.n_hblk * p.flag_stride;
-  uint32_t* const sync = p.ws_sync + static_cast<int64_t>(unit) * kvc::kWideSyncWords;
+  uint32_t* const flags = p.ws_flag + (static_cast<int64_t>(unit) * p.n_hblk + pb) * p.flag_stride;
+  uint32_t* const sync = p.ws_sync + (static_cast<int64_t>(unit) * p.n_pb + pb) * kvc::kWideSyncWords;
   uint32_t* const sync_epoch = sync + (kvc::kWideSyncWords - 1);
   uint32_t epoch = 0u;
 
@@ -174,7 +179,10 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int kh = wave >> 2;                          // which half of each tile's keys
   const int r16 = lane & 15;
   const int grp = lane >> 4;
-  const int gv = p.group * p.t_q;                    // (query, head) pairs of this KV head
+  // (query, head) pairs v0 .. v0 + gv - 1 of this KV head's group * t_q;
+  // below, v is a pair's index within the block, v0 + v its index in the unit
+  const int v0 = pb * kvc::kWidePairBlock;
+  const int gv = min(p.group * p.t_q - v0, kvc::kWidePairBlock);
   const int ncb = (gv + 15) / 16;
 
   // The wave's pairs as B operands of the score product (column = pair r16
@@ -192,9 +200,9 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     const int cb = cbw + 4 * j;
     cb_on[j] = cb < ncb;
     const int v = cb * 16 + r16;
-    const int qi = v / p.group;
+    const int qi = (v0 + v) / p.group;
     const uint32_t qoff = cb_on[j] && v < gv
-                              ? static_cast<uint32_t>(((qi * p.n_q + (v - qi * p.group)) * D + 8 * grp) * 2)
+                              ? static_cast<uint32_t>(((qi * p.n_q + (v0 + v - qi * p.group)) * D + 8 * grp) * 2)
                               : 0x80000000u;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) qf[j][cc] = wload<0>(qrs, qoff + 64u * cc);
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // Rows attended (n), the slot the fused append writes, device-side flags.
   const int c0 = p.seq_lens[b];
   // kvc_decode_step_advance: the next step's lengths, into another array
-  if (p.lens_next != nullptr && g == 0 && split == 0 && threadIdx.x == 0) p.lens_next[b] = c0 + 1;
+  if (p.lens_next != nullptr && g == 0 && split == 0 && pb == 0 && threadIdx.x == 0) p.lens_next[b] = c0 + 1;
   const int c = c0 < 0 ? 0 : c0;
   uint32_t dflags = c0 < 0 ? KVC_DEVERR_BADLEN : 0u;
   const int add = p.block ? p.t_q : (p.k_new != nullptr ? 1 : p.n_pending);
@@ -222,14 +230,16 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     if (n64 > p.max_len) dflags |= KVC_DEVERR_CAPACITY;
     if (c0 < 0) n = 0;             // a negative length: a zero row, nothing attended
   }
-  if (dflags != 0 && g == 0 && split == 0 && threadIdx.x == 0 && p.status != nullptr) atomicOr(p.status, dflags);
+  if (dflags != 0 && g == 0 && split == 0 && pb == 0 && threadIdx.x == 0 && p.status != nullptr)
+    atomicOr(p.status, dflags);
   auto store_out = [&](int64_t idx, float x) {
     if (p.out_f32) static_cast<float*>(p.out)[idx] = x;
     else ET::store(p.out, idx, x);
   };
   if (n <= 0) {                                      // empty sequence: zero rows
     if (split == 0)
-      for (int t = threadIdx.x; t < gv * D; t += blockDim.x) store_out(wpair_row(p, b, g, t / D) * D + t % D, 0.f);
+      for (int t = threadIdx.x; t < gv * D; t += blockDim.x)
+        store_out(wpair_row(p, b, g, v0 + t / D) * D + t % D, 0.f);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the query loads)
     return;
   }
@@ -263,7 +273,8 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // (loads read zero, stores are dropped), as a load under a branch would
   // make the compiler wait for every load issued before it.
   const int64_t nst = p.block ? p.nst : static_cast<int64_t>(D * 2);   // between the new rows
-  const uint32_t arange = x_new ? static_cast<uint32_t>((xrows - 1) * nst + D * 2) : 0u;
+  const bool x_write = x_new && pb == 0;             // the first pair block writes the rows
+  const uint32_t arange = x_write ? static_cast<uint32_t>((xrows - 1) * nst + D * 2) : 0u;
   const uint32_t aoff_new = static_cast<uint32_t>((tid / CPR) * nst + (tid % CPR) * 16);
   const int64_t nrow = b * p.nsb + g * p.nsh;
   const __amdgpu_buffer_rsrc_t kn_rs = wrsrc(uniform_cptr(p.k_new != nullptr ? p.k_new + nrow : p.k), arange);
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     const int v = (cbw + 4 * j) * 16 + r16;
-    plim[j] = p.block ? n - p.t_q + v / p.group + 1 : n;
+    plim[j] = p.block ? n - p.t_q + (v0 + v) / p.group + 1 : n;
   }
 
   const uint32_t st = static_cast<uint32_t>(p.st);
@@ -463,7 +474,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   {
     // the fused append's stores (the rows' loads were issued at entry)
     const int64_t aoff = static_cast<int64_t>(append_row < 0 ? 0 : append_row) * p.st;
-    const uint32_t crange = x_new ? static_cast<uint32_t>((xrows - 1) * st + D * 2) : 0u;
+    const uint32_t crange = x_write ? static_cast<uint32_t>((xrows - 1) * st + D * 2) : 0u;
     const __amdgpu_buffer_rsrc_t ka_rs = wrsrc(uniform_cptr(kunit + aoff), crange);
     const __amdgpu_buffer_rsrc_t va_rs = wrsrc(uniform_cptr(vunit + aoff), crange);
     const int coff = static_cast<int>((tid / CPR) * st + (tid % CPR) * 16);
@@ -543,7 +554,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     const int v = (cbw + 4 * j) * 16 + r16;
     if (v >= gv) return;
     const float inv = 1.f / l;
-    const int64_t row = wpair_row(p, b, g, v) * D;
+    const int64_t row = wpair_row(p, b, g, v0 + v) * D;
 #pragma unroll
     for (int h = 0; h < NDH; ++h) {
       const int64_t idx = row + 16 * (NDH * kh + h) + 4 * grp;
@@ -567,9 +578,11 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // advances the unit's epoch. It has the highest workgroup id of its unit
   // on the XCD, and a publishing workgroup never waits, so every awaited
   // workgroup is dispatched and finishes; the wait is bounded all the same.
-  // This unit's exchange: gv * S * D partial output floats (in the order
-  // pofs gives below) and (reference, sum) pairs [split][pair].
-  const int64_t ubase = static_cast<int64_t>(unit) * p.n_splits * gv;
+  // This pair block's exchange: gv * S * D partial output floats (in the
+  // order pofs gives below) and (reference, sum) pairs [split][pair], the
+  // unit's pair blocks one after the other.
+  const int64_t ubase = static_cast<int64_t>(unit) * p.n_splits * (p.group * p.t_q) +
+                        static_cast<int64_t>(p.n_splits) * v0;
   const __amdgpu_buffer_rsrc_t ors = wrsrc(p.ws_o + ubase * D, static_cast<uint32_t>(gv) * p.n_splits * D * 4u);
   const __amdgpu_buffer_rsrc_t mrs = wrsrc(p.ws_ml + ubase * 2, static_cast<uint32_t>(gv) * p.n_splits * 8u);
   const __amdgpu_buffer_rsrc_t frs = wrsrc(flags, static_cast<uint32_t>(p.flag_stride) * 4u);
@@ -700,7 +713,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
         f32x4 y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = acc[i] * inv;
-        store4(wpair_row(p, b, g, v) * D + 16 * db + 4 * g4, y);
+        store4(wpair_row(p, b, g, v0 + v) * D + 16 * db + 4 * g4, y);
       }
     };
     if (state != 0u) merge_slice(split, true);
@@ -843,7 +856,7 @@ WideKernel pick_wide_kernel(int32_t dtype, int32_t d, int qb) {
 
 bool kvc::wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs) {
   return (dtype == KVC_BF16 || dtype == KVC_F16) && (head_dim == 64 || head_dim == 128) &&
-         pairs >= KVC_WIDE_MIN_PAIRS && pairs <= 128;
+         pairs >= KVC_WIDE_MIN_PAIRS && pairs <= kvc::kWideMaxPairs;
 }
 
 kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
@@ -857,9 +870,9 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   const int32_t tq = t_q > 0 ? t_q : 1;
   const int32_t group = n_q_heads / cache->n_kv_heads;
   const int32_t pairs = group * tq;
-  const int qb = (pairs + 63) / 64;
+  const int qb = (std::min(pairs, kvc::kWidePairBlock) + 63) / 64;   // column blocks of 64 pairs per workgroup
   WideKernel kern = pick_wide_kernel(cache->dtype, cache->head_dim, qb);
-  if (kern == nullptr || qb > 2) return KVC_ERR_UNSUPPORTED;
+  if (kern == nullptr || qb > 2 || pairs > kvc::kWideMaxPairs) return KVC_ERR_UNSUPPORTED;
   WideParams p;
   p.k = static_cast<char*>(cache->k);
   p.v = static_cast<char*>(cache->v);
@@ -891,6 +904,8 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.n_kv = cache->n_kv_heads;
   p.group = group;
   p.n_hblk = kvc::head_blocks(pairs);
+  p.n_pb = kvc::wide_pair_blocks(pairs);
+  if (p.n_pb > p.n_hblk) return KVC_ERR_UNSUPPORTED;    // (a flag row per pair block: never with 8+ pairs)
   p.max_len = cache->max_len;
   p.n_pending = n_pending;
   p.n_splits = splits;
@@ -901,7 +916,7 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.scale_log2 = scale_log2;
   p.merge_spins = kvc::merge_spin_limit();
   const int64_t units = static_cast<int64_t>(cache->batch) * cache->n_kv_heads;
-  const int64_t wgs = (units + 7) / 8 * 8 * splits;    // see the placement in the kernel
+  const int64_t wgs = (units + 7) / 8 * 8 * p.n_pb * splits;    // see the placement in the kernel
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
   if (check_only) return KVC_OK;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(wgs)), dim3(512), 0, stream, p);

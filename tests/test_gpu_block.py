@@ -81,9 +81,11 @@ def test_block_matches_oracle(gpu, dtype, hq, hkv, t_q):
     ("fp16", 128, 32, 8, 32),     # 128 pairs
     ("bf16", 64, 16, 8, 64),      # D = 64, 128 pairs
     ("bf16", 128, 4, 4, 40),      # 40 pairs, a block that is not a multiple of 16
+    ("bf16", 128, 64, 1, 8),      # MQA verify of 8 tokens: 512 pairs in four pair blocks
+    ("fp16", 128, 32, 8, 64),     # 256 pairs, 64 queries: two pair blocks
 ])
 def test_blocks_up_to_64_queries_on_the_wide_kernel(gpu, dtype, d, hq, hkv, t_q):
-    """Blocks of 8..64 queries with 8..128 (query, head) pairs per KV head
+    """Blocks of 8..64 queries with 8..512 (query, head) pairs per KV head
     (the wide-group kernel's range): within the bar of the oracle, the
     block's own keys under the causal mask included, and run to run
     deterministic."""
@@ -194,11 +196,14 @@ def test_block_negative_length_is_flagged(gpu):
     assert torch.count_nonzero(got[1]) == 0
 
 
-def test_verify_step_at_gqa_8b_shape_sampled(gpu):
-    """A speculative verify step of 4 tokens at the 8B GQA shape (B=16, 32/8
-    heads, D=128, T=2048, bf16), with the library's split choice, checked on
+@pytest.mark.parametrize("t_q", [4, 8, 16, 32])
+def test_verify_step_at_gqa_8b_shape_sampled(gpu, t_q):
+    """A block of t_q new tokens at the 8B GQA shape (B=16, 32/8 heads,
+    D=128, T=2048, bf16; 16 to 128 (query, head) pairs per KV head, all on
+    the wide-group kernel), with the library's split choice, checked on
     sampled sequences."""
-    case = BlockCase(batch=16, n_q=32, n_kv=8, d=128, dtype="bf16", lengths=[2048] * 16, t_q=4, tag="blkv8b")
+    case = BlockCase(batch=16, n_q=32, n_kv=8, d=128, dtype="bf16", lengths=[2048] * 16, t_q=t_q,
+                     tag=f"blkv8b{t_q}")
     case.fill()
     got = _run(case)
     k, v = case.k.cpu(), case.v.cpu()
@@ -216,7 +221,8 @@ def test_verify_step_at_gqa_8b_shape_sampled(gpu):
     ("bf16", 128, 1, 1, 20),      # 20 pairs, t_q = 20: fused (the block's rows fill most of a tile)
     ("bf16", 64, 16, 2, 3),       # D = 64: fused
     ("fp16", 128, 8, 8, 3),       # 3 pairs: fill, then the decode kernel
-    ("fp16", 128, 64, 1, 3),      # 192 pairs: fill, then the decode kernel
+    ("fp16", 128, 64, 1, 3),      # 192 pairs: fused, two pair blocks
+    ("bf16", 128, 64, 1, 8),      # 512 pairs: fused, four pair blocks
     ("bf16", 128, 32, 8, 8),      # 32 pairs, t_q = 8: fused
     ("bf16", 128, 32, 8, 32),     # 128 pairs, t_q = 32: fused (the rows fill the threads' one pass)
     ("bf16", 128, 8, 8, 48),      # 48 pairs, t_q = 48: fill, then the wide-group kernel
@@ -283,7 +289,8 @@ def test_block_step_repeated_with_a_strided_source(gpu):
         assert torch.equal(got_k[bb, :, :n].view(torch.int16), k_ref[bb, :, :n].view(torch.int16))
 
 
-@pytest.mark.parametrize("hq", [32, 2])     # one fused launch (80 pairs); fill then attention (5 pairs)
+# one fused launch (80 pairs); fill then attention (5 pairs); one fused launch in three pair blocks (320 pairs)
+@pytest.mark.parametrize("hq", [32, 2, 128])
 def test_block_step_that_does_not_fit_or_has_a_negative_length(gpu, hq):
     """A block past max_len is not written and gets zero rows (capacity flag);
     a negative length gets zero rows (bad-length flag); the other sequences

@@ -35,13 +35,14 @@ def _oracle_all(case: DecodeCase):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("n_q,n_kv", [(8, 1), (24, 2), (16, 1), (32, 1), (64, 1), (128, 1), (64, 2)])
+@pytest.mark.parametrize("n_q,n_kv", [(8, 1), (24, 2), (16, 1), (32, 1), (64, 1), (128, 1), (64, 2), (256, 1), (320, 2)])
 @pytest.mark.parametrize("splits", [0, 1, 2, 3])
 def test_wide_decode_step_matches_oracle(gpu, dtype, d, n_q, n_kv, splits):
     """The fused step (append + attend T_b + 1 rows) on the wide kernel, for
     lengths on and around the 64-key tile and empty sequences, with one, two
     (last-split merge), three (spread merge) or the library's number of
-    splits; the appended rows are exact."""
+    splits; groups of 256 and 160 heads run in two pair blocks of up to 128
+    heads; the appended rows are exact."""
     case = DecodeCase(batch=len(LENS), n_q=n_q, n_kv=n_kv, head_dim=d, dtype=dtype, lengths=LENS,
                       tag=f"wide{dtype}{d}{n_q}{n_kv}", device=gpu)
     ws = kvc.workspace(case.k, case.v, n_q, splits)
@@ -123,12 +124,15 @@ def test_wide_out_in_cache_dtype_is_rounded_fp32_out(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("hq,hkv,t_q", [(4, 1, 4), (8, 1, 2), (4, 1, 7), (16, 1, 3), (8, 2, 5), (64, 1, 2)])
-@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("hq,hkv,t_q", [(4, 1, 4), (8, 1, 2), (4, 1, 7), (16, 1, 3), (8, 2, 5), (64, 1, 2),
+                                        (64, 1, 4), (64, 1, 8), (32, 8, 40), (16, 2, 20)])
+@pytest.mark.parametrize("splits", [0, 2, 3])
 def test_wide_query_block_matches_oracle(gpu, dtype, hq, hkv, t_q, splits):
     """A block of t_q new queries per sequence (speculative verify, short
-    prefill chunks) with 8..128 (query, head) pairs per KV head runs on the
-    wide kernel; the lower-right causal mask of course notes §3.3."""
+    prefill chunks) with 8..512 (query, head) pairs per KV head runs on the
+    wide kernel (more than 128 pairs in pair blocks of up to 128: 256, 512
+    and 160 pairs here, the last block partly filled), with one merge of
+    each kind; the lower-right causal mask of course notes §3.3."""
     case = BlockCase(batch=4, n_q=hq, n_kv=hkv, d=128, dtype=dtype, lengths=[0, 37, 300, 1025], t_q=t_q,
                      tag=f"wblk{dtype}{hq}{hkv}{t_q}", device=gpu)
     case.fill()

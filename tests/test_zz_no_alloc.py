@@ -27,6 +27,7 @@ def _noalloc(case: DecodeCase, out, n_splits, status):
     # (batch, n_q, n_kv, lengths, splits): a large call, then a smaller one
     ((16, 32, 8, [2048] * 16, 0), (3, 8, 2, [5, 300, 77], 3)),
     ((8, 64, 1, [4096] * 8, 0), (2, 32, 1, [100, 1500], 2)),         # wide-group kernel
+    ((4, 256, 1, [900] * 4, 0), (2, 160, 1, [100, 1500], 3)),        # wide-group kernel, two pair blocks
 ])
 def test_noalloc_step_equals_workspace_step(gpu, shapes):
     for i, (b, nq, nkv, lens, splits) in enumerate(shapes):
