@@ -212,11 +212,11 @@ int32_t kvc_decode_splits_for_lengths(const kvc_cache_t* cache, int32_t n_q_head
  * Accumulation is fp32; results are run-to-run deterministic.
  * Supported: head_dim in {64, 128, 256} for every dtype, plus head_dim 4..32
  * (powers of two with head_dim * elem_bytes >= 16); any group size.
- * Groups of 8..128 query heads per KV head on fp16/bf16 caches with head_dim
- * 64 or 128 run on a kernel that streams each KV head's K/V once for the
- * whole group, both products on the matrix cores (course notes §2.2, §2.5:
- * the group shares its K/V, saving bytes, not FLOPs); the other shapes read
- * K/V once per block of up to 8 query heads.
+ * Groups of 8..512 query heads per KV head on fp16/bf16 caches with head_dim
+ * 64 or 128 run on a kernel that streams each KV head's K/V once per 128
+ * heads of the group, both products on the matrix cores (course notes §2.2,
+ * §2.5: the group shares its K/V, saving bytes, not FLOPs); the other shapes
+ * read K/V once per block of up to 8 query heads.
  */
 kvc_status_t kvc_decode_attn(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending,
                              const void* q, int32_t n_q_heads, float scale,
@@ -312,8 +312,8 @@ kvc_status_t kvc_decode_step_noalloc(const kvc_cache_t* cache, const int32_t* se
  *
  * The (query, head) pairs of a KV head are processed like the query heads of
  * a larger group, so K/V rows are streamed once per block of up to 8 pairs,
- * or, on fp16/bf16 caches with head_dim 64 or 128, 8..128 pairs per KV head
- * and t_q <= 64, once for all of them (the wide-group kernel, as for decode
+ * or, on fp16/bf16 caches with head_dim 64 or 128, 8..512 pairs per KV head
+ * and t_q <= 64, once per 128 of them (the wide-group kernel, as for decode
  * with 8+ query heads per KV head); this suits verify steps and chunks of up
  * to 64 tokens. Other blocks of t_q >= 8 with t_q * (n_q_heads / n_kv_heads)
  * >= 32 on fp16/bf16 caches with head_dim 64 or 128 run on the kernel of
@@ -351,7 +351,7 @@ size_t kvc_block_workspace_bytes(const kvc_cache_t* cache, int32_t n_q_heads, in
  *             kvc_block_workspace_bytes); seq_lens is only read.
  *
  * Where the block runs on the wide-group kernel (fp16/bf16, head_dim 64 or
- * 128, 8..128 (query, head) pairs per KV head), t_q * head_dim <= 4096 and
+ * 128, 8..512 (query, head) pairs per KV head), t_q * head_dim <= 4096 and
  * k_new/v_new rows are 16-byte aligned, this is one launch: the kernel
  * folds the block's rows in from k_new/v_new and writes them into the cache
  * (no workgroup reads those slots from the cache). Otherwise it enqueues the
