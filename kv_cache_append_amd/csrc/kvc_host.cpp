@@ -157,6 +157,13 @@ int head_blocks(int32_t group) {
   return (group + hb - 1) / hb;
 }
 
+bool quant_routes_wide(const kvc_qcache_t* c, int32_t n_q_heads) {
+  if (c == nullptr || c->n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return false;
+  const int32_t group = n_q_heads / c->n_kv_heads;
+  return (c->in_dtype == KVC_F16 || c->in_dtype == KVC_BF16) && group >= KVC_WIDE_QUANT_MIN_GROUP &&
+         wide_supported(c->in_dtype, c->head_dim, group);
+}
+
 bool routes_wide(const kvc_cache_t* c, int32_t n_q_heads) {
   if (c == nullptr || c->n_kv_heads <= 0 || n_q_heads <= 0) return false;
   return wide_supported(c->dtype, c->head_dim, n_q_heads / c->n_kv_heads);
@@ -367,7 +374,8 @@ extern "C" size_t kvc_quant_decode_workspace_bytes(const kvc_qcache_t* cache, in
   if (kvc::check_qcache(cache, true) != KVC_OK) return 0;
   if (n_q_heads <= 0 || n_q_heads % cache->n_kv_heads != 0 || n_splits < 0 || n_splits > KVC_MAX_SPLITS) return 0;
   const kvc_cache_t view = kvc::qcache_view(cache);
-  const int32_t s = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads);
+  const int32_t s =
+      n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads, kvc::quant_routes_wide(cache, n_q_heads));
   return kvc::workspace_bytes(&view, n_q_heads, s);
 }
 

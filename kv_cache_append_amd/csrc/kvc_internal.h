@@ -148,13 +148,31 @@ bool wide_supported(int32_t dtype, int32_t head_dim, int32_t pairs);
 // The longest block of queries the wide-group kernel takes: the block's
 // rows are folded in as one LDS tile of keys.
 constexpr int kWideMaxBlock = 64;
+// The kernel's 8-bit mode (kvc_quant_decode_attn): the cache view's k and v
+// hold the codes (one byte each, strides in bytes); the scales as here.
+struct WideQuant {
+  int32_t format;             // KVC_QFMT_*
+  int32_t q_dtype;            // KVC_F16 or KVC_BF16: the queries' type, which the codes are widened to
+  const float* k_scale;
+  const float* v_scale;
+  int64_t scale_stride_b, scale_stride_h;   // in floats; the token axis is contiguous
+};
 // check_only: every host check, nothing enqueued (for a call that enqueues a
-// second launch after a first one and must fail before either).
+// second launch after a first one and must fail before either). quant: the
+// 8-bit mode (decode only, no fused append).
 kvc_status_t launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,
                          const void* v_new, int64_t new_stride_b, int64_t new_stride_h, int64_t new_stride_t,
                          const void* q, int32_t n_q_heads, int32_t t_q, float scale_log2, void* out,
                          int32_t out_dtype, const WsRegions& ws, int32_t splits, int32_t* lens_next,
-                         uint32_t* dev_status, hipStream_t stream, bool check_only = false);
+                         uint32_t* dev_status, hipStream_t stream, bool check_only = false,
+                         const WideQuant* quant = nullptr);
+// Whether a decode on this 8-bit cache runs on the wide-group kernel's 8-bit
+// mode: fp16/bf16 queries, head dim 64 or 128, KVC_WIDE_QUANT_MIN_GROUP ..
+// kWideMaxPairs query heads per KV head.
+#ifndef KVC_WIDE_QUANT_MIN_GROUP
+#define KVC_WIDE_QUANT_MIN_GROUP 16
+#endif
+bool quant_routes_wide(const kvc_qcache_t* c, int32_t n_q_heads);
 
 // Bound on the polls of the decode split merge's wait for ready flags (about
 // 2^20 by default; kvc_debug_set_merge_spin_limit changes it for tests of the

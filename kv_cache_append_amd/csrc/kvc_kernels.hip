@@ -1705,7 +1705,7 @@ QuantKernel pick_quant_rows_t(int in_dtype, int d) {
 
 kvc_status_t launch_quant_rows(const kvc_qcache_t* c, const int32_t* seq_lens, const void* k, const void* v,
                                int64_t sb, int64_t sh, int64_t st, int32_t t_new, uint32_t* status,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool check_only = false) {
   kvc_status_t rc = kvc::check_qcache(c, false);
   if (rc != KVC_OK) return rc;
   if (t_new < 0) return KVC_ERR_SHAPE;
@@ -1742,6 +1742,7 @@ kvc_status_t launch_quant_rows(const kvc_qcache_t* c, const int32_t* seq_lens, c
   const int64_t waves = 2 * static_cast<int64_t>(c->batch) * c->n_kv_heads * t_new;
   int64_t blocks = (waves + 3) / 4;             // 4 waves per 256-thread block
   if (blocks > 65536) blocks = 65536;           // the wave loop covers the rest
+  if (check_only) return KVC_OK;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
@@ -1752,7 +1753,7 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
                                  int32_t n_q_heads, float scale, void* out, int32_t out_dtype, void* workspace,
                                  size_t workspace_bytes, int32_t n_splits, uint32_t* dev_status,
                                  hipStream_t stream, const void* k_new = nullptr, const void* v_new = nullptr,
-                                 int64_t new_stride_b = 0, int64_t new_stride_h = 0) {
+                                 int64_t new_stride_b = 0, int64_t new_stride_h = 0, bool check_only = false) {
   kvc_status_t rc = kvc::check_qcache(c, true);
   if (rc != KVC_OK) return rc;
   if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return KVC_ERR_GQA;
@@ -1773,11 +1774,29 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
     if (reinterpret_cast<uintptr_t>(k_new) % s_in || reinterpret_cast<uintptr_t>(v_new) % s_in) return KVC_ERR_ALIGN;
   }
   const kvc_cache_t view = kvc::qcache_view(c);
-  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads);
+  // Groups of 16+ query heads (MQA, wide GQA) run on the wide-group kernel's
+  // 8-bit mode, which reads each KV head's codes once per 128 heads; the
+  // decode kernel's head blocks of 8 would read them once per block. (A
+  // fused append is not part of that mode: kvc_quant_decode_step then
+  // enqueues the append and this call.)
+  const bool wide = k_new == nullptr && kvc::quant_routes_wide(c, n_q_heads);
+  const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(&view, n_q_heads, wide);
   const size_t need = kvc::workspace_bytes(&view, n_q_heads, splits);
   if (workspace == nullptr || workspace_bytes < need) return KVC_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 16) return KVC_ERR_ALIGN;
   const int group = n_q_heads / c->n_kv_heads;
+  if (wide) {
+    const kvc::WsRegions wr = kvc::workspace_regions(&view, n_q_heads, splits, workspace);
+    kvc::WideQuant wq;
+    wq.format = c->format;
+    wq.q_dtype = c->in_dtype;
+    wq.k_scale = c->k_scale;
+    wq.v_scale = c->v_scale;
+    wq.scale_stride_b = c->scale_stride_b;
+    wq.scale_stride_h = c->scale_stride_h;
+    return kvc::launch_wide(&view, seq_lens, n_pending, nullptr, nullptr, 0, 0, 0, q, n_q_heads, 0, scale_log2, out,
+                            out_dtype, wr, splits, nullptr, dev_status, stream, check_only, &wq);
+  }
   const DecodeKernel k = pick_quant_kernel(c->format, c->in_dtype, c->head_dim, kvc::heads_per_block(group));
   if (k == nullptr) return KVC_ERR_UNSUPPORTED;
 
@@ -1822,6 +1841,7 @@ kvc_status_t launch_quant_decode(const kvc_qcache_t* c, const int32_t* seq_lens,
   p.merge_spins = kvc::merge_spin_limit();
   const int64_t wgs = decode_grid(static_cast<int64_t>(c->batch) * c->n_kv_heads, splits, p.n_hblk);
   if (wgs > 0x7fffffffll) return KVC_ERR_SHAPE;
+  if (check_only) return KVC_OK;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(wgs)), dim3(KVC_WAVES * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
@@ -2291,6 +2311,23 @@ extern "C" kvc_status_t kvc_quant_decode_step(const kvc_qcache_t* cache, const i
                                               int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                               int32_t n_splits, uint32_t* dev_status, hipStream_t stream) {
   if (cache != nullptr && cache->batch > 0 && (k_new == nullptr || v_new == nullptr)) return KVC_ERR_NULL;
+  if (cache != nullptr && cache->batch > 0 && kvc::check_qcache(cache, true) == KVC_OK &&
+      kvc::quant_routes_wide(cache, n_q_heads)) {
+    // On the wide-group kernel: the append, then the attention (every host
+    // check of both first), so the result is that of the two separate calls.
+    if (new_stride_b < 0 || new_stride_h < 0) return KVC_ERR_SHAPE;
+    if (cache->n_kv_heads > 1 && new_stride_h < cache->head_dim) return KVC_ERR_SHAPE;
+    kvc_status_t st = launch_quant_decode(cache, seq_lens, 1, q, n_q_heads, scale, out, out_dtype, workspace,
+                                          workspace_bytes, n_splits, dev_status, stream, nullptr, nullptr, 0, 0,
+                                          true);
+    if (st != KVC_OK) return st;
+    st = launch_quant_rows(cache, seq_lens, k_new, v_new, new_stride_b, new_stride_h, 0, 1, dev_status, stream, true);
+    if (st != KVC_OK) return st;
+    st = launch_quant_rows(cache, seq_lens, k_new, v_new, new_stride_b, new_stride_h, 0, 1, dev_status, stream);
+    if (st != KVC_OK) return st;
+    return launch_quant_decode(cache, seq_lens, 1, q, n_q_heads, scale, out, out_dtype, workspace, workspace_bytes,
+                               n_splits, dev_status, stream);
+  }
   return launch_quant_decode(cache, seq_lens, 1, q, n_q_heads, scale, out, out_dtype, workspace, workspace_bytes,
                              n_splits, dev_status, stream, k_new, v_new, new_stride_b, new_stride_h);
 }

@@ -59,6 +59,35 @@ static_assert(kSpreadMax <= 32, "one lane of a wave per slice, claims in 32 bits
 constexpr int kSyncScope =
     (KVC_XCD_COLOCATE && KVC_LOCAL_EXCHANGE) ? __HIP_MEMORY_SCOPE_WORKGROUP : __HIP_MEMORY_SCOPE_AGENT;
 
+// The 8-bit mode (KQ = 1: OCP E4M3 codes, KQ = 2: int8 codes, each with one
+// fp32 scale per token and KV head). Every code's value has at most 8
+// significant bits, so widening it to the queries' 16-bit type is exact; the
+// scales are applied to the scores (K) and to the weights in the weighted
+// sum (V), in fp32.
+constexpr int kWQFp8 = 1;
+constexpr int kWQInt8 = 2;
+// Codes in bytes 2 HI, 2 HI + 1 of w as two packed 16-bit values.
+template <int KQ, bool kF16, bool HI>
+__device__ inline uint32_t wcode_pair16(uint32_t w) {
+  float a, b;
+  if constexpr (KQ == kWQFp8) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    a = f[0];
+    b = f[1];
+  } else {
+    a = static_cast<float>(static_cast<int32_t>(w << (HI ? 8 : 24)) >> 24);
+    b = static_cast<float>(static_cast<int32_t>(w << (HI ? 0 : 16)) >> 24);
+  }
+  if constexpr (kF16) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  else return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);   // bf16: the exact high half
+}
+// Eight codes as one 16-byte chunk of eight 16-bit values, in order.
+template <int KQ, bool kF16>
+__device__ inline u32x4 wcodes8(u32x2 c) {
+  return u32x4{wcode_pair16<KQ, kF16, false>(c[0]), wcode_pair16<KQ, kF16, true>(c[0]),
+               wcode_pair16<KQ, kF16, false>(c[1]), wcode_pair16<KQ, kF16, true>(c[1])};
+}
+
 #ifndef KVC_WIDE_BUFFERS
 #define KVC_WIDE_BUFFERS 4       // LDS tile buffers: the tiles in flight behind the one computed, plus it
 #endif
@@ -86,6 +115,9 @@ struct WideParams {
   int32_t merge_spins;           // bound on the merge's wait for ready flags (polls)
   int32_t flag_stride;           // words per flag row (>= n_splits); the last is the epoch
   int32_t* lens_next;            // kvc_decode_step_advance: seq_lens[b] + 1 written here, or null
+  const char* k_scale;           // the 8-bit mode: fp32 scales [B, H_kv, T] (token axis contiguous)
+  const char* v_scale;
+  int64_t ssb, ssh;              // their strides in bytes
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t wrsrc(const void* base, uint32_t bytes) {
@@ -122,8 +154,10 @@ __device__ inline int64_t wpair_row(const WideParams& p, int b, int g, int v) {
 // latency. The two halves' softmax states are merged through LDS at the end,
 // each wave keeping half of the head dim; the split merge then runs on all
 // eight waves, each over its (column block, half of D).
-template <typename ET, int D, int QB>
+template <typename ET, int D, int QB, int KQ = 0>
 __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p) {
+  constexpr bool kQuant = KQ != 0;       // 8-bit codes and scales (k and v hold codes, one byte each)
+  constexpr bool kF16 = std::is_same<ET, F16P>::value;
   constexpr int NT = 512;               // threads per workgroup
   constexpr int NC = D / 32;            // 32-element slices of a row (score product depth)
   constexpr int ND = D / 16;            // 16-element output blocks
@@ -133,6 +167,10 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   constexpr int TB = kWTile * RB;       // one K or one V tile
   constexpr int NL = kWTile * CPR / NT;   // 16-byte loads per thread per tile, K and V each
   constexpr int NBUF = KVC_WIDE_BUFFERS;
+  // vector-memory loads every wave issues per tile (in the 8-bit mode waves 0
+  // and 1 issue one more, the scales: their waits below are then stricter
+  // than they need be)
+  constexpr int kLoadsPerTile = kQuant ? (D == 128 ? 2 : 1) : 2 * NL;
   constexpr float kLazy = 8.f;          // the reference moves only past ref + 8 (log2 domain)
   // Reference of a pair that has seen no key: finite, so that exp2 of a
   // masked (-inf) score against it is 0 rather than NaN, and far below any
@@ -145,10 +183,18 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // NBUF - 1 of them filling while one is computed; at the end the halves
   // each wave passes its partner ([8 waves][QB][NDH][64 lanes] f32x4) and
   // the references and sums ([8 waves][QB][64 lanes][2]).
-  constexpr int kBufBytes = 2 * TB;
+  // The 8-bit mode stages the codes instead: NBUF buffers of a K and a V
+  // code tile (rows of D bytes, in order) and their K and V scales, and one
+  // more K/V tile, the current tile's codes widened, which the products
+  // read as they read a 16-bit tile.
+  constexpr int kCodeBytes = kWTile * D;                 // one K or V code tile
+  constexpr int kScaleBytes = kWTile * 4;                // one tile's K or V scales
+  constexpr int kBufBytes = kQuant ? 2 * kCodeBytes + 2 * kScaleBytes : 2 * TB;
+  constexpr int kCvt = NBUF * kBufBytes;                 // the widened tile (8-bit mode)
+  constexpr int kStreamBytes = kQuant ? kCvt + 2 * TB : NBUF * kBufBytes;
   constexpr int kXoBytes = 8 * QB * NDH_ * 64 * 16;
   constexpr int kXmlBytes = 8 * QB * 64 * 8;
-  constexpr int kLds = NBUF * kBufBytes > kXoBytes + kXmlBytes ? NBUF * kBufBytes : kXoBytes + kXmlBytes;
+  constexpr int kLds = kStreamBytes > kXoBytes + kXmlBytes ? kStreamBytes : kXoBytes + kXmlBytes;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
 
   // Workgroup placement: every split of a unit on one XCD (id residue mod 8),
@@ -317,8 +363,68 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       lds_load16<true>(vr_, off, kb + TB + m * 1024);
     }
   };
+  // The 8-bit mode: code rows base .. (64 rows, rstride bytes apart, D
+  // bytes each, in order) and their 64 K and 64 V scales (from byte sbase
+  // of the scale resources) into staging buffer buf. D = 128: every thread
+  // takes a K and a V chunk; D = 64: waves 0-3 the K chunks, 4-7 the V
+  // chunks; lanes 0-15 of waves 0 and 1 the scales, four each. Rows past a
+  // resource's range read as zeros.
+  auto load_qtile_from = [&](const u32x4& kr_, const u32x4& vr_, const u32x4& ksr_, const u32x4& vsr_,
+                             uint32_t base, uint32_t rstride, uint32_t sbase, int buf) {
+    constexpr int CPQ = D / 16;                          // 16-byte chunks per code row
+    const uint32_t sb0 = smem_lds + buf * kBufBytes;
+    if constexpr (D == 128) {
+      const int q = wave * 64 + lane;
+      const uint32_t off = base + static_cast<uint32_t>(q / CPQ) * rstride + static_cast<uint32_t>(q % CPQ) * 16u;
+      lds_load16<true>(kr_, off, sb0 + wave * 1024);
+      lds_load16<true>(vr_, off, sb0 + kCodeBytes + wave * 1024);
+    } else {
+      const int q = (wave & 3) * 64 + lane;
+      const uint32_t off = base + static_cast<uint32_t>(q / CPQ) * rstride + static_cast<uint32_t>(q % CPQ) * 16u;
+      if (wave < 4) lds_load16<true>(kr_, off, sb0 + wave * 1024);
+      else lds_load16<true>(vr_, off, sb0 + kCodeBytes + (wave - 4) * 1024);
+    }
+    if (wave < 2 && lane < 16)
+      lds_load16<true>(wave == 0 ? ksr_ : vsr_, sbase + static_cast<uint32_t>(lane) * 16u,
+                       sb0 + 2 * kCodeBytes + wave * kScaleBytes);
+  };
+  const char* ksunit = nullptr;
+  const char* vsunit = nullptr;
+  u32x4 ksrs = u32x4{0u, 0u, 0u, 0u}, vsrs = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (kQuant) {
+    ksunit = uniform_cptr(p.k_scale + (b * p.ssb + g * p.ssh));
+    vsunit = uniform_cptr(p.v_scale + (b * p.ssb + g * p.ssh));
+    ksrs = rsrc_words(ksunit, static_cast<uint32_t>(t_end) * 4u);
+    vsrs = rsrc_words(vsunit, static_cast<uint32_t>(t_end) * 4u);
+  }
   auto load_tile = [&](int t, int buf) {
-    load_tile_from(krs, vrs, static_cast<uint32_t>(t0 + t * kWTile) * st, buf, st);
+    if constexpr (kQuant)
+      load_qtile_from(krs, vrs, ksrs, vsrs, static_cast<uint32_t>(t0 + t * kWTile) * st, st,
+                      static_cast<uint32_t>(t0 + t * kWTile) * 4u, buf);
+    else
+      load_tile_from(krs, vrs, static_cast<uint32_t>(t0 + t * kWTile) * st, buf, st);
+  };
+  // The 8-bit mode: the codes of staging buffer buf widened into the tile the
+  // products read (row r's chunk c at chunk position c ^ tile_swz(r), as the
+  // 16-bit loads place them); eight threads per row.
+  auto convert = [&](int buf) {
+    const char* const src = smem + buf * kBufBytes;
+    char* const dst = smem + kCvt;
+    const int row = tid >> 3, part = tid & 7;
+    const int sw = tile_swz(row);
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const char* const cs = src + kv * kCodeBytes + row * D;
+      char* const cd = dst + kv * TB + row * RB;
+      if constexpr (D == 128) {              // sixteen codes: chunks 2 part and 2 part + 1
+        const u32x4 c = *reinterpret_cast<const u32x4*>(cs + 16 * part);
+        *reinterpret_cast<u32x4*>(cd + ((2 * part) ^ sw) * 16) = wcodes8<KQ, kF16>(u32x2{c[0], c[1]});
+        *reinterpret_cast<u32x4*>(cd + ((2 * part + 1) ^ sw) * 16) = wcodes8<KQ, kF16>(u32x2{c[2], c[3]});
+      } else {                               // eight codes: chunk part
+        const u32x2 c = *reinterpret_cast<const u32x2*>(cs + 8 * part);
+        *reinterpret_cast<u32x4*>(cd + (part ^ sw) * 16) = wcodes8<KQ, kF16>(c);
+      }
+    }
   };
 
   // Per pair: the reference r (log2 domain) the weights are taken against,
@@ -348,8 +454,18 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int vx = ((r16 & 3) >> 1) ^ tile_swz(vrow);
   const int voff = (32 * kh + vrow) * RB + 8 * (r16 & 1);
   auto compute = [&](int tb, int lim, int buf) {
-    const char* const sk = smem + buf * kBufBytes;
+    const char* const sk = kQuant ? smem + kCvt : smem + buf * kBufBytes;
     const char* const sv = sk + TB;
+    // 8-bit mode: the scales of this lane's keys 32 kh + 16 kk + 4 grp + i
+    f32x4 ksc[2], vsc[2];
+    if constexpr (kQuant) {
+      const float* const scl = reinterpret_cast<const float*>(smem + buf * kBufBytes + 2 * kCodeBytes);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        ksc[kk] = *reinterpret_cast<const f32x4*>(scl + 32 * kh + 16 * kk + 4 * grp);
+        vsc[kk] = *reinterpret_cast<const f32x4*>(scl + kWTile + 32 * kh + 16 * kk + 4 * grp);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       if (!cb_on[j]) continue;                // wave-uniform
@@ -375,6 +491,12 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) s[kk] = ET::mfma(ka[kk][cc], qf[j][cc], s[kk]);
+      if constexpr (kQuant) {                 // scores of the codes times the keys' scales
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[kk][i] *= ksc[kk][i];
+      }
       // keys at or past lim, or past the pair's own limit, get weight 0: room
       // is how many keys from this lane's first one are still attended (64
       // or more in every tile but the last of a split and a block's tail)
@@ -406,6 +528,10 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       for (int jj = 0; jj < 8; ++jj) {
         e[jj] = __builtin_amdgcn_exp2f(fmaf(s[jj >> 2][jj & 3], sc, nr));   // masked: 0
         lrun[j] += e[jj];
+      }
+      if constexpr (kQuant) {                 // the weights of the codes: times the values' scales
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) e[jj] *= vsc[jj >> 2][jj & 3];
       }
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -449,10 +575,16 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
 #pragma unroll
     for (int r = 0; r < NBUF; ++r) {          // unrolled: buffers are compile-time
       const int t = it + r;
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * 2 * NL));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * kLoadsPerTile));
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       load_tile(t + NBUF - 1, (r + NBUF - 1) % NBUF);
-      if (t < n_tiles) compute(t0 + t * kWTile, t_end, r);   // uniform
+      if (t < n_tiles) {                      // uniform
+        if constexpr (kQuant) {               // the codes widened, then the products
+          convert(r);
+          __syncthreads();
+        }
+        compute(t0 + t * kWTile, t_end, r);
+      }
     }
   }
   // every load landed and every wave done with the buffers
@@ -462,13 +594,26 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     // The newest rows as keys 0 .. xrows - 1 of one more tile: from
     // k_new/v_new in the fused step, else from the cache; the other keys read
     // as zero (the range ends with the last row) and are masked.
-    const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xfirst) * p.st;
-    const char* vx_ = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xfirst) * p.st;
-    const uint32_t xstride = x_new ? static_cast<uint32_t>(nst) : st;
-    const uint32_t xrange = static_cast<uint32_t>(xrows - 1) * xstride + D * 2;
-    load_tile_from(rsrc_words(kx, xrange), rsrc_words(vx_, xrange), 0u, 0, xstride);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
+    if constexpr (kQuant) {                   // (from the cache: the 8-bit mode has no fused append)
+      const char* kx = kunit + static_cast<int64_t>(xfirst) * p.st;
+      const char* vx_ = vunit + static_cast<int64_t>(xfirst) * p.st;
+      const uint32_t xrange = static_cast<uint32_t>(xrows - 1) * st + D;
+      const uint32_t srange = static_cast<uint32_t>(xrows) * 4u;
+      load_qtile_from(rsrc_words(kx, xrange), rsrc_words(vx_, xrange), rsrc_words(ksunit + 4 * xfirst, srange),
+                      rsrc_words(vsunit + 4 * xfirst, srange), 0u, st, 0u, 0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+      convert(0);
+      __syncthreads();
+    } else {
+      const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xfirst) * p.st;
+      const char* vx_ = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xfirst) * p.st;
+      const uint32_t xstride = x_new ? static_cast<uint32_t>(nst) : st;
+      const uint32_t xrange = static_cast<uint32_t>(xrows - 1) * xstride + D * 2;
+      load_tile_from(rsrc_words(kx, xrange), rsrc_words(vx_, xrange), 0u, 0, xstride);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+    }
     compute(xfirst, n, 0);
   }
   {
@@ -844,6 +989,27 @@ WideKernel pick_wide_qb(int qb) {
   return qb <= 1 ? wide_decode_kernel<ET, D, 1> : wide_decode_kernel<ET, D, 2>;
 }
 
+template <typename ET, int D, int KQ>
+WideKernel pick_wide_qb_q(int qb) {
+  return qb <= 1 ? wide_decode_kernel<ET, D, 1, KQ> : wide_decode_kernel<ET, D, 2, KQ>;
+}
+
+template <typename ET, int KQ>
+WideKernel pick_wide_d_q(int32_t d, int qb) {
+  if (d == 128) return pick_wide_qb_q<ET, 128, KQ>(qb);
+  if (d == 64) return pick_wide_qb_q<ET, 64, KQ>(qb);
+  return nullptr;
+}
+
+// The 8-bit mode: codes of this format widened to the queries' type.
+WideKernel pick_wide_kernel_q(int32_t format, int32_t q_dtype, int32_t d, int qb) {
+  if (format != KVC_QFMT_FP8_E4M3 && format != KVC_QFMT_INT8) return nullptr;
+  const bool fp8 = format == KVC_QFMT_FP8_E4M3;
+  if (q_dtype == KVC_BF16) return fp8 ? pick_wide_d_q<Bf16P, kWQFp8>(d, qb) : pick_wide_d_q<Bf16P, kWQInt8>(d, qb);
+  if (q_dtype == KVC_F16) return fp8 ? pick_wide_d_q<F16P, kWQFp8>(d, qb) : pick_wide_d_q<F16P, kWQInt8>(d, qb);
+  return nullptr;
+}
+
 WideKernel pick_wide_kernel(int32_t dtype, int32_t d, int qb) {
   if (dtype == KVC_BF16 && d == 128) return pick_wide_qb<Bf16P, 128>(qb);
   if (dtype == KVC_BF16 && d == 64) return pick_wide_qb<Bf16P, 64>(qb);
@@ -864,15 +1030,17 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
                               int64_t new_stride_t, const void* q, int32_t n_q_heads, int32_t t_q,
                               float scale_log2, void* out, int32_t out_dtype, const kvc::WsRegions& ws,
                               int32_t splits, int32_t* lens_next, uint32_t* dev_status, hipStream_t stream,
-                              bool check_only) {
+                              bool check_only, const kvc::WideQuant* quant) {
   // (arguments validated by the caller)
-  const int s = kvc::elem_bytes(cache->dtype);
+  const int s = quant != nullptr ? 1 : kvc::elem_bytes(cache->dtype);   // 8-bit mode: strides in bytes
   const int32_t tq = t_q > 0 ? t_q : 1;
   const int32_t group = n_q_heads / cache->n_kv_heads;
   const int32_t pairs = group * tq;
   const int qb = (std::min(pairs, kvc::kWidePairBlock) + 63) / 64;   // column blocks of 64 pairs per workgroup
-  WideKernel kern = pick_wide_kernel(cache->dtype, cache->head_dim, qb);
+  WideKernel kern = quant != nullptr ? pick_wide_kernel_q(quant->format, quant->q_dtype, cache->head_dim, qb)
+                                     : pick_wide_kernel(cache->dtype, cache->head_dim, qb);
   if (kern == nullptr || qb > 2 || pairs > kvc::kWideMaxPairs) return KVC_ERR_UNSUPPORTED;
+  if (quant != nullptr && (t_q > 0 || k_new != nullptr || lens_next != nullptr)) return KVC_ERR_UNSUPPORTED;
   WideParams p;
   p.k = static_cast<char*>(cache->k);
   p.v = static_cast<char*>(cache->v);
@@ -897,6 +1065,10 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.ws_o = ws.o;
   p.ws_ml = ws.ml;
   p.lens_next = lens_next;
+  p.k_scale = quant != nullptr ? reinterpret_cast<const char*>(quant->k_scale) : nullptr;
+  p.v_scale = quant != nullptr ? reinterpret_cast<const char*>(quant->v_scale) : nullptr;
+  p.ssb = quant != nullptr ? quant->scale_stride_b * 4 : 0;
+  p.ssh = quant != nullptr ? quant->scale_stride_h * 4 : 0;
   p.out = out;
   p.status = dev_status;
   p.batch = cache->batch;

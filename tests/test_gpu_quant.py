@@ -120,7 +120,7 @@ def test_quant_zero_row_and_extremes(gpu):
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
 @pytest.mark.parametrize("q_dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (8, 8), (64, 8), (16, 1)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (8, 8), (64, 8), (16, 1), (64, 1), (32, 2)])
 def test_quant_decode_matches_oracle(gpu, fmt, q_dtype, hq, hkv):
     c = QuantCase(batch=5, n_q=hq, n_kv=hkv, d=128, in_dtype=q_dtype, fmt=fmt, lengths=[0, 1, 37, 300, 1100],
                   tag=f"qd{fmt}{q_dtype}{hq}{hkv}")
@@ -128,6 +128,29 @@ def test_quant_decode_matches_oracle(gpu, fmt, q_dtype, hq, hkv):
     got = c.decode(n_pending=1).double().cpu().numpy()
     assert not np.isnan(got).any()
     assert np.abs(got - c.oracle_decode(n_pending=1)).max() <= TOL[q_dtype]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("hq,hkv", [(64, 1), (32, 2)])
+@pytest.mark.parametrize("n_splits", [0, 1, 2, 3])
+def test_quant_decode_wide_groups(gpu, fmt, d, hq, hkv, n_splits):
+    """Groups of 16+ query heads per KV head run on the wide-group kernel's
+    8-bit mode (codes widened to the queries' type in LDS, K scales on the
+    scores, V scales on the weights): lengths on and around the 64-key tile
+    and empty sequences, one, two (last-split merge), three (spread merge) or
+    the library's number of splits, pending rows 0 and 1."""
+    q_dtype = "fp16" if d == 64 else "bf16"
+    c = QuantCase(batch=6, n_q=hq, n_kv=hkv, d=d, in_dtype=q_dtype, fmt=fmt, lengths=[0, 1, 63, 64, 65, 700],
+                  tag=f"qw{fmt}{d}{hq}{hkv}")
+    for n_pending in (0, 1):
+        if n_pending:
+            kvc.quant_append(c.desc, c.seq_lens, c.k_new, c.v_new)
+        st = torch.zeros(1, dtype=torch.int32, device=gpu)
+        got = c.decode(n_pending=n_pending, n_splits=n_splits, status=st).double().cpu().numpy()
+        assert int(st.item()) == 0
+        assert np.isfinite(got).all()
+        assert np.abs(got - c.oracle_decode(n_pending=n_pending)).max() <= TOL[q_dtype]
 
 
 @pytest.mark.parametrize("d", [64, 256])
@@ -150,24 +173,25 @@ def test_quant_split_counts_and_determinism(gpu, n_splits):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
-def test_quant_step_equals_append_plus_decode(gpu, fmt):
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (64, 1)])     # the decode kernel (fused); the wide-group kernel
+def test_quant_step_equals_append_plus_decode(gpu, fmt, hq, hkv):
     """20 steps: kvc_quant_decode_step leaves the same codes/scales and gives
     the same output bits as kvc_quant_append + kvc_quant_decode_attn."""
-    c = QuantCase(batch=3, n_q=8, n_kv=2, d=128, in_dtype="bf16", fmt=fmt, lengths=[0, 30, 250], t_max=280,
-                  tag=f"qst{fmt}")
+    c = QuantCase(batch=3, n_q=hq, n_kv=hkv, d=128, in_dtype="bf16", fmt=fmt, lengths=[0, 30, 250], t_max=280,
+                  tag=f"qst{fmt}{hq}")
     kc2, vc2, ks2, vs2 = c.kc.clone(), c.vc.clone(), c.ks.clone(), c.vs.clone()
     d2 = kvc.qcache_desc(kc2, vc2, ks2, vs2, kvc.QFMT[fmt], torch.bfloat16)
     seq2 = c.seq_lens.clone()
-    ws1, ws2 = kvc.quant_workspace(c.desc, 8), kvc.quant_workspace(d2, 8)
+    ws1, ws2 = kvc.quant_workspace(c.desc, hq), kvc.quant_workspace(d2, hq)
     for step in range(20):
-        kn = synth.normal((3, 2, 128), "bf16", step, "qst", "kn", device=gpu)
-        vn = synth.normal((3, 2, 128), "bf16", step, "qst", "vn", device=gpu)
-        q = synth.normal((3, 8, 128), "bf16", step, "qst", "q", device=gpu)
-        o1 = torch.empty((3, 8, 128), device=gpu)
+        kn = synth.normal((3, hkv, 128), "bf16", step, "qst", "kn", device=gpu)
+        vn = synth.normal((3, hkv, 128), "bf16", step, "qst", "vn", device=gpu)
+        q = synth.normal((3, hq, 128), "bf16", step, "qst", "q", device=gpu)
+        o1 = torch.empty((3, hq, 128), device=gpu)
         kvc.quant_decode_step(c.desc, c.seq_lens, kn, vn, q, o1, ws1)
         kvc.seq_lens_advance(c.seq_lens)
         kvc.quant_append(d2, seq2, kn, vn)
-        o2 = torch.empty((3, 8, 128), device=gpu)
+        o2 = torch.empty((3, hq, 128), device=gpu)
         kvc.quant_decode_attn(d2, seq2, q, o2, ws2, n_pending=1)
         kvc.seq_lens_advance(seq2)
         torch.cuda.synchronize()
@@ -213,6 +237,29 @@ def test_quant_decode_at_gqa_8b_shape_sampled(gpu):
     for b in (0, 7, 15):
         ref = oracle.quant_decode_attention(q[b:b + 1], kc[b:b + 1], ks[b:b + 1], vc[b:b + 1], vs[b:b + 1],
                                             np.array([2048]), oracle.QFMT_FP8_E4M3, n_pending=1)
+        assert np.abs(got[b:b + 1] - ref).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_quant_decode_at_mqa_70b_shape_sampled(gpu, fmt):
+    """The 70B MQA decode shape (B=32, 64 query heads on one KV head, D=128,
+    T=8192) on an 8-bit cache with bf16 queries, the timed step
+    (kvc_quant_decode_step: the append, then the wide-group kernel) with the
+    library's split choice, on sampled sequences."""
+    c = QuantCase(batch=32, n_q=64, n_kv=1, d=128, in_dtype="bf16", fmt=fmt, lengths=[8192] * 32, t_max=8193,
+                  tag=f"q70m{fmt}")
+    out = torch.empty(c.q.shape, device=gpu)
+    st = torch.zeros(1, dtype=torch.int32, device=gpu)
+    ws = kvc.quant_workspace(c.desc, 64)
+    kvc.quant_decode_step(c.desc, c.seq_lens, c.k_new, c.v_new, c.q, out, ws, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got = out.double().cpu().numpy()
+    kc, ks, vc, vs = c.host()
+    q = c.q.cpu()
+    for b in (0, 13, 31):
+        ref = oracle.quant_decode_attention(q[b:b + 1], kc[b:b + 1], ks[b:b + 1], vc[b:b + 1], vs[b:b + 1],
+                                            np.array([8192]), OFMT[fmt], n_pending=1)
         assert np.abs(got[b:b + 1] - ref).max() <= TOL["bf16"]
 
 
