@@ -570,12 +570,17 @@ kvc_status_t kvc_quant_prefill_fill(const kvc_qcache_t* cache, const int32_t* se
  * kvc_decode_workspace_bytes and kvc_decode_attn over the values the codes
  * stand for. q is [B, H_q, D] in in_dtype (KVC_F16 or KVC_BF16, else
  * KVC_ERR_UNSUPPORTED); out is fp32 or in_dtype. The workspace rules are the
- * contiguous decode's.
+ * contiguous decode's. Groups of 16..512 query heads per KV head (head_dim
+ * 64 or 128) read each KV head's codes once per 128 heads (the wide-group
+ * kernel, its codes widened exactly to in_dtype); other groups once per
+ * block of up to 8 heads.
  *
  * kvc_quant_decode_step -- kvc_quant_append then kvc_quant_decode_attn with
  * n_pending = 1, in one launch: the workgroup that attends slot seq_lens[b]
- * quantises the new row itself, folds it in and writes its codes and scale.
- * Codes, scales and output equal those of the two calls bit for bit.
+ * quantises the new row itself, folds it in and writes its codes and scale
+ * (for the groups the wide-group kernel takes: the two launches, enqueued
+ * after every host check of both). Codes, scales and output equal those of
+ * the two calls bit for bit.
  */
 size_t kvc_quant_decode_workspace_bytes(const kvc_qcache_t* cache, int32_t n_q_heads, int32_t n_splits);
 kvc_status_t kvc_quant_decode_attn(const kvc_qcache_t* cache, const int32_t* seq_lens, int32_t n_pending,
