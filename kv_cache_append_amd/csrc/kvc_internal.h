@@ -159,13 +159,14 @@ struct WideQuant {
 };
 // check_only: every host check, nothing enqueued (for a call that enqueues a
 // second launch after a first one and must fail before either). quant: the
-// 8-bit mode (decode only, no fused append).
+// 8-bit mode (decode only, no fused append). pg: a paged cache (cache is its
+// view, see paged_view); ring: a sliding-window ring cache; both decode only.
 kvc_status_t launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens, int32_t n_pending, const void* k_new,
                          const void* v_new, int64_t new_stride_b, int64_t new_stride_h, int64_t new_stride_t,
                          const void* q, int32_t n_q_heads, int32_t t_q, float scale_log2, void* out,
                          int32_t out_dtype, const WsRegions& ws, int32_t splits, int32_t* lens_next,
                          uint32_t* dev_status, hipStream_t stream, bool check_only = false,
-                         const WideQuant* quant = nullptr);
+                         const WideQuant* quant = nullptr, const PageInfo* pg = nullptr, bool ring = false);
 // Whether a decode on this 8-bit cache runs on the wide-group kernel's 8-bit
 // mode: fp16/bf16 queries, head dim 64 or 128, KVC_WIDE_QUANT_MIN_GROUP ..
 // kWideMaxPairs query heads per KV head.

@@ -1934,10 +1934,10 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   // The kernels address one (sequence, KV head) slice of K/V with 32-bit
   // byte offsets (plus up to two tiles past the end, read back as zeros).
   if ((static_cast<int64_t>(cache->max_len) + 2048) * cache->stride_t * s > 0x7fffffffll) return KVC_ERR_SHAPE;
-  // Contiguous 16-bit caches with 8..128 (query, head) pairs per KV head run
-  // on the wide-group kernel (K/V streamed once for all pairs, both products
-  // on the matrix cores).
-  const bool wide = pg == nullptr && !ring && kvc::routes_wide(cache, n_qv);
+  // 16-bit caches with 8..512 (query, head) pairs per KV head run on the
+  // wide-group kernel (K/V streamed once per 128 pairs, both products on the
+  // matrix cores): contiguous caches, and paged and ring caches in decode.
+  const bool wide = kvc::routes_wide(cache, n_qv) && ((pg == nullptr && !ring) || t_q == 0);
   const int32_t splits = n_splits > 0 ? n_splits : kvc::auto_splits(cache, n_qv, wide);
   kvc::WsRegions wr;
   if (regions_fn != nullptr) {                   // exchange space the caller of this function lays out
@@ -1967,7 +1967,7 @@ kvc_status_t launch_decode(const kvc_cache_t* cache, const int32_t* seq_lens, in
   if (wide)
     return kvc::launch_wide(cache, seq_lens, n_pending, k_new, v_new, new_stride_b, new_stride_h, new_stride_t, q,
                             n_q_heads, t_q, scale_log2, out, out_dtype, wr, splits, lens_next, dev_status, stream,
-                            check_only);
+                            check_only, nullptr, pg, ring);
   const int gb = kvc::heads_per_block(group * tq);
   DecodeParams p;
   p.k = static_cast<char*>(cache->k);

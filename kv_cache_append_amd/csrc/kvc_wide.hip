@@ -115,6 +115,8 @@ struct WideParams {
   int32_t merge_spins;           // bound on the merge's wait for ready flags (polls)
   int32_t flag_stride;           // words per flag row (>= n_splits); the last is the epoch
   int32_t* lens_next;            // kvc_decode_step_advance: seq_lens[b] + 1 written here, or null
+  const int32_t* table;          // paged mode: page table [B, table_stride] (slot r: page table[b][r >> page_shift])
+  int32_t table_stride, page_shift, n_pages;
   const char* k_scale;           // the 8-bit mode: fp32 scales [B, H_kv, T] (token axis contiguous)
   const char* v_scale;
   int64_t ssb, ssh;              // their strides in bytes
@@ -154,9 +156,15 @@ __device__ inline int64_t wpair_row(const WideParams& p, int b, int g, int v) {
 // latency. The two halves' softmax states are merged through LDS at the end,
 // each wave keeping half of the head dim; the split merge then runs on all
 // eight waves, each over its (column block, half of D).
-template <typename ET, int D, int QB, int KQ = 0>
+// AM: the cache's addressing. 0: contiguous; 1: paged (k and v are page
+// pools, sb the page stride; decode only); 2: ring (a sliding window of
+// max_len slots, token i in slot i mod max_len; decode only).
+template <typename ET, int D, int QB, int KQ = 0, int AM = 0>
 __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p) {
   constexpr bool kQuant = KQ != 0;       // 8-bit codes and scales (k and v hold codes, one byte each)
+  constexpr bool kPaged = AM == 1;
+  constexpr bool kRing = AM == 2;
+  static_assert(!kQuant || AM == 0, "the 8-bit mode is contiguous");
   constexpr bool kF16 = std::is_same<ET, F16P>::value;
   constexpr int NT = 512;               // threads per workgroup
   constexpr int NC = D / 32;            // 32-element slices of a row (score product depth)
@@ -262,8 +270,12 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   uint32_t dflags = c0 < 0 ? KVC_DEVERR_BADLEN : 0u;
   const int add = p.block ? p.t_q : (p.k_new != nullptr ? 1 : p.n_pending);
   const int64_t n64 = static_cast<int64_t>(c) + add;
-  int n, append_row = -1;
-  if (p.block) {                                     // the whole block must fit
+  int n, append_row = -1, newest = -1;
+  if constexpr (kRing) {                             // no capacity limit: the ring wraps
+    if (c0 >= 0 && p.k_new != nullptr) append_row = c0 % p.max_len;
+    n = c0 < 0 ? 0 : static_cast<int>(min(n64, static_cast<int64_t>(p.max_len)));
+    newest = c0 < 0 ? -1 : static_cast<int>((n64 - 1) % p.max_len);
+  } else if (p.block) {                              // the whole block must fit
     if (c0 >= 0 && n64 > p.max_len) dflags |= KVC_DEVERR_CAPACITY;
     n = (c0 < 0 || n64 > p.max_len) ? 0 : static_cast<int>(n64);
     if (p.k_new != nullptr && n > 0) append_row = c0;   // the fused fill writes slots c0 .. c0 + t_q - 1
@@ -295,8 +307,11 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // append (or fill), whose rows come from k_new/v_new, and the separate
   // calls, which read them from the cache, add the same rows in the same
   // order.
+  // (Ring: the newest row's slot can be anywhere in [0, n); every slot is
+  // streamed and that one masked in the stream, the order of keys being
+  // immaterial to the result.)
   const int xrows = p.block ? p.t_q : 1;
-  const int streamed = n - xrows;
+  const int streamed = kRing ? n : n - xrows;
   const int chunk = max(kWTile, ((streamed + p.n_splits - 1) / p.n_splits + kWTile - 1) & ~(kWTile - 1));
   const int ns = streamed > 0 ? min(p.n_splits, (streamed + chunk - 1) / chunk) : 1;
   if (split >= ns) {                                 // inactive split
@@ -307,7 +322,8 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int t0 = split * chunk;
   const int t_end = split == ns - 1 ? streamed : t0 + chunk;   // rows streamed from the cache: [t0, t_end)
   const bool has_x = split == ns - 1;
-  const int xfirst = n - xrows;                      // the first folded row
+  const int xfirst = kRing ? newest : n - xrows;     // the first folded row
+  const int skip = kRing ? newest : -1;              // a slot the stream masks
   const bool x_new = has_x && append_row == xfirst;
 
   // The fused append (or fill): the newest rows into their slots (no
@@ -350,15 +366,20 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   // (q / CPR, q % CPR), from the row's chunk q % CPR ^ tile_swz(row). Rows
   // past the streamed ones read as zeros (and are masked).
   const uint32_t smem_lds = KVC_LDS_ADDR(smem);
-  auto load_tile_from = [&](const u32x4& kr_, const u32x4& vr_, uint32_t base, int buf, uint32_t rstride) {
+  // Ring mode: row `hole` of the tile (the newest slot, folded in apart)
+  // reads as zeros too, whatever the slot holds (a stale or not yet written
+  // row: its weight is 0, and 0 times a non-finite value is not).
+  auto load_tile_from = [&](const u32x4& kr_, const u32x4& vr_, uint32_t base, int buf, uint32_t rstride,
+                            int hole) {
     const uint32_t kb = smem_lds + buf * kBufBytes;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int m = wave * NL + i;
       const int q = m * 64 + lane;
       const int row = q / CPR;
-      const uint32_t off =
+      uint32_t off =
           base + static_cast<uint32_t>(row) * rstride + static_cast<uint32_t>((q % CPR) ^ tile_swz(row)) * 16u;
+      if constexpr (kRing) off = row == hole ? 0x80000000u : off;   // past every range (< 2^31 bytes)
       lds_load16<true>(kr_, off, kb + m * 1024);
       lds_load16<true>(vr_, off, kb + TB + m * 1024);
     }
@@ -397,12 +418,65 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
     ksrs = rsrc_words(ksunit, static_cast<uint32_t>(t_end) * 4u);
     vsrs = rsrc_words(vsunit, static_cast<uint32_t>(t_end) * 4u);
   }
+  // Paged mode: wave w loads rows 8w .. 8w + 7 of a tile (its NL loads of 64
+  // chunks), which lie in one page (pages hold 16+ rows, tiles start on a
+  // multiple of 64): one buffer resource per wave and tile. Lane j of pidv
+  // holds that page for tile (t & ~63) + j, read 64 tiles at a time; a tile's
+  // page is taken with readlane. A page outside the pool reads as zeros and
+  // is reported.
+  int pidv = -1, pid_block = -1;
+  auto tile_page = [&](int t) {               // t: wave-uniform
+    if ((t >> 6) != pid_block) {
+      pid_block = t >> 6;
+      const int row = t0 + ((pid_block << 6) + lane) * kWTile + 8 * wave;
+      pidv = -1;
+      if (row < t_end) pidv = p.table[static_cast<int64_t>(b) * p.table_stride + (row >> p.page_shift)];
+    }
+    return __builtin_amdgcn_readlane(pidv, t & 63);
+  };
+  auto load_tile_paged = [&](int t, int buf) {
+    const int r0 = t0 + t * kWTile + 8 * wave;  // this wave's first row
+    const int left = t_end - r0;
+    const int pg = left > 0 ? tile_page(t) : 0;
+    const bool bad = left > 0 && (pg < 0 || pg >= p.n_pages);
+    if (bad && lane == 0 && p.status != nullptr) atomicOr(p.status, KVC_DEVERR_PAGE);
+    const bool ok = left > 0 && !bad;
+    const uint32_t range = ok ? static_cast<uint32_t>(min(left, 8)) * st : 0u;
+    const int64_t boff =
+        ok ? pg * p.sb + g * p.sh + static_cast<int64_t>(r0 & ((1 << p.page_shift) - 1)) * p.st : int64_t{0};
+    const u32x4 kr = rsrc_words(p.k + boff, range);
+    const u32x4 vr = rsrc_words(p.v + boff, range);
+    const uint32_t kb = smem_lds + buf * kBufBytes;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int m = wave * NL + i;
+      const int q = m * 64 + lane;
+      const int row = q / CPR;                  // 8 wave .. 8 wave + 7
+      const uint32_t off =
+          static_cast<uint32_t>(row - 8 * wave) * st + static_cast<uint32_t>((q % CPR) ^ tile_swz(row)) * 16u;
+      lds_load16<true>(kr, off, kb + m * 1024);
+      lds_load16<true>(vr, off, kb + TB + m * 1024);
+    }
+  };
+  // Byte offset of slot `row` of (sequence b, KV head g) in the cache or page
+  // pool, or -1 when its page is not in the pool.
+  auto slot_offset = [&](int row) -> int64_t {
+    if constexpr (kPaged) {
+      const int pg = p.table[static_cast<int64_t>(b) * p.table_stride + (row >> p.page_shift)];
+      if (pg < 0 || pg >= p.n_pages) return -1;
+      return pg * p.sb + g * p.sh + static_cast<int64_t>(row & ((1 << p.page_shift) - 1)) * p.st;
+    } else {
+      return b * p.sb + g * p.sh + static_cast<int64_t>(row) * p.st;
+    }
+  };
   auto load_tile = [&](int t, int buf) {
-    if constexpr (kQuant)
+    if constexpr (kPaged)
+      load_tile_paged(t, buf);
+    else if constexpr (kQuant)
       load_qtile_from(krs, vrs, ksrs, vsrs, static_cast<uint32_t>(t0 + t * kWTile) * st, st,
                       static_cast<uint32_t>(t0 + t * kWTile) * 4u, buf);
     else
-      load_tile_from(krs, vrs, static_cast<uint32_t>(t0 + t * kWTile) * st, buf, st);
+      load_tile_from(krs, vrs, static_cast<uint32_t>(t0 + t * kWTile) * st, buf, st, skip - (t0 + t * kWTile));
   };
   // The 8-bit mode: the codes of staging buffer buf widened into the tile the
   // products read (row r's chunk c at chunk position c ^ tile_swz(r), as the
@@ -453,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
   const int vrow = 4 * grp + (r16 >> 2);
   const int vx = ((r16 & 3) >> 1) ^ tile_swz(vrow);
   const int voff = (32 * kh + vrow) * RB + 8 * (r16 & 1);
-  auto compute = [&](int tb, int lim, int buf) {
+  auto compute = [&](int tb, int lim, int buf, int skp) {
     const char* const sk = kQuant ? smem + kCvt : smem + buf * kBufBytes;
     const char* const sv = sk + TB;
     // 8-bit mode: the scales of this lane's keys 32 kh + 16 kk + 4 grp + i
@@ -501,12 +575,14 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       // is how many keys from this lane's first one are still attended (64
       // or more in every tile but the last of a split and a block's tail)
       const int room = min(lim, plim[j]) - tb - (32 * kh + 4 * grp);
+      const int hole = skp - tb - (32 * kh + 4 * grp);    // ring: the newest slot, folded in apart
       float mx = -INFINITY;                   // raw scores: the scale is positive
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[kk][i] = 16 * kk + i < room ? s[kk][i] : -INFINITY;
+          if constexpr (kRing) s[kk][i] = (16 * kk + i < room && 16 * kk + i != hole) ? s[kk][i] : -INFINITY;
+          else s[kk][i] = 16 * kk + i < room ? s[kk][i] : -INFINITY;
           mx = fmaxf(mx, s[kk][i]);
         }
       if (__any(mx * sc > mrun[j] + kLazy)) {   // wave-uniform; the first tile always
@@ -583,7 +659,7 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
           convert(r);
           __syncthreads();
         }
-        compute(t0 + t * kWTile, t_end, r);
+        compute(t0 + t * kWTile, t_end, r, skip);
       }
     }
   }
@@ -609,19 +685,44 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
       const char* kx = x_new ? p.k_new + (b * p.nsb + g * p.nsh) : kunit + static_cast<int64_t>(xfirst) * p.st;
       const char* vx_ = x_new ? p.v_new + (b * p.nsb + g * p.nsh) : vunit + static_cast<int64_t>(xfirst) * p.st;
       const uint32_t xstride = x_new ? static_cast<uint32_t>(nst) : st;
-      const uint32_t xrange = static_cast<uint32_t>(xrows - 1) * xstride + D * 2;
-      load_tile_from(rsrc_words(kx, xrange), rsrc_words(vx_, xrange), 0u, 0, xstride);
+      uint32_t xrange = static_cast<uint32_t>(xrows - 1) * xstride + D * 2;
+      if constexpr (kPaged) {                 // (decode: one row, in one page)
+        if (!x_new) {
+          const int64_t xo = slot_offset(xfirst);
+          if (xo < 0) {                       // not in the pool: zeros, reported
+            xrange = 0u;
+            if (tid == 0 && p.status != nullptr) atomicOr(p.status, KVC_DEVERR_PAGE);
+          }
+          kx = p.k + (xo < 0 ? 0 : xo);
+          vx_ = p.v + (xo < 0 ? 0 : xo);
+        }
+      }
+      load_tile_from(rsrc_words(kx, xrange), rsrc_words(vx_, xrange), 0u, 0, xstride, -1);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
     }
-    compute(xfirst, n, 0);
+    compute(xfirst, xfirst + xrows, 0, -1);   // (its rows only: in a ring they need not be the last)
   }
   {
     // the fused append's stores (the rows' loads were issued at entry)
-    const int64_t aoff = static_cast<int64_t>(append_row < 0 ? 0 : append_row) * p.st;
-    const uint32_t crange = x_write ? static_cast<uint32_t>((xrows - 1) * st + D * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t ka_rs = wrsrc(uniform_cptr(kunit + aoff), crange);
-    const __amdgpu_buffer_rsrc_t va_rs = wrsrc(uniform_cptr(vunit + aoff), crange);
+    int64_t aoff = static_cast<int64_t>(append_row < 0 ? 0 : append_row) * p.st;
+    uint32_t crange = x_write ? static_cast<uint32_t>((xrows - 1) * st + D * 2) : 0u;
+    const char* abase_k = kunit;
+    const char* abase_v = vunit;
+    if constexpr (kPaged) {                   // the new row's page (decode: one row)
+      aoff = 0;
+      if (x_write) {
+        const int64_t so = slot_offset(append_row);
+        if (so < 0) {                         // not in the pool: not written, reported
+          crange = 0u;
+          if (tid == 0 && p.status != nullptr) atomicOr(p.status, KVC_DEVERR_PAGE);
+        }
+        abase_k = p.k + (so < 0 ? 0 : so);
+        abase_v = p.v + (so < 0 ? 0 : so);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t ka_rs = wrsrc(uniform_cptr(abase_k + aoff), crange);
+    const __amdgpu_buffer_rsrc_t va_rs = wrsrc(uniform_cptr(abase_v + aoff), crange);
     const int coff = static_cast<int>((tid / CPR) * st + (tid % CPR) * 16);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, kn_row),
                                            ka_rs, coff, 0, 0);
@@ -984,9 +1085,17 @@ __global__ __launch_bounds__(512, 1) void wide_decode_kernel(const WideParams p)
 
 typedef void (*WideKernel)(const WideParams);
 
-template <typename ET, int D>
+template <typename ET, int D, int AM>
 WideKernel pick_wide_qb(int qb) {
-  return qb <= 1 ? wide_decode_kernel<ET, D, 1> : wide_decode_kernel<ET, D, 2>;
+  return qb <= 1 ? wide_decode_kernel<ET, D, 1, 0, AM> : wide_decode_kernel<ET, D, 2, 0, AM>;
+}
+
+// am: the cache's addressing (0 contiguous, 1 paged, 2 ring)
+template <typename ET, int D>
+WideKernel pick_wide_am(int qb, int am) {
+  if (am == 1) return pick_wide_qb<ET, D, 1>(qb);
+  if (am == 2) return pick_wide_qb<ET, D, 2>(qb);
+  return pick_wide_qb<ET, D, 0>(qb);
 }
 
 template <typename ET, int D, int KQ>
@@ -1010,11 +1119,11 @@ WideKernel pick_wide_kernel_q(int32_t format, int32_t q_dtype, int32_t d, int qb
   return nullptr;
 }
 
-WideKernel pick_wide_kernel(int32_t dtype, int32_t d, int qb) {
-  if (dtype == KVC_BF16 && d == 128) return pick_wide_qb<Bf16P, 128>(qb);
-  if (dtype == KVC_BF16 && d == 64) return pick_wide_qb<Bf16P, 64>(qb);
-  if (dtype == KVC_F16 && d == 128) return pick_wide_qb<F16P, 128>(qb);
-  if (dtype == KVC_F16 && d == 64) return pick_wide_qb<F16P, 64>(qb);
+WideKernel pick_wide_kernel(int32_t dtype, int32_t d, int qb, int am) {
+  if (dtype == KVC_BF16 && d == 128) return pick_wide_am<Bf16P, 128>(qb, am);
+  if (dtype == KVC_BF16 && d == 64) return pick_wide_am<Bf16P, 64>(qb, am);
+  if (dtype == KVC_F16 && d == 128) return pick_wide_am<F16P, 128>(qb, am);
+  if (dtype == KVC_F16 && d == 64) return pick_wide_am<F16P, 64>(qb, am);
   return nullptr;
 }
 
@@ -1030,15 +1139,17 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
                               int64_t new_stride_t, const void* q, int32_t n_q_heads, int32_t t_q,
                               float scale_log2, void* out, int32_t out_dtype, const kvc::WsRegions& ws,
                               int32_t splits, int32_t* lens_next, uint32_t* dev_status, hipStream_t stream,
-                              bool check_only, const kvc::WideQuant* quant) {
+                              bool check_only, const kvc::WideQuant* quant, const kvc::PageInfo* pg, bool ring) {
   // (arguments validated by the caller)
   const int s = quant != nullptr ? 1 : kvc::elem_bytes(cache->dtype);   // 8-bit mode: strides in bytes
   const int32_t tq = t_q > 0 ? t_q : 1;
   const int32_t group = n_q_heads / cache->n_kv_heads;
   const int32_t pairs = group * tq;
   const int qb = (std::min(pairs, kvc::kWidePairBlock) + 63) / 64;   // column blocks of 64 pairs per workgroup
+  const int am = pg != nullptr ? 1 : (ring ? 2 : 0);
+  if (am != 0 && (t_q > 0 || quant != nullptr)) return KVC_ERR_UNSUPPORTED;   // paged and ring: decode, 16-bit
   WideKernel kern = quant != nullptr ? pick_wide_kernel_q(quant->format, quant->q_dtype, cache->head_dim, qb)
-                                     : pick_wide_kernel(cache->dtype, cache->head_dim, qb);
+                                     : pick_wide_kernel(cache->dtype, cache->head_dim, qb, am);
   if (kern == nullptr || qb > 2 || pairs > kvc::kWideMaxPairs) return KVC_ERR_UNSUPPORTED;
   if (quant != nullptr && (t_q > 0 || k_new != nullptr || lens_next != nullptr)) return KVC_ERR_UNSUPPORTED;
   WideParams p;
@@ -1065,6 +1176,10 @@ kvc_status_t kvc::launch_wide(const kvc_cache_t* cache, const int32_t* seq_lens,
   p.ws_o = ws.o;
   p.ws_ml = ws.ml;
   p.lens_next = lens_next;
+  p.table = pg != nullptr ? pg->table : nullptr;
+  p.table_stride = pg != nullptr ? pg->table_stride : 0;
+  p.page_shift = pg != nullptr ? pg->page_shift : 0;
+  p.n_pages = pg != nullptr ? pg->n_pages : 0;
   p.k_scale = quant != nullptr ? reinterpret_cast<const char*>(quant->k_scale) : nullptr;
   p.v_scale = quant != nullptr ? reinterpret_cast<const char*>(quant->v_scale) : nullptr;
   p.ssb = quant != nullptr ? quant->scale_stride_b * 4 : 0;
