@@ -417,7 +417,9 @@ kvc_status_t kvc_prefill_attn(const kvc_cache_t* cache, const int32_t* seq_lens,
  * step, which also writes the new token into slot seq_lens[b] % W). With no
  * mask the order of the slots does not matter. Arguments, workspace
  * (kvc_decode_workspace_bytes) and errors as for the contiguous calls; the
- * step equals kvc_ring_append + kvc_ring_decode_attn bit for bit.
+ * step equals kvc_ring_append + kvc_ring_decode_attn bit for bit. Groups of
+ * 8..512 query heads on fp16/bf16 caches with head_dim 64 or 128 stream each
+ * KV head once per 128 heads, as in kvc_decode_attn.
  */
 kvc_status_t kvc_ring_append(const kvc_cache_t* cache, const int32_t* seq_lens,
                              const void* k_new, const void* v_new,
@@ -489,7 +491,8 @@ kvc_status_t kvc_paged_prefill_fill(const kvc_paged_cache_t* cache, const int32_
  * through the page table (and, for the step, writing the new row into its
  * page). fp16/bf16 caches with head_dim a multiple of 32 and page_size a
  * power of two >= 16 (else KVC_ERR_UNSUPPORTED). The result equals the
- * contiguous call on the same logical cache bit for bit. A table entry
+ * contiguous call on the same logical cache bit for bit (groups of 8..512
+ * heads at head_dim 64 or 128 on the same wide-group kernel). A table entry
  * outside the pool sets KVC_DEVERR_PAGE; that page reads as zeros and the
  * sequence's output is not valid.
  */
