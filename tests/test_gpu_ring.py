@@ -91,6 +91,32 @@ def test_ring_decode_matches_oracle(gpu, dtype, hq, hkv):
         assert np.abs(out[bb:bb + 1].double().cpu().numpy() - r2).max() <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_splits", [0, 2])
+def test_ring_wide_groups_odd_window(gpu, d, n_splits):
+    """16 query heads per KV head (the wide-group kernel's ring mode) on a
+    37-slot ring: the newest slot lands anywhere inside a 64-row tile, and a
+    tile holds the whole window; against the oracle and plain decode over
+    the last W tokens."""
+    window, hq, hkv = 37, 32, 2
+    lengths = [1, 36, 37, 38, 100, 1000]
+    k_hist, v_hist = _history(len(lengths), hkv, max(lengths), d, "fp16", f"rw{d}{n_splits}", gpu)
+    k, v = _ring_device(k_hist, v_hist, lengths, window, gpu)
+    q = synth.normal((len(lengths), hq, d), "fp16", 6, "rwq", d, device=gpu)
+    seq = torch.tensor(lengths, dtype=torch.int32, device=gpu)
+    out = torch.empty((len(lengths), hq, d), device=gpu)
+    ws = kvc.workspace(k, v, hq, n_splits)
+    kvc.ring_decode_attn(k, v, seq, q, out, ws, n_pending=0, n_splits=n_splits)
+    torch.cuda.synchronize()
+    ref = oracle.ring_decode_attention(q.cpu(), k.cpu(), v.cpu(), np.array(lengths), n_pending=0)
+    assert np.abs(out.double().cpu().numpy() - ref).max() <= TOL["fp16"]
+    for bb, n in enumerate(lengths):
+        lo = max(0, n - window)
+        r2 = oracle.decode_attention(q[bb:bb + 1].cpu(), k_hist[bb:bb + 1, :, lo:n].cpu(),
+                                     v_hist[bb:bb + 1, :, lo:n].cpu(), np.array([n - lo]), n_pending=0)
+        assert np.abs(out[bb:bb + 1].double().cpu().numpy() - r2).max() <= TOL["fp16"]
+
+
 @pytest.mark.parametrize("n_splits", [1, 3, 8])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("hq", [8, 32])
