@@ -104,7 +104,7 @@ def test_paged_fill_places_rows_through_the_table(gpu):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("page", [16, 64, 256])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (8, 8), (16, 1), (8, 1), (32, 2), (64, 1)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (8, 8), (16, 1), (8, 1), (32, 2), (64, 1), (128, 1), (512, 2)])
 def test_paged_decode_matches_oracle_and_contiguous(gpu, dtype, page, hq, hkv):
     c = PagedCase(batch=3, n_q=hq, n_kv=hkv, d=128, dtype=dtype, lengths=[0, 300, 1100], page=page,
                   tag=f"pg{dtype}{page}{hq}{hkv}")
@@ -137,12 +137,12 @@ def test_paged_other_head_dims(gpu, d, hq):
     assert torch.equal(_paged_out(c, n_pending=0), _contig_out(c, n_pending=0))
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (64, 1)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (64, 1), (256, 1)])
 def test_paged_step_equals_append_plus_decode_over_many_steps(gpu, hq, hkv):
     """Fused paged step, 40 steps crossing page boundaries (P = 16): cache and
     output bit-identical to paged append + paged decode, and the pool matches
-    the oracle's paged append. 64 query heads on one KV head run on the
-    wide-group kernel."""
+    the oracle's paged append. 64 and 256 query heads on one KV head run on
+    the wide-group kernel (256: two pair blocks, the first writing the row)."""
     c = PagedCase(batch=3, n_q=hq, n_kv=hkv, d=128, dtype="bf16", lengths=[5, 31, 200], page=16,
                   tag=f"pgstep{hq}", cap_tokens=260)
     kp2, vp2 = c.kp.clone(), c.vp.clone()

@@ -68,7 +68,7 @@ def test_ring_fill_keeps_the_last_window_bitwise(gpu, dtype, d):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (4, 4), (16, 2), (64, 1)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (4, 4), (16, 2), (64, 1), (128, 1), (512, 2)])
 def test_ring_decode_matches_oracle(gpu, dtype, hq, hkv):
     window = 512
     lengths = [1, 300, 511, 512, 513, 2000]
@@ -119,12 +119,13 @@ def test_ring_wide_groups_odd_window(gpu, d, n_splits):
 
 @pytest.mark.parametrize("n_splits", [1, 3, 8])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("hq", [8, 32])
+@pytest.mark.parametrize("hq", [8, 32, 512])
 def test_ring_step_equals_append_plus_decode_across_wraps(gpu, n_splits, dtype, hq):
     """60 fused steps on a 48-slot ring from lengths around the window: cache
     and output bit-identical to ring append + ring decode, and within
     tolerance of the oracle, while the newest slot walks through the ring.
-    16 query heads per KV head in bf16 run on the wide-group kernel."""
+    16 and 256 query heads per KV head in bf16 run on the wide-group kernel
+    (256: two pair blocks)."""
     window, hkv, d = 48, 2, 128 if dtype == "bf16" else 64
     lengths = [0, 20, 47, 48, 100]
     k_hist, v_hist = _history(5, hkv, max(lengths) + 1, d, dtype, f"rs{dtype}{n_splits}{hq}", gpu)
